@@ -1,0 +1,267 @@
+"""Decode-step benchmark of the RTPurbo sparse decode path on one MI355X.
+
+One step = one decode step through a 48-layer attention stack at N = 2^20
+cached tokens (batch 1, 32 query / 4 KV heads, d = 128, bf16 K/V ~ 96 GiB
+resident): per layer, the indexer scan, top-p selection and sparse
+attention for the 8 retrieval query heads of KV head 0, and sink + window
+attention for the 24 local query heads.  Layers run in sequence.  The step is
+captured once in a HIP graph and replayed.
+
+Prints ONE JSON line (rank 0) with steps/s, the dominant kernel's roofline
+and the CPU oracle's baseline on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--p", type=float, default=0.9)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import sparse_long_context_indexer_amd as rtp
+    from sparse_long_context_indexer_amd.runner import DecodeLayer
+
+    rtp.lib()  # fails loudly if librtp.so is missing
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    B, L, N, Hq, Hkv, H_r, d = cfg.B, cfg.L, cfg.N, cfg.Hq, cfg.Hkv, cfg.H_r, cfg.d
+    G_r = cfg.G_r
+    p = args.p if args.p else cfg.p_list[0]
+
+    # ---------------------------------------------------------- inputs
+    t0 = time.time()
+    log(f"allocating {cfg.name}: L={L} B={B} N={N} Hq={Hq} Hkv={Hkv} H_r={H_r}")
+    K_all = torch.empty((L, B, Hkv, N, d), dtype=torch.int16, device=dev)
+    V_all = torch.empty((L, B, Hkv, N, d), dtype=torch.int16, device=dev)
+    kr_all = torch.empty((L, B, G_r, N, cfg.r), dtype=torch.float32, device=dev)
+    qr_all = torch.empty((L, B, H_r, cfg.r), dtype=torch.float32, device=dev)
+    q_all = torch.empty((L, B, Hq, d), dtype=torch.int16, device=dev)
+    out_all = torch.zeros((L, B, Hq, d), dtype=torch.float32, device=dev)
+    stage = [torch.empty((B, Hkv, N, d), dtype=torch.int16, pin_memory=True) for _ in range(2)]
+    copy_stream = torch.cuda.Stream(device=dev)
+    evs = [None, None]
+    n = 0
+    for l in range(L):
+        for which, dst in (("K", K_all), ("V", V_all)):
+            buf = n % 2
+            if evs[buf] is not None:
+                evs[buf].synchronize()
+            synth.layer_kv(cfg, l, which, out=stage[buf].numpy().view(np.uint16))
+            with torch.cuda.stream(copy_stream):
+                dst[l].copy_(stage[buf], non_blocking=True)
+                evs[buf] = torch.cuda.Event()
+                evs[buf].record(copy_stream)
+            n += 1
+        kr_all[l].copy_(torch.from_numpy(synth.layer_kr(cfg, l)))
+        qr_all[l].copy_(torch.from_numpy(synth.layer_qr(cfg, l)))
+        q_all[l].copy_(torch.from_numpy(synth.layer_q(cfg, l).view(np.int16)))
+        if l % 8 == 7:
+            log(f"  uploaded layers 0..{l} ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    del stage
+    log(f"inputs resident ({time.time() - t0:.1f}s)")
+
+    step_layer = DecodeLayer(B, Hq, Hkv, N, H_r, cfg.n_sink, cfg.window, dev)
+    scale = cfg.scale
+
+    def step():
+        for l in range(L):
+            step_layer(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l], p, scale, out_all[l])
+
+    stream = torch.cuda.current_stream(dev)
+    if args.no_graph:
+        run = step
+    else:
+        step()  # warm the caching allocator outside capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+
+    # ---------------------------------------------------------- timing
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f})")
+
+    # ------------------------------------------ per-call timing (eager)
+    # Each C-ABI call of the step, launched alone over all layers on the
+    # current stream and bracketed by HIP events on that stream.
+    def time_call(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / L * 1e3  # us per layer
+
+    sl = step_layer
+    us = {
+        "rtp_index_scores": time_call(lambda: [rtp.rtp_index_scores(qr_all[l], kr_all[l], sl.scores)
+                                                for l in range(L)]),
+        "rtp_topp_select": time_call(lambda: [rtp.rtp_topp_select(sl.scores, p, sl.idx, sl.count, sl.ws_sel)
+                                               for l in range(L)]),
+        "rtp_sparse_decode": time_call(lambda: [rtp.rtp_sparse_decode(q_all[l], K_all[l], V_all[l], sl.idx, sl.count, 0, scale, out_all[l], sl.ws_sparse)
+                                                 for l in range(L)]),
+        "rtp_local_decode": time_call(lambda: [rtp.rtp_local_decode(q_all[l], K_all[l], V_all[l], N, H_r, Hq - H_r, cfg.n_sink, cfg.window, scale, out_all[l], sl.ws_local)
+                                                for l in range(L)]),
+    }
+    log("per-call us/layer: " + ", ".join(f"{k}={v:.2f}" for k, v in us.items()))
+
+    # --------------------------------------------- algorithmic bytes
+    # Per layer: the k_r scan (N * 16 fp32 per retrieval KV head), the union
+    # of the retrieval heads' kept rows (K + V, 512 B each), and the local
+    # heads' sink + window rows (512 B each, once per local KV head).
+    w_start = max(0, N - cfg.window)
+    w_rows = min(cfg.n_sink, w_start) + (N - w_start)
+    local_kv = Hkv - G_r
+    n_sel = []
+    union = []
+    for l in range(L):
+        step_layer.retrieval(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l], p, scale, out_all[l])
+        cnt = step_layer.count.cpu().numpy()
+        u = 0
+        for b in range(B):
+            for g in range(G_r):
+                mark = torch.zeros(N, dtype=torch.bool, device=dev)
+                for h in range(g * cfg.G, min(H_r, (g + 1) * cfg.G)):
+                    mark[step_layer.idx[b, h, :int(cnt[b, h])].long()] = True
+                u += int(mark.sum().item())
+        union.append(u)
+        n_sel.append(cnt.reshape(-1).tolist())
+    torch.cuda.synchronize()
+    kr_bytes = B * G_r * N * cfg.r * 4
+    gather_bytes = np.array(union) * 2 * d * 2
+    window_bytes = B * local_kv * w_rows * 2 * d * 2
+    B_alg = float(L * kr_bytes + gather_bytes.sum() + L * window_bytes)
+    B_ns = float(sum(B * G_r * N * cfg.r * 2 + u * 2 * d * 2 + B * local_kv * w_rows * 2 * d * 2
+                     for u in union))
+    steps_per_s = 1e3 / ms_step
+    achieved_gbps = B_alg / (ms_step * 1e-3) / 1e9
+
+    # Dominant kernel: the indexer scan (one kernel per call).  Algorithmic
+    # bytes per launch: 64 B of k_r read + 4 B of score written per query
+    # head, per token and KV head.
+    scan_bytes = B * G_r * N * (cfg.r * 4 + cfg.G * 4)
+    scan_us = us["rtp_index_scores"]
+    roof = {"kernel": "index_scores_kernel<8>", "bound": "hbm",
+            "achieved": scan_bytes / (scan_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+
+    # ---------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, p, args.cpu_seconds)
+
+    tokens_scanned = B * G_r * N * L
+    rec = {
+        "metric": "sparse-decode steps/s at 128K-1M ctx; achieved HBM GB/s vs MI355X peak",
+        "value": round(steps_per_s, 3), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": L, "batch": B, "ctx_tokens": N,
+                   "q_heads": Hq, "kv_heads": Hkv, "retrieval_q_heads": H_r,
+                   "head_dim": d, "indexer_dim": cfg.r, "p": p, "sinks": cfg.n_sink,
+                   "window": cfg.window, "kv_dtype": "bf16", "graph": not args.no_graph},
+        "B_alg_bytes": B_alg, "B_ns_bytes": B_ns,
+        "achieved_GBps": round(achieved_gbps, 1),
+        "frac_of_hbm_peak": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+        "tokens_scanned_per_s": tokens_scanned * steps_per_s,
+        "selected_per_head_mean": float(np.mean(n_sel)),
+        "union_rows_per_layer_mean": float(np.mean(union)),
+        "per_call_us_per_layer": {k: round(v, 2) for k, v in us.items()},
+        "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(cfg, p, target_s):
+    """The CPU oracle on whole layers of the same workload (same generator,
+    same inputs): scores, full-sort top-p and fp64 attention for every
+    retrieval head, fp64 sink + window attention for every local head.
+    Only oracle calls are timed; input generation is not."""
+    import oracle
+    import synth
+    layers = 0
+    spent = 0.0
+    while spent < target_s and layers < cfg.L:
+        l = layers
+        q_r, k_r, q = synth.layer_qr(cfg, l), synth.layer_kr(cfg, l), synth.layer_q(cfg, l)
+        for b in range(cfg.B):
+            sets = []
+            t = time.perf_counter()
+            for h in range(cfg.H_r):
+                s = oracle.scores(q_r[b, h], k_r[b, min(h // cfg.G, cfg.G_r - 1)])
+                sets.append(oracle.topp(s, p).sel)
+            spent += time.perf_counter() - t
+            for h in range(cfg.Hq):
+                g = h // cfg.G
+                rows = np.sort(sets[h]) if h < cfg.H_r else oracle.local_rows(cfg.N, cfg.n_sink, cfg.window)
+                Kr = synth.kv_rows(cfg, l, "K", b, g, rows)
+                Vr = synth.kv_rows(cfg, l, "V", b, g, rows)
+                t = time.perf_counter()
+                oracle.attention(q[b, h], Kr, Vr, cfg.scale)
+                spent += time.perf_counter() - t
+        layers += 1
+        log(f"  cpu oracle: {layers} layer(s), {spent:.1f}s")
+    return {"value": round(layers / cfg.L / spent, 5), "unit": "steps/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{layers} of {cfg.L} layers of {cfg.name} (all 32 heads), "
+                      f"{spent:.1f}s single-threaded; value = layers/{cfg.L}/seconds"}
+
+
+if __name__ == "__main__":
+    main()

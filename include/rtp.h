@@ -1,0 +1,175 @@
+/*
+ * rtp.h -- C ABI of the RTPurbo sparse decode attention path on MI355X
+ * (gfx950), "Full Attention Strikes Back: Transferring Full Attention into
+ * Sparse within Hundred Training Steps" (arXiv 2605.16928).
+ *
+ * One decode step of one attention layer, per the pages' statement of the
+ * method (gist.science summary, method sections 1-3 and 5):
+ *   - retrieval heads score every cached token with a 16-dim low-rank
+ *     indexer taken before RoPE            -> rtp_index_scores
+ *   - keep the smallest set of tokens whose low-dim softmax mass reaches p,
+ *     found by a sort-free histogram threshold       -> rtp_topp_select
+ *   - exact attention over the selected K/V rows only -> rtp_sparse_decode
+ *   - local heads attend sink tokens plus a sliding window
+ *                                                     -> rtp_local_decode
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees, or keeps a pointer after the call.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream).  No call synchronises the host; results are ready when the
+ *     stream reaches them.  Calls are stateless and may be captured in a HIP
+ *     graph.  Calls that overlap on one device must use distinct workspaces.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     any error nothing is launched and no output is touched.  A failure
+ *     reported by the HIP runtime at launch returns RTP_ERR_HIP.
+ *   - Inputs must be finite; non-finite values give unspecified results.
+ *   - bf16 tensors are passed as their 16-bit patterns (rtp_bf16).
+ *   - Layouts are row-major.  "cap" is a cache's capacity in tokens (its
+ *     row count per head); only the first N rows of each head are read.
+ *   - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ */
+#ifndef RTP_H
+#define RTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t rtp_bf16; /* bfloat16 bit pattern */
+
+typedef enum rtp_status {
+    RTP_OK = 0,
+    RTP_ERR_NULL = 1,        /* a required pointer is NULL                  */
+    RTP_ERR_SHAPE = 2,       /* a size is out of range or inconsistent      */
+    RTP_ERR_UNSUPPORTED = 3, /* r != 16, d != 128, too many heads per group */
+    RTP_ERR_VALUE = 4,       /* p not in (0,1], bad window/sink, bad scale  */
+    RTP_ERR_ALIGN = 5,       /* a pointer or capacity breaks alignment      */
+    RTP_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required     */
+    RTP_ERR_HIP = 7          /* the HIP runtime reported an error           */
+} rtp_status;
+
+/* Workspace kinds for rtp_workspace_size. */
+enum {
+    RTP_WS_TOPP_SELECT = 1,
+    RTP_WS_SPARSE_DECODE = 2,
+    RTP_WS_LOCAL_DECODE = 3
+};
+
+/*
+ * rtp_index_scores -- indexer score of every cached token for each
+ * retrieval query head (gist.science summary, method section 2: a 16-dim
+ * projector applied to queries and keys before RoPE; arXiv abstract,
+ * "16-dimensional indexer").
+ *
+ *   scores[b][h][i] = q_r[b][h] . k_r[b][h / (Hq_r/Hkv_r)][i],  i < N,
+ * in fp32, accumulated as one fused multiply-add per dimension in the order
+ * j = 0..15 starting from +0, with a zero result stored as +0.  The result
+ * is bit-exact: no reassociation, no flush of denormals.
+ *
+ *   q_r     fp32 [B][Hq_r][r]          16-B aligned
+ *   k_r     fp32 [B][Hkv_r][kr_cap][r] 16-B aligned
+ *   scores  fp32 [B][Hq_r][N]          out, 4-B aligned
+ *   r must be 16; Hq_r must be a multiple of Hkv_r; 1 <= N <= kr_cap.
+ */
+rtp_status rtp_index_scores(const float *q_r, const float *k_r, float *scores,
+                            int32_t B, int32_t Hq_r, int32_t Hkv_r, int32_t N,
+                            int64_t kr_cap, int32_t r, void *stream);
+
+/*
+ * rtp_topp_select -- dynamic top-p token selection per head (gist.science
+ * summary, method section 3: accumulate low-dim attention mass until the
+ * cumulative threshold p is reached; section 5: a sort-free,
+ * histogram-based threshold).
+ *
+ * For each of the B*H score rows, with e_i = exp(s_i - max s) in fp64 and
+ * Z = sum of e_i over all N tokens: order tokens by score, descending, ties
+ * to the lower index; keep the shortest prefix whose mass is >= p*Z
+ * (p widened to fp64).  p == 1 keeps all N tokens.
+ *
+ *   scores     fp32  [B][H][N]   4-B aligned; -0 is treated as +0
+ *   p          in (0, 1]
+ *   idx        int32 [B][H][N]   out: the kept token indices of row (b,h)
+ *                                in idx[b][h][0 .. count[b][h]), in no
+ *                                particular order; the rest is untouched
+ *   count      int32 [B][H]      out: size of each kept set (>= 1)
+ *   workspace  device memory of at least
+ *              rtp_workspace_size(RTP_WS_TOPP_SELECT, B, H, N) bytes,
+ *              256-B aligned; contents need no initialisation.
+ */
+rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H,
+                           int32_t N, float p, int32_t *idx, int32_t *count,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * rtp_sparse_decode -- exact attention of each retrieval query head over
+ * its selected rows only (arXiv abstract: sparse attention over the
+ * indexer's tokens; gist.science summary, method section 5: bandwidth-
+ * optimised sparse decode).
+ *
+ *   out[b][h][:] = sum_{i in S} softmax_S(scale * q[b][h] . K[b][g][i])
+ *                  * V[b][g][i][:],  g = h / (Hq/Hkv),
+ * with S = idx[b][h - q_head_begin][0 .. count), fp32 arithmetic, softmax
+ * renormalised over S.
+ *
+ *   q          bf16  [B][Hq][d]          16-B aligned
+ *   K, V       bf16  [B][Hkv][kv_cap][d] 16-B aligned
+ *   idx        int32 [B][n_q_heads][N]   as written by rtp_topp_select;
+ *                                        every entry must be < N
+ *   count      int32 [B][n_q_heads]      each in [1, N]
+ *   heads      q_head_begin .. q_head_begin + n_q_heads - 1 (within Hq)
+ *   out        fp32  [B][Hq][d]          only the heads in range written
+ *   workspace  >= rtp_workspace_size(RTP_WS_SPARSE_DECODE, B, n_q_heads, N)
+ *   d must be 128; 1 <= N <= kv_cap; scale finite.
+ */
+rtp_status rtp_sparse_decode(const rtp_bf16 *q, const rtp_bf16 *K,
+                             const rtp_bf16 *V, const int32_t *idx,
+                             const int32_t *count, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,
+                             int32_t q_head_begin, int32_t n_q_heads,
+                             float scale, float *out, void *workspace,
+                             size_t ws_bytes, void *stream);
+
+/*
+ * rtp_local_decode -- local heads: attention over the first n_sink cached
+ * rows (attention sinks) plus the newest `window` rows, each row once
+ * (gist.science summary, method section 1: local heads use a sliding window
+ * with attention sinks).  The query is the newest token, whose K/V is row
+ * N-1.  Each K/V row is read once per KV head and serves all its query
+ * heads in range.
+ *
+ *   q, K, V, out, heads, d, scale as in rtp_sparse_decode
+ *   n_sink >= 0, window >= 1
+ *   workspace  >= rtp_workspace_size(RTP_WS_LOCAL_DECODE, B, n_q_heads, N)
+ */
+rtp_status rtp_local_decode(const rtp_bf16 *q, const rtp_bf16 *K,
+                            const rtp_bf16 *V, int32_t B, int32_t Hq,
+                            int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,
+                            int32_t q_head_begin, int32_t n_q_heads,
+                            int32_t n_sink, int32_t window, float scale,
+                            float *out, void *workspace, size_t ws_bytes,
+                            void *stream);
+
+/*
+ * rtp_workspace_size -- bytes of workspace a call needs (host only, pure).
+ *   which  RTP_WS_TOPP_SELECT:   H = score rows per batch row
+ *          RTP_WS_SPARSE_DECODE: H = n_q_heads
+ *          RTP_WS_LOCAL_DECODE:  H = n_q_heads (sized for any n_sink,
+ *                                window, since the row list is <= N)
+ * Returns RTP_ERR_VALUE for an unknown `which`, RTP_ERR_SHAPE for sizes < 1,
+ * RTP_ERR_NULL when bytes is NULL.
+ */
+rtp_status rtp_workspace_size(int32_t which, int32_t B, int32_t H, int32_t N,
+                              size_t *bytes);
+
+/* Static English text for a status code (host only). */
+const char *rtp_status_string(rtp_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RTP_H */

@@ -1,0 +1,161 @@
+"""Python binding of librtp (include/rtp.h): the RTPurbo sparse decode path
+on MI355X (arXiv 2605.16928).
+
+Argument marshalling only: each function checks dtypes and shapes of the
+torch tensors it is given, reads their device pointers and the current HIP
+stream, and calls the C function of the same name.  Every step of the path
+runs in the HIP kernels of librtp.so; there is no fallback.  If the library
+is not built, calls raise RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librtp.so")
+
+RTP_WS_TOPP_SELECT = 1
+RTP_WS_SPARSE_DECODE = 2
+RTP_WS_LOCAL_DECODE = 3
+
+STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPPORTED",
+          4: "RTP_ERR_VALUE", 5: "RTP_ERR_ALIGN", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
+
+# Every symbol include/rtp.h declares.
+SYMBOLS = ("rtp_index_scores", "rtp_topp_select", "rtp_sparse_decode",
+           "rtp_local_decode", "rtp_workspace_size", "rtp_status_string")
+
+
+class RtpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librtp.so with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                ctypes.c_float, ctypes.c_size_t)
+        L.rtp_index_scores.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, P]
+        L.rtp_topp_select.argtypes = [P, I32, I32, I32, F32, P, P, P, SZ, P]
+        L.rtp_sparse_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32,
+                                        I32, I32, F32, P, P, SZ, P]
+        L.rtp_local_decode.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, I32, I32,
+                                       I32, I32, F32, P, P, SZ, P]
+        L.rtp_workspace_size.argtypes = [I32, I32, I32, I32, ctypes.POINTER(SZ)]
+        L.rtp_status_string.argtypes = [I32]
+        L.rtp_status_string.restype = ctypes.c_char_p
+        for name in SYMBOLS[:5]:
+            getattr(L, name).restype = I32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().rtp_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise RtpError(status, where)
+
+
+def workspace_size(which: int, B: int, H: int, N: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().rtp_workspace_size(which, B, H, N, ctypes.byref(out)), "rtp_workspace_size")
+    return out.value
+
+
+# ------------------------------------------------------------ torch glue
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t, dtype, name, ndim):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _bf16(t, name, ndim):
+    import torch
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    return _dev(t, torch.int16, name, ndim)
+
+
+def rtp_index_scores(q_r, k_r, scores, stream=None) -> None:
+    """q_r f32 [B][Hq_r][16]; k_r f32 [B][Hkv_r][cap][16];
+    scores f32 [B][Hq_r][N] (out)."""
+    import torch
+    B, Hq_r, r = q_r.shape
+    _, Hkv_r, cap, _ = k_r.shape
+    N = scores.shape[-1]
+    _check(lib().rtp_index_scores(
+        _dev(q_r, torch.float32, "q_r", 3), _dev(k_r, torch.float32, "k_r", 4),
+        _dev(scores, torch.float32, "scores", 3), B, Hq_r, Hkv_r, N, cap, r,
+        _stream(q_r, stream)), "rtp_index_scores")
+
+
+def rtp_topp_select(scores, p, idx, count, workspace, stream=None) -> None:
+    """scores f32 [B][H][N]; idx i32 [B][H][N] (out); count i32 [B][H] (out);
+    workspace uint8 [>= workspace_size(RTP_WS_TOPP_SELECT, B, H, N)]."""
+    import torch
+    B, H, N = scores.shape
+    _check(lib().rtp_topp_select(
+        _dev(scores, torch.float32, "scores", 3), B, H, N, float(p),
+        _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2),
+        _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
+        _stream(scores, stream)), "rtp_topp_select")
+
+
+def rtp_sparse_decode(q, K, V, idx, count, q_head_begin, scale, out, workspace,
+                      N=None, stream=None) -> None:
+    """q bf16 [B][Hq][d]; K, V bf16 [B][Hkv][cap][d]; idx i32 [B][n_q][N];
+    count i32 [B][n_q]; out f32 [B][Hq][d] (heads in range written)."""
+    import torch
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    n_q = count.shape[1]
+    N = idx.shape[-1] if N is None else N
+    _check(lib().rtp_sparse_decode(
+        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4),
+        _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2),
+        B, Hq, Hkv, N, cap, d, q_head_begin, n_q, float(scale),
+        _dev(out, torch.float32, "out", 3), _dev(workspace, torch.uint8, "workspace", 1),
+        workspace.numel(), _stream(q, stream)), "rtp_sparse_decode")
+
+
+def rtp_local_decode(q, K, V, N, q_head_begin, n_q_heads, n_sink, window, scale, out,
+                     workspace, stream=None) -> None:
+    """Local heads [q_head_begin, q_head_begin + n_q_heads): sinks + window."""
+    import torch
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    _check(lib().rtp_local_decode(
+        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4), B, Hq, Hkv, N, cap, d,
+        q_head_begin, n_q_heads, n_sink, window, float(scale),
+        _dev(out, torch.float32, "out", 3), _dev(workspace, torch.uint8, "workspace", 1),
+        workspace.numel(), _stream(q, stream)), "rtp_local_decode")

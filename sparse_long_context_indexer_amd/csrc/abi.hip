@@ -1,0 +1,135 @@
+// C ABI (include/rtp.h): host-side validation, workspace sizing, dispatch.
+// Every argument is checked before anything is enqueued; no C++ exception
+// crosses the boundary.
+#include <math.h>
+#include <stdint.h>
+
+#include "rtp.h"
+#include "rtp_launch.h"
+
+namespace {
+
+constexpr int kMaxGridY = 65535;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+rtp_status from_hip(hipError_t e) { return e == hipSuccess ? RTP_OK : RTP_ERR_HIP; }
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+rtp_status check_attention_common(const void *q, const void *K, const void *V, const void *out,
+                                  const void *ws, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t N, int64_t kv_cap, int32_t d,
+                                  int32_t q_head_begin, int32_t n_q_heads, float scale)
+{
+    if (!q || !K || !V || !out || !ws) return RTP_ERR_NULL;
+    if (d != 128) return RTP_ERR_UNSUPPORTED;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N < 1 || kv_cap < N) return RTP_ERR_SHAPE;
+    if (q_head_begin < 0 || n_q_heads < 1 || (int64_t)q_head_begin + n_q_heads > Hq)
+        return RTP_ERR_SHAPE;
+    if (B > kMaxGridY || n_q_heads > kMaxGridY) return RTP_ERR_SHAPE;
+    if (!isfinite(scale)) return RTP_ERR_VALUE;
+    if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 4) ||
+        !aligned(ws, 256))
+        return RTP_ERR_ALIGN;
+    return RTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rtp_status_string(rtp_status s)
+{
+    switch (s) {
+    case RTP_OK: return "ok";
+    case RTP_ERR_NULL: return "a required pointer is NULL";
+    case RTP_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case RTP_ERR_UNSUPPORTED: return "unsupported dimension (r must be 16, d must be 128)";
+    case RTP_ERR_VALUE: return "a parameter value is out of range";
+    case RTP_ERR_ALIGN: return "a pointer breaks the required alignment";
+    case RTP_ERR_WORKSPACE: return "workspace missing or too small";
+    case RTP_ERR_HIP: return "the HIP runtime reported an error";
+    }
+    return "unknown status";
+}
+
+rtp_status rtp_workspace_size(int32_t which, int32_t B, int32_t H, int32_t N, size_t *bytes)
+{
+    if (!bytes) return RTP_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1) return RTP_ERR_SHAPE;
+    switch (which) {
+    case RTP_WS_TOPP_SELECT: *bytes = rtp::sel_layout((int64_t)B * H, N).total; return RTP_OK;
+    case RTP_WS_SPARSE_DECODE: *bytes = rtp::sparse_ws_bytes(B, H, N); return RTP_OK;
+    case RTP_WS_LOCAL_DECODE: *bytes = rtp::local_ws_bytes(B, H, N); return RTP_OK;
+    default: return RTP_ERR_VALUE;
+    }
+}
+
+rtp_status rtp_index_scores(const float *q_r, const float *k_r, float *scores, int32_t B,
+                            int32_t Hq_r, int32_t Hkv_r, int32_t N, int64_t kr_cap, int32_t r,
+                            void *stream)
+{
+    if (!q_r || !k_r || !scores) return RTP_ERR_NULL;
+    if (r != 16) return RTP_ERR_UNSUPPORTED;
+    if (B < 1 || Hq_r < 1 || Hkv_r < 1 || Hq_r % Hkv_r != 0 || N < 1 || kr_cap < N)
+        return RTP_ERR_SHAPE;
+    const int64_t group = Hq_r / Hkv_r;
+    if ((int64_t)B * Hkv_r * ((group + 7) / 8) > kMaxGridY) return RTP_ERR_SHAPE;
+    if (!aligned(q_r, 16) || !aligned(k_r, 16) || !aligned(scores, 4)) return RTP_ERR_ALIGN;
+    return from_hip(rtp::launch_index_scores(q_r, k_r, scores, B, Hq_r, Hkv_r, N, kr_cap,
+                                             as_stream(stream)));
+}
+
+rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H, int32_t N, float p,
+                           int32_t *idx, int32_t *count, void *workspace, size_t ws_bytes,
+                           void *stream)
+{
+    if (!scores || !idx || !count || !workspace) return RTP_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1 || (int64_t)B * H > kMaxGridY) return RTP_ERR_SHAPE;
+    if (!(p > 0.0f && p <= 1.0f)) return RTP_ERR_VALUE;  // NaN fails too
+    if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(count, 4) || !aligned(workspace, 256))
+        return RTP_ERR_ALIGN;
+    const int64_t R = (int64_t)B * H;
+    if (ws_bytes < rtp::sel_layout(R, N).total) return RTP_ERR_WORKSPACE;
+    return from_hip(rtp::launch_topp_select(scores, R, N, p, idx, count, workspace,
+                                            as_stream(stream)));
+}
+
+rtp_status rtp_sparse_decode(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,
+                             const int32_t *idx, const int32_t *count, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,
+                             int32_t q_head_begin, int32_t n_q_heads, float scale, float *out,
+                             void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!idx || !count) return RTP_ERR_NULL;
+    rtp_status st = check_attention_common(q, K, V, out, workspace, B, Hq, Hkv, N, kv_cap, d,
+                                           q_head_begin, n_q_heads, scale);
+    if (st != RTP_OK) return st;
+    if (!aligned(idx, 4) || !aligned(count, 4)) return RTP_ERR_ALIGN;
+    if (ws_bytes < rtp::sparse_ws_bytes(B, n_q_heads, N)) return RTP_ERR_WORKSPACE;
+    return from_hip(rtp::launch_sparse_decode(q, K, V, idx, count, B, Hq, Hkv, N, kv_cap,
+                                              q_head_begin, n_q_heads, scale, out, workspace,
+                                              as_stream(stream)));
+}
+
+rtp_status rtp_local_decode(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,
+                            int32_t q_head_begin, int32_t n_q_heads, int32_t n_sink,
+                            int32_t window, float scale, float *out, void *workspace,
+                            size_t ws_bytes, void *stream)
+{
+    rtp_status st = check_attention_common(q, K, V, out, workspace, B, Hq, Hkv, N, kv_cap, d,
+                                           q_head_begin, n_q_heads, scale);
+    if (st != RTP_OK) return st;
+    if (n_sink < 0 || window < 1) return RTP_ERR_VALUE;
+    const int64_t G = Hq / Hkv;
+    const int64_t groups = ((int64_t)q_head_begin + n_q_heads - 1) / G - q_head_begin / G + 1;
+    if (groups * ((G + 7) / 8) > kMaxGridY) return RTP_ERR_SHAPE;
+    if (ws_bytes < rtp::local_ws_bytes(B, n_q_heads, N)) return RTP_ERR_WORKSPACE;
+    return from_hip(rtp::launch_local_decode(q, K, V, B, Hq, Hkv, N, kv_cap, q_head_begin,
+                                             n_q_heads, n_sink, window, scale, out, workspace,
+                                             as_stream(stream)));
+}
+
+}  // extern "C"

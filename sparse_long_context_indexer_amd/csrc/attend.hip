@@ -1,0 +1,455 @@
+// Exact decode attention over (a) each retrieval head's selected rows and
+// (b) each local head's sinks plus sliding window (gist.science summary of
+// arXiv 2605.16928, method sections 1 and 5).
+//
+// Both are HBM-bound GEMV-shaped work on bf16 K/V rows of 256 B, so no
+// matrix cores: a row is spread over 16 lanes (16 B = 8 bf16 each), which
+// makes every row read two whole 128-B lines; a wave works on 4 rows at a
+// time and several rows are loaded before any is used, to keep enough
+// gathers in flight.  Split-K: each block owns a contiguous slice of the
+// row list and runs an online softmax over it (base-2 exponent, with
+// scale*log2(e) folded into q); partial (max, sum, o[128]) records are
+// merged across splits by combine_kernel.
+//
+// Local heads: the 8 query heads of a KV head share each row read.  Each lane
+// forms 8 partial dot products; a butterfly over the 16 lanes of a row
+// reduces all 8 in 8 exchanges (each step halves the heads a lane carries).
+#include <float.h>
+#include <math.h>
+
+#include "rtp_device.h"
+#include "rtp_launch.h"
+
+namespace rtp {
+
+constexpr int kAttThreads = 256;
+constexpr int kGroups = kAttThreads / 16;  // 16-lane row groups per block
+constexpr int kPart = 132;                 // floats per partial: m, l, pad, o[128]
+constexpr int kSparseU = 4;                // rows per group per iteration
+constexpr int kLocalU = 2;
+constexpr int kMaxSplits = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float sum16(float v)
+{
+    v += __shfl_xor(v, 1, 16);
+    v += __shfl_xor(v, 2, 16);
+    v += __shfl_xor(v, 4, 16);
+    v += __shfl_xor(v, 8, 16);
+    return v;
+}
+
+__device__ __forceinline__ float rescale(float m_old, float m_new)
+{
+    return m_old == -INFINITY ? 0.0f : exp2f(m_old - m_new);
+}
+
+// ------------------------------------------------------------ sparse
+
+int sparse_splits(int N)
+{
+    int s = (N + 255) / 256;
+    return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
+}
+
+size_t sparse_ws_bytes(int64_t B, int64_t n_q, int N)
+{
+    return align_up((size_t)(B * n_q * sparse_splits(N)) * kPart * sizeof(float), 256);
+}
+
+__global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ count, int N, int64_t kv_cap, int Hq, int Hkv,
+    int q_head_begin, int n_q, float qscale, int S, float *__restrict__ part)
+{
+    __shared__ float wm[kAttThreads / kWave], wl[kAttThreads / kWave];
+    __shared__ float wo[kAttThreads / kWave][128];
+    const int s = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
+    const int h = q_head_begin + hr;
+    const int g = h / (Hq / Hkv);
+    const int64_t prow = (int64_t)b * n_q + hr;
+    float *pr = part + (prow * S + s) * kPart;
+
+    int cnt = count[prow];
+    cnt = cnt < 0 ? 0 : (cnt > N ? N : cnt);
+    constexpr int kRowsPerIter = kGroups * kSparseU;
+    int chunk = (cnt + S - 1) / S;
+    chunk = chunk < kRowsPerIter ? kRowsPerIter : chunk;
+    chunk = (chunk + kRowsPerIter - 1) / kRowsPerIter * kRowsPerIter;
+    const int begin = s * chunk;
+    const int end = min(cnt, begin + chunk);
+    if (begin >= end) {
+        if (threadIdx.x < kPart) pr[threadIdx.x] = threadIdx.x == 0 ? -INFINITY : 0.0f;
+        return;
+    }
+
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int grp = lane >> 4, sub = lane & 15;
+    float qf[8];
+    {
+        const uint4 qw = *reinterpret_cast<const uint4 *>(q + ((int64_t)b * Hq + h) * 128 + sub * 8);
+        bf16x8_to_f32(qw, qf);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) qf[c] *= qscale;
+    }
+    const int64_t kvb = ((int64_t)b * Hkv + g) * kv_cap * 128 + sub * 8;
+    const uint16_t *Kb = K + kvb;
+    const uint16_t *Vb = V + kvb;
+    const int32_t *ir = idx + prow * (int64_t)N;
+
+    float m = -INFINITY, l = 0.0f, o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = 0.0f;
+
+    for (int base = begin; base < end; base += kRowsPerIter) {
+        uint4 kw[kSparseU], vw[kSparseU];
+        bool ok[kSparseU];
+#pragma unroll
+        for (int u = 0; u < kSparseU; ++u) {
+            const int j = base + u * kGroups + w * 4 + grp;
+            int t = j < end ? ir[j] : -1;
+            ok[u] = (unsigned)t < (unsigned)N;
+            const int64_t off = ok[u] ? (int64_t)t * 128 : 0;
+            kw[u] = *reinterpret_cast<const uint4 *>(Kb + off);
+            vw[u] = *reinterpret_cast<const uint4 *>(Vb + off);
+        }
+        float lg[kSparseU];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kSparseU; ++u) {
+            float kf[8];
+            bf16x8_to_f32(kw[u], kf);
+            float d = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) d = fmaf(qf[c], kf[c], d);
+            d = sum16(d);
+            lg[u] = ok[u] ? d : -INFINITY;
+            mx = fmaxf(mx, lg[u]);
+        }
+        const float mn = fmaxf(m, mx);
+        if (mn == -INFINITY) continue;
+        const float corr = rescale(m, mn);
+        l *= corr;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] *= corr;
+#pragma unroll
+        for (int u = 0; u < kSparseU; ++u) {
+            const float pw = ok[u] ? exp2f(lg[u] - mn) : 0.0f;
+            float vf[8];
+            bf16x8_to_f32(vw[u], vf);
+            l += pw;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) o[c] = fmaf(pw, vf[c], o[c]);
+        }
+        m = mn;
+    }
+
+    // Merge the 4 row groups of the wave, then the waves of the block.
+#pragma unroll
+    for (int off = 16; off < kWave; off <<= 1) {
+        const float mo = __shfl_xor(m, off);
+        const float lo = __shfl_xor(l, off);
+        const float mn = fmaxf(m, mo);
+        const float a = rescale(m, mn), bb = rescale(mo, mn);
+        l = l * a + lo * bb;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float oo = __shfl_xor(o[c], off);
+            o[c] = o[c] * a + oo * bb;
+        }
+        m = mn;
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) wo[w][sub * 8 + c] = o[c];
+        if (lane == 0) {
+            wm[w] = m;
+            wl[w] = l;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < 128) {
+        float M = -INFINITY;
+        for (int i = 0; i < kAttThreads / kWave; ++i) M = fmaxf(M, wm[i]);
+        float L = 0.0f, O = 0.0f;
+        for (int i = 0; i < kAttThreads / kWave; ++i) {
+            const float f = rescale(wm[i], M);
+            L += wl[i] * f;
+            O += wo[i][threadIdx.x] * f;
+        }
+        pr[4 + threadIdx.x] = O;
+        if (threadIdx.x == 0) {
+            pr[0] = M;
+            pr[1] = L;
+        }
+    }
+}
+
+// Merges the S split partials of each head into out[b][h][:].
+__global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ part, int S,
+                                                      int Hq, int q_head_begin, int n_q,
+                                                      float *__restrict__ out)
+{
+    const int hr = blockIdx.x, b = blockIdx.y;
+    const float *pr = part + ((int64_t)b * n_q + hr) * S * kPart;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, pr[s * kPart]);
+    float L = 0.0f, O = 0.0f;
+    for (int s = 0; s < S; ++s) {
+        const float ms = pr[s * kPart];
+        if (ms == -INFINITY) continue;
+        const float f = exp2f(ms - M);
+        L += pr[s * kPart + 1] * f;
+        O += pr[s * kPart + 4 + threadIdx.x] * f;
+    }
+    out[((int64_t)b * Hq + q_head_begin + hr) * 128 + threadIdx.x] = L > 0.0f ? O / L : 0.0f;
+}
+
+hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                                const int32_t *idx, const int32_t *count, int B, int Hq,
+                                int Hkv, int N, int64_t kv_cap, int q_head_begin,
+                                int n_q_heads, float scale, float *out, void *ws,
+                                hipStream_t stream)
+{
+    const int S = sparse_splits(N);
+    float *part = static_cast<float *>(ws);
+    hipLaunchKernelGGL(sparse_attn_kernel, dim3(S, n_q_heads, B), dim3(kAttThreads), 0,
+                       stream, q, K, V, idx, count, N, kv_cap, Hq, Hkv, q_head_begin,
+                       n_q_heads, scale * kLog2e, S, part);
+    hipLaunchKernelGGL(combine_kernel, dim3(n_q_heads, B), dim3(128), 0, stream, part, S,
+                       Hq, q_head_begin, n_q_heads, out);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------- local
+
+static int64_t local_rows_count(int N, int n_sink, int window)
+{
+    const int64_t w_start = N > window ? (int64_t)N - window : 0;
+    const int64_t sink_end = n_sink < w_start ? n_sink : w_start;
+    return sink_end + (N - w_start);
+}
+
+int local_splits(int64_t n_rows)
+{
+    int64_t s = (n_rows + 63) / 64;
+    return (int)(s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s));
+}
+
+size_t local_ws_bytes(int64_t B, int64_t n_q, int N)
+{
+    // The row list never exceeds N rows, so this bounds every n_sink/window.
+    return align_up((size_t)(B * n_q * local_splits(N)) * kPart * sizeof(float), 256);
+}
+
+// Block (s, y, b): KV head g = g_first + y / chunks_per_g, query heads
+// [h_lo, h_hi) of that head within the local range (at most 8), rows of
+// split s of the local row list.
+__global__ __launch_bounds__(kAttThreads) void local_attn_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, int N, int64_t kv_cap, int Hq, int Hkv,
+    int q_head_begin, int n_q, int n_sink, int window, float qscale, int S,
+    int chunks_per_g, float *__restrict__ part)
+{
+    __shared__ float wm[kAttThreads / kWave][8], wl[kAttThreads / kWave][8];
+    __shared__ float wo[kAttThreads / kWave][8][128];
+    const int G = Hq / Hkv;
+    const int s = blockIdx.x, b = blockIdx.z;
+    const int g = q_head_begin / G + (int)blockIdx.y / chunks_per_g;
+    const int ck = (int)blockIdx.y % chunks_per_g;
+    const int h_lo = max(q_head_begin, g * G + ck * 8);
+    const int h_hi = min(q_head_begin + n_q, min(g * G + G, g * G + ck * 8 + 8));
+    const int nh = h_hi - h_lo;
+    if (nh <= 0) return;
+
+    const int64_t w_start = N > window ? (int64_t)N - window : 0;
+    const int64_t sink_end = n_sink < w_start ? n_sink : w_start;
+    const int64_t n_rows = sink_end + (N - w_start);
+    constexpr int kRowsPerIter = kGroups * kLocalU;
+    int64_t chunk = (n_rows + S - 1) / S;
+    chunk = (chunk + kRowsPerIter - 1) / kRowsPerIter * kRowsPerIter;
+    const int64_t begin = (int64_t)s * chunk;
+    const int64_t end = min(n_rows, begin + chunk);
+
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int grp = lane >> 4, sub = lane & 15;
+
+    float qf[8][8];
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+        if (hh < nh) {
+            const uint4 qw = *reinterpret_cast<const uint4 *>(
+                q + ((int64_t)b * Hq + h_lo + hh) * 128 + sub * 8);
+            bf16x8_to_f32(qw, qf[hh]);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) qf[hh][c] *= qscale;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) qf[hh][c] = 0.0f;
+        }
+    }
+    const int64_t kvb = ((int64_t)b * Hkv + g) * kv_cap * 128 + sub * 8;
+    const uint16_t *Kb = K + kvb;
+    const uint16_t *Vb = V + kvb;
+
+    float m[8], l[8], o[8][8];
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+        m[hh] = -INFINITY;
+        l[hh] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[hh][c] = 0.0f;
+    }
+    const int b3 = (sub >> 3) & 1, b2 = (sub >> 2) & 1, b1 = (sub >> 1) & 1;
+
+    for (int64_t base = begin; base < end; base += kRowsPerIter) {
+        uint4 kw[kLocalU], vw[kLocalU];
+        bool ok[kLocalU];
+#pragma unroll
+        for (int u = 0; u < kLocalU; ++u) {
+            const int64_t j = base + u * kGroups + w * 4 + grp;
+            ok[u] = j < end;
+            const int64_t row = j < sink_end ? j : w_start + (j - sink_end);
+            const int64_t off = ok[u] ? row * 128 : 0;
+            kw[u] = *reinterpret_cast<const uint4 *>(Kb + off);
+            vw[u] = *reinterpret_cast<const uint4 *>(Vb + off);
+        }
+        float lg[kLocalU][8];
+#pragma unroll
+        for (int u = 0; u < kLocalU; ++u) {
+            float kf[8];
+            bf16x8_to_f32(kw[u], kf);
+            float d[8];
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh) {
+                float a = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) a = fmaf(qf[hh][c], kf[c], a);
+                d[hh] = a;
+            }
+            // Butterfly: after the steps over lane bits 3, 2, 1 a lane holds
+            // one head, 4*b3 + 2*b2 + b1, summed over 8 lanes; bit 0 finishes.
+            float d4[4], d2[2], d1;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float send = b3 ? d[k] : d[k + 4];
+                const float keep = b3 ? d[k + 4] : d[k];
+                d4[k] = keep + __shfl_xor(send, 8, 16);
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const float send = b2 ? d4[k] : d4[k + 2];
+                const float keep = b2 ? d4[k + 2] : d4[k];
+                d2[k] = keep + __shfl_xor(send, 4, 16);
+            }
+            {
+                const float send = b1 ? d2[0] : d2[1];
+                const float keep = b1 ? d2[1] : d2[0];
+                d1 = keep + __shfl_xor(send, 2, 16);
+            }
+            d1 += __shfl_xor(d1, 1, 16);
+            // Head hh's logit sits in lanes 2*hh and 2*hh + 1 of the group.
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh) {
+                const float v = __shfl(d1, 2 * hh, 16);
+                lg[u][hh] = ok[u] ? v : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            float mx = lg[0][hh];
+#pragma unroll
+            for (int u = 1; u < kLocalU; ++u) mx = fmaxf(mx, lg[u][hh]);
+            const float mn = fmaxf(m[hh], mx);
+            if (mn == -INFINITY) continue;
+            const float corr = rescale(m[hh], mn);
+            l[hh] *= corr;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) o[hh][c] *= corr;
+            m[hh] = mn;
+        }
+#pragma unroll
+        for (int u = 0; u < kLocalU; ++u) {
+            float vf[8];
+            bf16x8_to_f32(vw[u], vf);
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh) {
+                const float pw = ok[u] ? exp2f(lg[u][hh] - m[hh]) : 0.0f;
+                l[hh] += pw;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) o[hh][c] = fmaf(pw, vf[c], o[hh][c]);
+            }
+        }
+    }
+
+    // Merge the 4 row groups of the wave, then the waves of the block.
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+#pragma unroll
+        for (int off = 16; off < kWave; off <<= 1) {
+            const float mo = __shfl_xor(m[hh], off);
+            const float lo = __shfl_xor(l[hh], off);
+            const float mn = fmaxf(m[hh], mo);
+            const float a = rescale(m[hh], mn), bb = rescale(mo, mn);
+            l[hh] = l[hh] * a + lo * bb;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float oo = __shfl_xor(o[hh][c], off);
+                o[hh][c] = o[hh][c] * a + oo * bb;
+            }
+            m[hh] = mn;
+        }
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) wo[w][hh][sub * 8 + c] = o[hh][c];
+            if (lane == 0) {
+                wm[w][hh] = m[hh];
+                wl[w][hh] = l[hh];
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nh * 128; e += kAttThreads) {
+        const int hh = e / 128, c = e % 128;
+        float M = -INFINITY;
+        for (int i = 0; i < kAttThreads / kWave; ++i) M = fmaxf(M, wm[i][hh]);
+        float L = 0.0f, O = 0.0f;
+        for (int i = 0; i < kAttThreads / kWave; ++i) {
+            const float f = rescale(wm[i][hh], M);
+            L += wl[i][hh] * f;
+            O += wo[i][hh][c] * f;
+        }
+        float *pr = part + (((int64_t)b * n_q + (h_lo - q_head_begin + hh)) * S + s) * kPart;
+        pr[4 + c] = O;
+        if (c == 0) {
+            pr[0] = M;
+            pr[1] = L;
+        }
+    }
+}
+
+hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                               int B, int Hq, int Hkv, int N, int64_t kv_cap,
+                               int q_head_begin, int n_q_heads, int n_sink, int window,
+                               float scale, float *out, void *ws, hipStream_t stream)
+{
+    const int G = Hq / Hkv;
+    const int S = local_splits(local_rows_count(N, n_sink, window));
+    const int g_first = q_head_begin / G;
+    const int g_last = (q_head_begin + n_q_heads - 1) / G;
+    const int chunks_per_g = (G + 7) / 8;
+    const int ny = (g_last - g_first + 1) * chunks_per_g;
+    float *part = static_cast<float *>(ws);
+    hipLaunchKernelGGL(local_attn_kernel, dim3(S, ny, B), dim3(kAttThreads), 0, stream, q, K,
+                       V, N, kv_cap, Hq, Hkv, q_head_begin, n_q_heads, n_sink, window,
+                       scale * kLog2e, S, chunks_per_g, part);
+    hipLaunchKernelGGL(combine_kernel, dim3(n_q_heads, B), dim3(128), 0, stream, part, S, Hq,
+                       q_head_begin, n_q_heads, out);
+    return hipGetLastError();
+}
+
+}  // namespace rtp

@@ -1,0 +1,51 @@
+"""One decode step of one attention layer through the four C-ABI calls.
+
+Query heads [0, H_r) are retrieval heads (indexer scan, top-p select, sparse
+attention); heads [H_r, Hq) are local heads (sinks + sliding window), as in
+the head-role split of the gist.science summary of arXiv 2605.16928, method
+section 1.  Buffers that one layer uses and the next reuses (scores, kept
+indices, workspaces) are allocated once here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (RTP_WS_LOCAL_DECODE, RTP_WS_SPARSE_DECODE, RTP_WS_TOPP_SELECT,
+               rtp_index_scores, rtp_local_decode, rtp_sparse_decode, rtp_topp_select,
+               workspace_size)
+
+
+class DecodeLayer:
+    def __init__(self, B: int, Hq: int, Hkv: int, N: int, H_r: int, n_sink: int,
+                 window: int, device, d: int = 128):
+        self.B, self.Hq, self.Hkv, self.N, self.H_r = B, Hq, Hkv, N, H_r
+        self.n_sink, self.window, self.d = n_sink, window, d
+        self.H_l = Hq - H_r
+        dev = torch.device(device)
+        if H_r > 0:
+            self.scores = torch.empty((B, H_r, N), dtype=torch.float32, device=dev)
+            self.idx = torch.empty((B, H_r, N), dtype=torch.int32, device=dev)
+            self.count = torch.empty((B, H_r), dtype=torch.int32, device=dev)
+            self.ws_sel = torch.empty(workspace_size(RTP_WS_TOPP_SELECT, B, H_r, N),
+                                      dtype=torch.uint8, device=dev)
+            self.ws_sparse = torch.empty(workspace_size(RTP_WS_SPARSE_DECODE, B, H_r, N),
+                                         dtype=torch.uint8, device=dev)
+        if self.H_l > 0:
+            self.ws_local = torch.empty(workspace_size(RTP_WS_LOCAL_DECODE, B, self.H_l, N),
+                                        dtype=torch.uint8, device=dev)
+
+    def retrieval(self, q_r, k_r, q, K, V, p: float, scale: float, out, stream=None):
+        rtp_index_scores(q_r, k_r, self.scores, stream=stream)
+        rtp_topp_select(self.scores, p, self.idx, self.count, self.ws_sel, stream=stream)
+        rtp_sparse_decode(q, K, V, self.idx, self.count, 0, scale, out, self.ws_sparse,
+                          stream=stream)
+
+    def local(self, q, K, V, scale: float, out, stream=None):
+        rtp_local_decode(q, K, V, self.N, self.H_r, self.H_l, self.n_sink, self.window,
+                         scale, out, self.ws_local, stream=stream)
+
+    def __call__(self, q_r, k_r, q, K, V, p: float, scale: float, out, stream=None):
+        if self.H_r > 0:
+            self.retrieval(q_r, k_r, q, K, V, p, scale, out, stream)
+        if self.H_l > 0:
+            self.local(q, K, V, scale, out, stream)

@@ -1,0 +1,180 @@
+"""Shared helpers for the GPU parity tests: upload seeded inputs, run the
+HIP path, judge its results against the CPU oracle.
+
+Acceptance rules (one reading of each is fixed here):
+  scores  bit-exact.
+  sets    D = (GPU set) xor (oracle set); every token in D must have a score
+          within 1e-6 relative of the oracle's threshold score tau; the GPU
+          set's mass (computed by the oracle) must be >= p - 1e-5.
+  outputs the oracle's fp64 attention over the GPU's own set; pass when
+          max|o_gpu - o| <= 2e-3 and max|o_gpu - o| / max|o| <= 1e-2 per head.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+MAX_ABS = 2e-3
+MAX_REL = 1e-2
+SET_REL = 1e-6
+MASS_SLACK = 1e-5
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray, device=None) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device or dev())
+
+
+@dataclass
+class Layer:
+    """Host and device copies of one layer's inputs."""
+    cfg: synth.Config
+    layer: int
+    q_r: np.ndarray
+    k_r: np.ndarray
+    q: np.ndarray
+    K: np.ndarray = None
+    V: np.ndarray = None
+    d: dict = field(default_factory=dict)
+
+    def kv_rows(self, which, b, g, rows):
+        src = self.K if which == "K" else self.V
+        if src is not None:
+            return src[b, g, np.asarray(rows, dtype=np.int64)]
+        return synth.kv_rows(self.cfg, self.layer, which, b, g, rows)
+
+
+def load_layer(cfg: synth.Config, layer: int = 0, keep_host_kv: bool = True) -> Layer:
+    L = Layer(cfg, layer, synth.layer_qr(cfg, layer), synth.layer_kr(cfg, layer),
+              synth.layer_q(cfg, layer))
+    L.d["q_r"] = to_dev(L.q_r)
+    L.d["k_r"] = to_dev(L.k_r)
+    L.d["q"] = to_dev(L.q)
+    for which in ("K", "V"):
+        host = synth.layer_kv(cfg, layer, which)
+        L.d[which] = to_dev(host)
+        if keep_host_kv:
+            setattr(L, which, host)
+        del host
+    return L
+
+
+def oracle_scores(q_r_row: np.ndarray, k_r_head: np.ndarray) -> np.ndarray:
+    return oracle.scores(q_r_row, k_r_head)
+
+
+@dataclass
+class SetVerdict:
+    ok: bool
+    k_gpu: int
+    k_oracle: int
+    exempt: list          # (index, score, side) for tokens in the symmetric difference
+    bad: list             # tokens in the difference that are not exempt
+    mass: float
+    note: str = ""
+
+
+def judge_set(s: np.ndarray, p: float, gpu_set: np.ndarray) -> SetVerdict:
+    ref = oracle.topp(s, p)
+    g = np.asarray(gpu_set, dtype=np.int64)
+    gs, os_ = set(g.tolist()), set(ref.sel.tolist())
+    dup = len(gs) != len(g)
+    out_of_range = bool(len(g)) and (g.min() < 0 or g.max() >= len(s))
+    exempt, bad = [], []
+    tau = float(ref.tau)
+    for i in sorted(gs ^ os_):
+        side = "gpu" if i in gs else "oracle"
+        si = float(s[i])
+        if abs(si - tau) <= SET_REL * abs(tau) or si == tau:
+            exempt.append((i, si, side))
+        else:
+            bad.append((i, si, side))
+    mass = oracle.set_mass(s, g) if len(g) and not out_of_range else 0.0
+    pf = float(np.float32(p))
+    ok = not dup and not out_of_range and not bad and mass >= pf - MASS_SLACK
+    note = ("duplicates " if dup else "") + ("out-of-range " if out_of_range else "")
+    return SetVerdict(ok, len(g), ref.k, exempt, bad, mass, note)
+
+
+def judge_out(gpu: np.ndarray, ref: np.ndarray):
+    err = float(np.max(np.abs(gpu.astype(np.float64) - ref)))
+    scale = float(np.max(np.abs(ref)))
+    rel = err / scale if scale > 0 else err
+    return err <= MAX_ABS and rel <= MAX_REL, err, rel
+
+
+def run_layer(L: Layer, p: float, step=None):
+    """Runs the whole layer on the GPU; returns host copies of the results."""
+    from sparse_long_context_indexer_amd.runner import DecodeLayer
+    cfg = L.cfg
+    if step is None:
+        step = DecodeLayer(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.H_r, cfg.n_sink, cfg.window, dev())
+    out = torch.full((cfg.B, cfg.Hq, cfg.d), float("nan"), dtype=torch.float32, device=dev())
+    step(L.d["q_r"], L.d["k_r"], L.d["q"], L.d["K"], L.d["V"], p, cfg.scale, out)
+    torch.cuda.synchronize()
+    res = {"out": out.cpu().numpy()}
+    if cfg.H_r:
+        res["scores"] = step.scores.cpu().numpy()
+        cnt = step.count.cpu().numpy()
+        idx = step.idx.cpu().numpy()
+        res["count"] = cnt
+        res["sets"] = [[idx[b, h, :cnt[b, h]].copy() for h in range(cfg.H_r)]
+                       for b in range(cfg.B)]
+    return res
+
+
+def check_layer(L: Layer, p: float, res: dict, heads=None, report=None):
+    """Judges scores, sets and outputs of a layer; returns a list of failures."""
+    cfg = L.cfg
+    fails = []
+    rep = report if report is not None else {}
+    rep.setdefault("exempt", 0)
+    rep.setdefault("k", [])
+    for b in range(cfg.B):
+        for h in range(cfg.H_r):
+            if heads is not None and h not in heads:
+                continue
+            g = min(h // cfg.G, cfg.G_r - 1)
+            s_ref = oracle.scores(L.q_r[b, h], L.k_r[b, g])
+            s_gpu = res["scores"][b, h]
+            if not np.array_equal(s_gpu.view(np.uint32), s_ref.view(np.uint32)):
+                n = int(np.sum(s_gpu.view(np.uint32) != s_ref.view(np.uint32)))
+                fails.append(f"scores b={b} h={h}: {n} words differ")
+                continue
+            v = judge_set(s_ref, p, res["sets"][b][h])
+            rep["exempt"] += len(v.exempt)
+            rep["k"].append(v.k_gpu)
+            if not v.ok:
+                fails.append(f"set b={b} h={h} p={p}: k_gpu={v.k_gpu} k_oracle={v.k_oracle} "
+                             f"bad={v.bad[:5]} mass={v.mass} {v.note}")
+                continue
+            kv = h // cfg.G
+            rows = np.sort(res["sets"][b][h])
+            ref = oracle.attention(L.q[b, h], L.kv_rows("K", b, kv, rows),
+                                   L.kv_rows("V", b, kv, rows), cfg.scale)
+            ok, err, rel = judge_out(res["out"][b, h], ref)
+            if not ok:
+                fails.append(f"sparse out b={b} h={h}: abs={err:.3e} rel={rel:.3e}")
+        for h in range(cfg.H_r, cfg.Hq):
+            if heads is not None and h not in heads:
+                continue
+            kv = h // cfg.G
+            rows = oracle.local_rows(cfg.N, cfg.n_sink, cfg.window)
+            ref = oracle.attention(L.q[b, h], L.kv_rows("K", b, kv, rows),
+                                   L.kv_rows("V", b, kv, rows), cfg.scale)
+            ok, err, rel = judge_out(res["out"][b, h], ref)
+            if not ok:
+                fails.append(f"local out b={b} h={h}: abs={err:.3e} rel={rel:.3e}")
+    return fails

@@ -1,0 +1,134 @@
+"""The C-ABI library on the host: it loads, exports every symbol that
+include/rtp.h declares, sizes workspaces, and rejects bad arguments before
+launching anything (so these calls never reach a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_long_context_indexer_amd as rtp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rtp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rtp.LIB_PATH):
+        from sparse_long_context_indexer_amd import _build
+        _build.build()
+    return rtp.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:rtp_status|const char \*)\s*(rtp_\w+)\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 6
+    assert sorted(rtp.SYMBOLS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+    dyn = os.popen(f"nm -D --defined-only {rtp.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", dyn), n
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert rtp.status_string(code)
+    assert rtp.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    a = rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 1, 8, 1 << 20)
+    assert a >= 8 * (1 << 20) * 8          # candidate list capacity
+    assert a % 256 == 0
+    assert rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 1, 8, 4096) < a
+    for which in (rtp.RTP_WS_SPARSE_DECODE, rtp.RTP_WS_LOCAL_DECODE):
+        s = rtp.workspace_size(which, 2, 8, 65536)
+        assert s > 0 and s % 256 == 0
+    with pytest.raises(rtp.RtpError) as e:
+        rtp.workspace_size(9, 1, 1, 1)
+    assert e.value.status == 4
+    with pytest.raises(rtp.RtpError) as e:
+        rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 0, 1, 1)
+    assert e.value.status == 2
+    assert lib.rtp_workspace_size(1, 1, 1, 1, None) == 1
+
+
+# Fake device addresses: never dereferenced, since every call below fails
+# validation before anything is launched.
+A = 0x7f0000000000
+A4 = A + 4
+
+
+def test_index_scores_validation(lib):
+    f = lib.rtp_index_scores
+    assert f(None, A, A, 1, 8, 1, 100, 100, 16, None) == 1
+    assert f(A, A, A, 1, 8, 1, 100, 100, 8, None) == 3          # r != 16
+    assert f(A, A, A, 1, 8, 3, 100, 100, 16, None) == 2         # 8 % 3
+    assert f(A, A, A, 1, 8, 1, 0, 100, 16, None) == 2           # N < 1
+    assert f(A, A, A, 1, 8, 1, 101, 100, 16, None) == 2         # N > cap
+    assert f(A, A, A, 0, 8, 1, 100, 100, 16, None) == 2         # B < 1
+    assert f(A4, A, A, 1, 8, 1, 100, 100, 16, None) == 5        # q_r alignment
+    assert f(A, A4, A, 1, 8, 1, 100, 100, 16, None) == 5        # k_r alignment
+
+
+def test_topp_select_validation(lib):
+    f = lib.rtp_topp_select
+    ws = rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 1, 8, 1000)
+    assert f(None, 1, 8, 1000, 0.9, A, A, A, ws, None) == 1
+    assert f(A, 1, 8, 1000, 0.9, A, A, None, ws, None) == 1
+    for p in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        assert f(A, 1, 8, 1000, p, A, A, A, ws, None) == 4, p
+    assert f(A, 1, 8, 0, 0.9, A, A, A, ws, None) == 2
+    assert f(A, 1, 8, 1000, 0.9, A, A, A, ws - 1, None) == 6
+    assert f(A, 1, 8, 1000, 0.9, A, A, A + 16, ws, None) == 5   # workspace alignment
+    assert f(A + 2, 1, 8, 1000, 0.9, A, A, A, ws, None) == 5
+
+
+def test_sparse_decode_validation(lib):
+    f = lib.rtp_sparse_decode
+    ws = rtp.workspace_size(rtp.RTP_WS_SPARSE_DECODE, 1, 8, 1000)
+    args = [A, A, A, A, A, 1, 32, 4, 1000, 1000, 128, 0, 8, 0.088, A, A, ws, None]
+
+    def call(**kw):
+        a = list(args)
+        pos = {"q": 0, "idx": 3, "Hq": 6, "Hkv": 7, "N": 8, "cap": 9, "d": 10, "hb": 11,
+               "nq": 12, "scale": 13, "out": 14, "ws": 15, "wsb": 16}
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    assert call(q=None) == 1
+    assert call(idx=None) == 1
+    assert call(d=64) == 3
+    assert call(Hkv=5) == 2
+    assert call(cap=999) == 2
+    assert call(hb=30) == 2                     # 30 + 8 > 32
+    assert call(nq=0) == 2
+    assert call(scale=float("nan")) == 4
+    assert call(q=A + 8) == 5
+    assert call(wsb=ws - 1) == 6
+
+
+def test_local_decode_validation(lib):
+    f = lib.rtp_local_decode
+    ws = rtp.workspace_size(rtp.RTP_WS_LOCAL_DECODE, 1, 24, 1000)
+    base = [A, A, A, 1, 32, 4, 1000, 1000, 128, 8, 24, 4, 4096, 0.088, A, A, ws, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(0, None) == 1
+    assert call(8, 96) == 3
+    assert call(11, -1) == 4                    # n_sink < 0
+    assert call(12, 0) == 4                     # window < 1
+    assert call(16, ws - 256) == 6
+    assert call(15, A + 64) == 5
