@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--p", type=float, default=0.9)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-side-stream", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -98,9 +99,14 @@ def main():
     step_layer = DecodeLayer(B, Hq, Hkv, N, H_r, cfg.n_sink, cfg.window, dev)
     scale = cfg.scale
 
+    # Local heads of a layer run on a side stream, overlapping the retrieval
+    # chain of the same layer; each layer joins both before the next starts.
+    side = None if args.no_side_stream else torch.cuda.Stream(device=dev)
+
     def step():
         for l in range(L):
-            step_layer(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l], p, scale, out_all[l])
+            step_layer(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l], p, scale, out_all[l],
+                       side_stream=side)
 
     stream = torch.cuda.current_stream(dev)
     if args.no_graph:
@@ -214,7 +220,8 @@ def main():
         "config": {"workload": cfg.name, "layers": L, "batch": B, "ctx_tokens": N,
                    "q_heads": Hq, "kv_heads": Hkv, "retrieval_q_heads": H_r,
                    "head_dim": d, "indexer_dim": cfg.r, "p": p, "sinks": cfg.n_sink,
-                   "window": cfg.window, "kv_dtype": "bf16", "graph": not args.no_graph},
+                   "window": cfg.window, "kv_dtype": "bf16", "graph": not args.no_graph,
+                   "local_side_stream": side is not None},
         "B_alg_bytes": B_alg, "B_ns_bytes": B_ns,
         "achieved_GBps": round(achieved_gbps, 1),
         "frac_of_hbm_peak": round(achieved_gbps / HBM_PEAK_GBPS, 4),

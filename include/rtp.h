@@ -168,6 +168,10 @@ rtp_status rtp_workspace_size(int32_t which, int32_t B, int32_t H, int32_t N,
 /* Static English text for a status code (host only). */
 const char *rtp_status_string(rtp_status status);
 
+/* The hipError_t code behind the most recent RTP_ERR_HIP returned on the
+ * calling thread (0 = hipSuccess if there was none).  Host only. */
+int32_t rtp_last_hip_error(void);
+
 #ifdef __cplusplus
 }
 #endif

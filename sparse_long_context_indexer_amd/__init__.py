@@ -24,13 +24,17 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPP
 
 # Every symbol include/rtp.h declares.
 SYMBOLS = ("rtp_index_scores", "rtp_topp_select", "rtp_sparse_decode",
-           "rtp_local_decode", "rtp_workspace_size", "rtp_status_string")
+           "rtp_local_decode", "rtp_workspace_size", "rtp_status_string",
+           "rtp_last_hip_error")
 
 
 class RtpError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+        msg = f"{where}: {STATUS.get(status, status)} ({status_string(status)})"
+        if status == 7:
+            msg += f"; hipError_t {lib().rtp_last_hip_error()}"
+        super().__init__(msg)
 
 
 _lib = None
@@ -42,6 +46,10 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        # PyTorch ships its own HIP runtime (soname libamdhip64.so.7).  Loading
+        # torch first makes librtp bind to that copy; loading librtp first
+        # would map a second HIP runtime into the process.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                 ctypes.c_float, ctypes.c_size_t)
@@ -54,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.rtp_workspace_size.argtypes = [I32, I32, I32, I32, ctypes.POINTER(SZ)]
         L.rtp_status_string.argtypes = [I32]
         L.rtp_status_string.restype = ctypes.c_char_p
+        L.rtp_last_hip_error.argtypes = []
+        L.rtp_last_hip_error.restype = I32
         for name in SYMBOLS[:5]:
             getattr(L, name).restype = I32
         _lib = L

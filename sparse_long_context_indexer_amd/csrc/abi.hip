@@ -13,7 +13,14 @@ constexpr int kMaxGridY = 65535;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-rtp_status from_hip(hipError_t e) { return e == hipSuccess ? RTP_OK : RTP_ERR_HIP; }
+thread_local int32_t last_hip_error = 0;
+
+rtp_status from_hip(hipError_t e)
+{
+    if (e == hipSuccess) return RTP_OK;
+    last_hip_error = (int32_t)e;
+    return RTP_ERR_HIP;
+}
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
@@ -53,6 +60,8 @@ const char *rtp_status_string(rtp_status s)
     }
     return "unknown status";
 }
+
+int32_t rtp_last_hip_error(void) { return last_hip_error; }
 
 rtp_status rtp_workspace_size(int32_t which, int32_t B, int32_t H, int32_t N, size_t *bytes)
 {

@@ -27,7 +27,7 @@ constexpr int kGroups = kAttThreads / 16;  // 16-lane row groups per block
 constexpr int kPart = 132;                 // floats per partial: m, l, pad, o[128]
 constexpr int kSparseU = 4;                // rows per group per iteration
 constexpr int kLocalU = 2;
-constexpr int kMaxSplits = 128;
+constexpr int kMaxSplits = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float sum16(float v)
@@ -46,43 +46,101 @@ __device__ __forceinline__ float rescale(float m_old, float m_new)
 
 // ------------------------------------------------------------ sparse
 
-int sparse_splits(int N)
-{
-    int s = (N + 255) / 256;
-    return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
-}
+// Work split: the kept rows of all B*n_q heads are cut into chunks of one
+// common size, chosen on the device from the counts so that about
+// kSparseTarget blocks have work whatever the per-head budgets are; block j
+// takes chunk j of the concatenated per-head lists.  The grid is sized for
+// the worst case (kSparseTarget + heads); blocks past the last chunk exit.
+constexpr int kSparseTarget = 1024;
+
+int sparse_grid(int64_t R) { return (int)(kSparseTarget + R); }
 
 size_t sparse_ws_bytes(int64_t B, int64_t n_q, int N)
 {
-    return align_up((size_t)(B * n_q * sparse_splits(N)) * kPart * sizeof(float), 256);
+    (void)N;
+    return align_up((size_t)sparse_grid(B * n_q) * kPart * sizeof(float), 256);
+}
+
+struct SplitPlan {
+    int chunk;     // rows per split
+    int r;         // head row (b * n_q + hr) of this block's split, -1 if none
+    int first;     // index of the head row's first split
+    int splits;    // splits of that head row
+};
+
+__device__ __forceinline__ int clamp_count(int c, int N) { return c < 0 ? 0 : (c > N ? N : c); }
+
+// Every thread of the block must call this; all get the same plan.  Finds
+// either the split that global index j falls in (j >= 0) or, for j < 0,
+// the splits of head row `row`.
+template <int NT>
+__device__ SplitPlan plan_splits(const int32_t *count, int R, int N, int rows_per_iter, int j,
+                                 int row, int64_t *s64, int *s32)
+{
+    // Total kept rows.
+    int64_t tot = 0;
+    for (int r = threadIdx.x; r < R; r += NT) tot += clamp_count(count[r], N);
+    tot = wave_sum(tot);
+    if (lane_id() == 0) s64[threadIdx.x / kWave] = tot;
+    __syncthreads();
+    int64_t T = 0;
+    for (int w = 0; w < NT / kWave; ++w) T += s64[w];
+    int64_t chunk = (T + kSparseTarget - 1) / kSparseTarget;
+    if (chunk < rows_per_iter) chunk = rows_per_iter;
+    chunk = (chunk + rows_per_iter - 1) / rows_per_iter * rows_per_iter;
+    // Splits per head row over contiguous per-thread segments, then a scan.
+    const int per = (R + NT - 1) / NT;
+    const int r0 = threadIdx.x * per, r1 = min(R, r0 + per);
+    int seg = 0;
+    for (int r = r0; r < r1; ++r) seg += (int)((clamp_count(count[r], N) + chunk - 1) / chunk);
+    int total;
+    const int pre = block_exclusive_scan<NT>(seg, s32, &total);
+    SplitPlan P;
+    P.chunk = (int)chunk;
+    __shared__ int sh_r, sh_first, sh_splits;
+    if (threadIdx.x == 0) sh_r = -1;
+    __syncthreads();
+    int acc = pre;
+    for (int r = r0; r < r1; ++r) {
+        const int sp = (int)((clamp_count(count[r], N) + chunk - 1) / chunk);
+        const bool hit = j >= 0 ? (j >= acc && j < acc + sp) : (r == row);
+        if (hit) {
+            sh_r = r;
+            sh_first = acc;
+            sh_splits = sp;
+        }
+        acc += sp;
+    }
+    __syncthreads();
+    P.r = sh_r;
+    P.first = sh_r >= 0 ? sh_first : 0;
+    P.splits = sh_r >= 0 ? sh_splits : 0;
+    __syncthreads();
+    return P;
 }
 
 __global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ count, int N, int64_t kv_cap, int Hq, int Hkv,
-    int q_head_begin, int n_q, float qscale, int S, float *__restrict__ part)
+    int q_head_begin, int n_q, int R, float qscale, float *__restrict__ part)
 {
     __shared__ float wm[kAttThreads / kWave], wl[kAttThreads / kWave];
     __shared__ float wo[kAttThreads / kWave][128];
-    const int s = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
+    __shared__ int64_t s64[kAttThreads / kWave];
+    __shared__ int s32[kAttThreads / kWave + 1];
+    constexpr int kRowsPerIter = kGroups * kSparseU;
+    const int blk = blockIdx.x;
+    const SplitPlan plan = plan_splits<kAttThreads>(count, R, N, kRowsPerIter, blk, -1, s64, s32);
+    if (plan.r < 0) return;  // past the last split: no partial to write
+    const int prow = plan.r;
+    const int b = prow / n_q, hr = prow % n_q;
     const int h = q_head_begin + hr;
     const int g = h / (Hq / Hkv);
-    const int64_t prow = (int64_t)b * n_q + hr;
-    float *pr = part + (prow * S + s) * kPart;
-
-    int cnt = count[prow];
-    cnt = cnt < 0 ? 0 : (cnt > N ? N : cnt);
-    constexpr int kRowsPerIter = kGroups * kSparseU;
-    int chunk = (cnt + S - 1) / S;
-    chunk = chunk < kRowsPerIter ? kRowsPerIter : chunk;
-    chunk = (chunk + kRowsPerIter - 1) / kRowsPerIter * kRowsPerIter;
-    const int begin = s * chunk;
-    const int end = min(cnt, begin + chunk);
-    if (begin >= end) {
-        if (threadIdx.x < kPart) pr[threadIdx.x] = threadIdx.x == 0 ? -INFINITY : 0.0f;
-        return;
-    }
+    float *pr = part + (int64_t)blk * kPart;
+    const int cnt = clamp_count(count[prow], N);
+    const int begin = (blk - plan.first) * plan.chunk;
+    const int end = min(cnt, begin + plan.chunk);
 
     const int lane = lane_id(), w = threadIdx.x / kWave;
     const int grp = lane >> 4, sub = lane & 15;
@@ -96,7 +154,7 @@ __global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
     const int64_t kvb = ((int64_t)b * Hkv + g) * kv_cap * 128 + sub * 8;
     const uint16_t *Kb = K + kvb;
     const uint16_t *Vb = V + kvb;
-    const int32_t *ir = idx + prow * (int64_t)N;
+    const int32_t *ir = idx + (int64_t)prow * N;
 
     float m = -INFINITY, l = 0.0f, o[8];
 #pragma unroll
@@ -186,24 +244,86 @@ __global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
     }
 }
 
-// Merges the S split partials of each head into out[b][h][:].
-__global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ part, int S,
-                                                      int Hq, int q_head_begin, int n_q,
-                                                      float *__restrict__ out)
+// Merges n split partials (max, sum, o[128]) into one output row with a
+// block of kCombThreads: kCombGroups groups of 128 threads (one per output
+// dimension) take every kCombGroups-th partial, then the groups are summed.
+constexpr int kCombGroups = 8;
+constexpr int kCombThreads = kCombGroups * 128;
+constexpr int kCombCap = 4096;  // per-partial factors kept in LDS
+
+struct CombShared {
+    float f[kCombCap];
+    float o[kCombGroups][128];
+    float red[kCombThreads / kWave];
+};
+
+__device__ void merge_partials(const float *__restrict__ pr, int n, float *__restrict__ dst,
+                               CombShared &S)
 {
-    const int hr = blockIdx.x, b = blockIdx.y;
-    const float *pr = part + ((int64_t)b * n_q + hr) * S * kPart;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, pr[s * kPart]);
-    float L = 0.0f, O = 0.0f;
-    for (int s = 0; s < S; ++s) {
-        const float ms = pr[s * kPart];
-        if (ms == -INFINITY) continue;
-        const float f = exp2f(ms - M);
-        L += pr[s * kPart + 1] * f;
-        O += pr[s * kPart + 4 + threadIdx.x] * f;
+    constexpr int kNW = kCombThreads / kWave;
+    const int tid = threadIdx.x;
+    const int c = tid & 127, grp = tid >> 7;
+    float m = -INFINITY;
+    for (int k = tid; k < n; k += kCombThreads) m = fmaxf(m, pr[(int64_t)k * kPart]);
+    m = wave_max(m);
+    if (lane_id() == 0) S.red[tid / kWave] = m;
+    __syncthreads();
+    float M = S.red[0];
+    for (int i = 1; i < kNW; ++i) M = fmaxf(M, S.red[i]);
+    __syncthreads();
+    float l = 0.0f;
+    for (int k = tid; k < n; k += kCombThreads) {
+        const float f = rescale(pr[(int64_t)k * kPart], M);
+        if (k < kCombCap) S.f[k] = f;
+        l += pr[(int64_t)k * kPart + 1] * f;
     }
-    out[((int64_t)b * Hq + q_head_begin + hr) * 128 + threadIdx.x] = L > 0.0f ? O / L : 0.0f;
+    l = wave_sum(l);
+    if (lane_id() == 0) S.red[tid / kWave] = l;
+    __syncthreads();
+    float L = 0.0f;
+    for (int i = 0; i < kNW; ++i) L += S.red[i];
+    float o = 0.0f;
+#pragma unroll 4
+    for (int k = grp; k < n; k += kCombGroups) {
+        const float f = k < kCombCap ? S.f[k] : rescale(pr[(int64_t)k * kPart], M);
+        o = fmaf(pr[(int64_t)k * kPart + 4 + c], f, o);
+    }
+    S.o[grp][c] = o;
+    __syncthreads();
+    if (grp == 0) {
+        float t = 0.0f;
+#pragma unroll
+        for (int g = 0; g < kCombGroups; ++g) t += S.o[g][c];
+        dst[c] = L > 0.0f ? t / L : 0.0f;
+    }
+}
+
+// Sparse heads: head row r's partials are its splits in the balanced plan.
+__global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
+    const float *__restrict__ part, const int32_t *__restrict__ count, int N, int R, int Hq,
+    int q_head_begin, int n_q, float *__restrict__ out)
+{
+    __shared__ CombShared S;
+    __shared__ int64_t s64[kCombThreads / kWave];
+    __shared__ int s32[kCombThreads / kWave + 1];
+    const int r = blockIdx.x;
+    const SplitPlan plan =
+        plan_splits<kCombThreads>(count, R, N, kGroups * kSparseU, -1, r, s64, s32);
+    const int b = r / n_q, hr = r % n_q;
+    merge_partials(part + (int64_t)plan.first * kPart, plan.splits,
+                   out + ((int64_t)b * Hq + q_head_begin + hr) * 128, S);
+}
+
+// Local heads: S static splits per head row.
+__global__ __launch_bounds__(kCombThreads) void local_combine_kernel(
+    const float *__restrict__ part, int S_, int Hq, int q_head_begin, int n_q,
+    float *__restrict__ out)
+{
+    __shared__ CombShared S;
+    const int r = blockIdx.x;
+    const int b = r / n_q, hr = r % n_q;
+    merge_partials(part + (int64_t)r * S_ * kPart, S_,
+                   out + ((int64_t)b * Hq + q_head_begin + hr) * 128, S);
 }
 
 hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,
@@ -212,14 +332,13 @@ hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint
                                 int n_q_heads, float scale, float *out, void *ws,
                                 hipStream_t stream)
 {
-    const int S = sparse_splits(N);
+    const int R = B * n_q_heads;
     float *part = static_cast<float *>(ws);
-    hipLaunchKernelGGL(sparse_attn_kernel, dim3(S, n_q_heads, B), dim3(kAttThreads), 0,
-                       stream, q, K, V, idx, count, N, kv_cap, Hq, Hkv, q_head_begin,
-                       n_q_heads, scale * kLog2e, S, part);
-    hipLaunchKernelGGL(combine_kernel, dim3(n_q_heads, B), dim3(128), 0, stream, part, S,
-                       Hq, q_head_begin, n_q_heads, out);
-    return hipGetLastError();
+    RTP_TRY(launch(sparse_attn_kernel, dim3(sparse_grid(R)), dim3(kAttThreads), 0, stream, q,
+                   K, V, idx, count, N, kv_cap, Hq, Hkv, q_head_begin, n_q_heads, R,
+                   scale * kLog2e, part));
+    return launch(sparse_combine_kernel, dim3(R), dim3(kCombThreads), 0, stream, part, count, N,
+                  R, Hq, q_head_begin, n_q_heads, out);
 }
 
 // ------------------------------------------------------------- local
@@ -233,7 +352,7 @@ static int64_t local_rows_count(int N, int n_sink, int window)
 
 int local_splits(int64_t n_rows)
 {
-    int64_t s = (n_rows + 63) / 64;
+    int64_t s = (n_rows + kGroups * kLocalU - 1) / (kGroups * kLocalU);
     return (int)(s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s));
 }
 
@@ -444,12 +563,11 @@ hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K, const uint1
     const int chunks_per_g = (G + 7) / 8;
     const int ny = (g_last - g_first + 1) * chunks_per_g;
     float *part = static_cast<float *>(ws);
-    hipLaunchKernelGGL(local_attn_kernel, dim3(S, ny, B), dim3(kAttThreads), 0, stream, q, K,
-                       V, N, kv_cap, Hq, Hkv, q_head_begin, n_q_heads, n_sink, window,
-                       scale * kLog2e, S, chunks_per_g, part);
-    hipLaunchKernelGGL(combine_kernel, dim3(n_q_heads, B), dim3(128), 0, stream, part, S, Hq,
-                       q_head_begin, n_q_heads, out);
-    return hipGetLastError();
+    RTP_TRY(launch(local_attn_kernel, dim3(S, ny, B), dim3(kAttThreads), 0, stream, q, K, V, N,
+                   kv_cap, Hq, Hkv, q_head_begin, n_q_heads, n_sink, window, scale * kLog2e,
+                   S, chunks_per_g, part));
+    return launch(local_combine_kernel, dim3(B * n_q_heads), dim3(kCombThreads), 0, stream, part,
+                  S, Hq, q_head_begin, n_q_heads, out);
 }
 
 }  // namespace rtp

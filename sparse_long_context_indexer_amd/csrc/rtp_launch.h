@@ -17,10 +17,9 @@ hipError_t launch_index_scores(const float *q_r, const float *k_r, float *scores
 struct SelLayout {
     int64_t nblk;     // score chunks per row
     size_t rows;      // per-row state
-    size_t mass1;     // level-1 histogram mass, fp64
-    size_t cnt1;      // level-1 histogram count, u32
-    size_t zero_end;  // [rows, zero_end) is cleared at the start of a call
-    size_t pmax;      // per-chunk maxima
+    size_t hist2;     // per-row level-2 histogram
+    size_t hdr;       // per-chunk max and list length
+    size_t lists;     // per-chunk lists of non-empty level-1 bins
     size_t cand;      // boundary-bin candidates (key, index)
     size_t total;
 };
@@ -30,7 +29,6 @@ hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p,
                               hipStream_t stream);
 
 // ---- attention (attend.hip)
-int sparse_splits(int N);
 size_t sparse_ws_bytes(int64_t B, int64_t n_q, int N);
 hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K,
                                 const uint16_t *V, const int32_t *idx,
@@ -48,5 +46,30 @@ hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K,
                                void *ws, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+template <typename... KArgs>
+hipError_t launch_impl(const void *k, dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                       KArgs... args)
+{
+    void *ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1] = {static_cast<void *>(&args)...};
+    return hipLaunchKernel(k, grid, block, ptrs, shmem, stream);
+}
+
+// Launches kernel k and returns the status of this launch alone
+// (hipGetLastError would also report errors left by unrelated HIP calls).
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*k)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                  Args... args)
+{
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    return launch_impl<KArgs...>(reinterpret_cast<const void *>(k), grid, block, shmem, stream,
+                                 static_cast<KArgs>(args)...);
+}
+
+#define RTP_TRY(expr)                          \
+    do {                                       \
+        hipError_t rtp_e_ = (expr);            \
+        if (rtp_e_ != hipSuccess) return rtp_e_; \
+    } while (0)
 
 }  // namespace rtp

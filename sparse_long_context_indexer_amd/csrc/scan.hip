@@ -81,14 +81,13 @@ hipError_t launch_index_scores(const float *q_r, const float *k_r, float *scores
     auto go = [&](auto kern, int G) {
         const int chunks = (group + G - 1) / G;
         dim3 grid(gx, B * Hkv_r * chunks);
-        hipLaunchKernelGGL(kern, grid, dim3(kScanThreads), 0, stream, q_r, k_r,
-                           scores, N, kr_cap, Hq_r, Hkv_r, group, chunks);
+        return launch(kern, grid, dim3(kScanThreads), 0, stream, q_r, k_r, scores, N, kr_cap,
+                      Hq_r, Hkv_r, group, chunks);
     };
-    if (group == 1) go(index_scores_kernel<1>, 1);
-    else if (group == 2) go(index_scores_kernel<2>, 2);
-    else if (group <= 4) go(index_scores_kernel<4>, 4);
-    else go(index_scores_kernel<8>, 8);
-    return hipGetLastError();
+    if (group == 1) return go(index_scores_kernel<1>, 1);
+    if (group == 2) return go(index_scores_kernel<2>, 2);
+    if (group <= 4) return go(index_scores_kernel<4>, 4);
+    return go(index_scores_kernel<8>, 8);
 }
 
 }  // namespace rtp

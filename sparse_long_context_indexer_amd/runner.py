@@ -44,8 +44,19 @@ class DecodeLayer:
         rtp_local_decode(q, K, V, self.N, self.H_r, self.H_l, self.n_sink, self.window,
                          scale, out, self.ws_local, stream=stream)
 
-    def __call__(self, q_r, k_r, q, K, V, p: float, scale: float, out, stream=None):
+    def __call__(self, q_r, k_r, q, K, V, p: float, scale: float, out, side_stream=None):
+        """Runs the layer on the current stream.  With side_stream, the local
+        heads run there concurrently with the retrieval chain (the two share
+        no buffer); the current stream waits for them before returning."""
+        if side_stream is not None and self.H_r > 0 and self.H_l > 0:
+            main = torch.cuda.current_stream(out.device)
+            side_stream.wait_stream(main)
+            with torch.cuda.stream(side_stream):
+                self.local(q, K, V, scale, out)
+            self.retrieval(q_r, k_r, q, K, V, p, scale, out)
+            main.wait_stream(side_stream)
+            return
         if self.H_r > 0:
-            self.retrieval(q_r, k_r, q, K, V, p, scale, out, stream)
+            self.retrieval(q_r, k_r, q, K, V, p, scale, out)
         if self.H_l > 0:
-            self.local(q, K, V, scale, out, stream)
+            self.local(q, K, V, scale, out)

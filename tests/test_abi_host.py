@@ -23,12 +23,12 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:rtp_status|const char \*)\s*(rtp_\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:rtp_status|const char \*|int32_t)\s*(rtp_\w+)\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 6
+    assert len(names) == 7
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -41,6 +41,7 @@ def test_status_strings(lib):
     for code in range(8):
         assert rtp.status_string(code)
     assert rtp.status_string(99) == "unknown status"
+    assert lib.rtp_last_hip_error() == 0
 
 
 def test_workspace_sizes(lib):
@@ -132,3 +133,11 @@ def test_local_decode_validation(lib):
     assert call(12, 0) == 4                     # window < 1
     assert call(16, ws - 256) == 6
     assert call(15, A + 64) == 5
+
+
+def test_one_hip_runtime_in_process(lib):
+    # librtp must bind to the HIP runtime torch already loaded, not map a
+    # second copy (two runtimes in one process report no device).
+    maps = open("/proc/self/maps").read()
+    hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(hip) == 1, hip
