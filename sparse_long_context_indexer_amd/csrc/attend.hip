@@ -27,7 +27,8 @@ constexpr int kGroups = kAttThreads / 16;  // 16-lane row groups per block
 constexpr int kPart = 132;                 // floats per partial: m, l, pad, o[128]
 constexpr int kSparseU = 4;                // rows per group per iteration
 constexpr int kLocalU = 2;
-constexpr int kMaxSplits = 256;
+constexpr int kLocalRows = 128;      // rows per local split (at least)
+constexpr int kMaxLocalSplits = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float sum16(float v)
@@ -51,14 +52,40 @@ __device__ __forceinline__ float rescale(float m_old, float m_new)
 // kSparseTarget blocks have work whatever the per-head budgets are; block j
 // takes chunk j of the concatenated per-head lists.  The grid is sized for
 // the worst case (kSparseTarget + heads); blocks past the last chunk exit.
-constexpr int kSparseTarget = 1024;
+constexpr int kSparseTarget = 768;
+constexpr int kSlice = 64;  // partials merged per block in the first merge level
 
 int sparse_grid(int64_t R) { return (int)(kSparseTarget + R); }
+int sparse_slices(int64_t R) { return (sparse_grid(R) + kSlice - 1) / kSlice; }
+
+struct SparseWs {
+    float *part;      // one partial per attention block
+    float *super;     // [R][slices] first-level merges
+    uint32_t *ctr;    // [R] slices merged so far
+};
+
+static size_t sparse_ws_layout(int64_t R, SparseWs *W, void *base)
+{
+    size_t off = 0;
+    const size_t part = off;
+    off += align_up((size_t)sparse_grid(R) * kPart * sizeof(float), 256);
+    const size_t sup = off;
+    off += align_up((size_t)R * sparse_slices(R) * kPart * sizeof(float), 256);
+    const size_t ctr = off;
+    off += align_up((size_t)R * sizeof(uint32_t), 256);
+    if (W) {
+        char *b = static_cast<char *>(base);
+        W->part = reinterpret_cast<float *>(b + part);
+        W->super = reinterpret_cast<float *>(b + sup);
+        W->ctr = reinterpret_cast<uint32_t *>(b + ctr);
+    }
+    return off;
+}
 
 size_t sparse_ws_bytes(int64_t B, int64_t n_q, int N)
 {
     (void)N;
-    return align_up((size_t)sparse_grid(B * n_q) * kPart * sizeof(float), 256);
+    return sparse_ws_layout(B * n_q, nullptr, nullptr);
 }
 
 struct SplitPlan {
@@ -123,7 +150,8 @@ __global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ count, int N, int64_t kv_cap, int Hq, int Hkv,
-    int q_head_begin, int n_q, int R, float qscale, float *__restrict__ part)
+    int q_head_begin, int n_q, int R, float qscale, float *__restrict__ part,
+    uint32_t *__restrict__ ctr)
 {
     __shared__ float wm[kAttThreads / kWave], wl[kAttThreads / kWave];
     __shared__ float wo[kAttThreads / kWave][128];
@@ -131,6 +159,8 @@ __global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
     __shared__ int s32[kAttThreads / kWave + 1];
     constexpr int kRowsPerIter = kGroups * kSparseU;
     const int blk = blockIdx.x;
+    if (blk == 0)  // the merge that follows counts slices from zero
+        for (int i = threadIdx.x; i < R; i += kAttThreads) ctr[i] = 0u;
     const SplitPlan plan = plan_splits<kAttThreads>(count, R, N, kRowsPerIter, blk, -1, s64, s32);
     if (plan.r < 0) return;  // past the last split: no partial to write
     const int prow = plan.r;
@@ -244,21 +274,22 @@ __global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
     }
 }
 
-// Merges n split partials (max, sum, o[128]) into one output row with a
-// block of kCombThreads: kCombGroups groups of 128 threads (one per output
-// dimension) take every kCombGroups-th partial, then the groups are summed.
-constexpr int kCombGroups = 8;
+// Merges n partials (max, sum, o[128]) with a block of kCombThreads:
+// kCombGroups groups of 128 threads (one per dimension) take every
+// kCombGroups-th partial, then the groups are summed.  Writes either a
+// merged partial (dst_part) or the normalised output row (dst_out).
+constexpr int kCombGroups = 4;
 constexpr int kCombThreads = kCombGroups * 128;
-constexpr int kCombCap = 4096;  // per-partial factors kept in LDS
 
 struct CombShared {
-    float f[kCombCap];
+    float f[kSlice > 128 ? kSlice : 128];
     float o[kCombGroups][128];
     float red[kCombThreads / kWave];
+    int last;
 };
 
-__device__ void merge_partials(const float *__restrict__ pr, int n, float *__restrict__ dst,
-                               CombShared &S)
+__device__ void merge_partials(const float *__restrict__ pr, int n, float *dst_part,
+                               float *dst_out, CombShared &S)
 {
     constexpr int kNW = kCombThreads / kWave;
     const int tid = threadIdx.x;
@@ -274,7 +305,7 @@ __device__ void merge_partials(const float *__restrict__ pr, int n, float *__res
     float l = 0.0f;
     for (int k = tid; k < n; k += kCombThreads) {
         const float f = rescale(pr[(int64_t)k * kPart], M);
-        if (k < kCombCap) S.f[k] = f;
+        S.f[k] = f;
         l += pr[(int64_t)k * kPart + 1] * f;
     }
     l = wave_sum(l);
@@ -283,38 +314,62 @@ __device__ void merge_partials(const float *__restrict__ pr, int n, float *__res
     float L = 0.0f;
     for (int i = 0; i < kNW; ++i) L += S.red[i];
     float o = 0.0f;
-#pragma unroll 4
-    for (int k = grp; k < n; k += kCombGroups) {
-        const float f = k < kCombCap ? S.f[k] : rescale(pr[(int64_t)k * kPart], M);
-        o = fmaf(pr[(int64_t)k * kPart + 4 + c], f, o);
-    }
+#pragma unroll 16
+    for (int k = grp; k < n; k += kCombGroups) o = fmaf(pr[(int64_t)k * kPart + 4 + c], S.f[k], o);
     S.o[grp][c] = o;
     __syncthreads();
     if (grp == 0) {
         float t = 0.0f;
 #pragma unroll
         for (int g = 0; g < kCombGroups; ++g) t += S.o[g][c];
-        dst[c] = L > 0.0f ? t / L : 0.0f;
+        if (dst_out) dst_out[c] = L > 0.0f ? t / L : 0.0f;
+        if (dst_part) {
+            dst_part[4 + c] = t;
+            if (c == 0) {
+                dst_part[0] = M;
+                dst_part[1] = L;
+            }
+        }
     }
+    __syncthreads();
 }
 
-// Sparse heads: head row r's partials are its splits in the balanced plan.
+// Sparse heads, block (q, r): merges slice q (up to kSlice partials) of head
+// row r's splits; the block that completes the row's last slice merges the
+// slices into the output.
 __global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
-    const float *__restrict__ part, const int32_t *__restrict__ count, int N, int R, int Hq,
-    int q_head_begin, int n_q, float *__restrict__ out)
+    const float *__restrict__ part, float *__restrict__ super, uint32_t *__restrict__ ctr,
+    const int32_t *__restrict__ count, int N, int R, int Hq, int q_head_begin, int n_q,
+    int max_slices, float *__restrict__ out)
 {
     __shared__ CombShared S;
     __shared__ int64_t s64[kCombThreads / kWave];
     __shared__ int s32[kCombThreads / kWave + 1];
-    const int r = blockIdx.x;
+    const int q = blockIdx.x, r = blockIdx.y;
     const SplitPlan plan =
         plan_splits<kCombThreads>(count, R, N, kGroups * kSparseU, -1, r, s64, s32);
     const int b = r / n_q, hr = r % n_q;
-    merge_partials(part + (int64_t)plan.first * kPart, plan.splits,
-                   out + ((int64_t)b * Hq + q_head_begin + hr) * 128, S);
+    float *dst = out + ((int64_t)b * Hq + q_head_begin + hr) * 128;
+    const int slices = (plan.splits + kSlice - 1) / kSlice;
+    if (slices == 0) {  // an empty row: nothing was kept
+        if (q == 0 && threadIdx.x < 128) dst[threadIdx.x] = 0.0f;
+        return;
+    }
+    if (q >= slices) return;
+    float *sp = super + ((int64_t)r * max_slices) * kPart;
+    const int k0 = q * kSlice;
+    merge_partials(part + (int64_t)(plan.first + k0) * kPart, min(kSlice, plan.splits - k0),
+                   sp + (int64_t)q * kPart, nullptr, S);
+    // Publish this slice, then count it; the last one merges them all.
+    __threadfence();
+    if (threadIdx.x == 0) S.last = atomicAdd(&ctr[r], 1u) == (uint32_t)(slices - 1);
+    __syncthreads();
+    if (!S.last) return;
+    __threadfence();
+    merge_partials(sp, slices, nullptr, dst, S);
 }
 
-// Local heads: S static splits per head row.
+// Local heads: S static splits per head row (S <= 128).
 __global__ __launch_bounds__(kCombThreads) void local_combine_kernel(
     const float *__restrict__ part, int S_, int Hq, int q_head_begin, int n_q,
     float *__restrict__ out)
@@ -322,7 +377,7 @@ __global__ __launch_bounds__(kCombThreads) void local_combine_kernel(
     __shared__ CombShared S;
     const int r = blockIdx.x;
     const int b = r / n_q, hr = r % n_q;
-    merge_partials(part + (int64_t)r * S_ * kPart, S_,
+    merge_partials(part + (int64_t)r * S_ * kPart, S_, nullptr,
                    out + ((int64_t)b * Hq + q_head_begin + hr) * 128, S);
 }
 
@@ -333,12 +388,14 @@ hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint
                                 hipStream_t stream)
 {
     const int R = B * n_q_heads;
-    float *part = static_cast<float *>(ws);
+    SparseWs W;
+    sparse_ws_layout(R, &W, ws);
     RTP_TRY(launch(sparse_attn_kernel, dim3(sparse_grid(R)), dim3(kAttThreads), 0, stream, q,
                    K, V, idx, count, N, kv_cap, Hq, Hkv, q_head_begin, n_q_heads, R,
-                   scale * kLog2e, part));
-    return launch(sparse_combine_kernel, dim3(R), dim3(kCombThreads), 0, stream, part, count, N,
-                  R, Hq, q_head_begin, n_q_heads, out);
+                   scale * kLog2e, W.part, W.ctr));
+    const int slices = sparse_slices(R);
+    return launch(sparse_combine_kernel, dim3(slices, R), dim3(kCombThreads), 0, stream, W.part,
+                  W.super, W.ctr, count, N, R, Hq, q_head_begin, n_q_heads, slices, out);
 }
 
 // ------------------------------------------------------------- local
@@ -352,8 +409,8 @@ static int64_t local_rows_count(int N, int n_sink, int window)
 
 int local_splits(int64_t n_rows)
 {
-    int64_t s = (n_rows + kGroups * kLocalU - 1) / (kGroups * kLocalU);
-    return (int)(s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s));
+    int64_t s = (n_rows + kLocalRows - 1) / kLocalRows;
+    return (int)(s < 1 ? 1 : (s > kMaxLocalSplits ? kMaxLocalSplits : s));
 }
 
 size_t local_ws_bytes(int64_t B, int64_t n_q, int N)

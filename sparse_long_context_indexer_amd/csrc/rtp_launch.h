@@ -17,9 +17,9 @@ hipError_t launch_index_scores(const float *q_r, const float *k_r, float *scores
 struct SelLayout {
     int64_t nblk;     // score chunks per row
     size_t rows;      // per-row state
-    size_t hist2;     // per-row level-2 histogram
-    size_t hdr;       // per-chunk max and list length
-    size_t lists;     // per-chunk lists of non-empty level-1 bins
+    size_t hist1;     // per-row level-1 histogram
+    size_t zero_end;  // [rows, zero_end) is cleared at the start of a call
+    size_t tops;      // per-chunk top-bin records
     size_t cand;      // boundary-bin candidates (key, index)
     size_t total;
 };

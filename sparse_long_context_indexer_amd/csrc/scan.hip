@@ -15,7 +15,7 @@
 namespace rtp {
 
 constexpr int kScanThreads = 256;
-constexpr int kScanTPT = 4;                          // tokens per thread
+constexpr int kScanTPT = 2;                          // tokens per thread
 constexpr int kScanTile = kScanThreads * kScanTPT;   // tokens per block
 
 template <int G>
