@@ -8,7 +8,7 @@
 // 64-bit composite key (order-preserving score key, then token index):
 //
 //   zero    clears the level-1 histograms and the per-row state
-//   hist    one block per 8192-score chunk: per level-1 bin (score key bits
+//   hist    one block per 32768-score chunk: per level-1 bin (score key bits
 //           [31:20]) the fp64 mass exp(s - top(bin)), top(bin)
 //           being the bin's largest representable score, merged into the
 //           row's histogram with global atomics; the chunk's own top bin is
@@ -36,7 +36,7 @@
 
 namespace rtp {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;
 constexpr int kSelPerThread = 32;
 constexpr int kSelChunk = kSelThreads * kSelPerThread;  // scores per block
 constexpr int kBins1 = 4096;
@@ -52,8 +52,8 @@ struct SelRow {
     double T;        // p * Z
     float M;         // row max
     uint32_t j1;     // level-1 boundary bin
-    uint32_t n_cand; // candidates appended by emit
-    uint32_t pad[7];
+    uint64_t slots;  // emit's slot counters: kept (high 32 bits), candidates (low)
+    uint32_t pad[6];
 };
 static_assert(sizeof(SelRow) == 64, "SelRow is one 64-B record");
 
@@ -209,8 +209,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
 
 // --------------------------------------------------------------- pick
 
-__global__ __launch_bounds__(kPickThreads) void sel_pick_kernel(SelPtrs P, float p,
-                                                                int32_t *__restrict__ count)
+__global__ __launch_bounds__(kPickThreads) void sel_pick_kernel(SelPtrs P, float p)
 {
     constexpr int kPer = kBins1 / kPickThreads;  // bins per thread
     constexpr int kNW = kPickThreads / kWave;
@@ -297,18 +296,17 @@ __global__ __launch_bounds__(kPickThreads) void sel_pick_kernel(SelPtrs P, float
         P.rows[r].Z = Z;
         P.rows[r].T = T;
         P.rows[r].M = Mf;
-        count[r] = 0;
     }
 }
 
 // --------------------------------------------------------------- emit
 
 __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
-    const float *__restrict__ scores, int N, SelPtrs P, int32_t *__restrict__ idx,
-    int32_t *__restrict__ count)
+    const float *__restrict__ scores, int N, SelPtrs P, int32_t *__restrict__ idx)
 {
-    __shared__ uint32_t scan[kSelThreads / kWave + 1];
-    __shared__ uint32_t base[2];
+    __shared__ unsigned long long wbase[kSelThreads / kWave];
+    __shared__ unsigned long long bcount;
+    __shared__ unsigned long long gbase;
     const int64_t r = blockIdx.y;
     const uint32_t j1 = P.rows[r].j1;
     const float *sr = scores + r * (int64_t)N;
@@ -316,25 +314,35 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     uint2 *cr = P.cand + r * (int64_t)N;
     float v[kSelPerThread];
     const ChunkView cv = load_chunk(sr, N, (int64_t)blockIdx.x * kSelChunk, v);
-    // One slot reservation per block and list.
-    uint32_t na = 0, nc = 0;
+    if (threadIdx.x == 0) bcount = 0ull;
+    // Per lane: kept count (high half) and candidate count (low half).
+    uint32_t mine = 0;
 #pragma unroll
     for (int t = 0; t < kSelPerThread; ++t) {
         const uint32_t bin = score_key(v[t]) >> 20;
         const bool valid = cv.index(t) < N;
-        na += (valid && bin > j1) ? 1u : 0u;
-        nc += (valid && bin == j1) ? 1u : 0u;
+        mine += (valid && bin > j1) ? 0x10000u : 0u;
+        mine += (valid && bin == j1) ? 1u : 0u;
     }
-    uint32_t ta, tc;
-    uint32_t oa = block_exclusive_scan<kSelThreads>(na, scan, &ta);
-    uint32_t oc = block_exclusive_scan<kSelThreads>(nc, scan, &tc);
-    if (threadIdx.x == 0) {
-        base[0] = ta ? atomicAdd(reinterpret_cast<uint32_t *>(count + r), ta) : 0u;
-        base[1] = tc ? atomicAdd(&P.rows[r].n_cand, tc) : 0u;
-    }
+    // Wave prefix (a wave holds at most 2048 of each, so halves never
+    // carry), then one LDS atomic per wave for its block offset and one
+    // global atomic per block for its row offset.
+    const uint32_t inc = wave_inclusive_scan(mine);
+    const uint32_t wtot = __shfl(inc, kWave - 1);
     __syncthreads();
-    oa += base[0];
-    oc += base[1];
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0)
+        wbase[w] = atomicAdd(&bcount, ((unsigned long long)(wtot >> 16) << 32) | (wtot & 0xFFFFu));
+    __syncthreads();
+    if (threadIdx.x == 0)
+        gbase = bcount ? atomicAdd(reinterpret_cast<unsigned long long *>(&P.rows[r].slots),
+                                   bcount)
+                       : 0ull;
+    __syncthreads();
+    const unsigned long long base = gbase + wbase[w];
+    const uint32_t ex = inc - mine;
+    uint32_t oa = (uint32_t)(base >> 32) + (ex >> 16);
+    uint32_t oc = (uint32_t)base + (ex & 0xFFFFu);
 #pragma unroll
     for (int t = 0; t < kSelPerThread; ++t) {
         const uint32_t key = score_key(v[t]);
@@ -499,10 +507,10 @@ __global__ __launch_bounds__(kResThreads) void sel_resolve_kernel(
     const double M = (double)row.M;
     const double T = row.T;
     double A = row.A;
-    int64_t n = row.n_cand;
+    int64_t n = (uint32_t)row.slots;
     uint2 *gc = P.cand + r * (int64_t)N;
     const int tid = threadIdx.x;
-    const uint32_t emitted = (uint32_t)count[r];  // written by emit
+    const uint32_t emitted = (uint32_t)(row.slots >> 32);  // kept by emit
     int32_t *ir = idx + r * (int64_t)N + emitted;
     const bool in_lds = n <= kResCap;
     int cur = 0;  // LDS buffer holding the candidates
@@ -620,10 +628,8 @@ hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p, in
     dim3 grid((unsigned)P.nblk, (unsigned)R);
     RTP_TRY(launch(sel_zero_kernel, dim3(kZeroBlocks), dim3(256), 0, stream, P));
     RTP_TRY(launch(sel_hist_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P));
-    RTP_TRY(launch(sel_pick_kernel, dim3((unsigned)R), dim3(kPickThreads), 0, stream, P, p,
-                   count));
-    RTP_TRY(launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, idx,
-                   count));
+    RTP_TRY(launch(sel_pick_kernel, dim3((unsigned)R), dim3(kPickThreads), 0, stream, P, p));
+    RTP_TRY(launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, idx));
     return launch(sel_resolve_kernel, dim3((unsigned)R), dim3(kResThreads), 0, stream, N, P,
                   idx, count);
 }
