@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+
 #include "rtp.h"
 #include "rtp_launch.h"
 

@@ -8,8 +8,9 @@
 // time and several rows are loaded before any is used, to keep enough
 // gathers in flight.  Split-K: each block owns a contiguous slice of the
 // row list and runs an online softmax over it (base-2 exponent, with
-// scale*log2(e) folded into q); partial (max, sum, o[128]) records are
-// merged across splits by combine_kernel.
+// scale*log2(e) folded into q); its partial (max, sum, o[128]) record is
+// merged inside the same kernel: the last block to finish a group of
+// splits merges the group, and the last group merger writes the output.
 //
 // Local heads: the 8 query heads of a KV head share each row read.  Each lane
 // forms 8 partial dot products; a butterfly over the 16 lanes of a row
@@ -26,8 +27,8 @@ constexpr int kAttThreads = 256;
 constexpr int kGroups = kAttThreads / 16;  // 16-lane row groups per block
 constexpr int kPart = 132;                 // floats per partial: m, l, pad, o[128]
 constexpr int kSparseU = 4;                // rows per group per iteration
-constexpr int kLocalU = 2;
-constexpr int kLocalRows = 128;      // rows per local split (at least)
+constexpr int kLocalU = 4;
+constexpr int kLocalRows = 64;       // rows per local split (at least)
 constexpr int kMaxLocalSplits = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -53,15 +54,16 @@ __device__ __forceinline__ float rescale(float m_old, float m_new)
 // takes chunk j of the concatenated per-head lists.  The grid is sized for
 // the worst case (kSparseTarget + heads); blocks past the last chunk exit.
 constexpr int kSparseTarget = 768;
-constexpr int kSlice = 64;  // partials merged per block in the first merge level
+constexpr int kSlice = 32;  // split partials merged per block in the first merge level
+constexpr int kMaxSlices = (kSparseTarget + 1 + kSlice - 1) / kSlice;
 
 int sparse_grid(int64_t R) { return (int)(kSparseTarget + R); }
-int sparse_slices(int64_t R) { return (sparse_grid(R) + kSlice - 1) / kSlice; }
 
 struct SparseWs {
-    float *part;      // one partial per attention block
-    float *super;     // [R][slices] first-level merges
-    uint32_t *ctr;    // [R] slices merged so far
+    float *part;                    // one partial per attention block
+    float *super;                   // [R][kMaxSlices] slice merges
+    unsigned long long *slice_ctr;  // [R][kMaxSlices] arrivals per slice
+    unsigned long long *head_ctr;   // [R] slices merged per head row
 };
 
 static size_t sparse_ws_layout(int64_t R, SparseWs *W, void *base)
@@ -70,14 +72,17 @@ static size_t sparse_ws_layout(int64_t R, SparseWs *W, void *base)
     const size_t part = off;
     off += align_up((size_t)sparse_grid(R) * kPart * sizeof(float), 256);
     const size_t sup = off;
-    off += align_up((size_t)R * sparse_slices(R) * kPart * sizeof(float), 256);
-    const size_t ctr = off;
-    off += align_up((size_t)R * sizeof(uint32_t), 256);
+    off += align_up((size_t)R * kMaxSlices * kPart * sizeof(float), 256);
+    const size_t sc = off;
+    off += align_up((size_t)R * kMaxSlices * sizeof(unsigned long long), 256);
+    const size_t hc = off;
+    off += align_up((size_t)R * sizeof(unsigned long long), 256);
     if (W) {
         char *b = static_cast<char *>(base);
         W->part = reinterpret_cast<float *>(b + part);
         W->super = reinterpret_cast<float *>(b + sup);
-        W->ctr = reinterpret_cast<uint32_t *>(b + ctr);
+        W->slice_ctr = reinterpret_cast<unsigned long long *>(b + sc);
+        W->head_ctr = reinterpret_cast<unsigned long long *>(b + hc);
     }
     return off;
 }
@@ -97,77 +102,135 @@ struct SplitPlan {
 
 __device__ __forceinline__ int clamp_count(int c, int N) { return c < 0 ? 0 : (c > N ? N : c); }
 
-// Every thread of the block must call this; all get the same plan.  Finds
-// either the split that global index j falls in (j >= 0) or, for j < 0,
-// the splits of head row `row`.
-template <int NT>
+// Every thread of the block must call this; all get the same plan.  Wave 0
+// computes it (one pass over the counts, 64 head rows at a time) and
+// publishes it through LDS, so the block pays one barrier.  Finds either the
+// split that global index j falls in (j >= 0) or, for j < 0, the splits of
+// head row `row`.
 __device__ SplitPlan plan_splits(const int32_t *count, int R, int N, int rows_per_iter, int j,
-                                 int row, int64_t *s64, int *s32)
+                                 int row, SplitPlan *sh)
 {
-    // Total kept rows.
-    int64_t tot = 0;
-    for (int r = threadIdx.x; r < R; r += NT) tot += clamp_count(count[r], N);
-    tot = wave_sum(tot);
-    if (lane_id() == 0) s64[threadIdx.x / kWave] = tot;
-    __syncthreads();
-    int64_t T = 0;
-    for (int w = 0; w < NT / kWave; ++w) T += s64[w];
-    int64_t chunk = (T + kSparseTarget - 1) / kSparseTarget;
-    if (chunk < rows_per_iter) chunk = rows_per_iter;
-    chunk = (chunk + rows_per_iter - 1) / rows_per_iter * rows_per_iter;
-    // Splits per head row over contiguous per-thread segments, then a scan.
-    const int per = (R + NT - 1) / NT;
-    const int r0 = threadIdx.x * per, r1 = min(R, r0 + per);
-    int seg = 0;
-    for (int r = r0; r < r1; ++r) seg += (int)((clamp_count(count[r], N) + chunk - 1) / chunk);
-    int total;
-    const int pre = block_exclusive_scan<NT>(seg, s32, &total);
-    SplitPlan P;
-    P.chunk = (int)chunk;
-    __shared__ int sh_r, sh_first, sh_splits;
-    if (threadIdx.x == 0) sh_r = -1;
-    __syncthreads();
-    int acc = pre;
-    for (int r = r0; r < r1; ++r) {
-        const int sp = (int)((clamp_count(count[r], N) + chunk - 1) / chunk);
-        const bool hit = j >= 0 ? (j >= acc && j < acc + sp) : (r == row);
-        if (hit) {
-            sh_r = r;
-            sh_first = acc;
-            sh_splits = sp;
+    if (threadIdx.x < kWave) {
+        const int lane = lane_id();
+        int64_t tot = 0;
+        for (int r = lane; r < R; r += kWave) tot += clamp_count(count[r], N);
+        const int64_t T = wave_sum(tot);
+        int64_t chunk = (T + kSparseTarget - 1) / kSparseTarget;
+        if (chunk < rows_per_iter) chunk = rows_per_iter;
+        chunk = (chunk + rows_per_iter - 1) / rows_per_iter * rows_per_iter;
+        int base = 0, hit_r = -1, hit_first = 0, hit_splits = 0;
+        for (int r0 = 0; r0 < R; r0 += kWave) {
+            const int r = r0 + lane;
+            const int sp = r < R ? (int)((clamp_count(count[r], N) + chunk - 1) / chunk) : 0;
+            const int inc = wave_inclusive_scan(sp);
+            const int first = base + inc - sp;
+            const bool hit = r < R && (j >= 0 ? (j >= first && j < first + sp) : r == row);
+            const uint64_t hm = __ballot(hit);
+            if (hm && hit_r < 0) {
+                const int src = __ffsll((unsigned long long)hm) - 1;
+                hit_r = __shfl(r, src);
+                hit_first = __shfl(first, src);
+                hit_splits = __shfl(sp, src);
+            }
+            base += __shfl(inc, kWave - 1);
         }
-        acc += sp;
+        if (lane == 0) {
+            sh->chunk = (int)chunk;
+            sh->r = hit_r;
+            sh->first = hit_first;
+            sh->splits = hit_splits;
+        }
     }
     __syncthreads();
-    P.r = sh_r;
-    P.first = sh_r >= 0 ? sh_first : 0;
-    P.splits = sh_r >= 0 ? sh_splits : 0;
+    return *sh;
+}
+
+// Counts this block on `ctr` once its agent-scope stores have completed,
+// and tells whether it was the last of `expected` blocks; the last one then
+// reads the others' results with agent-scope loads.
+__device__ bool arrive_last(unsigned long long *ctr, int expected, int *flag)
+{
+    wait_vmem();
     __syncthreads();
-    return P;
+    if (threadIdx.x == 0) {
+        *flag = ctr_arrive(ctr) == (uint32_t)(expected - 1);
+        if (*flag) ctr_reset(ctr);
+    }
+    __syncthreads();
+    return *flag != 0;
+}
+
+// Merges n <= kSlice partials (max, sum, o[128]) with a block of
+// kAttThreads (two groups of 128 threads, one per output dimension, take
+// alternate partials).  Writes a merged partial (dst_part) or the
+// normalised output row (dst_out).
+struct MergeShared {
+    float f[kSlice];
+    float o[kAttThreads / 128][128];
+    float M, L;
+};
+
+__device__ void merge_partials(const float *pr, int n, float *dst_part, float *dst_out,
+                               MergeShared &S)
+{
+    constexpr int kG = kAttThreads / 128;
+    const int tid = threadIdx.x;
+    const int c = tid & 127, grp = tid >> 7;
+    if (tid < kWave) {
+        // wave 0: the merged max, the factors and the merged sum
+        const float m = tid < n ? ld_agent(pr + (int64_t)tid * kPart) : -INFINITY;
+        const float M = wave_max(m);
+        const float f = tid < n ? rescale(m, M) : 0.0f;
+        const float l = wave_sum(tid < n ? ld_agent(pr + (int64_t)tid * kPart + 1) * f : 0.0f);
+        if (tid < n) S.f[tid] = f;
+        if (tid == 0) {
+            S.M = M;
+            S.L = l;
+        }
+    }
+    __syncthreads();
+    float o = 0.0f;
+#pragma unroll 16
+    for (int k = grp; k < n; k += kG) o = fmaf(ld_agent(pr + (int64_t)k * kPart + 4 + c), S.f[k], o);
+    S.o[grp][c] = o;
+    __syncthreads();
+    if (grp == 0) {
+        float t = 0.0f;
+#pragma unroll
+        for (int g = 0; g < kG; ++g) t += S.o[g][c];
+        if (dst_out) dst_out[c] = S.L > 0.0f ? t / S.L : 0.0f;
+        if (dst_part) {
+            st_agent(dst_part + 4 + c, t);
+            if (c == 0) {
+                st_agent(dst_part, S.M);
+                st_agent(dst_part + 1, S.L);
+            }
+        }
+    }
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ count, int N, int64_t kv_cap, int Hq, int Hkv,
-    int q_head_begin, int n_q, int R, float qscale, float *__restrict__ part,
-    uint32_t *__restrict__ ctr)
+    int q_head_begin, int n_q, int R, float qscale, SparseWs W,
+    float *__restrict__ out)
 {
     __shared__ float wm[kAttThreads / kWave], wl[kAttThreads / kWave];
     __shared__ float wo[kAttThreads / kWave][128];
-    __shared__ int64_t s64[kAttThreads / kWave];
-    __shared__ int s32[kAttThreads / kWave + 1];
+    __shared__ SplitPlan sh_plan;
     constexpr int kRowsPerIter = kGroups * kSparseU;
+    __shared__ MergeShared MS;
+    __shared__ int last;
     const int blk = blockIdx.x;
-    if (blk == 0)  // the merge that follows counts slices from zero
-        for (int i = threadIdx.x; i < R; i += kAttThreads) ctr[i] = 0u;
-    const SplitPlan plan = plan_splits<kAttThreads>(count, R, N, kRowsPerIter, blk, -1, s64, s32);
+    const SplitPlan plan = plan_splits(count, R, N, kRowsPerIter, blk, -1, &sh_plan);
     if (plan.r < 0) return;  // past the last split: no partial to write
     const int prow = plan.r;
     const int b = prow / n_q, hr = prow % n_q;
     const int h = q_head_begin + hr;
     const int g = h / (Hq / Hkv);
-    float *pr = part + (int64_t)blk * kPart;
+    float *pr = W.part + (int64_t)blk * kPart;
     const int cnt = clamp_count(count[prow], N);
     const int begin = (blk - plan.first) * plan.chunk;
     const int end = min(cnt, begin + plan.chunk);
@@ -266,119 +329,31 @@ __global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
             L += wl[i] * f;
             O += wo[i][threadIdx.x] * f;
         }
-        pr[4 + threadIdx.x] = O;
+        st_agent(pr + 4 + threadIdx.x, O);
         if (threadIdx.x == 0) {
-            pr[0] = M;
-            pr[1] = L;
+            st_agent(pr, M);
+            st_agent(pr + 1, L);
         }
     }
-}
 
-// Merges n partials (max, sum, o[128]) with a block of kCombThreads:
-// kCombGroups groups of 128 threads (one per dimension) take every
-// kCombGroups-th partial, then the groups are summed.  Writes either a
-// merged partial (dst_part) or the normalised output row (dst_out).
-constexpr int kCombGroups = 4;
-constexpr int kCombThreads = kCombGroups * 128;
-
-struct CombShared {
-    float f[kSlice > 128 ? kSlice : 128];
-    float o[kCombGroups][128];
-    float red[kCombThreads / kWave];
-    int last;
-};
-
-__device__ void merge_partials(const float *__restrict__ pr, int n, float *dst_part,
-                               float *dst_out, CombShared &S)
-{
-    constexpr int kNW = kCombThreads / kWave;
-    const int tid = threadIdx.x;
-    const int c = tid & 127, grp = tid >> 7;
-    float m = -INFINITY;
-    for (int k = tid; k < n; k += kCombThreads) m = fmaxf(m, pr[(int64_t)k * kPart]);
-    m = wave_max(m);
-    if (lane_id() == 0) S.red[tid / kWave] = m;
-    __syncthreads();
-    float M = S.red[0];
-    for (int i = 1; i < kNW; ++i) M = fmaxf(M, S.red[i]);
-    __syncthreads();
-    float l = 0.0f;
-    for (int k = tid; k < n; k += kCombThreads) {
-        const float f = rescale(pr[(int64_t)k * kPart], M);
-        S.f[k] = f;
-        l += pr[(int64_t)k * kPart + 1] * f;
-    }
-    l = wave_sum(l);
-    if (lane_id() == 0) S.red[tid / kWave] = l;
-    __syncthreads();
-    float L = 0.0f;
-    for (int i = 0; i < kNW; ++i) L += S.red[i];
-    float o = 0.0f;
-#pragma unroll 16
-    for (int k = grp; k < n; k += kCombGroups) o = fmaf(pr[(int64_t)k * kPart + 4 + c], S.f[k], o);
-    S.o[grp][c] = o;
-    __syncthreads();
-    if (grp == 0) {
-        float t = 0.0f;
-#pragma unroll
-        for (int g = 0; g < kCombGroups; ++g) t += S.o[g][c];
-        if (dst_out) dst_out[c] = L > 0.0f ? t / L : 0.0f;
-        if (dst_part) {
-            dst_part[4 + c] = t;
-            if (c == 0) {
-                dst_part[0] = M;
-                dst_part[1] = L;
-            }
-        }
-    }
-    __syncthreads();
-}
-
-// Sparse heads, block (q, r): merges slice q (up to kSlice partials) of head
-// row r's splits; the block that completes the row's last slice merges the
-// slices into the output.
-__global__ __launch_bounds__(kCombThreads) void sparse_combine_kernel(
-    const float *__restrict__ part, float *__restrict__ super, uint32_t *__restrict__ ctr,
-    const int32_t *__restrict__ count, int N, int R, int Hq, int q_head_begin, int n_q,
-    int max_slices, float *__restrict__ out)
-{
-    __shared__ CombShared S;
-    __shared__ int64_t s64[kCombThreads / kWave];
-    __shared__ int s32[kCombThreads / kWave + 1];
-    const int q = blockIdx.x, r = blockIdx.y;
-    const SplitPlan plan =
-        plan_splits<kCombThreads>(count, R, N, kGroups * kSparseU, -1, r, s64, s32);
-    const int b = r / n_q, hr = r % n_q;
-    float *dst = out + ((int64_t)b * Hq + q_head_begin + hr) * 128;
+    // Two-level merge inside the kernel: the last block of a slice of
+    // kSlice splits merges the slice; the last slice merger finishes the row.
+    const int k = blk - plan.first;
+    const int slice = k / kSlice;
     const int slices = (plan.splits + kSlice - 1) / kSlice;
-    if (slices == 0) {  // an empty row: nothing was kept
-        if (q == 0 && threadIdx.x < 128) dst[threadIdx.x] = 0.0f;
+    const int in_slice = min(kSlice, plan.splits - slice * kSlice);
+    float *dst = out + ((int64_t)b * Hq + h) * 128;
+    unsigned long long *sc = W.slice_ctr + (int64_t)prow * kMaxSlices + slice;
+    if (!arrive_last(sc, in_slice, &last)) return;
+    const float *first = W.part + (int64_t)(plan.first + slice * kSlice) * kPart;
+    if (slices == 1) {
+        merge_partials(first, in_slice, nullptr, dst, MS);
         return;
     }
-    if (q >= slices) return;
-    float *sp = super + ((int64_t)r * max_slices) * kPart;
-    const int k0 = q * kSlice;
-    merge_partials(part + (int64_t)(plan.first + k0) * kPart, min(kSlice, plan.splits - k0),
-                   sp + (int64_t)q * kPart, nullptr, S);
-    // Publish this slice, then count it; the last one merges them all.
-    __threadfence();
-    if (threadIdx.x == 0) S.last = atomicAdd(&ctr[r], 1u) == (uint32_t)(slices - 1);
-    __syncthreads();
-    if (!S.last) return;
-    __threadfence();
-    merge_partials(sp, slices, nullptr, dst, S);
-}
-
-// Local heads: S static splits per head row (S <= 128).
-__global__ __launch_bounds__(kCombThreads) void local_combine_kernel(
-    const float *__restrict__ part, int S_, int Hq, int q_head_begin, int n_q,
-    float *__restrict__ out)
-{
-    __shared__ CombShared S;
-    const int r = blockIdx.x;
-    const int b = r / n_q, hr = r % n_q;
-    merge_partials(part + (int64_t)r * S_ * kPart, S_, nullptr,
-                   out + ((int64_t)b * Hq + q_head_begin + hr) * 128, S);
+    float *sp = W.super + ((int64_t)prow * kMaxSlices) * kPart;
+    merge_partials(first, in_slice, sp + (int64_t)slice * kPart, nullptr, MS);
+    if (!arrive_last(W.head_ctr + prow, slices, &last)) return;
+    merge_partials(sp, slices, nullptr, dst, MS);
 }
 
 hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,
@@ -390,12 +365,9 @@ hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint
     const int R = B * n_q_heads;
     SparseWs W;
     sparse_ws_layout(R, &W, ws);
-    RTP_TRY(launch(sparse_attn_kernel, dim3(sparse_grid(R)), dim3(kAttThreads), 0, stream, q,
-                   K, V, idx, count, N, kv_cap, Hq, Hkv, q_head_begin, n_q_heads, R,
-                   scale * kLog2e, W.part, W.ctr));
-    const int slices = sparse_slices(R);
-    return launch(sparse_combine_kernel, dim3(slices, R), dim3(kCombThreads), 0, stream, W.part,
-                  W.super, W.ctr, count, N, R, Hq, q_head_begin, n_q_heads, slices, out);
+    return launch(sparse_attn_kernel, dim3(sparse_grid(R)), dim3(kAttThreads), 0, stream, q, K,
+                  V, idx, count, N, kv_cap, Hq, Hkv, q_head_begin, n_q_heads, R,
+                  scale * kLog2e, W, out);
 }
 
 // ------------------------------------------------------------- local
@@ -413,10 +385,83 @@ int local_splits(int64_t n_rows)
     return (int)(s < 1 ? 1 : (s > kMaxLocalSplits ? kMaxLocalSplits : s));
 }
 
+constexpr int kLocalSlice = 16;  // split partials merged per block, first level
+constexpr int kMaxLocalSlices = (kMaxLocalSplits + kLocalSlice - 1) / kLocalSlice;
+
+struct LocalWs {
+    float *part;                    // [B*n_q][S] per-split partials
+    float *super;                   // [B*n_q][kMaxLocalSlices] slice merges
+    unsigned long long *slice_ctr;  // [B*n_q][kMaxLocalSlices], by a chunk's first head
+    unsigned long long *group_ctr;  // [B*n_q]
+};
+
+// The row list never exceeds N rows, so sizing with N bounds every
+// n_sink / window.
+static size_t local_ws_layout(int64_t B, int64_t n_q, int N, LocalWs *W, void *base)
+{
+    const int64_t R = B * n_q;
+    size_t off = 0;
+    const size_t part = off;
+    off += align_up((size_t)R * local_splits(N) * kPart * sizeof(float), 256);
+    const size_t sup = off;
+    off += align_up((size_t)R * kMaxLocalSlices * kPart * sizeof(float), 256);
+    const size_t sc = off;
+    off += align_up((size_t)R * kMaxLocalSlices * sizeof(unsigned long long), 256);
+    const size_t gc = off;
+    off += align_up((size_t)R * sizeof(unsigned long long), 256);
+    if (W) {
+        char *b = static_cast<char *>(base);
+        W->part = reinterpret_cast<float *>(b + part);
+        W->super = reinterpret_cast<float *>(b + sup);
+        W->slice_ctr = reinterpret_cast<unsigned long long *>(b + sc);
+        W->group_ctr = reinterpret_cast<unsigned long long *>(b + gc);
+    }
+    return off;
+}
+
 size_t local_ws_bytes(int64_t B, int64_t n_q, int N)
 {
-    // The row list never exceeds N rows, so this bounds every n_sink/window.
-    return align_up((size_t)(B * n_q * local_splits(N)) * kPart * sizeof(float), 256);
+    return local_ws_layout(B, n_q, N, nullptr, nullptr);
+}
+
+// Merges n <= kLocalSlice partials for each of nh <= 8 heads at once:
+// thread t takes head t/32 and output dimensions 4*(t%32) .. +3.  Head hh's
+// partials start at first + hh*head_stride (floats), kPart apart.  Writes
+// merged partials (dst_part, same head stride) or output rows (dst_out,
+// 128 apart).
+__device__ void merge_heads(const float *first, int64_t head_stride, int n, int nh,
+                            float *dst_part, int64_t dst_stride, float *dst_out)
+{
+    const int hh = threadIdx.x >> 5, d = (threadIdx.x & 31) * 4;
+    if (hh >= nh) return;
+    const float *src = first + hh * head_stride;
+    float M = -INFINITY;
+#pragma unroll 16
+    for (int k = 0; k < n; ++k) M = fmaxf(M, ld_agent(src + (int64_t)k * kPart));
+    float L = 0.0f;
+    float O[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+    for (int k = 0; k < n; ++k) {
+        const float *pk = src + (int64_t)k * kPart;
+        const float f = rescale(ld_agent(pk), M);
+        L = fmaf(ld_agent(pk + 1), f, L);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[e] = fmaf(ld_agent(pk + 4 + d + e), f, O[e]);
+    }
+    if (dst_out) {
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        *reinterpret_cast<float4 *>(dst_out + hh * 128 + d) =
+            make_float4(O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv);
+    }
+    if (dst_part) {
+        float *pd = dst_part + hh * dst_stride;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st_agent(pd + 4 + d + e, O[e]);
+        if (d == 0) {
+            st_agent(pd, M);
+            st_agent(pd + 1, L);
+        }
+    }
 }
 
 // Block (s, y, b): KV head g = g_first + y / chunks_per_g, query heads
@@ -426,8 +471,9 @@ __global__ __launch_bounds__(kAttThreads) void local_attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int N, int64_t kv_cap, int Hq, int Hkv,
     int q_head_begin, int n_q, int n_sink, int window, float qscale, int S,
-    int chunks_per_g, float *__restrict__ part)
+    int chunks_per_g, LocalWs W, float *__restrict__ out)
 {
+    __shared__ int last;
     __shared__ float wm[kAttThreads / kWave][8], wl[kAttThreads / kWave][8];
     __shared__ float wo[kAttThreads / kWave][8][128];
     const int G = Hq / Hkv;
@@ -599,13 +645,32 @@ __global__ __launch_bounds__(kAttThreads) void local_attn_kernel(
             L += wl[i][hh] * f;
             O += wo[i][hh][c] * f;
         }
-        float *pr = part + (((int64_t)b * n_q + (h_lo - q_head_begin + hh)) * S + s) * kPart;
-        pr[4 + c] = O;
+        float *pr = W.part + (((int64_t)b * n_q + (h_lo - q_head_begin + hh)) * S + s) * kPart;
+        st_agent(pr + 4 + c, O);
         if (c == 0) {
-            pr[0] = M;
-            pr[1] = L;
+            st_agent(pr, M);
+            st_agent(pr + 1, L);
         }
     }
+
+    // Two-level merge inside the kernel, for all nh heads of this chunk at
+    // once (counters indexed by the chunk's first head row).
+    const int64_t r0 = (int64_t)b * n_q + (h_lo - q_head_begin);
+    const int slice = s / kLocalSlice;
+    const int slices = (S + kLocalSlice - 1) / kLocalSlice;
+    const int in_slice = min(kLocalSlice, S - slice * kLocalSlice);
+    float *dst = out + ((int64_t)b * Hq + h_lo) * 128;
+    if (!arrive_last(W.slice_ctr + r0 * kMaxLocalSlices + slice, in_slice, &last)) return;
+    const float *first = W.part + (r0 * S + slice * kLocalSlice) * kPart;
+    if (slices == 1) {
+        merge_heads(first, (int64_t)S * kPart, in_slice, nh, nullptr, 0, dst);
+        return;
+    }
+    float *sp = W.super + r0 * kMaxLocalSlices * kPart;
+    merge_heads(first, (int64_t)S * kPart, in_slice, nh, sp + (int64_t)slice * kPart,
+                (int64_t)kMaxLocalSlices * kPart, nullptr);
+    if (!arrive_last(W.group_ctr + r0, slices, &last)) return;
+    merge_heads(sp, (int64_t)kMaxLocalSlices * kPart, slices, nh, nullptr, 0, dst);
 }
 
 hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,
@@ -619,12 +684,11 @@ hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K, const uint1
     const int g_last = (q_head_begin + n_q_heads - 1) / G;
     const int chunks_per_g = (G + 7) / 8;
     const int ny = (g_last - g_first + 1) * chunks_per_g;
-    float *part = static_cast<float *>(ws);
-    RTP_TRY(launch(local_attn_kernel, dim3(S, ny, B), dim3(kAttThreads), 0, stream, q, K, V, N,
-                   kv_cap, Hq, Hkv, q_head_begin, n_q_heads, n_sink, window, scale * kLog2e,
-                   S, chunks_per_g, part));
-    return launch(local_combine_kernel, dim3(B * n_q_heads), dim3(kCombThreads), 0, stream, part,
-                  S, Hq, q_head_begin, n_q_heads, out);
+    LocalWs W;
+    local_ws_layout(B, n_q_heads, N, &W, ws);
+    return launch(local_attn_kernel, dim3(S, ny, B), dim3(kAttThreads), 0, stream, q, K, V, N,
+                  kv_cap, Hq, Hkv, q_head_begin, n_q_heads, n_sink, window, scale * kLog2e, S,
+                  chunks_per_g, W, out);
 }
 
 }  // namespace rtp

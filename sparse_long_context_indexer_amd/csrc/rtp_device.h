@@ -110,4 +110,70 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *scratch, T *total)
     return ex;
 }
 
+// Cross-block hand-off inside one kernel.  Data another block of the same
+// kernel will read is written with agent-scope stores (global_store sc1:
+// written through the per-XCD L2) and read with agent-scope loads (sc1);
+// before a block counts itself done, each wave waits for its stores to
+// complete.  No L2 write-back or invalidate is needed.
+__device__ __forceinline__ void st_agent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(double *p, double v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned long long *p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_agent(const double *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_agent(const unsigned long long *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until every vector memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Arrival counter shared by the blocks of one call.  A counter word holds
+// a tag (low 32 bits) and a count (high 32 bits); after every call it is
+// left as (kCtrTag, 0), so a call normally arrives with one atomicAdd.  A
+// word without the tag (fresh or reused memory) is claimed with a
+// compare-and-swap.  kCtrTag is a NaN payload that arithmetic never
+// produces, so no float or index the library writes can look like a
+// counter.  Returns how many blocks of this call arrived before the caller.
+constexpr uint32_t kCtrTag = 0x7FA5C3E1u;
+constexpr unsigned long long kCtrOne = 1ull << 32;
+
+__device__ __forceinline__ uint32_t ctr_arrive(unsigned long long *ctr)
+{
+    const unsigned long long old = atomicAdd(ctr, kCtrOne);
+    if ((uint32_t)old == kCtrTag) return (uint32_t)(old >> 32);
+    // The word was not a counter (this add landed on it and is void): the
+    // first block to swap in (kCtrTag, 1) starts the count, later blocks
+    // count on the tagged word.  Adds to the high half never change the tag.
+    unsigned long long cur = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        if ((uint32_t)cur == kCtrTag) return (uint32_t)(atomicAdd(ctr, kCtrOne) >> 32);
+        const unsigned long long prev = atomicCAS(ctr, cur, kCtrOne | kCtrTag);
+        if (prev == cur) return 0u;
+        cur = prev;
+    }
+}
+
+// Called by the last block of a call, when no other block of the call will
+// touch the counter again.
+__device__ __forceinline__ void ctr_reset(unsigned long long *ctr) { atomicExch(ctr, (unsigned long long)kCtrTag); }
+
 }  // namespace rtp

@@ -47,6 +47,7 @@ hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K,
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+
 template <typename... KArgs>
 hipError_t launch_impl(const void *k, dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
                        KArgs... args)

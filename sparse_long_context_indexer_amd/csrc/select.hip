@@ -53,7 +53,9 @@ struct SelRow {
     float M;         // row max
     uint32_t j1;     // level-1 boundary bin
     uint64_t slots;  // emit's slot counters: kept (high 32 bits), candidates (low)
-    uint32_t pad[6];
+    uint32_t hist_done;  // hist blocks finished
+    uint32_t emit_done;  // emit blocks finished
+    uint32_t pad[4];
 };
 static_assert(sizeof(SelRow) == 64, "SelRow is one 64-B record");
 
@@ -110,6 +112,19 @@ static SelPtrs sel_ptrs(void *ws, int64_t R, int64_t N)
     return P;
 }
 
+// Candidates (key, index) cross from the emit blocks to the row's resolving
+// block through agent-scope 8-byte accesses.
+__device__ __forceinline__ uint2 ld_cand(const uint2 *p)
+{
+    const unsigned long long v = ld_agent(reinterpret_cast<const unsigned long long *>(p));
+    return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
+__device__ __forceinline__ void st_cand(uint2 *p, uint2 e)
+{
+    st_agent(reinterpret_cast<unsigned long long *>(p),
+             (unsigned long long)e.x | ((unsigned long long)e.y << 32));
+}
+
 // Largest finite score whose key lies in level-1 bin `bin` (bins that hold
 // finite scores only).
 __device__ __forceinline__ float bin_top(uint32_t bin) { return key_score((bin << 20) | 0xFFFFFu); }
@@ -164,11 +179,24 @@ __global__ __launch_bounds__(256) void sel_zero_kernel(SelPtrs P)
 
 // --------------------------------------------------------------- hist
 
+struct PickShared {
+    double hm[kBins1];
+    double scan[kPickThreads / kWave + 1];
+    float red[kPickThreads / kWave];
+    int chosen;  // highest bin whose running mass reaches T
+    int lowest;  // lowest bin with mass
+    int last;
+};
+
+__device__ void pick_row(SelPtrs P, int64_t r, float p, PickShared &S);
+
 __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__restrict__ scores,
-                                                               int N, SelPtrs P)
+                                                               int N, SelPtrs P, float p)
 {
-    __shared__ double hm[kBins1];
-    __shared__ float red[kSelThreads / kWave];
+    static_assert(kSelThreads == kPickThreads, "the last hist block runs the pick");
+    __shared__ PickShared S;
+    double *hm = S.hm;
+    float *red = S.red;
     const int64_t r = blockIdx.y;
     const int blk = blockIdx.x;
     const float *sr = scores + r * (int64_t)N;
@@ -200,31 +228,39 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
         if (w > 0.0 && (uint32_t)i != tb) atomicAdd(&g.mass[i], w);
     }
     if (threadIdx.x == 0) {
-        ChunkTop t;
-        t.m = mb;
-        t.mass = hm[tb];
-        P.tops[r * P.nblk + blk] = t;
+        ChunkTop &t = P.tops[r * P.nblk + blk];
+        st_agent(&t.m, mb);
+        st_agent(&t.mass, hm[tb]);
     }
+    // The last chunk of the row to finish computes the row's threshold; it
+    // reads the others' histogram atomics and chunk tops with agent-scope
+    // loads once every block's writes have completed.
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) S.last = atomicAdd(&P.rows[r].hist_done, 1u) == (uint32_t)(P.nblk - 1);
+    __syncthreads();
+    if (!S.last) return;
+    pick_row(P, r, p, S);
 }
 
 // --------------------------------------------------------------- pick
 
-__global__ __launch_bounds__(kPickThreads) void sel_pick_kernel(SelPtrs P, float p)
+__device__ void pick_row(SelPtrs P, int64_t r, float p, PickShared &S)
 {
     constexpr int kPer = kBins1 / kPickThreads;  // bins per thread
     constexpr int kNW = kPickThreads / kWave;
-    __shared__ double hm[kBins1];
-    __shared__ double scan[kNW + 1];
-    __shared__ float red[kNW];
-    __shared__ int chosen;  // highest bin where the running mass crosses T
-    __shared__ int lowest;  // lowest non-empty bin
-    const int64_t r = blockIdx.x;
+    double *hm = S.hm;
+    double *scan = S.scan;
+    float *red = S.red;
+    int &chosen = S.chosen;
+    int &lowest = S.lowest;
     const ChunkTop *tops = P.tops + r * P.nblk;
     const Hist1 &g = P.hist1[r];
     const int tid = threadIdx.x;
 
+    __syncthreads();  // the block's own histogram in hm is done with
     float m = -INFINITY;
-    for (int k = tid; k < P.nblk; k += kPickThreads) m = fmaxf(m, tops[k].m);
+    for (int k = tid; k < P.nblk; k += kPickThreads) m = fmaxf(m, ld_agent(&tops[k].m));
     m = wave_max(m);
     if (lane_id() == 0) red[tid / kWave] = m;
     if (tid == 0) {
@@ -238,13 +274,13 @@ __global__ __launch_bounds__(kPickThreads) void sel_pick_kernel(SelPtrs P, float
     // A bin counted in Hist1 lies below some chunk's top bin, so its top
     // score is below M: every factor is <= 1.
     for (int i = tid; i < kBins1; i += kPickThreads) {
-        const double gm = g.mass[i];
+        const double gm = ld_agent(&g.mass[i]);
         hm[i] = gm > 0.0 ? gm * exp((double)bin_top(i) - M) : 0.0;
     }
     __syncthreads();
     for (int k = tid; k < P.nblk; k += kPickThreads) {
-        const ChunkTop t = tops[k];
-        atomicAdd(&hm[score_key(t.m) >> 20], t.mass * exp((double)t.m - M));
+        const float tm = ld_agent(&tops[k].m);
+        atomicAdd(&hm[score_key(tm) >> 20], ld_agent(&tops[k].mass) * exp((double)tm - M));
     }
     __syncthreads();
 
@@ -301,57 +337,9 @@ __global__ __launch_bounds__(kPickThreads) void sel_pick_kernel(SelPtrs P, float
 
 // --------------------------------------------------------------- emit
 
-__global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
-    const float *__restrict__ scores, int N, SelPtrs P, int32_t *__restrict__ idx)
-{
-    __shared__ unsigned long long wbase[kSelThreads / kWave];
-    __shared__ unsigned long long bcount;
-    __shared__ unsigned long long gbase;
-    const int64_t r = blockIdx.y;
-    const uint32_t j1 = P.rows[r].j1;
-    const float *sr = scores + r * (int64_t)N;
-    int32_t *ir = idx + r * (int64_t)N;
-    uint2 *cr = P.cand + r * (int64_t)N;
-    float v[kSelPerThread];
-    const ChunkView cv = load_chunk(sr, N, (int64_t)blockIdx.x * kSelChunk, v);
-    if (threadIdx.x == 0) bcount = 0ull;
-    // Per lane: kept count (high half) and candidate count (low half).
-    uint32_t mine = 0;
-#pragma unroll
-    for (int t = 0; t < kSelPerThread; ++t) {
-        const uint32_t bin = score_key(v[t]) >> 20;
-        const bool valid = cv.index(t) < N;
-        mine += (valid && bin > j1) ? 0x10000u : 0u;
-        mine += (valid && bin == j1) ? 1u : 0u;
-    }
-    // Wave prefix (a wave holds at most 2048 of each, so halves never
-    // carry), then one LDS atomic per wave for its block offset and one
-    // global atomic per block for its row offset.
-    const uint32_t inc = wave_inclusive_scan(mine);
-    const uint32_t wtot = __shfl(inc, kWave - 1);
-    __syncthreads();
-    const int w = threadIdx.x / kWave;
-    if (lane_id() == 0)
-        wbase[w] = atomicAdd(&bcount, ((unsigned long long)(wtot >> 16) << 32) | (wtot & 0xFFFFu));
-    __syncthreads();
-    if (threadIdx.x == 0)
-        gbase = bcount ? atomicAdd(reinterpret_cast<unsigned long long *>(&P.rows[r].slots),
-                                   bcount)
-                       : 0ull;
-    __syncthreads();
-    const unsigned long long base = gbase + wbase[w];
-    const uint32_t ex = inc - mine;
-    uint32_t oa = (uint32_t)(base >> 32) + (ex >> 16);
-    uint32_t oc = (uint32_t)base + (ex & 0xFFFFu);
-#pragma unroll
-    for (int t = 0; t < kSelPerThread; ++t) {
-        const uint32_t key = score_key(v[t]);
-        const uint32_t bin = key >> 20;
-        const int64_t i = cv.index(t);
-        if (i < N && bin > j1) ir[oa++] = (int32_t)i;
-        if (i < N && bin == j1) cr[oc++] = make_uint2(key, (uint32_t)i);
-    }
-}
+struct ResShared;
+__device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
+                            ResShared &S);
 
 // ------------------------------------------------------------ resolve
 //
@@ -376,6 +364,10 @@ struct ResShared {
     uint32_t j;      // chosen digit
     uint32_t cbefore;
     double abefore;  // A plus the mass above the chosen digit
+    // emit's own use of the block's LDS
+    unsigned long long wbase[kSelThreads / kWave];
+    unsigned long long bcount, gbase;
+    int last;
 };
 
 // Wave 0 chooses the boundary digit of a score level from S.hm/S.hc over
@@ -458,7 +450,7 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
     for (int64_t c0 = 0; c0 < n; c0 += kResThreads) {
         const int64_t k = c0 + threadIdx.x;
         const bool valid = k < n;
-        uint2 e = valid ? cr[k] : make_uint2(0, 0);
+        uint2 e = valid ? ld_cand(cr + k) : make_uint2(0, 0);
         const uint32_t field = by_index ? e.y : e.x;
         const uint32_t dg = (field >> shift) & mask;
         const bool out = valid && (emit_above ? dg > keep_digit : dg < keep_digit);
@@ -469,25 +461,27 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
         const uint32_t pos = block_exclusive_scan<kResThreads>((uint32_t)keep, S.uscan, &tot);
         // All reads of this chunk are done (the scan synchronised the block),
         // and survivors land at or below their read position.
-        if (keep) cr[kept_total + pos] = e;
+        if (keep) st_cand(cr + kept_total + pos, e);
         kept_total += tot;
         __syncthreads();
     }
     return kept_total;
 }
 
-// One pass over n candidates in src (LDS): emits the kept side of digit j,
-// moves digit j's candidates to dst (LDS).  Returns the number moved.
-__device__ uint32_t res_filter_lds(const uint2 *src, uint32_t n, uint2 *dst, int shift,
+// One pass over n candidates in src (LDS, or global memory when kGlobal):
+// emits the kept side of digit j, moves digit j's candidates to dst (LDS,
+// which must hold them).  Returns the number moved.
+template <bool kGlobal>
+__device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int shift,
                                    uint32_t mask, uint32_t j, bool emit_above, bool by_index,
                                    int32_t *ir, ResShared &S)
 {
     if (threadIdx.x == 0) S.nnext = 0u;
     __syncthreads();
-    for (uint32_t c0 = 0; c0 < n; c0 += kResThreads) {
-        const uint32_t k = c0 + threadIdx.x;
+    for (int64_t c0 = 0; c0 < n; c0 += kResThreads) {
+        const int64_t k = c0 + threadIdx.x;
         const bool valid = k < n;
-        const uint2 e = valid ? src[k] : make_uint2(0, 0);
+        const uint2 e = valid ? (kGlobal ? ld_cand(src + k) : src[k]) : make_uint2(0, 0);
         const uint32_t dg = ((by_index ? e.y : e.x) >> shift) & mask;
         const int64_t pa = wave_append(valid && (emit_above ? dg > j : dg < j), &S.nout);
         if (pa >= 0) ir[pa] = (int32_t)e.y;
@@ -498,27 +492,30 @@ __device__ uint32_t res_filter_lds(const uint2 *src, uint32_t n, uint2 *dst, int
     return S.nnext;
 }
 
-__global__ __launch_bounds__(kResThreads) void sel_resolve_kernel(
-    int N, SelPtrs P, int32_t *__restrict__ idx, int32_t *__restrict__ count)
+__device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
+                            ResShared &S)
 {
-    __shared__ ResShared S;
-    const int64_t r = blockIdx.x;
-    const SelRow row = P.rows[r];
+    __syncthreads();  // emit is done with the shared words it used
+    const SelRow &row = P.rows[r];
     const double M = (double)row.M;
     const double T = row.T;
     double A = row.A;
-    int64_t n = (uint32_t)row.slots;
+    const unsigned long long slots =
+        ld_agent(reinterpret_cast<const unsigned long long *>(&row.slots));
+    int64_t n = (uint32_t)slots;
     uint2 *gc = P.cand + r * (int64_t)N;
     const int tid = threadIdx.x;
-    const uint32_t emitted = (uint32_t)(row.slots >> 32);  // kept by emit
+    const uint32_t emitted = (uint32_t)(slots >> 32);  // kept by emit
     int32_t *ir = idx + r * (int64_t)N + emitted;
-    const bool in_lds = n <= kResCap;
+    bool in_lds = n <= kResCap;
     int cur = 0;  // LDS buffer holding the candidates
     if (tid == 0) S.nout = 0u;
     if (in_lds)
-        for (int64_t k = tid; k < n; k += kResThreads) S.buf[0][k] = gc[k];
+        for (int64_t k = tid; k < n; k += kResThreads) S.buf[0][k] = ld_cand(gc + k);
     __syncthreads();
     const uint2 *cr = in_lds ? S.buf[0] : gc;
+    // Candidate k from LDS, or from global memory for rows too large for it.
+    auto cand = [&](int64_t k) { return in_lds ? cr[k] : ld_cand(cr + k); };
 
     // Score levels: key bits [19:10], then [9:0].
     for (int level = 0; level < 2 && n > 0; ++level) {
@@ -527,7 +524,7 @@ __global__ __launch_bounds__(kResThreads) void sel_resolve_kernel(
         S.hc[tid] = 0u;
         __syncthreads();
         for (int64_t k = tid; k < n; k += kResThreads) {
-            const uint32_t key = cr[k].x;
+            const uint32_t key = cand(k).x;
             const uint32_t dg = (key >> shift) & 1023u;
             atomicAdd(&S.hm[dg], exp((double)key_score(key) - M));
             atomicAdd(&S.hc[dg], 1u);
@@ -538,10 +535,16 @@ __global__ __launch_bounds__(kResThreads) void sel_resolve_kernel(
         const uint32_t j = S.j;
         A = S.abefore;  // A plus the mass of the digits above j
         if (in_lds) {
-            n = res_filter_lds(S.buf[cur], (uint32_t)n, S.buf[cur ^ 1], shift, 1023u, j, true,
-                               false, ir, S);
+            n = res_filter_lds<false>(S.buf[cur], n, S.buf[cur ^ 1], shift, 1023u, j, true,
+                                      false, ir, S);
             cur ^= 1;
             cr = S.buf[cur];
+        } else if (S.hc[j] <= (uint32_t)kResCap) {
+            // The boundary digit's candidates fit in LDS: continue there.
+            n = res_filter_lds<true>(gc, n, S.buf[0], shift, 1023u, j, true, false, ir, S);
+            in_lds = true;
+            cur = 0;
+            cr = S.buf[0];
         } else {
             n = res_filter_global(gc, n, shift, 1023u, j, true, false, ir, S);
         }
@@ -550,7 +553,7 @@ __global__ __launch_bounds__(kResThreads) void sel_resolve_kernel(
     if (n > 0) {
         // Every survivor now has the same score tau.  Keep the first c of
         // them in index order: the smallest c with A + c * e_tau >= T.
-        const uint32_t tau_key = cr[0].x;
+        const uint32_t tau_key = cand(0).x;
         const double e_tau = exp((double)key_score(tau_key) - M);
         int64_t c = 1;
         if (A + (double)n * e_tau < T) {
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(kResThreads) void sel_resolve_kernel(
             for (int64_t c0 = 0; c0 < n; c0 += kResThreads) {
                 const int64_t k = c0 + tid;
                 const bool valid = k < n;
-                const uint32_t ix = valid ? cr[k].y : 0u;
+                const uint32_t ix = valid ? cand(k).y : 0u;
                 const int64_t pa = wave_append(valid, &S.nout);
                 if (pa >= 0) ir[pa] = (int32_t)ix;
             }
@@ -583,27 +586,94 @@ __global__ __launch_bounds__(kResThreads) void sel_resolve_kernel(
                 for (int i = tid; i < nb; i += kResThreads) S.hc[i] = 0u;
                 __syncthreads();
                 for (int64_t k = tid; k < n; k += kResThreads)
-                    atomicAdd(&S.hc[(cr[k].y >> shift) & mask], 1u);
+                    atomicAdd(&S.hc[(cand(k).y >> shift) & mask], 1u);
                 __syncthreads();
                 if (tid < kWave) res_choose_count((uint32_t)c, nb, S);
                 __syncthreads();
                 const uint32_t j = S.j;
                 c -= S.cbefore;
                 if (in_lds) {
-                    n = res_filter_lds(S.buf[cur], (uint32_t)n, S.buf[cur ^ 1], shift, mask, j,
-                                       false, true, ir, S);
+                    n = res_filter_lds<false>(S.buf[cur], n, S.buf[cur ^ 1], shift, mask, j,
+                                              false, true, ir, S);
                     cur ^= 1;
                     cr = S.buf[cur];
+                } else if (S.hc[j] <= (uint32_t)kResCap) {
+                    n = res_filter_lds<true>(gc, n, S.buf[0], shift, mask, j, false, true, ir, S);
+                    in_lds = true;
+                    cur = 0;
+                    cr = S.buf[0];
                 } else {
                     n = res_filter_global(gc, n, shift, mask, j, false, true, ir, S);
                 }
             }
             // One token left (its index is fully determined): keep it.
-            if (tid == 0 && n > 0 && c > 0) ir[S.nout++] = (int32_t)cr[0].y;
+            if (tid == 0 && n > 0 && c > 0) ir[S.nout++] = (int32_t)cand(0).y;
         }
     }
     __syncthreads();
     if (tid == 0) count[r] = (int32_t)(emitted + S.nout);
+}
+
+__global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
+    const float *__restrict__ scores, int N, SelPtrs P, int32_t *__restrict__ idx,
+    int32_t *__restrict__ count)
+{
+    static_assert(kSelThreads == kResThreads, "the last emit block runs the resolve");
+    __shared__ ResShared S;
+    unsigned long long *wbase = S.wbase;
+    const int64_t r = blockIdx.y;
+    const uint32_t j1 = P.rows[r].j1;
+    const float *sr = scores + r * (int64_t)N;
+    int32_t *ir = idx + r * (int64_t)N;
+    uint2 *cr = P.cand + r * (int64_t)N;
+    float v[kSelPerThread];
+    const ChunkView cv = load_chunk(sr, N, (int64_t)blockIdx.x * kSelChunk, v);
+    if (threadIdx.x == 0) S.bcount = 0ull;
+    // Per lane: kept count (high half) and candidate count (low half).
+    uint32_t mine = 0;
+#pragma unroll
+    for (int t = 0; t < kSelPerThread; ++t) {
+        const uint32_t bin = score_key(v[t]) >> 20;
+        const bool valid = cv.index(t) < N;
+        mine += (valid && bin > j1) ? 0x10000u : 0u;
+        mine += (valid && bin == j1) ? 1u : 0u;
+    }
+    // Wave prefix (a wave holds at most 2048 of each, so halves never
+    // carry), then one LDS atomic per wave for its block offset and one
+    // global atomic per block for its row offset.
+    const uint32_t inc = wave_inclusive_scan(mine);
+    const uint32_t wtot = __shfl(inc, kWave - 1);
+    __syncthreads();
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0)
+        wbase[w] = atomicAdd(&S.bcount, ((unsigned long long)(wtot >> 16) << 32) | (wtot & 0xFFFFu));
+    __syncthreads();
+    if (threadIdx.x == 0)
+        S.gbase = S.bcount ? atomicAdd(reinterpret_cast<unsigned long long *>(&P.rows[r].slots),
+                                       S.bcount)
+                           : 0ull;
+    __syncthreads();
+    const unsigned long long base = S.gbase + wbase[w];
+    const uint32_t ex = inc - mine;
+    uint32_t oa = (uint32_t)(base >> 32) + (ex >> 16);
+    uint32_t oc = (uint32_t)base + (ex & 0xFFFFu);
+#pragma unroll
+    for (int t = 0; t < kSelPerThread; ++t) {
+        const uint32_t key = score_key(v[t]);
+        const uint32_t bin = key >> 20;
+        const int64_t i = cv.index(t);
+        if (i < N && bin > j1) ir[oa++] = (int32_t)i;
+        if (i < N && bin == j1) st_cand(cr + oc++, make_uint2(key, (uint32_t)i));
+    }
+    // The last chunk of the row to finish resolves the boundary bin, once
+    // every block's candidate stores have completed.
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        S.last = atomicAdd(&P.rows[r].emit_done, 1u) == (uint32_t)(gridDim.x - 1);
+    __syncthreads();
+    if (!S.last) return;
+    resolve_row(N, P, r, idx, count, S);
 }
 
 // ---------------------------------------------------------------- p >= 1
@@ -627,11 +697,8 @@ hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p, in
     SelPtrs P = sel_ptrs(ws, R, N);
     dim3 grid((unsigned)P.nblk, (unsigned)R);
     RTP_TRY(launch(sel_zero_kernel, dim3(kZeroBlocks), dim3(256), 0, stream, P));
-    RTP_TRY(launch(sel_hist_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P));
-    RTP_TRY(launch(sel_pick_kernel, dim3((unsigned)R), dim3(kPickThreads), 0, stream, P, p));
-    RTP_TRY(launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, idx));
-    return launch(sel_resolve_kernel, dim3((unsigned)R), dim3(kResThreads), 0, stream, N, P,
-                  idx, count);
+    RTP_TRY(launch(sel_hist_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, p));
+    return launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, idx, count);
 }
 
 }  // namespace rtp

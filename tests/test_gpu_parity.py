@@ -226,3 +226,34 @@ def test_local_unaligned_head_range():
             assert ok, (h, err, rel)
         else:
             assert np.all(np.isnan(got[0, h]))
+
+
+# ------------------------------------------------------------ workspaces
+
+def test_workspace_garbage_and_reuse():
+    # Workspaces start as arbitrary bytes (no initialisation is required),
+    # are reused by the next call, and are then reused for a smaller call
+    # whose layout differs.
+    from sparse_long_context_indexer_amd.runner import DecodeLayer
+    cfg = synth.CONFIGS[1]
+    L = load_layer(cfg)
+    step = DecodeLayer(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.H_r, cfg.n_sink, cfg.window, dev())
+    g = torch.Generator(device="cpu").manual_seed(7)
+    for ws in (step.ws_sel, step.ws_sparse, step.ws_local):
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=g))
+    for rep in range(2):
+        _print(f"full-size call {rep}")
+        res = run_layer(L, 0.9, step=step)
+        fails = check_layer(L, 0.9, res)
+        assert not fails, "\n".join(fails[:20])
+    small = cfg.with_(N=20000, B=1)
+    Ls = load_layer(small)
+    s2 = DecodeLayer(1, cfg.Hq, cfg.Hkv, 20000, cfg.H_r, cfg.n_sink, cfg.window, dev())
+    s2.ws_sparse, s2.ws_local, s2.ws_sel = step.ws_sparse, step.ws_local, step.ws_sel
+    for ws in (step.ws_sparse, step.ws_local):
+        ws[ws.numel() // 3:].fill_(0xFF)
+    for rep in range(2):
+        _print(f"smaller call {rep} on the same workspaces")
+        res = run_layer(Ls, 0.9, step=s2)
+        fails = check_layer(Ls, 0.9, res)
+        assert not fails, "\n".join(fails[:20])
