@@ -32,6 +32,7 @@
 #include <float.h>
 
 #include "rtp_device.h"
+#include "rtp_exp.h"
 #include "rtp_launch.h"
 
 namespace rtp {
@@ -179,8 +180,12 @@ __global__ __launch_bounds__(256) void sel_zero_kernel(SelPtrs P)
 
 // --------------------------------------------------------------- hist
 
+// 2^(j/64) for exp_tang; each kernel copies it to LDS.
+__constant__ double kExp2Tbl[kExpTable] = RTP_EXP2_TABLE;
+
 struct PickShared {
     double hm[kBins1];
+    double etbl[kExpTable];
     double scan[kPickThreads / kWave + 1];
     float red[kPickThreads / kWave];
     int chosen;  // highest bin whose running mass reaches T
@@ -204,6 +209,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
     load_chunk(sr, N, (int64_t)blk * kSelChunk, v);  // missing elements: -inf
 
     for (int i = threadIdx.x; i < kBins1; i += kSelThreads) hm[i] = 0.0;
+    if (threadIdx.x < kExpTable) S.etbl[threadIdx.x] = kExp2Tbl[threadIdx.x];
     float m = -INFINITY;
 #pragma unroll
     for (int t = 0; t < kSelPerThread; ++t) m = fmaxf(m, v[t]);
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
         if (v[t] == -INFINITY) continue;  // past the end of the row
         const uint32_t bin = score_key(v[t]) >> 20;
         const double ref = bin == tb ? mbd : (double)bin_top(bin);
-        atomicAdd(&hm[bin], exp((double)v[t] - ref));
+        atomicAdd(&hm[bin], exp_tang((double)v[t] - ref, S.etbl));
     }
     __syncthreads();
     Hist1 &g = P.hist1[r];
@@ -258,9 +264,19 @@ __device__ void pick_row(SelPtrs P, int64_t r, float p, PickShared &S)
     const Hist1 &g = P.hist1[r];
     const int tid = threadIdx.x;
 
+    // Every load up front, so the block waits for memory once.
+    double gmv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) gmv[k] = ld_agent(&g.mass[tid + k * kPickThreads]);
+    float tm0 = -INFINITY;
+    double tmass0 = 0.0;
+    if (tid < P.nblk) {
+        tm0 = ld_agent(&tops[tid].m);
+        tmass0 = ld_agent(&tops[tid].mass);
+    }
+    float m = tm0;
+    for (int k = tid + kPickThreads; k < P.nblk; k += kPickThreads) m = fmaxf(m, ld_agent(&tops[k].m));
     __syncthreads();  // the block's own histogram in hm is done with
-    float m = -INFINITY;
-    for (int k = tid; k < P.nblk; k += kPickThreads) m = fmaxf(m, ld_agent(&tops[k].m));
     m = wave_max(m);
     if (lane_id() == 0) red[tid / kWave] = m;
     if (tid == 0) {
@@ -273,14 +289,17 @@ __device__ void pick_row(SelPtrs P, int64_t r, float p, PickShared &S)
     const double M = (double)Mf;
     // A bin counted in Hist1 lies below some chunk's top bin, so its top
     // score is below M: every factor is <= 1.
-    for (int i = tid; i < kBins1; i += kPickThreads) {
-        const double gm = ld_agent(&g.mass[i]);
-        hm[i] = gm > 0.0 ? gm * exp((double)bin_top(i) - M) : 0.0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kPickThreads;
+        hm[i] = gmv[k] > 0.0 ? gmv[k] * exp_tang((double)bin_top(i) - M, S.etbl) : 0.0;
     }
     __syncthreads();
-    for (int k = tid; k < P.nblk; k += kPickThreads) {
+    if (tid < P.nblk)
+        atomicAdd(&hm[score_key(tm0) >> 20], tmass0 * exp_tang((double)tm0 - M, S.etbl));
+    for (int k = tid + kPickThreads; k < P.nblk; k += kPickThreads) {
         const float tm = ld_agent(&tops[k].m);
-        atomicAdd(&hm[score_key(tm) >> 20], ld_agent(&tops[k].mass) * exp((double)tm - M));
+        atomicAdd(&hm[score_key(tm) >> 20], ld_agent(&tops[k].mass) * exp_tang((double)tm - M, S.etbl));
     }
     __syncthreads();
 
@@ -356,6 +375,7 @@ constexpr int kResNW = kResThreads / kWave;
 
 struct ResShared {
     uint2 buf[2][kResCap];
+    double etbl[kExpTable];
     double hm[kResBins];
     uint32_t hc[kResBins];
     uint32_t uscan[kResNW + 1];
@@ -526,7 +546,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
         for (int64_t k = tid; k < n; k += kResThreads) {
             const uint32_t key = cand(k).x;
             const uint32_t dg = (key >> shift) & 1023u;
-            atomicAdd(&S.hm[dg], exp((double)key_score(key) - M));
+            atomicAdd(&S.hm[dg], exp_tang((double)key_score(key) - M, S.etbl));
             atomicAdd(&S.hc[dg], 1u);
         }
         __syncthreads();
@@ -554,7 +574,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
         // Every survivor now has the same score tau.  Keep the first c of
         // them in index order: the smallest c with A + c * e_tau >= T.
         const uint32_t tau_key = cand(0).x;
-        const double e_tau = exp((double)key_score(tau_key) - M);
+        const double e_tau = exp_tang((double)key_score(tau_key) - M, S.etbl);
         int64_t c = 1;
         if (A + (double)n * e_tau < T) {
             c = n;
@@ -621,6 +641,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     static_assert(kSelThreads == kResThreads, "the last emit block runs the resolve");
     __shared__ ResShared S;
     unsigned long long *wbase = S.wbase;
+    if (threadIdx.x < kExpTable) S.etbl[threadIdx.x] = kExp2Tbl[threadIdx.x];
     const int64_t r = blockIdx.y;
     const uint32_t j1 = P.rows[r].j1;
     const float *sr = scores + r * (int64_t)N;
