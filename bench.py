@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="end with a 256 MiB device-to-device copy, whose known size "
+                         "calibrates the HBM byte counters of a --pmc profile")
     return ap.parse_args()
 
 
@@ -139,7 +142,7 @@ def main():
     # ------------------------------------------ per-call timing (eager)
     # Each C-ABI call of the step, launched alone over all layers on the
     # current stream and bracketed by HIP events on that stream.
-    def time_call(fn, reps=3):
+    def time_call(fn, reps=10):
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -203,7 +206,9 @@ def main():
             "achieved": scan_bytes / (scan_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(os.path.join(ROOT, "profiles", "index_scores_pmc_ctx1m.md"),
+                                       os.path.join(ROOT, "sparse_long_context_indexer_amd",
+                                                    "csrc", "scan.hip"))
 
     # ---------------------------------------------------- CPU baseline
     cpu = None
@@ -233,6 +238,33 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+    if args.calib_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+
+def measured_traffic(summary, source):
+    """HBM bytes per launch of the roofline kernel from the committed PMC
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's
+    reading for a copy of known size), or None when the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(summary).read()
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in text.splitlines()
+                  if l.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
+    if "source_sha256" not in fields or "traffic_bytes_per_launch" not in fields:
+        return None
+    sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    if fields["source_sha256"].strip() != sha:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, p, target_s):

@@ -62,8 +62,8 @@ enum {
 /*
  * rtp_index_scores -- indexer score of every cached token for each
  * retrieval query head (gist.science summary, method section 2: a 16-dim
- * projector applied to queries and keys before RoPE; arXiv abstract,
- * "16-dimensional indexer").
+ * projector applied to queries and keys before RoPE; the arXiv abstract
+ * gives the indexer's width as 16).
  *
  *   scores[b][h][i] = q_r[b][h] . k_r[b][h / (Hq_r/Hkv_r)][i],  i < N,
  * in fp32, accumulated as one fused multiply-add per dimension in the order
@@ -81,9 +81,9 @@ rtp_status rtp_index_scores(const float *q_r, const float *k_r, float *scores,
 
 /*
  * rtp_topp_select -- dynamic top-p token selection per head (gist.science
- * summary, method section 3: accumulate low-dim attention mass until the
- * cumulative threshold p is reached; section 5: a sort-free,
- * histogram-based threshold).
+ * summary, method section 3: the low-dim attention mass is summed, largest
+ * first, until it reaches p; section 5: the threshold is found with a
+ * histogram instead of a sort).
  *
  * For each of the B*H score rows, with e_i = exp(s_i - max s) in fp64 and
  * Z = sum of e_i over all N tokens: order tokens by score, descending, ties

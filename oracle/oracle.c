@@ -14,8 +14,8 @@
  * What each function follows (citations name the page and its section):
  *   orc_scores      -- 16-dim low-rank indexer score of every cached token,
  *                      taken before RoPE (gist.science summary, method
- *                      section 2 "low-dimensional token indexing"; arXiv
- *                      abstract, "16-dimensional indexer").  The pages give
+ *                      section 2 "low-dimensional token indexing"; the arXiv
+ *                      abstract gives the indexer's width as 16).  The pages give
  *                      no formula; the score is the plain dot product
  *                      q_r . k_r in fp32, accumulated as one fused
  *                      multiply-add per dimension, dimensions 0..15 in order.

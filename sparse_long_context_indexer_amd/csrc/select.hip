@@ -13,22 +13,22 @@
 //           being the bin's largest representable score, merged into the
 //           row's histogram with global atomics; the chunk's own top bin is
 //           kept apart, as mass exp(s - m_b) with m_b the chunk max, so every
-//           term is <= 1 and nothing overflows for any finite input
-//   pick    one block per row: M = max m_b, the histogram rescaled to
-//           exp(s - M), Z, the target p*Z, the boundary bin j1 (the first
-//           bin, from the top, where the running mass reaches the target)
-//           and the mass A above it
+//           term is <= 1 and nothing overflows for any finite input.
+//           The row's last block to finish then runs the pick: M = max m_b,
+//           the histogram rescaled to exp(s - M), Z, the target p*Z, the
+//           boundary bin j1 (the highest bin whose running mass from the top
+//           reaches the target) and the mass A above it
 //   emit    tokens in bins above j1 are kept; tokens of bin j1 become
-//           candidates (key, index)
-//   resolve one block per row: the same step over key bits [19:10], then
-//           [9:0] (the boundary is now one score value tau), then how many
-//           tokens of score tau are needed and, if not all of them, the
-//           lowest indices among them by a count-only radix select over the
-//           index bits
+//           candidates (key, index).  The row's last block to finish then
+//           resolves: the same step over key bits [19:10], then [9:0] (the
+//           boundary is now one score value tau), then how many tokens of
+//           score tau are needed and, if not all of them, the lowest indices
+//           among them by a count-only radix select over the index bits
 //
-// Masses are fp64 (exp in fp64, fp64 sums), so running sums agree with an
-// fp64 reference to ~1e-16 relative.  HBM traffic: the scores are read twice
-// (hist, emit); candidates are few except for near-flat rows.
+// Masses are fp64 (exp_tang, a table-driven fp64 exp within 1.3 ulp, and
+// fp64 sums), so running sums agree with an fp64 reference to ~1e-15
+// relative.  HBM traffic: the scores are read twice (hist, emit);
+// candidates are few except for near-flat rows.
 #include <float.h>
 
 #include "rtp_device.h"
