@@ -141,6 +141,13 @@ struct ChunkView {
         return vec ? c0 + ((int64_t)(t >> 2) * kSelThreads + threadIdx.x) * 4 + (t & 3)
                    : c0 + (int64_t)t * kSelThreads + threadIdx.x;
     }
+    // The same in 32 bits (token indices are below N <= INT32_MAX).
+    __device__ uint32_t index32(int t) const
+    {
+        const uint32_t c = (uint32_t)c0;
+        return vec ? c + ((uint32_t)(t >> 2) * kSelThreads + threadIdx.x) * 4u + (uint32_t)(t & 3)
+                   : c + (uint32_t)t * kSelThreads + threadIdx.x;
+    }
 };
 
 __device__ __forceinline__ ChunkView load_chunk(const float *__restrict__ sr, int N, int64_t c0,
@@ -597,11 +604,11 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
             // Count-only radix select of the c lowest indices: bits [30:20],
             // [19:10], [9:0].  Indices are distinct, so the last level leaves
             // one token.
-            const int shifts[3] = {20, 10, 0};
-            const uint32_t masks[3] = {2047u, 1023u, 1023u};
             for (int level = 0; level < 3 && n > 0 && c > 0; ++level) {
-                const int shift = shifts[level];
-                const uint32_t mask = masks[level];
+                // (computed, not table-driven: a small local table indexed by
+                // the loop counter would live in scratch memory)
+                const int shift = level == 0 ? 20 : (level == 1 ? 10 : 0);
+                const uint32_t mask = level == 0 ? 2047u : 1023u;
                 const int nb = (int)mask + 1;
                 for (int i = tid; i < nb; i += kResThreads) S.hc[i] = 0u;
                 __syncthreads();
@@ -650,15 +657,18 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     float v[kSelPerThread];
     const ChunkView cv = load_chunk(sr, N, (int64_t)blockIdx.x * kSelChunk, v);
     if (threadIdx.x == 0) S.bcount = 0ull;
-    // Per lane: kept count (high half) and candidate count (low half).
-    uint32_t mine = 0;
+    // Per lane: bit t of `above` / `atb` marks slot t as kept / candidate;
+    // `mine` packs their counts (kept in the high half).
+    static_assert(kSelPerThread == 32, "one mask bit per slot");
+    uint32_t above = 0, atb = 0;
 #pragma unroll
     for (int t = 0; t < kSelPerThread; ++t) {
         const uint32_t bin = score_key(v[t]) >> 20;
-        const bool valid = cv.index(t) < N;
-        mine += (valid && bin > j1) ? 0x10000u : 0u;
-        mine += (valid && bin == j1) ? 1u : 0u;
+        const bool valid = cv.vec || cv.index32(t) < (uint32_t)N;
+        above |= (valid && bin > j1) ? (1u << t) : 0u;
+        atb |= (valid && bin == j1) ? (1u << t) : 0u;
     }
+    const uint32_t mine = ((uint32_t)__popc(above) << 16) | (uint32_t)__popc(atb);
     // Wave prefix (a wave holds at most 2048 of each, so halves never
     // carry), then one LDS atomic per wave for its block offset and one
     // global atomic per block for its row offset.
@@ -678,14 +688,10 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     const uint32_t ex = inc - mine;
     uint32_t oa = (uint32_t)(base >> 32) + (ex >> 16);
     uint32_t oc = (uint32_t)base + (ex & 0xFFFFu);
+    for (uint32_t m = above; m; m &= m - 1) ir[oa++] = (int32_t)cv.index32(__ffs(m) - 1);
 #pragma unroll
-    for (int t = 0; t < kSelPerThread; ++t) {
-        const uint32_t key = score_key(v[t]);
-        const uint32_t bin = key >> 20;
-        const int64_t i = cv.index(t);
-        if (i < N && bin > j1) ir[oa++] = (int32_t)i;
-        if (i < N && bin == j1) st_cand(cr + oc++, make_uint2(key, (uint32_t)i));
-    }
+    for (int t = 0; t < kSelPerThread; ++t)
+        if (atb & (1u << t)) st_cand(cr + oc++, make_uint2(score_key(v[t]), cv.index32(t)));
     // The last chunk of the row to finish resolves the boundary bin, once
     // every block's candidate stores have completed.
     wait_vmem();
