@@ -9,7 +9,7 @@
 //
 //   zero    clears the level-1 histograms and the per-row state
 //   hist    one block per 32768-score chunk: per level-1 bin (score key bits
-//           [31:20]) the fp64 mass exp(s - top(bin)), top(bin)
+//           [31:20], 4096 bins) the fp64 mass exp(s - top(bin)), top(bin)
 //           being the bin's largest representable score, merged into the
 //           row's histogram with global atomics; the chunk's own top bin is
 //           kept apart, as mass exp(s - m_b) with m_b the chunk max, so every
@@ -40,7 +40,10 @@ namespace rtp {
 constexpr int kSelThreads = 1024;
 constexpr int kSelPerThread = 32;
 constexpr int kSelChunk = kSelThreads * kSelPerThread;  // scores per block
-constexpr int kBins1 = 4096;
+constexpr int kShift1 = 20;                  // level-1 bin = score key bits [31:20]
+constexpr int kBins1 = 1 << (32 - kShift1);  // 4096 bins
+constexpr int kShift2 = 10;                  // refinement digits: key bits [19:10], [9:0]
+constexpr int kDig = 1 << kShift2;           // 1024 digits per refinement level
 constexpr int kPickThreads = 1024;
 constexpr int kZeroBlocks = 64;
 constexpr int kResThreads = 1024;
@@ -64,6 +67,11 @@ struct Hist1 {                 // level-1 histogram of one row; masses are
     double mass[kBins1];       // relative to each bin's top score
 };
 
+struct Hist2 {                 // the boundary bin's candidates by key bits
+    double mass[kDig];         // [19:10]: mass exp(s - M) and count, built
+    uint32_t cnt[kDig];        // by the emit blocks
+};
+
 struct ChunkTop {              // a chunk's top bin, kept out of Hist1
     float m;                   // chunk max
     uint32_t pad;
@@ -79,6 +87,8 @@ SelLayout sel_layout(int64_t R, int64_t N)
     off += align_up((size_t)R * sizeof(SelRow), 256);
     L.hist1 = off;
     off += align_up((size_t)R * sizeof(Hist1), 256);
+    L.hist2 = off;
+    off += align_up((size_t)R * sizeof(Hist2), 256);
     L.zero_end = off;
     L.tops = off;
     off += align_up((size_t)R * L.nblk * sizeof(ChunkTop), 256);
@@ -91,6 +101,7 @@ SelLayout sel_layout(int64_t R, int64_t N)
 struct SelPtrs {
     SelRow *rows;
     Hist1 *hist1;
+    Hist2 *hist2;
     ChunkTop *tops;
     uint2 *cand;
     uint4 *zero;
@@ -105,6 +116,7 @@ static SelPtrs sel_ptrs(void *ws, int64_t R, int64_t N)
     SelPtrs P;
     P.rows = reinterpret_cast<SelRow *>(base + L.rows);
     P.hist1 = reinterpret_cast<Hist1 *>(base + L.hist1);
+    P.hist2 = reinterpret_cast<Hist2 *>(base + L.hist2);
     P.tops = reinterpret_cast<ChunkTop *>(base + L.tops);
     P.cand = reinterpret_cast<uint2 *>(base + L.cand);
     P.zero = reinterpret_cast<uint4 *>(base + L.rows);
@@ -128,7 +140,10 @@ __device__ __forceinline__ void st_cand(uint2 *p, uint2 e)
 
 // Largest finite score whose key lies in level-1 bin `bin` (bins that hold
 // finite scores only).
-__device__ __forceinline__ float bin_top(uint32_t bin) { return key_score((bin << 20) | 0xFFFFFu); }
+__device__ __forceinline__ float bin_top(uint32_t bin)
+{
+    return key_score((bin << kShift1) | ((1u << kShift1) - 1u));
+}
 
 // One chunk of a score row in registers.  Full chunks of 16-B aligned rows
 // use 16-B loads (slot t of thread x: element c0 + ((t/4)*256 + x)*4 + t%4);
@@ -225,12 +240,12 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
     __syncthreads();
     float mb = red[0];
     for (int i = 1; i < kSelThreads / kWave; ++i) mb = fmaxf(mb, red[i]);
-    const uint32_t tb = score_key(mb) >> 20;
+    const uint32_t tb = score_key(mb) >> kShift1;
     const double mbd = (double)mb;
 #pragma unroll 8
     for (int t = 0; t < kSelPerThread; ++t) {
         if (v[t] == -INFINITY) continue;  // past the end of the row
-        const uint32_t bin = score_key(v[t]) >> 20;
+        const uint32_t bin = score_key(v[t]) >> kShift1;
         const double ref = bin == tb ? mbd : (double)bin_top(bin);
         atomicAdd(&hm[bin], exp_tang((double)v[t] - ref, S.etbl));
     }
@@ -303,10 +318,10 @@ __device__ void pick_row(SelPtrs P, int64_t r, float p, PickShared &S)
     }
     __syncthreads();
     if (tid < P.nblk)
-        atomicAdd(&hm[score_key(tm0) >> 20], tmass0 * exp_tang((double)tm0 - M, S.etbl));
+        atomicAdd(&hm[score_key(tm0) >> kShift1], tmass0 * exp_tang((double)tm0 - M, S.etbl));
     for (int k = tid + kPickThreads; k < P.nblk; k += kPickThreads) {
         const float tm = ld_agent(&tops[k].m);
-        atomicAdd(&hm[score_key(tm) >> 20], ld_agent(&tops[k].mass) * exp_tang((double)tm - M, S.etbl));
+        atomicAdd(&hm[score_key(tm) >> kShift1], ld_agent(&tops[k].mass) * exp_tang((double)tm - M, S.etbl));
     }
     __syncthreads();
 
@@ -398,23 +413,24 @@ struct ResShared {
 };
 
 // Wave 0 chooses the boundary digit of a score level from S.hm/S.hc over
-// digits 0..1023: the highest non-empty digit whose running mass (A plus
+// digits 0..kDig-1: the highest non-empty digit whose running mass (A plus
 // every digit down to and including it) reaches T -- a test no rounding of
 // the parallel prefix can skip -- or, if the total stays below T, the
-// lowest non-empty digit.  Lane l owns digits 1023 - 16l - [0, 16).
+// lowest non-empty digit.  Lane l owns digits kDig - 1 - 16l - [0, 16).
 __device__ void res_choose_mass(double A, double T, ResShared &S)
 {
     const int lane = lane_id();
-    const int top = 1023 - 16 * lane;
+    constexpr int kPerLane = kDig / kWave;
+    const int top = kDig - 1 - kPerLane * lane;
     double local = 0.0;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) local += S.hm[top - k];
+    for (int k = 0; k < kPerLane; ++k) local += S.hm[top - k];
     const double inc = wave_inclusive_scan(local);
     double cum = A + (inc - local);
     int cross = -1, low = -1;
     double cross_b = 0.0, low_b = 0.0;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kPerLane; ++k) {
         const int d = top - k;
         const double w = S.hm[d];
         if (S.hc[d]) {
@@ -534,46 +550,52 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
     const int tid = threadIdx.x;
     const uint32_t emitted = (uint32_t)(slots >> 32);  // kept by emit
     int32_t *ir = idx + r * (int64_t)N + emitted;
-    bool in_lds = n <= kResCap;
-    int cur = 0;  // LDS buffer holding the candidates
+    bool in_lds = false;  // candidates start in global memory
+    int cur = 0;          // LDS buffer holding them once they fit
     if (tid == 0) S.nout = 0u;
-    if (in_lds)
-        for (int64_t k = tid; k < n; k += kResThreads) S.buf[0][k] = ld_cand(gc + k);
-    __syncthreads();
-    const uint2 *cr = in_lds ? S.buf[0] : gc;
-    // Candidate k from LDS, or from global memory for rows too large for it.
+    const uint2 *cr = gc;
+    // Candidate k from LDS, or from global memory.
     auto cand = [&](int64_t k) { return in_lds ? cr[k] : ld_cand(cr + k); };
 
-    // Score levels: key bits [19:10], then [9:0].
+    // Score levels: key bits [19:10] (histogram built by the emit blocks),
+    // then [9:0] (histogram of the survivors).
+    static_assert(kResThreads == kDig, "one digit per thread");
+    const Hist2 &h2 = P.hist2[r];
     for (int level = 0; level < 2 && n > 0; ++level) {
-        const int shift = level == 0 ? 10 : 0;
-        S.hm[tid] = 0.0;
-        S.hc[tid] = 0u;
-        __syncthreads();
-        for (int64_t k = tid; k < n; k += kResThreads) {
-            const uint32_t key = cand(k).x;
-            const uint32_t dg = (key >> shift) & 1023u;
-            atomicAdd(&S.hm[dg], exp_tang((double)key_score(key) - M, S.etbl));
-            atomicAdd(&S.hc[dg], 1u);
+        const int shift = level == 0 ? kShift2 : 0;
+        if (level == 0) {
+            S.hm[tid] = ld_agent(&h2.mass[tid]);
+            S.hc[tid] = ld_agent(&h2.cnt[tid]);
+            __syncthreads();
+        } else {
+            S.hm[tid] = 0.0;
+            S.hc[tid] = 0u;
+            __syncthreads();
+            for (int64_t k = tid; k < n; k += kResThreads) {
+                const uint32_t key = cand(k).x;
+                const uint32_t dg = (key >> shift) & (uint32_t)(kDig - 1);
+                atomicAdd(&S.hm[dg], exp_tang((double)key_score(key) - M, S.etbl));
+                atomicAdd(&S.hc[dg], 1u);
+            }
+            __syncthreads();
         }
-        __syncthreads();
         if (tid < kWave) res_choose_mass(A, T, S);
         __syncthreads();
         const uint32_t j = S.j;
         A = S.abefore;  // A plus the mass of the digits above j
         if (in_lds) {
-            n = res_filter_lds<false>(S.buf[cur], n, S.buf[cur ^ 1], shift, 1023u, j, true,
+            n = res_filter_lds<false>(S.buf[cur], n, S.buf[cur ^ 1], shift, kDig - 1, j, true,
                                       false, ir, S);
             cur ^= 1;
             cr = S.buf[cur];
         } else if (S.hc[j] <= (uint32_t)kResCap) {
             // The boundary digit's candidates fit in LDS: continue there.
-            n = res_filter_lds<true>(gc, n, S.buf[0], shift, 1023u, j, true, false, ir, S);
+            n = res_filter_lds<true>(gc, n, S.buf[0], shift, kDig - 1, j, true, false, ir, S);
             in_lds = true;
             cur = 0;
             cr = S.buf[0];
         } else {
-            n = res_filter_global(gc, n, shift, 1023u, j, true, false, ir, S);
+            n = res_filter_global(gc, n, shift, kDig - 1, j, true, false, ir, S);
         }
     }
 
@@ -657,13 +679,15 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     float v[kSelPerThread];
     const ChunkView cv = load_chunk(sr, N, (int64_t)blockIdx.x * kSelChunk, v);
     if (threadIdx.x == 0) S.bcount = 0ull;
+    S.hm[threadIdx.x] = 0.0;  // this block's share of the row's Hist2
+    S.hc[threadIdx.x] = 0u;
     // Per lane: bit t of `above` / `atb` marks slot t as kept / candidate;
     // `mine` packs their counts (kept in the high half).
     static_assert(kSelPerThread == 32, "one mask bit per slot");
     uint32_t above = 0, atb = 0;
 #pragma unroll
     for (int t = 0; t < kSelPerThread; ++t) {
-        const uint32_t bin = score_key(v[t]) >> 20;
+        const uint32_t bin = score_key(v[t]) >> kShift1;
         const bool valid = cv.vec || cv.index32(t) < (uint32_t)N;
         above |= (valid && bin > j1) ? (1u << t) : 0u;
         atb |= (valid && bin == j1) ? (1u << t) : 0u;
@@ -687,11 +711,42 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     const unsigned long long base = S.gbase + wbase[w];
     const uint32_t ex = inc - mine;
     uint32_t oa = (uint32_t)(base >> 32) + (ex >> 16);
-    uint32_t oc = (uint32_t)base + (ex & 0xFFFFu);
     for (uint32_t m = above; m; m &= m - 1) ir[oa++] = (int32_t)cv.index32(__ffs(m) - 1);
+    // Candidates: staged in LDS in block order (the resolve's buffers are
+    // free until then), then written out coalesced; a block with more
+    // candidates than the stage holds writes them directly.
+    const uint32_t bc = (uint32_t)S.bcount;                 // this block's candidates
+    uint2 *gcb = cr + (uint32_t)S.gbase;                      // ... their place in the row
+    uint2 *stage = &S.buf[0][0];
+    const bool staged = bc <= (uint32_t)(2 * kResCap);
+    uint32_t oc = (uint32_t)wbase[w] + (ex & 0xFFFFu);
 #pragma unroll
-    for (int t = 0; t < kSelPerThread; ++t)
-        if (atb & (1u << t)) st_cand(cr + oc++, make_uint2(score_key(v[t]), cv.index32(t)));
+    for (int t = 0; t < kSelPerThread; ++t) {
+        if (!(atb & (1u << t))) continue;
+        const uint2 e = make_uint2(score_key(v[t]), cv.index32(t));
+        if (staged)
+            stage[oc++] = e;
+        else
+            st_cand(gcb + oc++, e);
+    }
+    wait_vmem();
+    __syncthreads();
+    // This block's share of the row's Hist2: candidates by key bits
+    // [19:10], with mass exp(s - M).
+    const double M = (double)P.rows[r].M;
+    for (uint32_t k = threadIdx.x; k < bc; k += kSelThreads) {
+        const uint2 e = staged ? stage[k] : ld_cand(gcb + k);
+        if (staged) st_cand(gcb + k, e);
+        const uint32_t dg = (e.x >> kShift2) & (uint32_t)(kDig - 1);
+        atomicAdd(&S.hm[dg], exp_tang((double)key_score(e.x) - M, S.etbl));
+        atomicAdd(&S.hc[dg], 1u);
+    }
+    __syncthreads();
+    if (S.hc[threadIdx.x]) {
+        Hist2 &h2 = P.hist2[r];
+        atomicAdd(&h2.mass[threadIdx.x], S.hm[threadIdx.x]);
+        atomicAdd(&h2.cnt[threadIdx.x], S.hc[threadIdx.x]);
+    }
     // The last chunk of the row to finish resolves the boundary bin, once
     // every block's candidate stores have completed.
     wait_vmem();
