@@ -519,17 +519,26 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
                                    uint32_t mask, uint32_t j, bool emit_above, bool by_index,
                                    int32_t *ir, ResShared &S)
 {
+    // From global memory, kB loads per thread are in flight before any is used.
+    constexpr int kB = kGlobal ? 8 : 1;
     if (threadIdx.x == 0) S.nnext = 0u;
     __syncthreads();
-    for (int64_t c0 = 0; c0 < n; c0 += kResThreads) {
-        const int64_t k = c0 + threadIdx.x;
-        const bool valid = k < n;
-        const uint2 e = valid ? (kGlobal ? ld_cand(src + k) : src[k]) : make_uint2(0, 0);
-        const uint32_t dg = ((by_index ? e.y : e.x) >> shift) & mask;
-        const int64_t pa = wave_append(valid && (emit_above ? dg > j : dg < j), &S.nout);
-        if (pa >= 0) ir[pa] = (int32_t)e.y;
-        const int64_t pk = wave_append(valid && dg == j, &S.nnext);
-        if (pk >= 0) dst[pk] = e;
+    for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kResThreads * kB) {
+        uint2 e[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int64_t k = c0 + (int64_t)u * kResThreads + threadIdx.x;
+            e[u] = k < n ? (kGlobal ? ld_cand(src + k) : src[k]) : make_uint2(0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const bool valid = c0 + (int64_t)u * kResThreads + threadIdx.x < n;
+            const uint32_t dg = ((by_index ? e[u].y : e[u].x) >> shift) & mask;
+            const int64_t pa = wave_append(valid && (emit_above ? dg > j : dg < j), &S.nout);
+            if (pa >= 0) ir[pa] = (int32_t)e[u].y;
+            const int64_t pk = wave_append(valid && dg == j, &S.nnext);
+            if (pk >= 0) dst[pk] = e[u];
+        }
     }
     __syncthreads();
     return S.nnext;
