@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--p", type=float, default=0.9)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-side-stream", action="store_true")
+    ap.add_argument("--sparse-mode", choices=["union", "per_head"], default="per_head",
+                    help="union: each kept row read once per KV head for all its query heads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -99,7 +101,8 @@ def main():
     del stage
     log(f"inputs resident ({time.time() - t0:.1f}s)")
 
-    step_layer = DecodeLayer(B, Hq, Hkv, N, H_r, cfg.n_sink, cfg.window, dev)
+    step_layer = DecodeLayer(B, Hq, Hkv, N, H_r, cfg.n_sink, cfg.window, dev,
+                             mode=args.sparse_mode)
     scale = cfg.scale
 
     # Local heads of a layer run on a side stream, overlapping the retrieval
@@ -157,13 +160,22 @@ def main():
     us = {
         "rtp_index_scores": time_call(lambda: [rtp.rtp_index_scores(qr_all[l], kr_all[l], sl.scores)
                                                 for l in range(L)]),
-        "rtp_topp_select": time_call(lambda: [rtp.rtp_topp_select(sl.scores, p, sl.idx, sl.count, sl.ws_sel)
+        "rtp_topp_select": time_call(lambda: [rtp.rtp_topp_select(sl.scores, p, sl.idx, sl.count, sl.ws_sel,
+                                                                  keep_bits=sl.keep_bits)
                                                for l in range(L)]),
-        "rtp_sparse_decode": time_call(lambda: [rtp.rtp_sparse_decode(q_all[l], K_all[l], V_all[l], sl.idx, sl.count, 0, scale, out_all[l], sl.ws_sparse)
-                                                 for l in range(L)]),
+    }
+    if sl.mode == "union":
+        us["rtp_sparse_decode_union"] = time_call(lambda: [rtp.rtp_sparse_decode_union(
+            q_all[l], K_all[l], V_all[l], sl.keep_bits, N, 0, scale, out_all[l], sl.ws_sparse)
+            for l in range(L)])
+    else:
+        us["rtp_sparse_decode"] = time_call(lambda: [rtp.rtp_sparse_decode(
+            q_all[l], K_all[l], V_all[l], sl.idx, sl.count, 0, scale, out_all[l], sl.ws_sparse)
+            for l in range(L)])
+    us.update({
         "rtp_local_decode": time_call(lambda: [rtp.rtp_local_decode(q_all[l], K_all[l], V_all[l], N, H_r, Hq - H_r, cfg.n_sink, cfg.window, scale, out_all[l], sl.ws_local)
                                                 for l in range(L)]),
-    }
+    })
     log("per-call us/layer: " + ", ".join(f"{k}={v:.2f}" for k, v in us.items()))
 
     # --------------------------------------------- algorithmic bytes
@@ -226,6 +238,7 @@ def main():
                    "q_heads": Hq, "kv_heads": Hkv, "retrieval_q_heads": H_r,
                    "head_dim": d, "indexer_dim": cfg.r, "p": p, "sinks": cfg.n_sink,
                    "window": cfg.window, "kv_dtype": "bf16", "graph": not args.no_graph,
+                   "sparse_mode": args.sparse_mode,
                    "local_side_stream": side is not None},
         "B_alg_bytes": B_alg, "B_ns_bytes": B_ns,
         "achieved_GBps": round(achieved_gbps, 1),

@@ -56,7 +56,8 @@ typedef enum rtp_status {
 enum {
     RTP_WS_TOPP_SELECT = 1,
     RTP_WS_SPARSE_DECODE = 2,
-    RTP_WS_LOCAL_DECODE = 3
+    RTP_WS_LOCAL_DECODE = 3,
+    RTP_WS_SPARSE_UNION = 4
 };
 
 /*
@@ -96,13 +97,19 @@ rtp_status rtp_index_scores(const float *q_r, const float *k_r, float *scores,
  *                                in idx[b][h][0 .. count[b][h]), in no
  *                                particular order; the rest is untouched
  *   count      int32 [B][H]      out: size of each kept set (>= 1)
+ *   keep_bits  uint32 [B][H][ceil(N/32)]  optional out (NULL: not written):
+ *                                the same sets as a bitmap, bit i%32 of
+ *                                word i/32 set iff token i is kept; every
+ *                                word is written (no initialisation needed).
+ *                                rtp_sparse_decode_union reads it.
  *   workspace  device memory of at least
  *              rtp_workspace_size(RTP_WS_TOPP_SELECT, B, H, N) bytes,
  *              256-B aligned; contents need no initialisation.
  */
 rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H,
                            int32_t N, float p, int32_t *idx, int32_t *count,
-                           void *workspace, size_t ws_bytes, void *stream);
+                           uint32_t *keep_bits, void *workspace,
+                           size_t ws_bytes, void *stream);
 
 /*
  * rtp_sparse_decode -- exact attention of each retrieval query head over
@@ -134,6 +141,34 @@ rtp_status rtp_sparse_decode(const rtp_bf16 *q, const rtp_bf16 *K,
                              size_t ws_bytes, void *stream);
 
 /*
+ * rtp_sparse_decode_union -- the same attention as rtp_sparse_decode, with
+ * the kept sets given as keep bitmaps (as written by rtp_topp_select) and
+ * each K/V row read once for all query heads of its KV head that kept it
+ * (grouped-query attention: the heads of one KV head share its rows).
+ *
+ *   out[b][h][:] = sum_{i in S_h} softmax_{S_h}(scale * q[b][h] . K[b][g][i])
+ *                  * V[b][g][i][:],  g = h / (Hq/Hkv),
+ * with S_h = { i < N : bit i%32 of keep_bits[b][h - q_head_begin][i/32] },
+ * fp32 arithmetic, softmax renormalised over S_h.  Bits at or past N in the
+ * last word are ignored.  Every S_h must be non-empty.
+ *
+ *   q          bf16   [B][Hq][d]                 16-B aligned
+ *   K, V       bf16   [B][Hkv][kv_cap][d]        16-B aligned
+ *   keep_bits  uint32 [B][n_q_heads][ceil(N/32)] 4-B aligned
+ *   heads      q_head_begin .. q_head_begin + n_q_heads - 1 (within Hq)
+ *   out        fp32   [B][Hq][d]                 only the heads in range written
+ *   workspace  >= rtp_workspace_size(RTP_WS_SPARSE_UNION, B, n_q_heads, N)
+ *   d must be 128; 1 <= N <= kv_cap; scale finite.
+ */
+rtp_status rtp_sparse_decode_union(const rtp_bf16 *q, const rtp_bf16 *K,
+                                   const rtp_bf16 *V, const uint32_t *keep_bits,
+                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                                   int64_t kv_cap, int32_t d,
+                                   int32_t q_head_begin, int32_t n_q_heads,
+                                   float scale, float *out, void *workspace,
+                                   size_t ws_bytes, void *stream);
+
+/*
  * rtp_local_decode -- local heads: attention over the first n_sink cached
  * rows (attention sinks) plus the newest `window` rows, each row once
  * (gist.science summary, method section 1: local heads use a sliding window
@@ -159,6 +194,7 @@ rtp_status rtp_local_decode(const rtp_bf16 *q, const rtp_bf16 *K,
  *          RTP_WS_SPARSE_DECODE: H = n_q_heads
  *          RTP_WS_LOCAL_DECODE:  H = n_q_heads (sized for any n_sink,
  *                                window, since the row list is <= N)
+ *          RTP_WS_SPARSE_UNION:  H = n_q_heads
  * Returns RTP_ERR_VALUE for an unknown `which`, RTP_ERR_SHAPE for sizes < 1,
  * RTP_ERR_NULL when bytes is NULL.
  */

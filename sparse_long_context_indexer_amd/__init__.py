@@ -18,14 +18,15 @@ LIB_PATH = os.path.join(_PKG, "librtp.so")
 RTP_WS_TOPP_SELECT = 1
 RTP_WS_SPARSE_DECODE = 2
 RTP_WS_LOCAL_DECODE = 3
+RTP_WS_SPARSE_UNION = 4
 
 STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPPORTED",
           4: "RTP_ERR_VALUE", 5: "RTP_ERR_ALIGN", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
 
 # Every symbol include/rtp.h declares.
 SYMBOLS = ("rtp_index_scores", "rtp_topp_select", "rtp_sparse_decode",
-           "rtp_local_decode", "rtp_workspace_size", "rtp_status_string",
-           "rtp_last_hip_error")
+           "rtp_sparse_decode_union", "rtp_local_decode", "rtp_workspace_size",
+           "rtp_status_string", "rtp_last_hip_error")
 
 
 class RtpError(RuntimeError):
@@ -54,9 +55,11 @@ def lib() -> ctypes.CDLL:
         P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                 ctypes.c_float, ctypes.c_size_t)
         L.rtp_index_scores.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, P]
-        L.rtp_topp_select.argtypes = [P, I32, I32, I32, F32, P, P, P, SZ, P]
+        L.rtp_topp_select.argtypes = [P, I32, I32, I32, F32, P, P, P, P, SZ, P]
         L.rtp_sparse_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32,
                                         I32, I32, F32, P, P, SZ, P]
+        L.rtp_sparse_decode_union.argtypes = [P, P, P, P, I32, I32, I32, I32, I64, I32, I32,
+                                              I32, F32, P, P, SZ, P]
         L.rtp_local_decode.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, I32, I32,
                                        I32, I32, F32, P, P, SZ, P]
         L.rtp_workspace_size.argtypes = [I32, I32, I32, I32, ctypes.POINTER(SZ)]
@@ -64,7 +67,7 @@ def lib() -> ctypes.CDLL:
         L.rtp_status_string.restype = ctypes.c_char_p
         L.rtp_last_hip_error.argtypes = []
         L.rtp_last_hip_error.restype = I32
-        for name in SYMBOLS[:5]:
+        for name in SYMBOLS[:6]:
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -129,14 +132,25 @@ def rtp_index_scores(q_r, k_r, scores, stream=None) -> None:
         _stream(q_r, stream)), "rtp_index_scores")
 
 
-def rtp_topp_select(scores, p, idx, count, workspace, stream=None) -> None:
+def keep_words(N: int) -> int:
+    """32-bit words per row of a keep bitmap over N tokens."""
+    return (N + 31) // 32
+
+
+def rtp_topp_select(scores, p, idx, count, workspace, keep_bits=None, stream=None) -> None:
     """scores f32 [B][H][N]; idx i32 [B][H][N] (out); count i32 [B][H] (out);
-    workspace uint8 [>= workspace_size(RTP_WS_TOPP_SELECT, B, H, N)]."""
+    keep_bits i32 [B][H][keep_words(N)] (optional out, the same sets as
+    bitmaps); workspace uint8 [>= workspace_size(RTP_WS_TOPP_SELECT, B, H, N)]."""
     import torch
     B, H, N = scores.shape
+    kb = None
+    if keep_bits is not None:
+        if tuple(keep_bits.shape) != (B, H, keep_words(N)):
+            raise ValueError(f"keep_bits must have shape {(B, H, keep_words(N))}")
+        kb = _dev(keep_bits, torch.int32, "keep_bits", 3)
     _check(lib().rtp_topp_select(
         _dev(scores, torch.float32, "scores", 3), B, H, N, float(p),
-        _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2),
+        _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2), kb,
         _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
         _stream(scores, stream)), "rtp_topp_select")
 
@@ -156,6 +170,24 @@ def rtp_sparse_decode(q, K, V, idx, count, q_head_begin, scale, out, workspace,
         B, Hq, Hkv, N, cap, d, q_head_begin, n_q, float(scale),
         _dev(out, torch.float32, "out", 3), _dev(workspace, torch.uint8, "workspace", 1),
         workspace.numel(), _stream(q, stream)), "rtp_sparse_decode")
+
+
+def rtp_sparse_decode_union(q, K, V, keep_bits, N, q_head_begin, scale, out, workspace,
+                            stream=None) -> None:
+    """q bf16 [B][Hq][d]; K, V bf16 [B][Hkv][cap][d]; keep_bits i32
+    [B][n_q][keep_words(N)] as written by rtp_topp_select; out f32 [B][Hq][d]."""
+    import torch
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    n_q = keep_bits.shape[1]
+    if tuple(keep_bits.shape) != (B, n_q, keep_words(N)):
+        raise ValueError(f"keep_bits must have shape {(B, n_q, keep_words(N))}")
+    _check(lib().rtp_sparse_decode_union(
+        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4),
+        _dev(keep_bits, torch.int32, "keep_bits", 3), B, Hq, Hkv, N, cap, d, q_head_begin, n_q,
+        float(scale), _dev(out, torch.float32, "out", 3),
+        _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(), _stream(q, stream)),
+        "rtp_sparse_decode_union")
 
 
 def rtp_local_decode(q, K, V, N, q_head_begin, n_q_heads, n_sink, window, scale, out,

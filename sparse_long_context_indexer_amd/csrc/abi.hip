@@ -72,6 +72,7 @@ rtp_status rtp_workspace_size(int32_t which, int32_t B, int32_t H, int32_t N, si
     case RTP_WS_TOPP_SELECT: *bytes = rtp::sel_layout((int64_t)B * H, N).total; return RTP_OK;
     case RTP_WS_SPARSE_DECODE: *bytes = rtp::sparse_ws_bytes(B, H, N); return RTP_OK;
     case RTP_WS_LOCAL_DECODE: *bytes = rtp::local_ws_bytes(B, H, N); return RTP_OK;
+    case RTP_WS_SPARSE_UNION: *bytes = rtp::union_ws_bytes(B, H, N); return RTP_OK;
     default: return RTP_ERR_VALUE;
     }
 }
@@ -92,17 +93,18 @@ rtp_status rtp_index_scores(const float *q_r, const float *k_r, float *scores, i
 }
 
 rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H, int32_t N, float p,
-                           int32_t *idx, int32_t *count, void *workspace, size_t ws_bytes,
-                           void *stream)
+                           int32_t *idx, int32_t *count, uint32_t *keep_bits, void *workspace,
+                           size_t ws_bytes, void *stream)
 {
     if (!scores || !idx || !count || !workspace) return RTP_ERR_NULL;
     if (B < 1 || H < 1 || N < 1 || (int64_t)B * H > kMaxGridY) return RTP_ERR_SHAPE;
     if (!(p > 0.0f && p <= 1.0f)) return RTP_ERR_VALUE;  // NaN fails too
-    if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(count, 4) || !aligned(workspace, 256))
+    if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(count, 4) ||
+        !aligned(keep_bits, 4) || !aligned(workspace, 256))
         return RTP_ERR_ALIGN;
     const int64_t R = (int64_t)B * H;
     if (ws_bytes < rtp::sel_layout(R, N).total) return RTP_ERR_WORKSPACE;
-    return from_hip(rtp::launch_topp_select(scores, R, N, p, idx, count, workspace,
+    return from_hip(rtp::launch_topp_select(scores, R, N, p, idx, count, keep_bits, workspace,
                                             as_stream(stream)));
 }
 
@@ -121,6 +123,26 @@ rtp_status rtp_sparse_decode(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf1
     return from_hip(rtp::launch_sparse_decode(q, K, V, idx, count, B, Hq, Hkv, N, kv_cap,
                                               q_head_begin, n_q_heads, scale, out, workspace,
                                               as_stream(stream)));
+}
+
+rtp_status rtp_sparse_decode_union(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,
+                                   const uint32_t *keep_bits, int32_t B, int32_t Hq,
+                                   int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,
+                                   int32_t q_head_begin, int32_t n_q_heads, float scale,
+                                   float *out, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!keep_bits) return RTP_ERR_NULL;
+    rtp_status st = check_attention_common(q, K, V, out, workspace, B, Hq, Hkv, N, kv_cap, d,
+                                           q_head_begin, n_q_heads, scale);
+    if (st != RTP_OK) return st;
+    if (!aligned(keep_bits, 4)) return RTP_ERR_ALIGN;
+    const int64_t G = Hq / Hkv;
+    const int64_t groups = ((int64_t)q_head_begin + n_q_heads - 1) / G - q_head_begin / G + 1;
+    if (groups * ((G + 7) / 8) > kMaxGridY) return RTP_ERR_SHAPE;
+    if (ws_bytes < rtp::union_ws_bytes(B, n_q_heads, N)) return RTP_ERR_WORKSPACE;
+    return from_hip(rtp::launch_sparse_decode_union(q, K, V, keep_bits, B, Hq, Hkv, N, kv_cap,
+                                                    q_head_begin, n_q_heads, scale, out,
+                                                    workspace, as_stream(stream)));
 }
 
 rtp_status rtp_local_decode(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V, int32_t B,

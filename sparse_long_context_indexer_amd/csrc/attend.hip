@@ -370,43 +370,35 @@ hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint
                   scale * kLog2e, W, out);
 }
 
-// ------------------------------------------------------------- local
+// ------------------------------------------- 8 query heads per KV row
+//
+// Local heads and the union mode of sparse heads read each K/V row once for
+// all (up to 8) query heads of its KV head that attend it.  A row is spread
+// over 16 lanes (8 bf16 each); each lane forms 8 partial dot products, and a
+// butterfly over the 16 lanes reduces all 8 in 8 exchanges (each step
+// halves the heads a lane carries).  Each block produces one partial
+// (max, sum, o[128]) per head for its split; splits are merged in two levels
+// inside the kernel, as for the per-head sparse kernel.
 
-static int64_t local_rows_count(int N, int n_sink, int window)
-{
-    const int64_t w_start = N > window ? (int64_t)N - window : 0;
-    const int64_t sink_end = n_sink < w_start ? n_sink : w_start;
-    return sink_end + (N - w_start);
-}
-
-int local_splits(int64_t n_rows)
-{
-    int64_t s = (n_rows + kLocalRows - 1) / kLocalRows;
-    return (int)(s < 1 ? 1 : (s > kMaxLocalSplits ? kMaxLocalSplits : s));
-}
-
-constexpr int kLocalSlice = 16;  // split partials merged per block, first level
-constexpr int kMaxLocalSlices = (kMaxLocalSplits + kLocalSlice - 1) / kLocalSlice;
-
-struct LocalWs {
-    float *part;                    // [B*n_q][S] per-split partials
-    float *super;                   // [B*n_q][kMaxLocalSlices] slice merges
-    unsigned long long *slice_ctr;  // [B*n_q][kMaxLocalSlices], by a chunk's first head
-    unsigned long long *group_ctr;  // [B*n_q]
+struct GroupWs {
+    float *part;                    // [R][S] per-split partials
+    float *super;                   // [R][max_slices] slice merges
+    unsigned long long *slice_ctr;  // [R][max_slices], by a chunk's first head row
+    unsigned long long *group_ctr;  // [R]
+    int slice;                      // splits merged per block, first level
+    int max_slices;
 };
 
-// The row list never exceeds N rows, so sizing with N bounds every
-// n_sink / window.
-static size_t local_ws_layout(int64_t B, int64_t n_q, int N, LocalWs *W, void *base)
+static size_t group_ws_layout(int64_t R, int max_splits, int slice, GroupWs *W, void *base)
 {
-    const int64_t R = B * n_q;
+    const int max_slices = (max_splits + slice - 1) / slice;
     size_t off = 0;
     const size_t part = off;
-    off += align_up((size_t)R * local_splits(N) * kPart * sizeof(float), 256);
+    off += align_up((size_t)R * max_splits * kPart * sizeof(float), 256);
     const size_t sup = off;
-    off += align_up((size_t)R * kMaxLocalSlices * kPart * sizeof(float), 256);
+    off += align_up((size_t)R * max_slices * kPart * sizeof(float), 256);
     const size_t sc = off;
-    off += align_up((size_t)R * kMaxLocalSlices * sizeof(unsigned long long), 256);
+    off += align_up((size_t)R * max_slices * sizeof(unsigned long long), 256);
     const size_t gc = off;
     off += align_up((size_t)R * sizeof(unsigned long long), 256);
     if (W) {
@@ -415,38 +407,56 @@ static size_t local_ws_layout(int64_t B, int64_t n_q, int N, LocalWs *W, void *b
         W->super = reinterpret_cast<float *>(b + sup);
         W->slice_ctr = reinterpret_cast<unsigned long long *>(b + sc);
         W->group_ctr = reinterpret_cast<unsigned long long *>(b + gc);
+        W->slice = slice;
+        W->max_slices = max_slices;
     }
     return off;
 }
 
-size_t local_ws_bytes(int64_t B, int64_t n_q, int N)
-{
-    return local_ws_layout(B, n_q, N, nullptr, nullptr);
-}
-
-// Merges n <= kLocalSlice partials for each of nh <= 8 heads at once:
-// thread t takes head t/32 and output dimensions 4*(t%32) .. +3.  Head hh's
-// partials start at first + hh*head_stride (floats), kPart apart.  Writes
-// merged partials (dst_part, same head stride) or output rows (dst_out,
-// 128 apart).
+// Merges n partials for each of nh <= 8 heads at once: thread t takes head
+// t/32 and output dimensions 4*(t%32) .. +3.  Head hh's partials start at
+// first + hh*head_stride (floats), kPart apart.  Writes merged partials
+// (dst_part, same head stride) or output rows (dst_out, 128 apart).
 __device__ void merge_heads(const float *first, int64_t head_stride, int n, int nh,
                             float *dst_part, int64_t dst_stride, float *dst_out)
 {
     const int hh = threadIdx.x >> 5, d = (threadIdx.x & 31) * 4;
     if (hh >= nh) return;
     const float *src = first + hh * head_stride;
-    float M = -INFINITY;
-#pragma unroll 16
-    for (int k = 0; k < n; ++k) M = fmaxf(M, ld_agent(src + (int64_t)k * kPart));
-    float L = 0.0f;
+    // One pass: kB partials loaded together, merged with a running max.
+    constexpr int kB = 8;
+    float M = -INFINITY, L = 0.0f;
     float O[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 16
-    for (int k = 0; k < n; ++k) {
-        const float *pk = src + (int64_t)k * kPart;
-        const float f = rescale(ld_agent(pk), M);
-        L = fmaf(ld_agent(pk + 1), f, L);
+    for (int k0 = 0; k0 < n; k0 += kB) {
+        float pm[kB], pl[kB];
+        float4 po[kB];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) O[e] = fmaf(ld_agent(pk + 4 + d + e), f, O[e]);
+        for (int u = 0; u < kB; ++u) {
+            const bool ok = k0 + u < n;
+            const float *pk = src + (int64_t)(ok ? k0 + u : k0) * kPart;
+            pm[u] = ok ? ld_agent(pk) : -INFINITY;
+            pl[u] = ld_agent(pk + 1);
+            po[u] = make_float4(ld_agent(pk + 4 + d), ld_agent(pk + 5 + d), ld_agent(pk + 6 + d),
+                                ld_agent(pk + 7 + d));
+        }
+        float mb = M;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) mb = fmaxf(mb, pm[u]);
+        if (mb == -INFINITY) continue;
+        const float c = rescale(M, mb);
+        L *= c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[e] *= c;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const float f = rescale(pm[u], mb);
+            L = fmaf(pl[u], f, L);
+            O[0] = fmaf(po[u].x, f, O[0]);
+            O[1] = fmaf(po[u].y, f, O[1]);
+            O[2] = fmaf(po[u].z, f, O[2]);
+            O[3] = fmaf(po[u].w, f, O[3]);
+        }
+        M = mb;
     }
     if (dst_out) {
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -464,26 +474,249 @@ __device__ void merge_heads(const float *first, int64_t head_stride, int n, int 
     }
 }
 
-// Block (s, y, b): KV head g = g_first + y / chunks_per_g, query heads
-// [h_lo, h_hi) of that head within the local range (at most 8), rows of
-// split s of the local row list.
+// Per-lane state of the 8-head online softmax.  A row is spread over 16
+// lanes (8 bf16 each, one 16-B load); each lane forms 8 partial dot
+// products, and a butterfly over the 16 lanes reduces all 8 in 8 exchanges
+// (each step halves the heads a lane carries).  A wave works on 4 rows at a
+// time, kLocalU times over, before it updates the softmax state.
+struct Heads8 {
+    float qf[8][8];  // q * scale * log2(e), this lane's 8 dimensions
+    float m[8], l[8], o[8][8];
+    int b3, b2, b1;  // lane bits of the butterfly
+};
+
+__device__ __forceinline__ void heads8_init(Heads8 &st, const uint16_t *__restrict__ q, int64_t q0,
+                                            int nh, float qscale, int sub)
+{
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+        if (hh < nh) {
+            const uint4 qw = *reinterpret_cast<const uint4 *>(q + q0 + hh * 128 + sub * 8);
+            bf16x8_to_f32(qw, st.qf[hh]);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st.qf[hh][c] *= qscale;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st.qf[hh][c] = 0.0f;
+        }
+        st.m[hh] = -INFINITY;
+        st.l[hh] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st.o[hh][c] = 0.0f;
+    }
+    st.b3 = (sub >> 3) & 1;
+    st.b2 = (sub >> 2) & 1;
+    st.b1 = (sub >> 1) & 1;
+}
+
+// One online-softmax step over kLocalU rows of this lane group: kw/vw hold
+// the rows' K and V (8 bf16 per lane), bit hh of hb[u] says whether head hh
+// attends row u.
+__device__ __forceinline__ void heads8_step(Heads8 &st, const uint4 (&kw)[kLocalU],
+                                            const uint4 (&vw)[kLocalU],
+                                            const uint32_t (&hb)[kLocalU])
+{
+    float lg[kLocalU][8];
+#pragma unroll
+    for (int u = 0; u < kLocalU; ++u) {
+        float kf[8];
+        bf16x8_to_f32(kw[u], kf);
+        float d[8];
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            float a = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) a = fmaf(st.qf[hh][c], kf[c], a);
+            d[hh] = a;
+        }
+        // Butterfly: after the steps over lane bits 3, 2, 1 a lane holds
+        // one head, 4*b3 + 2*b2 + b1, summed over 8 lanes; bit 0 finishes.
+        float d4[4], d2[2], d1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float send = st.b3 ? d[k] : d[k + 4];
+            const float keep = st.b3 ? d[k + 4] : d[k];
+            d4[k] = keep + __shfl_xor(send, 8, 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float send = st.b2 ? d4[k] : d4[k + 2];
+            const float keep = st.b2 ? d4[k + 2] : d4[k];
+            d2[k] = keep + __shfl_xor(send, 4, 16);
+        }
+        {
+            const float send = st.b1 ? d2[0] : d2[1];
+            const float keep = st.b1 ? d2[1] : d2[0];
+            d1 = keep + __shfl_xor(send, 2, 16);
+        }
+        d1 += __shfl_xor(d1, 1, 16);
+        // Head hh's logit sits in lanes 2*hh and 2*hh + 1 of the group.
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            const float v = __shfl(d1, 2 * hh, 16);
+            lg[u][hh] = (hb[u] >> hh) & 1u ? v : -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+        float mx = lg[0][hh];
+#pragma unroll
+        for (int u = 1; u < kLocalU; ++u) mx = fmaxf(mx, lg[u][hh]);
+        const float mn = fmaxf(st.m[hh], mx);
+        if (mn == -INFINITY) continue;
+        const float corr = rescale(st.m[hh], mn);
+        st.l[hh] *= corr;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st.o[hh][c] *= corr;
+        st.m[hh] = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < kLocalU; ++u) {
+        float vf[8];
+        bf16x8_to_f32(vw[u], vf);
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            const float pw = (hb[u] >> hh) & 1u ? exp2f(lg[u][hh] - st.m[hh]) : 0.0f;
+            st.l[hh] += pw;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st.o[hh][c] = fmaf(pw, vf[c], st.o[hh][c]);
+        }
+    }
+}
+
+struct Heads8Shared {
+    float wm[kAttThreads / kWave][8], wl[kAttThreads / kWave][8];
+    float wo[kAttThreads / kWave][8][128];
+    int last;
+};
+
+// Merges the block's lane groups and waves into one partial per head for
+// split s of S, then
+// merges the splits: the last block of a slice merges the slice, the last
+// slice merger writes out[b][h_lo .. h_lo + nh).  Rows of the partials are
+// R = B * n_q, head row r0 = b * n_q + (h_lo - q_head_begin).
+__device__ void heads8_finish(Heads8 &st, Heads8Shared &sh, int nh, int s, int S, int64_t r0,
+                              const GroupWs &W, float *dst)
+{
+    const int lane = lane_id(), w = threadIdx.x / kWave, sub = lane & 15;
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+#pragma unroll
+        for (int off = 16; off < kWave; off <<= 1) {
+            const float mo = __shfl_xor(st.m[hh], off);
+            const float lo = __shfl_xor(st.l[hh], off);
+            const float mn = fmaxf(st.m[hh], mo);
+            const float a = rescale(st.m[hh], mn), bb = rescale(mo, mn);
+            st.l[hh] = st.l[hh] * a + lo * bb;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float oo = __shfl_xor(st.o[hh][c], off);
+                st.o[hh][c] = st.o[hh][c] * a + oo * bb;
+            }
+            st.m[hh] = mn;
+        }
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sh.wo[w][hh][sub * 8 + c] = st.o[hh][c];
+            if (lane == 0) {
+                sh.wm[w][hh] = st.m[hh];
+                sh.wl[w][hh] = st.l[hh];
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nh * 128; e += kAttThreads) {
+        const int hh = e / 128, c = e % 128;
+        float M = -INFINITY;
+        for (int i = 0; i < kAttThreads / kWave; ++i) M = fmaxf(M, sh.wm[i][hh]);
+        float L = 0.0f, O = 0.0f;
+        for (int i = 0; i < kAttThreads / kWave; ++i) {
+            const float f = rescale(sh.wm[i][hh], M);
+            L += sh.wl[i][hh] * f;
+            O += sh.wo[i][hh][c] * f;
+        }
+        float *pr = W.part + ((r0 + hh) * S + s) * kPart;
+        st_agent(pr + 4 + c, O);
+        if (c == 0) {
+            st_agent(pr, M);
+            st_agent(pr + 1, L);
+        }
+    }
+
+    // Two-level merge, for all nh heads at once (counters indexed by r0).
+    const int slice = s / W.slice;
+    const int slices = (S + W.slice - 1) / W.slice;
+    const int in_slice = min(W.slice, S - slice * W.slice);
+    if (!arrive_last(W.slice_ctr + r0 * W.max_slices + slice, in_slice, &sh.last)) return;
+    const float *first = W.part + (r0 * S + slice * W.slice) * kPart;
+    if (slices == 1) {
+        merge_heads(first, (int64_t)S * kPart, in_slice, nh, nullptr, 0, dst);
+        return;
+    }
+    float *sp = W.super + r0 * W.max_slices * kPart;
+    merge_heads(first, (int64_t)S * kPart, in_slice, nh, sp + (int64_t)slice * kPart,
+                (int64_t)W.max_slices * kPart, nullptr);
+    if (!arrive_last(W.group_ctr + r0, slices, &sh.last)) return;
+    merge_heads(sp, (int64_t)W.max_slices * kPart, slices, nh, nullptr, 0, dst);
+}
+
+// Heads of KV head g handled by block row y: chunk ck of up to 8 query heads
+// of g within [q_head_begin, q_head_begin + n_q).
+struct HeadChunk {
+    int g, h_lo, nh;
+};
+
+__device__ __forceinline__ HeadChunk head_chunk(int y, int G, int q_head_begin, int n_q,
+                                                int chunks_per_g)
+{
+    HeadChunk c;
+    c.g = q_head_begin / G + y / chunks_per_g;
+    const int ck = y % chunks_per_g;
+    c.h_lo = max(q_head_begin, c.g * G + ck * 8);
+    const int h_hi = min(q_head_begin + n_q, min(c.g * G + G, c.g * G + ck * 8 + 8));
+    c.nh = h_hi - c.h_lo;
+    return c;
+}
+
+// ------------------------------------------------------------- local
+
+static int64_t local_rows_count(int N, int n_sink, int window)
+{
+    const int64_t w_start = N > window ? (int64_t)N - window : 0;
+    const int64_t sink_end = n_sink < w_start ? n_sink : w_start;
+    return sink_end + (N - w_start);
+}
+
+int local_splits(int64_t n_rows)
+{
+    int64_t s = (n_rows + kLocalRows - 1) / kLocalRows;
+    return (int)(s < 1 ? 1 : (s > kMaxLocalSplits ? kMaxLocalSplits : s));
+}
+
+constexpr int kLocalSlice = 16;  // split partials merged per block, first level
+
+// The row list never exceeds N rows, so sizing with N bounds every
+// n_sink / window.
+size_t local_ws_bytes(int64_t B, int64_t n_q, int N)
+{
+    return group_ws_layout(B * n_q, local_splits(N), kLocalSlice, nullptr, nullptr);
+}
+
+// Block (s, y, b): the heads of head_chunk(y), rows of split s of the local
+// row list (sinks, then the window).
 __global__ __launch_bounds__(kAttThreads) void local_attn_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int N, int64_t kv_cap, int Hq, int Hkv,
     int q_head_begin, int n_q, int n_sink, int window, float qscale, int S,
-    int chunks_per_g, LocalWs W, float *__restrict__ out)
+    int chunks_per_g, GroupWs W, float *__restrict__ out)
 {
-    __shared__ int last;
-    __shared__ float wm[kAttThreads / kWave][8], wl[kAttThreads / kWave][8];
-    __shared__ float wo[kAttThreads / kWave][8][128];
-    const int G = Hq / Hkv;
+    __shared__ Heads8Shared sh;
     const int s = blockIdx.x, b = blockIdx.z;
-    const int g = q_head_begin / G + (int)blockIdx.y / chunks_per_g;
-    const int ck = (int)blockIdx.y % chunks_per_g;
-    const int h_lo = max(q_head_begin, g * G + ck * 8);
-    const int h_hi = min(q_head_begin + n_q, min(g * G + G, g * G + ck * 8 + 8));
-    const int nh = h_hi - h_lo;
-    if (nh <= 0) return;
+    const HeadChunk hc = head_chunk(blockIdx.y, Hq / Hkv, q_head_begin, n_q, chunks_per_g);
+    if (hc.nh <= 0) return;
 
     const int64_t w_start = N > window ? (int64_t)N - window : 0;
     const int64_t sink_end = n_sink < w_start ? n_sink : w_start;
@@ -496,181 +729,43 @@ __global__ __launch_bounds__(kAttThreads) void local_attn_kernel(
 
     const int lane = lane_id(), w = threadIdx.x / kWave;
     const int grp = lane >> 4, sub = lane & 15;
-
-    float qf[8][8];
-#pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-        if (hh < nh) {
-            const uint4 qw = *reinterpret_cast<const uint4 *>(
-                q + ((int64_t)b * Hq + h_lo + hh) * 128 + sub * 8);
-            bf16x8_to_f32(qw, qf[hh]);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) qf[hh][c] *= qscale;
-        } else {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) qf[hh][c] = 0.0f;
-        }
-    }
-    const int64_t kvb = ((int64_t)b * Hkv + g) * kv_cap * 128 + sub * 8;
+    const int64_t kvb = ((int64_t)b * Hkv + hc.g) * kv_cap * 128 + sub * 8;
     const uint16_t *Kb = K + kvb;
     const uint16_t *Vb = V + kvb;
-
-    float m[8], l[8], o[8][8];
-#pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-        m[hh] = -INFINITY;
-        l[hh] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[hh][c] = 0.0f;
-    }
-    const int b3 = (sub >> 3) & 1, b2 = (sub >> 2) & 1, b1 = (sub >> 1) & 1;
-
-    for (int64_t base = begin; base < end; base += kRowsPerIter) {
-        uint4 kw[kLocalU], vw[kLocalU];
-        bool ok[kLocalU];
+    uint4 kw[kLocalU], vw[kLocalU];
+    uint32_t hb[kLocalU];
+    auto load_rows = [&](int64_t base) {
 #pragma unroll
         for (int u = 0; u < kLocalU; ++u) {
             const int64_t j = base + u * kGroups + w * 4 + grp;
-            ok[u] = j < end;
+            const bool ok = j < end;
+            hb[u] = ok ? 0xFFu : 0u;
             const int64_t row = j < sink_end ? j : w_start + (j - sink_end);
-            const int64_t off = ok[u] ? row * 128 : 0;
+            const int64_t off = ok ? row * 128 : 0;
             kw[u] = *reinterpret_cast<const uint4 *>(Kb + off);
             vw[u] = *reinterpret_cast<const uint4 *>(Vb + off);
         }
-        float lg[kLocalU][8];
-#pragma unroll
-        for (int u = 0; u < kLocalU; ++u) {
-            float kf[8];
-            bf16x8_to_f32(kw[u], kf);
-            float d[8];
-#pragma unroll
-            for (int hh = 0; hh < 8; ++hh) {
-                float a = 0.0f;
-#pragma unroll
-                for (int c = 0; c < 8; ++c) a = fmaf(qf[hh][c], kf[c], a);
-                d[hh] = a;
-            }
-            // Butterfly: after the steps over lane bits 3, 2, 1 a lane holds
-            // one head, 4*b3 + 2*b2 + b1, summed over 8 lanes; bit 0 finishes.
-            float d4[4], d2[2], d1;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float send = b3 ? d[k] : d[k + 4];
-                const float keep = b3 ? d[k + 4] : d[k];
-                d4[k] = keep + __shfl_xor(send, 8, 16);
-            }
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const float send = b2 ? d4[k] : d4[k + 2];
-                const float keep = b2 ? d4[k + 2] : d4[k];
-                d2[k] = keep + __shfl_xor(send, 4, 16);
-            }
-            {
-                const float send = b1 ? d2[0] : d2[1];
-                const float keep = b1 ? d2[1] : d2[0];
-                d1 = keep + __shfl_xor(send, 2, 16);
-            }
-            d1 += __shfl_xor(d1, 1, 16);
-            // Head hh's logit sits in lanes 2*hh and 2*hh + 1 of the group.
-#pragma unroll
-            for (int hh = 0; hh < 8; ++hh) {
-                const float v = __shfl(d1, 2 * hh, 16);
-                lg[u][hh] = ok[u] ? v : -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
-            float mx = lg[0][hh];
-#pragma unroll
-            for (int u = 1; u < kLocalU; ++u) mx = fmaxf(mx, lg[u][hh]);
-            const float mn = fmaxf(m[hh], mx);
-            if (mn == -INFINITY) continue;
-            const float corr = rescale(m[hh], mn);
-            l[hh] *= corr;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) o[hh][c] *= corr;
-            m[hh] = mn;
-        }
-#pragma unroll
-        for (int u = 0; u < kLocalU; ++u) {
-            float vf[8];
-            bf16x8_to_f32(vw[u], vf);
-#pragma unroll
-            for (int hh = 0; hh < 8; ++hh) {
-                const float pw = ok[u] ? exp2f(lg[u][hh] - m[hh]) : 0.0f;
-                l[hh] += pw;
-#pragma unroll
-                for (int c = 0; c < 8; ++c) o[hh][c] = fmaf(pw, vf[c], o[hh][c]);
-            }
-        }
+    };
+    // The first rows are requested before q, so both loads overlap.
+    if (begin < end) load_rows(begin);
+    Heads8 st;
+    heads8_init(st, q, ((int64_t)b * Hq + hc.h_lo) * 128, hc.nh, qscale, sub);
+    for (int64_t base = begin; base < end; base += kRowsPerIter) {
+        if (base != begin) load_rows(base);
+        heads8_step(st, kw, vw, hb);
     }
+    const int64_t r0 = (int64_t)b * n_q + (hc.h_lo - q_head_begin);
+    heads8_finish(st, sh, hc.nh, s, S, r0, W, out + ((int64_t)b * Hq + hc.h_lo) * 128);
+}
 
-    // Merge the 4 row groups of the wave, then the waves of the block.
-#pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-#pragma unroll
-        for (int off = 16; off < kWave; off <<= 1) {
-            const float mo = __shfl_xor(m[hh], off);
-            const float lo = __shfl_xor(l[hh], off);
-            const float mn = fmaxf(m[hh], mo);
-            const float a = rescale(m[hh], mn), bb = rescale(mo, mn);
-            l[hh] = l[hh] * a + lo * bb;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float oo = __shfl_xor(o[hh][c], off);
-                o[hh][c] = o[hh][c] * a + oo * bb;
-            }
-            m[hh] = mn;
-        }
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) wo[w][hh][sub * 8 + c] = o[hh][c];
-            if (lane == 0) {
-                wm[w][hh] = m[hh];
-                wl[w][hh] = l[hh];
-            }
-        }
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < nh * 128; e += kAttThreads) {
-        const int hh = e / 128, c = e % 128;
-        float M = -INFINITY;
-        for (int i = 0; i < kAttThreads / kWave; ++i) M = fmaxf(M, wm[i][hh]);
-        float L = 0.0f, O = 0.0f;
-        for (int i = 0; i < kAttThreads / kWave; ++i) {
-            const float f = rescale(wm[i][hh], M);
-            L += wl[i][hh] * f;
-            O += wo[i][hh][c] * f;
-        }
-        float *pr = W.part + (((int64_t)b * n_q + (h_lo - q_head_begin + hh)) * S + s) * kPart;
-        st_agent(pr + 4 + c, O);
-        if (c == 0) {
-            st_agent(pr, M);
-            st_agent(pr + 1, L);
-        }
-    }
-
-    // Two-level merge inside the kernel, for all nh heads of this chunk at
-    // once (counters indexed by the chunk's first head row).
-    const int64_t r0 = (int64_t)b * n_q + (h_lo - q_head_begin);
-    const int slice = s / kLocalSlice;
-    const int slices = (S + kLocalSlice - 1) / kLocalSlice;
-    const int in_slice = min(kLocalSlice, S - slice * kLocalSlice);
-    float *dst = out + ((int64_t)b * Hq + h_lo) * 128;
-    if (!arrive_last(W.slice_ctr + r0 * kMaxLocalSlices + slice, in_slice, &last)) return;
-    const float *first = W.part + (r0 * S + slice * kLocalSlice) * kPart;
-    if (slices == 1) {
-        merge_heads(first, (int64_t)S * kPart, in_slice, nh, nullptr, 0, dst);
-        return;
-    }
-    float *sp = W.super + r0 * kMaxLocalSlices * kPart;
-    merge_heads(first, (int64_t)S * kPart, in_slice, nh, sp + (int64_t)slice * kPart,
-                (int64_t)kMaxLocalSlices * kPart, nullptr);
-    if (!arrive_last(W.group_ctr + r0, slices, &last)) return;
-    merge_heads(sp, (int64_t)kMaxLocalSlices * kPart, slices, nh, nullptr, 0, dst);
+static dim3 group_grid(int S, int B, int Hq, int Hkv, int q_head_begin, int n_q_heads,
+                       int *chunks_per_g)
+{
+    const int G = Hq / Hkv;
+    const int g_first = q_head_begin / G;
+    const int g_last = (q_head_begin + n_q_heads - 1) / G;
+    *chunks_per_g = (G + 7) / 8;
+    return dim3(S, (g_last - g_first + 1) * *chunks_per_g, B);
 }
 
 hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,
@@ -678,17 +773,135 @@ hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K, const uint1
                                int q_head_begin, int n_q_heads, int n_sink, int window,
                                float scale, float *out, void *ws, hipStream_t stream)
 {
-    const int G = Hq / Hkv;
     const int S = local_splits(local_rows_count(N, n_sink, window));
-    const int g_first = q_head_begin / G;
-    const int g_last = (q_head_begin + n_q_heads - 1) / G;
-    const int chunks_per_g = (G + 7) / 8;
-    const int ny = (g_last - g_first + 1) * chunks_per_g;
-    LocalWs W;
-    local_ws_layout(B, n_q_heads, N, &W, ws);
-    return launch(local_attn_kernel, dim3(S, ny, B), dim3(kAttThreads), 0, stream, q, K, V, N,
-                  kv_cap, Hq, Hkv, q_head_begin, n_q_heads, n_sink, window, scale * kLog2e, S,
-                  chunks_per_g, W, out);
+    int chunks_per_g;
+    const dim3 grid = group_grid(S, B, Hq, Hkv, q_head_begin, n_q_heads, &chunks_per_g);
+    GroupWs W;
+    group_ws_layout((int64_t)B * n_q_heads, local_splits(N), kLocalSlice, &W, ws);
+    return launch(local_attn_kernel, grid, dim3(kAttThreads), 0, stream, q, K, V, N, kv_cap, Hq,
+                  Hkv, q_head_begin, n_q_heads, n_sink, window, scale * kLog2e, S, chunks_per_g,
+                  W, out);
+}
+
+// ------------------------------------------------------------- union
+//
+// Sparse heads in union mode: each split is a range of token words; a block
+// ORs the keep bitmaps of its heads over the range, lists the union's tokens
+// with their head masks in LDS, and gathers each listed row once for every
+// head that kept it.
+
+constexpr int kUnionWordsPerSplit = 16;  // at least (512 tokens)
+constexpr int kMaxUnionSplits = 768;
+constexpr int kUnionSlice = 32;
+constexpr int kUnionRound = kWave;  // words listed per round (by wave 0)
+constexpr int kUnionCap = kUnionRound * 32;
+
+int union_splits(int N)
+{
+    const int64_t words = ((int64_t)N + 31) / 32;
+    const int64_t s = (words + kUnionWordsPerSplit - 1) / kUnionWordsPerSplit;
+    return (int)(s < 1 ? 1 : (s > kMaxUnionSplits ? kMaxUnionSplits : s));
+}
+
+size_t union_ws_bytes(int64_t B, int64_t n_q, int N)
+{
+    return group_ws_layout(B * n_q, union_splits(N), kUnionSlice, nullptr, nullptr);
+}
+
+// Block (s, y, b): the heads of head_chunk(y), token words of split s.
+__global__ __launch_bounds__(kAttThreads) void union_attn_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint32_t *__restrict__ keep_bits, int N,
+    int64_t kv_cap, int Hq, int Hkv, int q_head_begin, int n_q, float qscale, int S,
+    int chunks_per_g, GroupWs W, float *__restrict__ out)
+{
+    __shared__ Heads8Shared sh;
+    __shared__ uint32_t tok[kUnionCap];
+    __shared__ uint8_t msk[kUnionCap];
+    __shared__ uint32_t listed;
+    const int s = blockIdx.x, b = blockIdx.z;
+    const HeadChunk hc = head_chunk(blockIdx.y, Hq / Hkv, q_head_begin, n_q, chunks_per_g);
+    if (hc.nh <= 0) return;
+
+    const int64_t n_words = ((int64_t)N + 31) / 32;
+    const int64_t per = (n_words + S - 1) / S;
+    const int64_t w_begin = (int64_t)s * per;
+    const int64_t w_end = min(n_words, w_begin + per);
+    const int64_t r0 = (int64_t)b * n_q + (hc.h_lo - q_head_begin);
+    const uint32_t *kb = keep_bits + r0 * n_words;
+
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int grp = lane >> 4, sub = lane & 15;
+    Heads8 st;
+    heads8_init(st, q, ((int64_t)b * Hq + hc.h_lo) * 128, hc.nh, qscale, sub);
+    const int64_t kvb = ((int64_t)b * Hkv + hc.g) * kv_cap * 128 + sub * 8;
+    const uint16_t *Kb = K + kvb;
+    const uint16_t *Vb = V + kvb;
+    constexpr int kRowsPerIter = kGroups * kLocalU;
+
+    for (int64_t w0 = w_begin; w0 < w_end; w0 += kUnionRound) {
+        // Wave 0 lists the union's tokens of up to kUnionRound words, with
+        // each token's head mask.
+        if (w == 0) {
+            const int64_t wi = w0 + lane;
+            // Bits past token N - 1 in the last word are ignored.
+            const uint32_t valid =
+                wi == n_words - 1 && (N & 31) ? (1u << (N & 31)) - 1u : ~0u;
+            uint32_t hw[8];
+            uint32_t un = 0;
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh) {
+                hw[hh] = (hh < hc.nh && wi < w_end) ? kb[hh * n_words + wi] & valid : 0u;
+                un |= hw[hh];
+            }
+            const uint32_t cnt = (uint32_t)__popc(un);
+            const uint32_t inc = wave_inclusive_scan(cnt);
+            uint32_t pos = inc - cnt;
+            for (uint32_t m = un; m; m &= m - 1) {
+                const int bit = __ffs(m) - 1;
+                uint32_t mk = 0;
+#pragma unroll
+                for (int hh = 0; hh < 8; ++hh) mk |= ((hw[hh] >> bit) & 1u) << hh;
+                tok[pos] = (uint32_t)(wi * 32 + bit);
+                msk[pos] = (uint8_t)mk;
+                ++pos;
+            }
+            if (lane == kWave - 1) listed = inc;
+        }
+        __syncthreads();
+        const uint32_t total = listed;
+        for (uint32_t base = 0; base < total; base += kRowsPerIter) {
+            uint4 kw[kLocalU], vw[kLocalU];
+            uint32_t hb[kLocalU];
+#pragma unroll
+            for (int u = 0; u < kLocalU; ++u) {
+                const uint32_t j = base + u * kGroups + w * 4 + grp;
+                const bool ok = j < total;
+                hb[u] = ok ? msk[j] : 0u;
+                const int64_t off = ok ? (int64_t)tok[j] * 128 : 0;
+                kw[u] = *reinterpret_cast<const uint4 *>(Kb + off);
+                vw[u] = *reinterpret_cast<const uint4 *>(Vb + off);
+            }
+            heads8_step(st, kw, vw, hb);
+        }
+        __syncthreads();  // the list is rebuilt next round
+    }
+    heads8_finish(st, sh, hc.nh, s, S, r0, W, out + ((int64_t)b * Hq + hc.h_lo) * 128);
+}
+
+hipError_t launch_sparse_decode_union(const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                                      const uint32_t *keep_bits, int B, int Hq, int Hkv, int N,
+                                      int64_t kv_cap, int q_head_begin, int n_q_heads,
+                                      float scale, float *out, void *ws, hipStream_t stream)
+{
+    const int S = union_splits(N);
+    int chunks_per_g;
+    const dim3 grid = group_grid(S, B, Hq, Hkv, q_head_begin, n_q_heads, &chunks_per_g);
+    GroupWs W;
+    group_ws_layout((int64_t)B * n_q_heads, S, kUnionSlice, &W, ws);
+    return launch(union_attn_kernel, grid, dim3(kAttThreads), 0, stream, q, K, V, keep_bits, N,
+                  kv_cap, Hq, Hkv, q_head_begin, n_q_heads, scale * kLog2e, S, chunks_per_g, W,
+                  out);
 }
 
 }  // namespace rtp

@@ -115,6 +115,10 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *scratch, T *total)
 // written through the per-XCD L2) and read with agent-scope loads (sc1);
 // before a block counts itself done, each wave waits for its stores to
 // complete.  No L2 write-back or invalidate is needed.
+__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_agent(float *p, float v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -146,31 +150,34 @@ __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p)
 // Waits until every vector memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Arrival counter shared by the blocks of one call.  A counter word holds
-// a tag (low 32 bits) and a count (high 32 bits); after every call it is
-// left as (kCtrTag, 0), so a call normally arrives with one atomicAdd.  A
-// word without the tag (fresh or reused memory) is claimed with a
-// compare-and-swap.  kCtrTag is a NaN payload that arithmetic never
-// produces, so no float or index the library writes can look like a
-// counter.  Returns how many blocks of this call arrived before the caller.
+// Counters shared by the blocks of one call (arrivals, output slots).  A
+// counter word holds a tag (low 32 bits) and a count (high 32 bits); after
+// every call it is left as (kCtrTag, 0), so a block normally counts with one
+// atomicAdd.  A word without the tag (fresh or reused memory) is claimed with
+// a compare-and-swap: the add that landed on it is void, and the first block
+// to swap in (kCtrTag, its n) starts the count.  Adds to the high half never
+// change the tag.  kCtrTag is a NaN payload that arithmetic never produces,
+// so no float or index the library writes can look like a counter.
 constexpr uint32_t kCtrTag = 0x7FA5C3E1u;
-constexpr unsigned long long kCtrOne = 1ull << 32;
 
-__device__ __forceinline__ uint32_t ctr_arrive(unsigned long long *ctr)
+// Adds n (every participant adds, even 0, so the word is always claimed) and
+// returns the count before the add.
+__device__ __forceinline__ uint32_t ctr_add(unsigned long long *ctr, uint32_t n)
 {
-    const unsigned long long old = atomicAdd(ctr, kCtrOne);
+    const unsigned long long add = (unsigned long long)n << 32;
+    const unsigned long long old = atomicAdd(ctr, add);
     if ((uint32_t)old == kCtrTag) return (uint32_t)(old >> 32);
-    // The word was not a counter (this add landed on it and is void): the
-    // first block to swap in (kCtrTag, 1) starts the count, later blocks
-    // count on the tagged word.  Adds to the high half never change the tag.
     unsigned long long cur = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (;;) {
-        if ((uint32_t)cur == kCtrTag) return (uint32_t)(atomicAdd(ctr, kCtrOne) >> 32);
-        const unsigned long long prev = atomicCAS(ctr, cur, kCtrOne | kCtrTag);
+        if ((uint32_t)cur == kCtrTag) return (uint32_t)(atomicAdd(ctr, add) >> 32);
+        const unsigned long long prev = atomicCAS(ctr, cur, add | kCtrTag);
         if (prev == cur) return 0u;
         cur = prev;
     }
 }
+
+// Arrival: returns how many blocks of this call arrived before the caller.
+__device__ __forceinline__ uint32_t ctr_arrive(unsigned long long *ctr) { return ctr_add(ctr, 1u); }
 
 // Called by the last block of a call, when no other block of the call will
 // touch the counter again.

@@ -26,8 +26,8 @@ struct SelLayout {
 };
 SelLayout sel_layout(int64_t R, int64_t N);
 hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p,
-                              int32_t *idx, int32_t *count, void *ws,
-                              hipStream_t stream);
+                              int32_t *idx, int32_t *count, uint32_t *keep_bits,
+                              void *ws, hipStream_t stream);
 
 // ---- attention (attend.hip)
 size_t sparse_ws_bytes(int64_t B, int64_t n_q, int N);
@@ -37,6 +37,13 @@ hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K,
                                 int N, int64_t kv_cap, int q_head_begin,
                                 int n_q_heads, float scale, float *out,
                                 void *ws, hipStream_t stream);
+
+size_t union_ws_bytes(int64_t B, int64_t n_q, int N);
+hipError_t launch_sparse_decode_union(const uint16_t *q, const uint16_t *K,
+                                      const uint16_t *V, const uint32_t *keep_bits,
+                                      int B, int Hq, int Hkv, int N, int64_t kv_cap,
+                                      int q_head_begin, int n_q_heads, float scale,
+                                      float *out, void *ws, hipStream_t stream);
 
 int local_splits(int64_t n_rows);
 size_t local_ws_bytes(int64_t B, int64_t n_q, int N);

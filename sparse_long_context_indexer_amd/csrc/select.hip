@@ -380,7 +380,7 @@ __device__ void pick_row(SelPtrs P, int64_t r, float p, PickShared &S)
 
 struct ResShared;
 __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
-                            ResShared &S);
+                            uint32_t *kbr, ResShared &S);
 
 // ------------------------------------------------------------ resolve
 //
@@ -483,11 +483,20 @@ __device__ void res_choose_count(uint32_t c, int nb, ResShared &S)
     }
 }
 
+// Appends token i to the row's kept list at slot pa and, when the row has
+// a keep bitmap, sets its bit (the emit blocks wrote the bitmap's words with
+// agent-scope stores before the resolve started).
+__device__ __forceinline__ void keep_token(int32_t *ir, int64_t pa, uint32_t i, uint32_t *kbr)
+{
+    ir[pa] = (int32_t)i;
+    if (kbr) atomicOr(kbr + (i >> 5), 1u << (i & 31u));
+}
+
 // Ordered in-place filter for candidates in global memory (see the header
 // comment); survivors keep their relative order.
 __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t mask,
                                      uint32_t keep_digit, bool emit_above, bool by_index,
-                                     int32_t *ir, ResShared &S)
+                                     int32_t *ir, uint32_t *kbr, ResShared &S)
 {
     int64_t kept_total = 0;
     for (int64_t c0 = 0; c0 < n; c0 += kResThreads) {
@@ -499,7 +508,7 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
         const bool out = valid && (emit_above ? dg > keep_digit : dg < keep_digit);
         const bool keep = valid && dg == keep_digit;
         const int64_t pa = wave_append(out, &S.nout);
-        if (pa >= 0) ir[pa] = (int32_t)e.y;
+        if (pa >= 0) keep_token(ir, pa, e.y, kbr);
         uint32_t tot;
         const uint32_t pos = block_exclusive_scan<kResThreads>((uint32_t)keep, S.uscan, &tot);
         // All reads of this chunk are done (the scan synchronised the block),
@@ -517,7 +526,7 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
 template <bool kGlobal>
 __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int shift,
                                    uint32_t mask, uint32_t j, bool emit_above, bool by_index,
-                                   int32_t *ir, ResShared &S)
+                                   int32_t *ir, uint32_t *kbr, ResShared &S)
 {
     // From global memory, kB loads per thread are in flight before any is used.
     constexpr int kB = kGlobal ? 8 : 1;
@@ -535,7 +544,7 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
             const bool valid = c0 + (int64_t)u * kResThreads + threadIdx.x < n;
             const uint32_t dg = ((by_index ? e[u].y : e[u].x) >> shift) & mask;
             const int64_t pa = wave_append(valid && (emit_above ? dg > j : dg < j), &S.nout);
-            if (pa >= 0) ir[pa] = (int32_t)e[u].y;
+            if (pa >= 0) keep_token(ir, pa, e[u].y, kbr);
             const int64_t pk = wave_append(valid && dg == j, &S.nnext);
             if (pk >= 0) dst[pk] = e[u];
         }
@@ -545,18 +554,21 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
 }
 
 __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
-                            ResShared &S)
+                            uint32_t *kbr, ResShared &S)
 {
     __syncthreads();  // emit is done with the shared words it used
     const SelRow &row = P.rows[r];
+    const int tid = threadIdx.x;
+    uint2 *gc = P.cand + r * (int64_t)N;
+    // The emit totals and the level-2 histogram are requested together.
+    const unsigned long long slots =
+        ld_agent(reinterpret_cast<const unsigned long long *>(&row.slots));
+    const double h2m = ld_agent(&P.hist2[r].mass[tid]);
+    const uint32_t h2c = ld_agent(&P.hist2[r].cnt[tid]);
     const double M = (double)row.M;
     const double T = row.T;
     double A = row.A;
-    const unsigned long long slots =
-        ld_agent(reinterpret_cast<const unsigned long long *>(&row.slots));
     int64_t n = (uint32_t)slots;
-    uint2 *gc = P.cand + r * (int64_t)N;
-    const int tid = threadIdx.x;
     const uint32_t emitted = (uint32_t)(slots >> 32);  // kept by emit
     int32_t *ir = idx + r * (int64_t)N + emitted;
     bool in_lds = false;  // candidates start in global memory
@@ -569,12 +581,11 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
     // Score levels: key bits [19:10] (histogram built by the emit blocks),
     // then [9:0] (histogram of the survivors).
     static_assert(kResThreads == kDig, "one digit per thread");
-    const Hist2 &h2 = P.hist2[r];
     for (int level = 0; level < 2 && n > 0; ++level) {
         const int shift = level == 0 ? kShift2 : 0;
         if (level == 0) {
-            S.hm[tid] = ld_agent(&h2.mass[tid]);
-            S.hc[tid] = ld_agent(&h2.cnt[tid]);
+            S.hm[tid] = h2m;
+            S.hc[tid] = h2c;
             __syncthreads();
         } else {
             S.hm[tid] = 0.0;
@@ -594,17 +605,17 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
         A = S.abefore;  // A plus the mass of the digits above j
         if (in_lds) {
             n = res_filter_lds<false>(S.buf[cur], n, S.buf[cur ^ 1], shift, kDig - 1, j, true,
-                                      false, ir, S);
+                                      false, ir, kbr, S);
             cur ^= 1;
             cr = S.buf[cur];
         } else if (S.hc[j] <= (uint32_t)kResCap) {
             // The boundary digit's candidates fit in LDS: continue there.
-            n = res_filter_lds<true>(gc, n, S.buf[0], shift, kDig - 1, j, true, false, ir, S);
+            n = res_filter_lds<true>(gc, n, S.buf[0], shift, kDig - 1, j, true, false, ir, kbr, S);
             in_lds = true;
             cur = 0;
             cr = S.buf[0];
         } else {
-            n = res_filter_global(gc, n, shift, kDig - 1, j, true, false, ir, S);
+            n = res_filter_global(gc, n, shift, kDig - 1, j, true, false, ir, kbr, S);
         }
     }
 
@@ -629,7 +640,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
                 const bool valid = k < n;
                 const uint32_t ix = valid ? cand(k).y : 0u;
                 const int64_t pa = wave_append(valid, &S.nout);
-                if (pa >= 0) ir[pa] = (int32_t)ix;
+                if (pa >= 0) keep_token(ir, pa, ix, kbr);
             }
         } else {
             // Count-only radix select of the c lowest indices: bits [30:20],
@@ -652,20 +663,21 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
                 c -= S.cbefore;
                 if (in_lds) {
                     n = res_filter_lds<false>(S.buf[cur], n, S.buf[cur ^ 1], shift, mask, j,
-                                              false, true, ir, S);
+                                              false, true, ir, kbr, S);
                     cur ^= 1;
                     cr = S.buf[cur];
                 } else if (S.hc[j] <= (uint32_t)kResCap) {
-                    n = res_filter_lds<true>(gc, n, S.buf[0], shift, mask, j, false, true, ir, S);
+                    n = res_filter_lds<true>(gc, n, S.buf[0], shift, mask, j, false, true, ir,
+                                             kbr, S);
                     in_lds = true;
                     cur = 0;
                     cr = S.buf[0];
                 } else {
-                    n = res_filter_global(gc, n, shift, mask, j, false, true, ir, S);
+                    n = res_filter_global(gc, n, shift, mask, j, false, true, ir, kbr, S);
                 }
             }
             // One token left (its index is fully determined): keep it.
-            if (tid == 0 && n > 0 && c > 0) ir[S.nout++] = (int32_t)cand(0).y;
+            if (tid == 0 && n > 0 && c > 0) keep_token(ir, S.nout++, cand(0).y, kbr);
         }
     }
     __syncthreads();
@@ -674,7 +686,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
 
 __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     const float *__restrict__ scores, int N, SelPtrs P, int32_t *__restrict__ idx,
-    int32_t *__restrict__ count)
+    int32_t *__restrict__ count, uint32_t *__restrict__ keep_bits)
 {
     static_assert(kSelThreads == kResThreads, "the last emit block runs the resolve");
     __shared__ ResShared S;
@@ -702,6 +714,37 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
         atb |= (valid && bin == j1) ? (1u << t) : 0u;
     }
     const uint32_t mine = ((uint32_t)__popc(above) << 16) | (uint32_t)__popc(atb);
+    // Keep bitmap: this chunk's words, with the bits of the tokens kept here
+    // (the resolve adds the boundary bin's kept tokens).  Agent-scope
+    // stores, so the resolve's atomics land on the written words.
+    uint32_t *kbr = keep_bits ? keep_bits + r * (int64_t)((N + 31) / 32) : nullptr;
+    if (kbr) {
+        const int lane = lane_id();
+        uint32_t *kw = kbr + (uint32_t)(cv.c0 >> 5);
+        if (cv.vec) {
+            // Slots 4g..4g+3 of thread x are tokens g*4096 + 4x + 0..3: a
+            // nibble of word g*128 + x/8; eight lanes fill one word.
+#pragma unroll
+            for (int g = 0; g < kSelPerThread / 4; ++g) {
+                uint32_t wv = ((above >> (4 * g)) & 0xFu) << (4 * (lane & 7));
+                wv |= __shfl_xor(wv, 1);
+                wv |= __shfl_xor(wv, 2);
+                wv |= __shfl_xor(wv, 4);
+                if ((lane & 7) == 0) st_agent(kw + g * 128 + (threadIdx.x >> 3), wv);
+            }
+        } else {
+            // Slot t of thread x is token t*1024 + x: a wave's ballot is two
+            // words; words past the end of the row are not written.
+            const uint32_t n_words = (uint32_t)(((int64_t)N - cv.c0 + 31) >> 5);
+#pragma unroll
+            for (int t = 0; t < kSelPerThread; ++t) {
+                const unsigned long long bal = __ballot((above >> t) & 1u);
+                const uint32_t wi = (uint32_t)t * 32u + (threadIdx.x >> 5);
+                if ((lane & 31) == 0 && wi < n_words)
+                    st_agent(kw + wi, (uint32_t)(lane == 0 ? bal : bal >> 32));
+            }
+        }
+    }
     // Wave prefix (a wave holds at most 2048 of each, so halves never
     // carry), then one LDS atomic per wave for its block offset and one
     // global atomic per block for its row offset.
@@ -764,32 +807,39 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
         S.last = atomicAdd(&P.rows[r].emit_done, 1u) == (uint32_t)(gridDim.x - 1);
     __syncthreads();
     if (!S.last) return;
-    resolve_row(N, P, r, idx, count, S);
+    resolve_row(N, P, r, idx, count, kbr, S);
 }
 
 // ---------------------------------------------------------------- p >= 1
 
 __global__ __launch_bounds__(256) void sel_all_kernel(int N, int32_t *__restrict__ idx,
-                                                      int32_t *__restrict__ count)
+                                                      int32_t *__restrict__ count,
+                                                      uint32_t *__restrict__ keep_bits)
 {
     const int64_t r = blockIdx.y;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < N) idx[r * (int64_t)N + i] = (int32_t)i;
     if (blockIdx.x == 0 && threadIdx.x == 0) count[r] = N;
+    const int64_t n_words = ((int64_t)N + 31) / 32;
+    if (keep_bits && i < n_words) {
+        const int64_t left = (int64_t)N - i * 32;  // tokens in this word
+        keep_bits[r * n_words + i] = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
+    }
 }
 
 hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p, int32_t *idx,
-                              int32_t *count, void *ws, hipStream_t stream)
+                              int32_t *count, uint32_t *keep_bits, void *ws, hipStream_t stream)
 {
     if (p >= 1.0f) {
         dim3 grid((unsigned)((N + 255) / 256), (unsigned)R);
-        return launch(sel_all_kernel, grid, dim3(256), 0, stream, N, idx, count);
+        return launch(sel_all_kernel, grid, dim3(256), 0, stream, N, idx, count, keep_bits);
     }
     SelPtrs P = sel_ptrs(ws, R, N);
     dim3 grid((unsigned)P.nblk, (unsigned)R);
     RTP_TRY(launch(sel_zero_kernel, dim3(kZeroBlocks), dim3(256), 0, stream, P));
     RTP_TRY(launch(sel_hist_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, p));
-    return launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, idx, count);
+    return launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, idx, count,
+                  keep_bits);
 }
 
 }  // namespace rtp

@@ -10,35 +10,53 @@ from __future__ import annotations
 
 import torch
 
-from . import (RTP_WS_LOCAL_DECODE, RTP_WS_SPARSE_DECODE, RTP_WS_TOPP_SELECT,
-               rtp_index_scores, rtp_local_decode, rtp_sparse_decode, rtp_topp_select,
-               workspace_size)
+from . import (RTP_WS_LOCAL_DECODE, RTP_WS_SPARSE_DECODE, RTP_WS_SPARSE_UNION,
+               RTP_WS_TOPP_SELECT, keep_words, rtp_index_scores, rtp_local_decode,
+               rtp_sparse_decode, rtp_sparse_decode_union, rtp_topp_select, workspace_size)
 
 
 class DecodeLayer:
+    """mode "union": the selector also writes keep bitmaps and the sparse
+    heads run rtp_sparse_decode_union (each kept row read once per KV head);
+    mode "per_head": rtp_sparse_decode over each head's index list."""
+
     def __init__(self, B: int, Hq: int, Hkv: int, N: int, H_r: int, n_sink: int,
-                 window: int, device, d: int = 128):
+                 window: int, device, d: int = 128, mode: str = "union"):
+        if mode not in ("union", "per_head"):
+            raise ValueError(f"unknown mode {mode!r}")
         self.B, self.Hq, self.Hkv, self.N, self.H_r = B, Hq, Hkv, N, H_r
-        self.n_sink, self.window, self.d = n_sink, window, d
+        self.n_sink, self.window, self.d, self.mode = n_sink, window, d, mode
         self.H_l = Hq - H_r
         dev = torch.device(device)
+        self.keep_bits = None
         if H_r > 0:
             self.scores = torch.empty((B, H_r, N), dtype=torch.float32, device=dev)
             self.idx = torch.empty((B, H_r, N), dtype=torch.int32, device=dev)
             self.count = torch.empty((B, H_r), dtype=torch.int32, device=dev)
             self.ws_sel = torch.empty(workspace_size(RTP_WS_TOPP_SELECT, B, H_r, N),
                                       dtype=torch.uint8, device=dev)
-            self.ws_sparse = torch.empty(workspace_size(RTP_WS_SPARSE_DECODE, B, H_r, N),
-                                         dtype=torch.uint8, device=dev)
+            if mode == "union":
+                self.keep_bits = torch.empty((B, H_r, keep_words(N)), dtype=torch.int32,
+                                             device=dev)
+                self.ws_sparse = torch.empty(workspace_size(RTP_WS_SPARSE_UNION, B, H_r, N),
+                                             dtype=torch.uint8, device=dev)
+            else:
+                self.ws_sparse = torch.empty(workspace_size(RTP_WS_SPARSE_DECODE, B, H_r, N),
+                                             dtype=torch.uint8, device=dev)
         if self.H_l > 0:
             self.ws_local = torch.empty(workspace_size(RTP_WS_LOCAL_DECODE, B, self.H_l, N),
                                         dtype=torch.uint8, device=dev)
 
     def retrieval(self, q_r, k_r, q, K, V, p: float, scale: float, out, stream=None):
         rtp_index_scores(q_r, k_r, self.scores, stream=stream)
-        rtp_topp_select(self.scores, p, self.idx, self.count, self.ws_sel, stream=stream)
-        rtp_sparse_decode(q, K, V, self.idx, self.count, 0, scale, out, self.ws_sparse,
-                          stream=stream)
+        rtp_topp_select(self.scores, p, self.idx, self.count, self.ws_sel,
+                        keep_bits=self.keep_bits, stream=stream)
+        if self.mode == "union":
+            rtp_sparse_decode_union(q, K, V, self.keep_bits, self.N, 0, scale, out,
+                                    self.ws_sparse, stream=stream)
+        else:
+            rtp_sparse_decode(q, K, V, self.idx, self.count, 0, scale, out, self.ws_sparse,
+                              stream=stream)
 
     def local(self, q, K, V, scale: float, out, stream=None):
         rtp_local_decode(q, K, V, self.N, self.H_r, self.H_l, self.n_sink, self.window,

@@ -115,12 +115,20 @@ def judge_out(gpu: np.ndarray, ref: np.ndarray):
     return err <= MAX_ABS and rel <= MAX_REL, err, rel
 
 
-def run_layer(L: Layer, p: float, step=None):
+def bits_to_set(words: np.ndarray, N: int) -> np.ndarray:
+    """Token indices whose bit is set in a keep bitmap row (bit i%32 of
+    word i/32), tokens < N only."""
+    bits = np.unpackbits(words.astype("<u4").view(np.uint8), bitorder="little")
+    return np.flatnonzero(bits[:N]).astype(np.int64)
+
+
+def run_layer(L: Layer, p: float, step=None, mode: str = "union"):
     """Runs the whole layer on the GPU; returns host copies of the results."""
     from sparse_long_context_indexer_amd.runner import DecodeLayer
     cfg = L.cfg
     if step is None:
-        step = DecodeLayer(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.H_r, cfg.n_sink, cfg.window, dev())
+        step = DecodeLayer(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.H_r, cfg.n_sink, cfg.window, dev(),
+                           mode=mode)
     out = torch.full((cfg.B, cfg.Hq, cfg.d), float("nan"), dtype=torch.float32, device=dev())
     step(L.d["q_r"], L.d["k_r"], L.d["q"], L.d["K"], L.d["V"], p, cfg.scale, out)
     torch.cuda.synchronize()
@@ -132,6 +140,10 @@ def run_layer(L: Layer, p: float, step=None):
         res["count"] = cnt
         res["sets"] = [[idx[b, h, :cnt[b, h]].copy() for h in range(cfg.H_r)]
                        for b in range(cfg.B)]
+        if step.keep_bits is not None:
+            kb = step.keep_bits.cpu().numpy()
+            res["bits"] = [[bits_to_set(kb[b, h], cfg.N) for h in range(cfg.H_r)]
+                           for b in range(cfg.B)]
     return res
 
 
@@ -153,6 +165,9 @@ def check_layer(L: Layer, p: float, res: dict, heads=None, report=None):
                 n = int(np.sum(s_gpu.view(np.uint32) != s_ref.view(np.uint32)))
                 fails.append(f"scores b={b} h={h}: {n} words differ")
                 continue
+            if "bits" in res and not np.array_equal(np.sort(res["sets"][b][h]),
+                                                    res["bits"][b][h]):
+                fails.append(f"keep bitmap b={b} h={h} differs from the index list")
             v = judge_set(s_ref, p, res["sets"][b][h])
             rep["exempt"] += len(v.exempt)
             rep["k"].append(v.k_gpu)

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 7
+    assert len(names) == 8
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -49,7 +49,7 @@ def test_workspace_sizes(lib):
     assert a >= 8 * (1 << 20) * 8          # candidate list capacity
     assert a % 256 == 0
     assert rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 1, 8, 4096) < a
-    for which in (rtp.RTP_WS_SPARSE_DECODE, rtp.RTP_WS_LOCAL_DECODE):
+    for which in (rtp.RTP_WS_SPARSE_DECODE, rtp.RTP_WS_LOCAL_DECODE, rtp.RTP_WS_SPARSE_UNION):
         s = rtp.workspace_size(which, 2, 8, 65536)
         assert s > 0 and s % 256 == 0
     with pytest.raises(rtp.RtpError) as e:
@@ -82,14 +82,35 @@ def test_index_scores_validation(lib):
 def test_topp_select_validation(lib):
     f = lib.rtp_topp_select
     ws = rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 1, 8, 1000)
-    assert f(None, 1, 8, 1000, 0.9, A, A, A, ws, None) == 1
-    assert f(A, 1, 8, 1000, 0.9, A, A, None, ws, None) == 1
+    assert f(None, 1, 8, 1000, 0.9, A, A, None, A, ws, None) == 1
+    assert f(A, 1, 8, 1000, 0.9, A, A, None, None, ws, None) == 1
     for p in (0.0, -0.5, 1.5, float("nan"), float("inf")):
-        assert f(A, 1, 8, 1000, p, A, A, A, ws, None) == 4, p
-    assert f(A, 1, 8, 0, 0.9, A, A, A, ws, None) == 2
-    assert f(A, 1, 8, 1000, 0.9, A, A, A, ws - 1, None) == 6
-    assert f(A, 1, 8, 1000, 0.9, A, A, A + 16, ws, None) == 5   # workspace alignment
-    assert f(A + 2, 1, 8, 1000, 0.9, A, A, A, ws, None) == 5
+        assert f(A, 1, 8, 1000, p, A, A, None, A, ws, None) == 4, p
+    assert f(A, 1, 8, 0, 0.9, A, A, None, A, ws, None) == 2
+    assert f(A, 1, 8, 1000, 0.9, A, A, None, A, ws - 1, None) == 6
+    assert f(A, 1, 8, 1000, 0.9, A, A, None, A + 16, ws, None) == 5   # workspace alignment
+    assert f(A + 2, 1, 8, 1000, 0.9, A, A, None, A, ws, None) == 5
+    assert f(A, 1, 8, 1000, 0.9, A, A, A + 2, A, ws, None) == 5       # keep_bits alignment
+
+
+def test_sparse_decode_union_validation(lib):
+    f = lib.rtp_sparse_decode_union
+    ws = rtp.workspace_size(rtp.RTP_WS_SPARSE_UNION, 1, 8, 1000)
+    base = [A, A, A, A, 1, 32, 4, 1000, 1000, 128, 0, 8, 0.088, A, A, ws, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert f(*base[:3], None, *base[4:]) == 1
+    assert call(0, None) == 1
+    assert call(3, A + 2) == 5                  # keep_bits alignment
+    assert call(9, 64) == 3                     # d != 128
+    assert call(6, 5) == 2                      # 32 % 5
+    assert call(10, 30) == 2                    # 30 + 8 > 32
+    assert call(12, float("inf")) == 4
+    assert call(15, ws - 1) == 6
 
 
 def test_sparse_decode_validation(lib):

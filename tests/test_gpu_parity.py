@@ -22,13 +22,14 @@ def _print(*a):
 
 # ------------------------------------------------------------ full configs
 
+@pytest.mark.parametrize("mode", ["union", "per_head"])
 @pytest.mark.parametrize("ci", [0, 1, 3])
-def test_config_layer(ci):
+def test_config_layer(ci, mode):
     cfg = synth.CONFIGS[ci]
-    _print(f"config {ci} {cfg.name}")
+    _print(f"config {ci} {cfg.name} ({mode})")
     L = load_layer(cfg)
     rep = {}
-    res = run_layer(L, cfg.p_list[0])
+    res = run_layer(L, cfg.p_list[0], mode=mode)
     fails = check_layer(L, cfg.p_list[0], res, report=rep)
     _print(f"  k per head {rep['k']} exempt {rep['exempt']}")
     assert not fails, "\n".join(fails[:20])
@@ -50,11 +51,11 @@ def test_config4_sampled_layers():
     # Full-size layers of the 48-layer 1M-context stack (same kernels and
     # launch shapes as the benchmark), judged in full for every head.
     cfg = synth.CONFIGS[4]
-    for layer in (0, 47):
-        _print(f"config 4 layer {layer}")
+    for layer, mode in ((0, "union"), (47, "per_head"), (47, "union")):
+        _print(f"config 4 layer {layer} ({mode})")
         L = load_layer(cfg, layer, keep_host_kv=False)
         rep = {}
-        res = run_layer(L, 0.9)
+        res = run_layer(L, 0.9, mode=mode)
         fails = check_layer(L, 0.9, res, report=rep)
         _print(f"  k per head {rep['k']} exempt {rep['exempt']}")
         del L
@@ -239,6 +240,8 @@ def test_workspace_garbage_and_reuse():
     L = load_layer(cfg)
     step = DecodeLayer(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.H_r, cfg.n_sink, cfg.window, dev())
     g = torch.Generator(device="cpu").manual_seed(7)
+    step.keep_bits.copy_(torch.randint(-2**31, 2**31 - 1, step.keep_bits.shape,
+                                       dtype=torch.int32, generator=g))
     for ws in (step.ws_sel, step.ws_sparse, step.ws_local):
         ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=g))
     for rep in range(2):
@@ -257,3 +260,62 @@ def test_workspace_garbage_and_reuse():
         res = run_layer(Ls, 0.9, step=s2)
         fails = check_layer(Ls, 0.9, res)
         assert not fails, "\n".join(fails[:20])
+
+
+# ------------------------------------------------------------- union mode
+
+@pytest.mark.parametrize("N,hb,nq", [(70001, 0, 8), (5000, 3, 8), (33, 0, 8), (100000, 4, 12)])
+def test_union_decode_random_sets(N, hb, nq):
+    # Keep bitmaps built on the host (random densities per head, stray bits
+    # past N in the last word, head ranges across KV heads), against the
+    # oracle's attention over each head's set.
+    cfg = synth.CONFIGS[1].with_(N=N, needles_per_head=0)
+    L = load_layer(cfg)
+    rng = np.random.default_rng(N + hb)
+    words = (N + 31) // 32
+    kb = np.zeros((1, nq, words), dtype=np.uint32)
+    sets = []
+    for i in range(nq):
+        dens = [0.001, 0.05, 0.5, 1.0][i % 4]
+        sel = np.flatnonzero(rng.random(N) < dens)
+        if len(sel) == 0:
+            sel = np.array([rng.integers(N)])
+        bits = np.zeros(words * 32, dtype=np.uint8)
+        bits[sel] = 1
+        bits[N:] = 1  # past the end: must be ignored
+        kb[0, i] = np.packbits(bits, bitorder="little").view("<u4")
+        sets.append(sel)
+    out = torch.full((1, cfg.Hq, 128), float("nan"), dtype=torch.float32, device=dev())
+    ws = torch.empty(rtp.workspace_size(rtp.RTP_WS_SPARSE_UNION, 1, nq, N), dtype=torch.uint8,
+                     device=dev())
+    ws.fill_(0xA5)
+    kbt = torch.from_numpy(kb.view(np.int32)).to(dev())
+    for rep in range(2):
+        rtp.rtp_sparse_decode_union(L.d["q"], L.d["K"], L.d["V"], kbt, N, hb, cfg.scale, out, ws)
+        got = out.cpu().numpy()
+        for i in range(nq):
+            h = hb + i
+            ref = oracle.attention(L.q[0, h], L.K[0, h // 8, sets[i]], L.V[0, h // 8, sets[i]],
+                                   cfg.scale)
+            ok, err, rel = judge_out(got[0, h], ref)
+            assert ok, (rep, h, len(sets[i]), err, rel)
+        outside = [h for h in range(cfg.Hq) if not hb <= h < hb + nq]
+        assert np.all(np.isnan(got[0, outside]))
+
+
+def test_union_single_row_is_value_row():
+    cfg = synth.CONFIGS[1].with_(N=300, needles_per_head=0)
+    L = load_layer(cfg)
+    for t in (0, 31, 32, 299):
+        kb = np.zeros((1, 8, 10), dtype=np.uint32)
+        kb[0, :, t // 32] = np.uint32(1) << np.uint32(t % 32)
+        out = torch.zeros((1, 32, 128), dtype=torch.float32, device=dev())
+        ws = torch.empty(rtp.workspace_size(rtp.RTP_WS_SPARSE_UNION, 1, 8, 300),
+                         dtype=torch.uint8, device=dev())
+        rtp.rtp_sparse_decode_union(L.d["q"], L.d["K"], L.d["V"],
+                                    torch.from_numpy(kb.view(np.int32)).to(dev()), 300, 0,
+                                    cfg.scale, out, ws)
+        got = out.cpu().numpy()
+        want = synth.bf16_to_f32(L.V[0, 0, t])
+        for h in range(8):
+            assert np.array_equal(got[0, h], want), (t, h)
