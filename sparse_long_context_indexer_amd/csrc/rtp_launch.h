@@ -19,7 +19,6 @@ struct SelLayout {
     size_t rows;      // per-row state
     size_t hist1;     // per-row level-1 histogram
     size_t hist2;     // per-row histogram of the boundary bin's candidates
-    size_t zero_end;  // [rows, zero_end) is cleared at the start of a call
     size_t tops;      // per-chunk top-bin records
     size_t cand;      // boundary-bin candidates (key, index)
     size_t total;

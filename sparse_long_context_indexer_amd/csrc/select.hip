@@ -45,7 +45,6 @@ constexpr int kBins1 = 1 << (32 - kShift1);  // 4096 bins
 constexpr int kShift2 = 10;                  // refinement digits: key bits [19:10], [9:0]
 constexpr int kDig = 1 << kShift2;           // 1024 digits per refinement level
 constexpr int kPickThreads = 1024;
-constexpr int kZeroBlocks = 64;
 constexpr int kResThreads = 1024;
 constexpr int kResBins = 2048;
 constexpr int kResCap = 8192;  // candidates resolved from LDS (two buffers)
@@ -59,7 +58,8 @@ struct SelRow {
     uint64_t slots;  // emit's slot counters: kept (high 32 bits), candidates (low)
     uint32_t hist_done;  // hist blocks finished
     uint32_t emit_done;  // emit blocks finished
-    uint32_t pad[4];
+    unsigned long long ready;  // tagged: the row's state below was cleared
+    uint32_t pad[2];
 };
 static_assert(sizeof(SelRow) == 64, "SelRow is one 64-B record");
 
@@ -89,7 +89,6 @@ SelLayout sel_layout(int64_t R, int64_t N)
     off += align_up((size_t)R * sizeof(Hist1), 256);
     L.hist2 = off;
     off += align_up((size_t)R * sizeof(Hist2), 256);
-    L.zero_end = off;
     L.tops = off;
     off += align_up((size_t)R * L.nblk * sizeof(ChunkTop), 256);
     L.cand = off;
@@ -104,8 +103,6 @@ struct SelPtrs {
     Hist2 *hist2;
     ChunkTop *tops;
     uint2 *cand;
-    uint4 *zero;
-    int64_t zero_words;  // uint4 words to clear: the rows and histograms
     int nblk;
 };
 
@@ -119,8 +116,6 @@ static SelPtrs sel_ptrs(void *ws, int64_t R, int64_t N)
     P.hist2 = reinterpret_cast<Hist2 *>(base + L.hist2);
     P.tops = reinterpret_cast<ChunkTop *>(base + L.tops);
     P.cand = reinterpret_cast<uint2 *>(base + L.cand);
-    P.zero = reinterpret_cast<uint4 *>(base + L.rows);
-    P.zero_words = (int64_t)((L.zero_end - L.rows) / sizeof(uint4));
     P.nblk = (int)L.nblk;
     return P;
 }
@@ -191,13 +186,42 @@ __device__ __forceinline__ ChunkView load_chunk(const float *__restrict__ sr, in
     return cv;
 }
 
-// --------------------------------------------------------------- zero
+// ----------------------------------------------------- row state
+//
+// Block 0 of each row's hist grid clears the row's state (histograms,
+// counters) at the start of a call and then counts itself on the row's
+// tagged `ready` counter; the row's other blocks wait for it before their
+// first global add, which comes after their whole LDS pass, so the wait is
+// almost always already over.  Block 0 is dispatched before the row's other
+// blocks (it has the lowest index), so the wait always ends.  The pick
+// resets `ready` for the next call.
 
-__global__ __launch_bounds__(256) void sel_zero_kernel(SelPtrs P)
+__device__ void clear_row(SelPtrs P, int64_t r)
 {
-    const int64_t n = (int64_t)gridDim.x * 256;
-    for (int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x; w < P.zero_words; w += n)
-        P.zero[w] = make_uint4(0, 0, 0, 0);
+    Hist1 &g = P.hist1[r];
+    Hist2 &h2 = P.hist2[r];
+    for (int i = threadIdx.x; i < kBins1; i += kSelThreads) st_agent(&g.mass[i], 0.0);
+    for (int i = threadIdx.x; i < kDig; i += kSelThreads) {
+        st_agent(&h2.mass[i], 0.0);
+        st_agent(&h2.cnt[i], 0u);
+    }
+    if (threadIdx.x == 0) {
+        st_agent(reinterpret_cast<unsigned long long *>(&P.rows[r].slots), 0ull);
+        st_agent(&P.rows[r].hist_done, 0u);
+        st_agent(&P.rows[r].emit_done, 0u);
+    }
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) ctr_add(&P.rows[r].ready, 1u);
+}
+
+__device__ void wait_row_ready(const SelRow &row)
+{
+    for (;;) {
+        const unsigned long long v = ld_agent(&row.ready);
+        if ((uint32_t)v == kCtrTag && (v >> 32) != 0) return;
+        __builtin_amdgcn_s_sleep(2);
+    }
 }
 
 // --------------------------------------------------------------- hist
@@ -229,6 +253,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
     const float *sr = scores + r * (int64_t)N;
     float v[kSelPerThread];
     load_chunk(sr, N, (int64_t)blk * kSelChunk, v);  // missing elements: -inf
+    if (blk == 0) clear_row(P, r);
 
     for (int i = threadIdx.x; i < kBins1; i += kSelThreads) hm[i] = 0.0;
     if (threadIdx.x < kExpTable) S.etbl[threadIdx.x] = kExp2Tbl[threadIdx.x];
@@ -249,6 +274,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
         const double ref = bin == tb ? mbd : (double)bin_top(bin);
         atomicAdd(&hm[bin], exp_tang((double)v[t] - ref, S.etbl));
     }
+    if (blk != 0 && threadIdx.x == 0) wait_row_ready(P.rows[r]);
     __syncthreads();
     Hist1 &g = P.hist1[r];
     for (int i = threadIdx.x; i < kBins1; i += kSelThreads) {
@@ -268,6 +294,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
     if (threadIdx.x == 0) S.last = atomicAdd(&P.rows[r].hist_done, 1u) == (uint32_t)(P.nblk - 1);
     __syncthreads();
     if (!S.last) return;
+    if (threadIdx.x == 0) ctr_reset(&P.rows[r].ready);
     pick_row(P, r, p, S);
 }
 
@@ -836,7 +863,6 @@ hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p, in
     }
     SelPtrs P = sel_ptrs(ws, R, N);
     dim3 grid((unsigned)P.nblk, (unsigned)R);
-    RTP_TRY(launch(sel_zero_kernel, dim3(kZeroBlocks), dim3(256), 0, stream, P));
     RTP_TRY(launch(sel_hist_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, p));
     return launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, idx, count,
                   keep_bits);
