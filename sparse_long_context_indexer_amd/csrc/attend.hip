@@ -26,7 +26,7 @@ namespace rtp {
 constexpr int kAttThreads = 256;
 constexpr int kGroups = kAttThreads / 16;  // 16-lane row groups per block
 constexpr int kPart = 132;                 // floats per partial: m, l, pad, o[128]
-constexpr int kSparseU = 4;                // rows per group per iteration
+constexpr int kSparseU = 8;                // rows per group per iteration
 constexpr int kLocalU = 4;
 constexpr int kLocalRows = 64;       // rows per local split (at least)
 constexpr int kMaxLocalSplits = 128;
@@ -56,6 +56,7 @@ __device__ __forceinline__ float rescale(float m_old, float m_new)
 constexpr int kSparseTarget = 768;
 constexpr int kSlice = 32;  // split partials merged per block in the first merge level
 constexpr int kMaxSlices = (kSparseTarget + 1 + kSlice - 1) / kSlice;
+static_assert(kMaxSlices <= kSlice, "the second merge level takes at most kSlice partials");
 
 int sparse_grid(int64_t R) { return (int)(kSparseTarget + R); }
 
@@ -174,14 +175,24 @@ __device__ void merge_partials(const float *pr, int n, float *dst_part, float *d
                                MergeShared &S)
 {
     constexpr int kG = kAttThreads / 128;
+    constexpr int kPer = kSlice / kG;  // partials per thread
     const int tid = threadIdx.x;
     const int c = tid & 127, grp = tid >> 7;
+    // Every load is issued before any is used: the output columns of this
+    // thread's partials, and (wave 0) their max and sum.
+    float ov[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int k = grp + i * kG;
+        ov[i] = k < n ? ld_agent(pr + (int64_t)k * kPart + 4 + c) : 0.0f;
+    }
     if (tid < kWave) {
         // wave 0: the merged max, the factors and the merged sum
         const float m = tid < n ? ld_agent(pr + (int64_t)tid * kPart) : -INFINITY;
+        const float lp = tid < n ? ld_agent(pr + (int64_t)tid * kPart + 1) : 0.0f;
         const float M = wave_max(m);
         const float f = tid < n ? rescale(m, M) : 0.0f;
-        const float l = wave_sum(tid < n ? ld_agent(pr + (int64_t)tid * kPart + 1) * f : 0.0f);
+        const float l = wave_sum(lp * f);
         if (tid < n) S.f[tid] = f;
         if (tid == 0) {
             S.M = M;
@@ -190,8 +201,11 @@ __device__ void merge_partials(const float *pr, int n, float *dst_part, float *d
     }
     __syncthreads();
     float o = 0.0f;
-#pragma unroll 16
-    for (int k = grp; k < n; k += kG) o = fmaf(ld_agent(pr + (int64_t)k * kPart + 4 + c), S.f[k], o);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int k = grp + i * kG;
+        if (k < n) o = fmaf(ov[i], S.f[k], o);
+    }
     S.o[grp][c] = o;
     __syncthreads();
     if (grp == 0) {
@@ -791,7 +805,7 @@ hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K, const uint1
 // head that kept it.
 
 constexpr int kUnionWordsPerSplit = 16;  // at least (512 tokens)
-constexpr int kMaxUnionSplits = 768;
+constexpr int kMaxUnionSplits = 512;
 constexpr int kUnionSlice = 32;
 constexpr int kUnionRound = kWave;  // words listed per round (by wave 0)
 constexpr int kUnionCap = kUnionRound * 32;
@@ -832,6 +846,18 @@ __global__ __launch_bounds__(kAttThreads) void union_attn_kernel(
 
     const int lane = lane_id(), w = threadIdx.x / kWave;
     const int grp = lane >> 4, sub = lane & 15;
+    // Wave 0 lists the union's tokens of up to kUnionRound words per round,
+    // with each token's head mask.  Bits past token N - 1 are ignored.
+    uint32_t hw[8];
+    auto load_words = [&](int64_t w0) {
+        const int64_t wi = w0 + lane;
+        const uint32_t valid = wi == n_words - 1 && (N & 31) ? (1u << (N & 31)) - 1u : ~0u;
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh)
+            hw[hh] = (hh < hc.nh && wi < w_end) ? kb[hh * n_words + wi] & valid : 0u;
+    };
+    // The first round's words are requested before q, so both loads overlap.
+    if (w == 0) load_words(w_begin);
     Heads8 st;
     heads8_init(st, q, ((int64_t)b * Hq + hc.h_lo) * 128, hc.nh, qscale, sub);
     const int64_t kvb = ((int64_t)b * Hkv + hc.g) * kv_cap * 128 + sub * 8;
@@ -840,20 +866,12 @@ __global__ __launch_bounds__(kAttThreads) void union_attn_kernel(
     constexpr int kRowsPerIter = kGroups * kLocalU;
 
     for (int64_t w0 = w_begin; w0 < w_end; w0 += kUnionRound) {
-        // Wave 0 lists the union's tokens of up to kUnionRound words, with
-        // each token's head mask.
         if (w == 0) {
+            if (w0 != w_begin) load_words(w0);
             const int64_t wi = w0 + lane;
-            // Bits past token N - 1 in the last word are ignored.
-            const uint32_t valid =
-                wi == n_words - 1 && (N & 31) ? (1u << (N & 31)) - 1u : ~0u;
-            uint32_t hw[8];
             uint32_t un = 0;
 #pragma unroll
-            for (int hh = 0; hh < 8; ++hh) {
-                hw[hh] = (hh < hc.nh && wi < w_end) ? kb[hh * n_words + wi] & valid : 0u;
-                un |= hw[hh];
-            }
+            for (int hh = 0; hh < 8; ++hh) un |= hw[hh];
             const uint32_t cnt = (uint32_t)__popc(un);
             const uint32_t inc = wave_inclusive_scan(cnt);
             uint32_t pos = inc - cnt;

@@ -21,7 +21,7 @@ class DecodeLayer:
     mode "per_head": rtp_sparse_decode over each head's index list."""
 
     def __init__(self, B: int, Hq: int, Hkv: int, N: int, H_r: int, n_sink: int,
-                 window: int, device, d: int = 128, mode: str = "union"):
+                 window: int, device, d: int = 128, mode: str = "per_head"):
         if mode not in ("union", "per_head"):
             raise ValueError(f"unknown mode {mode!r}")
         self.B, self.Hq, self.Hkv, self.N, self.H_r = B, Hq, Hkv, N, H_r

@@ -231,17 +231,20 @@ def test_local_unaligned_head_range():
 
 # ------------------------------------------------------------ workspaces
 
-def test_workspace_garbage_and_reuse():
+@pytest.mark.parametrize("mode", ["per_head", "union"])
+def test_workspace_garbage_and_reuse(mode):
     # Workspaces start as arbitrary bytes (no initialisation is required),
     # are reused by the next call, and are then reused for a smaller call
     # whose layout differs.
     from sparse_long_context_indexer_amd.runner import DecodeLayer
     cfg = synth.CONFIGS[1]
     L = load_layer(cfg)
-    step = DecodeLayer(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.H_r, cfg.n_sink, cfg.window, dev())
+    step = DecodeLayer(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.H_r, cfg.n_sink, cfg.window, dev(),
+                       mode=mode)
     g = torch.Generator(device="cpu").manual_seed(7)
-    step.keep_bits.copy_(torch.randint(-2**31, 2**31 - 1, step.keep_bits.shape,
-                                       dtype=torch.int32, generator=g))
+    if step.keep_bits is not None:
+        step.keep_bits.copy_(torch.randint(-2**31, 2**31 - 1, step.keep_bits.shape,
+                                           dtype=torch.int32, generator=g))
     for ws in (step.ws_sel, step.ws_sparse, step.ws_local):
         ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=g))
     for rep in range(2):
@@ -251,7 +254,8 @@ def test_workspace_garbage_and_reuse():
         assert not fails, "\n".join(fails[:20])
     small = cfg.with_(N=20000, B=1)
     Ls = load_layer(small)
-    s2 = DecodeLayer(1, cfg.Hq, cfg.Hkv, 20000, cfg.H_r, cfg.n_sink, cfg.window, dev())
+    s2 = DecodeLayer(1, cfg.Hq, cfg.Hkv, 20000, cfg.H_r, cfg.n_sink, cfg.window, dev(),
+                     mode=mode)
     s2.ws_sparse, s2.ws_local, s2.ws_sel = step.ws_sparse, step.ws_local, step.ws_sel
     for ws in (step.ws_sparse, step.ws_local):
         ws[ws.numel() // 3:].fill_(0xFF)
