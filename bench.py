@@ -209,18 +209,34 @@ def main():
     steps_per_s = 1e3 / ms_step
     achieved_gbps = B_alg / (ms_step * 1e-3) / 1e9
 
-    # Dominant kernel: the indexer scan (one kernel per call).  Algorithmic
-    # bytes per launch: 64 B of k_r read + 4 B of score written per query
-    # head, per token and KV head.
-    scan_bytes = B * G_r * N * (cfg.r * 4 + cfg.G * 4)
-    scan_us = us["rtp_index_scores"]
-    roof = {"kernel": "index_scores_kernel<8>", "bound": "hbm",
-            "achieved": scan_bytes / (scan_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s"}
+    # Roofline of the dominant kernel: of the calls that launch one kernel
+    # (so HIP events around the call time that kernel alone), the one with the
+    # largest time per layer.  Algorithmic bytes per launch (one layer):
+    #   scan    64 B of k_r read + 4 B of score written per query head, per
+    #           token and retrieval KV head;
+    #   sparse  512 B (K + V row) per row of the union of the group's kept
+    #           sets (re-reads by several heads earn no credit) + the 4-B
+    #           indices read;
+    #   local   512 B per sink/window row per local KV head.
+    csrc = os.path.join(ROOT, "sparse_long_context_indexer_amd", "csrc")
+    sel_total = float(np.mean([sum(x) for x in n_sel]))
+    cands = {
+        "rtp_index_scores": ("index_scores_kernel<8>", B * G_r * N * (cfg.r * 4 + cfg.G * 4),
+                             "scan.hip"),
+        "rtp_sparse_decode": ("sparse_attn_kernel",
+                              float(np.mean(union)) * 2 * d * 2 + sel_total * 4, "attend.hip"),
+        "rtp_sparse_decode_union": ("union_attn_kernel",
+                                    float(np.mean(union)) * 2 * d * 2 + B * H_r * ((N + 31) // 32) * 4,
+                                    "attend.hip"),
+        "rtp_local_decode": ("local_attn_kernel", window_bytes, "attend.hip"),
+    }
+    call = max((c for c in cands if c in us), key=lambda c: us[c])
+    kname, kbytes, ksrc = cands[call]
+    roof = {"kernel": kname, "bound": "hbm",
+            "achieved": kbytes / (us[call] * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(os.path.join(ROOT, "profiles", "index_scores_pmc_ctx1m.md"),
-                                       os.path.join(ROOT, "sparse_long_context_indexer_amd",
-                                                    "csrc", "scan.hip"))
+    roof["traffic"] = measured_traffic(os.path.join(ROOT, "profiles", "hbm_traffic_ctx1m.md"),
+                                       kname, os.path.join(csrc, ksrc))
 
     # ---------------------------------------------------- CPU baseline
     cpu = None
@@ -260,24 +276,23 @@ def main():
         torch.cuda.synchronize()
 
 
-def measured_traffic(summary, source):
-    """HBM bytes per launch of the roofline kernel from the committed PMC
-    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's
-    reading for a copy of known size), or None when the kernel source has
-    changed since the counters were taken."""
+def measured_traffic(summary, kernel, source):
+    """HBM bytes per launch of `kernel` from the committed PMC summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a
+    copy of known size), or None when that kernel's source file has changed
+    since the counters were taken.  The summary holds lines
+    `traffic <kernel> <bytes per launch> <sha256 of its source file>`."""
     import hashlib
     try:
-        text = open(summary).read()
+        lines = open(summary).read().splitlines()
     except OSError:
         return None
-    fields = dict(l.split(":", 1) for l in text.splitlines()
-                  if l.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
-    if "source_sha256" not in fields or "traffic_bytes_per_launch" not in fields:
-        return None
     sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
-    if fields["source_sha256"].strip() != sha:
-        return None
-    return float(fields["traffic_bytes_per_launch"])
+    for line in lines:
+        f = line.split()
+        if len(f) == 4 and f[0] == "traffic" and f[1] == kernel:
+            return float(f[2]) if f[3] == sha else None
+    return None
 
 
 def cpu_baseline(cfg, p, target_s):
