@@ -12,9 +12,8 @@ constexpr int kWave = 64;
 // larger score, and equal scores (with -0 folded into +0) give equal keys.
 __device__ __forceinline__ uint32_t score_key(float s)
 {
-    uint32_t u = __float_as_uint(s);
-    if ((u & 0x7fffffffu) == 0u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(s + 0.0f);  // -0 + 0 is +0; nothing else changes
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float key_score(uint32_t k)
@@ -37,6 +36,57 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 &w, float f[8])
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// ---- cross-lane moves (DPP, gfx9 encoding; no LDS round trip)
+//
+// dpp<Ctrl, RowMask>(old, v): lane i receives v from the lane Ctrl names;
+// lanes in rows outside RowMask, or whose source lies outside their row,
+// receive `old`.  Works on any 4- or 8-byte type.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111;     // row_shr:n = 0x110 + n
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppWaveShr1 = 0x138;    // lane i <- lane i-1 across the wave
+constexpr int kDppRowMirror = 0x140;   // i <- 15-i within 16 lanes
+constexpr int kDppRowHalfMirror = 0x141;  // i <- 7-i within 8 lanes
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+
+template <int Ctrl, int RowMask = 0xf, typename T>
+__device__ __forceinline__ T dpp(T old, T v)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte lanes");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(
+            T, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                           Ctrl, RowMask, 0xf, false));
+    } else {
+        const unsigned long long o = __builtin_bit_cast(unsigned long long, old);
+        const unsigned long long x = __builtin_bit_cast(unsigned long long, v);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)o, (int)(uint32_t)x,
+                                                                  Ctrl, RowMask, 0xf, false);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(
+            (int)(uint32_t)(o >> 32), (int)(uint32_t)(x >> 32), Ctrl, RowMask, 0xf, false);
+        return __builtin_bit_cast(T, (unsigned long long)lo | ((unsigned long long)hi << 32));
+    }
+}
+
+// Value of v in lane `lane` (wave-uniform), for every lane.
+template <typename T>
+__device__ __forceinline__ T read_lane(T v, int lane)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte lanes");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+    } else {
+        const unsigned long long x = __builtin_bit_cast(unsigned long long, v);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+        return __builtin_bit_cast(T, (unsigned long long)lo | ((unsigned long long)hi << 32));
+    }
+}
+
 // Slot reservation for a wave: every lane of the wave must call this with
 // the same counter.  Lanes with pred=true get distinct slots (one atomic per
 // wave); the others get -1.
@@ -48,66 +98,78 @@ __device__ __forceinline__ int64_t wave_append(bool pred, uint32_t *counter)
     const int lane = lane_id();
     uint32_t base = 0;
     if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-    base = __shfl(base, leader);
+    base = read_lane(base, leader);
     if (!pred) return -1;
     const uint64_t below = (lane == 0) ? 0ull : (mask & (~0ull >> (64 - lane)));
     return (int64_t)base + __popcll(below);
 }
 
+// Inclusive prefix sum over the wave in lane order: a scan within each row
+// of 16 lanes, then the row totals carried into the rows above.
 template <typename T>
 __device__ __forceinline__ T wave_inclusive_scan(T v)
 {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        T o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
+    v += dpp<kDppRowShr1>(T(0), v);
+    v += dpp<kDppRowShr2>(T(0), v);
+    v += dpp<kDppRowShr4>(T(0), v);
+    v += dpp<kDppRowShr8>(T(0), v);
+    v += dpp<kDppRowBcast15, 0xa>(T(0), v);
+    v += dpp<kDppRowBcast31, 0xc>(T(0), v);
     return v;
 }
 
+// The exclusive prefix from the inclusive one: each lane takes the lane
+// below's (lane 0 takes 0).
+template <typename T>
+__device__ __forceinline__ T wave_shift_up(T inc)
+{
+    return dpp<kDppWaveShr1>(T(0), inc);
+}
+
+// Sum over the wave, in every lane: each row of 16 lanes is reduced in
+// place, then the four row totals are added in row order.
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v)
 {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+    v += dpp<kDppQuadXor1>(v, v);
+    v += dpp<kDppQuadXor2>(v, v);
+    v += dpp<kDppRowHalfMirror>(v, v);
+    v += dpp<kDppRowMirror>(v, v);
+    return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
+    v = fmaxf(v, dpp<kDppQuadXor1>(v, v));
+    v = fmaxf(v, dpp<kDppQuadXor2>(v, v));
+    v = fmaxf(v, dpp<kDppRowHalfMirror>(v, v));
+    v = fmaxf(v, dpp<kDppRowMirror>(v, v));
+    return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
 }
 
 // Exclusive prefix sum over a block of NT threads in thread order; every
-// thread must call it.  `scratch` holds NT/64 + 1 elements of LDS.  Returns
-// the exclusive prefix; *total receives the block-wide sum.
+// thread must call it.  `scratch` holds NT/64 elements of LDS.  Returns
+// the exclusive prefix; *total receives the block-wide sum.  Every thread
+// adds the wave totals in the same order, so all agree on *total.
 template <int NT, typename T>
 __device__ __forceinline__ T block_exclusive_scan(T v, T *scratch, T *total)
 {
     constexpr int NW = NT / kWave;
-    const int lane = lane_id();
     const int w = (int)threadIdx.x / kWave;
-    T inc = wave_inclusive_scan(v);
-    T prev = __shfl_up(inc, 1);
-    if (lane == kWave - 1) scratch[w] = inc;
+    const T inc = wave_inclusive_scan(v);
+    const T prev = wave_shift_up(inc);
+    if (lane_id() == kWave - 1) scratch[w] = inc;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        T run = T(0);
-        for (int i = 0; i < NW; ++i) {
-            T t = scratch[i];
-            scratch[i] = run;
-            run += t;
-        }
-        scratch[NW] = run;
+    T before = T(0), run = T(0);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const T t = scratch[i];
+        if (i == w) before = run;
+        run += t;
     }
+    *total = run;
     __syncthreads();
-    T ex = scratch[w] + (lane == 0 ? T(0) : prev);
-    *total = scratch[NW];
-    __syncthreads();
-    return ex;
+    return before + prev;
 }
 
 // Cross-block hand-off inside one kernel.  Data another block of the same

@@ -51,11 +51,14 @@ constexpr double kExpInvStep = 0x1.71547652b82fep+6;  // 64 / ln 2
 constexpr double kExpStepHi = 0x1.62e42fefa0000p-7;   // ln2/64 to 36 significant bits
 constexpr double kExpStepLo = 0x1.cf79abc9e3b3ap-46;  // ln2/64 - kExpStepHi
 
-// exp(x) for x <= 709; `tbl` holds RTP_EXP2_TABLE.  Returns +0 below -745.5
-// (where exp rounds to zero) and for x = -inf.
+// exp(x) for x <= 709; `tbl` holds RTP_EXP2_TABLE.  The reduction runs on
+// max(x, -745.5), whose exp rounds to +0, so the result is +0 for every x
+// below that, for x = -inf, and for NaN (max returns the other operand): a
+// mass term of a NaN score is 0.  No branch and no select, so the callers'
+// loops stay free of divergence.
 RTP_HD inline double exp_tang(double x, const double *tbl)
 {
-    if (!(x >= -745.5)) return x != x ? x : 0.0;
+    x = fmax(x, -745.5);
     const double n = rint(x * kExpInvStep);
     double r = fma(-n, kExpStepHi, x);
     r = fma(-n, kExpStepLo, r);

@@ -7,23 +7,26 @@
 // found exactly, without sorting, as a mass-weighted radix select over the
 // 64-bit composite key (order-preserving score key, then token index):
 //
-//   zero    clears the level-1 histograms and the per-row state
 //   hist    one block per 32768-score chunk: per level-1 bin (score key bits
 //           [31:20], 4096 bins) the fp64 mass exp(s - top(bin)), top(bin)
 //           being the bin's largest representable score, merged into the
 //           row's histogram with global atomics; the chunk's own top bin is
 //           kept apart, as mass exp(s - m_b) with m_b the chunk max, so every
-//           term is <= 1 and nothing overflows for any finite input.
-//           The row's last block to finish then runs the pick: M = max m_b,
-//           the histogram rescaled to exp(s - M), Z, the target p*Z, the
-//           boundary bin j1 (the highest bin whose running mass from the top
-//           reaches the target) and the mass A above it
-//   emit    tokens in bins above j1 are kept; tokens of bin j1 become
-//           candidates (key, index).  The row's last block to finish then
-//           resolves: the same step over key bits [19:10], then [9:0] (the
-//           boundary is now one score value tau), then how many tokens of
-//           score tau are needed and, if not all of them, the lowest indices
-//           among them by a count-only radix select over the index bits
+//           term is <= 1 and nothing overflows for any finite input.  Block 0
+//           of each row first clears the row's state.
+//   emit    every block first derives its row's threshold from the finished
+//           histogram (the pick): M = max m_b, the histogram rescaled to
+//           exp(s - M), Z, the target p*Z, the boundary bin j1 (the highest
+//           bin whose running mass from the top reaches the target) and the
+//           mass A above it.  The same inputs and arithmetic give every block
+//           of a row the same result, and the histogram loads overlap the
+//           chunk's score loads.  Tokens in bins above j1 are kept; tokens of
+//           bin j1 become candidates (key, index) and are counted by key bits
+//           [19:10].  The row's last block to finish then resolves: the same
+//           step over key bits [19:10], then [9:0] (the boundary is now one
+//           score value tau), then how many tokens of score tau are needed
+//           and, if not all of them, the lowest indices among them by a
+//           count-only radix select over the index bits
 //
 // Masses are fp64 (exp_tang, a table-driven fp64 exp within 1.3 ulp, and
 // fp64 sums), so running sums agree with an fp64 reference to ~1e-15
@@ -44,22 +47,16 @@ constexpr int kShift1 = 20;                  // level-1 bin = score key bits [31
 constexpr int kBins1 = 1 << (32 - kShift1);  // 4096 bins
 constexpr int kShift2 = 10;                  // refinement digits: key bits [19:10], [9:0]
 constexpr int kDig = 1 << kShift2;           // 1024 digits per refinement level
-constexpr int kPickThreads = 1024;
 constexpr int kResThreads = 1024;
 constexpr int kResBins = 2048;
 constexpr int kResCap = 8192;  // candidates resolved from LDS (two buffers)
 
 struct SelRow {
-    double Z;        // sum of exp(s - M) over the row
-    double A;        // mass above the level-1 boundary bin
-    double T;        // p * Z
-    float M;         // row max
-    uint32_t j1;     // level-1 boundary bin
-    uint64_t slots;  // emit's slot counters: kept (high 32 bits), candidates (low)
+    uint64_t slots;      // emit's slot counters: kept (high 32 bits), candidates (low)
     uint32_t hist_done;  // hist blocks finished
     uint32_t emit_done;  // emit blocks finished
     unsigned long long ready;  // tagged: the row's state below was cleared
-    uint32_t pad[2];
+    uint32_t pad[10];
 };
 static_assert(sizeof(SelRow) == 64, "SelRow is one 64-B record");
 
@@ -193,8 +190,8 @@ __device__ __forceinline__ ChunkView load_chunk(const float *__restrict__ sr, in
 // tagged `ready` counter; the row's other blocks wait for it before their
 // first global add, which comes after their whole LDS pass, so the wait is
 // almost always already over.  Block 0 is dispatched before the row's other
-// blocks (it has the lowest index), so the wait always ends.  The pick
-// resets `ready` for the next call.
+// blocks (it has the lowest index), so the wait always ends.  The row's
+// last hist block resets `ready` for the next call.
 
 __device__ void clear_row(SelPtrs P, int64_t r)
 {
@@ -229,23 +226,16 @@ __device__ void wait_row_ready(const SelRow &row)
 // 2^(j/64) for exp_tang; each kernel copies it to LDS.
 __constant__ double kExp2Tbl[kExpTable] = RTP_EXP2_TABLE;
 
-struct PickShared {
+struct HistShared {
     double hm[kBins1];
     double etbl[kExpTable];
-    double scan[kPickThreads / kWave + 1];
-    float red[kPickThreads / kWave];
-    int chosen;  // highest bin whose running mass reaches T
-    int lowest;  // lowest bin with mass
-    int last;
+    float red[kSelThreads / kWave];
 };
 
-__device__ void pick_row(SelPtrs P, int64_t r, float p, PickShared &S);
-
 __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__restrict__ scores,
-                                                               int N, SelPtrs P, float p)
+                                                               int N, SelPtrs P)
 {
-    static_assert(kSelThreads == kPickThreads, "the last hist block runs the pick");
-    __shared__ PickShared S;
+    __shared__ HistShared S;
     double *hm = S.hm;
     float *red = S.red;
     const int64_t r = blockIdx.y;
@@ -266,13 +256,14 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
     float mb = red[0];
     for (int i = 1; i < kSelThreads / kWave; ++i) mb = fmaxf(mb, red[i]);
     const uint32_t tb = score_key(mb) >> kShift1;
-    const double mbd = (double)mb;
-#pragma unroll 8
+    // s - ref is exact in fp32: a bin's scores and its reference share one
+    // sign and binade.  A slot past the end of the row (-inf) has a NaN
+    // reference, and exp_tang gives NaN +0.
+#pragma unroll
     for (int t = 0; t < kSelPerThread; ++t) {
-        if (v[t] == -INFINITY) continue;  // past the end of the row
         const uint32_t bin = score_key(v[t]) >> kShift1;
-        const double ref = bin == tb ? mbd : (double)bin_top(bin);
-        atomicAdd(&hm[bin], exp_tang((double)v[t] - ref, S.etbl));
+        const float ref = bin == tb ? mb : bin_top(bin);
+        atomicAdd(&hm[bin], exp_tang((double)(v[t] - ref), S.etbl));
     }
     if (blk != 0 && threadIdx.x == 0) wait_row_ready(P.rows[r]);
     __syncthreads();
@@ -283,123 +274,12 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
     }
     if (threadIdx.x == 0) {
         ChunkTop &t = P.tops[r * P.nblk + blk];
-        st_agent(&t.m, mb);
-        st_agent(&t.mass, hm[tb]);
-    }
-    // The last chunk of the row to finish computes the row's threshold; it
-    // reads the others' histogram atomics and chunk tops with agent-scope
-    // loads once every block's writes have completed.
-    wait_vmem();
-    __syncthreads();
-    if (threadIdx.x == 0) S.last = atomicAdd(&P.rows[r].hist_done, 1u) == (uint32_t)(P.nblk - 1);
-    __syncthreads();
-    if (!S.last) return;
-    if (threadIdx.x == 0) ctr_reset(&P.rows[r].ready);
-    pick_row(P, r, p, S);
-}
-
-// --------------------------------------------------------------- pick
-
-__device__ void pick_row(SelPtrs P, int64_t r, float p, PickShared &S)
-{
-    constexpr int kPer = kBins1 / kPickThreads;  // bins per thread
-    constexpr int kNW = kPickThreads / kWave;
-    double *hm = S.hm;
-    double *scan = S.scan;
-    float *red = S.red;
-    int &chosen = S.chosen;
-    int &lowest = S.lowest;
-    const ChunkTop *tops = P.tops + r * P.nblk;
-    const Hist1 &g = P.hist1[r];
-    const int tid = threadIdx.x;
-
-    // Every load up front, so the block waits for memory once.
-    double gmv[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) gmv[k] = ld_agent(&g.mass[tid + k * kPickThreads]);
-    float tm0 = -INFINITY;
-    double tmass0 = 0.0;
-    if (tid < P.nblk) {
-        tm0 = ld_agent(&tops[tid].m);
-        tmass0 = ld_agent(&tops[tid].mass);
-    }
-    float m = tm0;
-    for (int k = tid + kPickThreads; k < P.nblk; k += kPickThreads) m = fmaxf(m, ld_agent(&tops[k].m));
-    __syncthreads();  // the block's own histogram in hm is done with
-    m = wave_max(m);
-    if (lane_id() == 0) red[tid / kWave] = m;
-    if (tid == 0) {
-        chosen = -1;
-        lowest = kBins1;
-    }
-    __syncthreads();
-    float Mf = red[0];
-    for (int i = 1; i < kNW; ++i) Mf = fmaxf(Mf, red[i]);
-    const double M = (double)Mf;
-    // A bin counted in Hist1 lies below some chunk's top bin, so its top
-    // score is below M: every factor is <= 1.
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int i = tid + k * kPickThreads;
-        hm[i] = gmv[k] > 0.0 ? gmv[k] * exp_tang((double)bin_top(i) - M, S.etbl) : 0.0;
-    }
-    __syncthreads();
-    if (tid < P.nblk)
-        atomicAdd(&hm[score_key(tm0) >> kShift1], tmass0 * exp_tang((double)tm0 - M, S.etbl));
-    for (int k = tid + kPickThreads; k < P.nblk; k += kPickThreads) {
-        const float tm = ld_agent(&tops[k].m);
-        atomicAdd(&hm[score_key(tm) >> kShift1], ld_agent(&tops[k].mass) * exp_tang((double)tm - M, S.etbl));
-    }
-    __syncthreads();
-
-    // Thread t owns bins top - t*kPer - [0, kPer): thread order is score order.
-    const int top = kBins1 - 1 - tid * kPer;
-    double wv[kPer];
-    double local = 0.0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        wv[k] = hm[top - k];
-        local += wv[k];
-    }
-    double Z;
-    const double before = block_exclusive_scan<kPickThreads>(local, scan, &Z);
-    const double T = (double)p * Z;
-    // The boundary is the highest bin with mass whose running sum (every bin
-    // down to and including it) reaches T; each thread tests its own bins,
-    // so no rounding of the block prefix can skip it.  If the total stays
-    // below T, the lowest bin with mass.  Bins whose mass underflows to 0
-    // hold nothing a prefix can need.
-    double cum = before;
-    int my_cross = -1, my_lowest = -1;
-    double cross_before = 0.0, lowest_before = 0.0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        if (wv[k] > 0.0) {
-            if (my_cross < 0 && cum + wv[k] >= T) {
-                my_cross = top - k;
-                cross_before = cum;
-            }
-            my_lowest = top - k;
-            lowest_before = cum;
-        }
-        cum += wv[k];
-    }
-    if (my_cross >= 0) atomicMax(&chosen, my_cross);
-    if (my_lowest >= 0) atomicMin(&lowest, my_lowest);
-    __syncthreads();
-    if (chosen >= 0) {
-        if (my_cross == chosen) {
-            P.rows[r].j1 = (uint32_t)my_cross;
-            P.rows[r].A = cross_before;
-        }
-    } else if (my_lowest >= 0 && my_lowest == lowest) {
-        P.rows[r].j1 = (uint32_t)my_lowest;
-        P.rows[r].A = lowest_before;
-    }
-    if (tid == 0) {
-        P.rows[r].Z = Z;
-        P.rows[r].T = T;
-        P.rows[r].M = Mf;
+        t.m = mb;
+        t.mass = hm[tb];
+        // Every block of the row has passed its wait once all have counted
+        // themselves here, so the last one resets `ready` for the next call.
+        if (atomicAdd(&P.rows[r].hist_done, 1u) == (uint32_t)(P.nblk - 1))
+            ctr_reset(&P.rows[r].ready);
     }
 }
 
@@ -423,11 +303,23 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
 constexpr int kResNW = kResThreads / kWave;
 
 struct ResShared {
+    // The pick's level-1 histogram (aliased), then emit's candidate stage,
+    // then the resolve's candidate buffers.
     uint2 buf[2][kResCap];
     double etbl[kExpTable];
     double hm[kResBins];
     uint32_t hc[kResBins];
     uint32_t uscan[kResNW + 1];
+    double dscan[kResNW + 1];
+    float red[kResNW];
+    // pick: per wave, its first crossing bin and its last bin with mass
+    int wcross[kResNW], wlow[kResNW];
+    double wcross_before[kResNW], wlow_before[kResNW];
+    // The row's threshold (the same in every block of the row)
+    float M;      // row max
+    uint32_t j1;  // level-1 boundary bin
+    double A;     // mass above bin j1
+    double T;     // p * Z
     uint32_t nout;   // tokens kept by this block so far
     uint32_t nnext;  // candidates moved to the other buffer
     uint32_t j;      // chosen digit
@@ -438,6 +330,114 @@ struct ResShared {
     unsigned long long bcount, gbase;
     int last;
 };
+static_assert(sizeof(double) * kBins1 <= sizeof(uint2) * kResCap, "pick histogram fits in buf");
+
+// --------------------------------------------------------------- pick
+//
+// The row's threshold from its finished level-1 histogram (g) and chunk
+// tops; gmv holds this thread's bins tid + k*kSelThreads, tm0/tmass0 the
+// top of chunk tid (when tid < nblk).  Leaves M, T, j1 and A in S.
+constexpr int kPickPer = kBins1 / kSelThreads;  // bins per thread
+
+__device__ void pick_block(const ChunkTop *tops, int nblk, float p, const double (&gmv)[kPickPer],
+                           float tm0, double tmass0, ResShared &S)
+{
+    double *hm = reinterpret_cast<double *>(&S.buf[0][0]);
+    const int tid = threadIdx.x;
+    float m = tm0;
+    for (int k = tid + kSelThreads; k < nblk; k += kSelThreads) m = fmaxf(m, tops[k].m);
+    m = wave_max(m);
+    if (lane_id() == 0) S.red[tid / kWave] = m;
+    __syncthreads();
+    float Mf = S.red[0];
+    for (int i = 1; i < kResNW; ++i) Mf = fmaxf(Mf, S.red[i]);
+    const double M = (double)Mf;
+    // A bin counted in Hist1 lies below some chunk's top bin, so its top
+    // score is below M: every factor is <= 1.
+#pragma unroll
+    for (int k = 0; k < kPickPer; ++k) {
+        const int i = tid + k * kSelThreads;
+        hm[i] = gmv[k] > 0.0 ? gmv[k] * exp_tang((double)bin_top(i) - M, S.etbl) : 0.0;
+    }
+    __syncthreads();
+    if (tid < nblk)
+        atomicAdd(&hm[score_key(tm0) >> kShift1], tmass0 * exp_tang((double)tm0 - M, S.etbl));
+    for (int k = tid + kSelThreads; k < nblk; k += kSelThreads) {
+        const float tm = tops[k].m;
+        atomicAdd(&hm[score_key(tm) >> kShift1], tops[k].mass * exp_tang((double)tm - M, S.etbl));
+    }
+    __syncthreads();
+
+    // Thread t owns bins top - t*kPickPer - [0, kPickPer): thread order is
+    // score order.
+    const int top = kBins1 - 1 - tid * kPickPer;
+    double wv[kPickPer];
+    double local = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPickPer; ++k) {
+        wv[k] = hm[top - k];
+        local += wv[k];
+    }
+    double Z;
+    const double before = block_exclusive_scan<kSelThreads>(local, S.dscan, &Z);
+    const double T = (double)p * Z;
+    // The boundary is the highest bin with mass whose running sum (every bin
+    // down to and including it) reaches T; each thread tests its own bins,
+    // so no rounding of the block prefix can skip it.  If the total stays
+    // below T, the lowest bin with mass.  Bins whose mass underflows to 0
+    // hold nothing a prefix can need.
+    double cum = before;
+    int my_cross = -1, my_lowest = -1;
+    double cross_before = 0.0, lowest_before = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPickPer; ++k) {
+        if (wv[k] > 0.0) {
+            if (my_cross < 0 && cum + wv[k] >= T) {
+                my_cross = top - k;
+                cross_before = cum;
+            }
+            my_lowest = top - k;
+            lowest_before = cum;
+        }
+        cum += wv[k];
+    }
+    // Thread order is score order: the highest crossing bin belongs to the
+    // first thread with a crossing, the lowest bin with mass to the last
+    // thread with mass.  Each wave reports its own first / last such lane.
+    const int lane = lane_id(), w = tid / kWave;
+    const uint64_t cm = __ballot(my_cross >= 0);
+    const uint64_t lm = __ballot(my_lowest >= 0);
+    if (lane == 0) {
+        S.wcross[w] = -1;
+        S.wlow[w] = -1;
+    }
+    if (cm && lane == __ffsll((unsigned long long)cm) - 1) {
+        S.wcross[w] = my_cross;
+        S.wcross_before[w] = cross_before;
+    }
+    if (lm && lane == 63 - __clzll((unsigned long long)lm)) {
+        S.wlow[w] = my_lowest;
+        S.wlow_before[w] = lowest_before;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int wc = -1, wl = -1;
+        for (int i = 0; i < kResNW && wc < 0; ++i)
+            if (S.wcross[i] >= 0) wc = i;
+        for (int i = kResNW - 1; i >= 0 && wl < 0; --i)
+            if (S.wlow[i] >= 0) wl = i;
+        if (wc >= 0) {
+            S.j1 = (uint32_t)S.wcross[wc];
+            S.A = S.wcross_before[wc];
+        } else {
+            S.j1 = wl >= 0 ? (uint32_t)S.wlow[wl] : 0u;
+            S.A = wl >= 0 ? S.wlow_before[wl] : 0.0;
+        }
+        S.T = T;
+        S.M = Mf;
+    }
+    __syncthreads();
+}
 
 // Wave 0 chooses the boundary digit of a score level from S.hm/S.hc over
 // digits 0..kDig-1: the highest non-empty digit whose running mass (A plus
@@ -556,7 +556,7 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
                                    int32_t *ir, uint32_t *kbr, ResShared &S)
 {
     // From global memory, kB loads per thread are in flight before any is used.
-    constexpr int kB = kGlobal ? 8 : 1;
+    constexpr int kB = kGlobal ? 10 : 1;
     if (threadIdx.x == 0) S.nnext = 0u;
     __syncthreads();
     for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kResThreads * kB) {
@@ -592,9 +592,9 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
         ld_agent(reinterpret_cast<const unsigned long long *>(&row.slots));
     const double h2m = ld_agent(&P.hist2[r].mass[tid]);
     const uint32_t h2c = ld_agent(&P.hist2[r].cnt[tid]);
-    const double M = (double)row.M;
-    const double T = row.T;
-    double A = row.A;
+    const double M = (double)S.M;
+    const double T = S.T;
+    double A = S.A;
     int64_t n = (uint32_t)slots;
     const uint32_t emitted = (uint32_t)(slots >> 32);  // kept by emit
     int32_t *ir = idx + r * (int64_t)N + emitted;
@@ -712,33 +712,58 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
 }
 
 __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
-    const float *__restrict__ scores, int N, SelPtrs P, int32_t *__restrict__ idx,
+    const float *__restrict__ scores, int N, SelPtrs P, float p, int32_t *__restrict__ idx,
     int32_t *__restrict__ count, uint32_t *__restrict__ keep_bits)
 {
     static_assert(kSelThreads == kResThreads, "the last emit block runs the resolve");
     __shared__ ResShared S;
     unsigned long long *wbase = S.wbase;
-    if (threadIdx.x < kExpTable) S.etbl[threadIdx.x] = kExp2Tbl[threadIdx.x];
     const int64_t r = blockIdx.y;
-    const uint32_t j1 = P.rows[r].j1;
     const float *sr = scores + r * (int64_t)N;
     int32_t *ir = idx + r * (int64_t)N;
     uint2 *cr = P.cand + r * (int64_t)N;
+    // The row's histogram and chunk tops (finished by the hist kernel) are
+    // requested together with the chunk's scores.
+    const ChunkTop *tops = P.tops + r * P.nblk;
+    const Hist1 &g = P.hist1[r];
+    double gmv[kPickPer];
+#pragma unroll
+    for (int k = 0; k < kPickPer; ++k) gmv[k] = g.mass[threadIdx.x + k * kSelThreads];
+    float tm0 = -INFINITY;
+    double tmass0 = 0.0;
+    if ((int)threadIdx.x < P.nblk) {
+        tm0 = tops[threadIdx.x].m;
+        tmass0 = tops[threadIdx.x].mass;
+    }
     float v[kSelPerThread];
     const ChunkView cv = load_chunk(sr, N, (int64_t)blockIdx.x * kSelChunk, v);
+    if (threadIdx.x < kExpTable) S.etbl[threadIdx.x] = kExp2Tbl[threadIdx.x];
+    pick_block(tops, P.nblk, p, gmv, tm0, tmass0, S);
+    const uint32_t j1 = S.j1;
     if (threadIdx.x == 0) S.bcount = 0ull;
     S.hm[threadIdx.x] = 0.0;  // this block's share of the row's Hist2
     S.hc[threadIdx.x] = 0u;
     // Per lane: bit t of `above` / `atb` marks slot t as kept / candidate;
     // `mine` packs their counts (kept in the high half).
     static_assert(kSelPerThread == 32, "one mask bit per slot");
+    // Keys above hi lie in bins above j1; keys in [lo, hi] in bin j1.
+    const uint32_t lo = j1 << kShift1, hi = lo | ((1u << kShift1) - 1u);
     uint32_t above = 0, atb = 0;
+    if (cv.vec) {
 #pragma unroll
-    for (int t = 0; t < kSelPerThread; ++t) {
-        const uint32_t bin = score_key(v[t]) >> kShift1;
-        const bool valid = cv.vec || cv.index32(t) < (uint32_t)N;
-        above |= (valid && bin > j1) ? (1u << t) : 0u;
-        atb |= (valid && bin == j1) ? (1u << t) : 0u;
+        for (int t = 0; t < kSelPerThread; ++t) {
+            const uint32_t key = score_key(v[t]);
+            above |= key > hi ? (1u << t) : 0u;
+            atb |= (key >= lo && key <= hi) ? (1u << t) : 0u;
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < kSelPerThread; ++t) {
+            const uint32_t key = score_key(v[t]);
+            const bool valid = cv.index32(t) < (uint32_t)N;
+            above |= (valid && key > hi) ? (1u << t) : 0u;
+            atb |= (valid && key >= lo && key <= hi) ? (1u << t) : 0u;
+        }
     }
     const uint32_t mine = ((uint32_t)__popc(above) << 16) | (uint32_t)__popc(atb);
     // Keep bitmap: this chunk's words, with the bits of the tokens kept here
@@ -754,9 +779,9 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
 #pragma unroll
             for (int g = 0; g < kSelPerThread / 4; ++g) {
                 uint32_t wv = ((above >> (4 * g)) & 0xFu) << (4 * (lane & 7));
-                wv |= __shfl_xor(wv, 1);
-                wv |= __shfl_xor(wv, 2);
-                wv |= __shfl_xor(wv, 4);
+                wv |= dpp<kDppQuadXor1>(wv, wv);
+                wv |= dpp<kDppQuadXor2>(wv, wv);
+                wv |= dpp<kDppRowHalfMirror>(wv, wv);
                 if ((lane & 7) == 0) st_agent(kw + g * 128 + (threadIdx.x >> 3), wv);
             }
         } else {
@@ -776,7 +801,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     // carry), then one LDS atomic per wave for its block offset and one
     // global atomic per block for its row offset.
     const uint32_t inc = wave_inclusive_scan(mine);
-    const uint32_t wtot = __shfl(inc, kWave - 1);
+    const uint32_t wtot = read_lane(inc, kWave - 1);
     __syncthreads();
     const int w = threadIdx.x / kWave;
     if (lane_id() == 0)
@@ -812,7 +837,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     __syncthreads();
     // This block's share of the row's Hist2: candidates by key bits
     // [19:10], with mass exp(s - M).
-    const double M = (double)P.rows[r].M;
+    const double M = (double)S.M;
     for (uint32_t k = threadIdx.x; k < bc; k += kSelThreads) {
         const uint2 e = staged ? stage[k] : ld_cand(gcb + k);
         if (staged) st_cand(gcb + k, e);
@@ -863,8 +888,8 @@ hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p, in
     }
     SelPtrs P = sel_ptrs(ws, R, N);
     dim3 grid((unsigned)P.nblk, (unsigned)R);
-    RTP_TRY(launch(sel_hist_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, p));
-    return launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, idx, count,
+    RTP_TRY(launch(sel_hist_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P));
+    return launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, p, idx, count,
                   keep_bits);
 }
 
