@@ -32,12 +32,14 @@ constexpr int kLocalRows = 64;       // rows per local split (at least)
 constexpr int kMaxLocalSplits = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Sum over each row of 16 lanes, in every lane of the row (DPP: quads,
+// then mirrored halves, then mirrored rows).
 __device__ __forceinline__ float sum16(float v)
 {
-    v += __shfl_xor(v, 1, 16);
-    v += __shfl_xor(v, 2, 16);
-    v += __shfl_xor(v, 4, 16);
-    v += __shfl_xor(v, 8, 16);
+    v += dpp<kDppQuadXor1>(v, v);
+    v += dpp<kDppQuadXor2>(v, v);
+    v += dpp<kDppRowHalfMirror>(v, v);
+    v += dpp<kDppRowMirror>(v, v);
     return v;
 }
 
@@ -175,7 +177,8 @@ __device__ void merge_partials(const float *pr, int n, float *dst_part, float *d
                                MergeShared &S)
 {
     constexpr int kG = kAttThreads / 128;
-    constexpr int kPer = kSlice / kG;  // partials per thread
+    constexpr int kPer = kSlice / kG;   // partials per thread
+    constexpr int kW = (kSlice + kWave - 1) / kWave;  // partials per lane of wave 0
     const int tid = threadIdx.x;
     const int c = tid & 127, grp = tid >> 7;
     // Every load is issued before any is used: the output columns of this
@@ -188,12 +191,25 @@ __device__ void merge_partials(const float *pr, int n, float *dst_part, float *d
     }
     if (tid < kWave) {
         // wave 0: the merged max, the factors and the merged sum
-        const float m = tid < n ? ld_agent(pr + (int64_t)tid * kPart) : -INFINITY;
-        const float lp = tid < n ? ld_agent(pr + (int64_t)tid * kPart + 1) : 0.0f;
-        const float M = wave_max(m);
-        const float f = tid < n ? rescale(m, M) : 0.0f;
-        const float l = wave_sum(lp * f);
-        if (tid < n) S.f[tid] = f;
+        float m[kW], lp[kW];
+        float mm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+            const int k = tid + i * kWave;
+            m[i] = k < n ? ld_agent(pr + (int64_t)k * kPart) : -INFINITY;
+            lp[i] = k < n ? ld_agent(pr + (int64_t)k * kPart + 1) : 0.0f;
+            mm = fmaxf(mm, m[i]);
+        }
+        const float M = wave_max(mm);
+        float ls = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+            const int k = tid + i * kWave;
+            const float f = k < n ? rescale(m[i], M) : 0.0f;
+            ls = fmaf(lp[i], f, ls);
+            if (k < n) S.f[k] = f;
+        }
+        const float l = wave_sum(ls);
         if (tid == 0) {
             S.M = M;
             S.L = l;
@@ -267,18 +283,28 @@ __global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[c] = 0.0f;
 
+    // The next iteration's row indices are requested while this one's rows
+    // are gathered and used.
+    int tn[kSparseU];
+    auto load_idx = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < kSparseU; ++u) {
+            const int j = base + u * kGroups + w * 4 + grp;
+            tn[u] = j < end ? ir[j] : -1;
+        }
+    };
+    if (begin < end) load_idx(begin);
     for (int base = begin; base < end; base += kRowsPerIter) {
         uint4 kw[kSparseU], vw[kSparseU];
         bool ok[kSparseU];
 #pragma unroll
         for (int u = 0; u < kSparseU; ++u) {
-            const int j = base + u * kGroups + w * 4 + grp;
-            int t = j < end ? ir[j] : -1;
-            ok[u] = (unsigned)t < (unsigned)N;
-            const int64_t off = ok[u] ? (int64_t)t * 128 : 0;
+            ok[u] = (unsigned)tn[u] < (unsigned)N;
+            const int64_t off = ok[u] ? (int64_t)tn[u] * 128 : 0;
             kw[u] = *reinterpret_cast<const uint4 *>(Kb + off);
             vw[u] = *reinterpret_cast<const uint4 *>(Vb + off);
         }
+        if (base + kRowsPerIter < end) load_idx(base + kRowsPerIter);
         float lg[kSparseU];
         float mx = -INFINITY;
 #pragma unroll

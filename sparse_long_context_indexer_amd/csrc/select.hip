@@ -320,8 +320,10 @@ struct ResShared {
     uint32_t j1;  // level-1 boundary bin
     double A;     // mass above bin j1
     double T;     // p * Z
-    uint32_t nout;   // tokens kept by this block so far
-    uint32_t nnext;  // candidates moved to the other buffer
+    // Two counters in one word, so a wave reserves both with one atomic:
+    // tokens kept by this block so far (low half) and candidates moved to
+    // the other buffer (high half).
+    unsigned long long nn;
     uint32_t j;      // chosen digit
     uint32_t cbefore;
     double abefore;  // A plus the mass above the chosen digit
@@ -519,6 +521,9 @@ __device__ __forceinline__ void keep_token(int32_t *ir, int64_t pa, uint32_t i, 
     if (kbr) atomicOr(kbr + (i >> 5), 1u << (i & 31u));
 }
 
+// The kept-token counter (the low half of S.nn).
+__device__ __forceinline__ uint32_t *nout_ptr(ResShared &S) { return reinterpret_cast<uint32_t *>(&S.nn); }
+
 // Ordered in-place filter for candidates in global memory (see the header
 // comment); survivors keep their relative order.
 __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t mask,
@@ -534,7 +539,7 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
         const uint32_t dg = (field >> shift) & mask;
         const bool out = valid && (emit_above ? dg > keep_digit : dg < keep_digit);
         const bool keep = valid && dg == keep_digit;
-        const int64_t pa = wave_append(out, &S.nout);
+        const int64_t pa = wave_append(out, nout_ptr(S));
         if (pa >= 0) keep_token(ir, pa, e.y, kbr);
         uint32_t tot;
         const uint32_t pos = block_exclusive_scan<kResThreads>((uint32_t)keep, S.uscan, &tot);
@@ -549,15 +554,19 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
 
 // One pass over n candidates in src (LDS, or global memory when kGlobal):
 // emits the kept side of digit j, moves digit j's candidates to dst (LDS,
-// which must hold them).  Returns the number moved.
+// which must hold them).  Returns the number moved.  Each thread takes kB
+// candidates at a time; a wave reserves the slots of all of them with one
+// LDS atomic (both counts packed in 16-bit halves, which never carry: a
+// wave holds at most 64 * kB of each).
 template <bool kGlobal>
 __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int shift,
                                    uint32_t mask, uint32_t j, bool emit_above, bool by_index,
                                    int32_t *ir, uint32_t *kbr, ResShared &S)
 {
     // From global memory, kB loads per thread are in flight before any is used.
-    constexpr int kB = kGlobal ? 10 : 1;
-    if (threadIdx.x == 0) S.nnext = 0u;
+    constexpr int kB = kGlobal ? 10 : 4;
+    static_assert(kWave * kB < 65536, "per-wave counts fit in 16 bits");
+    if (threadIdx.x == 0) S.nn &= 0xFFFFFFFFull;  // no candidates moved yet
     __syncthreads();
     for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kResThreads * kB) {
         uint2 e[kB];
@@ -566,18 +575,33 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
             const int64_t k = c0 + (int64_t)u * kResThreads + threadIdx.x;
             e[u] = k < n ? (kGlobal ? ld_cand(src + k) : src[k]) : make_uint2(0, 0);
         }
+        uint32_t outm = 0, keepm = 0;  // bit u: candidate u is emitted / moved
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
             const bool valid = c0 + (int64_t)u * kResThreads + threadIdx.x < n;
             const uint32_t dg = ((by_index ? e[u].y : e[u].x) >> shift) & mask;
-            const int64_t pa = wave_append(valid && (emit_above ? dg > j : dg < j), &S.nout);
-            if (pa >= 0) keep_token(ir, pa, e[u].y, kbr);
-            const int64_t pk = wave_append(valid && dg == j, &S.nnext);
-            if (pk >= 0) dst[pk] = e[u];
+            outm |= (valid && (emit_above ? dg > j : dg < j)) ? (1u << u) : 0u;
+            keepm |= (valid && dg == j) ? (1u << u) : 0u;
+        }
+        const uint32_t mine = (uint32_t)__popc(outm) | ((uint32_t)__popc(keepm) << 16);
+        const uint32_t inc = wave_inclusive_scan(mine);
+        const uint32_t wtot = read_lane(inc, kWave - 1);
+        unsigned long long base = 0;
+        if (wtot && lane_id() == 0)
+            base = atomicAdd(&S.nn, (unsigned long long)(wtot & 0xFFFFu) |
+                                        ((unsigned long long)(wtot >> 16) << 32));
+        base = read_lane(base, 0);
+        const uint32_t ex = inc - mine;
+        uint32_t pa = (uint32_t)base + (ex & 0xFFFFu);
+        uint32_t pk = (uint32_t)(base >> 32) + (ex >> 16);
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            if (outm & (1u << u)) keep_token(ir, pa++, e[u].y, kbr);
+            if (keepm & (1u << u)) dst[pk++] = e[u];
         }
     }
     __syncthreads();
-    return S.nnext;
+    return (uint32_t)(S.nn >> 32);
 }
 
 __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
@@ -600,7 +624,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
     int32_t *ir = idx + r * (int64_t)N + emitted;
     bool in_lds = false;  // candidates start in global memory
     int cur = 0;          // LDS buffer holding them once they fit
-    if (tid == 0) S.nout = 0u;
+    if (tid == 0) S.nn = 0ull;
     const uint2 *cr = gc;
     // Candidate k from LDS, or from global memory.
     auto cand = [&](int64_t k) { return in_lds ? cr[k] : ld_cand(cr + k); };
@@ -666,7 +690,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
                 const int64_t k = c0 + tid;
                 const bool valid = k < n;
                 const uint32_t ix = valid ? cand(k).y : 0u;
-                const int64_t pa = wave_append(valid, &S.nout);
+                const int64_t pa = wave_append(valid, nout_ptr(S));
                 if (pa >= 0) keep_token(ir, pa, ix, kbr);
             }
         } else {
@@ -704,11 +728,11 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
                 }
             }
             // One token left (its index is fully determined): keep it.
-            if (tid == 0 && n > 0 && c > 0) keep_token(ir, S.nout++, cand(0).y, kbr);
+            if (tid == 0 && n > 0 && c > 0) keep_token(ir, (uint32_t)S.nn++, cand(0).y, kbr);
         }
     }
     __syncthreads();
-    if (tid == 0) count[r] = (int32_t)(emitted + S.nout);
+    if (tid == 0) count[r] = (int32_t)(emitted + (uint32_t)S.nn);
 }
 
 __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
