@@ -39,8 +39,10 @@ def parse():
     ap.add_argument("--p", type=float, default=0.9)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-side-stream", action="store_true")
-    ap.add_argument("--sparse-mode", choices=["union", "per_head"], default="per_head",
-                    help="union: each kept row read once per KV head for all its query heads")
+    ap.add_argument("--sparse-mode", choices=["fused", "union", "per_head"], default="fused",
+                    help="fused: sparse and local heads in one rtp_decode_attend launch; "
+                         "per_head: separate calls, local heads on a side stream; union: "
+                         "each kept row read once per KV head for all its query heads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -107,7 +109,8 @@ def main():
 
     # Local heads of a layer run on a side stream, overlapping the retrieval
     # chain of the same layer; each layer joins both before the next starts.
-    side = None if args.no_side_stream else torch.cuda.Stream(device=dev)
+    side = (None if args.no_side_stream or args.sparse_mode == "fused"
+            else torch.cuda.Stream(device=dev))
 
     def step():
         for l in range(L):
@@ -164,7 +167,11 @@ def main():
                                                                   keep_bits=sl.keep_bits)
                                                for l in range(L)]),
     }
-    if sl.mode == "union":
+    if sl.mode == "fused":
+        us["rtp_decode_attend"] = time_call(lambda: [sl.attend(q_all[l], K_all[l], V_all[l],
+                                                               scale, out_all[l])
+                                                     for l in range(L)])
+    elif sl.mode == "union":
         us["rtp_sparse_decode_union"] = time_call(lambda: [rtp.rtp_sparse_decode_union(
             q_all[l], K_all[l], V_all[l], sl.keep_bits, N, 0, scale, out_all[l], sl.ws_sparse)
             for l in range(L)])
@@ -172,10 +179,10 @@ def main():
         us["rtp_sparse_decode"] = time_call(lambda: [rtp.rtp_sparse_decode(
             q_all[l], K_all[l], V_all[l], sl.idx, sl.count, 0, scale, out_all[l], sl.ws_sparse)
             for l in range(L)])
-    us.update({
-        "rtp_local_decode": time_call(lambda: [rtp.rtp_local_decode(q_all[l], K_all[l], V_all[l], N, H_r, Hq - H_r, cfg.n_sink, cfg.window, scale, out_all[l], sl.ws_local)
-                                                for l in range(L)]),
-    })
+    if sl.mode != "fused":
+        us["rtp_local_decode"] = time_call(lambda: [rtp.rtp_local_decode(
+            q_all[l], K_all[l], V_all[l], N, H_r, Hq - H_r, cfg.n_sink, cfg.window, scale,
+            out_all[l], sl.ws_local) for l in range(L)])
     log("per-call us/layer: " + ", ".join(f"{k}={v:.2f}" for k, v in us.items()))
 
     # --------------------------------------------- algorithmic bytes
@@ -217,18 +224,20 @@ def main():
     #   sparse  512 B (K + V row) per row of the union of the group's kept
     #           sets (re-reads by several heads earn no credit) + the 4-B
     #           indices read;
-    #   local   512 B per sink/window row per local KV head.
+    #   local   512 B per sink/window row per local KV head;
+    #   attend  sparse + local, one launch.
     csrc = os.path.join(ROOT, "sparse_long_context_indexer_amd", "csrc")
     sel_total = float(np.mean([sum(x) for x in n_sel]))
+    sparse_bytes = float(np.mean(union)) * 2 * d * 2 + sel_total * 4
     cands = {
         "rtp_index_scores": ("index_scores_kernel<8>", B * G_r * N * (cfg.r * 4 + cfg.G * 4),
                              "scan.hip"),
-        "rtp_sparse_decode": ("sparse_attn_kernel",
-                              float(np.mean(union)) * 2 * d * 2 + sel_total * 4, "attend.hip"),
+        "rtp_decode_attend": ("attend_kernel", sparse_bytes + window_bytes, "attend.hip"),
+        "rtp_sparse_decode": ("attend_kernel", sparse_bytes, "attend.hip"),
         "rtp_sparse_decode_union": ("union_attn_kernel",
                                     float(np.mean(union)) * 2 * d * 2 + B * H_r * ((N + 31) // 32) * 4,
                                     "attend.hip"),
-        "rtp_local_decode": ("local_attn_kernel", window_bytes, "attend.hip"),
+        "rtp_local_decode": ("attend_kernel", window_bytes, "attend.hip"),
     }
     call = max((c for c in cands if c in us), key=lambda c: us[c])
     kname, kbytes, ksrc = cands[call]

@@ -57,7 +57,8 @@ enum {
     RTP_WS_TOPP_SELECT = 1,
     RTP_WS_SPARSE_DECODE = 2,
     RTP_WS_LOCAL_DECODE = 3,
-    RTP_WS_SPARSE_UNION = 4
+    RTP_WS_SPARSE_UNION = 4,
+    RTP_WS_DECODE_ATTEND = 5
 };
 
 /*
@@ -189,12 +190,40 @@ rtp_status rtp_local_decode(const rtp_bf16 *q, const rtp_bf16 *K,
                             void *stream);
 
 /*
+ * rtp_decode_attend -- rtp_sparse_decode for the query heads
+ * sparse_head_begin .. sparse_head_begin + n_sparse_heads - 1 and
+ * rtp_local_decode for the query heads local_head_begin ..
+ * local_head_begin + n_local_heads - 1, in one launch, so that neither set
+ * waits for the other's tail (the head-role split of the gist.science
+ * summary, method section 1: retrieval and local heads of one layer).  The
+ * results are those of the two calls.  The two head ranges must not overlap;
+ * either count may be 0, which skips that set (idx and count may then be
+ * NULL; n_sink and window are ignored when n_local_heads is 0).
+ *
+ *   q, K, V, out, d, scale         as in rtp_sparse_decode
+ *   idx, count                     as in rtp_sparse_decode, for the sparse heads
+ *   n_sink, window                 as in rtp_local_decode
+ *   workspace  >= rtp_workspace_size(RTP_WS_DECODE_ATTEND, B, Hq, N)
+ */
+rtp_status rtp_decode_attend(const rtp_bf16 *q, const rtp_bf16 *K,
+                             const rtp_bf16 *V, const int32_t *idx,
+                             const int32_t *count, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,
+                             int32_t sparse_head_begin, int32_t n_sparse_heads,
+                             int32_t local_head_begin, int32_t n_local_heads,
+                             int32_t n_sink, int32_t window, float scale,
+                             float *out, void *workspace, size_t ws_bytes,
+                             void *stream);
+
+/*
  * rtp_workspace_size -- bytes of workspace a call needs (host only, pure).
  *   which  RTP_WS_TOPP_SELECT:   H = score rows per batch row
  *          RTP_WS_SPARSE_DECODE: H = n_q_heads
  *          RTP_WS_LOCAL_DECODE:  H = n_q_heads (sized for any n_sink,
  *                                window, since the row list is <= N)
  *          RTP_WS_SPARSE_UNION:  H = n_q_heads
+ *          RTP_WS_DECODE_ATTEND: H = Hq (sized for any split of the Hq
+ *                                heads into sparse and local heads)
  * Returns RTP_ERR_VALUE for an unknown `which`, RTP_ERR_SHAPE for sizes < 1,
  * RTP_ERR_NULL when bytes is NULL.
  */

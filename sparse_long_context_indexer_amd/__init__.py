@@ -19,14 +19,15 @@ RTP_WS_TOPP_SELECT = 1
 RTP_WS_SPARSE_DECODE = 2
 RTP_WS_LOCAL_DECODE = 3
 RTP_WS_SPARSE_UNION = 4
+RTP_WS_DECODE_ATTEND = 5
 
 STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPPORTED",
           4: "RTP_ERR_VALUE", 5: "RTP_ERR_ALIGN", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
 
 # Every symbol include/rtp.h declares.
 SYMBOLS = ("rtp_index_scores", "rtp_topp_select", "rtp_sparse_decode",
-           "rtp_sparse_decode_union", "rtp_local_decode", "rtp_workspace_size",
-           "rtp_status_string", "rtp_last_hip_error")
+           "rtp_sparse_decode_union", "rtp_local_decode", "rtp_decode_attend",
+           "rtp_workspace_size", "rtp_status_string", "rtp_last_hip_error")
 
 
 class RtpError(RuntimeError):
@@ -62,12 +63,14 @@ def lib() -> ctypes.CDLL:
                                               I32, F32, P, P, SZ, P]
         L.rtp_local_decode.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, I32, I32,
                                        I32, I32, F32, P, P, SZ, P]
+        L.rtp_decode_attend.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32, I32, I32,
+                                        I32, I32, I32, I32, F32, P, P, SZ, P]
         L.rtp_workspace_size.argtypes = [I32, I32, I32, I32, ctypes.POINTER(SZ)]
         L.rtp_status_string.argtypes = [I32]
         L.rtp_status_string.restype = ctypes.c_char_p
         L.rtp_last_hip_error.argtypes = []
         L.rtp_last_hip_error.restype = I32
-        for name in SYMBOLS[:6]:
+        for name in SYMBOLS[:7]:
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -188,6 +191,27 @@ def rtp_sparse_decode_union(q, K, V, keep_bits, N, q_head_begin, scale, out, wor
         float(scale), _dev(out, torch.float32, "out", 3),
         _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(), _stream(q, stream)),
         "rtp_sparse_decode_union")
+
+
+def rtp_decode_attend(q, K, V, idx, count, N, sparse_head_begin, local_head_begin,
+                      n_local_heads, n_sink, window, scale, out, workspace,
+                      stream=None) -> None:
+    """rtp_sparse_decode for the heads [sparse_head_begin, + count.shape[1])
+    and rtp_local_decode for [local_head_begin, + n_local_heads), one launch.
+    idx/count may be None (no sparse heads); workspace uint8
+    [>= workspace_size(RTP_WS_DECODE_ATTEND, B, Hq, N)]."""
+    import torch
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    n_sparse = 0 if count is None else count.shape[1]
+    idx_p = None if idx is None else _dev(idx, torch.int32, "idx", 3)
+    count_p = None if count is None else _dev(count, torch.int32, "count", 2)
+    _check(lib().rtp_decode_attend(
+        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4), idx_p, count_p,
+        B, Hq, Hkv, N, cap, d, sparse_head_begin, n_sparse, local_head_begin, n_local_heads,
+        n_sink, window, float(scale), _dev(out, torch.float32, "out", 3),
+        _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(), _stream(q, stream)),
+        "rtp_decode_attend")
 
 
 def rtp_local_decode(q, K, V, N, q_head_begin, n_q_heads, n_sink, window, scale, out,

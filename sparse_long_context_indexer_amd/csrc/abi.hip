@@ -73,6 +73,7 @@ rtp_status rtp_workspace_size(int32_t which, int32_t B, int32_t H, int32_t N, si
     case RTP_WS_SPARSE_DECODE: *bytes = rtp::sparse_ws_bytes(B, H, N); return RTP_OK;
     case RTP_WS_LOCAL_DECODE: *bytes = rtp::local_ws_bytes(B, H, N); return RTP_OK;
     case RTP_WS_SPARSE_UNION: *bytes = rtp::union_ws_bytes(B, H, N); return RTP_OK;
+    case RTP_WS_DECODE_ATTEND: *bytes = rtp::attend_ws_bytes(B, H, H, N); return RTP_OK;
     default: return RTP_ERR_VALUE;
     }
 }
@@ -162,6 +163,48 @@ rtp_status rtp_local_decode(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16
     return from_hip(rtp::launch_local_decode(q, K, V, B, Hq, Hkv, N, kv_cap, q_head_begin,
                                              n_q_heads, n_sink, window, scale, out, workspace,
                                              as_stream(stream)));
+}
+
+rtp_status rtp_decode_attend(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,
+                             const int32_t *idx, const int32_t *count, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,
+                             int32_t sparse_head_begin, int32_t n_sparse_heads,
+                             int32_t local_head_begin, int32_t n_local_heads, int32_t n_sink,
+                             int32_t window, float scale, float *out, void *workspace,
+                             size_t ws_bytes, void *stream)
+{
+    if (n_sparse_heads < 0 || n_local_heads < 0) return RTP_ERR_SHAPE;
+    if (n_sparse_heads == 0 && n_local_heads == 0) return RTP_ERR_SHAPE;
+    if (n_sparse_heads > 0) {
+        if (!idx || !count) return RTP_ERR_NULL;
+        rtp_status st = check_attention_common(q, K, V, out, workspace, B, Hq, Hkv, N, kv_cap,
+                                               d, sparse_head_begin, n_sparse_heads, scale);
+        if (st != RTP_OK) return st;
+        if (!aligned(idx, 4) || !aligned(count, 4)) return RTP_ERR_ALIGN;
+    }
+    int64_t local_blocks = 0;
+    if (n_local_heads > 0) {
+        rtp_status st = check_attention_common(q, K, V, out, workspace, B, Hq, Hkv, N, kv_cap,
+                                               d, local_head_begin, n_local_heads, scale);
+        if (st != RTP_OK) return st;
+        if (n_sink < 0 || window < 1) return RTP_ERR_VALUE;
+        const int64_t G = Hq / Hkv;
+        const int64_t groups =
+            ((int64_t)local_head_begin + n_local_heads - 1) / G - local_head_begin / G + 1;
+        local_blocks = (int64_t)B * groups * ((G + 7) / 8) * rtp::local_splits(N);
+    }
+    if (n_sparse_heads > 0 && n_local_heads > 0 &&
+        sparse_head_begin < (int64_t)local_head_begin + n_local_heads &&
+        local_head_begin < (int64_t)sparse_head_begin + n_sparse_heads)
+        return RTP_ERR_SHAPE;  // the two head ranges overlap
+    const int64_t sparse_blocks = n_sparse_heads > 0 ? rtp::sparse_grid((int64_t)B * n_sparse_heads) : 0;
+    if (local_blocks + sparse_blocks > INT32_MAX) return RTP_ERR_SHAPE;
+    if (ws_bytes < rtp::attend_ws_bytes(B, n_sparse_heads, n_local_heads, N))
+        return RTP_ERR_WORKSPACE;
+    return from_hip(rtp::launch_decode_attend(q, K, V, idx, count, B, Hq, Hkv, N, kv_cap,
+                                              sparse_head_begin, n_sparse_heads,
+                                              local_head_begin, n_local_heads, n_sink, window,
+                                              scale, out, workspace, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -240,21 +240,28 @@ __device__ void merge_partials(const float *pr, int n, float *dst_part, float *d
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ count, int N, int64_t kv_cap, int Hq, int Hkv,
-    int q_head_begin, int n_q, int R, float qscale, SparseWs W,
-    float *__restrict__ out)
+struct SparseShared {
+    float wm[kAttThreads / kWave], wl[kAttThreads / kWave];
+    float wo[kAttThreads / kWave][128];
+    SplitPlan plan;
+    MergeShared ms;
+    int last;
+};
+
+// Per-head sparse attention, split blk of the plan over all heads' kept rows.
+__device__ void sparse_block(const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
+                             const uint16_t *__restrict__ V, const int32_t *__restrict__ idx,
+                             const int32_t *__restrict__ count, int N, int64_t kv_cap, int Hq,
+                             int Hkv, int q_head_begin, int n_q, int R, float qscale,
+                             const SparseWs &W, float *__restrict__ out, int blk,
+                             SparseShared &SS)
 {
-    __shared__ float wm[kAttThreads / kWave], wl[kAttThreads / kWave];
-    __shared__ float wo[kAttThreads / kWave][128];
-    __shared__ SplitPlan sh_plan;
+    float *wm = SS.wm, *wl = SS.wl;
+    float(*wo)[128] = SS.wo;
+    MergeShared &MS = SS.ms;
+    int &last = SS.last;
     constexpr int kRowsPerIter = kGroups * kSparseU;
-    __shared__ MergeShared MS;
-    __shared__ int last;
-    const int blk = blockIdx.x;
-    const SplitPlan plan = plan_splits(count, R, N, kRowsPerIter, blk, -1, &sh_plan);
+    const SplitPlan plan = plan_splits(count, R, N, kRowsPerIter, blk, -1, &SS.plan);
     if (plan.r < 0) return;  // past the last split: no partial to write
     const int prow = plan.r;
     const int b = prow / n_q, hr = prow % n_q;
@@ -396,20 +403,6 @@ __global__ __launch_bounds__(kAttThreads) void sparse_attn_kernel(
     merge_partials(sp, slices, nullptr, dst, MS);
 }
 
-hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,
-                                const int32_t *idx, const int32_t *count, int B, int Hq,
-                                int Hkv, int N, int64_t kv_cap, int q_head_begin,
-                                int n_q_heads, float scale, float *out, void *ws,
-                                hipStream_t stream)
-{
-    const int R = B * n_q_heads;
-    SparseWs W;
-    sparse_ws_layout(R, &W, ws);
-    return launch(sparse_attn_kernel, dim3(sparse_grid(R)), dim3(kAttThreads), 0, stream, q, K,
-                  V, idx, count, N, kv_cap, Hq, Hkv, q_head_begin, n_q_heads, R,
-                  scale * kLog2e, W, out);
-}
-
 // ------------------------------------------- 8 query heads per KV row
 //
 // Local heads and the union mode of sparse heads read each K/V row once for
@@ -512,6 +505,29 @@ __device__ void merge_heads(const float *first, int64_t head_stride, int n, int 
             st_agent(pd + 1, L);
         }
     }
+}
+
+// After split s of S has stored its partials for heads r0 .. r0 + nh - 1:
+// the two-level merge of the splits, for all nh heads at once (counters
+// indexed by r0).  The last block of a slice merges the slice; the last
+// slice merger writes the output rows dst (128 floats apart).
+__device__ void merge_group_splits(int nh, int s, int S, int64_t r0, const GroupWs &W,
+                                   float *dst, int *last)
+{
+    const int slice = s / W.slice;
+    const int slices = (S + W.slice - 1) / W.slice;
+    const int in_slice = min(W.slice, S - slice * W.slice);
+    if (!arrive_last(W.slice_ctr + r0 * W.max_slices + slice, in_slice, last)) return;
+    const float *first = W.part + (r0 * S + slice * W.slice) * kPart;
+    if (slices == 1) {
+        merge_heads(first, (int64_t)S * kPart, in_slice, nh, nullptr, 0, dst);
+        return;
+    }
+    float *sp = W.super + r0 * W.max_slices * kPart;
+    merge_heads(first, (int64_t)S * kPart, in_slice, nh, sp + (int64_t)slice * kPart,
+                (int64_t)W.max_slices * kPart, nullptr);
+    if (!arrive_last(W.group_ctr + r0, slices, last)) return;
+    merge_heads(sp, (int64_t)W.max_slices * kPart, slices, nh, nullptr, 0, dst);
 }
 
 // Per-lane state of the 8-head online softmax.  A row is spread over 16
@@ -686,21 +702,7 @@ __device__ void heads8_finish(Heads8 &st, Heads8Shared &sh, int nh, int s, int S
         }
     }
 
-    // Two-level merge, for all nh heads at once (counters indexed by r0).
-    const int slice = s / W.slice;
-    const int slices = (S + W.slice - 1) / W.slice;
-    const int in_slice = min(W.slice, S - slice * W.slice);
-    if (!arrive_last(W.slice_ctr + r0 * W.max_slices + slice, in_slice, &sh.last)) return;
-    const float *first = W.part + (r0 * S + slice * W.slice) * kPart;
-    if (slices == 1) {
-        merge_heads(first, (int64_t)S * kPart, in_slice, nh, nullptr, 0, dst);
-        return;
-    }
-    float *sp = W.super + r0 * W.max_slices * kPart;
-    merge_heads(first, (int64_t)S * kPart, in_slice, nh, sp + (int64_t)slice * kPart,
-                (int64_t)W.max_slices * kPart, nullptr);
-    if (!arrive_last(W.group_ctr + r0, slices, &sh.last)) return;
-    merge_heads(sp, (int64_t)W.max_slices * kPart, slices, nh, nullptr, 0, dst);
+    merge_group_splits(nh, s, S, r0, W, dst, &sh.last);
 }
 
 // Heads of KV head g handled by block row y: chunk ck of up to 8 query heads
@@ -722,6 +724,16 @@ __device__ __forceinline__ HeadChunk head_chunk(int y, int G, int q_head_begin, 
 }
 
 // ------------------------------------------------------------- local
+//
+// Local heads: each K/V row is read once for the (up to 8) query heads of a
+// chunk of its KV head.  Two 16-lane groups take each row, one for heads 0-3
+// of the chunk and one for heads 4-7 (their loads of the row are the same
+// lines); a lane holds 8 dims of the row and forms 4 partial dot products.
+// A butterfly over the 16 lanes leaves each head's full dot in 4 lanes:
+// lanes i and i^8 trade head pairs {0,1} / {2,3}, lanes i and i^7 trade the
+// heads of the pair, then i^2 and i^1 add; head 2*b3 + b2 (lane bits) ends
+// in lanes 4h .. 4h+3, and a per-row broadcast hands every lane all 4.
+// All exchanges are DPP moves.
 
 static int64_t local_rows_count(int N, int n_sink, int window)
 {
@@ -745,57 +757,202 @@ size_t local_ws_bytes(int64_t B, int64_t n_q, int N)
     return group_ws_layout(B * n_q, local_splits(N), kLocalSlice, nullptr, nullptr);
 }
 
-// Block (s, y, b): the heads of head_chunk(y), rows of split s of the local
-// row list (sinks, then the window).
-__global__ __launch_bounds__(kAttThreads) void local_attn_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, int N, int64_t kv_cap, int Hq, int Hkv,
-    int q_head_begin, int n_q, int n_sink, int window, float qscale, int S,
-    int chunks_per_g, GroupWs W, float *__restrict__ out)
+constexpr int kLocSlots = kAttThreads / 32;         // rows in progress per block step
+constexpr int kLocRowsPerIter = kLocSlots * kLocalU;
+
+struct LocalShared {
+    float m[kLocSlots][8], l[kLocSlots][8];
+    float o[kLocSlots][8][128];
+    int last;
+};
+
+struct Heads4 {
+    float qf[4][8];  // q * scale * log2(e) of this group's heads, this lane's 8 dims
+    float m[4], l[4], o[4][8];
+};
+
+__device__ __forceinline__ void heads4_init(Heads4 &st, const uint16_t *__restrict__ q, int64_t q0,
+                                            int nh, int half, float qscale, int sub)
 {
-    __shared__ Heads8Shared sh;
-    const int s = blockIdx.x, b = blockIdx.z;
-    const HeadChunk hc = head_chunk(blockIdx.y, Hq / Hkv, q_head_begin, n_q, chunks_per_g);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int hh = half * 4 + k;
+        if (hh < nh) {
+            const uint4 qw = *reinterpret_cast<const uint4 *>(q + q0 + hh * 128 + sub * 8);
+            bf16x8_to_f32(qw, st.qf[k]);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st.qf[k][c] *= qscale;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st.qf[k][c] = 0.0f;
+        }
+        st.m[k] = -INFINITY;
+        st.l[k] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st.o[k][c] = 0.0f;
+    }
+}
+
+// One online-softmax step over kLocalU rows of this lane group.
+__device__ __forceinline__ void heads4_step(Heads4 &st, const uint4 (&kw)[kLocalU],
+                                            const uint4 (&vw)[kLocalU],
+                                            const bool (&ok)[kLocalU], bool b3, bool b2)
+{
+    float lg[kLocalU][4];
+#pragma unroll
+    for (int u = 0; u < kLocalU; ++u) {
+        float kf[8];
+        bf16x8_to_f32(kw[u], kf);
+        float d[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float a = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) a = fmaf(st.qf[k][c], kf[c], a);
+            d[k] = a;
+        }
+        float d2[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float keep = b3 ? d[2 + k] : d[k];
+            const float send = b3 ? d[k] : d[2 + k];
+            d2[k] = keep + dpp<kDppRowRor8>(send, send);
+        }
+        const float keep = b2 ? d2[1] : d2[0];
+        const float send = b2 ? d2[0] : d2[1];
+        float d1 = keep + dpp<kDppRowHalfMirror>(send, send);
+        d1 += dpp<kDppQuadXor2>(d1, d1);
+        d1 += dpp<kDppQuadXor1>(d1, d1);
+        lg[u][0] = ok[u] ? dpp<kDppRowNewBcast0>(d1, d1) : -INFINITY;
+        lg[u][1] = ok[u] ? dpp<kDppRowNewBcast0 + 4>(d1, d1) : -INFINITY;
+        lg[u][2] = ok[u] ? dpp<kDppRowNewBcast0 + 8>(d1, d1) : -INFINITY;
+        lg[u][3] = ok[u] ? dpp<kDppRowNewBcast0 + 12>(d1, d1) : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float mx = lg[0][k];
+#pragma unroll
+        for (int u = 1; u < kLocalU; ++u) mx = fmaxf(mx, lg[u][k]);
+        const float mn = fmaxf(st.m[k], mx);
+        if (mn == -INFINITY) continue;
+        const float corr = rescale(st.m[k], mn);
+        st.l[k] *= corr;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st.o[k][c] *= corr;
+        st.m[k] = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < kLocalU; ++u) {
+        float vf[8];
+        bf16x8_to_f32(vw[u], vf);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float pw = ok[u] ? exp2f(lg[u][k] - st.m[k]) : 0.0f;
+            st.l[k] += pw;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st.o[k][c] = fmaf(pw, vf[c], st.o[k][c]);
+        }
+    }
+}
+
+struct LocalArgs {
+    int q_head_begin, n_q, n_sink, window;
+    int S;             // splits of the row list
+    int ny;            // head chunks (block rows)
+    int chunks_per_g;
+    int blocks;        // S * ny * B
+    GroupWs W;
+};
+
+// Local block i: split s, head chunk y, batch row b.  The rows of split s of
+// the row list (sinks, then the window) for the chunk's heads.
+__device__ void local_block(const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
+                            const uint16_t *__restrict__ V, int N, int64_t kv_cap, int Hq,
+                            int Hkv, float qscale, const LocalArgs &A, float *__restrict__ out,
+                            int i, LocalShared &sh)
+{
+    const int s = i % A.S, y = (i / A.S) % A.ny, b = i / (A.S * A.ny);
+    const HeadChunk hc = head_chunk(y, Hq / Hkv, A.q_head_begin, A.n_q, A.chunks_per_g);
     if (hc.nh <= 0) return;
 
-    const int64_t w_start = N > window ? (int64_t)N - window : 0;
-    const int64_t sink_end = n_sink < w_start ? n_sink : w_start;
+    const int64_t w_start = N > A.window ? (int64_t)N - A.window : 0;
+    const int64_t sink_end = A.n_sink < w_start ? A.n_sink : w_start;
     const int64_t n_rows = sink_end + (N - w_start);
-    constexpr int kRowsPerIter = kGroups * kLocalU;
-    int64_t chunk = (n_rows + S - 1) / S;
-    chunk = (chunk + kRowsPerIter - 1) / kRowsPerIter * kRowsPerIter;
+    int64_t chunk = (n_rows + A.S - 1) / A.S;
+    chunk = (chunk + kLocRowsPerIter - 1) / kLocRowsPerIter * kLocRowsPerIter;
     const int64_t begin = (int64_t)s * chunk;
     const int64_t end = min(n_rows, begin + chunk);
 
     const int lane = lane_id(), w = threadIdx.x / kWave;
     const int grp = lane >> 4, sub = lane & 15;
+    const int half = grp & 1, slot = w * 2 + (grp >> 1);
     const int64_t kvb = ((int64_t)b * Hkv + hc.g) * kv_cap * 128 + sub * 8;
     const uint16_t *Kb = K + kvb;
     const uint16_t *Vb = V + kvb;
     uint4 kw[kLocalU], vw[kLocalU];
-    uint32_t hb[kLocalU];
+    bool ok[kLocalU];
     auto load_rows = [&](int64_t base) {
 #pragma unroll
         for (int u = 0; u < kLocalU; ++u) {
-            const int64_t j = base + u * kGroups + w * 4 + grp;
-            const bool ok = j < end;
-            hb[u] = ok ? 0xFFu : 0u;
+            const int64_t j = base + u * kLocSlots + slot;
+            ok[u] = j < end;
             const int64_t row = j < sink_end ? j : w_start + (j - sink_end);
-            const int64_t off = ok ? row * 128 : 0;
+            const int64_t off = ok[u] ? row * 128 : 0;
             kw[u] = *reinterpret_cast<const uint4 *>(Kb + off);
             vw[u] = *reinterpret_cast<const uint4 *>(Vb + off);
         }
     };
     // The first rows are requested before q, so both loads overlap.
     if (begin < end) load_rows(begin);
-    Heads8 st;
-    heads8_init(st, q, ((int64_t)b * Hq + hc.h_lo) * 128, hc.nh, qscale, sub);
-    for (int64_t base = begin; base < end; base += kRowsPerIter) {
+    Heads4 st;
+    heads4_init(st, q, ((int64_t)b * Hq + hc.h_lo) * 128, hc.nh, half, qscale, sub);
+    const bool b3 = (sub >> 3) & 1, b2 = (sub >> 2) & 1;
+    for (int64_t base = begin; base < end; base += kLocRowsPerIter) {
         if (base != begin) load_rows(base);
-        heads8_step(st, kw, vw, hb);
+        heads4_step(st, kw, vw, ok, b3, b2);
     }
-    const int64_t r0 = (int64_t)b * n_q + (hc.h_lo - q_head_begin);
-    heads8_finish(st, sh, hc.nh, s, S, r0, W, out + ((int64_t)b * Hq + hc.h_lo) * 128);
+
+    // The block's row slots, merged in LDS: one partial per head of the chunk.
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int hh = half * 4 + k;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sh.o[slot][hh][sub * 8 + c] = st.o[k][c];
+        if (sub == 0) {
+            sh.m[slot][hh] = st.m[k];
+            sh.l[slot][hh] = st.l[k];
+        }
+    }
+    __syncthreads();
+    const int64_t r0 = (int64_t)b * A.n_q + (hc.h_lo - A.q_head_begin);
+    {
+        const int hh = threadIdx.x >> 5, d = (threadIdx.x & 31) * 4;
+        if (hh < hc.nh) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < kLocSlots; ++k) M = fmaxf(M, sh.m[k][hh]);
+            float L = 0.0f, O[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < kLocSlots; ++k) {
+                const float f = rescale(sh.m[k][hh], M);
+                L = fmaf(sh.l[k][hh], f, L);
+                const float4 ov = *reinterpret_cast<const float4 *>(&sh.o[k][hh][d]);
+                O[0] = fmaf(ov.x, f, O[0]);
+                O[1] = fmaf(ov.y, f, O[1]);
+                O[2] = fmaf(ov.z, f, O[2]);
+                O[3] = fmaf(ov.w, f, O[3]);
+            }
+            float *pr = A.W.part + ((r0 + hh) * A.S + s) * kPart;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st_agent(pr + 4 + d + e, O[e]);
+            if (d == 0) {
+                st_agent(pr, M);
+                st_agent(pr + 1, L);
+            }
+        }
+    }
+    merge_group_splits(hc.nh, s, A.S, r0, A.W, out + ((int64_t)b * Hq + hc.h_lo) * 128,
+                       &sh.last);
 }
 
 static dim3 group_grid(int S, int B, int Hq, int Hkv, int q_head_begin, int n_q_heads,
@@ -808,19 +965,122 @@ static dim3 group_grid(int S, int B, int Hq, int Hkv, int q_head_begin, int n_q_
     return dim3(S, (g_last - g_first + 1) * *chunks_per_g, B);
 }
 
+// ------------------------------------------------------ attention launch
+//
+// One kernel serves local heads, per-head sparse heads or both: blocks
+// [0, L.blocks) are local blocks, the rest sparse splits.  Run together, the
+// two sets share the launch, so neither waits on the other's tail.
+
+struct SparseArgs {
+    const int32_t *idx, *count;
+    int q_head_begin, n_q, R;
+    int blocks;  // 0: no sparse heads
+    SparseWs W;
+};
+
+union AttendShared {
+    SparseShared sp;
+    LocalShared lo;
+};
+
+__global__ __launch_bounds__(kAttThreads, 4) void attend_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, int N, int64_t kv_cap, int Hq, int Hkv, float qscale,
+    LocalArgs L, SparseArgs P, float *__restrict__ out)
+{
+    __shared__ AttendShared sh;
+    const int i = blockIdx.x;
+    if (i < L.blocks)
+        local_block(q, K, V, N, kv_cap, Hq, Hkv, qscale, L, out, i, sh.lo);
+    else
+        sparse_block(q, K, V, P.idx, P.count, N, kv_cap, Hq, Hkv, P.q_head_begin, P.n_q, P.R,
+                     qscale, P.W, out, i - L.blocks, sh.sp);
+}
+
+static LocalArgs local_args(int B, int Hq, int Hkv, int N, int q_head_begin, int n_q_heads,
+                            int n_sink, int window, void *ws)
+{
+    LocalArgs A{};
+    if (n_q_heads <= 0) return A;
+    A.q_head_begin = q_head_begin;
+    A.n_q = n_q_heads;
+    A.n_sink = n_sink;
+    A.window = window;
+    A.S = local_splits(local_rows_count(N, n_sink, window));
+    const dim3 g = group_grid(A.S, B, Hq, Hkv, q_head_begin, n_q_heads, &A.chunks_per_g);
+    A.ny = (int)g.y;
+    A.blocks = A.S * A.ny * B;
+    group_ws_layout((int64_t)B * n_q_heads, local_splits(N), kLocalSlice, &A.W, ws);
+    return A;
+}
+
+static SparseArgs sparse_args(const int32_t *idx, const int32_t *count, int B, int q_head_begin,
+                              int n_q_heads, void *ws)
+{
+    SparseArgs A{};
+    if (n_q_heads <= 0) return A;
+    A.idx = idx;
+    A.count = count;
+    A.q_head_begin = q_head_begin;
+    A.n_q = n_q_heads;
+    A.R = B * n_q_heads;
+    A.blocks = sparse_grid(A.R);
+    sparse_ws_layout(A.R, &A.W, ws);
+    return A;
+}
+
+static hipError_t launch_attend(const uint16_t *q, const uint16_t *K, const uint16_t *V, int N,
+                                int64_t kv_cap, int Hq, int Hkv, float scale, const LocalArgs &L,
+                                const SparseArgs &P, float *out, hipStream_t stream)
+{
+    const int blocks = L.blocks + P.blocks;
+    if (blocks == 0) return hipSuccess;
+    return launch(attend_kernel, dim3(blocks), dim3(kAttThreads), 0, stream, q, K, V, N, kv_cap,
+                  Hq, Hkv, scale * kLog2e, L, P, out);
+}
+
+hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                                const int32_t *idx, const int32_t *count, int B, int Hq,
+                                int Hkv, int N, int64_t kv_cap, int q_head_begin,
+                                int n_q_heads, float scale, float *out, void *ws,
+                                hipStream_t stream)
+{
+    return launch_attend(q, K, V, N, kv_cap, Hq, Hkv, scale, LocalArgs{},
+                         sparse_args(idx, count, B, q_head_begin, n_q_heads, ws), out, stream);
+}
+
 hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,
                                int B, int Hq, int Hkv, int N, int64_t kv_cap,
                                int q_head_begin, int n_q_heads, int n_sink, int window,
                                float scale, float *out, void *ws, hipStream_t stream)
 {
-    const int S = local_splits(local_rows_count(N, n_sink, window));
-    int chunks_per_g;
-    const dim3 grid = group_grid(S, B, Hq, Hkv, q_head_begin, n_q_heads, &chunks_per_g);
-    GroupWs W;
-    group_ws_layout((int64_t)B * n_q_heads, local_splits(N), kLocalSlice, &W, ws);
-    return launch(local_attn_kernel, grid, dim3(kAttThreads), 0, stream, q, K, V, N, kv_cap, Hq,
-                  Hkv, q_head_begin, n_q_heads, n_sink, window, scale * kLog2e, S, chunks_per_g,
-                  W, out);
+    return launch_attend(q, K, V, N, kv_cap, Hq, Hkv, scale,
+                         local_args(B, Hq, Hkv, N, q_head_begin, n_q_heads, n_sink, window, ws),
+                         SparseArgs{}, out, stream);
+}
+
+size_t attend_ws_bytes(int64_t B, int64_t n_sparse, int64_t n_local, int N)
+{
+    size_t off = 0;
+    if (n_sparse > 0) off += align_up(sparse_ws_bytes(B, n_sparse, N), 256);
+    if (n_local > 0) off += local_ws_bytes(B, n_local, N);
+    return off;
+}
+
+hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                                const int32_t *idx, const int32_t *count, int B, int Hq,
+                                int Hkv, int N, int64_t kv_cap, int sparse_head_begin,
+                                int n_sparse_heads, int local_head_begin, int n_local_heads,
+                                int n_sink, int window, float scale, float *out, void *ws,
+                                hipStream_t stream)
+{
+    char *base = static_cast<char *>(ws);
+    const size_t sp = n_sparse_heads > 0 ? align_up(sparse_ws_bytes(B, n_sparse_heads, N), 256)
+                                         : 0;
+    return launch_attend(
+        q, K, V, N, kv_cap, Hq, Hkv, scale,
+        local_args(B, Hq, Hkv, N, local_head_begin, n_local_heads, n_sink, window, base + sp),
+        sparse_args(idx, count, B, sparse_head_begin, n_sparse_heads, base), out, stream);
 }
 
 // ------------------------------------------------------------- union

@@ -52,6 +52,8 @@ constexpr int kDppRowMirror = 0x140;   // i <- 15-i within 16 lanes
 constexpr int kDppRowHalfMirror = 0x141;  // i <- 7-i within 8 lanes
 constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> next row
 constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+constexpr int kDppRowRor8 = 0x128;     // i <- (i+8) mod 16 within 16 lanes (= i ^ 8)
+constexpr int kDppRowNewBcast0 = 0x150;  // + n: lane n of each row -> the whole row
 
 template <int Ctrl, int RowMask = 0xf, typename T>
 __device__ __forceinline__ T dpp(T old, T v)

@@ -30,6 +30,7 @@ hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p,
 
 // ---- attention (attend.hip)
 size_t sparse_ws_bytes(int64_t B, int64_t n_q, int N);
+int sparse_grid(int64_t R);
 hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K,
                                 const uint16_t *V, const int32_t *idx,
                                 const int32_t *count, int B, int Hq, int Hkv,
@@ -43,6 +44,16 @@ hipError_t launch_sparse_decode_union(const uint16_t *q, const uint16_t *K,
                                       int B, int Hq, int Hkv, int N, int64_t kv_cap,
                                       int q_head_begin, int n_q_heads, float scale,
                                       float *out, void *ws, hipStream_t stream);
+
+// Local and per-head sparse heads in one launch; the workspace holds the
+// sparse workspace, then (256-B aligned) the local one.
+size_t attend_ws_bytes(int64_t B, int64_t n_sparse, int64_t n_local, int N);
+hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                                const int32_t *idx, const int32_t *count, int B, int Hq,
+                                int Hkv, int N, int64_t kv_cap, int sparse_head_begin,
+                                int n_sparse_heads, int local_head_begin, int n_local_heads,
+                                int n_sink, int window, float scale, float *out, void *ws,
+                                hipStream_t stream);
 
 int local_splits(int64_t n_rows);
 size_t local_ws_bytes(int64_t B, int64_t n_q, int N);

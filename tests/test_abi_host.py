@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -49,9 +49,14 @@ def test_workspace_sizes(lib):
     assert a >= 8 * (1 << 20) * 8          # candidate list capacity
     assert a % 256 == 0
     assert rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 1, 8, 4096) < a
-    for which in (rtp.RTP_WS_SPARSE_DECODE, rtp.RTP_WS_LOCAL_DECODE, rtp.RTP_WS_SPARSE_UNION):
+    for which in (rtp.RTP_WS_SPARSE_DECODE, rtp.RTP_WS_LOCAL_DECODE, rtp.RTP_WS_SPARSE_UNION,
+                  rtp.RTP_WS_DECODE_ATTEND):
         s = rtp.workspace_size(which, 2, 8, 65536)
         assert s > 0 and s % 256 == 0
+    # The combined attention workspace holds both sets' workspaces.
+    assert rtp.workspace_size(rtp.RTP_WS_DECODE_ATTEND, 2, 32, 65536) >= (
+        rtp.workspace_size(rtp.RTP_WS_SPARSE_DECODE, 2, 32, 65536)
+        + rtp.workspace_size(rtp.RTP_WS_LOCAL_DECODE, 2, 32, 65536))
     with pytest.raises(rtp.RtpError) as e:
         rtp.workspace_size(9, 1, 1, 1)
     assert e.value.status == 4
@@ -162,3 +167,38 @@ def test_one_hip_runtime_in_process(lib):
     maps = open("/proc/self/maps").read()
     hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
     assert len(hip) == 1, hip
+
+
+def test_decode_attend_validation(lib):
+    f = lib.rtp_decode_attend
+    ws = rtp.workspace_size(rtp.RTP_WS_DECODE_ATTEND, 1, 32, 1000)
+    pos = {"q": 0, "idx": 3, "count": 4, "Hq": 6, "Hkv": 7, "N": 8, "d": 10, "sb": 11, "ns": 12,
+           "lb": 13, "nl": 14, "sink": 15, "win": 16, "scale": 17, "ws": 19, "wsb": 20}
+    args = [A, A, A, A, A, 1, 32, 4, 1000, 1000, 128, 0, 8, 8, 24, 4, 4096, 0.088, A, A, ws,
+            None]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    assert call(q=None) == 1
+    assert call(idx=None) == 1                  # sparse heads need idx and count
+    assert call(count=None) == 1
+    assert call(ns=0, nl=0) == 2                # nothing to do
+    assert call(ns=-1) == 2
+    assert call(lb=4) == 2                      # ranges 0..7 and 4..27 overlap
+    assert call(lb=9) == 2                      # 9 + 24 > 32
+    assert call(sink=-1) == 4
+    assert call(win=0) == 4
+    assert call(d=64) == 3
+    assert call(scale=float("nan")) == 4
+    assert call(idx=A + 2) == 5
+    assert call(wsb=0) == 6                     # (ws - 1 would still suffice: the size
+    assert call(ws=A + 16) == 5                 #  query covers any head split)
+    # With no sparse heads, idx and count are not needed (the call gets as
+    # far as the workspace check); with no local heads, n_sink and window
+    # are not checked.  Every call here fails before any launch.
+    assert call(ns=0, idx=None, count=None, wsb=0) == 6
+    assert call(nl=0, sink=-1, win=0, wsb=0) == 6

@@ -22,7 +22,7 @@ def _print(*a):
 
 # ------------------------------------------------------------ full configs
 
-@pytest.mark.parametrize("mode", ["union", "per_head"])
+@pytest.mark.parametrize("mode", ["fused", "union", "per_head"])
 @pytest.mark.parametrize("ci", [0, 1, 3])
 def test_config_layer(ci, mode):
     cfg = synth.CONFIGS[ci]
@@ -40,7 +40,7 @@ def test_config2_budget_mix_all_p():
     L = load_layer(cfg)
     for p in cfg.p_list:
         rep = {}
-        res = run_layer(L, p)
+        res = run_layer(L, p, mode="fused")
         fails = check_layer(L, p, res, report=rep)
         ks = np.array(rep["k"]).reshape(cfg.B, cfg.H_r)
         _print(f"config 2 p={p}: n_S per (row, head)\n{ks}\n  exempt {rep['exempt']}")
@@ -51,7 +51,7 @@ def test_config4_sampled_layers():
     # Full-size layers of the 48-layer 1M-context stack (same kernels and
     # launch shapes as the benchmark), judged in full for every head.
     cfg = synth.CONFIGS[4]
-    for layer, mode in ((0, "union"), (47, "per_head"), (47, "union")):
+    for layer, mode in ((0, "fused"), (0, "union"), (47, "per_head"), (47, "fused")):
         _print(f"config 4 layer {layer} ({mode})")
         L = load_layer(cfg, layer, keep_host_kv=False)
         rep = {}
@@ -229,9 +229,50 @@ def test_local_unaligned_head_range():
             assert np.all(np.isnan(got[0, h]))
 
 
+@pytest.mark.parametrize("sets", ["local_only", "sparse_only", "both_unaligned"])
+def test_decode_attend_head_sets(sets):
+    # rtp_decode_attend with one set empty, and with head ranges that cut
+    # KV groups (4 query heads per KV head: heads 1..6 sparse, 7..14 local).
+    cfg = synth.CONFIGS[1].with_(N=9000, Hq=16, Hkv=4, H_r=0, needles_per_head=0)
+    L = load_layer(cfg)
+    N = cfg.N
+    sb, ns, lb, nl = {"local_only": (0, 0, 3, 11), "sparse_only": (2, 9, 0, 0),
+                      "both_unaligned": (1, 6, 7, 8)}[sets]
+    rng = np.random.default_rng(11)
+    idx = torch.zeros((1, max(ns, 1), N), dtype=torch.int32)
+    count = torch.zeros((1, max(ns, 1)), dtype=torch.int32)
+    picks = []
+    for k in range(ns):
+        c = int(rng.integers(1, 3000))
+        sel = np.sort(rng.choice(N, c, replace=False))
+        idx[0, k, :c] = torch.from_numpy(sel.astype(np.int32))
+        count[0, k] = c
+        picks.append(sel)
+    out = torch.full((1, 16, 128), float("nan"), dtype=torch.float32, device=dev())
+    ws = torch.empty(rtp.workspace_size(rtp.RTP_WS_DECODE_ATTEND, 1, 16, N), dtype=torch.uint8,
+                     device=dev())
+    rtp.rtp_decode_attend(L.d["q"], L.d["K"], L.d["V"],
+                          idx.to(dev()) if ns else None, count.to(dev()) if ns else None, N,
+                          sb, lb, nl, 4, 4096, cfg.scale, out, ws)
+    got = out.cpu().numpy()
+    rows = oracle.local_rows(N, 4, 4096)
+    for h in range(16):
+        if sb <= h < sb + ns:
+            sel = picks[h - sb]
+            ref = oracle.attention(L.q[0, h], L.K[0, h // 4, sel], L.V[0, h // 4, sel], cfg.scale)
+        elif lb <= h < lb + nl:
+            ref = oracle.attention(L.q[0, h], L.K[0, h // 4, rows], L.V[0, h // 4, rows],
+                                   cfg.scale)
+        else:
+            assert np.all(np.isnan(got[0, h])), h
+            continue
+        ok, err, rel = judge_out(got[0, h], ref)
+        assert ok, (sets, h, err, rel)
+
+
 # ------------------------------------------------------------ workspaces
 
-@pytest.mark.parametrize("mode", ["per_head", "union"])
+@pytest.mark.parametrize("mode", ["fused", "per_head", "union"])
 def test_workspace_garbage_and_reuse(mode):
     # Workspaces start as arbitrary bytes (no initialisation is required),
     # are reused by the next call, and are then reused for a smaller call
@@ -245,7 +286,10 @@ def test_workspace_garbage_and_reuse(mode):
     if step.keep_bits is not None:
         step.keep_bits.copy_(torch.randint(-2**31, 2**31 - 1, step.keep_bits.shape,
                                            dtype=torch.int32, generator=g))
-    for ws in (step.ws_sel, step.ws_sparse, step.ws_local):
+    wss = [step.ws_sel, step.ws_sparse, step.ws_local]
+    if mode == "fused":
+        wss.append(step.ws_attend)
+    for ws in wss:
         ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=g))
     for rep in range(2):
         _print(f"full-size call {rep}")
@@ -257,7 +301,9 @@ def test_workspace_garbage_and_reuse(mode):
     s2 = DecodeLayer(1, cfg.Hq, cfg.Hkv, 20000, cfg.H_r, cfg.n_sink, cfg.window, dev(),
                      mode=mode)
     s2.ws_sparse, s2.ws_local, s2.ws_sel = step.ws_sparse, step.ws_local, step.ws_sel
-    for ws in (step.ws_sparse, step.ws_local):
+    if mode == "fused":
+        s2.ws_attend = step.ws_attend
+    for ws in wss[1:]:
         ws[ws.numel() // 3:].fill_(0xFF)
     for rep in range(2):
         _print(f"smaller call {rep} on the same workspaces")
