@@ -145,40 +145,67 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f})")
 
-    # ------------------------------------------ per-call timing (eager)
-    # Each C-ABI call of the step, launched alone over all layers on the
-    # current stream and bracketed by HIP events on that stream.
-    def time_call(fn, reps=10):
-        fn()
+    # ------------------------------------------ per-call timing
+    # Each C-ABI call of the step, for every layer with that layer's own
+    # inputs (scores, kept sets), captured as one HIP graph of L launches so
+    # that no host launch gap separates them, and replayed between HIP
+    # events on the stream the launches run on: the time per launch is the
+    # kernels' own duration back to back.
+    sl = step_layer
+    scores_l = torch.empty((L, B, H_r, N), dtype=torch.float32, device=dev)
+    idx_l = torch.empty((L, B, H_r, N), dtype=torch.int32, device=dev)
+    count_l = torch.empty((L, B, H_r), dtype=torch.int32, device=dev)
+    keep_l = (torch.empty((L,) + tuple(sl.keep_bits.shape), dtype=torch.int32, device=dev)
+              if sl.keep_bits is not None else None)
+    for l in range(L):
+        rtp.rtp_index_scores(qr_all[l], kr_all[l], scores_l[l])
+        rtp.rtp_topp_select(scores_l[l], p, idx_l[l], count_l[l], sl.ws_sel,
+                            keep_bits=None if keep_l is None else keep_l[l])
+    torch.cuda.synchronize()
+
+    def time_call(issue, reps=5):
+        issue()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            issue()
+        torch.cuda.synchronize()
+        g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(reps):
-            fn()
+            g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps / L * 1e3  # us per layer
+        del g
+        return a.elapsed_time(b) / reps / L * 1e3  # us per launch (one layer)
 
-    sl = step_layer
     us = {
-        "rtp_index_scores": time_call(lambda: [rtp.rtp_index_scores(qr_all[l], kr_all[l], sl.scores)
-                                                for l in range(L)]),
-        "rtp_topp_select": time_call(lambda: [rtp.rtp_topp_select(sl.scores, p, sl.idx, sl.count, sl.ws_sel,
-                                                                  keep_bits=sl.keep_bits)
+        "rtp_index_scores": time_call(lambda: [rtp.rtp_index_scores(qr_all[l], kr_all[l],
+                                                                    scores_l[l])
                                                for l in range(L)]),
+        "rtp_topp_select": time_call(lambda: [rtp.rtp_topp_select(
+            scores_l[l], p, idx_l[l], count_l[l], sl.ws_sel,
+            keep_bits=None if keep_l is None else keep_l[l]) for l in range(L)]),
+        "rtp_topp_hist": time_call(lambda: [rtp.rtp_topp_hist(scores_l[l], sl.ws_sel)
+                                            for l in range(L)]),
     }
+    # rtp_topp_select is the hist kernel then the emit kernel, back to back;
+    # the emit kernel's duration is the difference.
+    us_emit = us["rtp_topp_select"] - us["rtp_topp_hist"]
     if sl.mode == "fused":
-        us["rtp_decode_attend"] = time_call(lambda: [sl.attend(q_all[l], K_all[l], V_all[l],
-                                                               scale, out_all[l])
-                                                     for l in range(L)])
+        us["rtp_decode_attend"] = time_call(lambda: [rtp.rtp_decode_attend(
+            q_all[l], K_all[l], V_all[l], idx_l[l], count_l[l], N, 0, H_r, Hq - H_r,
+            cfg.n_sink, cfg.window, scale, out_all[l], sl.ws_attend) for l in range(L)])
     elif sl.mode == "union":
         us["rtp_sparse_decode_union"] = time_call(lambda: [rtp.rtp_sparse_decode_union(
-            q_all[l], K_all[l], V_all[l], sl.keep_bits, N, 0, scale, out_all[l], sl.ws_sparse)
+            q_all[l], K_all[l], V_all[l], keep_l[l], N, 0, scale, out_all[l], sl.ws_sparse)
             for l in range(L)])
     else:
         us["rtp_sparse_decode"] = time_call(lambda: [rtp.rtp_sparse_decode(
-            q_all[l], K_all[l], V_all[l], sl.idx, sl.count, 0, scale, out_all[l], sl.ws_sparse)
-            for l in range(L)])
+            q_all[l], K_all[l], V_all[l], idx_l[l], count_l[l], 0, scale, out_all[l],
+            sl.ws_sparse) for l in range(L)])
     if sl.mode != "fused":
         us["rtp_local_decode"] = time_call(lambda: [rtp.rtp_local_decode(
             q_all[l], K_all[l], V_all[l], N, H_r, Hq - H_r, cfg.n_sink, cfg.window, scale,
@@ -194,18 +221,19 @@ def main():
     local_kv = Hkv - G_r
     n_sel = []
     union = []
+    counts = count_l.cpu().numpy()
     for l in range(L):
-        step_layer.retrieval(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l], p, scale, out_all[l])
-        cnt = step_layer.count.cpu().numpy()
+        cnt = counts[l]
         u = 0
         for b in range(B):
             for g in range(G_r):
                 mark = torch.zeros(N, dtype=torch.bool, device=dev)
                 for h in range(g * cfg.G, min(H_r, (g + 1) * cfg.G)):
-                    mark[step_layer.idx[b, h, :int(cnt[b, h])].long()] = True
+                    mark[idx_l[l, b, h, :int(cnt[b, h])].long()] = True
                 u += int(mark.sum().item())
         union.append(u)
         n_sel.append(cnt.reshape(-1).tolist())
+    del scores_l, idx_l, keep_l
     torch.cuda.synchronize()
     kr_bytes = B * G_r * N * cfg.r * 4
     gather_bytes = np.array(union) * 2 * d * 2
@@ -216,9 +244,12 @@ def main():
     steps_per_s = 1e3 / ms_step
     achieved_gbps = B_alg / (ms_step * 1e-3) / 1e9
 
-    # Roofline of the dominant kernel: of the calls that launch one kernel
-    # (so HIP events around the call time that kernel alone), the one with the
-    # largest time per layer.  Algorithmic bytes per launch (one layer):
+    # Roofline of the dominant kernel: the kernel with the largest time per
+    # layer.  Calls that launch one kernel are timed directly; the emit
+    # kernel is rtp_topp_select minus rtp_topp_hist.  Algorithmic bytes per
+    # launch (one layer):
+    #   emit    4 B per score read + 4 B per kept index written;
+    #   hist    4 B per score read;
     #   scan    64 B of k_r read + 4 B of score written per query head, per
     #           token and retrieval KV head;
     #   sparse  512 B (K + V row) per row of the union of the group's kept
@@ -229,7 +260,10 @@ def main():
     csrc = os.path.join(ROOT, "sparse_long_context_indexer_amd", "csrc")
     sel_total = float(np.mean([sum(x) for x in n_sel]))
     sparse_bytes = float(np.mean(union)) * 2 * d * 2 + sel_total * 4
+    us["sel_emit_kernel"] = us_emit
     cands = {
+        "sel_emit_kernel": ("sel_emit_kernel", B * H_r * N * 4 + sel_total * 4, "select.hip"),
+        "rtp_topp_hist": ("sel_hist_kernel", B * H_r * N * 4, "select.hip"),
         "rtp_index_scores": ("index_scores_kernel<8>", B * G_r * N * (cfg.r * 4 + cfg.G * 4),
                              "scan.hip"),
         "rtp_decode_attend": ("attend_kernel", sparse_bytes + window_bytes, "attend.hip"),

@@ -113,6 +113,19 @@ rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H,
                            size_t ws_bytes, void *stream);
 
 /*
+ * rtp_topp_hist -- the first of rtp_topp_select's two launches on its own:
+ * the per-row mass histograms (same passage) are left in the workspace and
+ * no output is written.  rtp_topp_select launches this and then its second
+ * kernel, which consumes the histograms; calling rtp_topp_hist alone is
+ * harmless (a later rtp_topp_select starts over).  It exists so that the
+ * histogram pass can be timed or profiled apart.
+ *
+ *   scores, B, H, N, workspace as in rtp_topp_select.
+ */
+rtp_status rtp_topp_hist(const float *scores, int32_t B, int32_t H, int32_t N,
+                         void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * rtp_sparse_decode -- exact attention of each retrieval query head over
  * its selected rows only (arXiv abstract: sparse attention over the
  * indexer's tokens; gist.science summary, method section 5: bandwidth-

@@ -25,7 +25,7 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPP
           4: "RTP_ERR_VALUE", 5: "RTP_ERR_ALIGN", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
 
 # Every symbol include/rtp.h declares.
-SYMBOLS = ("rtp_index_scores", "rtp_topp_select", "rtp_sparse_decode",
+SYMBOLS = ("rtp_index_scores", "rtp_topp_select", "rtp_topp_hist", "rtp_sparse_decode",
            "rtp_sparse_decode_union", "rtp_local_decode", "rtp_decode_attend",
            "rtp_workspace_size", "rtp_status_string", "rtp_last_hip_error")
 
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
                                 ctypes.c_float, ctypes.c_size_t)
         L.rtp_index_scores.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, P]
         L.rtp_topp_select.argtypes = [P, I32, I32, I32, F32, P, P, P, P, SZ, P]
+        L.rtp_topp_hist.argtypes = [P, I32, I32, I32, P, SZ, P]
         L.rtp_sparse_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32,
                                         I32, I32, F32, P, P, SZ, P]
         L.rtp_sparse_decode_union.argtypes = [P, P, P, P, I32, I32, I32, I32, I64, I32, I32,
@@ -70,7 +71,7 @@ def lib() -> ctypes.CDLL:
         L.rtp_status_string.restype = ctypes.c_char_p
         L.rtp_last_hip_error.argtypes = []
         L.rtp_last_hip_error.restype = I32
-        for name in SYMBOLS[:7]:
+        for name in SYMBOLS[:8]:
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -156,6 +157,16 @@ def rtp_topp_select(scores, p, idx, count, workspace, keep_bits=None, stream=Non
         _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2), kb,
         _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
         _stream(scores, stream)), "rtp_topp_select")
+
+
+def rtp_topp_hist(scores, workspace, stream=None) -> None:
+    """The histogram pass of rtp_topp_select alone (no output written)."""
+    import torch
+    B, H, N = scores.shape
+    _check(lib().rtp_topp_hist(
+        _dev(scores, torch.float32, "scores", 3), B, H, N,
+        _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
+        _stream(scores, stream)), "rtp_topp_hist")
 
 
 def rtp_sparse_decode(q, K, V, idx, count, q_head_begin, scale, out, workspace,

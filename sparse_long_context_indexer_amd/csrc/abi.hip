@@ -109,6 +109,17 @@ rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H, int32_t N,
                                             as_stream(stream)));
 }
 
+rtp_status rtp_topp_hist(const float *scores, int32_t B, int32_t H, int32_t N, void *workspace,
+                         size_t ws_bytes, void *stream)
+{
+    if (!scores || !workspace) return RTP_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1 || (int64_t)B * H > kMaxGridY) return RTP_ERR_SHAPE;
+    if (!aligned(scores, 4) || !aligned(workspace, 256)) return RTP_ERR_ALIGN;
+    const int64_t R = (int64_t)B * H;
+    if (ws_bytes < rtp::sel_layout(R, N).total) return RTP_ERR_WORKSPACE;
+    return from_hip(rtp::launch_topp_hist(scores, R, N, workspace, as_stream(stream)));
+}
+
 rtp_status rtp_sparse_decode(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,
                              const int32_t *idx, const int32_t *count, int32_t B, int32_t Hq,
                              int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,

@@ -903,6 +903,13 @@ __global__ __launch_bounds__(256) void sel_all_kernel(int N, int32_t *__restrict
     }
 }
 
+hipError_t launch_topp_hist(const float *scores, int64_t R, int N, void *ws, hipStream_t stream)
+{
+    SelPtrs P = sel_ptrs(ws, R, N);
+    return launch(sel_hist_kernel, dim3((unsigned)P.nblk, (unsigned)R), dim3(kSelThreads), 0,
+                  stream, scores, N, P);
+}
+
 hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p, int32_t *idx,
                               int32_t *count, uint32_t *keep_bits, void *ws, hipStream_t stream)
 {

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -202,3 +202,15 @@ def test_decode_attend_validation(lib):
     # are not checked.  Every call here fails before any launch.
     assert call(ns=0, idx=None, count=None, wsb=0) == 6
     assert call(nl=0, sink=-1, win=0, wsb=0) == 6
+
+
+def test_topp_hist_validation(lib):
+    f = lib.rtp_topp_hist
+    ws = rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 1, 8, 1000)
+    assert f(None, 1, 8, 1000, A, ws, None) == 1
+    assert f(A, 1, 8, 1000, None, ws, None) == 1
+    assert f(A, 1, 8, 0, A, ws, None) == 2
+    assert f(A, 0, 8, 1000, A, ws, None) == 2
+    assert f(A + 2, 1, 8, 1000, A, ws, None) == 5
+    assert f(A, 1, 8, 1000, A + 16, ws, None) == 5
+    assert f(A, 1, 8, 1000, A, ws - 1, None) == 6

@@ -149,6 +149,30 @@ def test_select_p_one_keeps_all():
             assert np.array_equal(np.sort(sets[b][h]), np.arange(9000))
 
 
+def test_topp_hist_alone_then_select():
+    # The histogram pass alone writes no output, and a select after one or
+    # two of them still finds the oracle's sets.
+    rng = np.random.default_rng(5)
+    s = (rng.standard_normal((2, 3, 70_001)) * 3).astype(np.float32)
+    sd = torch.from_numpy(s).to(dev())
+    B, H, N = s.shape
+    ws = torch.empty(rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, B, H, N), dtype=torch.uint8,
+                     device=dev())
+    idx = torch.full((B, H, N), -7, dtype=torch.int32, device=dev())
+    cnt = torch.full((B, H), -7, dtype=torch.int32, device=dev())
+    rtp.rtp_topp_hist(sd, ws)
+    torch.cuda.synchronize()
+    assert torch.all(idx == -7) and torch.all(cnt == -7)
+    rtp.rtp_topp_hist(sd, ws)
+    rtp.rtp_topp_select(sd, 0.9, idx, cnt, ws)
+    c = cnt.cpu().numpy()
+    ix = idx.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            v = judge_set(s[b, h], 0.9, ix[b, h, :c[b, h]])
+            assert v.ok, (b, h, v.k_gpu, v.k_oracle)
+
+
 def test_select_repeatable():
     cfg = synth.CONFIGS[2].with_(N=65536)
     q_r, k_r = synth.layer_qr(cfg, 0), synth.layer_kr(cfg, 0)
