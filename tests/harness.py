@@ -122,7 +122,7 @@ def bits_to_set(words: np.ndarray, N: int) -> np.ndarray:
     return np.flatnonzero(bits[:N]).astype(np.int64)
 
 
-def run_layer(L: Layer, p: float, step=None, mode: str = "per_head"):
+def run_layer(L: Layer, p: float, step=None, mode: str = "fused"):
     """Runs the whole layer on the GPU; returns host copies of the results."""
     from sparse_long_context_indexer_amd.runner import DecodeLayer
     cfg = L.cfg
