@@ -422,21 +422,28 @@ __device__ void pick_block(const ChunkTop *tops, int nblk, float p, const double
         S.wlow_before[w] = lowest_before;
     }
     __syncthreads();
-    if (tid == 0) {
-        int wc = -1, wl = -1;
-        for (int i = 0; i < kResNW && wc < 0; ++i)
-            if (S.wcross[i] >= 0) wc = i;
-        for (int i = kResNW - 1; i >= 0 && wl < 0; --i)
-            if (S.wlow[i] >= 0) wl = i;
-        if (wc >= 0) {
-            S.j1 = (uint32_t)S.wcross[wc];
-            S.A = S.wcross_before[wc];
-        } else {
-            S.j1 = wl >= 0 ? (uint32_t)S.wlow[wl] : 0u;
-            S.A = wl >= 0 ? S.wlow_before[wl] : 0.0;
+    if (w == 0) {
+        // Lane i looks at wave i's reports; the first wave with a crossing,
+        // else the last wave with mass.
+        const bool hc = lane < kResNW && S.wcross[lane] >= 0;
+        const bool hl = lane < kResNW && S.wlow[lane] >= 0;
+        const uint64_t cb = __ballot(hc), lb = __ballot(hl);
+        if (lane == 0) {
+            if (cb) {
+                const int wc = __ffsll((unsigned long long)cb) - 1;
+                S.j1 = (uint32_t)S.wcross[wc];
+                S.A = S.wcross_before[wc];
+            } else if (lb) {
+                const int wl = 63 - __clzll((unsigned long long)lb);
+                S.j1 = (uint32_t)S.wlow[wl];
+                S.A = S.wlow_before[wl];
+            } else {
+                S.j1 = 0u;
+                S.A = 0.0;
+            }
+            S.T = T;
+            S.M = Mf;
         }
-        S.T = T;
-        S.M = Mf;
     }
     __syncthreads();
 }
@@ -558,16 +565,26 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
 // candidates at a time; a wave reserves the slots of all of them with one
 // LDS atomic (both counts packed in 16-bit halves, which never carry: a
 // wave holds at most 64 * kB of each).
+// With acc_next, the moved candidates' histogram over key bits [9:0]
+// (mass exp(s - M) and count) is built in S.hm / S.hc on the way, for the
+// next score level.
 template <bool kGlobal>
 __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int shift,
                                    uint32_t mask, uint32_t j, bool emit_above, bool by_index,
-                                   int32_t *ir, uint32_t *kbr, ResShared &S)
+                                   int32_t *ir, uint32_t *kbr, ResShared &S,
+                                   bool acc_next = false, double M = 0.0)
 {
     // From global memory, kB loads per thread are in flight before any is used.
     constexpr int kB = kGlobal ? 10 : 4;
     static_assert(kWave * kB < 65536, "per-wave counts fit in 16 bits");
+    static_assert(kResThreads == kDig, "one digit per thread");
     if (threadIdx.x == 0) S.nn &= 0xFFFFFFFFull;  // no candidates moved yet
-    __syncthreads();
+    __syncthreads();  // every thread has read what it needed of S.hm / S.hc
+    if (acc_next) {
+        S.hm[threadIdx.x] = 0.0;
+        S.hc[threadIdx.x] = 0u;
+        __syncthreads();
+    }
     for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kResThreads * kB) {
         uint2 e[kB];
 #pragma unroll
@@ -597,7 +614,14 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
             if (outm & (1u << u)) keep_token(ir, pa++, e[u].y, kbr);
-            if (keepm & (1u << u)) dst[pk++] = e[u];
+            if (keepm & (1u << u)) {
+                dst[pk++] = e[u];
+                if (acc_next) {
+                    const uint32_t d1 = e[u].x & (uint32_t)(kDig - 1);
+                    atomicAdd(&S.hm[d1], exp_tang((double)key_score(e[u].x) - M, S.etbl));
+                    atomicAdd(&S.hc[d1], 1u);
+                }
+            }
         }
     }
     __syncthreads();
@@ -632,13 +656,14 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
     // Score levels: key bits [19:10] (histogram built by the emit blocks),
     // then [9:0] (histogram of the survivors).
     static_assert(kResThreads == kDig, "one digit per thread");
+    bool next_built = false;  // level 1's histogram was built by level 0's filter
     for (int level = 0; level < 2 && n > 0; ++level) {
         const int shift = level == 0 ? kShift2 : 0;
         if (level == 0) {
             S.hm[tid] = h2m;
             S.hc[tid] = h2c;
             __syncthreads();
-        } else {
+        } else if (!next_built) {
             S.hm[tid] = 0.0;
             S.hc[tid] = 0u;
             __syncthreads();
@@ -660,8 +685,11 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
             cur ^= 1;
             cr = S.buf[cur];
         } else if (S.hc[j] <= (uint32_t)kResCap) {
-            // The boundary digit's candidates fit in LDS: continue there.
-            n = res_filter_lds<true>(gc, n, S.buf[0], shift, kDig - 1, j, true, false, ir, kbr, S);
+            // The boundary digit's candidates fit in LDS: continue there,
+            // building the next level's histogram on the way.
+            next_built = level == 0;
+            n = res_filter_lds<true>(gc, n, S.buf[0], shift, kDig - 1, j, true, false, ir, kbr, S,
+                                     next_built, M);
             in_lds = true;
             cur = 0;
             cr = S.buf[0];
@@ -831,43 +859,54 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     if (lane_id() == 0)
         wbase[w] = atomicAdd(&S.bcount, ((unsigned long long)(wtot >> 16) << 32) | (wtot & 0xFFFFu));
     __syncthreads();
-    if (threadIdx.x == 0)
-        S.gbase = S.bcount ? atomicAdd(reinterpret_cast<unsigned long long *>(&P.rows[r].slots),
-                                       S.bcount)
-                           : 0ull;
-    __syncthreads();
-    const unsigned long long base = S.gbase + wbase[w];
-    const uint32_t ex = inc - mine;
-    uint32_t oa = (uint32_t)(base >> 32) + (ex >> 16);
-    for (uint32_t m = above; m; m &= m - 1) ir[oa++] = (int32_t)cv.index32(__ffs(m) - 1);
-    // Candidates: staged in LDS in block order (the resolve's buffers are
-    // free until then), then written out coalesced; a block with more
-    // candidates than the stage holds writes them directly.
-    const uint32_t bc = (uint32_t)S.bcount;                 // this block's candidates
-    uint2 *gcb = cr + (uint32_t)S.gbase;                      // ... their place in the row
+    // The row offsets come back from a global atomic; until they are needed
+    // the block stages its candidates in LDS and builds its share of the
+    // row's Hist2 (candidates by key bits [19:10], mass exp(s - M)) there.
+    const uint32_t bc = (uint32_t)S.bcount;  // this block's candidates
+    unsigned long long gb = 0;
+    if (threadIdx.x == 0 && S.bcount)
+        gb = atomicAdd(reinterpret_cast<unsigned long long *>(&P.rows[r].slots), S.bcount);
     uint2 *stage = &S.buf[0][0];
     const bool staged = bc <= (uint32_t)(2 * kResCap);
-    uint32_t oc = (uint32_t)wbase[w] + (ex & 0xFFFFu);
-#pragma unroll
-    for (int t = 0; t < kSelPerThread; ++t) {
-        if (!(atb & (1u << t))) continue;
-        const uint2 e = make_uint2(score_key(v[t]), cv.index32(t));
-        if (staged)
-            stage[oc++] = e;
-        else
-            st_cand(gcb + oc++, e);
-    }
-    wait_vmem();
-    __syncthreads();
-    // This block's share of the row's Hist2: candidates by key bits
-    // [19:10], with mass exp(s - M).
+    const uint32_t ex = inc - mine;
     const double M = (double)S.M;
-    for (uint32_t k = threadIdx.x; k < bc; k += kSelThreads) {
-        const uint2 e = staged ? stage[k] : ld_cand(gcb + k);
-        if (staged) st_cand(gcb + k, e);
-        const uint32_t dg = (e.x >> kShift2) & (uint32_t)(kDig - 1);
-        atomicAdd(&S.hm[dg], exp_tang((double)key_score(e.x) - M, S.etbl));
-        atomicAdd(&S.hc[dg], 1u);
+    if (staged) {
+        uint32_t oc = (uint32_t)wbase[w] + (ex & 0xFFFFu);
+#pragma unroll
+        for (int t = 0; t < kSelPerThread; ++t)
+            if (atb & (1u << t)) stage[oc++] = make_uint2(score_key(v[t]), cv.index32(t));
+        __syncthreads();
+        for (uint32_t k = threadIdx.x; k < bc; k += kSelThreads) {
+            const uint2 e = stage[k];
+            const uint32_t dg = (e.x >> kShift2) & (uint32_t)(kDig - 1);
+            atomicAdd(&S.hm[dg], exp_tang((double)key_score(e.x) - M, S.etbl));
+            atomicAdd(&S.hc[dg], 1u);
+        }
+    }
+    if (threadIdx.x == 0) S.gbase = gb;
+    __syncthreads();
+    const unsigned long long base = S.gbase + wbase[w];
+    uint32_t oa = (uint32_t)(base >> 32) + (ex >> 16);
+    for (uint32_t m = above; m; m &= m - 1) ir[oa++] = (int32_t)cv.index32(__ffs(m) - 1);
+    uint2 *gcb = cr + (uint32_t)S.gbase;  // this block's candidates' place in the row
+    if (staged) {
+        // Written out coalesced, in block order.
+        for (uint32_t k = threadIdx.x; k < bc; k += kSelThreads) st_cand(gcb + k, stage[k]);
+    } else {
+        // More candidates than the stage holds: written directly, then read
+        // back for the histogram.
+        uint32_t oc = (uint32_t)wbase[w] + (ex & 0xFFFFu);
+#pragma unroll
+        for (int t = 0; t < kSelPerThread; ++t)
+            if (atb & (1u << t)) st_cand(gcb + oc++, make_uint2(score_key(v[t]), cv.index32(t)));
+        wait_vmem();
+        __syncthreads();
+        for (uint32_t k = threadIdx.x; k < bc; k += kSelThreads) {
+            const uint2 e = ld_cand(gcb + k);
+            const uint32_t dg = (e.x >> kShift2) & (uint32_t)(kDig - 1);
+            atomicAdd(&S.hm[dg], exp_tang((double)key_score(e.x) - M, S.etbl));
+            atomicAdd(&S.hc[dg], 1u);
+        }
     }
     __syncthreads();
     if (S.hc[threadIdx.x]) {
