@@ -152,8 +152,10 @@ __device__ __forceinline__ float wave_max(float v)
 // Exclusive prefix sum over a block of NT threads in thread order; every
 // thread must call it.  `scratch` holds NT/64 elements of LDS.  Returns
 // the exclusive prefix; *total receives the block-wide sum.  Every thread
-// adds the wave totals in the same order, so all agree on *total.
-template <int NT, typename T>
+// adds the wave totals in the same order, so all agree on *total.  With
+// kReuse false the caller promises not to write `scratch` again, and the
+// closing barrier is skipped.
+template <int NT, typename T, bool kReuse = true>
 __device__ __forceinline__ T block_exclusive_scan(T v, T *scratch, T *total)
 {
     constexpr int NW = NT / kWave;
@@ -170,7 +172,7 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *scratch, T *total)
         run += t;
     }
     *total = run;
-    __syncthreads();
+    if (kReuse) __syncthreads();
     return before + prev;
 }
 

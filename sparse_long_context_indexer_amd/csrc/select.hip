@@ -381,7 +381,7 @@ __device__ void pick_block(const ChunkTop *tops, int nblk, float p, const double
         local += wv[k];
     }
     double Z;
-    const double before = block_exclusive_scan<kSelThreads>(local, S.dscan, &Z);
+    const double before = block_exclusive_scan<kSelThreads, double, false>(local, S.dscan, &Z);
     const double T = (double)p * Z;
     // The boundary is the highest bin with mass whose running sum (every bin
     // down to and including it) reaches T; each thread tests its own bins,
@@ -452,32 +452,36 @@ __device__ void pick_block(const ChunkTop *tops, int nblk, float p, const double
 // digits 0..kDig-1: the highest non-empty digit whose running mass (A plus
 // every digit down to and including it) reaches T -- a test no rounding of
 // the parallel prefix can skip -- or, if the total stays below T, the
-// lowest non-empty digit.  Lane l owns digits kDig - 1 - 16l - [0, 16).
+// lowest non-empty digit.  Lane l owns digits kDig - 1 - 16l - [0, 16); it
+// reads them into registers once and decides with selects.
 __device__ void res_choose_mass(double A, double T, ResShared &S)
 {
     const int lane = lane_id();
     constexpr int kPerLane = kDig / kWave;
     const int top = kDig - 1 - kPerLane * lane;
+    double wv[kPerLane];
+    uint32_t cv[kPerLane];
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) {
+        wv[k] = S.hm[top - k];
+        cv[k] = S.hc[top - k];
+    }
     double local = 0.0;
 #pragma unroll
-    for (int k = 0; k < kPerLane; ++k) local += S.hm[top - k];
+    for (int k = 0; k < kPerLane; ++k) local += wv[k];
     const double inc = wave_inclusive_scan(local);
     double cum = A + (inc - local);
     int cross = -1, low = -1;
     double cross_b = 0.0, low_b = 0.0;
 #pragma unroll
     for (int k = 0; k < kPerLane; ++k) {
-        const int d = top - k;
-        const double w = S.hm[d];
-        if (S.hc[d]) {
-            if (cross < 0 && cum + w >= T) {
-                cross = d;
-                cross_b = cum;
-            }
-            low = d;
-            low_b = cum;
-        }
-        cum += w;
+        const bool ne = cv[k] != 0u;
+        const bool hit = ne && cross < 0 && cum + wv[k] >= T;
+        cross = hit ? top - k : cross;
+        cross_b = hit ? cum : cross_b;
+        low = ne ? top - k : low;
+        low_b = ne ? cum : low_b;
+        cum += wv[k];
     }
     // Highest crossing digit = lowest lane with a crossing; else the lowest
     // non-empty digit = highest lane with one.
