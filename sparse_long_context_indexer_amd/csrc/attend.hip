@@ -758,11 +758,19 @@ size_t local_ws_bytes(int64_t B, int64_t n_q, int N)
 }
 
 constexpr int kLocSlots = kAttThreads / 32;         // rows in progress per block step
-constexpr int kLocRowsPerIter = kLocSlots * kLocalU;
+
+constexpr int kLocTile = 64;  // rows staged in LDS at a time
 
 struct LocalShared {
-    float m[kLocSlots][8], l[kLocSlots][8];
-    float o[kLocSlots][8][128];
+    union {
+        struct {  // a tile of K and V rows (16 pieces of 16 B per row)
+            uint4 k[kLocTile][16], v[kLocTile][16];
+        } st;
+        struct {  // the row slots' softmax states, merged per head
+            float m[kLocSlots][8], l[kLocSlots][8];
+            float o[kLocSlots][8][128];
+        } mg;
+    };
     int last;
 };
 
@@ -771,21 +779,15 @@ struct Heads4 {
     float m[4], l[4], o[4][8];
 };
 
-__device__ __forceinline__ void heads4_init(Heads4 &st, const uint16_t *__restrict__ q, int64_t q0,
-                                            int nh, int half, float qscale, int sub)
+// q words (8 bf16 of this lane's dims for each of the group's 4 heads, zero
+// for heads past the chunk) to the scaled fp32 state; softmax state empty.
+__device__ __forceinline__ void heads4_init(Heads4 &st, const uint4 (&qw)[4], float qscale)
 {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int hh = half * 4 + k;
-        if (hh < nh) {
-            const uint4 qw = *reinterpret_cast<const uint4 *>(q + q0 + hh * 128 + sub * 8);
-            bf16x8_to_f32(qw, st.qf[k]);
+        bf16x8_to_f32(qw[k], st.qf[k]);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) st.qf[k][c] *= qscale;
-        } else {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) st.qf[k][c] = 0.0f;
-        }
+        for (int c = 0; c < 8; ++c) st.qf[k][c] *= qscale;
         st.m[k] = -INFINITY;
         st.l[k] = 0.0f;
 #pragma unroll
@@ -879,37 +881,80 @@ __device__ void local_block(const uint16_t *__restrict__ q, const uint16_t *__re
     const int64_t sink_end = A.n_sink < w_start ? A.n_sink : w_start;
     const int64_t n_rows = sink_end + (N - w_start);
     int64_t chunk = (n_rows + A.S - 1) / A.S;
-    chunk = (chunk + kLocRowsPerIter - 1) / kLocRowsPerIter * kLocRowsPerIter;
+    chunk = (chunk + kLocTile - 1) / kLocTile * kLocTile;
     const int64_t begin = (int64_t)s * chunk;
     const int64_t end = min(n_rows, begin + chunk);
 
     const int lane = lane_id(), w = threadIdx.x / kWave;
     const int grp = lane >> 4, sub = lane & 15;
     const int half = grp & 1, slot = w * 2 + (grp >> 1);
-    const int64_t kvb = ((int64_t)b * Hkv + hc.g) * kv_cap * 128 + sub * 8;
+    const int64_t kvb = ((int64_t)b * Hkv + hc.g) * kv_cap * 128;
     const uint16_t *Kb = K + kvb;
     const uint16_t *Vb = V + kvb;
-    uint4 kw[kLocalU], vw[kLocalU];
-    bool ok[kLocalU];
-    auto load_rows = [&](int64_t base) {
+    // A tile of kLocTile rows is staged in LDS with every load in flight at
+    // once (the rows of a split are contiguous apart from the sink/window
+    // seam): thread t moves 16-B pieces t + 256 i of the tile's K and V.
+    constexpr int kPieces = kLocTile * 16 / kAttThreads;
+    uint4 kx[kPieces], vx[kPieces];
+    auto load_tile = [&](int64_t t0, int nt) {
 #pragma unroll
-        for (int u = 0; u < kLocalU; ++u) {
-            const int64_t j = base + u * kLocSlots + slot;
-            ok[u] = j < end;
-            const int64_t row = j < sink_end ? j : w_start + (j - sink_end);
-            const int64_t off = ok[u] ? row * 128 : 0;
-            kw[u] = *reinterpret_cast<const uint4 *>(Kb + off);
-            vw[u] = *reinterpret_cast<const uint4 *>(Vb + off);
+        for (int i = 0; i < kPieces; ++i) {
+            const int e = threadIdx.x + i * kAttThreads, row = e >> 4, pc = e & 15;
+            const int64_t j = t0 + (row < nt ? row : 0);
+            const int64_t g = j < sink_end ? j : w_start + (j - sink_end);
+            kx[i] = *reinterpret_cast<const uint4 *>(Kb + g * 128 + pc * 8);
+            vx[i] = *reinterpret_cast<const uint4 *>(Vb + g * 128 + pc * 8);
         }
     };
-    // The first rows are requested before q, so both loads overlap.
-    if (begin < end) load_rows(begin);
+    // q and the first tile are requested together; q is converted once the
+    // tile is in LDS.
+    uint4 qw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int hh = half * 4 + k;
+        qw[k] = hh < hc.nh ? *reinterpret_cast<const uint4 *>(
+                                 q + ((int64_t)b * Hq + hc.h_lo + hh) * 128 + sub * 8)
+                           : make_uint4(0u, 0u, 0u, 0u);
+    }
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < kPieces; ++i) {
+            const int e = threadIdx.x + i * kAttThreads;
+            sh.st.k[e >> 4][e & 15] = kx[i];
+            sh.st.v[e >> 4][e & 15] = vx[i];
+        }
+    };
     Heads4 st;
-    heads4_init(st, q, ((int64_t)b * Hq + hc.h_lo) * 128, hc.nh, half, qscale, sub);
+    if (begin < end) {
+        load_tile(begin, (int)min<int64_t>(kLocTile, end - begin));
+        store_tile();
+    }
+    heads4_init(st, qw, qscale);
     const bool b3 = (sub >> 3) & 1, b2 = (sub >> 2) & 1;
-    for (int64_t base = begin; base < end; base += kLocRowsPerIter) {
-        if (base != begin) load_rows(base);
-        heads4_step(st, kw, vw, ok, b3, b2);
+    for (int64_t t0 = begin; t0 < end; t0 += kLocTile) {
+        const int nt = (int)min<int64_t>(kLocTile, end - t0);
+        if (t0 != begin) {
+            load_tile(t0, nt);
+            store_tile();
+        }
+        __syncthreads();
+        // Lane group (slot, half) takes rows slot, slot + kLocSlots, ...
+        // (kLocalU rows at a time: reading more from LDS ahead of use would
+        // not fit the register budget).
+#pragma unroll 1
+        for (int u0 = 0; u0 < kLocTile / kLocSlots; u0 += kLocalU) {
+            uint4 kw[kLocalU], vw[kLocalU];
+            bool ok[kLocalU];
+#pragma unroll
+            for (int u = 0; u < kLocalU; ++u) {
+                const int j = (u0 + u) * kLocSlots + slot;
+                ok[u] = j < nt;
+                kw[u] = sh.st.k[j][sub];
+                vw[u] = sh.st.v[j][sub];
+            }
+            heads4_step(st, kw, vw, ok, b3, b2);
+        }
+        __syncthreads();  // the tile area is reused by the next tile and the merge
     }
 
     // The block's row slots, merged in LDS: one partial per head of the chunk.
@@ -917,10 +962,10 @@ __device__ void local_block(const uint16_t *__restrict__ q, const uint16_t *__re
     for (int k = 0; k < 4; ++k) {
         const int hh = half * 4 + k;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sh.o[slot][hh][sub * 8 + c] = st.o[k][c];
+        for (int c = 0; c < 8; ++c) sh.mg.o[slot][hh][sub * 8 + c] = st.o[k][c];
         if (sub == 0) {
-            sh.m[slot][hh] = st.m[k];
-            sh.l[slot][hh] = st.l[k];
+            sh.mg.m[slot][hh] = st.m[k];
+            sh.mg.l[slot][hh] = st.l[k];
         }
     }
     __syncthreads();
@@ -930,13 +975,13 @@ __device__ void local_block(const uint16_t *__restrict__ q, const uint16_t *__re
         if (hh < hc.nh) {
             float M = -INFINITY;
 #pragma unroll
-            for (int k = 0; k < kLocSlots; ++k) M = fmaxf(M, sh.m[k][hh]);
+            for (int k = 0; k < kLocSlots; ++k) M = fmaxf(M, sh.mg.m[k][hh]);
             float L = 0.0f, O[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < kLocSlots; ++k) {
-                const float f = rescale(sh.m[k][hh], M);
-                L = fmaf(sh.l[k][hh], f, L);
-                const float4 ov = *reinterpret_cast<const float4 *>(&sh.o[k][hh][d]);
+                const float f = rescale(sh.mg.m[k][hh], M);
+                L = fmaf(sh.mg.l[k][hh], f, L);
+                const float4 ov = *reinterpret_cast<const float4 *>(&sh.mg.o[k][hh][d]);
                 O[0] = fmaf(ov.x, f, O[0]);
                 O[1] = fmaf(ov.y, f, O[1]);
                 O[2] = fmaf(ov.z, f, O[2]);
