@@ -259,10 +259,17 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
     // s - ref is exact in fp32: a bin's scores and its reference share one
     // sign and binade.  A slot past the end of the row (-inf) has a NaN
     // reference, and exp_tang gives NaN +0.
+    // A bin's top score shares the sign and the bits above kShift1 with
+    // every score of the bin: the low bits all set for a positive score,
+    // all clear for a negative one.
 #pragma unroll
     for (int t = 0; t < kSelPerThread; ++t) {
-        const uint32_t bin = score_key(v[t]) >> kShift1;
-        const float ref = bin == tb ? mb : bin_top(bin);
+        const uint32_t u = __float_as_uint(v[t] + 0.0f);  // -0 folded into +0
+        const uint32_t sm = (uint32_t)((int32_t)u >> 31);
+        const uint32_t bin = (u ^ (sm | 0x80000000u)) >> kShift1;  // score_key(v) >> kShift1
+        constexpr uint32_t kLow = (1u << kShift1) - 1u;
+        const uint32_t top = (u | (kLow & ~sm)) & ~(kLow & sm);      // bin_top(bin)
+        const float ref = bin == tb ? mb : __uint_as_float(top);
         atomicAdd(&hm[bin], exp_tang((double)(v[t] - ref), S.etbl));
     }
     if (blk != 0 && threadIdx.x == 0) wait_row_ready(P.rows[r]);

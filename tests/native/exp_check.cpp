@@ -27,7 +27,7 @@ int main()
 {
     long double tmax = 0;
     for (int j = 0; j < rtp::kExpTable; ++j) {
-        long double u = ulps(kTbl[j], exp2l((long double)j / 64.0L));
+        long double u = ulps(kTbl[j], exp2l((long double)j / (long double)rtp::kExpTable));
         if (u > tmax) tmax = u;
     }
     long double emax = 0, smax = 0;

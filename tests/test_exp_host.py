@@ -1,6 +1,6 @@
 """The selector's fp64 exponential (csrc/rtp_exp.h), compiled for the host
 with g++ and checked against the C library's long-double expl: the table
-2^(j/64) correctly rounded, and the function within 1.5 ulp of the exact
+2^(j/256) correctly rounded, and the function within 1.5 ulp of the exact
 value for normal results (subnormal results within 1.5 subnormal ulps)."""
 import os
 import subprocess
