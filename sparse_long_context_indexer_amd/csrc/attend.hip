@@ -308,8 +308,8 @@ __device__ void sparse_block(const uint16_t *__restrict__ q, const uint16_t *__r
         for (int u = 0; u < kSparseU; ++u) {
             ok[u] = (unsigned)tn[u] < (unsigned)N;
             const int64_t off = ok[u] ? (int64_t)tn[u] * 128 : 0;
-            kw[u] = *reinterpret_cast<const uint4 *>(Kb + off);
-            vw[u] = *reinterpret_cast<const uint4 *>(Vb + off);
+            kw[u] = ld_nt16(Kb + off);
+            vw[u] = ld_nt16(Vb + off);
         }
         if (base + kRowsPerIter < end) load_idx(base + kRowsPerIter);
         float lg[kSparseU];

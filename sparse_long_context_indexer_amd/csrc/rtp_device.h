@@ -213,6 +213,15 @@ __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-B load with the nontemporal hint: for data read once and not again
+// soon (gathered K/V rows), so it does not displace what is.
+__device__ __forceinline__ uint4 ld_nt16(const void *p)
+{
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // Waits until every vector memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
