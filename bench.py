@@ -39,10 +39,13 @@ def parse():
     ap.add_argument("--p", type=float, default=0.9)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-side-stream", action="store_true")
-    ap.add_argument("--sparse-mode", choices=["fused", "union", "per_head"], default="fused",
-                    help="fused: sparse and local heads in one rtp_decode_attend launch; "
-                         "per_head: separate calls, local heads on a side stream; union: "
-                         "each kept row read once per KV head for all its query heads")
+    ap.add_argument("--sparse-mode", choices=["fused", "scan_local", "union", "per_head"],
+                    default="fused",
+                    help="scan_local: scan and local heads in one rtp_scan_local launch, sparse "
+                         "heads in rtp_decode_attend; fused: sparse and local heads in one "
+                         "rtp_decode_attend launch; per_head: separate calls, local heads on "
+                         "a side stream; union: each kept row read once per KV head for all "
+                         "its query heads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -109,7 +112,7 @@ def main():
 
     # Local heads of a layer run on a side stream, overlapping the retrieval
     # chain of the same layer; each layer joins both before the next starts.
-    side = (None if args.no_side_stream or args.sparse_mode == "fused"
+    side = (None if args.no_side_stream or args.sparse_mode in ("fused", "scan_local")
             else torch.cuda.Stream(device=dev))
 
     def step():
@@ -194,7 +197,14 @@ def main():
     # rtp_topp_select is the hist kernel then the emit kernel, back to back;
     # the emit kernel's duration is the difference.
     us_emit = us["rtp_topp_select"] - us["rtp_topp_hist"]
-    if sl.mode == "fused":
+    if sl.mode == "scan_local":
+        us["rtp_scan_local"] = time_call(lambda: [rtp.rtp_scan_local(
+            qr_all[l], kr_all[l], scores_l[l], q_all[l], K_all[l], V_all[l], N, H_r, Hq - H_r,
+            cfg.n_sink, cfg.window, scale, out_all[l], sl.ws_local) for l in range(L)])
+        us["rtp_decode_attend"] = time_call(lambda: [rtp.rtp_decode_attend(
+            q_all[l], K_all[l], V_all[l], idx_l[l], count_l[l], N, 0, H_r, 0, 0, 1, scale,
+            out_all[l], sl.ws_attend) for l in range(L)])
+    elif sl.mode == "fused":
         us["rtp_decode_attend"] = time_call(lambda: [rtp.rtp_decode_attend(
             q_all[l], K_all[l], V_all[l], idx_l[l], count_l[l], N, 0, H_r, Hq - H_r,
             cfg.n_sink, cfg.window, scale, out_all[l], sl.ws_attend) for l in range(L)])
@@ -206,7 +216,7 @@ def main():
         us["rtp_sparse_decode"] = time_call(lambda: [rtp.rtp_sparse_decode(
             q_all[l], K_all[l], V_all[l], idx_l[l], count_l[l], 0, scale, out_all[l],
             sl.ws_sparse) for l in range(L)])
-    if sl.mode != "fused":
+    if sl.mode not in ("fused", "scan_local"):
         us["rtp_local_decode"] = time_call(lambda: [rtp.rtp_local_decode(
             q_all[l], K_all[l], V_all[l], N, H_r, Hq - H_r, cfg.n_sink, cfg.window, scale,
             out_all[l], sl.ws_local) for l in range(L)])
@@ -256,7 +266,8 @@ def main():
     #           sets (re-reads by several heads earn no credit) + the 4-B
     #           indices read;
     #   local   512 B per sink/window row per local KV head;
-    #   attend  sparse + local, one launch.
+    #   attend  sparse (+ local in mode "fused"), one launch;
+    #   scan + local, one launch (mode "scan_local").
     csrc = os.path.join(ROOT, "sparse_long_context_indexer_amd", "csrc")
     sel_total = float(np.mean([sum(x) for x in n_sel]))
     sparse_bytes = float(np.mean(union)) * 2 * d * 2 + sel_total * 4
@@ -266,14 +277,22 @@ def main():
         "rtp_topp_hist": ("sel_hist_kernel", B * H_r * N * 4, "select.hip"),
         "rtp_index_scores": ("index_scores_kernel<8>", B * G_r * N * (cfg.r * 4 + cfg.G * 4),
                              "scan.hip"),
-        "rtp_decode_attend": ("attend_kernel", sparse_bytes + window_bytes, "attend.hip"),
+        "rtp_decode_attend": ("attend_kernel",
+                              sparse_bytes + (window_bytes if sl.mode == "fused" else 0),
+                              "attend.hip"),
+        "rtp_scan_local": ("scan_local_kernel<8>",
+                           B * G_r * N * (cfg.r * 4 + cfg.G * 4) + window_bytes, "attend.hip"),
         "rtp_sparse_decode": ("attend_kernel", sparse_bytes, "attend.hip"),
         "rtp_sparse_decode_union": ("union_attn_kernel",
                                     float(np.mean(union)) * 2 * d * 2 + B * H_r * ((N + 31) // 32) * 4,
                                     "attend.hip"),
         "rtp_local_decode": ("attend_kernel", window_bytes, "attend.hip"),
     }
-    call = max((c for c in cands if c in us), key=lambda c: us[c])
+    # In mode "scan_local" rtp_index_scores is timed for reference only: the
+    # step runs the scan inside rtp_scan_local.
+    in_step = [c for c in cands if c in us
+               and not (sl.mode == "scan_local" and c == "rtp_index_scores")]
+    call = max(in_step, key=lambda c: us[c])
     kname, kbytes, ksrc = cands[call]
     roof = {"kernel": kname, "bound": "hbm",
             "achieved": kbytes / (us[call] * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}

@@ -229,6 +229,31 @@ rtp_status rtp_decode_attend(const rtp_bf16 *q, const rtp_bf16 *K,
                              void *stream);
 
 /*
+ * rtp_scan_local -- rtp_index_scores for the retrieval heads and
+ * rtp_local_decode for the query heads local_head_begin ..
+ * local_head_begin + n_local_heads - 1, in one launch: the scan of the
+ * gist.science summary, method section 2, and the local heads of method
+ * section 1, which read disjoint inputs and write disjoint outputs.  The
+ * results are those of the two calls.  Both sides use the same batch size B
+ * and token count N (scores [B][Hq_r][N], rows 0 .. N-1 of K and V).
+ *
+ *   q_r, k_r, scores, Hq_r, Hkv_r, kr_cap, r   as in rtp_index_scores
+ *   q, K, V, out, Hq, Hkv, kv_cap, d, scale,
+ *   n_sink, window                             as in rtp_local_decode
+ *   workspace  >= rtp_workspace_size(RTP_WS_LOCAL_DECODE, B, n_local_heads, N)
+ * Errors: those of either call, checked before anything is enqueued.
+ */
+rtp_status rtp_scan_local(const float *q_r, const float *k_r, float *scores,
+                          int32_t Hq_r, int32_t Hkv_r, int64_t kr_cap, int32_t r,
+                          const rtp_bf16 *q, const rtp_bf16 *K,
+                          const rtp_bf16 *V, int32_t B, int32_t Hq,
+                          int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,
+                          int32_t local_head_begin, int32_t n_local_heads,
+                          int32_t n_sink, int32_t window, float scale,
+                          float *out, void *workspace, size_t ws_bytes,
+                          void *stream);
+
+/*
  * rtp_workspace_size -- bytes of workspace a call needs (host only, pure).
  *   which  RTP_WS_TOPP_SELECT:   H = score rows per batch row
  *          RTP_WS_SPARSE_DECODE: H = n_q_heads

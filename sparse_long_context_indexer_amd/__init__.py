@@ -27,7 +27,7 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPP
 # Every symbol include/rtp.h declares.
 SYMBOLS = ("rtp_index_scores", "rtp_topp_select", "rtp_topp_hist", "rtp_sparse_decode",
            "rtp_sparse_decode_union", "rtp_local_decode", "rtp_decode_attend",
-           "rtp_workspace_size", "rtp_status_string", "rtp_last_hip_error")
+           "rtp_scan_local", "rtp_workspace_size", "rtp_status_string", "rtp_last_hip_error")
 
 
 class RtpError(RuntimeError):
@@ -66,12 +66,14 @@ def lib() -> ctypes.CDLL:
                                        I32, I32, F32, P, P, SZ, P]
         L.rtp_decode_attend.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32, I32, I32,
                                         I32, I32, I32, I32, F32, P, P, SZ, P]
+        L.rtp_scan_local.argtypes = [P, P, P, I32, I32, I64, I32, P, P, P, I32, I32, I32, I32,
+                                     I64, I32, I32, I32, I32, I32, F32, P, P, SZ, P]
         L.rtp_workspace_size.argtypes = [I32, I32, I32, I32, ctypes.POINTER(SZ)]
         L.rtp_status_string.argtypes = [I32]
         L.rtp_status_string.restype = ctypes.c_char_p
         L.rtp_last_hip_error.argtypes = []
         L.rtp_last_hip_error.restype = I32
-        for name in SYMBOLS[:8]:
+        for name in SYMBOLS[:9]:
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -223,6 +225,28 @@ def rtp_decode_attend(q, K, V, idx, count, N, sparse_head_begin, local_head_begi
         n_sink, window, float(scale), _dev(out, torch.float32, "out", 3),
         _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(), _stream(q, stream)),
         "rtp_decode_attend")
+
+
+def rtp_scan_local(q_r, k_r, scores, q, K, V, N, local_head_begin, n_local_heads, n_sink,
+                   window, scale, out, workspace, stream=None) -> None:
+    """rtp_index_scores(q_r, k_r, scores) and rtp_local_decode for the heads
+    [local_head_begin, + n_local_heads), one launch; scores f32 [B][Hq_r][N];
+    workspace uint8 [>= workspace_size(RTP_WS_LOCAL_DECODE, B, n_local_heads, N)]."""
+    import torch
+    B, Hq_r, r = q_r.shape
+    _, Hkv_r, kr_cap, _ = k_r.shape
+    _, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    if tuple(scores.shape) != (B, Hq_r, N) or q.shape[0] != B:
+        raise ValueError(f"scores must be [B][Hq_r][N] = {(B, Hq_r, N)} and q [B][Hq][d], "
+                         f"got {tuple(scores.shape)} and {tuple(q.shape)}")
+    _check(lib().rtp_scan_local(
+        _dev(q_r, torch.float32, "q_r", 3), _dev(k_r, torch.float32, "k_r", 4),
+        _dev(scores, torch.float32, "scores", 3), Hq_r, Hkv_r, kr_cap, r,
+        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4), B, Hq, Hkv, N, cap, d,
+        local_head_begin, n_local_heads, n_sink, window, float(scale),
+        _dev(out, torch.float32, "out", 3), _dev(workspace, torch.uint8, "workspace", 1),
+        workspace.numel(), _stream(q, stream)), "rtp_scan_local")
 
 
 def rtp_local_decode(q, K, V, N, q_head_begin, n_q_heads, n_sink, window, scale, out,

@@ -218,4 +218,34 @@ rtp_status rtp_decode_attend(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf1
                                               scale, out, workspace, as_stream(stream)));
 }
 
+rtp_status rtp_scan_local(const float *q_r, const float *k_r, float *scores, int32_t Hq_r,
+                          int32_t Hkv_r, int64_t kr_cap, int32_t r, const rtp_bf16 *q,
+                          const rtp_bf16 *K, const rtp_bf16 *V, int32_t B, int32_t Hq,
+                          int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,
+                          int32_t local_head_begin, int32_t n_local_heads, int32_t n_sink,
+                          int32_t window, float scale, float *out, void *workspace,
+                          size_t ws_bytes, void *stream)
+{
+    if (!q_r || !k_r || !scores) return RTP_ERR_NULL;
+    rtp_status st = check_attention_common(q, K, V, out, workspace, B, Hq, Hkv, N, kv_cap, d,
+                                           local_head_begin, n_local_heads, scale);
+    if (st != RTP_OK) return st;
+    if (r != 16) return RTP_ERR_UNSUPPORTED;
+    if (Hq_r < 1 || Hkv_r < 1 || Hq_r % Hkv_r != 0 || kr_cap < N) return RTP_ERR_SHAPE;
+    if (n_sink < 0 || window < 1) return RTP_ERR_VALUE;
+    const int64_t G = Hq / Hkv;
+    const int64_t groups =
+        ((int64_t)local_head_begin + n_local_heads - 1) / G - local_head_begin / G + 1;
+    if (groups * ((G + 7) / 8) > kMaxGridY) return RTP_ERR_SHAPE;
+    if (rtp::scan_local_blocks(B, Hq_r, Hkv_r, Hq, Hkv, N, local_head_begin, n_local_heads) >
+        INT32_MAX)
+        return RTP_ERR_SHAPE;
+    if (!aligned(q_r, 16) || !aligned(k_r, 16) || !aligned(scores, 4)) return RTP_ERR_ALIGN;
+    if (ws_bytes < rtp::local_ws_bytes(B, n_local_heads, N)) return RTP_ERR_WORKSPACE;
+    return from_hip(rtp::launch_scan_local(q_r, k_r, scores, Hq_r, Hkv_r, kr_cap, q, K, V, B, Hq,
+                                           Hkv, N, kv_cap, local_head_begin, n_local_heads,
+                                           n_sink, window, scale, out, workspace,
+                                           as_stream(stream)));
+}
+
 }  // extern "C"

@@ -16,10 +16,12 @@
 // forms 8 partial dot products; a butterfly over the 16 lanes of a row
 // reduces all 8 in 8 exchanges (each step halves the heads a lane carries).
 #include <float.h>
+#include <atomic>
 #include <math.h>
 
 #include "rtp_device.h"
 #include "rtp_launch.h"
+#include "scan_tile.h"
 
 namespace rtp {
 
@@ -511,8 +513,11 @@ __device__ void merge_heads(const float *first, int64_t head_stride, int n, int 
 // the two-level merge of the splits, for all nh heads at once (counters
 // indexed by r0).  The last block of a slice merges the slice; the last
 // slice merger writes the output rows dst (128 floats apart).
+// `merge` has merge_heads' signature (first, head_stride, n, nh, dst_part,
+// dst_stride, dst_out).
+template <class Merge>
 __device__ void merge_group_splits(int nh, int s, int S, int64_t r0, const GroupWs &W,
-                                   float *dst, int *last)
+                                   float *dst, int *last, Merge merge)
 {
     const int slice = s / W.slice;
     const int slices = (S + W.slice - 1) / W.slice;
@@ -520,14 +525,14 @@ __device__ void merge_group_splits(int nh, int s, int S, int64_t r0, const Group
     if (!arrive_last(W.slice_ctr + r0 * W.max_slices + slice, in_slice, last)) return;
     const float *first = W.part + (r0 * S + slice * W.slice) * kPart;
     if (slices == 1) {
-        merge_heads(first, (int64_t)S * kPart, in_slice, nh, nullptr, 0, dst);
+        merge(first, (int64_t)S * kPart, in_slice, nh, nullptr, 0, dst);
         return;
     }
     float *sp = W.super + r0 * W.max_slices * kPart;
-    merge_heads(first, (int64_t)S * kPart, in_slice, nh, sp + (int64_t)slice * kPart,
-                (int64_t)W.max_slices * kPart, nullptr);
+    merge(first, (int64_t)S * kPart, in_slice, nh, sp + (int64_t)slice * kPart,
+          (int64_t)W.max_slices * kPart, nullptr);
     if (!arrive_last(W.group_ctr + r0, slices, last)) return;
-    merge_heads(sp, (int64_t)W.max_slices * kPart, slices, nh, nullptr, 0, dst);
+    merge(sp, (int64_t)W.max_slices * kPart, slices, nh, nullptr, 0, dst);
 }
 
 // Per-lane state of the 8-head online softmax.  A row is spread over 16
@@ -702,7 +707,9 @@ __device__ void heads8_finish(Heads8 &st, Heads8Shared &sh, int nh, int s, int S
         }
     }
 
-    merge_group_splits(nh, s, S, r0, W, dst, &sh.last);
+    merge_group_splits(nh, s, S, r0, W, dst, &sh.last,
+                       [](const float *first, int64_t hs, int n, int nh_, float *dp, int64_t ds,
+                          float *dout) { merge_heads(first, hs, n, nh_, dp, ds, dout); });
 }
 
 // Heads of KV head g handled by block row y: chunk ck of up to 8 query heads
@@ -761,6 +768,13 @@ constexpr int kLocSlots = kAttThreads / 32;         // rows in progress per bloc
 
 constexpr int kLocTile = 64;  // rows staged in LDS at a time
 
+// Factors of one merge of split partials: per head, the merged max and sum
+// and each partial's weight.
+struct HeadMergeShared {
+    float f[8][kLocalSlice];
+    float M[8], L[8];
+};
+
 struct LocalShared {
     union {
         struct {  // a tile of K and V rows (16 pieces of 16 B per row)
@@ -770,9 +784,81 @@ struct LocalShared {
             float m[kLocSlots][8], l[kLocSlots][8];
             float o[kLocSlots][8][128];
         } mg;
+        HeadMergeShared hm;
     };
     int last;
 };
+
+__device__ __forceinline__ float max16(float v)
+{
+    v = fmaxf(v, dpp<kDppQuadXor1>(v, v));
+    v = fmaxf(v, dpp<kDppQuadXor2>(v, v));
+    v = fmaxf(v, dpp<kDppRowHalfMirror>(v, v));
+    v = fmaxf(v, dpp<kDppRowMirror>(v, v));
+    return v;
+}
+
+// Merges n <= kLocalSlice split partials for each of nh <= 8 heads with one
+// round of loads, all in flight together: thread t owns output column
+// t % 128 of heads t / 128 + 2j (j < 4), so each load instruction of a wave
+// reads 256 contiguous bytes of one partial; threads 0..127 take the max
+// and sum of partial t % 16 of head t / 16 (one head per 16-lane row, so
+// the per-head max and sum are row reductions), and the weights go through
+// LDS.  Head hh's partials start at first + hh * head_stride (floats),
+// kPart apart.  Writes merged partials (dst_part, dst_stride apart) or
+// output rows (dst_out, 128 apart).
+__device__ void merge_heads16(const float *first, int64_t head_stride, int n, int nh,
+                              float *dst_part, int64_t dst_stride, float *dst_out,
+                              HeadMergeShared &S)
+{
+    constexpr int kG = kAttThreads / 128;  // thread groups, one head each at a time
+    constexpr int kH = 8 / kG;             // heads per thread
+    static_assert(8 * kLocalSlice <= kAttThreads, "one thread per (head, partial)");
+    const int tid = threadIdx.x, c = tid & 127, g = tid >> 7;
+    float ov[kH][kLocalSlice];
+#pragma unroll
+    for (int j = 0; j < kH; ++j) {
+        const int hh = g + j * kG;
+        const float *ph = first + hh * head_stride + 4 + c;
+#pragma unroll
+        for (int k = 0; k < kLocalSlice; ++k)
+            ov[j][k] = hh < nh && k < n ? ld_agent(ph + k * kPart) : 0.0f;
+    }
+    if (tid < 8 * kLocalSlice) {
+        const int hh = tid / kLocalSlice, k = tid % kLocalSlice;
+        const bool ok = hh < nh && k < n;
+        const float *pk = first + hh * head_stride + k * kPart;
+        const float m = ok ? ld_agent(pk) : -INFINITY;
+        const float l = ok ? ld_agent(pk + 1) : 0.0f;
+        const float M = max16(m);
+        const float f = ok ? rescale(m, M) : 0.0f;
+        const float L = sum16(l * f);
+        S.f[hh][k] = f;
+        if (k == 0) {
+            S.M[hh] = M;
+            S.L[hh] = L;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kH; ++j) {
+        const int hh = g + j * kG;
+        if (hh >= nh) continue;
+        float o = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kLocalSlice; ++k) o = fmaf(ov[j][k], S.f[hh][k], o);
+        const float L = S.L[hh];
+        if (dst_out) dst_out[hh * 128 + c] = o * (L > 0.0f ? 1.0f / L : 0.0f);
+        if (dst_part) {
+            float *pd = dst_part + hh * dst_stride;
+            st_agent(pd + 4 + c, o);
+            if (c == 0) {
+                st_agent(pd, S.M[hh]);
+                st_agent(pd + 1, L);
+            }
+        }
+    }
+}
 
 struct Heads4 {
     float qf[4][8];  // q * scale * log2(e) of this group's heads, this lane's 8 dims
@@ -997,7 +1083,11 @@ __device__ void local_block(const uint16_t *__restrict__ q, const uint16_t *__re
         }
     }
     merge_group_splits(hc.nh, s, A.S, r0, A.W, out + ((int64_t)b * Hq + hc.h_lo) * 128,
-                       &sh.last);
+                       &sh.last,
+                       [&sh](const float *first, int64_t hs, int n, int nh, float *dp,
+                             int64_t ds, float *dout) {
+                           merge_heads16(first, hs, n, nh, dp, ds, dout, sh.hm);
+                       });
 }
 
 static dim3 group_grid(int S, int B, int Hq, int Hkv, int q_head_begin, int n_q_heads,
@@ -1126,6 +1216,114 @@ hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *K, const uint
         q, K, V, N, kv_cap, Hq, Hkv, scale,
         local_args(B, Hq, Hkv, N, local_head_begin, n_local_heads, n_sink, window, base + sp),
         sparse_args(idx, count, B, sparse_head_begin, n_sparse_heads, base), out, stream);
+}
+
+// ------------------------------------------------- scan + local heads
+//
+// The indexer scan of a layer's retrieval heads and the attention of its
+// local heads in one launch (the head-role split of the gist.science summary,
+// method section 1, and the scan of method section 2).  Neither reads what
+// the other writes.  Blocks [0, L.blocks) are local blocks, dispatched first
+// because their split merges form a chain of dependent steps; the rest are
+// scan blocks, whose streaming read of k_r runs meanwhile.  The scan blocks
+// are as many as fit beside the local blocks in one wave of the device
+// (kFusedPerCU blocks per compute unit), and each takes every scan_blocks-th
+// tile, so no scan tile waits for a second dispatch round.
+
+constexpr int kFusedTPT = 1;    // tokens per thread of a scan tile in this launch
+constexpr int kFusedPerCU = 4;  // resident blocks per compute unit (128 VGPRs, 256 threads)
+static_assert(kScanThreads == kAttThreads, "scan tiles and local blocks share the block size");
+
+struct ScanArgs {
+    const float *q_r, *k_r;
+    float *scores;
+    int64_t kr_cap;
+    int Hq_r, Hkv_r;
+    ScanGeom g;
+    int scan_blocks;  // blocks that run scan tiles
+};
+
+template <int G>
+__global__ __launch_bounds__(kAttThreads, 4) void scan_local_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, int N, int64_t kv_cap, int Hq, int Hkv, float qscale,
+    LocalArgs L, ScanArgs C, float *__restrict__ out)
+{
+    __shared__ LocalShared sh;
+    const int i = blockIdx.x;
+    if (i < L.blocks) {
+        local_block(q, K, V, N, kv_cap, Hq, Hkv, qscale, L, out, i, sh);
+        return;
+    }
+    const int tiles = C.g.gx * C.g.gy;
+    for (int j = i - L.blocks; j < tiles; j += C.scan_blocks)
+        scan_tile<G, kFusedTPT>(C.q_r, C.k_r, C.scores, N, C.kr_cap, C.Hq_r, C.Hkv_r, C.g.group,
+                                C.g.head_chunks, j % C.g.gx, j / C.g.gx);
+}
+
+hipError_t device_cus(int *cus)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];  // zero: not queried yet
+    int dev = 0;
+    RTP_TRY(hipGetDevice(&dev));
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    int c = cached ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (c < 1) {
+        RTP_TRY(hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev));
+        c = c < 1 ? 1 : c;
+        if (cached) cache[dev].store(c, std::memory_order_relaxed);
+    }
+    *cus = c;
+    return hipSuccess;
+}
+
+static int scan_chunk_heads(int Hq_r, int Hkv_r)
+{
+    const int group = Hq_r / Hkv_r;
+    return group == 1 ? 1 : group == 2 ? 2 : group <= 4 ? 4 : 8;
+}
+
+int64_t scan_local_blocks(int B, int Hq_r, int Hkv_r, int Hq, int Hkv, int N,
+                          int local_head_begin, int n_local_heads)
+{
+    const int G = scan_chunk_heads(Hq_r, Hkv_r);
+    const int64_t group = Hq_r / Hkv_r;
+    const int64_t tile = (int64_t)kScanThreads * kFusedTPT;
+    const int64_t scan = ((int64_t)N + tile - 1) / tile * B * Hkv_r * ((group + G - 1) / G);
+    const int64_t Gq = Hq / Hkv;
+    const int64_t groups =
+        ((int64_t)local_head_begin + n_local_heads - 1) / Gq - local_head_begin / Gq + 1;
+    const int64_t local = (int64_t)B * groups * ((Gq + 7) / 8) * local_splits(N);
+    return scan + local;
+}
+
+hipError_t launch_scan_local(const float *q_r, const float *k_r, float *scores, int Hq_r,
+                             int Hkv_r, int64_t kr_cap, const uint16_t *q, const uint16_t *K,
+                             const uint16_t *V, int B, int Hq, int Hkv, int N, int64_t kv_cap,
+                             int local_head_begin, int n_local_heads, int n_sink, int window,
+                             float scale, float *out, void *ws, hipStream_t stream)
+{
+    const LocalArgs L = local_args(B, Hq, Hkv, N, local_head_begin, n_local_heads, n_sink,
+                                   window, ws);
+    int cus = 0;
+    RTP_TRY(device_cus(&cus));
+    auto go = [&](auto kern, int G) {
+        ScanArgs C{q_r, k_r, scores, kr_cap, Hq_r, Hkv_r,
+                   scan_geom(B, Hq_r, Hkv_r, N, G, kFusedTPT), 0};
+        const int tiles = C.g.gx * C.g.gy;
+        const int room = kFusedPerCU * cus - L.blocks;  // slots left by the local blocks
+        C.scan_blocks = room >= kFusedPerCU * cus / 2 ? min(tiles, room) : tiles;
+        const unsigned blocks = (unsigned)(L.blocks + C.scan_blocks);
+        return launch(kern, dim3(blocks), dim3(kAttThreads), 0, stream, q, K, V, N, kv_cap, Hq,
+                      Hkv, scale * kLog2e, L, C, out);
+    };
+    switch (scan_chunk_heads(Hq_r, Hkv_r)) {
+    case 1: return go(scan_local_kernel<1>, 1);
+    case 2: return go(scan_local_kernel<2>, 2);
+    case 4: return go(scan_local_kernel<4>, 4);
+    default: return go(scan_local_kernel<8>, 8);
+    }
 }
 
 // ------------------------------------------------------------- union

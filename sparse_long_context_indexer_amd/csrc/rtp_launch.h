@@ -65,7 +65,21 @@ hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K,
                                int n_sink, int window, float scale, float *out,
                                void *ws, hipStream_t stream);
 
+// Indexer scan and local heads in one launch (the local workspace as for
+// launch_local_decode).  scan_local_blocks bounds the launch's block count
+// for any n_sink / window.
+int64_t scan_local_blocks(int B, int Hq_r, int Hkv_r, int Hq, int Hkv, int N,
+                          int local_head_begin, int n_local_heads);
+hipError_t launch_scan_local(const float *q_r, const float *k_r, float *scores, int Hq_r,
+                             int Hkv_r, int64_t kr_cap, const uint16_t *q, const uint16_t *K,
+                             const uint16_t *V, int B, int Hq, int Hkv, int N, int64_t kv_cap,
+                             int local_head_begin, int n_local_heads, int n_sink, int window,
+                             float scale, float *out, void *ws, hipStream_t stream);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Compute units of the current device (queried once per device).
+hipError_t device_cus(int *cus);
 
 
 template <typename... KArgs>

@@ -12,21 +12,23 @@ import torch
 
 from . import (RTP_WS_DECODE_ATTEND, RTP_WS_LOCAL_DECODE, RTP_WS_SPARSE_DECODE,
                RTP_WS_SPARSE_UNION, RTP_WS_TOPP_SELECT, keep_words, rtp_decode_attend,
-               rtp_index_scores, rtp_local_decode, rtp_sparse_decode, rtp_sparse_decode_union,
-               rtp_topp_select, workspace_size)
+               rtp_index_scores, rtp_local_decode, rtp_scan_local, rtp_sparse_decode,
+               rtp_sparse_decode_union, rtp_topp_select, workspace_size)
 
 
 class DecodeLayer:
-    """mode "fused": after the scan and the selection, one rtp_decode_attend
-    launch runs the sparse heads (per-head index lists) and the local heads
-    together; mode "per_head": rtp_sparse_decode and rtp_local_decode as
-    separate calls; mode "union": the selector also writes keep bitmaps and
-    the sparse heads run rtp_sparse_decode_union (each kept row read once per
-    KV head)."""
+    """mode "fused": the scan, the selection, then one rtp_decode_attend
+    launch for the sparse heads (per-head index lists) and the local heads
+    together; mode "scan_local": one rtp_scan_local launch runs the indexer
+    scan and the local heads, then the selection, then rtp_decode_attend for
+    the sparse heads alone; mode "per_head": rtp_sparse_decode and rtp_local_decode
+    as separate calls; mode "union": the selector also writes keep bitmaps
+    and the sparse heads run rtp_sparse_decode_union (each kept row read once
+    per KV head)."""
 
     def __init__(self, B: int, Hq: int, Hkv: int, N: int, H_r: int, n_sink: int,
                  window: int, device, d: int = 128, mode: str = "fused"):
-        if mode not in ("fused", "union", "per_head"):
+        if mode not in ("fused", "scan_local", "union", "per_head"):
             raise ValueError(f"unknown mode {mode!r}")
         self.B, self.Hq, self.Hkv, self.N, self.H_r = B, Hq, Hkv, N, H_r
         self.n_sink, self.window, self.d, self.mode = n_sink, window, d, mode
@@ -47,7 +49,7 @@ class DecodeLayer:
             else:
                 self.ws_sparse = torch.empty(workspace_size(RTP_WS_SPARSE_DECODE, B, H_r, N),
                                              dtype=torch.uint8, device=dev)
-            if mode == "fused":
+            if mode in ("fused", "scan_local"):
                 self.ws_attend = torch.empty(workspace_size(RTP_WS_DECODE_ATTEND, B, Hq, N),
                                              dtype=torch.uint8, device=dev)
         if self.H_l > 0:
@@ -75,11 +77,19 @@ class DecodeLayer:
                           self.n_sink, self.window, scale, out, self.ws_attend, stream=stream)
 
     def __call__(self, q_r, k_r, q, K, V, p: float, scale: float, out, side_stream=None):
-        """Runs the layer on the current stream.  In mode "fused" the local
-        heads share the sparse heads' launch and side_stream is not used.
-        Otherwise, with side_stream, the local heads run there concurrently
-        with the retrieval chain (the two share no buffer); the current
-        stream waits for them before returning."""
+        """Runs the layer on the current stream.  In modes "fused" and
+        "scan_local" the local heads share a launch with the sparse heads or
+        with the scan, and side_stream is not used.  Otherwise, with
+        side_stream, the local heads run there concurrently with the
+        retrieval chain (the two share no buffer); the current stream waits
+        for them before returning."""
+        if self.mode == "scan_local" and self.H_r > 0 and self.H_l > 0:
+            rtp_scan_local(q_r, k_r, self.scores, q, K, V, self.N, self.H_r, self.H_l,
+                           self.n_sink, self.window, scale, out, self.ws_local)
+            rtp_topp_select(self.scores, p, self.idx, self.count, self.ws_sel)
+            rtp_decode_attend(q, K, V, self.idx, self.count, self.N, 0, self.H_r, 0, 0, 1,
+                              scale, out, self.ws_attend)
+            return
         if self.mode == "fused" and self.H_r > 0 and self.H_l > 0:
             rtp_index_scores(q_r, k_r, self.scores)
             rtp_topp_select(self.scores, p, self.idx, self.count, self.ws_sel)

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -202,6 +202,46 @@ def test_decode_attend_validation(lib):
     # are not checked.  Every call here fails before any launch.
     assert call(ns=0, idx=None, count=None, wsb=0) == 6
     assert call(nl=0, sink=-1, win=0, wsb=0) == 6
+
+
+def test_scan_local_validation(lib):
+    f = lib.rtp_scan_local
+    ws = rtp.workspace_size(rtp.RTP_WS_LOCAL_DECODE, 1, 24, 1000)
+    pos = {"q_r": 0, "k_r": 1, "scores": 2, "Hq_r": 3, "Hkv_r": 4, "kr_cap": 5, "r": 6, "q": 7,
+           "B": 10, "Hq": 11, "Hkv": 12, "N": 13, "kv_cap": 14, "d": 15, "lb": 16, "nl": 17,
+           "sink": 18, "win": 19, "scale": 20, "out": 21, "ws": 22, "wsb": 23}
+    args = [A, A, A, 8, 1, 1000, 16, A, A, A, 1, 32, 4, 1000, 1000, 128, 8, 24, 4, 4096, 0.088,
+            A, A, ws, None]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    # Every call below breaks one rule, so none reaches a launch.
+    for name in ("q_r", "k_r", "scores", "q", "out", "ws"):
+        assert call(**{name: None}) == 1, name
+    assert call(r=8) == 3
+    assert call(d=64) == 3
+    assert call(Hq_r=7, Hkv_r=2) == 2           # not a multiple
+    assert call(Hkv_r=0) == 2
+    assert call(kr_cap=999) == 2                # k_r holds fewer than N rows
+    assert call(kv_cap=999) == 2
+    assert call(N=0) == 2
+    assert call(B=0) == 2
+    assert call(nl=0) == 2                      # the local set may not be empty
+    assert call(lb=9) == 2                      # 9 + 24 > 32
+    assert call(sink=-1) == 4
+    assert call(win=0) == 4
+    assert call(scale=float("nan")) == 4
+    assert call(q_r=A + 4) == 5
+    assert call(k_r=A + 8) == 5
+    assert call(scores=A + 2) == 5
+    assert call(q=A + 2) == 5
+    assert call(ws=A + 16) == 5
+    assert call(wsb=0) == 6
+    assert call(wsb=ws - 1) == 6                # sized for exactly these 24 heads
 
 
 def test_topp_hist_validation(lib):

@@ -22,7 +22,7 @@ def _print(*a):
 
 # ------------------------------------------------------------ full configs
 
-@pytest.mark.parametrize("mode", ["fused", "union", "per_head"])
+@pytest.mark.parametrize("mode", ["fused", "scan_local", "union", "per_head"])
 @pytest.mark.parametrize("ci", [0, 1, 3])
 def test_config_layer(ci, mode):
     cfg = synth.CONFIGS[ci]
@@ -51,7 +51,8 @@ def test_config4_sampled_layers():
     # Full-size layers of the 48-layer 1M-context stack (same kernels and
     # launch shapes as the benchmark), judged in full for every head.
     cfg = synth.CONFIGS[4]
-    for layer, mode in ((0, "fused"), (0, "union"), (47, "per_head"), (47, "fused")):
+    for layer, mode in ((0, "fused"), (0, "union"), (47, "per_head"), (47, "fused"),
+                        (21, "scan_local")):
         _print(f"config 4 layer {layer} ({mode})")
         L = load_layer(cfg, layer, keep_host_kv=False)
         rep = {}
@@ -294,9 +295,54 @@ def test_decode_attend_head_sets(sets):
         assert ok, (sets, h, err, rel)
 
 
+@pytest.mark.parametrize("N,Hq_r,Hkv_r,Hq,Hkv,lb,nl,n_sink,window", [
+    (1, 8, 1, 32, 4, 8, 24, 4, 4096),        # one token
+    (4101, 8, 1, 32, 4, 8, 24, 4, 4096),     # window + sinks + 1
+    (9000, 12, 1, 16, 4, 5, 9, 0, 333),      # 12 heads per KV group; cut KV groups
+    (70001, 3, 3, 8, 2, 1, 7, 17, 20000),    # 1 head per group, ragged tiles
+    (2049, 16, 2, 8, 8, 0, 8, 2, 1)])        # 8 heads per group; window of one row
+def test_scan_local_shapes(N, Hq_r, Hkv_r, Hq, Hkv, lb, nl, n_sink, window):
+    # The scan and the local heads in one launch: scores bit-exact, local
+    # outputs against the oracle's attention, heads outside the range untouched.
+    B = 2
+    cfg = synth.CONFIGS[1].with_(N=N, B=B, Hq=Hq, Hkv=Hkv, H_r=0, needles_per_head=0,
+                                 n_sink=n_sink, window=window)
+    L = load_layer(cfg)
+    k = synth.key(91, synth.KR, N, B, Hq_r)
+    q_r = synth.normal_f32(k, 0, B * Hq_r * 16).reshape(B, Hq_r, 16) * 3
+    cap = N + 5
+    k_r = synth.normal_f32(k, 10**9, B * Hkv_r * cap * 16).reshape(B, Hkv_r, cap, 16)
+    k_r[..., ::5, 7] = 0.0
+    s = torch.full((B, Hq_r, N), float("nan"), device=dev())
+    out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device=dev())
+    ws = torch.empty(rtp.workspace_size(rtp.RTP_WS_LOCAL_DECODE, B, nl, N), dtype=torch.uint8,
+                     device=dev())
+    ws.fill_(0xA5)
+    rtp.rtp_scan_local(to_dev(q_r.astype(np.float32)), to_dev(k_r), s, L.d["q"], L.d["K"],
+                       L.d["V"], N, lb, nl, n_sink, window, cfg.scale, out, ws)
+    got = s.cpu().numpy()
+    G = Hq_r // Hkv_r
+    for b in range(B):
+        for h in range(Hq_r):
+            ref = oracle.scores(q_r[b, h].astype(np.float32), k_r[b, h // G, :N])
+            assert np.array_equal(got[b, h].view(np.uint32), ref.view(np.uint32)), (b, h)
+    o = out.cpu().numpy()
+    rows = oracle.local_rows(N, n_sink, window)
+    Gq = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            if lb <= h < lb + nl:
+                ref = oracle.attention(L.q[b, h], L.K[b, h // Gq, rows], L.V[b, h // Gq, rows],
+                                       cfg.scale)
+                ok, err, rel = judge_out(o[b, h], ref)
+                assert ok, (b, h, err, rel)
+            else:
+                assert np.all(np.isnan(o[b, h])), (b, h)
+
+
 # ------------------------------------------------------------ workspaces
 
-@pytest.mark.parametrize("mode", ["fused", "per_head", "union"])
+@pytest.mark.parametrize("mode", ["fused", "scan_local", "per_head", "union"])
 def test_workspace_garbage_and_reuse(mode):
     # Workspaces start as arbitrary bytes (no initialisation is required),
     # are reused by the next call, and are then reused for a smaller call
@@ -311,7 +357,7 @@ def test_workspace_garbage_and_reuse(mode):
         step.keep_bits.copy_(torch.randint(-2**31, 2**31 - 1, step.keep_bits.shape,
                                            dtype=torch.int32, generator=g))
     wss = [step.ws_sel, step.ws_sparse, step.ws_local]
-    if mode == "fused":
+    if mode in ("fused", "scan_local"):
         wss.append(step.ws_attend)
     for ws in wss:
         ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=g))
@@ -325,7 +371,7 @@ def test_workspace_garbage_and_reuse(mode):
     s2 = DecodeLayer(1, cfg.Hq, cfg.Hkv, 20000, cfg.H_r, cfg.n_sink, cfg.window, dev(),
                      mode=mode)
     s2.ws_sparse, s2.ws_local, s2.ws_sel = step.ws_sparse, step.ws_local, step.ws_sel
-    if mode == "fused":
+    if mode in ("fused", "scan_local"):
         s2.ws_attend = step.ws_attend
     for ws in wss[1:]:
         ws[ws.numel() // 3:].fill_(0xFF)
