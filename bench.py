@@ -194,9 +194,14 @@ def main():
         "rtp_topp_hist": time_call(lambda: [rtp.rtp_topp_hist(scores_l[l], sl.ws_sel)
                                             for l in range(L)]),
     }
-    # rtp_topp_select is the hist kernel then the emit kernel, back to back;
+    # rtp_topp_select runs both passes in one launch (sel_fused_kernel) when
+    # its histogram and emit block rows fit one grid (2 * B * H_r <= 65535);
+    # rtp_topp_hist, the histogram pass alone, is then timed for reference
+    # only.  Otherwise it launches the hist kernel then the emit kernel, and
     # the emit kernel's duration is the difference.
-    us_emit = us["rtp_topp_select"] - us["rtp_topp_hist"]
+    fused_select = 2 * B * H_r <= 65535
+    if not fused_select:
+        us["sel_emit_kernel"] = us["rtp_topp_select"] - us["rtp_topp_hist"]
     if sl.mode == "scan_local":
         us["rtp_scan_local"] = time_call(lambda: [rtp.rtp_scan_local(
             qr_all[l], kr_all[l], scores_l[l], q_all[l], K_all[l], V_all[l], N, H_r, Hq - H_r,
@@ -255,10 +260,12 @@ def main():
     achieved_gbps = B_alg / (ms_step * 1e-3) / 1e9
 
     # Roofline of the dominant kernel: the kernel with the largest time per
-    # layer.  Calls that launch one kernel are timed directly; the emit
-    # kernel is rtp_topp_select minus rtp_topp_hist.  Algorithmic bytes per
-    # launch (one layer):
-    #   emit    4 B per score read + 4 B per kept index written;
+    # layer.  Calls that launch one kernel are timed directly.  Algorithmic
+    # bytes per launch (one layer):
+    #   select  4 B per score read + 4 B per kept index written (one launch:
+    #           its histogram and emit blocks each read the scores; the
+    #           second read earns no credit);
+    #   emit    the same, for the emit kernel of the two-launch selection;
     #   hist    4 B per score read;
     #   scan    64 B of k_r read + 4 B of score written per query head, per
     #           token and retrieval KV head;
@@ -271,9 +278,9 @@ def main():
     csrc = os.path.join(ROOT, "sparse_long_context_indexer_amd", "csrc")
     sel_total = float(np.mean([sum(x) for x in n_sel]))
     sparse_bytes = float(np.mean(union)) * 2 * d * 2 + sel_total * 4
-    us["sel_emit_kernel"] = us_emit
+    sel_bytes = B * H_r * N * 4 + sel_total * 4
     cands = {
-        "sel_emit_kernel": ("sel_emit_kernel", B * H_r * N * 4 + sel_total * 4, "select.hip"),
+        "sel_emit_kernel": ("sel_emit_kernel", sel_bytes, "select.hip"),
         "rtp_topp_hist": ("sel_hist_kernel", B * H_r * N * 4, "select.hip"),
         "rtp_index_scores": ("index_scores_kernel<8>", B * G_r * N * (cfg.r * 4 + cfg.G * 4),
                              "scan.hip"),
@@ -288,10 +295,14 @@ def main():
                                     "attend.hip"),
         "rtp_local_decode": ("attend_kernel", window_bytes, "attend.hip"),
     }
-    # In mode "scan_local" rtp_index_scores is timed for reference only: the
-    # step runs the scan inside rtp_scan_local.
+    if fused_select:
+        cands["rtp_topp_select"] = ("sel_fused_kernel", sel_bytes, "select.hip")
+    # Calls timed for reference only, outside the step: rtp_index_scores in
+    # mode "scan_local" (the step runs the scan inside rtp_scan_local) and
+    # rtp_topp_hist when the selection is one launch.
     in_step = [c for c in cands if c in us
-               and not (sl.mode == "scan_local" and c == "rtp_index_scores")]
+               and not (sl.mode == "scan_local" and c == "rtp_index_scores")
+               and not (fused_select and c == "rtp_topp_hist")]
     call = max(in_step, key=lambda c: us[c])
     kname, kbytes, ksrc = cands[call]
     roof = {"kernel": kname, "bound": "hbm",

@@ -212,11 +212,21 @@ __device__ void clear_row(SelPtrs P, int64_t r)
     if (threadIdx.x == 0) ctr_add(&P.rows[r].ready, 1u);
 }
 
-__device__ void wait_row_ready(const SelRow &row)
+// Polls before a wait gives up.  Every block waited for was dispatched
+// before the waiting one (block 0 of the row; in the one-launch selection,
+// the row's histogram blocks) and never waits for a later block, so a wait
+// ends long before this; the bound only keeps a fault elsewhere from
+// hanging the device.
+constexpr int kSpinMax = 1 << 24;
+
+// Waits until the row's tagged `ready` counter holds at least `level`: 1
+// once block 0 has cleared the row, 2 once the row's Hist1 is complete
+// (one-launch selection only).
+__device__ void wait_row_ready(const SelRow &row, uint32_t level)
 {
-    for (;;) {
+    for (int it = 0; it < kSpinMax; ++it) {
         const unsigned long long v = ld_agent(&row.ready);
-        if ((uint32_t)v == kCtrTag && (v >> 32) != 0) return;
+        if ((uint32_t)v == kCtrTag && (uint32_t)(v >> 32) >= level) return;
         __builtin_amdgcn_s_sleep(2);
     }
 }
@@ -232,21 +242,16 @@ struct HistShared {
     float red[kSelThreads / kWave];
 };
 
-__global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__restrict__ scores,
-                                                               int N, SelPtrs P)
+// The level-1 histogram of one chunk (scores in v): accumulated in LDS (hm,
+// kBins1 doubles; etbl receives the exp table; red kSelThreads/kWave
+// floats), then added to the row's Hist1 once block 0 has cleared it, and
+// the chunk's top-bin record stored.  Leaves the block's arrival to the
+// caller.
+__device__ void hist_body(const float (&v)[kSelPerThread], int64_t r, int blk, SelPtrs P,
+                          double *hm, double *etbl, float *red)
 {
-    __shared__ HistShared S;
-    double *hm = S.hm;
-    float *red = S.red;
-    const int64_t r = blockIdx.y;
-    const int blk = blockIdx.x;
-    const float *sr = scores + r * (int64_t)N;
-    float v[kSelPerThread];
-    load_chunk(sr, N, (int64_t)blk * kSelChunk, v);  // missing elements: -inf
-    if (blk == 0) clear_row(P, r);
-
     for (int i = threadIdx.x; i < kBins1; i += kSelThreads) hm[i] = 0.0;
-    if (threadIdx.x < kExpTable) S.etbl[threadIdx.x] = kExp2Tbl[threadIdx.x];
+    if (threadIdx.x < kExpTable) etbl[threadIdx.x] = kExp2Tbl[threadIdx.x];
     float m = -INFINITY;
 #pragma unroll
     for (int t = 0; t < kSelPerThread; ++t) m = fmaxf(m, v[t]);
@@ -270,9 +275,9 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
         constexpr uint32_t kLow = (1u << kShift1) - 1u;
         const uint32_t top = (u | (kLow & ~sm)) & ~(kLow & sm);      // bin_top(bin)
         const float ref = bin == tb ? mb : __uint_as_float(top);
-        atomicAdd(&hm[bin], exp_tang((double)(v[t] - ref), S.etbl));
+        atomicAdd(&hm[bin], exp_tang((double)(v[t] - ref), etbl));
     }
-    if (blk != 0 && threadIdx.x == 0) wait_row_ready(P.rows[r]);
+    if (blk != 0 && threadIdx.x == 0) wait_row_ready(P.rows[r], 1u);
     __syncthreads();
     Hist1 &g = P.hist1[r];
     for (int i = threadIdx.x; i < kBins1; i += kSelThreads) {
@@ -281,13 +286,26 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
     }
     if (threadIdx.x == 0) {
         ChunkTop &t = P.tops[r * P.nblk + blk];
-        t.m = mb;
-        t.mass = hm[tb];
-        // Every block of the row has passed its wait once all have counted
-        // themselves here, so the last one resets `ready` for the next call.
-        if (atomicAdd(&P.rows[r].hist_done, 1u) == (uint32_t)(P.nblk - 1))
-            ctr_reset(&P.rows[r].ready);
+        st_agent(&t.m, mb);
+        st_agent(&t.mass, hm[tb]);
     }
+}
+
+__global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__restrict__ scores,
+                                                               int N, SelPtrs P)
+{
+    __shared__ HistShared S;
+    const int64_t r = blockIdx.y;
+    const int blk = blockIdx.x;
+    float v[kSelPerThread];
+    load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);  // missing: -inf
+    if (blk == 0) clear_row(P, r);
+    hist_body(v, r, blk, P, S.hm, S.etbl, S.red);
+    // Every block of the row has passed its wait once all have counted
+    // themselves here, so the last one resets `ready` for the next call.
+    if (threadIdx.x == 0 &&
+        atomicAdd(&P.rows[r].hist_done, 1u) == (uint32_t)(P.nblk - 1))
+        ctr_reset(&P.rows[r].ready);
 }
 
 // --------------------------------------------------------------- emit
@@ -774,34 +792,44 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
     if (tid == 0) count[r] = (int32_t)(emitted + (uint32_t)S.nn);
 }
 
-__global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
-    const float *__restrict__ scores, int N, SelPtrs P, float p, int32_t *__restrict__ idx,
-    int32_t *__restrict__ count, uint32_t *__restrict__ keep_bits)
+// What the pick reads of the row: this thread's Hist1 bins and the top
+// record of chunk tid, with agent-scope loads (in the one-launch selection
+// the histogram blocks of the same launch wrote them).
+struct PickIn {
+    double gmv[kPickPer];
+    float tm0;
+    double tmass0;
+};
+
+__device__ __forceinline__ void pick_inputs(SelPtrs P, int64_t r, PickIn &pi)
+{
+    const Hist1 &g = P.hist1[r];
+#pragma unroll
+    for (int k = 0; k < kPickPer; ++k) pi.gmv[k] = ld_agent(&g.mass[threadIdx.x + k * kSelThreads]);
+    pi.tm0 = -INFINITY;
+    pi.tmass0 = 0.0;
+    if ((int)threadIdx.x < P.nblk) {
+        const ChunkTop &t = P.tops[r * P.nblk + threadIdx.x];
+        pi.tm0 = ld_agent(&t.m);
+        pi.tmass0 = ld_agent(&t.mass);
+    }
+}
+
+// One chunk's share of the emit pass (scores in v, the pick's inputs in
+// pi): the row's threshold, the chunk's kept tokens and boundary-bin
+// candidates, its share of Hist2; the last chunk of the row to finish
+// resolves the boundary bin.
+__device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, int N,
+                          SelPtrs P, int64_t r, float p, const PickIn &pi,
+                          int32_t *__restrict__ idx, int32_t *__restrict__ count,
+                          uint32_t *__restrict__ keep_bits, ResShared &S)
 {
     static_assert(kSelThreads == kResThreads, "the last emit block runs the resolve");
-    __shared__ ResShared S;
     unsigned long long *wbase = S.wbase;
-    const int64_t r = blockIdx.y;
-    const float *sr = scores + r * (int64_t)N;
     int32_t *ir = idx + r * (int64_t)N;
     uint2 *cr = P.cand + r * (int64_t)N;
-    // The row's histogram and chunk tops (finished by the hist kernel) are
-    // requested together with the chunk's scores.
-    const ChunkTop *tops = P.tops + r * P.nblk;
-    const Hist1 &g = P.hist1[r];
-    double gmv[kPickPer];
-#pragma unroll
-    for (int k = 0; k < kPickPer; ++k) gmv[k] = g.mass[threadIdx.x + k * kSelThreads];
-    float tm0 = -INFINITY;
-    double tmass0 = 0.0;
-    if ((int)threadIdx.x < P.nblk) {
-        tm0 = tops[threadIdx.x].m;
-        tmass0 = tops[threadIdx.x].mass;
-    }
-    float v[kSelPerThread];
-    const ChunkView cv = load_chunk(sr, N, (int64_t)blockIdx.x * kSelChunk, v);
     if (threadIdx.x < kExpTable) S.etbl[threadIdx.x] = kExp2Tbl[threadIdx.x];
-    pick_block(tops, P.nblk, p, gmv, tm0, tmass0, S);
+    pick_block(P.tops + r * P.nblk, P.nblk, p, pi.gmv, pi.tm0, pi.tmass0, S);
     const uint32_t j1 = S.j1;
     if (threadIdx.x == 0) S.bcount = 0ull;
     S.hm[threadIdx.x] = 0.0;  // this block's share of the row's Hist2
@@ -930,10 +958,66 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     wait_vmem();
     __syncthreads();
     if (threadIdx.x == 0)
-        S.last = atomicAdd(&P.rows[r].emit_done, 1u) == (uint32_t)(gridDim.x - 1);
+        S.last = atomicAdd(&P.rows[r].emit_done, 1u) == (uint32_t)(P.nblk - 1);
     __syncthreads();
     if (!S.last) return;
     resolve_row(N, P, r, idx, count, kbr, S);
+    // Every block of the row has passed its waits: `ready` is reset for the
+    // next call (in the two-launch selection it already is).
+    if (threadIdx.x == 0) ctr_reset(&P.rows[r].ready);
+}
+
+__global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
+    const float *__restrict__ scores, int N, SelPtrs P, float p, int32_t *__restrict__ idx,
+    int32_t *__restrict__ count, uint32_t *__restrict__ keep_bits)
+{
+    __shared__ ResShared S;
+    const int64_t r = blockIdx.y;
+    // The row's histogram and chunk tops (finished by the hist kernel) are
+    // requested together with the chunk's scores.
+    PickIn pi;
+    pick_inputs(P, r, pi);
+    float v[kSelPerThread];
+    const ChunkView cv =
+        load_chunk(scores + r * (int64_t)N, N, (int64_t)blockIdx.x * kSelChunk, v);
+    emit_body(v, cv, N, P, r, p, pi, idx, count, keep_bits, S);
+}
+
+// Both passes in one launch.  Block rows [0, R) are the histogram blocks,
+// rows [R, 2R) the emit blocks, so every histogram block is dispatched
+// before any emit block.  An emit block loads its chunk, then waits until
+// its row's Hist1 is complete (the last histogram block of the row raises
+// `ready` to 2); it never waits for a later block, and no histogram block
+// waits for an emit block, so the launch needs no co-residency.
+__global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(
+    const float *__restrict__ scores, int N, SelPtrs P, float p, int32_t *__restrict__ idx,
+    int32_t *__restrict__ count, uint32_t *__restrict__ keep_bits)
+{
+    __shared__ ResShared S;
+    const int R = (int)gridDim.y / 2;
+    const int blk = blockIdx.x;
+    if ((int)blockIdx.y < R) {
+        const int64_t r = blockIdx.y;
+        float v[kSelPerThread];
+        load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);
+        if (blk == 0) clear_row(P, r);
+        static_assert(sizeof(double) * kBins1 <= sizeof(S.buf), "the histogram fits in buf");
+        hist_body(v, r, blk, P, reinterpret_cast<double *>(&S.buf[0][0]), S.etbl, S.red);
+        wait_vmem();  // this block's Hist1 adds and top record are done
+        __syncthreads();
+        if (threadIdx.x == 0 &&
+            atomicAdd(&P.rows[r].hist_done, 1u) == (uint32_t)(P.nblk - 1))
+            ctr_add(&P.rows[r].ready, 1u);  // 2: the row's Hist1 is complete
+        return;
+    }
+    const int64_t r = blockIdx.y - R;
+    float v[kSelPerThread];
+    const ChunkView cv = load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);
+    if (threadIdx.x == 0) wait_row_ready(P.rows[r], 2u);
+    __syncthreads();
+    PickIn pi;
+    pick_inputs(P, r, pi);
+    emit_body(v, cv, N, P, r, p, pi, idx, count, keep_bits, S);
 }
 
 // ---------------------------------------------------------------- p >= 1
@@ -953,6 +1037,8 @@ __global__ __launch_bounds__(256) void sel_all_kernel(int N, int32_t *__restrict
     }
 }
 
+constexpr int64_t kMaxFusedRows = 65535;  // grid rows of one launch
+
 hipError_t launch_topp_hist(const float *scores, int64_t R, int N, void *ws, hipStream_t stream)
 {
     SelPtrs P = sel_ptrs(ws, R, N);
@@ -968,6 +1054,9 @@ hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p, in
         return launch(sel_all_kernel, grid, dim3(256), 0, stream, N, idx, count, keep_bits);
     }
     SelPtrs P = sel_ptrs(ws, R, N);
+    if (2 * R <= kMaxFusedRows)
+        return launch(sel_fused_kernel, dim3((unsigned)P.nblk, (unsigned)(2 * R)),
+                      dim3(kSelThreads), 0, stream, scores, N, P, p, idx, count, keep_bits);
     dim3 grid((unsigned)P.nblk, (unsigned)R);
     RTP_TRY(launch(sel_hist_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P));
     return launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, p, idx, count,

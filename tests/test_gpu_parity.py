@@ -185,6 +185,35 @@ def test_select_repeatable():
             assert set(a[r][h].tolist()) == set(b_[r][h].tolist())
 
 
+def test_select_many_chunks():
+    # 280 chunks of 32768 scores (more blocks than compute units), then the
+    # same rows cut to 8 chunks each, against the oracle, on rows with
+    # heavy-tailed, clustered and duplicated scores.
+    rng = np.random.default_rng(23)
+    B, H, N = 2, 5, 900_000
+    s = rng.standard_normal((B, H, N)).astype(np.float32) * np.float32(2.0)
+    s[:, :, ::97] += np.float32(6.0)                       # a heavy tail
+    s[0, 1, :] = np.round(s[0, 1, :] * 4) / 4              # many exact duplicates
+    s[1, 3, rng.integers(0, N, 2000)] = np.float32(9.5)    # a tie block at the top
+    for n in (N, 8 * 32768 - 123):
+        sub = np.ascontiguousarray(s[:, :, :n])
+        for p in (0.5, 0.9):
+            _assert_select(sub, p)
+
+
+def test_select_two_launch_path():
+    # 40000 score rows: more than one launch holds as histogram rows plus
+    # emit rows, so the selection runs as a histogram launch then an emit
+    # launch.
+    rng = np.random.default_rng(29)
+    s = (rng.standard_normal((1, 40000, 96)) * 3).astype(np.float32)
+    s[0, ::3, ::5] = np.float32(1.25)  # ties
+    sets, c = _select(s, 0.8)
+    for h in range(0, 40000, 7):
+        v = judge_set(s[0, h], 0.8, sets[0][h])
+        assert v.ok, (h, v.k_gpu, v.k_oracle, v.note)
+
+
 # -------------------------------------------------------- attention edges
 
 def test_sparse_single_row_is_value_row():
