@@ -267,8 +267,14 @@ __device__ void hist_body(const float (&v)[kSelPerThread], int64_t r, int blk, S
     // A bin's top score shares the sign and the bits above kShift1 with
     // every score of the bin: the low bits all set for a positive score,
     // all clear for a negative one.
+    // Block 0 of the row has usually cleared the row by mid-way through this
+    // loop: thread 0 reads `ready` there, so that the wait after the loop
+    // normally costs no round trip.
+    unsigned long long rdy = 0;
 #pragma unroll
     for (int t = 0; t < kSelPerThread; ++t) {
+        if (t == kSelPerThread / 2 && blk != 0 && threadIdx.x == 0)
+            rdy = ld_agent(&P.rows[r].ready);
         const uint32_t u = __float_as_uint(v[t] + 0.0f);  // -0 folded into +0
         const uint32_t sm = (uint32_t)((int32_t)u >> 31);
         const uint32_t bin = (u ^ (sm | 0x80000000u)) >> kShift1;  // score_key(v) >> kShift1
@@ -277,7 +283,8 @@ __device__ void hist_body(const float (&v)[kSelPerThread], int64_t r, int blk, S
         const float ref = bin == tb ? mb : __uint_as_float(top);
         atomicAdd(&hm[bin], exp_tang((double)(v[t] - ref), etbl));
     }
-    if (blk != 0 && threadIdx.x == 0) wait_row_ready(P.rows[r], 1u);
+    if (blk != 0 && threadIdx.x == 0 && !((uint32_t)rdy == kCtrTag && (rdy >> 32) >= 1))
+        wait_row_ready(P.rows[r], 1u);
     __syncthreads();
     Hist1 &g = P.hist1[r];
     for (int i = threadIdx.x; i < kBins1; i += kSelThreads) {
