@@ -113,12 +113,13 @@ rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H,
                            size_t ws_bytes, void *stream);
 
 /*
- * rtp_topp_hist -- the first of rtp_topp_select's two launches on its own:
- * the per-row mass histograms (same passage) are left in the workspace and
- * no output is written.  rtp_topp_select launches this and then its second
- * kernel, which consumes the histograms; calling rtp_topp_hist alone is
- * harmless (a later rtp_topp_select starts over).  It exists so that the
- * histogram pass can be timed or profiled apart.
+ * rtp_topp_hist -- the histogram pass of rtp_topp_select on its own: the
+ * per-row mass histograms (same passage) are left in the workspace and no
+ * output is written.  rtp_topp_select runs this pass and the emit pass that
+ * consumes the histograms in one launch (in two launches when B*H exceeds
+ * 32767); calling rtp_topp_hist alone is harmless (a later rtp_topp_select
+ * starts over).  It exists so that the histogram pass can be timed or
+ * profiled apart.
  *
  *   scores, B, H, N, workspace as in rtp_topp_select.
  */
