@@ -65,10 +65,10 @@ static_assert(kMaxSlices <= kSlice, "the second merge level takes at most kSlice
 int sparse_grid(int64_t R) { return (int)(kSparseTarget + R); }
 
 struct SparseWs {
-    float *part;                    // one partial per attention block
-    float *super;                   // [R][kMaxSlices] slice merges
-    unsigned long long *slice_ctr;  // [R][kMaxSlices] arrivals per slice
-    unsigned long long *head_ctr;   // [R] slices merged per head row
+    float *part;           // one partial per attention block
+    float *super;          // [R][kMaxSlices] slice merges
+    uint32_t *part_flag;   // one hand-off flag per partial
+    uint32_t *super_flag;  // [R][kMaxSlices]
 };
 
 static size_t sparse_ws_layout(int64_t R, SparseWs *W, void *base)
@@ -78,16 +78,16 @@ static size_t sparse_ws_layout(int64_t R, SparseWs *W, void *base)
     off += align_up((size_t)sparse_grid(R) * kPart * sizeof(float), 256);
     const size_t sup = off;
     off += align_up((size_t)R * kMaxSlices * kPart * sizeof(float), 256);
-    const size_t sc = off;
-    off += align_up((size_t)R * kMaxSlices * sizeof(unsigned long long), 256);
-    const size_t hc = off;
-    off += align_up((size_t)R * sizeof(unsigned long long), 256);
+    const size_t pf = off;
+    off += align_up((size_t)sparse_grid(R) * sizeof(uint32_t), 256);
+    const size_t sf = off;
+    off += align_up((size_t)R * kMaxSlices * sizeof(uint32_t), 256);
     if (W) {
         char *b = static_cast<char *>(base);
         W->part = reinterpret_cast<float *>(b + part);
         W->super = reinterpret_cast<float *>(b + sup);
-        W->slice_ctr = reinterpret_cast<unsigned long long *>(b + sc);
-        W->head_ctr = reinterpret_cast<unsigned long long *>(b + hc);
+        W->part_flag = reinterpret_cast<uint32_t *>(b + pf);
+        W->super_flag = reinterpret_cast<uint32_t *>(b + sf);
     }
     return off;
 }
@@ -385,23 +385,37 @@ __device__ void sparse_block(const uint16_t *__restrict__ q, const uint16_t *__r
         }
     }
 
-    // Two-level merge inside the kernel: the last block of a slice of
-    // kSlice splits merges the slice; the last slice merger finishes the row.
+    // Two-level merge inside the kernel.  The last split of each slice of
+    // kSlice splits merges the slice once the slice's other blocks have
+    // published their partials; the merger of the row's last slice merges
+    // the slices once the other slice mergers have published theirs.  A
+    // merger waits only for blocks with lower indices.
     const int k = blk - plan.first;
     const int slice = k / kSlice;
     const int slices = (plan.splits + kSlice - 1) / kSlice;
     const int in_slice = min(kSlice, plan.splits - slice * kSlice);
+    const int k0 = plan.first + slice * kSlice;  // the slice's first block
     float *dst = out + ((int64_t)b * Hq + h) * 128;
-    unsigned long long *sc = W.slice_ctr + (int64_t)prow * kMaxSlices + slice;
-    if (!arrive_last(sc, in_slice, &last)) return;
-    const float *first = W.part + (int64_t)(plan.first + slice * kSlice) * kPart;
+    if (blk != k0 + in_slice - 1) {
+        publish_flag(W.part_flag + blk);
+        return;
+    }
+    wait_vmem();  // this block's own partial, read back below by other threads
+    await_flags(W.part_flag + k0, in_slice - 1);
+    const float *first = W.part + (int64_t)k0 * kPart;
     if (slices == 1) {
         merge_partials(first, in_slice, nullptr, dst, MS);
         return;
     }
     float *sp = W.super + ((int64_t)prow * kMaxSlices) * kPart;
+    uint32_t *sf = W.super_flag + (int64_t)prow * kMaxSlices;
     merge_partials(first, in_slice, sp + (int64_t)slice * kPart, nullptr, MS);
-    if (!arrive_last(W.head_ctr + prow, slices, &last)) return;
+    if (slice != slices - 1) {
+        publish_flag(sf + slice);
+        return;
+    }
+    wait_vmem();
+    await_flags(sf, slices - 1);
     merge_partials(sp, slices, nullptr, dst, MS);
 }
 

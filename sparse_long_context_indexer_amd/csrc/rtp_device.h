@@ -225,6 +225,42 @@ __device__ __forceinline__ uint4 ld_nt16(const void *p)
 // Waits until every vector memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Polls before a wait on other blocks gives up.  Every wait in the library
+// is on blocks dispatched before the waiting one that never wait for a later
+// block, so a wait ends long before this; the bound only keeps a fault
+// elsewhere from hanging the device.
+constexpr int kSpinMax = 1 << 24;
+
+// Hand-off flags: a block publishes a result it stored with agent-scope
+// stores by setting a flag word to kFlagTag once every thread's stores have
+// completed; the consumer waits for the tag and clears the word again, so a
+// finished call leaves every flag it used at 0.  kFlagTag is a NaN payload,
+// like kCtrTag.
+constexpr uint32_t kFlagTag = 0x7FC3A96Bu;
+
+__device__ __forceinline__ void publish_flag(uint32_t *flag)
+{
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flag, kFlagTag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Threads 0 .. n-1 each wait for one of the flags f[0 .. n) and clear it;
+// the block then continues together.  n must not exceed the block size.
+__device__ __forceinline__ void await_flags(uint32_t *f, int n)
+{
+    if ((int)threadIdx.x < n) {
+        for (int it = 0; it < kSpinMax; ++it) {
+            if (__hip_atomic_load(f + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                kFlagTag)
+                break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __hip_atomic_store(f + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+}
+
 // Counters shared by the blocks of one call (arrivals, output slots).  A
 // counter word holds a tag (low 32 bits) and a count (high 32 bits); after
 // every call it is left as (kCtrTag, 0), so a block normally counts with one

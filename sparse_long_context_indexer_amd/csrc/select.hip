@@ -212,12 +212,9 @@ __device__ void clear_row(SelPtrs P, int64_t r)
     if (threadIdx.x == 0) ctr_add(&P.rows[r].ready, 1u);
 }
 
-// Polls before a wait gives up.  Every block waited for was dispatched
-// before the waiting one (block 0 of the row; in the one-launch selection,
-// the row's histogram blocks) and never waits for a later block, so a wait
-// ends long before this; the bound only keeps a fault elsewhere from
-// hanging the device.
-constexpr int kSpinMax = 1 << 24;
+// Every block waited for below was dispatched before the waiting one (block
+// 0 of the row; in the one-launch selection, the row's histogram blocks);
+// waits are bounded by kSpinMax polls.
 
 // Waits until the row's tagged `ready` counter holds at least `level`: 1
 // once block 0 has cleared the row, 2 once the row's Hist1 is complete
