@@ -9,8 +9,8 @@
 // gathers in flight.  Split-K: each block owns a contiguous slice of the
 // row list and runs an online softmax over it (base-2 exponent, with
 // scale*log2(e) folded into q); its partial (max, sum, o[128]) record is
-// merged inside the same kernel: the last block to finish a group of
-// splits merges the group, and the last group merger writes the output.
+// merged inside the same kernel in two levels (groups of splits, then the
+// groups).
 //
 // Local heads: the 8 query heads of a KV head share each row read.  Each lane
 // forms 8 partial dot products; a butterfly over the 16 lanes of a row
@@ -247,7 +247,6 @@ struct SparseShared {
     float wo[kAttThreads / kWave][128];
     SplitPlan plan;
     MergeShared ms;
-    int last;
 };
 
 // Per-head sparse attention, split blk of the plan over all heads' kept rows.
@@ -261,7 +260,6 @@ __device__ void sparse_block(const uint16_t *__restrict__ q, const uint16_t *__r
     float *wm = SS.wm, *wl = SS.wl;
     float(*wo)[128] = SS.wo;
     MergeShared &MS = SS.ms;
-    int &last = SS.last;
     constexpr int kRowsPerIter = kGroups * kSparseU;
     const SplitPlan plan = plan_splits(count, R, N, kRowsPerIter, blk, -1, &SS.plan);
     if (plan.r < 0) return;  // past the last split: no partial to write
