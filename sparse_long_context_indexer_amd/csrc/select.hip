@@ -23,10 +23,13 @@
 //           chunk's score loads.  Tokens in bins above j1 are kept; tokens of
 //           bin j1 become candidates (key, index) and are counted by key bits
 //           [19:10].  The row's last block to finish then resolves: the same
-//           step over key bits [19:10], then [9:0] (the boundary is now one
-//           score value tau), then how many tokens of score tau are needed
-//           and, if not all of them, the lowest indices among them by a
-//           count-only radix select over the index bits
+//           step over key bits [19:10]; when at most 64 candidates share the
+//           boundary digit, one wave ranks them by (score, index) and keeps
+//           the shortest rank prefix outright; otherwise the step runs again
+//           over [9:0] (the boundary is now one score value tau), then
+//           decides how many tokens of score tau are needed and, if not all
+//           of them, takes the lowest indices among them by a count-only
+//           radix select over the index bits
 //
 // Masses are fp64 (exp_tang, a table-driven fp64 exp within 1.3 ulp, and
 // fp64 sums), so running sums agree with an fp64 reference to ~1e-15
@@ -327,7 +330,9 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
 // block barrier), then one pass that emits the digits on the kept side and
 // moves the boundary digit's candidates to the other LDS buffer (order is
 // free: the kept set is a set).  Rows with more candidates than fit in LDS
-// use global memory with ordered in-place compaction instead.
+// use global memory with ordered in-place compaction instead.  A boundary
+// digit of at most one wave of candidates is finished by that wave alone,
+// with no further block barrier.
 
 constexpr int kResNW = kResThreads / kWave;
 
@@ -661,6 +666,35 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
     return (uint32_t)(S.nn >> 32);
 }
 
+// Wave 0 finishes a row whose last n <= kWave candidates sit in LDS: lane l
+// ranks candidate l against the others (score descending, then index
+// ascending: the order of the sorted definition), the masses exp(s - M) are
+// laid out in rank order and prefix-summed from A, and the wave keeps the
+// shortest rank prefix whose running mass reaches T (all n if none does).
+__device__ void resolve_few(const uint2 *cr, int n, double A, double T, double M, int32_t *ir,
+                            uint32_t *kbr, ResShared &S)
+{
+    const int l = lane_id();
+    const bool v = l < n;
+    const uint2 e = v ? cr[l] : make_uint2(0u, 0u);
+    int rank = 0;
+    for (int k = 0; k < n; ++k) {
+        const uint32_t kk = read_lane(e.x, k), ki = read_lane(e.y, k);
+        rank += (kk > e.x || (kk == e.x && ki < e.y)) ? 1 : 0;
+    }
+    // Only this wave uses S.hm until the block's next barrier; its LDS
+    // accesses complete in program order.
+    if (v) S.hm[rank] = exp_tang((double)key_score(e.x) - M, S.etbl);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const double w = v ? S.hm[l] : 0.0;
+    const double cum = A + wave_inclusive_scan(w);
+    const uint64_t hit = __ballot(v && cum >= T);
+    const int last = hit ? __ffsll((unsigned long long)hit) - 1 : n - 1;
+    const int64_t pa = wave_append(v && rank <= last, nout_ptr(S));
+    if (pa >= 0) keep_token(ir, pa, e.y, kbr);
+}
+
 __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
                             uint32_t *kbr, ResShared &S)
 {
@@ -690,7 +724,8 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
     // then [9:0] (histogram of the survivors).
     static_assert(kResThreads == kDig, "one digit per thread");
     bool next_built = false;  // level 1's histogram was built by level 0's filter
-    for (int level = 0; level < 2 && n > 0; ++level) {
+    bool few = false;         // at most a wave of candidates left, in LDS
+    for (int level = 0; level < 2 && n > 0 && !few; ++level) {
         const int shift = level == 0 ? kShift2 : 0;
         if (level == 0) {
             S.hm[tid] = h2m;
@@ -719,10 +754,13 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
             cr = S.buf[cur];
         } else if (S.hc[j] <= (uint32_t)kResCap) {
             // The boundary digit's candidates fit in LDS: continue there,
-            // building the next level's histogram on the way.
-            next_built = level == 0;
+            // building the next level's histogram on the way unless one
+            // wave can finish them.
+            few = S.hc[j] <= (uint32_t)kWave;
+            next_built = level == 0 && !few;
             n = res_filter_lds<true>(gc, n, S.buf[0], shift, kDig - 1, j, true, false, ir, kbr, S,
                                      next_built, M);
+            few = few && n <= kWave;
             in_lds = true;
             cur = 0;
             cr = S.buf[0];
@@ -731,7 +769,9 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
         }
     }
 
-    if (n > 0) {
+    if (few) {
+        if (tid < kWave) resolve_few(cr, (int)n, A, T, M, ir, kbr, S);
+    } else if (n > 0) {
         // Every survivor now has the same score tau.  Keep the first c of
         // them in index order: the smallest c with A + c * e_tau >= T.
         const uint32_t tau_key = cand(0).x;

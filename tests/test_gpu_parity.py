@@ -141,6 +141,28 @@ def test_select_tiny_rows_and_extremes():
     _assert_select(s, 0.95, exact=True)
 
 
+@pytest.mark.parametrize("k", [2, 17, 63, 64, 65, 300])
+@pytest.mark.parametrize("level", [6.0, 2.5])
+def test_select_boundary_tie_group(k, level):
+    # k tokens share one score; p puts the crossing inside that group, so
+    # the kept set holds the group's lowest indices.  At level 6.0 the group
+    # tops the row; at 2.5 distinct scores around it share its bins.  Sizes
+    # straddle one wave of boundary candidates.
+    rng = np.random.default_rng(17 + k)
+    N = 50_000
+    s = rng.standard_normal((1, 2, N)).astype(np.float32)
+    for h in range(2):
+        pos = rng.choice(N, k, replace=False)
+        s[0, h, pos] = np.float32(level)
+        x = s[0, h].astype(np.float64)
+        w = np.exp(x - x.max())
+        above = w[x > level].sum()
+        group = w[x == level].sum()
+        frac = 0.37 if h == 0 else 0.81
+        pv = np.float32((above + frac * group) / w.sum())
+        _assert_select(s[:, h:h + 1], float(pv), exact=True)
+
+
 def test_select_p_one_keeps_all():
     s = np.random.default_rng(3).standard_normal((2, 2, 9000)).astype(np.float32)
     sets, c = _select(s, 1.0)
