@@ -194,6 +194,14 @@ def main():
         "rtp_topp_hist": time_call(lambda: [rtp.rtp_topp_hist(scores_l[l], sl.ws_sel)
                                             for l in range(L)]),
     }
+    # Static top-k, the fixed budget that dynamic top-p replaces, timed on the
+    # same scores at the workload's mean top-p budget: a reference call, not
+    # part of the step (sel_fused_kernel<true>, the same launch shape).
+    k_budget = max(1, int(round(float(count_l.float().mean().item()))))
+    idx_k = torch.empty_like(idx_l[0])
+    count_k = torch.empty_like(count_l[0])
+    us["rtp_topk_select"] = time_call(lambda: [rtp.rtp_topk_select(
+        scores_l[l], k_budget, idx_k, count_k, sl.ws_sel) for l in range(L)])
     # rtp_topp_select runs both passes in one launch (sel_fused_kernel) when
     # its histogram and emit block rows fit one grid (2 * B * H_r <= 65535);
     # rtp_topp_hist, the histogram pass alone, is then timed for reference
@@ -336,6 +344,7 @@ def main():
         "selected_per_head_mean": float(np.mean(n_sel)),
         "union_rows_per_layer_mean": float(np.mean(union)),
         "per_call_us_per_layer": {k: round(v, 2) for k, v in us.items()},
+        "topk_budget": k_budget,
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
         "cpu_baseline": cpu,
     }

@@ -113,6 +113,30 @@ rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H,
                            size_t ws_bytes, void *stream);
 
 /*
+ * rtp_topk_select -- static top-k token selection per head: the fixed
+ * budget that dynamic top-p replaces (gist.science summary, method section
+ * 3, dynamic top-p versus static top-k; arXiv abstract, third observation).
+ *
+ * For each of the B*H score rows: order tokens by score, descending, ties
+ * to the lower index, and keep the first min(k, N).  It runs the machinery
+ * of rtp_topp_select with every token weighing 1 instead of its mass.
+ *
+ *   scores     fp32  [B][H][N]   4-B aligned; -0 is treated as +0
+ *   k          >= 1; k >= N keeps all N tokens
+ *   idx, count, keep_bits, workspace, ws_bytes, stream
+ *              as in rtp_topp_select (count[b][h] = min(k, N); the same
+ *              workspace size)
+ *
+ * Errors: RTP_ERR_NULL (scores, idx, count or workspace NULL),
+ * RTP_ERR_SHAPE (B, H or N < 1, or B*H > 65535), RTP_ERR_VALUE (k < 1),
+ * RTP_ERR_ALIGN, RTP_ERR_WORKSPACE.
+ */
+rtp_status rtp_topk_select(const float *scores, int32_t B, int32_t H,
+                           int32_t N, int32_t k, int32_t *idx, int32_t *count,
+                           uint32_t *keep_bits, void *workspace,
+                           size_t ws_bytes, void *stream);
+
+/*
  * rtp_topp_hist -- the histogram pass of rtp_topp_select on its own: the
  * per-row mass histograms (same passage) are left in the workspace and no
  * output is written.  rtp_topp_select runs this pass and the emit pass that

@@ -48,6 +48,8 @@ def _load():
         lib.orc_scores.restype = None
         lib.orc_topp.argtypes = [P, I64, ctypes.c_float, P, P]
         lib.orc_topp.restype = I64
+        lib.orc_topk.argtypes = [P, I64, I64, P]
+        lib.orc_topk.restype = I64
         lib.orc_set_mass.argtypes = [P, I64, P, I64]
         lib.orc_set_mass.restype = ctypes.c_double
         lib.orc_attention.argtypes = [P, P, P, I64, P, I64, ctypes.c_float, P]
@@ -102,6 +104,18 @@ def topp(s: np.ndarray, p: float) -> TopP:
     return TopP(sel=sel[:k].copy(), k=int(k), tau=float(rep.tau),
                 max_score=rep.max_score, Z=rep.Z, mass=rep.mass,
                 last_mass=rep.last_mass, slack=rep.slack)
+
+
+def topk(s: np.ndarray, k: int) -> np.ndarray:
+    """Top-k set of one head's scores (int64 indices, largest score first,
+    ties to the lower index); k >= N keeps all."""
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    n = s.shape[0]
+    sel = np.empty(max(n, 1), dtype=np.int64)
+    c = _load().orc_topk(_ptr(s), n, int(k), _ptr(sel))
+    if c < 0:
+        raise MemoryError("oracle top-k: out of memory")
+    return sel[:c].copy()
 
 
 def set_mass(s: np.ndarray, members) -> float:

@@ -27,6 +27,11 @@
  *                      cached tokens, in fp64; order is a full sort by score,
  *                      ties to the lower token index; the set is the shortest
  *                      prefix whose mass is >= p * Z.  p >= 1 keeps all.
+ *   orc_topk        -- static top-k selection, the fixed budget that dynamic
+ *                      top-p is set against (same section): the k highest
+ *                      scores, in the same order as orc_topp (the pages give
+ *                      no tie rule for either; ties go to the lower index).
+ *                      k >= N keeps all.
  *   orc_attention   -- exact softmax attention of one query row over a given
  *                      set of cached rows, in fp64 (arXiv abstract: sparse
  *                      attention over the indexer's tokens; summary
@@ -171,6 +176,25 @@ int64_t orc_topp(const float *s, int64_t N, float p, int64_t *sel,
     free(order);
     if (rep) *rep = r;
     return k;
+}
+
+/* Selects the top-k set of one head: the first min(k, N) tokens of the full
+ * order used by orc_topp.  sel must hold N entries; it receives them in that
+ * order.  Returns the set size (0 for k <= 0), or -1 if memory runs out. */
+int64_t orc_topk(const float *s, int64_t N, int64_t k, int64_t *sel)
+{
+    scored *order = (scored *)malloc((size_t)(N > 0 ? N : 1) * sizeof *order);
+    if (!order) return -1;
+    for (int64_t i = 0; i < N; ++i) {
+        order[i].s = s[i];
+        order[i].i = i;
+    }
+    qsort(order, (size_t)N, sizeof *order, by_score_desc);
+    const int64_t n = k < 0 ? 0 : (k < N ? k : N);
+    for (int64_t t = 0; t < n; ++t)
+        sel[t] = order[t].i;
+    free(order);
+    return n;
 }
 
 /* Mass of an arbitrary set of tokens, as a fraction of Z (O2 definitions).

@@ -25,9 +25,10 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPP
           4: "RTP_ERR_VALUE", 5: "RTP_ERR_ALIGN", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
 
 # Every symbol include/rtp.h declares.
-SYMBOLS = ("rtp_index_scores", "rtp_topp_select", "rtp_topp_hist", "rtp_sparse_decode",
-           "rtp_sparse_decode_union", "rtp_local_decode", "rtp_decode_attend",
-           "rtp_scan_local", "rtp_workspace_size", "rtp_status_string", "rtp_last_hip_error")
+SYMBOLS = ("rtp_index_scores", "rtp_topp_select", "rtp_topk_select", "rtp_topp_hist",
+           "rtp_sparse_decode", "rtp_sparse_decode_union", "rtp_local_decode",
+           "rtp_decode_attend", "rtp_scan_local", "rtp_workspace_size", "rtp_status_string",
+           "rtp_last_hip_error")
 
 
 class RtpError(RuntimeError):
@@ -57,6 +58,7 @@ def lib() -> ctypes.CDLL:
                                 ctypes.c_float, ctypes.c_size_t)
         L.rtp_index_scores.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, P]
         L.rtp_topp_select.argtypes = [P, I32, I32, I32, F32, P, P, P, P, SZ, P]
+        L.rtp_topk_select.argtypes = [P, I32, I32, I32, I32, P, P, P, P, SZ, P]
         L.rtp_topp_hist.argtypes = [P, I32, I32, I32, P, SZ, P]
         L.rtp_sparse_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32,
                                         I32, I32, F32, P, P, SZ, P]
@@ -73,7 +75,7 @@ def lib() -> ctypes.CDLL:
         L.rtp_status_string.restype = ctypes.c_char_p
         L.rtp_last_hip_error.argtypes = []
         L.rtp_last_hip_error.restype = I32
-        for name in SYMBOLS[:9]:
+        for name in SYMBOLS[:10]:
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -159,6 +161,24 @@ def rtp_topp_select(scores, p, idx, count, workspace, keep_bits=None, stream=Non
         _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2), kb,
         _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
         _stream(scores, stream)), "rtp_topp_select")
+
+
+def rtp_topk_select(scores, k, idx, count, workspace, keep_bits=None, stream=None) -> None:
+    """Static top-k: the first min(k, N) tokens of each row by (score
+    descending, index ascending).  Arguments as in rtp_topp_select, with the
+    integer budget k >= 1 in place of p."""
+    import torch
+    B, H, N = scores.shape
+    kb = None
+    if keep_bits is not None:
+        if tuple(keep_bits.shape) != (B, H, keep_words(N)):
+            raise ValueError(f"keep_bits must have shape {(B, H, keep_words(N))}")
+        kb = _dev(keep_bits, torch.int32, "keep_bits", 3)
+    _check(lib().rtp_topk_select(
+        _dev(scores, torch.float32, "scores", 3), B, H, N, int(k),
+        _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2), kb,
+        _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
+        _stream(scores, stream)), "rtp_topk_select")
 
 
 def rtp_topp_hist(scores, workspace, stream=None) -> None:

@@ -109,6 +109,22 @@ rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H, int32_t N,
                                             as_stream(stream)));
 }
 
+rtp_status rtp_topk_select(const float *scores, int32_t B, int32_t H, int32_t N, int32_t k,
+                           int32_t *idx, int32_t *count, uint32_t *keep_bits, void *workspace,
+                           size_t ws_bytes, void *stream)
+{
+    if (!scores || !idx || !count || !workspace) return RTP_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1 || (int64_t)B * H > kMaxGridY) return RTP_ERR_SHAPE;
+    if (k < 1) return RTP_ERR_VALUE;
+    if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(count, 4) ||
+        !aligned(keep_bits, 4) || !aligned(workspace, 256))
+        return RTP_ERR_ALIGN;
+    const int64_t R = (int64_t)B * H;
+    if (ws_bytes < rtp::sel_layout(R, N).total) return RTP_ERR_WORKSPACE;
+    return from_hip(rtp::launch_topk_select(scores, R, N, k, idx, count, keep_bits, workspace,
+                                            as_stream(stream)));
+}
+
 rtp_status rtp_topp_hist(const float *scores, int32_t B, int32_t H, int32_t N, void *workspace,
                          size_t ws_bytes, void *stream)
 {

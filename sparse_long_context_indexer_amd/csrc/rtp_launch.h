@@ -27,6 +27,8 @@ SelLayout sel_layout(int64_t R, int64_t N);
 hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p,
                               int32_t *idx, int32_t *count, uint32_t *keep_bits,
                               void *ws, hipStream_t stream);
+hipError_t launch_topk_select(const float *scores, int64_t R, int N, int k, int32_t *idx,
+                              int32_t *count, uint32_t *keep_bits, void *ws, hipStream_t stream);
 hipError_t launch_topp_hist(const float *scores, int64_t R, int N, void *ws,
                             hipStream_t stream);
 

@@ -236,6 +236,17 @@ __device__ void wait_row_ready(const SelRow &row, uint32_t level)
 // 2^(j/64) for exp_tang; each kernel copies it to LDS.
 __constant__ double kExp2Tbl[kExpTable] = RTP_EXP2_TABLE;
 
+// A token's weight in the running sums: its mass exp(x) (x = its score
+// minus a reference) for top-p; 1 for top-k, whose prefixes count tokens.
+template <bool kCount>
+__device__ __forceinline__ double weight(double x, const double *etbl)
+{
+    if constexpr (kCount)
+        return 1.0;
+    else
+        return exp_tang(x, etbl);
+}
+
 struct HistShared {
     double hm[kBins1];
     double etbl[kExpTable];
@@ -247,8 +258,9 @@ struct HistShared {
 // floats), then added to the row's Hist1 once block 0 has cleared it, and
 // the chunk's top-bin record stored.  Leaves the block's arrival to the
 // caller.
-__device__ void hist_body(const float (&v)[kSelPerThread], int64_t r, int blk, SelPtrs P,
-                          double *hm, double *etbl, float *red)
+template <bool kCount>
+__device__ void hist_body(const float (&v)[kSelPerThread], const ChunkView &cv, int N, int64_t r,
+                          int blk, SelPtrs P, double *hm, double *etbl, float *red)
 {
     for (int i = threadIdx.x; i < kBins1; i += kSelThreads) hm[i] = 0.0;
     if (threadIdx.x < kExpTable) etbl[threadIdx.x] = kExp2Tbl[threadIdx.x];
@@ -281,7 +293,10 @@ __device__ void hist_body(const float (&v)[kSelPerThread], int64_t r, int blk, S
         constexpr uint32_t kLow = (1u << kShift1) - 1u;
         const uint32_t top = (u | (kLow & ~sm)) & ~(kLow & sm);      // bin_top(bin)
         const float ref = bin == tb ? mb : __uint_as_float(top);
-        atomicAdd(&hm[bin], exp_tang((double)(v[t] - ref), etbl));
+        if constexpr (kCount)
+            atomicAdd(&hm[bin], cv.vec || cv.index32(t) < (uint32_t)N ? 1.0 : 0.0);
+        else
+            atomicAdd(&hm[bin], exp_tang((double)(v[t] - ref), etbl));
     }
     if (blk != 0 && threadIdx.x == 0 && !((uint32_t)rdy == kCtrTag && (rdy >> 32) >= 1))
         wait_row_ready(P.rows[r], 1u);
@@ -298,6 +313,7 @@ __device__ void hist_body(const float (&v)[kSelPerThread], int64_t r, int blk, S
     }
 }
 
+template <bool kCount>
 __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__restrict__ scores,
                                                                int N, SelPtrs P)
 {
@@ -305,9 +321,10 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
     const int64_t r = blockIdx.y;
     const int blk = blockIdx.x;
     float v[kSelPerThread];
-    load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);  // missing: -inf
+    const ChunkView cv =
+        load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);  // missing: -inf
     if (blk == 0) clear_row(P, r);
-    hist_body(v, r, blk, P, S.hm, S.etbl, S.red);
+    hist_body<kCount>(v, cv, N, r, blk, P, S.hm, S.etbl, S.red);
     // Every block of the row has passed its wait once all have counted
     // themselves here, so the last one resets `ready` for the next call.
     if (threadIdx.x == 0 &&
@@ -318,6 +335,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
 // --------------------------------------------------------------- emit
 
 struct ResShared;
+template <bool kCount>
 __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
                             uint32_t *kbr, ResShared &S);
 
@@ -375,8 +393,9 @@ static_assert(sizeof(double) * kBins1 <= sizeof(uint2) * kResCap, "pick histogra
 // top of chunk tid (when tid < nblk).  Leaves M, T, j1 and A in S.
 constexpr int kPickPer = kBins1 / kSelThreads;  // bins per thread
 
-__device__ void pick_block(const ChunkTop *tops, int nblk, float p, const double (&gmv)[kPickPer],
-                           float tm0, double tmass0, ResShared &S)
+template <bool kCount>
+__device__ void pick_block(const ChunkTop *tops, int nblk, double target,
+                           const double (&gmv)[kPickPer], float tm0, double tmass0, ResShared &S)
 {
     double *hm = reinterpret_cast<double *>(&S.buf[0][0]);
     const int tid = threadIdx.x;
@@ -393,14 +412,15 @@ __device__ void pick_block(const ChunkTop *tops, int nblk, float p, const double
 #pragma unroll
     for (int k = 0; k < kPickPer; ++k) {
         const int i = tid + k * kSelThreads;
-        hm[i] = gmv[k] > 0.0 ? gmv[k] * exp_tang((double)bin_top(i) - M, S.etbl) : 0.0;
+        hm[i] = gmv[k] > 0.0 ? gmv[k] * weight<kCount>((double)bin_top(i) - M, S.etbl) : 0.0;
     }
     __syncthreads();
     if (tid < nblk)
-        atomicAdd(&hm[score_key(tm0) >> kShift1], tmass0 * exp_tang((double)tm0 - M, S.etbl));
+        atomicAdd(&hm[score_key(tm0) >> kShift1], tmass0 * weight<kCount>((double)tm0 - M, S.etbl));
     for (int k = tid + kSelThreads; k < nblk; k += kSelThreads) {
         const float tm = tops[k].m;
-        atomicAdd(&hm[score_key(tm) >> kShift1], tops[k].mass * exp_tang((double)tm - M, S.etbl));
+        atomicAdd(&hm[score_key(tm) >> kShift1],
+                  tops[k].mass * weight<kCount>((double)tm - M, S.etbl));
     }
     __syncthreads();
 
@@ -416,7 +436,8 @@ __device__ void pick_block(const ChunkTop *tops, int nblk, float p, const double
     }
     double Z;
     const double before = block_exclusive_scan<kSelThreads, double, false>(local, S.dscan, &Z);
-    const double T = (double)p * Z;
+    // top-p: p * Z; top-k: k (Z is then the row's token count).
+    const double T = kCount ? target : target * Z;
     // The boundary is the highest bin with mass whose running sum (every bin
     // down to and including it) reaches T; each thread tests its own bins,
     // so no rounding of the block prefix can skip it.  If the total stays
@@ -606,7 +627,7 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
 // With acc_next, the moved candidates' histogram over key bits [9:0]
 // (mass exp(s - M) and count) is built in S.hm / S.hc on the way, for the
 // next score level.
-template <bool kGlobal>
+template <bool kGlobal, bool kCount>
 __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int shift,
                                    uint32_t mask, uint32_t j, bool emit_above, bool by_index,
                                    int32_t *ir, uint32_t *kbr, ResShared &S,
@@ -656,7 +677,7 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
                 dst[pk++] = e[u];
                 if (acc_next) {
                     const uint32_t d1 = e[u].x & (uint32_t)(kDig - 1);
-                    atomicAdd(&S.hm[d1], exp_tang((double)key_score(e[u].x) - M, S.etbl));
+                    atomicAdd(&S.hm[d1], weight<kCount>((double)key_score(e[u].x) - M, S.etbl));
                     atomicAdd(&S.hc[d1], 1u);
                 }
             }
@@ -671,6 +692,7 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
 // ascending: the order of the sorted definition), the masses exp(s - M) are
 // laid out in rank order and prefix-summed from A, and the wave keeps the
 // shortest rank prefix whose running mass reaches T (all n if none does).
+template <bool kCount>
 __device__ void resolve_few(const uint2 *cr, int n, double A, double T, double M, int32_t *ir,
                             uint32_t *kbr, ResShared &S)
 {
@@ -684,7 +706,7 @@ __device__ void resolve_few(const uint2 *cr, int n, double A, double T, double M
     }
     // Only this wave uses S.hm until the block's next barrier; its LDS
     // accesses complete in program order.
-    if (v) S.hm[rank] = exp_tang((double)key_score(e.x) - M, S.etbl);
+    if (v) S.hm[rank] = weight<kCount>((double)key_score(e.x) - M, S.etbl);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     const double w = v ? S.hm[l] : 0.0;
@@ -695,6 +717,7 @@ __device__ void resolve_few(const uint2 *cr, int n, double A, double T, double M
     if (pa >= 0) keep_token(ir, pa, e.y, kbr);
 }
 
+template <bool kCount>
 __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
                             uint32_t *kbr, ResShared &S)
 {
@@ -738,7 +761,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
             for (int64_t k = tid; k < n; k += kResThreads) {
                 const uint32_t key = cand(k).x;
                 const uint32_t dg = (key >> shift) & (uint32_t)(kDig - 1);
-                atomicAdd(&S.hm[dg], exp_tang((double)key_score(key) - M, S.etbl));
+                atomicAdd(&S.hm[dg], weight<kCount>((double)key_score(key) - M, S.etbl));
                 atomicAdd(&S.hc[dg], 1u);
             }
             __syncthreads();
@@ -748,7 +771,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
         const uint32_t j = S.j;
         A = S.abefore;  // A plus the mass of the digits above j
         if (in_lds) {
-            n = res_filter_lds<false>(S.buf[cur], n, S.buf[cur ^ 1], shift, kDig - 1, j, true,
+            n = res_filter_lds<false, kCount>(S.buf[cur], n, S.buf[cur ^ 1], shift, kDig - 1, j, true,
                                       false, ir, kbr, S);
             cur ^= 1;
             cr = S.buf[cur];
@@ -758,7 +781,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
             // wave can finish them.
             few = S.hc[j] <= (uint32_t)kWave;
             next_built = level == 0 && !few;
-            n = res_filter_lds<true>(gc, n, S.buf[0], shift, kDig - 1, j, true, false, ir, kbr, S,
+            n = res_filter_lds<true, kCount>(gc, n, S.buf[0], shift, kDig - 1, j, true, false, ir, kbr, S,
                                      next_built, M);
             few = few && n <= kWave;
             in_lds = true;
@@ -770,12 +793,12 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
     }
 
     if (few) {
-        if (tid < kWave) resolve_few(cr, (int)n, A, T, M, ir, kbr, S);
+        if (tid < kWave) resolve_few<kCount>(cr, (int)n, A, T, M, ir, kbr, S);
     } else if (n > 0) {
         // Every survivor now has the same score tau.  Keep the first c of
         // them in index order: the smallest c with A + c * e_tau >= T.
         const uint32_t tau_key = cand(0).x;
-        const double e_tau = exp_tang((double)key_score(tau_key) - M, S.etbl);
+        const double e_tau = weight<kCount>((double)key_score(tau_key) - M, S.etbl);
         int64_t c = 1;
         if (A + (double)n * e_tau < T) {
             c = n;
@@ -814,12 +837,12 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
                 const uint32_t j = S.j;
                 c -= S.cbefore;
                 if (in_lds) {
-                    n = res_filter_lds<false>(S.buf[cur], n, S.buf[cur ^ 1], shift, mask, j,
+                    n = res_filter_lds<false, kCount>(S.buf[cur], n, S.buf[cur ^ 1], shift, mask, j,
                                               false, true, ir, kbr, S);
                     cur ^= 1;
                     cr = S.buf[cur];
                 } else if (S.hc[j] <= (uint32_t)kResCap) {
-                    n = res_filter_lds<true>(gc, n, S.buf[0], shift, mask, j, false, true, ir,
+                    n = res_filter_lds<true, kCount>(gc, n, S.buf[0], shift, mask, j, false, true, ir,
                                              kbr, S);
                     in_lds = true;
                     cur = 0;
@@ -863,8 +886,9 @@ __device__ __forceinline__ void pick_inputs(SelPtrs P, int64_t r, PickIn &pi)
 // pi): the row's threshold, the chunk's kept tokens and boundary-bin
 // candidates, its share of Hist2; the last chunk of the row to finish
 // resolves the boundary bin.
+template <bool kCount>
 __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, int N,
-                          SelPtrs P, int64_t r, float p, const PickIn &pi,
+                          SelPtrs P, int64_t r, double target, const PickIn &pi,
                           int32_t *__restrict__ idx, int32_t *__restrict__ count,
                           uint32_t *__restrict__ keep_bits, ResShared &S)
 {
@@ -873,7 +897,7 @@ __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, 
     int32_t *ir = idx + r * (int64_t)N;
     uint2 *cr = P.cand + r * (int64_t)N;
     if (threadIdx.x < kExpTable) S.etbl[threadIdx.x] = kExp2Tbl[threadIdx.x];
-    pick_block(P.tops + r * P.nblk, P.nblk, p, pi.gmv, pi.tm0, pi.tmass0, S);
+    pick_block<kCount>(P.tops + r * P.nblk, P.nblk, target, pi.gmv, pi.tm0, pi.tmass0, S);
     const uint32_t j1 = S.j1;
     if (threadIdx.x == 0) S.bcount = 0ull;
     S.hm[threadIdx.x] = 0.0;  // this block's share of the row's Hist2
@@ -962,7 +986,7 @@ __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, 
         for (uint32_t k = threadIdx.x; k < bc; k += kSelThreads) {
             const uint2 e = stage[k];
             const uint32_t dg = (e.x >> kShift2) & (uint32_t)(kDig - 1);
-            atomicAdd(&S.hm[dg], exp_tang((double)key_score(e.x) - M, S.etbl));
+            atomicAdd(&S.hm[dg], weight<kCount>((double)key_score(e.x) - M, S.etbl));
             atomicAdd(&S.hc[dg], 1u);
         }
     }
@@ -987,7 +1011,7 @@ __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, 
         for (uint32_t k = threadIdx.x; k < bc; k += kSelThreads) {
             const uint2 e = ld_cand(gcb + k);
             const uint32_t dg = (e.x >> kShift2) & (uint32_t)(kDig - 1);
-            atomicAdd(&S.hm[dg], exp_tang((double)key_score(e.x) - M, S.etbl));
+            atomicAdd(&S.hm[dg], weight<kCount>((double)key_score(e.x) - M, S.etbl));
             atomicAdd(&S.hc[dg], 1u);
         }
     }
@@ -1005,14 +1029,15 @@ __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, 
         S.last = atomicAdd(&P.rows[r].emit_done, 1u) == (uint32_t)(P.nblk - 1);
     __syncthreads();
     if (!S.last) return;
-    resolve_row(N, P, r, idx, count, kbr, S);
+    resolve_row<kCount>(N, P, r, idx, count, kbr, S);
     // Every block of the row has passed its waits: `ready` is reset for the
     // next call (in the two-launch selection it already is).
     if (threadIdx.x == 0) ctr_reset(&P.rows[r].ready);
 }
 
+template <bool kCount>
 __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
-    const float *__restrict__ scores, int N, SelPtrs P, float p, int32_t *__restrict__ idx,
+    const float *__restrict__ scores, int N, SelPtrs P, double target, int32_t *__restrict__ idx,
     int32_t *__restrict__ count, uint32_t *__restrict__ keep_bits)
 {
     __shared__ ResShared S;
@@ -1024,7 +1049,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
     float v[kSelPerThread];
     const ChunkView cv =
         load_chunk(scores + r * (int64_t)N, N, (int64_t)blockIdx.x * kSelChunk, v);
-    emit_body(v, cv, N, P, r, p, pi, idx, count, keep_bits, S);
+    emit_body<kCount>(v, cv, N, P, r, target, pi, idx, count, keep_bits, S);
 }
 
 // Both passes in one launch.  Block rows [0, R) are the histogram blocks,
@@ -1033,8 +1058,9 @@ __global__ __launch_bounds__(kSelThreads) void sel_emit_kernel(
 // its row's Hist1 is complete (the last histogram block of the row raises
 // `ready` to 2); it never waits for a later block, and no histogram block
 // waits for an emit block, so the launch needs no co-residency.
+template <bool kCount>
 __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(
-    const float *__restrict__ scores, int N, SelPtrs P, float p, int32_t *__restrict__ idx,
+    const float *__restrict__ scores, int N, SelPtrs P, double target, int32_t *__restrict__ idx,
     int32_t *__restrict__ count, uint32_t *__restrict__ keep_bits)
 {
     __shared__ ResShared S;
@@ -1043,10 +1069,11 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(
     if ((int)blockIdx.y < R) {
         const int64_t r = blockIdx.y;
         float v[kSelPerThread];
-        load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);
+        const ChunkView cv = load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);
         if (blk == 0) clear_row(P, r);
         static_assert(sizeof(double) * kBins1 <= sizeof(S.buf), "the histogram fits in buf");
-        hist_body(v, r, blk, P, reinterpret_cast<double *>(&S.buf[0][0]), S.etbl, S.red);
+        hist_body<kCount>(v, cv, N, r, blk, P, reinterpret_cast<double *>(&S.buf[0][0]), S.etbl,
+                          S.red);
         wait_vmem();  // this block's Hist1 adds and top record are done
         __syncthreads();
         if (threadIdx.x == 0 &&
@@ -1061,7 +1088,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(
     __syncthreads();
     PickIn pi;
     pick_inputs(P, r, pi);
-    emit_body(v, cv, N, P, r, p, pi, idx, count, keep_bits, S);
+    emit_body<kCount>(v, cv, N, P, r, target, pi, idx, count, keep_bits, S);
 }
 
 // ---------------------------------------------------------------- p >= 1
@@ -1086,25 +1113,45 @@ constexpr int64_t kMaxFusedRows = 65535;  // grid rows of one launch
 hipError_t launch_topp_hist(const float *scores, int64_t R, int N, void *ws, hipStream_t stream)
 {
     SelPtrs P = sel_ptrs(ws, R, N);
-    return launch(sel_hist_kernel, dim3((unsigned)P.nblk, (unsigned)R), dim3(kSelThreads), 0,
-                  stream, scores, N, P);
+    return launch(sel_hist_kernel<false>, dim3((unsigned)P.nblk, (unsigned)R), dim3(kSelThreads),
+                  0, stream, scores, N, P);
+}
+
+static hipError_t launch_keep_all(int64_t R, int N, int32_t *idx, int32_t *count,
+                                  uint32_t *keep_bits, hipStream_t stream)
+{
+    dim3 grid((unsigned)((N + 255) / 256), (unsigned)R);
+    return launch(sel_all_kernel, grid, dim3(256), 0, stream, N, idx, count, keep_bits);
+}
+
+// target: p for top-p (kCount false), k for top-k (kCount true).
+template <bool kCount>
+static hipError_t launch_select(const float *scores, int64_t R, int N, double target,
+                                int32_t *idx, int32_t *count, uint32_t *keep_bits, void *ws,
+                                hipStream_t stream)
+{
+    SelPtrs P = sel_ptrs(ws, R, N);
+    if (2 * R <= kMaxFusedRows)
+        return launch(sel_fused_kernel<kCount>, dim3((unsigned)P.nblk, (unsigned)(2 * R)),
+                      dim3(kSelThreads), 0, stream, scores, N, P, target, idx, count, keep_bits);
+    dim3 grid((unsigned)P.nblk, (unsigned)R);
+    RTP_TRY(launch(sel_hist_kernel<kCount>, grid, dim3(kSelThreads), 0, stream, scores, N, P));
+    return launch(sel_emit_kernel<kCount>, grid, dim3(kSelThreads), 0, stream, scores, N, P, target,
+                  idx, count, keep_bits);
 }
 
 hipError_t launch_topp_select(const float *scores, int64_t R, int N, float p, int32_t *idx,
                               int32_t *count, uint32_t *keep_bits, void *ws, hipStream_t stream)
 {
-    if (p >= 1.0f) {
-        dim3 grid((unsigned)((N + 255) / 256), (unsigned)R);
-        return launch(sel_all_kernel, grid, dim3(256), 0, stream, N, idx, count, keep_bits);
-    }
-    SelPtrs P = sel_ptrs(ws, R, N);
-    if (2 * R <= kMaxFusedRows)
-        return launch(sel_fused_kernel, dim3((unsigned)P.nblk, (unsigned)(2 * R)),
-                      dim3(kSelThreads), 0, stream, scores, N, P, p, idx, count, keep_bits);
-    dim3 grid((unsigned)P.nblk, (unsigned)R);
-    RTP_TRY(launch(sel_hist_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P));
-    return launch(sel_emit_kernel, grid, dim3(kSelThreads), 0, stream, scores, N, P, p, idx, count,
-                  keep_bits);
+    if (p >= 1.0f) return launch_keep_all(R, N, idx, count, keep_bits, stream);
+    return launch_select<false>(scores, R, N, (double)p, idx, count, keep_bits, ws, stream);
+}
+
+hipError_t launch_topk_select(const float *scores, int64_t R, int N, int k, int32_t *idx,
+                              int32_t *count, uint32_t *keep_bits, void *ws, hipStream_t stream)
+{
+    if (k >= N) return launch_keep_all(R, N, idx, count, keep_bits, stream);
+    return launch_select<true>(scores, R, N, (double)k, idx, count, keep_bits, ws, stream);
 }
 
 }  // namespace rtp

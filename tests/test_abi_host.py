@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -96,6 +96,24 @@ def test_topp_select_validation(lib):
     assert f(A, 1, 8, 1000, 0.9, A, A, None, A + 16, ws, None) == 5   # workspace alignment
     assert f(A + 2, 1, 8, 1000, 0.9, A, A, None, A, ws, None) == 5
     assert f(A, 1, 8, 1000, 0.9, A, A, A + 2, A, ws, None) == 5       # keep_bits alignment
+
+
+def test_topk_select_validation(lib):
+    # Every call below fails validation (the pointers are not device memory).
+    f = lib.rtp_topk_select
+    ws = rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 1, 8, 1000)
+    assert f(None, 1, 8, 1000, 10, A, A, None, A, ws, None) == 1
+    assert f(A, 1, 8, 1000, 10, None, A, None, A, ws, None) == 1
+    assert f(A, 1, 8, 1000, 10, A, A, None, None, ws, None) == 1
+    for k in (0, -1, -(2 ** 31)):
+        assert f(A, 1, 8, 1000, k, A, A, None, A, ws, None) == 4, k
+    assert f(A, 1, 8, 0, 10, A, A, None, A, ws, None) == 2
+    assert f(A, 0, 8, 1000, 10, A, A, None, A, ws, None) == 2
+    assert f(A, 1, 65536, 1000, 10, A, A, None, A, ws, None) == 2     # B*H above one grid
+    assert f(A, 1, 8, 1000, 10, A, A, None, A, ws - 1, None) == 6
+    assert f(A, 1, 8, 1000, 10, A, A, None, A + 16, ws, None) == 5    # workspace alignment
+    assert f(A + 2, 1, 8, 1000, 10, A, A, None, A, ws, None) == 5
+    assert f(A, 1, 8, 1000, 10, A, A, A + 2, A, ws, None) == 5        # keep_bits alignment
 
 
 def test_sparse_decode_union_validation(lib):

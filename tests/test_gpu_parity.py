@@ -236,6 +236,96 @@ def test_select_two_launch_path():
         assert v.ok, (h, v.k_gpu, v.k_oracle, v.note)
 
 
+# ------------------------------------------------------------------ top-k
+
+def _select_k(scores: np.ndarray, k: int, keep_bits=False):
+    B, H, N = scores.shape
+    sd = to_dev(scores.astype(np.float32))
+    idx = torch.full((B, H, N), -7, dtype=torch.int32, device=dev())
+    cnt = torch.full((B, H), -7, dtype=torch.int32, device=dev())
+    kb = (torch.full((B, H, rtp.keep_words(N)), -1, dtype=torch.int32, device=dev())
+          if keep_bits else None)
+    ws = torch.empty(rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, B, H, N), dtype=torch.uint8,
+                     device=dev())
+    rtp.rtp_topk_select(sd, k, idx, cnt, ws, keep_bits=kb)
+    c = cnt.cpu().numpy()
+    ix = idx.cpu().numpy()
+    sets = [[ix[b, h, :c[b, h]] for h in range(H)] for b in range(B)]
+    return sets, c, (kb.cpu().numpy() if keep_bits else None)
+
+
+def _assert_topk(scores, k, keep_bits=False):
+    sets, c, kb = _select_k(scores, k, keep_bits)
+    B, H, N = scores.shape
+    for b in range(B):
+        for h in range(H):
+            want = oracle.topk(scores[b, h], k)
+            got = sets[b][h]
+            assert c[b, h] == min(k, N), (b, h, k, c[b, h])
+            assert np.array_equal(np.sort(got), np.sort(want)), (b, h, k)
+            if kb is not None:
+                bits = np.unpackbits(kb[b, h].view(np.uint8), bitorder="little")[:N]
+                assert np.array_equal(np.flatnonzero(bits), np.sort(want)), (b, h, k)
+
+
+@pytest.mark.parametrize("N", [1, 13, 4096, 70_001])
+def test_topk_random_rows(N):
+    rng = np.random.default_rng(31 + N)
+    s = (rng.standard_normal((2, 3, N)) * rng.choice([0.5, 3.0])).astype(np.float32)
+    for k in sorted({1, 2, max(1, N // 7), max(1, N - 1), N, N + 3}):
+        _assert_topk(s, k, keep_bits=(k == 2))
+
+
+def test_topk_ties_and_signed_zeros():
+    rng = np.random.default_rng(37)
+    s = np.round(rng.standard_normal((2, 3, 50_000)) * 2).astype(np.float32)
+    s[0, 0, ::3] = -0.0
+    s[1, 2, :] = 0.0                       # one score everywhere
+    s[0, 1, rng.integers(0, 50_000, 300)] = np.float32(9.0)
+    for k in (1, 17, 64, 65, 300, 4099, 49_999):
+        _assert_topk(s, k)
+
+
+def test_topk_many_chunks_and_boundary_groups():
+    # 28 chunks of 32768 scores per row, and k falling inside groups of
+    # equal scores of either side of one wave.
+    rng = np.random.default_rng(41)
+    B, H, N = 1, 4, 900_000
+    s = (rng.standard_normal((B, H, N)) * 2).astype(np.float32)
+    s[0, 1, :] = np.round(s[0, 1, :] * 4) / 4
+    s[0, 2, rng.choice(N, 100, replace=False)] = np.float32(7.0)
+    s[0, 3, rng.choice(N, 3000, replace=False)] = np.float32(7.0)
+    for k in (50, 2048, 12_345, 123_456):
+        _assert_topk(s, k)
+
+
+def test_topk_two_launch_path():
+    rng = np.random.default_rng(43)
+    s = (rng.standard_normal((1, 40000, 96)) * 3).astype(np.float32)
+    s[0, ::3, ::5] = np.float32(1.25)
+    sets, c, _ = _select_k(s, 30)
+    assert np.all(c == 30)
+    for h in range(0, 40000, 7):
+        assert np.array_equal(np.sort(sets[0][h]), np.sort(oracle.topk(s[0, h], 30))), h
+
+
+def test_topk_at_the_top_p_budget_keeps_the_top_p_set():
+    # With k set to each row's top-p count, the two selectors keep the same
+    # tokens (top-p keeps a prefix of the same order).
+    cfg = synth.CONFIGS[2].with_(N=65536)
+    q_r, k_r = synth.layer_qr(cfg, 0), synth.layer_kr(cfg, 0)
+    s = np.stack([[oracle.scores(q_r[b, h], k_r[b, 0]) for h in range(2)] for b in range(2)])
+    sets_p, c_p = _select(s, 0.9)
+    for b in range(2):
+        for h in range(2):
+            row = np.ascontiguousarray(s[b:b + 1, h:h + 1])
+            sets_k, c_k, _ = _select_k(row, int(c_p[b, h]))
+            assert np.array_equal(np.sort(sets_k[0][0]), np.sort(sets_p[b][h])), (b, h)
+            assert np.array_equal(np.sort(sets_k[0][0]),
+                                  np.sort(oracle.topk(s[b, h], int(c_p[b, h]))))
+
+
+# -------------------------------------------------------- attention edges
 # -------------------------------------------------------- attention edges
 
 def test_sparse_single_row_is_value_row():

@@ -195,6 +195,66 @@ def test_topp_permutation_equivariance():
     assert set(perm[r2.sel].tolist()) == set(r1.sel.tolist())
 
 
+# ------------------------------------------------------------------ top-k
+
+@pytest.mark.parametrize("seed", range(8))
+def test_topk_unique_dominating_subset_by_brute_force(seed):
+    # The top-k set is the one subset of size min(k, n) in which every member
+    # beats every non-member (a larger score, or an equal score and a lower
+    # index).  Scores are rounded so that ties are common.
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(1, 10))
+    s = np.round(rng.standard_normal(n) * 2).astype(np.float32)
+    s[rng.random(n) < 0.2] = -0.0
+
+    def beats(i, j):
+        return s[i] > s[j] or (s[i] == s[j] and i < j)
+
+    for k in range(0, n + 2):
+        m = min(k, n)
+        winners = [set(c) for c in itertools.combinations(range(n), m)
+                   if all(beats(i, j) for i in c for j in range(n) if j not in c)]
+        assert len(winners) == 1, (seed, k)
+        sel = oracle.topk(s, k)
+        assert set(sel.tolist()) == winners[0]
+        assert all(beats(sel[t], sel[t + 1]) for t in range(len(sel) - 1))
+
+
+def test_topk_matches_numpy_lexsort():
+    rng = np.random.default_rng(11)
+    for n in (1, 7, 1000, 20_000):
+        s = (np.round(rng.standard_normal(n) * 8) / 4).astype(np.float32)
+        order = np.lexsort((np.arange(n), -s.astype(np.float64)))
+        for k in (1, 2, n // 3, n - 1, n, n + 5):
+            if k < 1:
+                continue
+            assert np.array_equal(oracle.topk(s, k), order[:min(k, n)]), (n, k)
+
+
+def test_topk_one_is_first_argmax_and_ties_take_low_indices():
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        s = np.round(rng.standard_normal(300)).astype(np.float32)
+        assert oracle.topk(s, 1)[0] == int(np.argmax(s))
+    z = np.zeros(100, np.float32)
+    z[::2] = -0.0
+    assert np.array_equal(np.sort(oracle.topk(z, 37)), np.arange(37))
+    assert oracle.topk(z, 0).size == 0
+
+
+def test_topk_agrees_with_topp_prefix_and_nests():
+    cfg = synth.CONFIGS[2].with_(N=8192)
+    s = oracle.scores(synth.layer_qr(cfg, 0)[0, 0], synth.layer_kr(cfg, 0)[0, 0])
+    for p in (0.5, 0.9, 0.99):
+        r = oracle.topp(s, p)
+        assert np.array_equal(oracle.topk(s, r.k), r.sel)
+    prev = set()
+    for k in (1, 10, 100, 1000, 8192):
+        cur = set(oracle.topk(s, k).tolist())
+        assert prev <= cur and len(cur) == k
+        prev = cur
+
+
 # -------------------------------------------------------------- attention
 
 def _bf16(x):
