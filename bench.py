@@ -288,8 +288,8 @@ def main():
     sparse_bytes = float(np.mean(union)) * 2 * d * 2 + sel_total * 4
     sel_bytes = B * H_r * N * 4 + sel_total * 4
     cands = {
-        "sel_emit_kernel": ("sel_emit_kernel", sel_bytes, "select.hip"),
-        "rtp_topp_hist": ("sel_hist_kernel", B * H_r * N * 4, "select.hip"),
+        "sel_emit_kernel": ("sel_emit_kernel<false>", sel_bytes, "select.hip"),
+        "rtp_topp_hist": ("sel_hist_kernel<false>", B * H_r * N * 4, "select.hip"),
         "rtp_index_scores": ("index_scores_kernel<8>", B * G_r * N * (cfg.r * 4 + cfg.G * 4),
                              "scan.hip"),
         "rtp_decode_attend": ("attend_kernel",
@@ -304,7 +304,7 @@ def main():
         "rtp_local_decode": ("attend_kernel", window_bytes, "attend.hip"),
     }
     if fused_select:
-        cands["rtp_topp_select"] = ("sel_fused_kernel", sel_bytes, "select.hip")
+        cands["rtp_topp_select"] = ("sel_fused_kernel<false>", sel_bytes, "select.hip")
     # Calls timed for reference only, outside the step: rtp_index_scores in
     # mode "scan_local" (the step runs the scan inside rtp_scan_local) and
     # rtp_topp_hist when the selection is one launch.
