@@ -202,6 +202,26 @@ def main():
     count_k = torch.empty_like(count_l[0])
     us["rtp_topk_select"] = time_call(lambda: [rtp.rtp_topk_select(
         scores_l[l], k_budget, idx_k, count_k, sl.ws_sel) for l in range(L)])
+    # Indexer projections (reference calls, not part of the step, whose q_r
+    # and k_r are given): the prefill k_r build of one retrieval KV head
+    # over all N tokens (256 B of bf16 features read, 64 B of k_r written
+    # per token, on the matrix cores), and one decode token's q_r for the
+    # H_r retrieval heads plus its k_r row appended at row N - 1.
+    xp = torch.randint(-16000, 16000, (1, 1, N, d), dtype=torch.int16, device=dev)
+    Wp = torch.randint(-16000, 16000, (G_r, 16, d), dtype=torch.int16, device=dev)
+    kr_out = torch.empty((1, 1, N, 16), dtype=torch.float32, device=dev)
+    us["rtp_index_project_prefill"] = time_call(lambda: [rtp.rtp_index_project(
+        xp, Wp[:1], kr_out) for l in range(L)])
+    qp = torch.randint(-16000, 16000, (B, Hq, 1, d), dtype=torch.int16, device=dev)
+    Wq = torch.randint(-16000, 16000, (H_r, 16, d), dtype=torch.int16, device=dev)
+    qr_out = torch.empty((B, H_r, 1, 16), dtype=torch.float32, device=dev)
+    kp = torch.randint(-16000, 16000, (B, Hkv, 1, d), dtype=torch.int16, device=dev)
+    kr_cache = torch.empty((B, G_r, N, 16), dtype=torch.float32, device=dev)
+    us["rtp_index_project_decode"] = time_call(lambda: [
+        (rtp.rtp_index_project(qp, Wq, qr_out),
+         rtp.rtp_index_project(kp, Wp, kr_cache, out_pos=N - 1)) for l in range(L)])
+    proj_gbps = N * (d * 2 + 16 * 4) / (us["rtp_index_project_prefill"] * 1e-6) / 1e9
+    del xp, kr_out, kr_cache
     # rtp_topp_select runs both passes in one launch (sel_fused_kernel) when
     # its histogram and emit block rows fit one grid (2 * B * H_r <= 65535);
     # rtp_topp_hist, the histogram pass alone, is then timed for reference
@@ -345,6 +365,7 @@ def main():
         "union_rows_per_layer_mean": float(np.mean(union)),
         "per_call_us_per_layer": {k: round(v, 2) for k, v in us.items()},
         "topk_budget": k_budget,
+        "project_prefill_GBps": round(proj_gbps, 1),
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
         "cpu_baseline": cpu,
     }

@@ -82,6 +82,38 @@ rtp_status rtp_index_scores(const float *q_r, const float *k_r, float *scores,
                             int64_t kr_cap, int32_t r, void *stream);
 
 /*
+ * rtp_index_project -- the indexer's low-dim projection of query or key
+ * features taken before RoPE (gist.science summary, method section 2: a
+ * 16-dim projector applied to queries and keys before RoPE), for one decode
+ * token (q_r of the retrieval heads, or the new k_r row appended to the
+ * indexer key cache) or a whole prefill (the k_r cache of T tokens).
+ *
+ *   out[b][h][out_pos + t][j] = sum_{c < d} W[h][j][c] * x[b][head_begin + h][t][c]
+ *
+ * for t < T, j < r, h < H.  Each bf16 product is exact in fp32 and the sum
+ * is accumulated in fp32 on the matrix cores, in an unspecified order: the
+ * result is within 2 * d * 2^-24 * sum_c |W[h][j][c] * x[..][c]| of the
+ * exact sum, and the same inputs always give the same bits (a token's row
+ * does not depend on T or on the other tokens).
+ *
+ *   x        bf16 [B][Hx][x_cap][d]   16-B aligned; rows [0, T) of heads
+ *                                     [head_begin, head_begin + H) are read
+ *   W        bf16 [H][r][d]           16-B aligned; one projector per head
+ *   out      fp32 [B][H][out_cap][r]  4-B aligned; rows [out_pos,
+ *                                     out_pos + T) written, the rest untouched
+ *   d must be 128 and r must be 16; 1 <= T <= x_cap;
+ *   0 <= out_pos <= out_cap - T; 0 <= head_begin <= Hx - H; B*H <= 65535.
+ *
+ * Errors: RTP_ERR_NULL, RTP_ERR_UNSUPPORTED (d or r), RTP_ERR_SHAPE,
+ * RTP_ERR_ALIGN.
+ */
+rtp_status rtp_index_project(const rtp_bf16 *x, int32_t B, int32_t Hx,
+                             int64_t x_cap, int32_t head_begin, int32_t H,
+                             int32_t T, int32_t d, const rtp_bf16 *W,
+                             int32_t r, float *out, int64_t out_cap,
+                             int64_t out_pos, void *stream);
+
+/*
  * rtp_topp_select -- dynamic top-p token selection per head (gist.science
  * summary, method section 3: the low-dim attention mass is summed, largest
  * first, until it reaches p; section 5: the threshold is found with a

@@ -48,6 +48,8 @@ def _load():
         lib.orc_scores.restype = None
         lib.orc_topp.argtypes = [P, I64, ctypes.c_float, P, P]
         lib.orc_topp.restype = I64
+        lib.orc_project.argtypes = [P, I64, I64, P, I64, P]
+        lib.orc_project.restype = None
         lib.orc_topk.argtypes = [P, I64, I64, P]
         lib.orc_topk.restype = I64
         lib.orc_set_mass.argtypes = [P, I64, P, I64]
@@ -116,6 +118,20 @@ def topk(s: np.ndarray, k: int) -> np.ndarray:
     if c < 0:
         raise MemoryError("oracle top-k: out of memory")
     return sel[:c].copy()
+
+
+def project(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """fp64 projection of bf16 rows: x uint16 [T][d], W uint16 [r][d] (bf16
+    bit patterns) -> float64 [T][r] with out[t][j] = sum_c W[j][c] x[t][c]."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    T, d = x.shape
+    r, dw = W.shape
+    if dw != d:
+        raise ValueError("x and W disagree in d")
+    out = np.empty((T, r), np.float64)
+    _load().orc_project(_ptr(x), T, d, _ptr(W), r, _ptr(out))
+    return out
 
 
 def set_mass(s: np.ndarray, members) -> float:

@@ -32,6 +32,12 @@
  *                      scores, in the same order as orc_topp (the pages give
  *                      no tie rule for either; ties go to the lower index).
  *                      k >= N keeps all.
+ *   orc_project     -- the indexer's low-dim projection of pre-RoPE query or
+ *                      key features (summary section 2: a 16-dim projector
+ *                      before RoPE): out[t][j] = sum_c W[j][c] * x[t][c] for
+ *                      bf16 W [r][d] and x [T][d], every product and the
+ *                      sum in fp64, c = 0..d-1 in order (the pages fix no
+ *                      precision; fp64 stands in for the exact sum).
  *   orc_attention   -- exact softmax attention of one query row over a given
  *                      set of cached rows, in fp64 (arXiv abstract: sparse
  *                      attention over the indexer's tokens; summary
@@ -195,6 +201,19 @@ int64_t orc_topk(const float *s, int64_t N, int64_t k, int64_t *sel)
         sel[t] = order[t].i;
     free(order);
     return n;
+}
+
+/* out[t][j] = sum_c W[j][c] * x[t][c] in fp64, for t < T, j < r. */
+void orc_project(const uint16_t *x, int64_t T, int64_t d, const uint16_t *W, int64_t r,
+                 double *out)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                acc += bf16_value(W[j * d + c]) * bf16_value(x[t * d + c]);
+            out[t * r + j] = acc;
+        }
 }
 
 /* Mass of an arbitrary set of tokens, as a fraction of Z (O2 definitions).

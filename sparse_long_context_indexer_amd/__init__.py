@@ -25,7 +25,7 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPP
           4: "RTP_ERR_VALUE", 5: "RTP_ERR_ALIGN", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
 
 # Every symbol include/rtp.h declares.
-SYMBOLS = ("rtp_index_scores", "rtp_topp_select", "rtp_topk_select", "rtp_topp_hist",
+SYMBOLS = ("rtp_index_scores", "rtp_index_project", "rtp_topp_select", "rtp_topk_select", "rtp_topp_hist",
            "rtp_sparse_decode", "rtp_sparse_decode_union", "rtp_local_decode",
            "rtp_decode_attend", "rtp_scan_local", "rtp_workspace_size", "rtp_status_string",
            "rtp_last_hip_error")
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.rtp_index_scores.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, P]
         L.rtp_topp_select.argtypes = [P, I32, I32, I32, F32, P, P, P, P, SZ, P]
         L.rtp_topk_select.argtypes = [P, I32, I32, I32, I32, P, P, P, P, SZ, P]
+        L.rtp_index_project.argtypes = [P, I32, I32, I64, I32, I32, I32, I32, P, I32, P, I64,
+                                        I64, P]
         L.rtp_topp_hist.argtypes = [P, I32, I32, I32, P, SZ, P]
         L.rtp_sparse_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32,
                                         I32, I32, F32, P, P, SZ, P]
@@ -75,7 +77,7 @@ def lib() -> ctypes.CDLL:
         L.rtp_status_string.restype = ctypes.c_char_p
         L.rtp_last_hip_error.argtypes = []
         L.rtp_last_hip_error.restype = I32
-        for name in SYMBOLS[:10]:
+        for name in SYMBOLS[:11]:
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -161,6 +163,25 @@ def rtp_topp_select(scores, p, idx, count, workspace, keep_bits=None, stream=Non
         _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2), kb,
         _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
         _stream(scores, stream)), "rtp_topp_select")
+
+
+def rtp_index_project(x, W, out, head_begin=0, T=None, out_pos=0, stream=None) -> None:
+    """x bf16 [B][Hx][x_cap][128]; W bf16 [H][16][128] (one projector per
+    head); out f32 [B][H][out_cap][16]: rows [out_pos, out_pos + T) of out
+    get W[h] x for x rows [0, T) of heads [head_begin, head_begin + H)
+    (T defaults to x_cap)."""
+    import torch
+    if x.dim() != 4 or W.dim() != 3 or out.dim() != 4:
+        raise ValueError("x and out must be 4-D, W 3-D")
+    B, Hx, x_cap, d = x.shape
+    H, r, dw = W.shape
+    if dw != d or tuple(out.shape[:2]) != (B, H) or out.shape[3] != r:
+        raise ValueError("x, W and out disagree in shape")
+    T = x_cap if T is None else T
+    _check(lib().rtp_index_project(
+        _bf16(x, "x", 4), B, Hx, x_cap, head_begin, H, T, d,
+        _bf16(W, "W", 3), r, _dev(out, torch.float32, "out", 4), out.shape[2],
+        out_pos, _stream(x, stream)), "rtp_index_project")
 
 
 def rtp_topk_select(scores, k, idx, count, workspace, keep_bits=None, stream=None) -> None:

@@ -109,6 +109,22 @@ rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H, int32_t N,
                                             as_stream(stream)));
 }
 
+rtp_status rtp_index_project(const rtp_bf16 *x, int32_t B, int32_t Hx, int64_t x_cap,
+                             int32_t head_begin, int32_t H, int32_t T, int32_t d,
+                             const rtp_bf16 *W, int32_t r, float *out, int64_t out_cap,
+                             int64_t out_pos, void *stream)
+{
+    if (!x || !W || !out) return RTP_ERR_NULL;
+    if (d != 128 || r != 16) return RTP_ERR_UNSUPPORTED;
+    if (B < 1 || Hx < 1 || H < 1 || T < 1 || head_begin < 0 || head_begin > Hx - H ||
+        x_cap < T || out_pos < 0 || out_cap < T || out_pos > out_cap - T ||
+        (int64_t)B * H > kMaxGridY)
+        return RTP_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(out, 4)) return RTP_ERR_ALIGN;
+    return from_hip(rtp::launch_index_project(x, B, Hx, x_cap, head_begin, H, T, W, out, out_cap,
+                                              out_pos, as_stream(stream)));
+}
+
 rtp_status rtp_topk_select(const float *scores, int32_t B, int32_t H, int32_t N, int32_t k,
                            int32_t *idx, int32_t *count, uint32_t *keep_bits, void *workspace,
                            size_t ws_bytes, void *stream)

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -96,6 +96,27 @@ def test_topp_select_validation(lib):
     assert f(A, 1, 8, 1000, 0.9, A, A, None, A + 16, ws, None) == 5   # workspace alignment
     assert f(A + 2, 1, 8, 1000, 0.9, A, A, None, A, ws, None) == 5
     assert f(A, 1, 8, 1000, 0.9, A, A, A + 2, A, ws, None) == 5       # keep_bits alignment
+
+
+def test_index_project_validation(lib):
+    # Every call below fails validation (the pointers are not device memory).
+    f = lib.rtp_index_project
+    base = [A, 2, 5, 100, 1, 3, 50, 128, A, 16, A, 200, 10, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(0, None) == 1 and call(8, None) == 1 and call(10, None) == 1
+    assert call(7, 64) == 3 and call(9, 8) == 3        # d, r
+    assert call(1, 0) == 2 and call(2, 0) == 2 and call(5, 0) == 2 and call(6, 0) == 2
+    assert call(3, 49) == 2                              # x_cap < T
+    assert call(4, -1) == 2 and call(4, 3) == 2          # head range outside Hx
+    assert call(12, -1) == 2 and call(12, 151) == 2      # out rows past out_cap
+    assert call(11, 49) == 2
+    assert call(1, 30000) == 2                           # B*H above one grid
+    assert call(0, A + 8) == 5 and call(8, A + 8) == 5 and call(10, A + 2) == 5
 
 
 def test_topk_select_validation(lib):

@@ -236,6 +236,82 @@ def test_select_two_launch_path():
         assert v.ok, (h, v.k_gpu, v.k_oracle, v.note)
 
 
+# -------------------------------------------------------------- projection
+
+# fp32 accumulation of d exact products in any order: the error stays within
+# d * 2u * sum |terms| (u = 2^-24; 2u also covers a truncating adder).
+PROJ_REL = 2 * 128 * 2.0 ** -24
+
+
+def _proj_inputs(B, Hx, x_cap, H, seed):
+    x = synth.normal_bf16(synth.key(seed, 1), 0, B * Hx * x_cap * 128).reshape(B, Hx, x_cap, 128)
+    W = synth.bf16_to_f32(synth.normal_bf16(synth.key(seed, 2), 0, H * 16 * 128)) / 16.0
+    return x, synth.f32_to_bf16(W).reshape(H, 16, 128)   # W / 16 is exact in bf16
+
+
+def _proj_gpu(x, W, out_cap, hb, T, pos, sentinel=-3.5):
+    B, Hx, x_cap, _ = x.shape
+    H = W.shape[0]
+    out = torch.full((B, H, out_cap, 16), sentinel, dtype=torch.float32, device=dev())
+    rtp.rtp_index_project(torch.from_numpy(x.view(np.int16)).to(dev()),
+                          torch.from_numpy(W.view(np.int16)).to(dev()), out,
+                          head_begin=hb, T=T, out_pos=pos)
+    return out.cpu().numpy()
+
+
+def _assert_proj(x, W, got, hb, T, pos, sentinel=-3.5):
+    B, H = got.shape[:2]
+    xf = synth.bf16_to_f32(x).astype(np.float64)
+    Wf = synth.bf16_to_f32(W).astype(np.float64)
+    for b in range(B):
+        for h in range(H):
+            want = oracle.project(x[b, hb + h, :T], W[h])
+            bound = PROJ_REL * (np.abs(xf[b, hb + h, :T]) @ np.abs(Wf[h]).T) + 1e-30
+            rows = got[b, h, pos:pos + T].astype(np.float64)
+            assert np.all(np.abs(rows - want) <= bound), (b, h, np.max(np.abs(rows - want) / bound))
+            assert np.all(got[b, h, :pos] == sentinel) and np.all(got[b, h, pos + T:] == sentinel)
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 255, 256, 257, 4097])
+def test_project_shapes(T):
+    # Heads 1..3 of 5, caches wider than T, rows written at an offset.
+    x, W = _proj_inputs(2, 5, T + 3, 3, 60 + T)
+    for pos in (0, 7):
+        got = _proj_gpu(x, W, T + 9, 1, T, pos)
+        _assert_proj(x, W, got, 1, T, pos)
+
+
+def test_project_append_matches_prefill_bits():
+    # The k_r row of token n is the same whether it is projected within a
+    # prefill of n + 1 tokens or appended alone at row n, and q_r of decode
+    # heads takes the same path with one-row caches.
+    n = 1000
+    x, W = _proj_inputs(2, 4, n + 1, 2, 70)
+    full = _proj_gpu(x, W, n + 1, 2, n + 1, 0)
+    head = _proj_gpu(np.ascontiguousarray(x[:, :, :n]), W, n + 1, 2, n, 0, sentinel=0.0)
+    last = _proj_gpu(np.ascontiguousarray(x[:, :, n:n + 1]), W, n + 1, 2, 1, n, sentinel=0.0)
+    assert np.array_equal(full[:, :, :n], head[:, :, :n])
+    assert np.array_equal(full[:, :, n], last[:, :, n])
+    _assert_proj(x, W, full, 2, n + 1, 0)
+    q, Wq = _proj_inputs(1, 32, 1, 8, 71)            # 8 retrieval query heads of 32
+    _assert_proj(q, Wq, _proj_gpu(q, Wq, 1, 0, 1, 0), 0, 1, 0)
+
+
+def test_project_prefill_1m_sampled():
+    # The prefill k_r build at 2^20 tokens (one KV head), checked on sampled
+    # rows; the whole output is checked finite and the rows past T untouched.
+    N = 1 << 20
+    x, W = _proj_inputs(1, 1, N, 1, 72)
+    got = _proj_gpu(x, W, N + 5, 0, N, 0)
+    assert np.all(got[0, 0, N:] == -3.5) and np.all(np.isfinite(got[0, 0, :N]))
+    rows = np.concatenate([np.arange(32), np.random.default_rng(73).choice(N, 4000), N - 32 + np.arange(32)])
+    want = oracle.project(x[0, 0, rows], W[0])
+    bound = PROJ_REL * (np.abs(synth.bf16_to_f32(x[0, 0, rows]).astype(np.float64))
+                        @ np.abs(synth.bf16_to_f32(W[0]).astype(np.float64)).T) + 1e-30
+    assert np.all(np.abs(got[0, 0, rows].astype(np.float64) - want) <= bound)
+
+
+# ------------------------------------------------------------------ top-k
 # ------------------------------------------------------------------ top-k
 
 def _select_k(scores: np.ndarray, k: int, keep_bits=False):

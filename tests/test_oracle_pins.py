@@ -195,6 +195,45 @@ def test_topp_permutation_equivariance():
     assert set(perm[r2.sel].tolist()) == set(r1.sel.tolist())
 
 
+# -------------------------------------------------------------- projection
+
+def _bf16_of(v):
+    return synth.f32_to_bf16(np.asarray(v, np.float32))
+
+
+def test_project_selector_rows_copy_dims():
+    # A projector whose row j is the unit vector e_{perm[j]} copies those
+    # dims of every token row.
+    rng = np.random.default_rng(50)
+    x = synth.normal_bf16(synth.key(50, 1), 0, 37 * 128).reshape(37, 128)
+    perm = rng.choice(128, 16, replace=False)
+    W = np.zeros((16, 128), np.float32)
+    W[np.arange(16), perm] = 1.0
+    out = oracle.project(x, _bf16_of(W))
+    assert np.array_equal(out, synth.bf16_to_f32(x)[:, perm].astype(np.float64))
+
+
+def test_project_closed_form_and_transposition():
+    # x all ones, W[j][c] = (j - 7) / 8 (exact in bf16): out[t][j] = 16 (j - 7).
+    x = _bf16_of(np.ones((5, 128)))
+    W = _bf16_of(np.repeat(((np.arange(16) - 7) / 8.0)[:, None], 128, axis=1))
+    assert np.array_equal(oracle.project(x, W), np.tile(16.0 * (np.arange(16) - 7), (5, 1)))
+    # W[j][c] = c-dependent, x[t] = e_t: out[t][j] = W[j][t] (catches a
+    # transposed operand).
+    Wv = _bf16_of((np.arange(16 * 128).reshape(16, 128) % 29) - 14)
+    e = np.zeros((128, 128), np.float32)
+    e[np.arange(128), np.arange(128)] = 1.0
+    assert np.array_equal(oracle.project(_bf16_of(e), Wv), synth.bf16_to_f32(Wv).T.astype(np.float64))
+
+
+def test_project_matches_numpy_matmul_fp64():
+    x = synth.normal_bf16(synth.key(51, 1), 0, 300 * 128).reshape(300, 128)
+    W = synth.normal_bf16(synth.key(51, 2), 0, 16 * 128).reshape(16, 128)
+    ref = synth.bf16_to_f32(x).astype(np.float64) @ synth.bf16_to_f32(W).astype(np.float64).T
+    got = oracle.project(x, W)
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
 # ------------------------------------------------------------------ top-k
 
 @pytest.mark.parametrize("seed", range(8))
