@@ -202,20 +202,28 @@ def main():
     count_k = torch.empty_like(count_l[0])
     us["rtp_topk_select"] = time_call(lambda: [rtp.rtp_topk_select(
         scores_l[l], k_budget, idx_k, count_k, sl.ws_sel) for l in range(L)])
+    # The scan over a bf16 copy of the indexer key cache (32 B per token
+    # instead of 64), a reference call: the step scans the fp32 cache.
+    kr_b = kr_all.to(torch.bfloat16).view(torch.int16)
+    us["rtp_index_scores_bf16"] = time_call(lambda: [rtp.rtp_index_scores_bf16(
+        qr_all[l], kr_b[l % kr_b.shape[0]], scores_l[l]) for l in range(L)])
+    del kr_b
     # Indexer projections (reference calls, not part of the step, whose q_r
     # and k_r are given): the prefill k_r build of one retrieval KV head
     # over all N tokens (256 B of bf16 features read, 64 B of k_r written
     # per token, on the matrix cores), and one decode token's q_r for the
     # H_r retrieval heads plus its k_r row appended at row N - 1.
-    xp = torch.randint(-16000, 16000, (1, 1, N, d), dtype=torch.int16, device=dev)
-    Wp = torch.randint(-16000, 16000, (G_r, 16, d), dtype=torch.int16, device=dev)
+    def bf16_bits(*shape):  # N(0,1) values as bf16 bit patterns
+        return torch.randn(shape, dtype=torch.bfloat16, device=dev).view(torch.int16)
+    xp = bf16_bits(1, 1, N, d)
+    Wp = bf16_bits(G_r, 16, d)
     kr_out = torch.empty((1, 1, N, 16), dtype=torch.float32, device=dev)
     us["rtp_index_project_prefill"] = time_call(lambda: [rtp.rtp_index_project(
         xp, Wp[:1], kr_out) for l in range(L)])
-    qp = torch.randint(-16000, 16000, (B, Hq, 1, d), dtype=torch.int16, device=dev)
-    Wq = torch.randint(-16000, 16000, (H_r, 16, d), dtype=torch.int16, device=dev)
+    qp = bf16_bits(B, Hq, 1, d)
+    Wq = bf16_bits(H_r, 16, d)
     qr_out = torch.empty((B, H_r, 1, 16), dtype=torch.float32, device=dev)
-    kp = torch.randint(-16000, 16000, (B, Hkv, 1, d), dtype=torch.int16, device=dev)
+    kp = bf16_bits(B, Hkv, 1, d)
     kr_cache = torch.empty((B, G_r, N, 16), dtype=torch.float32, device=dev)
     us["rtp_index_project_decode"] = time_call(lambda: [
         (rtp.rtp_index_project(qp, Wq, qr_out),

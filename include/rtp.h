@@ -82,6 +82,23 @@ rtp_status rtp_index_scores(const float *q_r, const float *k_r, float *scores,
                             int64_t kr_cap, int32_t r, void *stream);
 
 /*
+ * rtp_index_scores_bf16 -- rtp_index_scores over an indexer key cache stored
+ * in bf16 (32 B per token instead of 64: the scan reads half the bytes).
+ * Each bf16 element is widened exactly to fp32 and the score is then the
+ * same fp32 fused multiply-add chain as rtp_index_scores, so it is
+ * bit-exact to rtp_index_scores run on the widened cache.
+ *
+ *   q_r     fp32 [B][Hq_r][r]          16-B aligned
+ *   k_r     bf16 [B][Hkv_r][kr_cap][r] 16-B aligned
+ *   scores  fp32 [B][Hq_r][N]          out, 4-B aligned
+ *   The same sizes and errors as rtp_index_scores.
+ */
+rtp_status rtp_index_scores_bf16(const float *q_r, const rtp_bf16 *k_r,
+                                 float *scores, int32_t B, int32_t Hq_r,
+                                 int32_t Hkv_r, int32_t N, int64_t kr_cap,
+                                 int32_t r, void *stream);
+
+/*
  * rtp_index_project -- the indexer's low-dim projection of query or key
  * features taken before RoPE (gist.science summary, method section 2: a
  * 16-dim projector applied to queries and keys before RoPE), for one decode

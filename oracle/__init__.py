@@ -46,6 +46,8 @@ def _load():
         I64 = ctypes.c_int64
         lib.orc_scores.argtypes = [P, P, I64, P]
         lib.orc_scores.restype = None
+        lib.orc_scores_bf16.argtypes = [P, P, I64, P]
+        lib.orc_scores_bf16.restype = None
         lib.orc_topp.argtypes = [P, I64, ctypes.c_float, P, P]
         lib.orc_topp.restype = I64
         lib.orc_project.argtypes = [P, I64, I64, P, I64, P]
@@ -91,6 +93,16 @@ def scores(q_r: np.ndarray, k_r: np.ndarray) -> np.ndarray:
     k = np.ascontiguousarray(k_r, dtype=np.float32).reshape(-1, 16)
     out = np.empty(k.shape[0], dtype=np.float32)
     _load().orc_scores(_ptr(q), _ptr(k), k.shape[0], _ptr(out))
+    return out
+
+
+def scores_bf16(q_r: np.ndarray, k_bits: np.ndarray) -> np.ndarray:
+    """Indexer scores of one query head over [N][16] bf16 keys (uint16 bit
+    patterns, widened to fp32)."""
+    q = np.ascontiguousarray(q_r, dtype=np.float32).reshape(16)
+    k = np.ascontiguousarray(k_bits, dtype=np.uint16).reshape(-1, 16)
+    out = np.empty(k.shape[0], dtype=np.float32)
+    _load().orc_scores_bf16(_ptr(q), _ptr(k), k.shape[0], _ptr(out))
     return out
 
 

@@ -19,6 +19,9 @@
  *                      no formula; the score is the plain dot product
  *                      q_r . k_r in fp32, accumulated as one fused
  *                      multiply-add per dimension, dimensions 0..15 in order.
+ *   orc_scores_bf16 -- orc_scores over bf16 indexer keys, each widened
+ *                      exactly to fp32 first (a storage variant of the same
+ *                      definition, halving the key bytes).
  *   orc_topp        -- dynamic top-p selection: accumulate low-dimensional
  *                      attention mass, largest first, until the cumulative
  *                      mass reaches p (gist.science summary, method
@@ -88,6 +91,20 @@ void orc_scores(const float *q, const float *k, int64_t N, float *s)
         float acc = 0.0f;
         for (int j = 0; j < 16; ++j)
             acc = fmaf(q[j], row[j], acc);
+        if (acc == 0.0f)
+            acc = 0.0f; /* -0 becomes +0 */
+        s[i] = acc;
+    }
+}
+
+/* The same scores from bf16 keys (bit patterns), widened to fp32. */
+void orc_scores_bf16(const float *q, const uint16_t *k, int64_t N, float *s)
+{
+    for (int64_t i = 0; i < N; ++i) {
+        const uint16_t *row = k + i * 16;
+        float acc = 0.0f;
+        for (int j = 0; j < 16; ++j)
+            acc = fmaf(q[j], (float)bf16_value(row[j]), acc);
         if (acc == 0.0f)
             acc = 0.0f; /* -0 becomes +0 */
         s[i] = acc;

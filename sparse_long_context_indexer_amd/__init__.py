@@ -25,7 +25,7 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPP
           4: "RTP_ERR_VALUE", 5: "RTP_ERR_ALIGN", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
 
 # Every symbol include/rtp.h declares.
-SYMBOLS = ("rtp_index_scores", "rtp_index_project", "rtp_topp_select", "rtp_topk_select", "rtp_topp_hist",
+SYMBOLS = ("rtp_index_scores", "rtp_index_scores_bf16", "rtp_index_project", "rtp_topp_select", "rtp_topk_select", "rtp_topp_hist",
            "rtp_sparse_decode", "rtp_sparse_decode_union", "rtp_local_decode",
            "rtp_decode_attend", "rtp_scan_local", "rtp_workspace_size", "rtp_status_string",
            "rtp_last_hip_error")
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                 ctypes.c_float, ctypes.c_size_t)
         L.rtp_index_scores.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, P]
+        L.rtp_index_scores_bf16.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, P]
         L.rtp_topp_select.argtypes = [P, I32, I32, I32, F32, P, P, P, P, SZ, P]
         L.rtp_topk_select.argtypes = [P, I32, I32, I32, I32, P, P, P, P, SZ, P]
         L.rtp_index_project.argtypes = [P, I32, I32, I64, I32, I32, I32, I32, P, I32, P, I64,
@@ -77,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.rtp_status_string.restype = ctypes.c_char_p
         L.rtp_last_hip_error.argtypes = []
         L.rtp_last_hip_error.restype = I32
-        for name in SYMBOLS[:11]:
+        for name in SYMBOLS[:12]:
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -140,6 +141,19 @@ def rtp_index_scores(q_r, k_r, scores, stream=None) -> None:
         _dev(q_r, torch.float32, "q_r", 3), _dev(k_r, torch.float32, "k_r", 4),
         _dev(scores, torch.float32, "scores", 3), B, Hq_r, Hkv_r, N, cap, r,
         _stream(q_r, stream)), "rtp_index_scores")
+
+
+def rtp_index_scores_bf16(q_r, k_r, scores, stream=None) -> None:
+    """rtp_index_scores over a bf16 k_r cache: k_r bf16 [B][Hkv_r][cap][16]
+    (torch.bfloat16 or its int16 bit patterns)."""
+    import torch
+    B, Hq_r, r = q_r.shape
+    _, Hkv_r, cap, _ = k_r.shape
+    N = scores.shape[-1]
+    _check(lib().rtp_index_scores_bf16(
+        _dev(q_r, torch.float32, "q_r", 3), _bf16(k_r, "k_r", 4),
+        _dev(scores, torch.float32, "scores", 3), B, Hq_r, Hkv_r, N, cap, r,
+        _stream(q_r, stream)), "rtp_index_scores_bf16")
 
 
 def keep_words(N: int) -> int:

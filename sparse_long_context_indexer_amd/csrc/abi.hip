@@ -93,6 +93,21 @@ rtp_status rtp_index_scores(const float *q_r, const float *k_r, float *scores, i
                                              as_stream(stream)));
 }
 
+rtp_status rtp_index_scores_bf16(const float *q_r, const rtp_bf16 *k_r, float *scores,
+                                 int32_t B, int32_t Hq_r, int32_t Hkv_r, int32_t N,
+                                 int64_t kr_cap, int32_t r, void *stream)
+{
+    if (!q_r || !k_r || !scores) return RTP_ERR_NULL;
+    if (r != 16) return RTP_ERR_UNSUPPORTED;
+    if (B < 1 || Hq_r < 1 || Hkv_r < 1 || Hq_r % Hkv_r != 0 || N < 1 || kr_cap < N)
+        return RTP_ERR_SHAPE;
+    const int64_t group = Hq_r / Hkv_r;
+    if ((int64_t)B * Hkv_r * ((group + 7) / 8) > kMaxGridY) return RTP_ERR_SHAPE;
+    if (!aligned(q_r, 16) || !aligned(k_r, 16) || !aligned(scores, 4)) return RTP_ERR_ALIGN;
+    return from_hip(rtp::launch_index_scores_bf16(q_r, k_r, scores, B, Hq_r, Hkv_r, N, kr_cap,
+                                                  as_stream(stream)));
+}
+
 rtp_status rtp_topp_select(const float *scores, int32_t B, int32_t H, int32_t N, float p,
                            int32_t *idx, int32_t *count, uint32_t *keep_bits, void *workspace,
                            size_t ws_bytes, void *stream)

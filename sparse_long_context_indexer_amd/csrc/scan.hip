@@ -9,14 +9,32 @@ namespace rtp {
 
 constexpr int kScanTPT = 2;  // tokens per thread
 
-template <int G>
+template <int G, bool kBf16 = false>
 __global__ __launch_bounds__(kScanThreads) void index_scores_kernel(
-    const float *__restrict__ q_r, const float *__restrict__ k_r,
+    const float *__restrict__ q_r, const void *__restrict__ k_r,
     float *__restrict__ scores, int N, int64_t kr_cap, int Hq_r, int Hkv_r,
     int group, int head_chunks)
 {
-    scan_tile<G, kScanTPT>(q_r, k_r, scores, N, kr_cap, Hq_r, Hkv_r, group, head_chunks,
-                           blockIdx.x, blockIdx.y);
+    scan_tile<G, kScanTPT, kBf16>(q_r, k_r, scores, N, kr_cap, Hq_r, Hkv_r, group, head_chunks,
+                                  blockIdx.x, blockIdx.y);
+}
+
+// The scan over bf16 k_r rows (32 B per token instead of 64).
+hipError_t launch_index_scores_bf16(const float *q_r, const uint16_t *k_r, float *scores,
+                                    int B, int Hq_r, int Hkv_r, int N, int64_t kr_cap,
+                                    hipStream_t stream)
+{
+    auto go = [&](auto kern, int G) {
+        const ScanGeom g = scan_geom(B, Hq_r, Hkv_r, N, G, kScanTPT);
+        return launch(kern, dim3(g.gx, g.gy), dim3(kScanThreads), 0, stream, q_r,
+                      static_cast<const void *>(k_r), scores, N, kr_cap, Hq_r, Hkv_r, g.group,
+                      g.head_chunks);
+    };
+    const int group = Hq_r / Hkv_r;
+    if (group == 1) return go(index_scores_kernel<1, true>, 1);
+    if (group == 2) return go(index_scores_kernel<2, true>, 2);
+    if (group <= 4) return go(index_scores_kernel<4, true>, 4);
+    return go(index_scores_kernel<8, true>, 8);
 }
 
 hipError_t launch_index_scores(const float *q_r, const float *k_r, float *scores,
@@ -25,8 +43,9 @@ hipError_t launch_index_scores(const float *q_r, const float *k_r, float *scores
 {
     auto go = [&](auto kern, int G) {
         const ScanGeom g = scan_geom(B, Hq_r, Hkv_r, N, G, kScanTPT);
-        return launch(kern, dim3(g.gx, g.gy), dim3(kScanThreads), 0, stream, q_r, k_r, scores,
-                      N, kr_cap, Hq_r, Hkv_r, g.group, g.head_chunks);
+        return launch(kern, dim3(g.gx, g.gy), dim3(kScanThreads), 0, stream, q_r,
+                      static_cast<const void *>(k_r), scores, N, kr_cap, Hq_r, Hkv_r, g.group,
+                      g.head_chunks);
     };
     const int group = Hq_r / Hkv_r;
     if (group == 1) return go(index_scores_kernel<1>, 1);

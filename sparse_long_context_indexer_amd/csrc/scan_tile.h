@@ -40,9 +40,11 @@ inline ScanGeom scan_geom(int B, int Hq_r, int Hkv_r, int N, int G, int tpt)
 
 // Tile (bx, y): thread t scores tokens bx*tile + t + k*kScanThreads,
 // k < TPT, for the heads of chunk y % head_chunks of group y / head_chunks.
-template <int G, int TPT>
+// k_r rows are 16 fp32 (64 B), or with kBf16 16 bf16 (32 B) widened exactly
+// to fp32 before the same fma chain.
+template <int G, int TPT, bool kBf16 = false>
 __device__ __forceinline__ void scan_tile(const float *__restrict__ q_r,
-                                          const float *__restrict__ k_r,
+                                          const void *__restrict__ k_r,
                                           float *__restrict__ scores, int N, int64_t kr_cap,
                                           int Hq_r, int Hkv_r, int group, int head_chunks,
                                           int bx, int y)
@@ -55,19 +57,51 @@ __device__ __forceinline__ void scan_tile(const float *__restrict__ q_r,
     const int h0 = g * group + chunk * G;
     const int nh = min(G, group - chunk * G);
 
-    const float4 *krow = reinterpret_cast<const float4 *>(k_r + (int64_t)bg * kr_cap * 16);
     const int64_t base = (int64_t)bx * kTile + threadIdx.x;
 
     float4 kv[TPT][4];
+    if constexpr (kBf16) {
+        const uint4 *krow = reinterpret_cast<const uint4 *>(
+            static_cast<const uint16_t *>(k_r) + (int64_t)bg * kr_cap * 16);
+        uint4 kw[TPT][2];
 #pragma unroll
-    for (int t = 0; t < TPT; ++t) {
-        const int64_t i = base + (int64_t)t * kScanThreads;
-        if (i < N) {
+        for (int t = 0; t < TPT; ++t) {
+            const int64_t i = base + (int64_t)t * kScanThreads;
+            if (i < N) {
+                kw[t][0] = krow[i * 2];
+                kw[t][1] = krow[i * 2 + 1];
+            } else {
+                kw[t][0] = kw[t][1] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        // Word e of a 16-B piece holds dims 2e (low half) and 2e + 1.
 #pragma unroll
-            for (int j = 0; j < 4; ++j) kv[t][j] = krow[i * 4 + j];
-        } else {
+        for (int t = 0; t < TPT; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) kv[t][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int j = 0; j < 2; ++j) {
+                const uint4 w = kw[t][j];
+                kv[t][2 * j] = make_float4(__uint_as_float(w.x << 16),
+                                           __uint_as_float(w.x & 0xFFFF0000u),
+                                           __uint_as_float(w.y << 16),
+                                           __uint_as_float(w.y & 0xFFFF0000u));
+                kv[t][2 * j + 1] = make_float4(__uint_as_float(w.z << 16),
+                                               __uint_as_float(w.z & 0xFFFF0000u),
+                                               __uint_as_float(w.w << 16),
+                                               __uint_as_float(w.w & 0xFFFF0000u));
+            }
+    } else {
+        const float4 *krow = reinterpret_cast<const float4 *>(
+            static_cast<const float *>(k_r) + (int64_t)bg * kr_cap * 16);
+#pragma unroll
+        for (int t = 0; t < TPT; ++t) {
+            const int64_t i = base + (int64_t)t * kScanThreads;
+            if (i < N) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kv[t][j] = krow[i * 4 + j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kv[t][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
     }
 

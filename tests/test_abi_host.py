@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -96,6 +96,16 @@ def test_topp_select_validation(lib):
     assert f(A, 1, 8, 1000, 0.9, A, A, None, A + 16, ws, None) == 5   # workspace alignment
     assert f(A + 2, 1, 8, 1000, 0.9, A, A, None, A, ws, None) == 5
     assert f(A, 1, 8, 1000, 0.9, A, A, A + 2, A, ws, None) == 5       # keep_bits alignment
+
+
+def test_index_scores_bf16_validation(lib):
+    # Every call below fails validation (the pointers are not device memory).
+    f = lib.rtp_index_scores_bf16
+    assert f(None, A, A, 1, 8, 1, 100, 100, 16, None) == 1
+    assert f(A, A, A, 1, 8, 1, 100, 100, 8, None) == 3          # r != 16
+    assert f(A, A, A, 1, 8, 3, 100, 100, 16, None) == 2         # 8 % 3
+    assert f(A, A, A, 1, 8, 1, 101, 100, 16, None) == 2         # N > cap
+    assert f(A, A + 8, A, 1, 8, 1, 100, 100, 16, None) == 5     # k_r alignment
 
 
 def test_index_project_validation(lib):

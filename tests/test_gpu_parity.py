@@ -236,6 +236,24 @@ def test_select_two_launch_path():
         assert v.ok, (h, v.k_gpu, v.k_oracle, v.note)
 
 
+@pytest.mark.parametrize("B, Hq_r, Hkv_r, N, cap", [(1, 1, 1, 1, 1), (2, 8, 1, 70_001, 70_005),
+                                                   (1, 12, 3, 4099, 4099), (1, 8, 1, 1 << 20, 1 << 20)])
+def test_scores_bf16_keys_bit_exact(B, Hq_r, Hkv_r, N, cap):
+    rng = np.random.default_rng(N + Hq_r)
+    q = rng.standard_normal((B, Hq_r, 16)).astype(np.float32)
+    kb = synth.f32_to_bf16(rng.standard_normal((B, Hkv_r, cap, 16)).astype(np.float32) * 2)
+    sc = torch.full((B, Hq_r, N), 7.0, dtype=torch.float32, device=dev())
+    rtp.rtp_index_scores_bf16(to_dev(q), torch.from_numpy(kb.view(np.int16)).to(dev()), sc)
+    got = sc.cpu().numpy()
+    G = Hq_r // Hkv_r
+    heads = range(Hq_r) if N < (1 << 20) else (0, Hq_r - 1)
+    for b in range(B):
+        for h in heads:
+            want = oracle.scores_bf16(q[b, h], kb[b, h // G, :N])
+            assert np.array_equal(got[b, h].view(np.uint32), want.view(np.uint32)), (b, h)
+
+
+# -------------------------------------------------------------- projection
 # -------------------------------------------------------------- projection
 
 # fp32 accumulation of d exact products in any order: the error stays within

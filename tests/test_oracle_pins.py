@@ -195,6 +195,20 @@ def test_topp_permutation_equivariance():
     assert set(perm[r2.sel].tolist()) == set(r1.sel.tolist())
 
 
+def test_scores_bf16_keys_widen_exactly():
+    # bf16 keys give the fp32 scores of their exact fp32 widening, and a key
+    # row of exact small integers gives the integer dot product.
+    cfg = synth.CONFIGS[0].with_(N=3000)
+    q = synth.layer_qr(cfg, 0)[0, 0]
+    kb = synth.f32_to_bf16(synth.layer_kr(cfg, 0)[0, 0])
+    assert np.array_equal(oracle.scores_bf16(q, kb),
+                          oracle.scores(q, synth.bf16_to_f32(kb)))
+    qi = np.arange(16, dtype=np.float32) - 8
+    ki = (np.arange(5 * 16, dtype=np.float32).reshape(5, 16) % 7) - 3
+    want = (ki.astype(np.int64) @ qi.astype(np.int64)).astype(np.float32)
+    assert np.array_equal(oracle.scores_bf16(qi, synth.f32_to_bf16(ki)), want)
+
+
 # -------------------------------------------------------------- projection
 
 def _bf16_of(v):
