@@ -318,7 +318,7 @@ def main():
     cands = {
         "sel_emit_kernel": ("sel_emit_kernel<false>", sel_bytes, "select.hip"),
         "rtp_topp_hist": ("sel_hist_kernel<false>", B * H_r * N * 4, "select.hip"),
-        "rtp_index_scores": ("index_scores_kernel<8>", B * G_r * N * (cfg.r * 4 + cfg.G * 4),
+        "rtp_index_scores": ("index_scores_kernel<8, false>", B * G_r * N * (cfg.r * 4 + cfg.G * 4),
                              "scan.hip"),
         "rtp_decode_attend": ("attend_kernel",
                               sparse_bytes + (window_bytes if sl.mode == "fused" else 0),
