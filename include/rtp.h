@@ -277,6 +277,29 @@ rtp_status rtp_local_decode(const rtp_bf16 *q, const rtp_bf16 *K,
                             void *stream);
 
 /*
+ * rtp_local_decode_ring -- rtp_local_decode over a ring-buffer local cache
+ * that keeps only the rows a local head can attend (arXiv abstract: the full
+ * KV cache is kept for retrieval heads only; summary section 1: local heads
+ * see sinks plus a window).  Token i < n_sink sits in slot i; token
+ * i >= n_sink in slot n_sink + (i - n_sink) % window, so a cache of
+ * n_sink + window slots always holds the newest window tokens.  N is the
+ * number of tokens seen (the newest is N-1); the result is bit-identical to
+ * rtp_local_decode on the linear cache.
+ *
+ *   K, V   bf16 [B][Hkv][kv_cap][d]  ring slots, kv_cap >= min(N, n_sink + window)
+ *   every other argument, and the errors, as in rtp_local_decode
+ *   (workspace sized with the same N)
+ */
+rtp_status rtp_local_decode_ring(const rtp_bf16 *q, const rtp_bf16 *K,
+                                 const rtp_bf16 *V, int32_t B, int32_t Hq,
+                                 int32_t Hkv, int32_t N, int64_t kv_cap,
+                                 int32_t d, int32_t q_head_begin,
+                                 int32_t n_q_heads, int32_t n_sink,
+                                 int32_t window, float scale, float *out,
+                                 void *workspace, size_t ws_bytes,
+                                 void *stream);
+
+/*
  * rtp_decode_attend -- rtp_sparse_decode for the query heads
  * sparse_head_begin .. sparse_head_begin + n_sparse_heads - 1 and
  * rtp_local_decode for the query heads local_head_begin ..

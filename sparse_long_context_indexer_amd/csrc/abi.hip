@@ -223,6 +223,30 @@ rtp_status rtp_local_decode(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16
                                              as_stream(stream)));
 }
 
+rtp_status rtp_local_decode_ring(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int64_t kv_cap,
+                                 int32_t d, int32_t q_head_begin, int32_t n_q_heads,
+                                 int32_t n_sink, int32_t window, float scale, float *out,
+                                 void *workspace, size_t ws_bytes, void *stream)
+{
+    if (N < 1) return RTP_ERR_SHAPE;
+    if (n_sink < 0 || window < 1) return RTP_ERR_VALUE;
+    // The ring holds every row it is asked for once it has n_sink + window
+    // slots (fewer tokens than that never wrap).
+    const int64_t ring = (int64_t)n_sink + window;
+    const int32_t rows = (int32_t)(N < ring ? N : ring);
+    rtp_status st = check_attention_common(q, K, V, out, workspace, B, Hq, Hkv, rows, kv_cap, d,
+                                           q_head_begin, n_q_heads, scale);
+    if (st != RTP_OK) return st;
+    const int64_t G = Hq / Hkv;
+    const int64_t groups = ((int64_t)q_head_begin + n_q_heads - 1) / G - q_head_begin / G + 1;
+    if (groups * ((G + 7) / 8) > kMaxGridY) return RTP_ERR_SHAPE;
+    if (ws_bytes < rtp::local_ws_bytes(B, n_q_heads, N)) return RTP_ERR_WORKSPACE;
+    return from_hip(rtp::launch_local_decode_ring(q, K, V, B, Hq, Hkv, N, kv_cap, q_head_begin,
+                                                  n_q_heads, n_sink, window, scale, out,
+                                                  workspace, as_stream(stream)));
+}
+
 rtp_status rtp_decode_attend(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,
                              const int32_t *idx, const int32_t *count, int32_t B, int32_t Hq,
                              int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,

@@ -957,6 +957,8 @@ __device__ __forceinline__ void heads4_step(Heads4 &st, const uint4 (&kw)[kLocal
 
 struct LocalArgs {
     int q_head_begin, n_q, n_sink, window;
+    int ring;          // K/V hold n_sink + window slots: token i >= n_sink at
+                       // slot n_sink + (i - n_sink) % window
     int S;             // splits of the row list
     int ny;            // head chunks (block rows)
     int chunks_per_g;
@@ -999,7 +1001,8 @@ __device__ void local_block(const uint16_t *__restrict__ q, const uint16_t *__re
         for (int i = 0; i < kPieces; ++i) {
             const int e = threadIdx.x + i * kAttThreads, row = e >> 4, pc = e & 15;
             const int64_t j = t0 + (row < nt ? row : 0);
-            const int64_t g = j < sink_end ? j : w_start + (j - sink_end);
+            int64_t g = j < sink_end ? j : w_start + (j - sink_end);
+            if (A.ring && g >= A.n_sink) g = A.n_sink + (g - A.n_sink) % A.window;
             kx[i] = *reinterpret_cast<const uint4 *>(Kb + g * 128 + pc * 8);
             vx[i] = *reinterpret_cast<const uint4 *>(Vb + g * 128 + pc * 8);
         }
@@ -1204,6 +1207,16 @@ hipError_t launch_local_decode(const uint16_t *q, const uint16_t *K, const uint1
     return launch_attend(q, K, V, N, kv_cap, Hq, Hkv, scale,
                          local_args(B, Hq, Hkv, N, q_head_begin, n_q_heads, n_sink, window, ws),
                          SparseArgs{}, out, stream);
+}
+
+hipError_t launch_local_decode_ring(const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                                    int B, int Hq, int Hkv, int N, int64_t kv_cap,
+                                    int q_head_begin, int n_q_heads, int n_sink, int window,
+                                    float scale, float *out, void *ws, hipStream_t stream)
+{
+    LocalArgs L = local_args(B, Hq, Hkv, N, q_head_begin, n_q_heads, n_sink, window, ws);
+    L.ring = 1;
+    return launch_attend(q, K, V, N, kv_cap, Hq, Hkv, scale, L, SparseArgs{}, out, stream);
 }
 
 size_t attend_ws_bytes(int64_t B, int64_t n_sparse, int64_t n_local, int N)

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -96,6 +96,26 @@ def test_topp_select_validation(lib):
     assert f(A, 1, 8, 1000, 0.9, A, A, None, A + 16, ws, None) == 5   # workspace alignment
     assert f(A + 2, 1, 8, 1000, 0.9, A, A, None, A, ws, None) == 5
     assert f(A, 1, 8, 1000, 0.9, A, A, A + 2, A, ws, None) == 5       # keep_bits alignment
+
+
+def test_local_decode_ring_validation(lib):
+    # Every call below fails validation (the pointers are not device memory).
+    f = lib.rtp_local_decode_ring
+    ws = rtp.workspace_size(rtp.RTP_WS_LOCAL_DECODE, 1, 8, 100000)
+    base = [A, A, A, 1, 32, 4, 100000, 4100, 128, 8, 24, 4, 4096, 0.088, A, A, ws, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(0, None) == 1 and call(1, None) == 1
+    assert call(7, 4099) == 2                   # kv_cap below n_sink + window
+    assert call(6, 0) == 2                      # N < 1
+    assert call(11, -1) == 4 and call(12, 0) == 4
+    assert call(8, 64) == 3                     # d
+    assert call(16, ws - 1) == 6
+    assert call(1, A + 8) == 5
 
 
 def test_index_scores_bf16_validation(lib):

@@ -469,6 +469,41 @@ def test_local_edges(N, n_sink, window):
         assert np.all(np.isnan(got[b, :8]))  # heads outside the range untouched
 
 
+@pytest.mark.parametrize("N,n_sink,window", [
+    (3, 4, 4096), (4100, 4, 4096), (4101, 4, 4096), (9000, 0, 4096), (9000, 4, 1),
+    (20000, 17, 333)])
+def test_local_ring_cache_matches_linear(N, n_sink, window):
+    # A ring cache holding the tokens a local head can still see (every
+    # other token's slot has been overwritten by a newer one) gives the
+    # linear cache's result bit for bit, and the oracle's.
+    cfg = synth.CONFIGS[1].with_(N=N, n_sink=n_sink, window=window, B=2, needles_per_head=0)
+    L = load_layer(cfg)
+    ring = min(N, n_sink + window)
+    live = oracle.local_rows(N, n_sink, window)
+    slot = np.where(live < n_sink, live, n_sink + (live - n_sink) % window)
+    assert len(np.unique(slot)) == len(live) and slot.max() < ring
+    Kr = np.zeros((2, L.K.shape[1], ring, 128), np.uint16)
+    Vr = np.zeros_like(Kr)
+    Kr[:, :, slot] = L.K[:, :, live]
+    Vr[:, :, slot] = L.V[:, :, live]
+    ws = torch.empty(rtp.workspace_size(rtp.RTP_WS_LOCAL_DECODE, 2, 24, N), dtype=torch.uint8,
+                     device=dev())
+    lin = torch.full((2, 32, 128), float("nan"), dtype=torch.float32, device=dev())
+    rtp.rtp_local_decode(L.d["q"], L.d["K"], L.d["V"], N, 8, 24, n_sink, window, cfg.scale,
+                         lin, ws)
+    out = torch.full((2, 32, 128), float("nan"), dtype=torch.float32, device=dev())
+    rtp.rtp_local_decode_ring(L.d["q"], torch.from_numpy(Kr.view(np.int16)).to(dev()),
+                              torch.from_numpy(Vr.view(np.int16)).to(dev()), N, 8, 24, n_sink,
+                              window, cfg.scale, out, ws)
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), lin.cpu().numpy().view(np.uint32))
+    rows = oracle.local_rows(N, n_sink, window)
+    for h in (8, 31):
+        ref = oracle.attention(L.q[1, h], L.K[1, h // 8, rows], L.V[1, h // 8, rows], cfg.scale)
+        ok, err, rel = judge_out(got[1, h], ref)
+        assert ok, (h, err, rel)
+
+
 def test_local_unaligned_head_range():
     # Heads 5..13 with 4 query heads per KV head: partial groups at both ends.
     cfg = synth.CONFIGS[1].with_(N=6000, Hq=16, Hkv=4, H_r=0, needles_per_head=0)
