@@ -186,6 +186,24 @@ rtp_status rtp_topk_select(const float *scores, int32_t B, int32_t H,
                            size_t ws_bytes, void *stream);
 
 /*
+ * rtp_keep_bits_add_local -- adds the local rows (the first n_sink tokens
+ * and the newest `window`, as rtp_local_decode reads them) to every keep
+ * bitmap row, so that rtp_sparse_decode_union lets a retrieval head attend
+ * its selected set plus the sinks and the window.  The pages let retrieval
+ * heads switch to the selected set alone (gist.science summary, method
+ * section 1); this is the variant where they keep the local rows too.
+ *
+ *   keep_bits  uint32 [B][H][ceil(N/32)]  in/out, 4-B aligned: bits are only set
+ *   n_sink >= 0, window >= 1
+ *
+ * Errors: RTP_ERR_NULL, RTP_ERR_SHAPE (B, H or N < 1, B*H > 65535),
+ * RTP_ERR_VALUE (n_sink or window), RTP_ERR_ALIGN.
+ */
+rtp_status rtp_keep_bits_add_local(uint32_t *keep_bits, int32_t B, int32_t H,
+                                   int32_t N, int32_t n_sink, int32_t window,
+                                   void *stream);
+
+/*
  * rtp_topp_hist -- the histogram pass of rtp_topp_select on its own: the
  * per-row mass histograms (same passage) are left in the workspace and no
  * output is written.  rtp_topp_select runs this pass and the emit pass that

@@ -27,7 +27,7 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPP
 # Every symbol include/rtp.h declares.
 SYMBOLS = ("rtp_index_scores", "rtp_index_scores_bf16", "rtp_index_project", "rtp_topp_select", "rtp_topk_select", "rtp_topp_hist",
            "rtp_sparse_decode", "rtp_sparse_decode_union", "rtp_local_decode",
-           "rtp_local_decode_ring", "rtp_decode_attend", "rtp_scan_local", "rtp_workspace_size", "rtp_status_string",
+           "rtp_local_decode_ring", "rtp_keep_bits_add_local", "rtp_decode_attend", "rtp_scan_local", "rtp_workspace_size", "rtp_status_string",
            "rtp_last_hip_error")
 
 
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.rtp_local_decode.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, I32, I32,
                                        I32, I32, F32, P, P, SZ, P]
         L.rtp_local_decode_ring.argtypes = L.rtp_local_decode.argtypes
+        L.rtp_keep_bits_add_local.argtypes = [P, I32, I32, I32, I32, I32, P]
         L.rtp_decode_attend.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32, I32, I32,
                                         I32, I32, I32, I32, F32, P, P, SZ, P]
         L.rtp_scan_local.argtypes = [P, P, P, I32, I32, I64, I32, P, P, P, I32, I32, I32, I32,
@@ -79,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.rtp_status_string.restype = ctypes.c_char_p
         L.rtp_last_hip_error.argtypes = []
         L.rtp_last_hip_error.restype = I32
-        for name in SYMBOLS[:13]:
+        for name in SYMBOLS[:14]:
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -215,6 +216,18 @@ def rtp_topk_select(scores, k, idx, count, workspace, keep_bits=None, stream=Non
         _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2), kb,
         _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
         _stream(scores, stream)), "rtp_topk_select")
+
+
+def rtp_keep_bits_add_local(keep_bits, N, n_sink, window, stream=None) -> None:
+    """Sets the sink and window bits of every row of keep_bits
+    (i32 [B][H][keep_words(N)])."""
+    import torch
+    B, H, nw = keep_bits.shape
+    if nw != keep_words(N):
+        raise ValueError(f"keep_bits must have {keep_words(N)} words per row")
+    _check(lib().rtp_keep_bits_add_local(_dev(keep_bits, torch.int32, "keep_bits", 3), B, H, N,
+                                         n_sink, window, _stream(keep_bits, stream)),
+           "rtp_keep_bits_add_local")
 
 
 def rtp_topp_hist(scores, workspace, stream=None) -> None:

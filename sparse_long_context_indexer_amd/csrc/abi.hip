@@ -156,6 +156,17 @@ rtp_status rtp_topk_select(const float *scores, int32_t B, int32_t H, int32_t N,
                                             as_stream(stream)));
 }
 
+rtp_status rtp_keep_bits_add_local(uint32_t *keep_bits, int32_t B, int32_t H, int32_t N,
+                                   int32_t n_sink, int32_t window, void *stream)
+{
+    if (!keep_bits) return RTP_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1 || (int64_t)B * H > kMaxGridY) return RTP_ERR_SHAPE;
+    if (n_sink < 0 || window < 1) return RTP_ERR_VALUE;
+    if (!aligned(keep_bits, 4)) return RTP_ERR_ALIGN;
+    return from_hip(rtp::launch_keep_local(keep_bits, (int64_t)B * H, N, n_sink, window,
+                                           as_stream(stream)));
+}
+
 rtp_status rtp_topp_hist(const float *scores, int32_t B, int32_t H, int32_t N, void *workspace,
                          size_t ws_bytes, void *stream)
 {

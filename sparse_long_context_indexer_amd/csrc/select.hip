@@ -1108,6 +1108,42 @@ __global__ __launch_bounds__(256) void sel_all_kernel(int N, int32_t *__restrict
     }
 }
 
+// ------------------------------------------------- sinks + window bits
+//
+// Adds the local rows [0, min(n_sink, w0)) and [w0, N), w0 = max(0, N -
+// window), to every keep bitmap row: thread w owns word w of its row, so no
+// two threads touch one word.
+
+__global__ __launch_bounds__(256) void keep_local_kernel(uint32_t *__restrict__ keep_bits, int N,
+                                                         int n_words, int64_t sink_end,
+                                                         int64_t w0)
+{
+    const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (w >= n_words) return;
+    const int64_t lo = w * 32, hi = lo + 32;
+    // Bits of [a, b) within this word.
+    auto span = [&](int64_t a, int64_t b) -> uint32_t {
+        a = a > lo ? a : lo;
+        b = b < hi ? b : hi;
+        if (a >= b) return 0u;
+        const uint32_t n = (uint32_t)(b - a), s = (uint32_t)(a - lo);
+        return (n == 32u ? 0xFFFFFFFFu : ((1u << n) - 1u)) << s;
+    };
+    const uint32_t m = span(0, sink_end) | span(w0, N);
+    if (m) keep_bits[(int64_t)blockIdx.y * n_words + w] |= m;
+}
+
+hipError_t launch_keep_local(uint32_t *keep_bits, int64_t R, int N, int n_sink, int window,
+                             hipStream_t stream)
+{
+    const int n_words = (N + 31) / 32;
+    const int64_t w0 = N > window ? (int64_t)N - window : 0;
+    const int64_t sink_end = n_sink < w0 ? n_sink : w0;
+    dim3 grid((unsigned)((n_words + 255) / 256), (unsigned)R);
+    return launch(keep_local_kernel, grid, dim3(256), 0, stream, keep_bits, N, n_words, sink_end,
+                  w0);
+}
+
 constexpr int64_t kMaxFusedRows = 65535;  // grid rows of one launch
 
 hipError_t launch_topp_hist(const float *scores, int64_t R, int N, void *ws, hipStream_t stream)

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -96,6 +96,16 @@ def test_topp_select_validation(lib):
     assert f(A, 1, 8, 1000, 0.9, A, A, None, A + 16, ws, None) == 5   # workspace alignment
     assert f(A + 2, 1, 8, 1000, 0.9, A, A, None, A, ws, None) == 5
     assert f(A, 1, 8, 1000, 0.9, A, A, A + 2, A, ws, None) == 5       # keep_bits alignment
+
+
+def test_keep_bits_add_local_validation(lib):
+    # Every call below fails validation (the pointer is not device memory).
+    f = lib.rtp_keep_bits_add_local
+    assert f(None, 1, 8, 1000, 4, 64, None) == 1
+    assert f(A, 0, 8, 1000, 4, 64, None) == 2 and f(A, 1, 8, 0, 4, 64, None) == 2
+    assert f(A, 1, 65536, 1000, 4, 64, None) == 2
+    assert f(A, 1, 8, 1000, -1, 64, None) == 4 and f(A, 1, 8, 1000, 4, 0, None) == 4
+    assert f(A + 2, 1, 8, 1000, 4, 64, None) == 5
 
 
 def test_local_decode_ring_validation(lib):

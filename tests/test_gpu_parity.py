@@ -654,6 +654,40 @@ def test_workspace_garbage_and_reuse(mode):
 
 # ------------------------------------------------------------- union mode
 
+@pytest.mark.parametrize("N,n_sink,window", [(5000, 4, 4096), (70_001, 4, 4096),
+                                              (70_001, 0, 31), (100, 7, 50)])
+def test_retrieval_heads_with_sinks_and_window(N, n_sink, window):
+    # The variant where retrieval heads attend their top-p set plus the local
+    # rows: the bitmap after the local bits are added is exactly S u local,
+    # and union attention over it matches the oracle over that set.
+    cfg = synth.CONFIGS[1].with_(N=N, needles_per_head=0)
+    L = load_layer(cfg)
+    H_r = 8
+    sc = torch.empty((1, H_r, N), dtype=torch.float32, device=dev())
+    rtp.rtp_index_scores(L.d["q_r"], L.d["k_r"], sc)
+    idx = torch.empty((1, H_r, N), dtype=torch.int32, device=dev())
+    cnt = torch.empty((1, H_r), dtype=torch.int32, device=dev())
+    kb = torch.empty((1, H_r, rtp.keep_words(N)), dtype=torch.int32, device=dev())
+    ws = torch.empty(rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 1, H_r, N), dtype=torch.uint8,
+                     device=dev())
+    rtp.rtp_topp_select(sc, 0.9, idx, cnt, ws, keep_bits=kb)
+    rtp.rtp_keep_bits_add_local(kb, N, n_sink, window)
+    out = torch.full((1, cfg.Hq, 128), float("nan"), dtype=torch.float32, device=dev())
+    wsu = torch.empty(rtp.workspace_size(rtp.RTP_WS_SPARSE_UNION, 1, H_r, N), dtype=torch.uint8,
+                      device=dev())
+    rtp.rtp_sparse_decode_union(L.d["q"], L.d["K"], L.d["V"], kb, N, 0, cfg.scale, out, wsu)
+    got, bits = out.cpu().numpy(), kb.cpu().numpy()
+    c, ix = cnt.cpu().numpy(), idx.cpu().numpy()
+    local = oracle.local_rows(N, n_sink, window)
+    for h in range(H_r):
+        rows = np.union1d(ix[0, h, :c[0, h]], local)
+        have = np.flatnonzero(np.unpackbits(bits[0, h].view(np.uint8), bitorder="little")[:N])
+        assert np.array_equal(have, rows), h
+        ref = oracle.attention(L.q[0, h], L.K[0, h // 8, rows], L.V[0, h // 8, rows], cfg.scale)
+        ok, err, rel = judge_out(got[0, h], ref)
+        assert ok, (h, err, rel)
+
+
 @pytest.mark.parametrize("N,hb,nq", [(70001, 0, 8), (5000, 3, 8), (33, 0, 8), (100000, 4, 12)])
 def test_union_decode_random_sets(N, hb, nq):
     # Keep bitmaps built on the host (random densities per head, stray bits
