@@ -318,6 +318,38 @@ rtp_status rtp_local_decode_ring(const rtp_bf16 *q, const rtp_bf16 *K,
                                  void *stream);
 
 /*
+ * rtp_prefill_attend -- causal prefill attention for a range of query heads,
+ * dense (retrieval heads) or sinks + window (local heads) (gist.science
+ * summary, method section 1: the two head roles; the arXiv abstract credits
+ * the prefill speed-up at 1M context to them).  For query token t < T:
+ *
+ *   window <= 0  keys [0, t]
+ *   window >= 1  keys [0, min(n_sink, w0)) and [w0, t], w0 = max(0, t+1-window)
+ *   out[b][h][t][:] = sum_i softmax_i(scale * q[b][h][t] . K[b][g][i]) * V[b][g][i][:]
+ *
+ * with g = h / (Hq/Hkv): the local rows of each t are those rtp_local_decode
+ * reads with N = t + 1.  bf16 products and fp32 accumulation on the matrix
+ * cores, fp32 softmax (the probabilities enter the second product as a bf16
+ * pair, good to about 2^-17), fp32 output.
+ *
+ *   q      bf16 [B][Hq][T][d]       16-B aligned (the prompt's queries, post-RoPE)
+ *   K, V   bf16 [B][Hkv][kv_cap][d] 16-B aligned; rows [0, T) are the prompt
+ *   out    fp32 [B][Hq][T][d]       4-B aligned; heads [head_begin,
+ *                                   head_begin + n_heads) written
+ *   d must be 128; 1 <= T <= kv_cap; B*n_heads <= 65535; n_sink >= 0 when
+ *   window >= 1; scale finite.
+ *
+ * Errors: RTP_ERR_NULL, RTP_ERR_UNSUPPORTED, RTP_ERR_SHAPE, RTP_ERR_VALUE,
+ * RTP_ERR_ALIGN.
+ */
+rtp_status rtp_prefill_attend(const rtp_bf16 *q, const rtp_bf16 *K,
+                              const rtp_bf16 *V, int32_t B, int32_t Hq,
+                              int32_t Hkv, int32_t T, int64_t kv_cap, int32_t d,
+                              int32_t head_begin, int32_t n_heads,
+                              int32_t n_sink, int32_t window, float scale,
+                              float *out, void *stream);
+
+/*
  * rtp_decode_attend -- rtp_sparse_decode for the query heads
  * sparse_head_begin .. sparse_head_begin + n_sparse_heads - 1 and
  * rtp_local_decode for the query heads local_head_begin ..

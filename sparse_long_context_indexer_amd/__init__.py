@@ -27,7 +27,8 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPP
 # Every symbol include/rtp.h declares.
 SYMBOLS = ("rtp_index_scores", "rtp_index_scores_bf16", "rtp_index_project", "rtp_topp_select", "rtp_topk_select", "rtp_topp_hist",
            "rtp_sparse_decode", "rtp_sparse_decode_union", "rtp_local_decode",
-           "rtp_local_decode_ring", "rtp_keep_bits_add_local", "rtp_decode_attend", "rtp_scan_local", "rtp_workspace_size", "rtp_status_string",
+           "rtp_local_decode_ring", "rtp_keep_bits_add_local", "rtp_prefill_attend",
+           "rtp_decode_attend", "rtp_scan_local", "rtp_workspace_size", "rtp_status_string",
            "rtp_last_hip_error")
 
 
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
                                        I32, I32, F32, P, P, SZ, P]
         L.rtp_local_decode_ring.argtypes = L.rtp_local_decode.argtypes
         L.rtp_keep_bits_add_local.argtypes = [P, I32, I32, I32, I32, I32, P]
+        L.rtp_prefill_attend.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, I32, I32, I32,
+                                         I32, F32, P, P]
         L.rtp_decode_attend.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32, I32, I32,
                                         I32, I32, I32, I32, F32, P, P, SZ, P]
         L.rtp_scan_local.argtypes = [P, P, P, I32, I32, I64, I32, P, P, P, I32, I32, I32, I32,
@@ -80,7 +83,7 @@ def lib() -> ctypes.CDLL:
         L.rtp_status_string.restype = ctypes.c_char_p
         L.rtp_last_hip_error.argtypes = []
         L.rtp_last_hip_error.restype = I32
-        for name in SYMBOLS[:14]:
+        for name in SYMBOLS[:15]:
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -316,6 +319,20 @@ def rtp_scan_local(q_r, k_r, scores, q, K, V, N, local_head_begin, n_local_heads
         local_head_begin, n_local_heads, n_sink, window, float(scale),
         _dev(out, torch.float32, "out", 3), _dev(workspace, torch.uint8, "workspace", 1),
         workspace.numel(), _stream(q, stream)), "rtp_scan_local")
+
+
+def rtp_prefill_attend(q, K, V, head_begin, n_heads, n_sink, window, scale, out,
+                       stream=None) -> None:
+    """q bf16 [B][Hq][T][128]; K, V bf16 [B][Hkv][cap][128]; out f32
+    [B][Hq][T][128]: causal prefill for heads [head_begin, + n_heads), dense
+    (window <= 0) or sinks + window."""
+    import torch
+    B, Hq, T, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    _check(lib().rtp_prefill_attend(
+        _bf16(q, "q", 4), _bf16(K, "K", 4), _bf16(V, "V", 4), B, Hq, Hkv, T, cap, d,
+        head_begin, n_heads, n_sink, window, float(scale), _dev(out, torch.float32, "out", 4),
+        _stream(q, stream)), "rtp_prefill_attend")
 
 
 def rtp_local_decode_ring(q, K, V, N, q_head_begin, n_q_heads, n_sink, window, scale, out,

@@ -258,6 +258,25 @@ rtp_status rtp_local_decode_ring(const rtp_bf16 *q, const rtp_bf16 *K, const rtp
                                                   workspace, as_stream(stream)));
 }
 
+rtp_status rtp_prefill_attend(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V, int32_t B,
+                              int32_t Hq, int32_t Hkv, int32_t T, int64_t kv_cap, int32_t d,
+                              int32_t head_begin, int32_t n_heads, int32_t n_sink,
+                              int32_t window, float scale, float *out, void *stream)
+{
+    if (!q || !K || !V || !out) return RTP_ERR_NULL;
+    if (d != 128) return RTP_ERR_UNSUPPORTED;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || T < 1 || kv_cap < T) return RTP_ERR_SHAPE;
+    if (head_begin < 0 || n_heads < 1 || (int64_t)head_begin + n_heads > Hq ||
+        (int64_t)B * n_heads > kMaxGridY)
+        return RTP_ERR_SHAPE;
+    if (!isfinite(scale) || (window >= 1 && n_sink < 0)) return RTP_ERR_VALUE;
+    if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 4))
+        return RTP_ERR_ALIGN;
+    return from_hip(rtp::launch_prefill_attend(q, K, V, B, Hq, Hkv, T, kv_cap, head_begin,
+                                               n_heads, window >= 1 ? n_sink : 0, window, scale,
+                                               out, as_stream(stream)));
+}
+
 rtp_status rtp_decode_attend(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,
                              const int32_t *idx, const int32_t *count, int32_t B, int32_t Hq,
                              int32_t Hkv, int32_t N, int64_t kv_cap, int32_t d,

@@ -38,6 +38,10 @@ hipError_t launch_local_decode_ring(const uint16_t *q, const uint16_t *K, const 
                                     float scale, float *out, void *ws, hipStream_t stream);
 hipError_t launch_keep_local(uint32_t *keep_bits, int64_t R, int N, int n_sink, int window,
                              hipStream_t stream);
+hipError_t launch_prefill_attend(const uint16_t *q, const uint16_t *K, const uint16_t *V, int B,
+                                 int Hq, int Hkv, int T, int64_t kv_cap, int head_begin,
+                                 int n_heads, int n_sink, int window, float scale, float *out,
+                                 hipStream_t stream);
 hipError_t launch_index_project(const uint16_t *x, int B, int Hx, int64_t x_cap, int head_begin,
                                 int H, int T, const uint16_t *W, float *out, int64_t out_cap,
                                 int64_t out_pos, hipStream_t stream);

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -96,6 +96,24 @@ def test_topp_select_validation(lib):
     assert f(A, 1, 8, 1000, 0.9, A, A, None, A + 16, ws, None) == 5   # workspace alignment
     assert f(A + 2, 1, 8, 1000, 0.9, A, A, None, A, ws, None) == 5
     assert f(A, 1, 8, 1000, 0.9, A, A, A + 2, A, ws, None) == 5       # keep_bits alignment
+
+
+def test_prefill_attend_validation(lib):
+    # Every call below fails validation (the pointers are not device memory).
+    f = lib.rtp_prefill_attend
+    base = [A, A, A, 1, 32, 4, 1000, 1000, 128, 8, 24, 4, 4096, 0.088, A, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(0, None) == 1 and call(14, None) == 1
+    assert call(8, 64) == 3
+    assert call(5, 3) == 2 and call(6, 0) == 2 and call(7, 999) == 2
+    assert call(9, 9) == 2 and call(10, 0) == 2 and call(3, 70000) == 2
+    assert call(11, -1) == 4 and call(13, float("nan")) == 4
+    assert call(1, A + 8) == 5 and call(14, A + 2) == 5
 
 
 def test_keep_bits_add_local_validation(lib):

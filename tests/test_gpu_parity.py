@@ -253,7 +253,40 @@ def test_scores_bf16_keys_bit_exact(B, Hq_r, Hkv_r, N, cap):
             assert np.array_equal(got[b, h].view(np.uint32), want.view(np.uint32)), (b, h)
 
 
-# -------------------------------------------------------------- projection
+# ----------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("T,n_sink,window,hb,nh", [
+    (1, 0, 0, 0, 8), (37, 0, 0, 2, 3), (300, 0, 0, 0, 8), (1000, 4, 64, 1, 6),
+    (1000, 0, 1, 0, 8), (2000, 4, 300, 3, 5), (130, 17, 16, 0, 8)])
+def test_prefill_attend_against_oracle(T, n_sink, window, hb, nh):
+    # Dense (window 0) and sinks + window heads, GQA with 4 query heads per
+    # KV head, a cache wider than T; sampled queries against the oracle's
+    # attention over each query's rows, heads outside the range untouched.
+    B, Hq, Hkv, cap = 2, 8, 2, T + 5
+    q = synth.normal_bf16(synth.key(80 + T, 1), 0, B * Hq * T * 128).reshape(B, Hq, T, 128)
+    K = synth.normal_bf16(synth.key(80 + T, 2), 0, B * Hkv * cap * 128).reshape(B, Hkv, cap, 128)
+    V = synth.normal_bf16(synth.key(80 + T, 3), 0, B * Hkv * cap * 128).reshape(B, Hkv, cap, 128)
+    scale = 1.0 / math.sqrt(128.0)
+    out = torch.full((B, Hq, T, 128), float("nan"), dtype=torch.float32, device=dev())
+    rtp.rtp_prefill_attend(torch.from_numpy(q.view(np.int16)).to(dev()),
+                           torch.from_numpy(K.view(np.int16)).to(dev()),
+                           torch.from_numpy(V.view(np.int16)).to(dev()), hb, nh, n_sink, window,
+                           scale, out)
+    got = out.cpu().numpy()
+    rng = np.random.default_rng(T)
+    ts = np.unique(np.concatenate([np.arange(min(T, 20)), np.arange(max(0, T - 20), T),
+                                   rng.integers(0, T, 40)]))
+    for b in range(B):
+        for h in range(hb, hb + nh):
+            for t in ts:
+                rows = np.arange(t + 1) if window <= 0 else oracle.local_rows(t + 1, n_sink, window)
+                ref = oracle.attention(q[b, h, t], K[b, h // 4, rows], V[b, h // 4, rows], scale)
+                ok, err, rel = judge_out(got[b, h, t], ref)
+                assert ok, (b, h, t, err, rel)
+        outside = [h for h in range(Hq) if not hb <= h < hb + nh]
+        assert np.all(np.isnan(got[b, outside]))
+
+
 # -------------------------------------------------------------- projection
 
 # fp32 accumulation of d exact products in any order: the error stays within
@@ -329,7 +362,6 @@ def test_project_prefill_1m_sampled():
     assert np.all(np.abs(got[0, 0, rows].astype(np.float64) - want) <= bound)
 
 
-# ------------------------------------------------------------------ top-k
 # ------------------------------------------------------------------ top-k
 
 def _select_k(scores: np.ndarray, k: int, keep_bits=False):
@@ -419,7 +451,6 @@ def test_topk_at_the_top_p_budget_keeps_the_top_p_set():
                                   np.sort(oracle.topk(s[b, h], int(c_p[b, h]))))
 
 
-# -------------------------------------------------------- attention edges
 # -------------------------------------------------------- attention edges
 
 def test_sparse_single_row_is_value_row():
