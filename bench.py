@@ -229,6 +229,22 @@ def main():
         (rtp.rtp_index_project(qp, Wq, qr_out),
          rtp.rtp_index_project(kp, Wp, kr_cache, out_pos=N - 1)) for l in range(L)])
     proj_gbps = N * (d * 2 + 16 * 4) / (us["rtp_index_project_prefill"] * 1e-6) / 1e9
+    # Prefill attention of a 16384-token prompt on layer 0's cache, a
+    # reference call: the retrieval heads dense, the local heads sinks +
+    # window, one launch each.  Flops: 4 * d per (query, key) pair.
+    T_pf = 16384
+    q_pf = bf16_bits(B, Hq, T_pf, d)
+    out_pf = torch.empty((B, Hq, T_pf, d), dtype=torch.float32, device=dev)
+    us["rtp_prefill_attend_16k"] = time_call(lambda: [(
+        rtp.rtp_prefill_attend(q_pf, K_all[0], V_all[0], 0, H_r, 0, 0, scale, out_pf),
+        rtp.rtp_prefill_attend(q_pf, K_all[0], V_all[0], H_r, Hq - H_r, cfg.n_sink, cfg.window,
+                               scale, out_pf)) for _ in range(4)]) * L / 4
+    t_idx = np.arange(T_pf, dtype=np.float64)
+    w0 = np.maximum(0, t_idx + 1 - cfg.window)
+    local_pairs = float(np.sum(np.minimum(cfg.n_sink, w0) + (t_idx + 1 - w0)))
+    pf_flops = B * 4 * d * (H_r * T_pf * (T_pf + 1) / 2 + (Hq - H_r) * local_pairs)
+    pf_tflops = pf_flops / (us["rtp_prefill_attend_16k"] * 1e-6) / 1e12
+    del q_pf, out_pf
     del xp, kr_out, kr_cache
     # rtp_topp_select runs both passes in one launch (sel_fused_kernel) when
     # its histogram and emit block rows fit one grid (2 * B * H_r <= 65535);
@@ -374,6 +390,7 @@ def main():
         "per_call_us_per_layer": {k: round(v, 2) for k, v in us.items()},
         "topk_budget": k_budget,
         "project_prefill_GBps": round(proj_gbps, 1),
+        "prefill_16k_TFLOPs": round(pf_tflops, 1),
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
         "cpu_baseline": cpu,
     }
