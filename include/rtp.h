@@ -118,7 +118,7 @@ rtp_status rtp_index_scores_bf16(const float *q_r, const rtp_bf16 *k_r,
  *   W        bf16 [H][r][d]           16-B aligned; one projector per head
  *   out      fp32 [B][H][out_cap][r]  4-B aligned; rows [out_pos,
  *                                     out_pos + T) written, the rest untouched
- *   d must be 128 and r must be 16; 1 <= T <= x_cap;
+ *   d must be 128 and r must be 16; 1 <= T <= x_cap, T <= 2^31 - 1025;
  *   0 <= out_pos <= out_cap - T; 0 <= head_begin <= Hx - H; B*H <= 65535.
  *
  * Errors: RTP_ERR_NULL, RTP_ERR_UNSUPPORTED (d or r), RTP_ERR_SHAPE,
@@ -336,7 +336,7 @@ rtp_status rtp_local_decode_ring(const rtp_bf16 *q, const rtp_bf16 *K,
  *   K, V   bf16 [B][Hkv][kv_cap][d] 16-B aligned; rows [0, T) are the prompt
  *   out    fp32 [B][Hq][T][d]       4-B aligned; heads [head_begin,
  *                                   head_begin + n_heads) written
- *   d must be 128; 1 <= T <= kv_cap; B*n_heads <= 65535; n_sink >= 0 when
+ *   d must be 128; 1 <= T <= kv_cap, T <= 2^31 - 1025; B*n_heads <= 65535; n_sink >= 0 when
  *   window >= 1; scale finite.
  *
  * Errors: RTP_ERR_NULL, RTP_ERR_UNSUPPORTED, RTP_ERR_SHAPE, RTP_ERR_VALUE,

@@ -131,7 +131,9 @@ rtp_status rtp_index_project(const rtp_bf16 *x, int32_t B, int32_t Hx, int64_t x
 {
     if (!x || !W || !out) return RTP_ERR_NULL;
     if (d != 128 || r != 16) return RTP_ERR_UNSUPPORTED;
-    if (B < 1 || Hx < 1 || H < 1 || T < 1 || head_begin < 0 || head_begin > Hx - H ||
+    // Token indices (plus a block's worth of tiles) stay within int32.
+    if (B < 1 || Hx < 1 || H < 1 || T < 1 || T > INT32_MAX - 1024 || head_begin < 0 ||
+        head_begin > Hx - H ||
         x_cap < T || out_pos < 0 || out_cap < T || out_pos > out_cap - T ||
         (int64_t)B * H > kMaxGridY)
         return RTP_ERR_SHAPE;
@@ -265,7 +267,9 @@ rtp_status rtp_prefill_attend(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf
 {
     if (!q || !K || !V || !out) return RTP_ERR_NULL;
     if (d != 128) return RTP_ERR_UNSUPPORTED;
-    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || T < 1 || kv_cap < T) return RTP_ERR_SHAPE;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || T < 1 || T > INT32_MAX - 1024 ||
+        kv_cap < T)
+        return RTP_ERR_SHAPE;
     if (head_begin < 0 || n_heads < 1 || (int64_t)head_begin + n_heads > Hq ||
         (int64_t)B * n_heads > kMaxGridY)
         return RTP_ERR_SHAPE;
