@@ -641,6 +641,72 @@ def test_scan_local_shapes(N, Hq_r, Hkv_r, Hq, Hkv, lb, nl, n_sink, window):
                 assert np.all(np.isnan(o[b, h])), (b, h)
 
 
+# ---------------------------------------------------------------- graphs
+
+@pytest.mark.parametrize("mode", ["fused", "union"])
+def test_graph_replays_match_eager(mode):
+    # One decode layer (and a top-k select, and a projection) captured as a
+    # HIP graph and replayed several times, with eager work on other inputs
+    # and host synchronisations between replays: every replay gives the
+    # eager run's scores and counts bit for bit, the same kept sets, and the
+    # same outputs up to the order of the kept rows.
+    from sparse_long_context_indexer_amd.runner import DecodeLayer
+    cfg = synth.CONFIGS[1]
+    L = load_layer(cfg)
+    step = DecodeLayer(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.H_r, cfg.n_sink, cfg.window, dev(),
+                       mode=mode)
+    out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=torch.float32, device=dev())
+    tk_idx = torch.empty_like(step.idx)
+    tk_cnt = torch.empty_like(step.count)
+    x = torch.from_numpy(synth.normal_bf16(synth.key(90, 1), 0, 4 * 300 * 128)
+                         .reshape(1, 4, 300, 128).view(np.int16)).to(dev())
+    Wp = torch.from_numpy(synth.normal_bf16(synth.key(90, 2), 0, 4 * 16 * 128)
+                          .reshape(4, 16, 128).view(np.int16)).to(dev())
+    pr = torch.empty((1, 4, 300, 16), dtype=torch.float32, device=dev())
+
+    def issue():
+        step(L.d["q_r"], L.d["k_r"], L.d["q"], L.d["K"], L.d["V"], 0.9, cfg.scale, out)
+        rtp.rtp_topk_select(step.scores, 777, tk_idx, tk_cnt, step.ws_sel)
+        rtp.rtp_index_project(x, Wp, pr)
+
+    def snap():
+        torch.cuda.synchronize()
+        c, ix = step.count.cpu().numpy(), step.idx.cpu().numpy()
+        tc, tix = tk_cnt.cpu().numpy(), tk_idx.cpu().numpy()
+        return (out.cpu().numpy(), step.scores.cpu().numpy(), c,
+                [np.sort(ix[b, h, :c[b, h]]) for b in range(cfg.B) for h in range(cfg.H_r)],
+                [np.sort(tix[b, h, :tc[b, h]]) for b in range(cfg.B) for h in range(cfg.H_r)],
+                pr.cpu().numpy())
+
+    issue()
+    ref = snap()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        issue()
+    other = torch.empty((2, 3, 50_000), dtype=torch.float32, device=dev())
+    for rep in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        got = snap()
+        assert np.array_equal(got[1], ref[1]) and np.array_equal(got[2], ref[2]), rep
+        assert all(np.array_equal(a_, b_) for a_, b_ in zip(got[3], ref[3])), rep
+        assert all(np.array_equal(a_, b_) for a_, b_ in zip(got[4], ref[4])), rep
+        assert np.array_equal(got[5], ref[5]), rep
+        assert np.allclose(got[0], ref[0], rtol=1e-5, atol=1e-6), rep
+        # eager work between replays: a selection on other scores in the
+        # same workspace
+        other.normal_()
+        _select(other.cpu().numpy(), 0.9)
+        rtp.rtp_topp_select(other, 0.5, torch.empty((2, 3, 50_000), dtype=torch.int32,
+                                                    device=dev()),
+                            torch.empty((2, 3), dtype=torch.int32, device=dev()),
+                            torch.empty(rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 2, 3, 50_000),
+                                        dtype=torch.uint8, device=dev()))
+        torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ workspaces
 # ------------------------------------------------------------ workspaces
 
 @pytest.mark.parametrize("mode", ["fused", "scan_local", "per_head", "union"])
