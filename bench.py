@@ -207,7 +207,28 @@ def main():
     kr_b = kr_all.to(torch.bfloat16).view(torch.int16)
     us["rtp_index_scores_bf16"] = time_call(lambda: [rtp.rtp_index_scores_bf16(
         qr_all[l], kr_b[l % kr_b.shape[0]], scores_l[l]) for l in range(L)])
-    del kr_b
+    # The whole step with the bf16 key caches (the runner scans them with
+    # rtp_index_scores_bf16), captured and replayed like the step above: a
+    # reference figure for that variant, not the headline.
+    def step_bf16():
+        for l in range(L):
+            step_layer(qr_all[l], kr_b[l], q_all[l], K_all[l], V_all[l], p, scale, out_all[l],
+                       side_stream=side)
+    step_bf16()
+    torch.cuda.synchronize()
+    g16 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g16):
+        step_bf16()
+    g16.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        g16.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_bf16 = e0.elapsed_time(e1) / 5
+    del g16, kr_b
     # Indexer projections (reference calls, not part of the step, whose q_r
     # and k_r are given): the prefill k_r build of one retrieval KV head
     # over all N tokens (256 B of bf16 features read, 64 B of k_r written
@@ -389,6 +410,7 @@ def main():
         "union_rows_per_layer_mean": float(np.mean(union)),
         "per_call_us_per_layer": {k: round(v, 2) for k, v in us.items()},
         "topk_budget": k_budget,
+        "ms_per_step_bf16_kr": round(ms_step_bf16, 4),
         "project_prefill_GBps": round(proj_gbps, 1),
         "prefill_16k_TFLOPs": round(pf_tflops, 1),
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},

@@ -12,7 +12,7 @@ import torch
 
 from . import (RTP_WS_DECODE_ATTEND, RTP_WS_LOCAL_DECODE, RTP_WS_SPARSE_DECODE,
                RTP_WS_SPARSE_UNION, RTP_WS_TOPP_SELECT, keep_words, rtp_decode_attend,
-               rtp_index_scores, rtp_local_decode, rtp_scan_local, rtp_sparse_decode,
+               rtp_index_scores, rtp_index_scores_bf16, rtp_local_decode, rtp_scan_local, rtp_sparse_decode,
                rtp_sparse_decode_union, rtp_topp_select, workspace_size)
 
 
@@ -56,8 +56,17 @@ class DecodeLayer:
             self.ws_local = torch.empty(workspace_size(RTP_WS_LOCAL_DECODE, B, self.H_l, N),
                                         dtype=torch.uint8, device=dev)
 
+    def scan(self, q_r, k_r, stream=None):
+        """The indexer scan; a bf16 k_r cache (torch.bfloat16 or its int16
+        bit patterns) takes rtp_index_scores_bf16."""
+        import torch
+        if k_r.dtype in (torch.bfloat16, torch.int16):
+            rtp_index_scores_bf16(q_r, k_r, self.scores, stream=stream)
+        else:
+            rtp_index_scores(q_r, k_r, self.scores, stream=stream)
+
     def retrieval(self, q_r, k_r, q, K, V, p: float, scale: float, out, stream=None):
-        rtp_index_scores(q_r, k_r, self.scores, stream=stream)
+        self.scan(q_r, k_r, stream=stream)
         rtp_topp_select(self.scores, p, self.idx, self.count, self.ws_sel,
                         keep_bits=self.keep_bits, stream=stream)
         if self.mode == "union":
@@ -91,7 +100,7 @@ class DecodeLayer:
                               scale, out, self.ws_attend)
             return
         if self.mode == "fused" and self.H_r > 0 and self.H_l > 0:
-            rtp_index_scores(q_r, k_r, self.scores)
+            self.scan(q_r, k_r)
             rtp_topp_select(self.scores, p, self.idx, self.count, self.ws_sel)
             self.attend(q, K, V, scale, out)
             return

@@ -253,6 +253,30 @@ def test_scores_bf16_keys_bit_exact(B, Hq_r, Hkv_r, N, cap):
             assert np.array_equal(got[b, h].view(np.uint32), want.view(np.uint32)), (b, h)
 
 
+def test_layer_with_bf16_key_cache():
+    # The runner takes a bf16 k_r cache through rtp_index_scores_bf16: its
+    # scores are the oracle's over the widened keys, bit for bit, and the
+    # kept sets are the oracle's top-p sets of those scores.
+    from sparse_long_context_indexer_amd.runner import DecodeLayer
+    cfg = synth.CONFIGS[1]
+    L = load_layer(cfg)
+    kb = synth.f32_to_bf16(L.k_r)
+    step = DecodeLayer(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.H_r, cfg.n_sink, cfg.window, dev())
+    out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=torch.float32, device=dev())
+    step(L.d["q_r"], torch.from_numpy(kb.view(np.int16)).to(dev()), L.d["q"], L.d["K"],
+         L.d["V"], 0.9, cfg.scale, out)
+    torch.cuda.synchronize()
+    sc, c, ix = step.scores.cpu().numpy(), step.count.cpu().numpy(), step.idx.cpu().numpy()
+    G = cfg.H_r // cfg.G_r
+    for b in range(cfg.B):
+        for h in range(cfg.H_r):
+            want = oracle.scores_bf16(L.q_r[b, h], kb[b, h // G, :cfg.N])
+            assert np.array_equal(sc[b, h].view(np.uint32), want.view(np.uint32)), (b, h)
+            v = judge_set(want, 0.9, ix[b, h, :c[b, h]])
+            assert v.ok, (b, h, v.k_gpu, v.k_oracle)
+
+
+# ----------------------------------------------------------------- prefill
 # ----------------------------------------------------------------- prefill
 
 @pytest.mark.parametrize("T,n_sink,window,hb,nh", [
