@@ -401,6 +401,84 @@ rtp_status rtp_scan_local(const float *q_r, const float *k_r, float *scores,
                           void *stream);
 
 /*
+ * rtp_decode_layer -- one decode step of one attention layer in a single
+ * launch: the indexer scan (rtp_index_scores), top-p selection
+ * (rtp_topp_select) and exact sparse attention (rtp_sparse_decode) for the
+ * retrieval heads, and sinks + window attention (rtp_local_decode) for the
+ * local heads (gist.science summary, method section 1: the two head roles;
+ * section 2: the 16-dim indexer; section 3: top-p mass; section 5: a
+ * sort-free histogram threshold and bandwidth-optimised sparse decode).
+ * The kept sets and outputs are those of the four calls run in sequence;
+ * the scores stay on chip unless `scores` is given.
+ *
+ * Head roles: query heads 0 .. Hq_r-1 are retrieval heads (on KV heads
+ * 0 .. Hq_r/G - 1, G = Hq/Hkv, so Hq_r must be a multiple of G); query heads
+ * Hq_r .. Hq-1 are local heads.
+ *
+ *   q_r     fp32 [B][Hq_r][r]           16-B aligned
+ *   k_r     fp32 [B][Hq_r/G][kr_cap][r] 16-B aligned
+ *   q       bf16 [B][Hq][d]             16-B aligned
+ *   K, V    bf16 [B][Hkv][kv_cap][d]    16-B aligned
+ *   p       in (0, 1] (the top-p mass; 1 keeps every token)
+ *   scale   finite (the attention scale, e.g. 1/sqrt(d))
+ *   n_sink, window   as in rtp_local_decode (ignored when Hq_r == Hq)
+ *   out     fp32 [B][Hq][d]             out, every head written
+ *   idx     int32 [B][Hq_r][N]          out: kept indices, in no particular order
+ *   count   int32 [B][Hq_r]             out: kept-set sizes
+ *   scores  fp32 [B][Hq_r][N]           optional out (NULL: not written)
+ *   workspace  >= rtp_decode_layer_workspace_size(...) bytes, 256-B aligned;
+ *              contents need no initialisation
+ *   d must be 128 and r must be 16; G must be 1, 2, 4 or 8.
+ *
+ * The launch is persistent: at most one block per compute unit, and the
+ * blocks of a score row wait for each other once (for the row's threshold),
+ * which needs them resident together; nothing else may run on the device
+ * during the call.  One launch holds up to 4096 tokens per compute unit
+ * (N <= 4096 * floor(CUs / (B * Hq_r / G))); larger shapes return
+ * RTP_ERR_UNSUPPORTED (use the four calls).
+ *
+ * Errors: RTP_ERR_NULL, RTP_ERR_UNSUPPORTED (d, r, G, or the shape above),
+ * RTP_ERR_SHAPE, RTP_ERR_VALUE (p, scale, n_sink, window), RTP_ERR_ALIGN,
+ * RTP_ERR_WORKSPACE.
+ */
+rtp_status rtp_decode_layer(const float *q_r, const float *k_r, int64_t kr_cap,
+                            const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,
+                            int64_t kv_cap, int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                            int32_t d, int32_t r, int32_t Hq_r, int32_t n_sink, int32_t window,
+                            float p, float scale, float *out, int32_t *idx, int32_t *count,
+                            float *scores, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * rtp_decode_layer_workspace_size -- bytes of workspace rtp_decode_layer
+ * needs for these sizes on the current device (host only).  The same errors
+ * as rtp_decode_layer for the sizes, plus RTP_ERR_NULL when bytes is NULL.
+ */
+rtp_status rtp_decode_layer_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                                           int32_t Hq_r, int32_t n_sink, int32_t window,
+                                           size_t *bytes);
+
+/*
+ * Waits between blocks.  Some kernels hand data from block to block inside
+ * one launch (rtp_topp_select, rtp_topk_select, rtp_sparse_decode,
+ * rtp_decode_attend, rtp_decode_layer); a block that waits polls at most
+ * `polls` times (default 2^24) and then gives up, sets the status bit
+ * RTP_STATUS_WAIT_TIMEOUT in the device's sticky status word, and goes on,
+ * so the kernel still ends; the results of that call, and the state of its
+ * workspace, are then undefined (fill the workspace with zeros before
+ * reusing it).  A wait never needs the limit unless something else is wrong.
+ *
+ * rtp_set_wait_limit sets the limit for launches that follow, in this
+ * process (0 gives up at once: a test hook).  Always RTP_OK.
+ *
+ * rtp_device_status waits for the current device to finish its work, then
+ * returns its status word in *flags and, when clear is nonzero, clears it.
+ * Errors: RTP_ERR_NULL (flags NULL), RTP_ERR_HIP.
+ */
+#define RTP_STATUS_WAIT_TIMEOUT 1u
+rtp_status rtp_set_wait_limit(uint32_t polls);
+rtp_status rtp_device_status(uint32_t *flags, int32_t clear);
+
+/*
  * rtp_workspace_size -- bytes of workspace a call needs (host only, pure).
  *   which  RTP_WS_TOPP_SELECT:   H = score rows per batch row
  *          RTP_WS_SPARSE_DECODE: H = n_q_heads

@@ -1,9 +1,12 @@
 """Python binding of librtp (include/rtp.h): the RTPurbo sparse decode path
 on MI355X (arXiv 2605.16928).
 
-Argument marshalling only: each function checks dtypes and shapes of the
-torch tensors it is given, reads their device pointers and the current HIP
-stream, and calls the C function of the same name.  Every step of the path
+Argument marshalling only: each function checks the dtype, device and
+full shape of every torch tensor it is given against the sizes the C call
+will read (a mismatch raises ValueError or TypeError before anything is
+launched, since the C ABI receives no tensor sizes), reads their device
+pointers and the current HIP stream, and calls the C function of the same
+name.  Every step of the path
 runs in the HIP kernels of librtp.so; there is no fallback.  If the library
 is not built, calls raise RuntimeError.
 """
@@ -25,11 +28,15 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPP
           4: "RTP_ERR_VALUE", 5: "RTP_ERR_ALIGN", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
 
 # Every symbol include/rtp.h declares.
-SYMBOLS = ("rtp_index_scores", "rtp_index_scores_bf16", "rtp_index_project", "rtp_topp_select", "rtp_topk_select", "rtp_topp_hist",
-           "rtp_sparse_decode", "rtp_sparse_decode_union", "rtp_local_decode",
-           "rtp_local_decode_ring", "rtp_keep_bits_add_local", "rtp_prefill_attend",
-           "rtp_decode_attend", "rtp_scan_local", "rtp_workspace_size", "rtp_status_string",
-           "rtp_last_hip_error")
+SYMBOLS = ("rtp_index_scores", "rtp_index_scores_bf16", "rtp_index_project", "rtp_topp_select",
+           "rtp_topk_select", "rtp_topp_hist", "rtp_sparse_decode", "rtp_sparse_decode_union",
+           "rtp_local_decode", "rtp_local_decode_ring", "rtp_keep_bits_add_local",
+           "rtp_prefill_attend", "rtp_decode_attend", "rtp_scan_local", "rtp_decode_layer",
+           "rtp_decode_layer_workspace_size", "rtp_set_wait_limit", "rtp_device_status",
+           "rtp_workspace_size", "rtp_status_string", "rtp_last_hip_error")
+
+# Bit of the device status word (rtp_device_status): a bounded wait gave up.
+RTP_STATUS_WAIT_TIMEOUT = 1
 
 
 class RtpError(RuntimeError):
@@ -78,12 +85,18 @@ def lib() -> ctypes.CDLL:
                                         I32, I32, I32, I32, F32, P, P, SZ, P]
         L.rtp_scan_local.argtypes = [P, P, P, I32, I32, I64, I32, P, P, P, I32, I32, I32, I32,
                                      I64, I32, I32, I32, I32, I32, F32, P, P, SZ, P]
+        L.rtp_decode_layer.argtypes = [P, P, I64, P, P, P, I64, I32, I32, I32, I32, I32, I32,
+                                       I32, I32, I32, F32, F32, P, P, P, P, P, SZ, P]
+        L.rtp_decode_layer_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32,
+                                                      ctypes.POINTER(SZ)]
+        L.rtp_set_wait_limit.argtypes = [ctypes.c_uint32]
+        L.rtp_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), I32]
         L.rtp_workspace_size.argtypes = [I32, I32, I32, I32, ctypes.POINTER(SZ)]
         L.rtp_status_string.argtypes = [I32]
         L.rtp_status_string.restype = ctypes.c_char_p
         L.rtp_last_hip_error.argtypes = []
         L.rtp_last_hip_error.restype = I32
-        for name in SYMBOLS[:15]:
+        for name in SYMBOLS[:-2]:
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -100,8 +113,29 @@ def _check(status: int, where: str) -> None:
 
 def workspace_size(which: int, B: int, H: int, N: int) -> int:
     out = ctypes.c_size_t(0)
-    _check(lib().rtp_workspace_size(which, B, H, N, ctypes.byref(out)), "rtp_workspace_size")
+    _call("rtp_workspace_size", which, B, H, N, ctypes.byref(out))
     return out.value
+
+
+def decode_layer_workspace_size(B: int, Hq: int, Hkv: int, N: int, Hq_r: int, n_sink: int,
+                                window: int) -> int:
+    """Workspace bytes of rtp_decode_layer on the current device."""
+    out = ctypes.c_size_t(0)
+    _call("rtp_decode_layer_workspace_size", B, Hq, Hkv, N, Hq_r, n_sink, window,
+                                                 ctypes.byref(out))
+    return out.value
+
+
+def set_wait_limit(polls: int) -> None:
+    """Poll limit of the kernels' waits on other blocks, for later launches."""
+    _call("rtp_set_wait_limit", int(polls))
+
+
+def device_status(clear: bool = False) -> int:
+    """The current device's sticky status word (waits for the device)."""
+    v = ctypes.c_uint32(0)
+    _call("rtp_device_status", ctypes.byref(v), 1 if clear else 0)
+    return v.value
 
 
 # ------------------------------------------------------------ torch glue
@@ -113,52 +147,98 @@ def _stream(t, stream):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _dev(t, dtype, name, ndim):
+def _dev(t, dtype, name, shape):
+    """Device pointer of a contiguous device tensor of this dtype; `shape` is
+    the expected shape (an int for the number of dims alone, or a tuple
+    whose None entries match any size)."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    ndim = shape if isinstance(shape, int) else len(shape)
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not isinstance(shape, int):
+        for got, want in zip(t.shape, shape):
+            if want is not None and got != want:
+                raise ValueError(f"{name} must have shape "
+                                 f"{tuple('*' if w is None else w for w in shape)}, "
+                                 f"got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if t.device.type != "cuda":
-        raise ValueError(f"{name} must be a device tensor")
+        return _OffDevice(name)  # reported by _call, once every shape is checked
     return t.data_ptr()
 
 
-def _bf16(t, name, ndim):
+class _OffDevice:
+    def __init__(self, name):
+        self.name = name
+
+
+def _call(name, *args):
+    """Calls C function `name` once no argument is a host tensor."""
+    for a in args:
+        if isinstance(a, _OffDevice):
+            raise ValueError(f"{a.name} must be a device tensor")
+    _check(getattr(lib(), name)(*args), name)
+
+
+def _bf16(t, name, shape):
     import torch
-    if t.dtype == torch.bfloat16:
+    if isinstance(t, torch.Tensor) and t.dtype == torch.bfloat16:
         t = t.view(torch.int16)
-    return _dev(t, torch.int16, name, ndim)
+    return _dev(t, torch.int16, name, shape)
+
+
+def _ws(workspace):
+    import torch
+    return _dev(workspace, torch.uint8, "workspace", 1), workspace.numel()
+
+
+def _qkv(q, K, V, out):
+    """q bf16 [B][Hq][d], K and V bf16 [B][Hkv][cap][d], out f32 [B][Hq][d]:
+    checked and marshalled; returns the pointers and (B, Hq, Hkv, cap, d)."""
+    import torch
+    if q.dim() != 3 or K.dim() != 4:
+        raise ValueError("q must be [B][Hq][d] and K [B][Hkv][cap][d]")
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    ptrs = (_bf16(q, "q", (B, Hq, d)), _bf16(K, "K", (B, Hkv, cap, d)),
+            _bf16(V, "V", (B, Hkv, cap, d)), _dev(out, torch.float32, "out", (B, Hq, d)))
+    return ptrs, (B, Hq, Hkv, cap, d)
 
 
 def rtp_index_scores(q_r, k_r, scores, stream=None) -> None:
     """q_r f32 [B][Hq_r][16]; k_r f32 [B][Hkv_r][cap][16];
     scores f32 [B][Hq_r][N] (out)."""
     import torch
+    if q_r.dim() != 3 or k_r.dim() != 4 or scores.dim() != 3:
+        raise ValueError("q_r must be 3-D, k_r 4-D, scores 3-D")
     B, Hq_r, r = q_r.shape
-    _, Hkv_r, cap, _ = k_r.shape
+    Hkv_r, cap = k_r.shape[1], k_r.shape[2]
     N = scores.shape[-1]
-    _check(lib().rtp_index_scores(
-        _dev(q_r, torch.float32, "q_r", 3), _dev(k_r, torch.float32, "k_r", 4),
-        _dev(scores, torch.float32, "scores", 3), B, Hq_r, Hkv_r, N, cap, r,
-        _stream(q_r, stream)), "rtp_index_scores")
+    _call("rtp_index_scores", 
+        _dev(q_r, torch.float32, "q_r", (B, Hq_r, r)),
+        _dev(k_r, torch.float32, "k_r", (B, Hkv_r, cap, r)),
+        _dev(scores, torch.float32, "scores", (B, Hq_r, N)), B, Hq_r, Hkv_r, N, cap, r,
+        _stream(q_r, stream))
 
 
 def rtp_index_scores_bf16(q_r, k_r, scores, stream=None) -> None:
     """rtp_index_scores over a bf16 k_r cache: k_r bf16 [B][Hkv_r][cap][16]
     (torch.bfloat16 or its int16 bit patterns)."""
     import torch
+    if q_r.dim() != 3 or k_r.dim() != 4 or scores.dim() != 3:
+        raise ValueError("q_r must be 3-D, k_r 4-D, scores 3-D")
     B, Hq_r, r = q_r.shape
-    _, Hkv_r, cap, _ = k_r.shape
+    Hkv_r, cap = k_r.shape[1], k_r.shape[2]
     N = scores.shape[-1]
-    _check(lib().rtp_index_scores_bf16(
-        _dev(q_r, torch.float32, "q_r", 3), _bf16(k_r, "k_r", 4),
-        _dev(scores, torch.float32, "scores", 3), B, Hq_r, Hkv_r, N, cap, r,
-        _stream(q_r, stream)), "rtp_index_scores_bf16")
+    _call("rtp_index_scores_bf16", 
+        _dev(q_r, torch.float32, "q_r", (B, Hq_r, r)), _bf16(k_r, "k_r", (B, Hkv_r, cap, r)),
+        _dev(scores, torch.float32, "scores", (B, Hq_r, N)), B, Hq_r, Hkv_r, N, cap, r,
+        _stream(q_r, stream))
 
 
 def keep_words(N: int) -> int:
@@ -166,22 +246,37 @@ def keep_words(N: int) -> int:
     return (N + 31) // 32
 
 
+def _select_outs(scores, idx, count, keep_bits):
+    import torch
+    if scores.dim() != 3:
+        raise ValueError("scores must be [B][H][N]")
+    B, H, N = scores.shape
+    kb = None
+    if keep_bits is not None:
+        kb = _dev(keep_bits, torch.int32, "keep_bits", (B, H, keep_words(N)))
+    return (B, H, N), (_dev(scores, torch.float32, "scores", (B, H, N)),
+                       _dev(idx, torch.int32, "idx", (B, H, N)),
+                       _dev(count, torch.int32, "count", (B, H)), kb)
+
+
 def rtp_topp_select(scores, p, idx, count, workspace, keep_bits=None, stream=None) -> None:
     """scores f32 [B][H][N]; idx i32 [B][H][N] (out); count i32 [B][H] (out);
     keep_bits i32 [B][H][keep_words(N)] (optional out, the same sets as
     bitmaps); workspace uint8 [>= workspace_size(RTP_WS_TOPP_SELECT, B, H, N)]."""
-    import torch
-    B, H, N = scores.shape
-    kb = None
-    if keep_bits is not None:
-        if tuple(keep_bits.shape) != (B, H, keep_words(N)):
-            raise ValueError(f"keep_bits must have shape {(B, H, keep_words(N))}")
-        kb = _dev(keep_bits, torch.int32, "keep_bits", 3)
-    _check(lib().rtp_topp_select(
-        _dev(scores, torch.float32, "scores", 3), B, H, N, float(p),
-        _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2), kb,
-        _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
-        _stream(scores, stream)), "rtp_topp_select")
+    (B, H, N), (sp, ip, cp, kb) = _select_outs(scores, idx, count, keep_bits)
+    wp, wn = _ws(workspace)
+    _call("rtp_topp_select", sp, B, H, N, float(p), ip, cp, kb, wp, wn,
+                                 _stream(scores, stream))
+
+
+def rtp_topk_select(scores, k, idx, count, workspace, keep_bits=None, stream=None) -> None:
+    """Static top-k: the first min(k, N) tokens of each row by (score
+    descending, index ascending).  Arguments as in rtp_topp_select, with the
+    integer budget k >= 1 in place of p."""
+    (B, H, N), (sp, ip, cp, kb) = _select_outs(scores, idx, count, keep_bits)
+    wp, wn = _ws(workspace)
+    _call("rtp_topk_select", sp, B, H, N, int(k), ip, cp, kb, wp, wn,
+                                 _stream(scores, stream))
 
 
 def rtp_index_project(x, W, out, head_begin=0, T=None, out_pos=0, stream=None) -> None:
@@ -197,50 +292,33 @@ def rtp_index_project(x, W, out, head_begin=0, T=None, out_pos=0, stream=None) -
     if dw != d or tuple(out.shape[:2]) != (B, H) or out.shape[3] != r:
         raise ValueError("x, W and out disagree in shape")
     T = x_cap if T is None else T
-    _check(lib().rtp_index_project(
-        _bf16(x, "x", 4), B, Hx, x_cap, head_begin, H, T, d,
-        _bf16(W, "W", 3), r, _dev(out, torch.float32, "out", 4), out.shape[2],
-        out_pos, _stream(x, stream)), "rtp_index_project")
-
-
-def rtp_topk_select(scores, k, idx, count, workspace, keep_bits=None, stream=None) -> None:
-    """Static top-k: the first min(k, N) tokens of each row by (score
-    descending, index ascending).  Arguments as in rtp_topp_select, with the
-    integer budget k >= 1 in place of p."""
-    import torch
-    B, H, N = scores.shape
-    kb = None
-    if keep_bits is not None:
-        if tuple(keep_bits.shape) != (B, H, keep_words(N)):
-            raise ValueError(f"keep_bits must have shape {(B, H, keep_words(N))}")
-        kb = _dev(keep_bits, torch.int32, "keep_bits", 3)
-    _check(lib().rtp_topk_select(
-        _dev(scores, torch.float32, "scores", 3), B, H, N, int(k),
-        _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2), kb,
-        _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
-        _stream(scores, stream)), "rtp_topk_select")
+    _call("rtp_index_project", 
+        _bf16(x, "x", (B, Hx, x_cap, d)), B, Hx, x_cap, head_begin, H, T, d,
+        _bf16(W, "W", (H, r, d)), r, _dev(out, torch.float32, "out", (B, H, None, r)),
+        out.shape[2], out_pos, _stream(x, stream))
 
 
 def rtp_keep_bits_add_local(keep_bits, N, n_sink, window, stream=None) -> None:
     """Sets the sink and window bits of every row of keep_bits
     (i32 [B][H][keep_words(N)])."""
     import torch
-    B, H, nw = keep_bits.shape
-    if nw != keep_words(N):
-        raise ValueError(f"keep_bits must have {keep_words(N)} words per row")
-    _check(lib().rtp_keep_bits_add_local(_dev(keep_bits, torch.int32, "keep_bits", 3), B, H, N,
-                                         n_sink, window, _stream(keep_bits, stream)),
-           "rtp_keep_bits_add_local")
+    if keep_bits.dim() != 3:
+        raise ValueError("keep_bits must be [B][H][keep_words(N)]")
+    B, H, _ = keep_bits.shape
+    _call("rtp_keep_bits_add_local", 
+        _dev(keep_bits, torch.int32, "keep_bits", (B, H, keep_words(N))), B, H, N, n_sink,
+        window, _stream(keep_bits, stream))
 
 
 def rtp_topp_hist(scores, workspace, stream=None) -> None:
     """The histogram pass of rtp_topp_select alone (no output written)."""
     import torch
+    if scores.dim() != 3:
+        raise ValueError("scores must be [B][H][N]")
     B, H, N = scores.shape
-    _check(lib().rtp_topp_hist(
-        _dev(scores, torch.float32, "scores", 3), B, H, N,
-        _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(),
-        _stream(scores, stream)), "rtp_topp_hist")
+    wp, wn = _ws(workspace)
+    _call("rtp_topp_hist", _dev(scores, torch.float32, "scores", (B, H, N)), B, H, N, wp,
+                               wn, _stream(scores, stream))
 
 
 def rtp_sparse_decode(q, K, V, idx, count, q_head_begin, scale, out, workspace,
@@ -248,16 +326,16 @@ def rtp_sparse_decode(q, K, V, idx, count, q_head_begin, scale, out, workspace,
     """q bf16 [B][Hq][d]; K, V bf16 [B][Hkv][cap][d]; idx i32 [B][n_q][N];
     count i32 [B][n_q]; out f32 [B][Hq][d] (heads in range written)."""
     import torch
-    B, Hq, d = q.shape
-    _, Hkv, cap, _ = K.shape
+    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
+    if count.dim() != 2 or idx.dim() != 3:
+        raise ValueError("count must be [B][n_q] and idx [B][n_q][N]")
     n_q = count.shape[1]
     N = idx.shape[-1] if N is None else N
-    _check(lib().rtp_sparse_decode(
-        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4),
-        _dev(idx, torch.int32, "idx", 3), _dev(count, torch.int32, "count", 2),
-        B, Hq, Hkv, N, cap, d, q_head_begin, n_q, float(scale),
-        _dev(out, torch.float32, "out", 3), _dev(workspace, torch.uint8, "workspace", 1),
-        workspace.numel(), _stream(q, stream)), "rtp_sparse_decode")
+    wp, wn = _ws(workspace)
+    _call("rtp_sparse_decode", 
+        qp, Kp, Vp, _dev(idx, torch.int32, "idx", (B, n_q, N)),
+        _dev(count, torch.int32, "count", (B, n_q)), B, Hq, Hkv, N, cap, d, q_head_begin, n_q,
+        float(scale), op, wp, wn, _stream(q, stream))
 
 
 def rtp_sparse_decode_union(q, K, V, keep_bits, N, q_head_begin, scale, out, workspace,
@@ -265,17 +343,14 @@ def rtp_sparse_decode_union(q, K, V, keep_bits, N, q_head_begin, scale, out, wor
     """q bf16 [B][Hq][d]; K, V bf16 [B][Hkv][cap][d]; keep_bits i32
     [B][n_q][keep_words(N)] as written by rtp_topp_select; out f32 [B][Hq][d]."""
     import torch
-    B, Hq, d = q.shape
-    _, Hkv, cap, _ = K.shape
+    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
+    if keep_bits.dim() != 3:
+        raise ValueError("keep_bits must be [B][n_q][keep_words(N)]")
     n_q = keep_bits.shape[1]
-    if tuple(keep_bits.shape) != (B, n_q, keep_words(N)):
-        raise ValueError(f"keep_bits must have shape {(B, n_q, keep_words(N))}")
-    _check(lib().rtp_sparse_decode_union(
-        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4),
-        _dev(keep_bits, torch.int32, "keep_bits", 3), B, Hq, Hkv, N, cap, d, q_head_begin, n_q,
-        float(scale), _dev(out, torch.float32, "out", 3),
-        _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(), _stream(q, stream)),
-        "rtp_sparse_decode_union")
+    wp, wn = _ws(workspace)
+    _call("rtp_sparse_decode_union", 
+        qp, Kp, Vp, _dev(keep_bits, torch.int32, "keep_bits", (B, n_q, keep_words(N))), B, Hq,
+        Hkv, N, cap, d, q_head_begin, n_q, float(scale), op, wp, wn, _stream(q, stream))
 
 
 def rtp_decode_attend(q, K, V, idx, count, N, sparse_head_begin, local_head_begin,
@@ -286,17 +361,19 @@ def rtp_decode_attend(q, K, V, idx, count, N, sparse_head_begin, local_head_begi
     idx/count may be None (no sparse heads); workspace uint8
     [>= workspace_size(RTP_WS_DECODE_ATTEND, B, Hq, N)]."""
     import torch
-    B, Hq, d = q.shape
-    _, Hkv, cap, _ = K.shape
+    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
     n_sparse = 0 if count is None else count.shape[1]
-    idx_p = None if idx is None else _dev(idx, torch.int32, "idx", 3)
-    count_p = None if count is None else _dev(count, torch.int32, "count", 2)
-    _check(lib().rtp_decode_attend(
-        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4), idx_p, count_p,
-        B, Hq, Hkv, N, cap, d, sparse_head_begin, n_sparse, local_head_begin, n_local_heads,
-        n_sink, window, float(scale), _dev(out, torch.float32, "out", 3),
-        _dev(workspace, torch.uint8, "workspace", 1), workspace.numel(), _stream(q, stream)),
-        "rtp_decode_attend")
+    idx_p = count_p = None
+    if n_sparse:
+        if count.dim() != 2:
+            raise ValueError("count must be [B][n_sparse]")
+        idx_p = _dev(idx, torch.int32, "idx", (B, n_sparse, N))
+        count_p = _dev(count, torch.int32, "count", (B, n_sparse))
+    wp, wn = _ws(workspace)
+    _call("rtp_decode_attend", 
+        qp, Kp, Vp, idx_p, count_p, B, Hq, Hkv, N, cap, d, sparse_head_begin, n_sparse,
+        local_head_begin, n_local_heads, n_sink, window, float(scale), op, wp, wn,
+        _stream(q, stream))
 
 
 def rtp_scan_local(q_r, k_r, scores, q, K, V, N, local_head_begin, n_local_heads, n_sink,
@@ -305,20 +382,46 @@ def rtp_scan_local(q_r, k_r, scores, q, K, V, N, local_head_begin, n_local_heads
     [local_head_begin, + n_local_heads), one launch; scores f32 [B][Hq_r][N];
     workspace uint8 [>= workspace_size(RTP_WS_LOCAL_DECODE, B, n_local_heads, N)]."""
     import torch
-    B, Hq_r, r = q_r.shape
-    _, Hkv_r, kr_cap, _ = k_r.shape
-    _, Hq, d = q.shape
-    _, Hkv, cap, _ = K.shape
-    if tuple(scores.shape) != (B, Hq_r, N) or q.shape[0] != B:
-        raise ValueError(f"scores must be [B][Hq_r][N] = {(B, Hq_r, N)} and q [B][Hq][d], "
-                         f"got {tuple(scores.shape)} and {tuple(q.shape)}")
-    _check(lib().rtp_scan_local(
-        _dev(q_r, torch.float32, "q_r", 3), _dev(k_r, torch.float32, "k_r", 4),
-        _dev(scores, torch.float32, "scores", 3), Hq_r, Hkv_r, kr_cap, r,
-        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4), B, Hq, Hkv, N, cap, d,
-        local_head_begin, n_local_heads, n_sink, window, float(scale),
-        _dev(out, torch.float32, "out", 3), _dev(workspace, torch.uint8, "workspace", 1),
-        workspace.numel(), _stream(q, stream)), "rtp_scan_local")
+    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
+    if q_r.dim() != 3 or k_r.dim() != 4:
+        raise ValueError("q_r must be [B][Hq_r][16] and k_r [B][Hkv_r][cap][16]")
+    Hq_r, r = q_r.shape[1], q_r.shape[2]
+    Hkv_r, kr_cap = k_r.shape[1], k_r.shape[2]
+    wp, wn = _ws(workspace)
+    _call("rtp_scan_local", 
+        _dev(q_r, torch.float32, "q_r", (B, Hq_r, r)),
+        _dev(k_r, torch.float32, "k_r", (B, Hkv_r, kr_cap, r)),
+        _dev(scores, torch.float32, "scores", (B, Hq_r, N)), Hq_r, Hkv_r, kr_cap, r,
+        qp, Kp, Vp, B, Hq, Hkv, N, cap, d, local_head_begin, n_local_heads, n_sink, window,
+        float(scale), op, wp, wn, _stream(q, stream))
+
+
+def rtp_decode_layer(q_r, k_r, q, K, V, N, Hq_r, n_sink, window, p, scale, out, idx, count,
+                     workspace, scores=None, stream=None) -> None:
+    """One decode layer in one launch: query heads [0, Hq_r) are retrieval
+    heads (scan, top-p select, sparse attention), [Hq_r, Hq) local heads
+    (sinks + window).  q_r f32 [B][Hq_r][16]; k_r f32 [B][Hq_r/G][cap][16];
+    q bf16 [B][Hq][d]; K, V bf16 [B][Hkv][cap][d]; out f32 [B][Hq][d];
+    idx i32 [B][Hq_r][N] and count i32 [B][Hq_r] (out); scores f32
+    [B][Hq_r][N] (optional out); workspace uint8
+    [>= decode_layer_workspace_size(B, Hq, Hkv, N, Hq_r, n_sink, window)]."""
+    import torch
+    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
+    if q_r.dim() != 3 or k_r.dim() != 4:
+        raise ValueError("q_r must be [B][Hq_r][16] and k_r [B][Hkv_r][cap][16]")
+    r = q_r.shape[2]
+    G = Hq // Hkv
+    if Hkv < 1 or Hq % Hkv or Hq_r % G:
+        raise ValueError("Hq must be a multiple of Hkv and Hq_r of Hq / Hkv")
+    kr_cap = k_r.shape[2]
+    sp = None if scores is None else _dev(scores, torch.float32, "scores", (B, Hq_r, N))
+    wp, wn = _ws(workspace)
+    _call("rtp_decode_layer", 
+        _dev(q_r, torch.float32, "q_r", (B, Hq_r, r)),
+        _dev(k_r, torch.float32, "k_r", (B, Hq_r // G, kr_cap, r)), kr_cap, qp, Kp, Vp, cap,
+        B, Hq, Hkv, N, d, r, Hq_r, n_sink, window, float(p), float(scale), op,
+        _dev(idx, torch.int32, "idx", (B, Hq_r, N)), _dev(count, torch.int32, "count", (B, Hq_r)),
+        sp, wp, wn, _stream(q, stream))
 
 
 def rtp_prefill_attend(q, K, V, head_begin, n_heads, n_sink, window, scale, out,
@@ -327,36 +430,33 @@ def rtp_prefill_attend(q, K, V, head_begin, n_heads, n_sink, window, scale, out,
     [B][Hq][T][128]: causal prefill for heads [head_begin, + n_heads), dense
     (window <= 0) or sinks + window."""
     import torch
+    if q.dim() != 4 or K.dim() != 4:
+        raise ValueError("q must be [B][Hq][T][d] and K [B][Hkv][cap][d]")
     B, Hq, T, d = q.shape
     _, Hkv, cap, _ = K.shape
-    _check(lib().rtp_prefill_attend(
-        _bf16(q, "q", 4), _bf16(K, "K", 4), _bf16(V, "V", 4), B, Hq, Hkv, T, cap, d,
-        head_begin, n_heads, n_sink, window, float(scale), _dev(out, torch.float32, "out", 4),
-        _stream(q, stream)), "rtp_prefill_attend")
+    _call("rtp_prefill_attend", 
+        _bf16(q, "q", (B, Hq, T, d)), _bf16(K, "K", (B, Hkv, cap, d)),
+        _bf16(V, "V", (B, Hkv, cap, d)), B, Hq, Hkv, T, cap, d, head_begin, n_heads, n_sink,
+        window, float(scale), _dev(out, torch.float32, "out", (B, Hq, T, d)),
+        _stream(q, stream))
 
 
 def rtp_local_decode_ring(q, K, V, N, q_head_begin, n_q_heads, n_sink, window, scale, out,
                           workspace, stream=None) -> None:
     """rtp_local_decode over ring-buffer caches of n_sink + window slots (token
     i >= n_sink in slot n_sink + (i - n_sink) % window); N tokens seen."""
-    import torch
-    B, Hq, d = q.shape
-    _, Hkv, cap, _ = K.shape
-    _check(lib().rtp_local_decode_ring(
-        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4), B, Hq, Hkv, N, cap, d,
-        q_head_begin, n_q_heads, n_sink, window, float(scale),
-        _dev(out, torch.float32, "out", 3), _dev(workspace, torch.uint8, "workspace", 1),
-        workspace.numel(), _stream(q, stream)), "rtp_local_decode_ring")
+    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
+    wp, wn = _ws(workspace)
+    _call("rtp_local_decode_ring", 
+        qp, Kp, Vp, B, Hq, Hkv, N, cap, d, q_head_begin, n_q_heads, n_sink, window,
+        float(scale), op, wp, wn, _stream(q, stream))
 
 
 def rtp_local_decode(q, K, V, N, q_head_begin, n_q_heads, n_sink, window, scale, out,
                      workspace, stream=None) -> None:
     """Local heads [q_head_begin, q_head_begin + n_q_heads): sinks + window."""
-    import torch
-    B, Hq, d = q.shape
-    _, Hkv, cap, _ = K.shape
-    _check(lib().rtp_local_decode(
-        _bf16(q, "q", 3), _bf16(K, "K", 4), _bf16(V, "V", 4), B, Hq, Hkv, N, cap, d,
-        q_head_begin, n_q_heads, n_sink, window, float(scale),
-        _dev(out, torch.float32, "out", 3), _dev(workspace, torch.uint8, "workspace", 1),
-        workspace.numel(), _stream(q, stream)), "rtp_local_decode")
+    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
+    wp, wn = _ws(workspace)
+    _call("rtp_local_decode", 
+        qp, Kp, Vp, B, Hq, Hkv, N, cap, d, q_head_begin, n_q_heads, n_sink, window,
+        float(scale), op, wp, wn, _stream(q, stream))

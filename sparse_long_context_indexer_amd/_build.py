@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librtp.so")
-SOURCES = ["abi.hip", "scan.hip", "select.hip", "attend.hip", "project.hip", "prefill.hip"]
+SOURCES = ["abi.hip", "scan.hip", "select.hip", "attend.hip", "layer.hip", "project.hip",
+           "prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

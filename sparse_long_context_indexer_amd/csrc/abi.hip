@@ -5,10 +5,38 @@
 #include <stdint.h>
 
 
+#include <atomic>
+
 #include "rtp.h"
+#include "rtp_device.h"
 #include "rtp_launch.h"
 
+// The library's sticky status word, one per device (each device holds its
+// own copy of a __device__ variable; its address is looked up per device).
+static __device__ uint32_t rtp_status_word;
+
 namespace {
+
+std::atomic<uint32_t> g_wait_limit{rtp::kSpinMax};
+
+// The current device's status word (looked up once per device).
+hipError_t status_word(uint32_t **p)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<uint32_t *> cache[kMaxDevices];
+    int dev = 0;
+    RTP_TRY(hipGetDevice(&dev));
+    uint32_t *w = dev >= 0 && dev < kMaxDevices ? cache[dev].load(std::memory_order_acquire)
+                                                : nullptr;
+    if (!w) {
+        void *a = nullptr;
+        RTP_TRY(hipGetSymbolAddress(&a, HIP_SYMBOL(rtp_status_word)));
+        w = static_cast<uint32_t *>(a);
+        if (dev >= 0 && dev < kMaxDevices) cache[dev].store(w, std::memory_order_release);
+    }
+    *p = w;
+    return hipSuccess;
+}
 
 constexpr int kMaxGridY = 65535;
 
@@ -45,6 +73,16 @@ rtp_status check_attention_common(const void *q, const void *K, const void *V, c
 
 }  // namespace
 
+namespace rtp {
+
+hipError_t wait_ctl(WaitCtl *wc)
+{
+    wc->limit = g_wait_limit.load(std::memory_order_relaxed);
+    return status_word(&wc->status);
+}
+
+}  // namespace rtp
+
 extern "C" {
 
 const char *rtp_status_string(rtp_status s)
@@ -63,6 +101,26 @@ const char *rtp_status_string(rtp_status s)
 }
 
 int32_t rtp_last_hip_error(void) { return last_hip_error; }
+
+rtp_status rtp_set_wait_limit(uint32_t polls)
+{
+    g_wait_limit.store(polls, std::memory_order_relaxed);
+    return RTP_OK;
+}
+
+rtp_status rtp_device_status(uint32_t *flags, int32_t clear)
+{
+    if (!flags) return RTP_ERR_NULL;
+    uint32_t *w = nullptr;
+    hipError_t e = status_word(&w);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(flags, w, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && clear) {
+        const uint32_t zero = 0;
+        e = hipMemcpy(w, &zero, sizeof(uint32_t), hipMemcpyHostToDevice);
+    }
+    return from_hip(e);
+}
 
 rtp_status rtp_workspace_size(int32_t which, int32_t B, int32_t H, int32_t N, size_t *bytes)
 {
@@ -321,6 +379,73 @@ rtp_status rtp_decode_attend(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf1
                                               sparse_head_begin, n_sparse_heads,
                                               local_head_begin, n_local_heads, n_sink, window,
                                               scale, out, workspace, as_stream(stream)));
+}
+
+// The sizes of a one-launch layer, checked on the host alone.
+static rtp_status layer_sizes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t Hq_r,
+                              int32_t n_sink, int32_t window)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N < 1 || Hq_r < 1 || Hq_r > Hq)
+        return RTP_ERR_SHAPE;
+    if (Hq_r % (Hq / Hkv) != 0) return RTP_ERR_SHAPE;  // whole KV heads
+    if (Hq_r < Hq && (n_sink < 0 || window < 1)) return RTP_ERR_VALUE;
+    return RTP_OK;
+}
+
+// The geometry of a one-launch layer on the current device (sizes checked).
+static rtp_status layer_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t Hq_r,
+                              int32_t n_sink, int32_t window, rtp::LayerGeom *L)
+{
+    const rtp_status st = layer_sizes(B, Hq, Hkv, N, Hq_r, n_sink, window);
+    if (st != RTP_OK) return st;
+    int cus = 0;
+    const hipError_t e = rtp::device_cus(&cus);
+    if (e != hipSuccess) return from_hip(e);
+    *L = rtp::layer_geom(cus, B, Hq, Hkv, N, Hq_r, Hq_r < Hq ? n_sink : 0,
+                         Hq_r < Hq ? window : 1);
+    return L->ok ? RTP_OK : RTP_ERR_UNSUPPORTED;
+}
+
+rtp_status rtp_decode_layer_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                                           int32_t Hq_r, int32_t n_sink, int32_t window,
+                                           size_t *bytes)
+{
+    if (!bytes) return RTP_ERR_NULL;
+    rtp::LayerGeom L;
+    const rtp_status st = layer_shape(B, Hq, Hkv, N, Hq_r, n_sink, window, &L);
+    if (st != RTP_OK) return st;
+    *bytes = rtp::layer_ws_bytes(L, B, N);
+    return RTP_OK;
+}
+
+rtp_status rtp_decode_layer(const float *q_r, const float *k_r, int64_t kr_cap,
+                            const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,
+                            int64_t kv_cap, int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                            int32_t d, int32_t r, int32_t Hq_r, int32_t n_sink, int32_t window,
+                            float p, float scale, float *out, int32_t *idx, int32_t *count,
+                            float *scores, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!q_r || !k_r || !q || !K || !V || !out || !idx || !count || !workspace)
+        return RTP_ERR_NULL;
+    if (d != 128 || r != 16) return RTP_ERR_UNSUPPORTED;
+    if (N < 1 || kr_cap < N || kv_cap < N) return RTP_ERR_SHAPE;
+    rtp_status st = layer_sizes(B, Hq, Hkv, N, Hq_r, n_sink, window);
+    if (st != RTP_OK) return st;
+    if (!(p > 0.0f && p <= 1.0f) || !isfinite(scale)) return RTP_ERR_VALUE;
+    if (!aligned(q_r, 16) || !aligned(k_r, 16) || !aligned(q, 16) || !aligned(K, 16) ||
+        !aligned(V, 16) || !aligned(out, 4) || !aligned(idx, 4) || !aligned(count, 4) ||
+        !aligned(scores, 4) || !aligned(workspace, 256))
+        return RTP_ERR_ALIGN;
+    rtp::LayerGeom L;
+    st = layer_shape(B, Hq, Hkv, N, Hq_r, n_sink, window, &L);
+    if (st != RTP_OK) return st;
+    if (ws_bytes < rtp::layer_ws_bytes(L, B, N)) return RTP_ERR_WORKSPACE;
+    rtp::WaitCtl wc;
+    hipError_t e = rtp::wait_ctl(&wc);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(rtp::launch_decode_layer(L, q_r, k_r, kr_cap, q, K, V, kv_cap, B, Hq, Hkv, N,
+                                             Hq_r, p, scale, out, idx, count, scores, workspace,
+                                             wc.limit, wc.status, as_stream(stream)));
 }
 
 rtp_status rtp_scan_local(const float *q_r, const float *k_r, float *scores, int32_t Hq_r,

@@ -69,6 +69,7 @@ struct SparseWs {
     float *super;          // [R][kMaxSlices] slice merges
     uint32_t *part_flag;   // one hand-off flag per partial
     uint32_t *super_flag;  // [R][kMaxSlices]
+    WaitCtl wc;            // poll limit of the flag waits, where a give-up is reported
 };
 
 static size_t sparse_ws_layout(int64_t R, SparseWs *W, void *base)
@@ -399,7 +400,7 @@ __device__ void sparse_block(const uint16_t *__restrict__ q, const uint16_t *__r
         return;
     }
     wait_vmem();  // this block's own partial, read back below by other threads
-    await_flags(W.part_flag + k0, in_slice - 1);
+    await_flags(W.part_flag + k0, in_slice - 1, W.wc);
     const float *first = W.part + (int64_t)k0 * kPart;
     if (slices == 1) {
         merge_partials(first, in_slice, nullptr, dst, MS);
@@ -413,7 +414,7 @@ __device__ void sparse_block(const uint16_t *__restrict__ q, const uint16_t *__r
         return;
     }
     wait_vmem();
-    await_flags(sf, slices - 1);
+    await_flags(sf, slices - 1, W.wc);
     merge_partials(sp, slices, nullptr, dst, MS);
 }
 
@@ -1185,8 +1186,10 @@ static hipError_t launch_attend(const uint16_t *q, const uint16_t *K, const uint
 {
     const int blocks = L.blocks + P.blocks;
     if (blocks == 0) return hipSuccess;
+    SparseArgs Pw = P;
+    RTP_TRY(wait_ctl(&Pw.W.wc));
     return launch(attend_kernel, dim3(blocks), dim3(kAttThreads), 0, stream, q, K, V, N, kv_cap,
-                  Hq, Hkv, scale * kLog2e, L, P, out);
+                  Hq, Hkv, scale * kLog2e, L, Pw, out);
 }
 
 hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,

@@ -225,11 +225,24 @@ __device__ __forceinline__ uint4 ld_nt16(const void *p)
 // Waits until every vector memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Polls before a wait on other blocks gives up.  Every wait in the library
-// is on blocks dispatched before the waiting one that never wait for a later
-// block, so a wait ends long before this; the bound only keeps a fault
-// elsewhere from hanging the device.
-constexpr int kSpinMax = 1 << 24;
+// Polls before a wait on other blocks gives up, unless the host sets
+// another limit (rtp_set_wait_limit).  A wait ends long before this; the
+// bound only keeps a fault elsewhere from hanging the device.
+constexpr uint32_t kSpinMax = 1u << 24;
+
+// Bits of the library's sticky status word (rtp_device_status).
+constexpr uint32_t kStatusWaitTimeout = 1u;  // a bounded wait gave up
+
+// What a waiting kernel needs: the poll limit and where to report a give-up.
+struct WaitCtl {
+    uint32_t limit;
+    uint32_t *status;
+};
+
+__device__ __forceinline__ void report_timeout(const WaitCtl &wc)
+{
+    if (wc.status) atomicOr(wc.status, kStatusWaitTimeout);
+}
 
 // Hand-off flags: a block publishes a result it stored with agent-scope
 // stores by setting a flag word to kFlagTag once every thread's stores have
@@ -247,13 +260,19 @@ __device__ __forceinline__ void publish_flag(uint32_t *flag)
 
 // Threads 0 .. n-1 each wait for one of the flags f[0 .. n) and clear it;
 // the block then continues together.  n must not exceed the block size.
-__device__ __forceinline__ void await_flags(uint32_t *f, int n)
+// A flag still unset after wc.limit polls is given up on and the give-up
+// reported in the status word.
+__device__ __forceinline__ void await_flags(uint32_t *f, int n, const WaitCtl &wc)
 {
     if ((int)threadIdx.x < n) {
-        for (int it = 0; it < kSpinMax; ++it) {
+        for (uint32_t it = 0;; ++it) {
             if (__hip_atomic_load(f + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                 kFlagTag)
                 break;
+            if (it >= wc.limit) {
+                report_timeout(wc);
+                break;
+            }
             __builtin_amdgcn_s_sleep(1);
         }
         __hip_atomic_store(f + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

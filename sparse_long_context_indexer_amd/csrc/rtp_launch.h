@@ -8,6 +8,12 @@
 
 namespace rtp {
 
+// Poll limit and status word for kernels whose blocks wait on each other
+// (rtp_device.h); filled from the host-set limit and the current device's
+// status word.
+struct WaitCtl;
+hipError_t wait_ctl(WaitCtl *wc);
+
 // ---- indexer scan (scan.hip)
 hipError_t launch_index_scores(const float *q_r, const float *k_r, float *scores,
                                int B, int Hq_r, int Hkv_r, int N, int64_t kr_cap,
@@ -95,6 +101,32 @@ hipError_t launch_scan_local(const float *q_r, const float *k_r, float *scores, 
                              float scale, float *out, void *ws, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- one-launch decode layer (layer.hip)
+struct LayerGeom {
+    bool ok;       // false: the shape is outside what one launch holds
+    int G;         // query heads per KV head
+    int Hkv_r;     // retrieval KV heads
+    int RG;        // B * Hkv_r score rows of G heads
+    int bpr;       // blocks per row
+    int C;         // tokens per block
+    int NB;        // blocks (at most one per compute unit)
+    int ngrp;      // groups of up to 16 blocks per row
+    int n_lkv;     // local KV heads
+    int nlt;       // local tiles per (batch row, local KV head)
+    int NI;        // local items
+    int nl_rows;   // sink + window rows
+    int sink_end;  // sinks are rows [0, sink_end)
+    int w0;        // the window is rows [w0, N)
+};
+LayerGeom layer_geom(int cus, int B, int Hq, int Hkv, int N, int Hq_r, int n_sink, int window);
+size_t layer_ws_bytes(const LayerGeom &L, int B, int N);
+hipError_t launch_decode_layer(const LayerGeom &L, const float *q_r, const float *k_r,
+                               int64_t kr_cap, const uint16_t *q, const uint16_t *K,
+                               const uint16_t *V, int64_t kv_cap, int B, int Hq, int Hkv, int N,
+                               int Hq_r, float p, float scale, float *out, int32_t *idx,
+                               int32_t *count, float *scores, void *ws, uint32_t spin_limit,
+                               uint32_t *status, hipStream_t stream);
 
 // Compute units of the current device (queried once per device).
 hipError_t device_cus(int *cus);

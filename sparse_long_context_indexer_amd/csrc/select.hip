@@ -104,6 +104,7 @@ struct SelPtrs {
     ChunkTop *tops;
     uint2 *cand;
     int nblk;
+    WaitCtl wc;  // poll limit of the waits on earlier blocks, and where a give-up is reported
 };
 
 static SelPtrs sel_ptrs(void *ws, int64_t R, int64_t N)
@@ -217,16 +218,21 @@ __device__ void clear_row(SelPtrs P, int64_t r)
 
 // Every block waited for below was dispatched before the waiting one (block
 // 0 of the row; in the one-launch selection, the row's histogram blocks);
-// waits are bounded by kSpinMax polls.
+// waits are bounded by wc.limit polls, and a give-up is reported in the
+// library's status word.
 
 // Waits until the row's tagged `ready` counter holds at least `level`: 1
 // once block 0 has cleared the row, 2 once the row's Hist1 is complete
 // (one-launch selection only).
-__device__ void wait_row_ready(const SelRow &row, uint32_t level)
+__device__ void wait_row_ready(const SelRow &row, uint32_t level, const WaitCtl &wc)
 {
-    for (int it = 0; it < kSpinMax; ++it) {
+    for (uint32_t it = 0;; ++it) {
         const unsigned long long v = ld_agent(&row.ready);
         if ((uint32_t)v == kCtrTag && (uint32_t)(v >> 32) >= level) return;
+        if (it >= wc.limit) {
+            report_timeout(wc);
+            return;
+        }
         __builtin_amdgcn_s_sleep(2);
     }
 }
@@ -299,7 +305,7 @@ __device__ void hist_body(const float (&v)[kSelPerThread], const ChunkView &cv, 
             atomicAdd(&hm[bin], exp_tang((double)(v[t] - ref), etbl));
     }
     if (blk != 0 && threadIdx.x == 0 && !((uint32_t)rdy == kCtrTag && (rdy >> 32) >= 1))
-        wait_row_ready(P.rows[r], 1u);
+        wait_row_ready(P.rows[r], 1u, P.wc);
     __syncthreads();
     Hist1 &g = P.hist1[r];
     for (int i = threadIdx.x; i < kBins1; i += kSelThreads) {
@@ -1084,7 +1090,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(
     const int64_t r = blockIdx.y - R;
     float v[kSelPerThread];
     const ChunkView cv = load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);
-    if (threadIdx.x == 0) wait_row_ready(P.rows[r], 2u);
+    if (threadIdx.x == 0) wait_row_ready(P.rows[r], 2u, P.wc);
     __syncthreads();
     PickIn pi;
     pick_inputs(P, r, pi);
@@ -1149,6 +1155,7 @@ constexpr int64_t kMaxFusedRows = 65535;  // grid rows of one launch
 hipError_t launch_topp_hist(const float *scores, int64_t R, int N, void *ws, hipStream_t stream)
 {
     SelPtrs P = sel_ptrs(ws, R, N);
+    RTP_TRY(wait_ctl(&P.wc));
     return launch(sel_hist_kernel<false>, dim3((unsigned)P.nblk, (unsigned)R), dim3(kSelThreads),
                   0, stream, scores, N, P);
 }
@@ -1167,6 +1174,7 @@ static hipError_t launch_select(const float *scores, int64_t R, int N, double ta
                                 hipStream_t stream)
 {
     SelPtrs P = sel_ptrs(ws, R, N);
+    RTP_TRY(wait_ctl(&P.wc));
     if (2 * R <= kMaxFusedRows)
         return launch(sel_fused_kernel<kCount>, dim3((unsigned)P.nblk, (unsigned)(2 * R)),
                       dim3(kSelThreads), 0, stream, scores, N, P, target, idx, count, keep_bits);

@@ -11,9 +11,10 @@ from __future__ import annotations
 import torch
 
 from . import (RTP_WS_DECODE_ATTEND, RTP_WS_LOCAL_DECODE, RTP_WS_SPARSE_DECODE,
-               RTP_WS_SPARSE_UNION, RTP_WS_TOPP_SELECT, keep_words, rtp_decode_attend,
-               rtp_index_scores, rtp_index_scores_bf16, rtp_local_decode, rtp_scan_local, rtp_sparse_decode,
-               rtp_sparse_decode_union, rtp_topp_select, workspace_size)
+               RTP_WS_SPARSE_UNION, RTP_WS_TOPP_SELECT, decode_layer_workspace_size, keep_words,
+               rtp_decode_attend, rtp_decode_layer, rtp_index_scores, rtp_index_scores_bf16,
+               rtp_local_decode, rtp_scan_local, rtp_sparse_decode, rtp_sparse_decode_union,
+               rtp_topp_select, workspace_size)
 
 
 class DecodeLayer:
@@ -24,17 +25,32 @@ class DecodeLayer:
     the sparse heads alone; mode "per_head": rtp_sparse_decode and rtp_local_decode
     as separate calls; mode "union": the selector also writes keep bitmaps
     and the sparse heads run rtp_sparse_decode_union (each kept row read once
-    per KV head)."""
+    per KV head); mode "layer": the whole layer in one rtp_decode_layer launch
+    (scores kept on chip; with keep_scores they are also written out, for
+    checking)."""
 
     def __init__(self, B: int, Hq: int, Hkv: int, N: int, H_r: int, n_sink: int,
-                 window: int, device, d: int = 128, mode: str = "fused"):
-        if mode not in ("fused", "scan_local", "union", "per_head"):
+                 window: int, device, d: int = 128, mode: str = "fused",
+                 keep_scores: bool = True):
+        if mode not in ("fused", "scan_local", "union", "per_head", "layer"):
             raise ValueError(f"unknown mode {mode!r}")
+        self.keep_scores = keep_scores
         self.B, self.Hq, self.Hkv, self.N, self.H_r = B, Hq, Hkv, N, H_r
         self.n_sink, self.window, self.d, self.mode = n_sink, window, d, mode
         self.H_l = Hq - H_r
         dev = torch.device(device)
         self.keep_bits = None
+        if mode == "layer":
+            if H_r < 1:
+                raise ValueError("mode 'layer' needs retrieval heads")
+            self.scores = (torch.empty((B, H_r, N), dtype=torch.float32, device=dev)
+                           if keep_scores else None)
+            self.idx = torch.empty((B, H_r, N), dtype=torch.int32, device=dev)
+            self.count = torch.empty((B, H_r), dtype=torch.int32, device=dev)
+            self.ws_layer = torch.empty(
+                decode_layer_workspace_size(B, Hq, Hkv, N, H_r, n_sink, window),
+                dtype=torch.uint8, device=dev)
+            return
         if H_r > 0:
             self.scores = torch.empty((B, H_r, N), dtype=torch.float32, device=dev)
             self.idx = torch.empty((B, H_r, N), dtype=torch.int32, device=dev)
@@ -92,6 +108,13 @@ class DecodeLayer:
         side_stream, the local heads run there concurrently with the
         retrieval chain (the two share no buffer); the current stream waits
         for them before returning."""
+        if self.mode == "layer":
+            if k_r.dtype != torch.float32:
+                raise ValueError("mode 'layer' takes an fp32 indexer key cache")
+            rtp_decode_layer(q_r, k_r, q, K, V, self.N, self.H_r, self.n_sink, self.window, p,
+                             scale, out, self.idx, self.count, self.ws_layer,
+                             scores=self.scores)
+            return
         if self.mode == "scan_local" and self.H_r > 0 and self.H_l > 0:
             rtp_scan_local(q_r, k_r, self.scores, q, K, V, self.N, self.H_r, self.H_l,
                            self.n_sink, self.window, scale, out, self.ws_local)

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 21
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -351,3 +351,111 @@ def test_topp_hist_validation(lib):
     assert f(A + 2, 1, 8, 1000, A, ws, None) == 5
     assert f(A, 1, 8, 1000, A + 16, ws, None) == 5
     assert f(A, 1, 8, 1000, A, ws - 1, None) == 6
+
+
+def test_decode_layer_validation(lib):
+    # Host-side checks of rtp_decode_layer, in order: NULL, unsupported
+    # dimensions, sizes, values, alignment; all before any device query.
+    f = lib.rtp_decode_layer
+    pos = {"q_r": 0, "k_r": 1, "kr_cap": 2, "q": 3, "K": 4, "V": 5, "kv_cap": 6, "B": 7,
+           "Hq": 8, "Hkv": 9, "N": 10, "d": 11, "r": 12, "Hq_r": 13, "sink": 14, "win": 15,
+           "p": 16, "scale": 17, "out": 18, "idx": 19, "count": 20, "scores": 21, "ws": 22,
+           "wsb": 23}
+    args = [A, A, 1000, A, A, A, 1000, 1, 32, 4, 1000, 128, 16, 8, 4, 4096, 0.9, 0.088, A, A, A,
+            None, A, 1 << 30, None]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    for name in ("q_r", "k_r", "q", "K", "V", "out", "idx", "count", "ws"):
+        assert call(**{name: None}) == 1, name
+    assert call(d=64) == 3 and call(r=8) == 3
+    assert call(N=0) == 2 and call(kr_cap=999) == 2 and call(kv_cap=999) == 2
+    assert call(B=0) == 2 and call(Hkv=3) == 2 and call(Hq_r=0) == 2 and call(Hq_r=33) == 2
+    assert call(Hq_r=12) == 2                   # not whole KV heads (G = 8)
+    assert call(sink=-1) == 4 and call(win=0) == 4
+    for p in (0.0, -0.1, 1.01, float("nan")):
+        assert call(p=p) == 4, p
+    assert call(scale=float("inf")) == 4
+    assert call(q_r=A + 4) == 5 and call(K=A + 8) == 5 and call(scores=A + 2) == 5
+    assert call(ws=A + 16) == 5 and call(idx=A + 2) == 5
+    # With every head a retrieval head, n_sink and window are not checked.
+    assert call(Hq_r=32, sink=-1, win=0, q_r=A + 4) == 5
+    with pytest.raises(rtp.RtpError) as e:
+        rtp.decode_layer_workspace_size(1, 32, 4, 0, 8, 4, 4096)
+    assert e.value.status == 2
+    assert lib.rtp_decode_layer_workspace_size(1, 32, 4, 100, 8, 4, 4096, None) == 1
+
+
+def test_wait_limit_and_status_entry_points(lib):
+    assert lib.rtp_set_wait_limit(1 << 24) == 0
+    assert lib.rtp_device_status(None, 0) == 1
+
+
+def _cpu(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_checks_every_shape():
+    # Every tensor's full shape is checked against the sizes the C call will
+    # read; a mismatch raises before anything reaches the library (these
+    # tensors live on the host, so a call that passed the checks would stop
+    # at the device check instead).
+    import torch
+    f32, i32, bf, u8 = torch.float32, torch.int32, torch.bfloat16, torch.uint8
+    ws = _cpu((64,), u8)
+    B, Hq, Hkv, N, cap = 2, 32, 4, 100, 120
+    q, K, V = _cpu((B, Hq, 128), bf), _cpu((B, Hkv, cap, 128), bf), _cpu((B, Hkv, cap, 128), bf)
+    out = _cpu((B, Hq, 128), f32)
+    bad = [
+        lambda: rtp.rtp_index_scores(_cpu((B, 8, 16), f32), _cpu((B + 1, 1, cap, 16), f32),
+                                     _cpu((B, 8, N), f32)),
+        lambda: rtp.rtp_index_scores(_cpu((B, 8, 16), f32), _cpu((B, 1, cap, 16), f32),
+                                     _cpu((B, 7, N), f32)),
+        lambda: rtp.rtp_topp_select(_cpu((B, 8, N), f32), 0.9, _cpu((B, 8, N - 1), i32),
+                                    _cpu((B, 8), i32), ws),
+        lambda: rtp.rtp_topp_select(_cpu((B, 8, N), f32), 0.9, _cpu((B, 8, N), i32),
+                                    _cpu((B, 7), i32), ws),
+        lambda: rtp.rtp_topk_select(_cpu((B, 8, N), f32), 5, _cpu((B, 8, N), i32),
+                                    _cpu((B + 1, 8), i32), ws),
+        lambda: rtp.rtp_sparse_decode(q, K, V, _cpu((B, 8, N), i32), _cpu((B, 8), i32), 0, 0.1,
+                                      _cpu((B, Hq, 64), f32), ws),
+        lambda: rtp.rtp_sparse_decode(q, K, _cpu((B, Hkv, cap - 1, 128), bf),
+                                      _cpu((B, 8, N), i32), _cpu((B, 8), i32), 0, 0.1, out, ws),
+        lambda: rtp.rtp_sparse_decode(q, K, V, _cpu((B, 8, N), i32), _cpu((B, 8), i32), 0, 0.1,
+                                      out, ws, N=N + 1),
+        lambda: rtp.rtp_sparse_decode(q, K, V, _cpu((1, 8, N), i32), _cpu((B, 8), i32), 0, 0.1,
+                                      out, ws),
+        lambda: rtp.rtp_sparse_decode_union(q, K, V, _cpu((B, 8, 3), i32), N, 0, 0.1, out, ws),
+        lambda: rtp.rtp_decode_attend(q, K, V, _cpu((B, 8, N - 1), i32), _cpu((B, 8), i32), N,
+                                      0, 8, 24, 4, 4096, 0.1, out, ws),
+        lambda: rtp.rtp_local_decode(q, _cpu((B + 1, Hkv, cap, 128), bf), V, N, 8, 24, 4, 4096,
+                                     0.1, out, ws),
+        lambda: rtp.rtp_local_decode_ring(q, K, V, N, 8, 24, 4, 4096, 0.1,
+                                          _cpu((B, Hq - 1, 128), f32), ws),
+        lambda: rtp.rtp_scan_local(_cpu((B, 8, 16), f32), _cpu((B, 1, cap, 16), f32),
+                                   _cpu((B, 8, N + 1), f32), q, K, V, N, 8, 24, 4, 4096, 0.1,
+                                   out, ws),
+        lambda: rtp.rtp_prefill_attend(_cpu((B, Hq, 50, 128), bf), K, V, 0, 8, 0, 0, 0.1,
+                                       _cpu((B, Hq, 49, 128), f32)),
+        lambda: rtp.rtp_decode_layer(_cpu((B, 8, 16), f32), _cpu((B, 2, cap, 16), f32), q, K, V,
+                                     N, 8, 4, 4096, 0.9, 0.1, out, _cpu((B, 8, N), i32),
+                                     _cpu((B, 8), i32), ws),
+        lambda: rtp.rtp_decode_layer(_cpu((B, 8, 16), f32), _cpu((B, 1, cap, 16), f32), q, K, V,
+                                     N, 8, 4, 4096, 0.9, 0.1, out, _cpu((B, 8, N + 1), i32),
+                                     _cpu((B, 8), i32), ws),
+        lambda: rtp.rtp_decode_layer(_cpu((B, 8, 16), f32), _cpu((B, 1, cap, 16), f32), q, K, V,
+                                     N, 8, 4, 4096, 0.9, 0.1, out, _cpu((B, 8, N), i32),
+                                     _cpu((B, 8), i32), ws, scores=_cpu((B, 8, N - 1), f32)),
+        lambda: rtp.rtp_index_project(_cpu((B, 4, 50, 128), bf), _cpu((2, 16, 128), bf),
+                                      _cpu((B, 3, 60, 16), f32)),
+        lambda: rtp.rtp_keep_bits_add_local(_cpu((B, 8, 5), i32), N, 4, 64),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError) as e:
+            call()
+        assert "device tensor" not in str(e.value), (i, str(e.value))
