@@ -4,16 +4,19 @@ One step = one decode step through a 48-layer attention stack at N = 2^20
 cached tokens (batch 1, 32 query / 4 KV heads, d = 128, bf16 K/V ~ 96 GiB
 resident): per layer, the indexer scan, top-p selection and sparse
 attention for the 8 retrieval query heads of KV head 0, and sink + window
-attention for the 24 local query heads.  Layers run in sequence.  The step is
-captured once in a HIP graph and replayed.
+attention for the 24 local query heads.  Layers run in sequence; by default
+each layer is one rtp_decode_layer launch.  The step is captured once in a
+HIP graph and replayed.
 
-Prints ONE JSON line (rank 0) with steps/s, the dominant kernel's roofline
-and the CPU oracle's baseline on a bounded sample.
+Prints ONE JSON line (rank 0) with steps/s, the dominant kernel's roofline,
+the CPU oracle's baseline on a bounded sample, the four-call path timed
+beside it, and one record per smaller workload (configs 1-3, each p).
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -39,13 +42,20 @@ def parse():
     ap.add_argument("--p", type=float, default=0.9)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-side-stream", action="store_true")
-    ap.add_argument("--sparse-mode", choices=["fused", "scan_local", "union", "per_head"],
+    ap.add_argument("--sparse-mode", choices=["layer", "fused", "scan_local", "union",
+                                              "per_head"],
                     default="fused",
-                    help="scan_local: scan and local heads in one rtp_scan_local launch, sparse "
+                    help="layer: the whole layer in one rtp_decode_layer launch; scan_local: "
+                         "scan and local heads in one rtp_scan_local launch, sparse "
                          "heads in rtp_decode_attend; fused: sparse and local heads in one "
                          "rtp_decode_attend launch; per_head: separate calls, local heads on "
                          "a side stream; union: each kept row read once per KV head for all "
                          "its query heads")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the records of the smaller workloads (configs 1-3)")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the reference calls (four-call path, top-k, bf16 keys, "
+                         "projections, prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -107,63 +117,68 @@ def main():
     log(f"inputs resident ({time.time() - t0:.1f}s)")
 
     step_layer = DecodeLayer(B, Hq, Hkv, N, H_r, cfg.n_sink, cfg.window, dev,
-                             mode=args.sparse_mode)
+                             mode=args.sparse_mode, keep_scores=False)
     scale = cfg.scale
 
     # Local heads of a layer run on a side stream, overlapping the retrieval
     # chain of the same layer; each layer joins both before the next starts.
-    side = (None if args.no_side_stream or args.sparse_mode in ("fused", "scan_local")
+    side = (None if args.no_side_stream or args.sparse_mode in ("layer", "fused", "scan_local")
             else torch.cuda.Stream(device=dev))
-
-    def step():
-        for l in range(L):
-            step_layer(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l], p, scale, out_all[l],
-                       side_stream=side)
-
     stream = torch.cuda.current_stream(dev)
-    if args.no_graph:
-        run = step
-    else:
-        step()  # warm the caching allocator outside capture
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
-        run = graph.replay
 
-    # ---------------------------------------------------------- timing
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        run()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f})")
+    def timed_step(layer_call, steps, warmup):
+        """ms per step of layer_call(l) for l < L, captured once as a HIP
+        graph (unless --no-graph) and replayed between HIP events."""
+        def step():
+            for l in range(L):
+                layer_call(l)
+        if args.no_graph:
+            run = step
+        else:
+            step()  # warm the caching allocator outside capture
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+            run = graph.replay
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - w) / steps * 1e3
+        return e0.elapsed_time(e1) / steps, wall
+
+    ms_step, wall_step = timed_step(
+        lambda l: step_layer(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l], p, scale,
+                             out_all[l], side_stream=side), args.steps, args.warmup)
+    log(f"timed {args.steps} steps ({args.sparse_mode}): {ms_step:.3f} ms/step "
+        f"(wall {wall_step:.3f})")
 
     # ------------------------------------------ per-call timing
-    # Each C-ABI call of the step, for every layer with that layer's own
-    # inputs (scores, kept sets), captured as one HIP graph of L launches so
-    # that no host launch gap separates them, and replayed between HIP
-    # events on the stream the launches run on: the time per launch is the
-    # kernels' own duration back to back.
-    sl = step_layer
-    scores_l = torch.empty((L, B, H_r, N), dtype=torch.float32, device=dev)
+    # Each C-ABI call, for every layer with that layer's own inputs, captured
+    # as one HIP graph of L launches so that no host launch gap separates
+    # them, and replayed between HIP events on the stream the launches run
+    # on: the time per launch is the kernels' own duration back to back.
     idx_l = torch.empty((L, B, H_r, N), dtype=torch.int32, device=dev)
     count_l = torch.empty((L, B, H_r), dtype=torch.int32, device=dev)
-    keep_l = (torch.empty((L,) + tuple(sl.keep_bits.shape), dtype=torch.int32, device=dev)
-              if sl.keep_bits is not None else None)
+    ws_layer = torch.empty(rtp.decode_layer_workspace_size(B, Hq, Hkv, N, H_r, cfg.n_sink,
+                                                           cfg.window),
+                           dtype=torch.uint8, device=dev)
+
+    def layer_call(l):
+        rtp.rtp_decode_layer(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l], N, H_r,
+                             cfg.n_sink, cfg.window, p, scale, out_all[l], idx_l[l], count_l[l],
+                             ws_layer)
+
     for l in range(L):
-        rtp.rtp_index_scores(qr_all[l], kr_all[l], scores_l[l])
-        rtp.rtp_topp_select(scores_l[l], p, idx_l[l], count_l[l], sl.ws_sel,
-                            keep_bits=None if keep_l is None else keep_l[l])
+        layer_call(l)
     torch.cuda.synchronize()
 
     def time_call(issue, reps=5):
@@ -184,144 +199,23 @@ def main():
         del g
         return a.elapsed_time(b) / reps / L * 1e3  # us per launch (one layer)
 
-    us = {
-        "rtp_index_scores": time_call(lambda: [rtp.rtp_index_scores(qr_all[l], kr_all[l],
-                                                                    scores_l[l])
-                                               for l in range(L)]),
-        "rtp_topp_select": time_call(lambda: [rtp.rtp_topp_select(
-            scores_l[l], p, idx_l[l], count_l[l], sl.ws_sel,
-            keep_bits=None if keep_l is None else keep_l[l]) for l in range(L)]),
-        "rtp_topp_hist": time_call(lambda: [rtp.rtp_topp_hist(scores_l[l], sl.ws_sel)
-                                            for l in range(L)]),
-    }
-    # Static top-k, the fixed budget that dynamic top-p replaces, timed on the
-    # same scores at the workload's mean top-p budget: a reference call, not
-    # part of the step (sel_fused_kernel<true>, the same launch shape).
-    k_budget = max(1, int(round(float(count_l.float().mean().item()))))
-    idx_k = torch.empty_like(idx_l[0])
-    count_k = torch.empty_like(count_l[0])
-    us["rtp_topk_select"] = time_call(lambda: [rtp.rtp_topk_select(
-        scores_l[l], k_budget, idx_k, count_k, sl.ws_sel) for l in range(L)])
-    # The scan over a bf16 copy of the indexer key cache (32 B per token
-    # instead of 64), a reference call: the step scans the fp32 cache.
-    kr_b = kr_all.to(torch.bfloat16).view(torch.int16)
-    us["rtp_index_scores_bf16"] = time_call(lambda: [rtp.rtp_index_scores_bf16(
-        qr_all[l], kr_b[l % kr_b.shape[0]], scores_l[l]) for l in range(L)])
-    # The whole step with the bf16 key caches (the runner scans them with
-    # rtp_index_scores_bf16), captured and replayed like the step above: a
-    # reference figure for that variant, not the headline.
-    def step_bf16():
-        for l in range(L):
-            step_layer(qr_all[l], kr_b[l], q_all[l], K_all[l], V_all[l], p, scale, out_all[l],
-                       side_stream=side)
-    step_bf16()
-    torch.cuda.synchronize()
-    g16 = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g16):
-        step_bf16()
-    g16.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(5):
-        g16.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step_bf16 = e0.elapsed_time(e1) / 5
-    del g16, kr_b
-    # Indexer projections (reference calls, not part of the step, whose q_r
-    # and k_r are given): the prefill k_r build of one retrieval KV head
-    # over all N tokens (256 B of bf16 features read, 64 B of k_r written
-    # per token, on the matrix cores), and one decode token's q_r for the
-    # H_r retrieval heads plus its k_r row appended at row N - 1.
-    def bf16_bits(*shape):  # N(0,1) values as bf16 bit patterns
-        return torch.randn(shape, dtype=torch.bfloat16, device=dev).view(torch.int16)
-    xp = bf16_bits(1, 1, N, d)
-    Wp = bf16_bits(G_r, 16, d)
-    kr_out = torch.empty((1, 1, N, 16), dtype=torch.float32, device=dev)
-    us["rtp_index_project_prefill"] = time_call(lambda: [rtp.rtp_index_project(
-        xp, Wp[:1], kr_out) for l in range(L)])
-    qp = bf16_bits(B, Hq, 1, d)
-    Wq = bf16_bits(H_r, 16, d)
-    qr_out = torch.empty((B, H_r, 1, 16), dtype=torch.float32, device=dev)
-    kp = bf16_bits(B, Hkv, 1, d)
-    kr_cache = torch.empty((B, G_r, N, 16), dtype=torch.float32, device=dev)
-    us["rtp_index_project_decode"] = time_call(lambda: [
-        (rtp.rtp_index_project(qp, Wq, qr_out),
-         rtp.rtp_index_project(kp, Wp, kr_cache, out_pos=N - 1)) for l in range(L)])
-    proj_gbps = N * (d * 2 + 16 * 4) / (us["rtp_index_project_prefill"] * 1e-6) / 1e9
-    # Prefill attention of a 16384-token prompt on layer 0's cache, a
-    # reference call: the retrieval heads dense, the local heads sinks +
-    # window, one launch each.  Flops: 4 * d per (query, key) pair.
-    T_pf = 16384
-    q_pf = bf16_bits(B, Hq, T_pf, d)
-    out_pf = torch.empty((B, Hq, T_pf, d), dtype=torch.float32, device=dev)
-    us["rtp_prefill_attend_16k"] = time_call(lambda: [(
-        rtp.rtp_prefill_attend(q_pf, K_all[0], V_all[0], 0, H_r, 0, 0, scale, out_pf),
-        rtp.rtp_prefill_attend(q_pf, K_all[0], V_all[0], H_r, Hq - H_r, cfg.n_sink, cfg.window,
-                               scale, out_pf)) for _ in range(4)]) * L / 4
-    t_idx = np.arange(T_pf, dtype=np.float64)
-    w0 = np.maximum(0, t_idx + 1 - cfg.window)
-    local_pairs = float(np.sum(np.minimum(cfg.n_sink, w0) + (t_idx + 1 - w0)))
-    pf_flops = B * 4 * d * (H_r * T_pf * (T_pf + 1) / 2 + (Hq - H_r) * local_pairs)
-    pf_tflops = pf_flops / (us["rtp_prefill_attend_16k"] * 1e-6) / 1e12
-    del q_pf, out_pf
-    del xp, kr_out, kr_cache
-    # rtp_topp_select runs both passes in one launch (sel_fused_kernel) when
-    # its histogram and emit block rows fit one grid (2 * B * H_r <= 65535);
-    # rtp_topp_hist, the histogram pass alone, is then timed for reference
-    # only.  Otherwise it launches the hist kernel then the emit kernel, and
-    # the emit kernel's duration is the difference.
-    fused_select = 2 * B * H_r <= 65535
-    if not fused_select:
-        us["sel_emit_kernel"] = us["rtp_topp_select"] - us["rtp_topp_hist"]
-    if sl.mode == "scan_local":
-        us["rtp_scan_local"] = time_call(lambda: [rtp.rtp_scan_local(
-            qr_all[l], kr_all[l], scores_l[l], q_all[l], K_all[l], V_all[l], N, H_r, Hq - H_r,
-            cfg.n_sink, cfg.window, scale, out_all[l], sl.ws_local) for l in range(L)])
-        us["rtp_decode_attend"] = time_call(lambda: [rtp.rtp_decode_attend(
-            q_all[l], K_all[l], V_all[l], idx_l[l], count_l[l], N, 0, H_r, 0, 0, 1, scale,
-            out_all[l], sl.ws_attend) for l in range(L)])
-    elif sl.mode == "fused":
-        us["rtp_decode_attend"] = time_call(lambda: [rtp.rtp_decode_attend(
-            q_all[l], K_all[l], V_all[l], idx_l[l], count_l[l], N, 0, H_r, Hq - H_r,
-            cfg.n_sink, cfg.window, scale, out_all[l], sl.ws_attend) for l in range(L)])
-    elif sl.mode == "union":
-        us["rtp_sparse_decode_union"] = time_call(lambda: [rtp.rtp_sparse_decode_union(
-            q_all[l], K_all[l], V_all[l], keep_l[l], N, 0, scale, out_all[l], sl.ws_sparse)
-            for l in range(L)])
-    else:
-        us["rtp_sparse_decode"] = time_call(lambda: [rtp.rtp_sparse_decode(
-            q_all[l], K_all[l], V_all[l], idx_l[l], count_l[l], 0, scale, out_all[l],
-            sl.ws_sparse) for l in range(L)])
-    if sl.mode not in ("fused", "scan_local"):
-        us["rtp_local_decode"] = time_call(lambda: [rtp.rtp_local_decode(
-            q_all[l], K_all[l], V_all[l], N, H_r, Hq - H_r, cfg.n_sink, cfg.window, scale,
-            out_all[l], sl.ws_local) for l in range(L)])
+    us = {"rtp_decode_layer": time_call(lambda: [layer_call(l) for l in range(L)])}
+    ref = {}
+    if not args.no_reference or args.sparse_mode != "layer":
+        ref = reference_calls(args, cfg, p, dev, stream, L, qr_all, kr_all, q_all, K_all, V_all,
+                              out_all, time_call, timed_step, us)
     log("per-call us/layer: " + ", ".join(f"{k}={v:.2f}" for k, v in us.items()))
 
     # --------------------------------------------- algorithmic bytes
     # Per layer: the k_r scan (N * 16 fp32 per retrieval KV head), the union
     # of the retrieval heads' kept rows (K + V, 512 B each), and the local
-    # heads' sink + window rows (512 B each, once per local KV head).
+    # heads' sink + window rows (512 B each, once per local KV head).  The
+    # kept sets are the layer call's own.
     w_start = max(0, N - cfg.window)
     w_rows = min(cfg.n_sink, w_start) + (N - w_start)
     local_kv = Hkv - G_r
-    n_sel = []
-    union = []
-    counts = count_l.cpu().numpy()
-    for l in range(L):
-        cnt = counts[l]
-        u = 0
-        for b in range(B):
-            for g in range(G_r):
-                mark = torch.zeros(N, dtype=torch.bool, device=dev)
-                for h in range(g * cfg.G, min(H_r, (g + 1) * cfg.G)):
-                    mark[idx_l[l, b, h, :int(cnt[b, h])].long()] = True
-                u += int(mark.sum().item())
-        union.append(u)
-        n_sel.append(cnt.reshape(-1).tolist())
-    del scores_l, idx_l, keep_l
+    n_sel, union = kept_stats(idx_l, count_l, cfg, dev)
+    del idx_l
     torch.cuda.synchronize()
     kr_bytes = B * G_r * N * cfg.r * 4
     gather_bytes = np.array(union) * 2 * d * 2
@@ -332,54 +226,17 @@ def main():
     steps_per_s = 1e3 / ms_step
     achieved_gbps = B_alg / (ms_step * 1e-3) / 1e9
 
-    # Roofline of the dominant kernel: the kernel with the largest time per
-    # layer.  Calls that launch one kernel are timed directly.  Algorithmic
-    # bytes per launch (one layer):
-    #   select  4 B per score read + 4 B per kept index written (one launch:
-    #           its histogram and emit blocks each read the scores; the
-    #           second read earns no credit);
-    #   emit    the same, for the emit kernel of the two-launch selection;
-    #   hist    4 B per score read;
-    #   scan    64 B of k_r read + 4 B of score written per query head, per
-    #           token and retrieval KV head;
-    #   sparse  512 B (K + V row) per row of the union of the group's kept
-    #           sets (re-reads by several heads earn no credit) + the 4-B
-    #           indices read;
-    #   local   512 B per sink/window row per local KV head;
-    #   attend  sparse (+ local in mode "fused"), one launch;
-    #   scan + local, one launch (mode "scan_local").
+    # Roofline of the dominant kernel of the step.  In mode "layer" that is
+    # the layer kernel itself (one launch per layer): its algorithmic bytes
+    # per launch are the layer's B_alg (k_r + union rows + window rows; score,
+    # histogram and workspace traffic earns no credit).
     csrc = os.path.join(ROOT, "sparse_long_context_indexer_amd", "csrc")
-    sel_total = float(np.mean([sum(x) for x in n_sel]))
-    sparse_bytes = float(np.mean(union)) * 2 * d * 2 + sel_total * 4
-    sel_bytes = B * H_r * N * 4 + sel_total * 4
-    cands = {
-        "sel_emit_kernel": ("sel_emit_kernel<false>", sel_bytes, "select.hip"),
-        "rtp_topp_hist": ("sel_hist_kernel<false>", B * H_r * N * 4, "select.hip"),
-        "rtp_index_scores": ("index_scores_kernel<8, false>", B * G_r * N * (cfg.r * 4 + cfg.G * 4),
-                             "scan.hip"),
-        "rtp_decode_attend": ("attend_kernel",
-                              sparse_bytes + (window_bytes if sl.mode == "fused" else 0),
-                              "attend.hip"),
-        "rtp_scan_local": ("scan_local_kernel<8>",
-                           B * G_r * N * (cfg.r * 4 + cfg.G * 4) + window_bytes, "attend.hip"),
-        "rtp_sparse_decode": ("attend_kernel", sparse_bytes, "attend.hip"),
-        "rtp_sparse_decode_union": ("union_attn_kernel",
-                                    float(np.mean(union)) * 2 * d * 2 + B * H_r * ((N + 31) // 32) * 4,
-                                    "attend.hip"),
-        "rtp_local_decode": ("attend_kernel", window_bytes, "attend.hip"),
-    }
-    if fused_select:
-        cands["rtp_topp_select"] = ("sel_fused_kernel<false>", sel_bytes, "select.hip")
-    # Calls timed for reference only, outside the step: rtp_index_scores in
-    # mode "scan_local" (the step runs the scan inside rtp_scan_local) and
-    # rtp_topp_hist when the selection is one launch.
-    in_step = [c for c in cands if c in us
-               and not (sl.mode == "scan_local" and c == "rtp_index_scores")
-               and not (fused_select and c == "rtp_topp_hist")]
-    call = max(in_step, key=lambda c: us[c])
-    kname, kbytes, ksrc = cands[call]
-    roof = {"kernel": kname, "bound": "hbm",
-            "achieved": kbytes / (us[call] * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    if args.sparse_mode == "layer":
+        kname, kbytes, ksrc, kus = "layer_kernel<8>", B_alg / L, "layer.hip", us["rtp_decode_layer"]
+    else:
+        kname, kbytes, ksrc, kus = ref["roof"]
+    roof = {"kernel": kname, "bound": "hbm", "achieved": kbytes / (kus * 1e-6) / 1e9,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(os.path.join(ROOT, "profiles", "hbm_traffic_ctx1m.md"),
                                        kname, os.path.join(csrc, ksrc))
@@ -409,13 +266,17 @@ def main():
         "selected_per_head_mean": float(np.mean(n_sel)),
         "union_rows_per_layer_mean": float(np.mean(union)),
         "per_call_us_per_layer": {k: round(v, 2) for k, v in us.items()},
-        "topk_budget": k_budget,
-        "ms_per_step_bf16_kr": round(ms_step_bf16, 4),
-        "project_prefill_GBps": round(proj_gbps, 1),
-        "prefill_16k_TFLOPs": round(pf_tflops, 1),
-        "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
-        "cpu_baseline": cpu,
     }
+    rec.update({k: v for k, v in ref.items() if k != "roof"})
+    rec["roofline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()}
+    rec["cpu_baseline"] = cpu
+
+    # ------------------------------------------- the smaller workloads
+    if not args.no_configs:
+        del K_all, V_all, kr_all, qr_all, q_all, out_all, ws_layer, step_layer
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        rec["configs"] = [r for ci in (1, 2, 3) for r in config_records(ci, dev, stream)]
     print(json.dumps(rec), flush=True)
 
     if args.calib_copy:
@@ -424,6 +285,222 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
+
+
+def kept_stats(idx, count, cfg, dev):
+    """Per layer: the kept-set sizes of every retrieval head and the size of
+    the union of each KV group's kept sets (summed over rows and groups)."""
+    import torch
+    L, B, H_r, N = idx.shape
+    counts = count.cpu().numpy()
+    n_sel, union = [], []
+    for l in range(L):
+        u = 0
+        for b in range(B):
+            for g in range(cfg.G_r):
+                mark = torch.zeros(N, dtype=torch.bool, device=dev)
+                for h in range(g * cfg.G, min(H_r, (g + 1) * cfg.G)):
+                    mark[idx[l, b, h, :int(counts[l, b, h])].long()] = True
+                u += int(mark.sum().item())
+        union.append(u)
+        n_sel.append(counts[l].reshape(-1).tolist())
+    return n_sel, union
+
+
+def reference_calls(args, cfg, p, dev, stream, L, qr_all, kr_all, q_all, K_all, V_all, out_all,
+                    time_call, timed_step, us):
+    """Calls timed beside the step for reference: the four-call layer
+    (scan, select, attend: its launches one by one and as a whole step), the
+    static top-k selector, the scan over bf16 keys, the indexer projections
+    and a 16K-token prefill.  Adds their microseconds per launch to `us`
+    and returns the extra record keys."""
+    import torch
+    import sparse_long_context_indexer_amd as rtp
+    from sparse_long_context_indexer_amd.runner import DecodeLayer
+    B, N, Hq, Hkv, H_r, d, G_r = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.H_r, cfg.d, cfg.G_r
+    scale = cfg.scale
+    four = DecodeLayer(B, Hq, Hkv, N, H_r, cfg.n_sink, cfg.window, dev, mode="fused")
+    scores_l = torch.empty((L, B, H_r, N), dtype=torch.float32, device=dev)
+    idx_l = torch.empty((L, B, H_r, N), dtype=torch.int32, device=dev)
+    count_l = torch.empty((L, B, H_r), dtype=torch.int32, device=dev)
+    for l in range(L):
+        rtp.rtp_index_scores(qr_all[l], kr_all[l], scores_l[l])
+        rtp.rtp_topp_select(scores_l[l], p, idx_l[l], count_l[l], four.ws_sel)
+    torch.cuda.synchronize()
+    us["rtp_index_scores"] = time_call(lambda: [rtp.rtp_index_scores(qr_all[l], kr_all[l],
+                                                                     scores_l[l])
+                                                for l in range(L)])
+    us["rtp_topp_select"] = time_call(lambda: [rtp.rtp_topp_select(
+        scores_l[l], p, idx_l[l], count_l[l], four.ws_sel) for l in range(L)])
+    us["rtp_topp_hist"] = time_call(lambda: [rtp.rtp_topp_hist(scores_l[l], four.ws_sel)
+                                             for l in range(L)])
+    us["rtp_decode_attend"] = time_call(lambda: [rtp.rtp_decode_attend(
+        q_all[l], K_all[l], V_all[l], idx_l[l], count_l[l], N, 0, H_r, Hq - H_r,
+        cfg.n_sink, cfg.window, scale, out_all[l], four.ws_attend) for l in range(L)])
+    ms_four, _ = timed_step(lambda l: four(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l],
+                                           p, scale, out_all[l]), 5, 1)
+    # Static top-k at the workload's mean top-p budget (sel_fused_kernel<true>).
+    k_budget = max(1, int(round(float(count_l.float().mean().item()))))
+    idx_k = torch.empty_like(idx_l[0])
+    count_k = torch.empty_like(count_l[0])
+    us["rtp_topk_select"] = time_call(lambda: [rtp.rtp_topk_select(
+        scores_l[l], k_budget, idx_k, count_k, four.ws_sel) for l in range(L)])
+    # The scan over a bf16 copy of the indexer key cache, and the four-call
+    # step with it.
+    kr_b = kr_all.to(torch.bfloat16).view(torch.int16)
+    us["rtp_index_scores_bf16"] = time_call(lambda: [rtp.rtp_index_scores_bf16(
+        qr_all[l], kr_b[l], scores_l[l]) for l in range(L)])
+    ms_bf16, _ = timed_step(lambda l: four(qr_all[l], kr_b[l], q_all[l], K_all[l], V_all[l], p,
+                                           scale, out_all[l]), 5, 1)
+    del kr_b, scores_l, idx_l, idx_k, count_k
+    # Indexer projections: the prefill k_r build of one retrieval KV head over
+    # all N tokens, and one decode token's q_r for the H_r heads plus its k_r
+    # row appended at row N - 1.
+    def bf16_bits(*shape):  # N(0,1) values as bf16 bit patterns
+        return torch.randn(shape, dtype=torch.bfloat16, device=dev).view(torch.int16)
+    xp = bf16_bits(1, 1, N, d)
+    Wp = bf16_bits(G_r, 16, d)
+    kr_out = torch.empty((1, 1, N, 16), dtype=torch.float32, device=dev)
+    us["rtp_index_project_prefill"] = time_call(lambda: [rtp.rtp_index_project(
+        xp, Wp[:1], kr_out) for l in range(L)])
+    qp = bf16_bits(B, Hq, 1, d)
+    Wq = bf16_bits(H_r, 16, d)
+    qr_out = torch.empty((B, H_r, 1, 16), dtype=torch.float32, device=dev)
+    kp = bf16_bits(B, Hkv, 1, d)
+    kr_cache = torch.empty((B, G_r, N, 16), dtype=torch.float32, device=dev)
+    us["rtp_index_project_decode"] = time_call(lambda: [
+        (rtp.rtp_index_project(qp, Wq, qr_out),
+         rtp.rtp_index_project(kp, Wp, kr_cache, out_pos=N - 1)) for l in range(L)])
+    proj_gbps = N * (d * 2 + 16 * 4) / (us["rtp_index_project_prefill"] * 1e-6) / 1e9
+    del xp, kr_out, kr_cache
+    # Prefill attention of a 16384-token prompt on layer 0's cache: the
+    # retrieval heads dense, the local heads sinks + window, one launch
+    # each.  Flops: 4 * d per (query, key) pair.
+    T_pf = 16384
+    q_pf = bf16_bits(B, Hq, T_pf, d)
+    out_pf = torch.empty((B, Hq, T_pf, d), dtype=torch.float32, device=dev)
+    us["rtp_prefill_attend_16k"] = time_call(lambda: [(
+        rtp.rtp_prefill_attend(q_pf, K_all[0], V_all[0], 0, H_r, 0, 0, scale, out_pf),
+        rtp.rtp_prefill_attend(q_pf, K_all[0], V_all[0], H_r, Hq - H_r, cfg.n_sink, cfg.window,
+                               scale, out_pf)) for _ in range(4)]) * L / 4
+    t_idx = np.arange(T_pf, dtype=np.float64)
+    w0 = np.maximum(0, t_idx + 1 - cfg.window)
+    local_pairs = float(np.sum(np.minimum(cfg.n_sink, w0) + (t_idx + 1 - w0)))
+    pf_flops = B * 4 * d * (H_r * T_pf * (T_pf + 1) / 2 + (Hq - H_r) * local_pairs)
+    pf_tflops = pf_flops / (us["rtp_prefill_attend_16k"] * 1e-6) / 1e12
+    del q_pf, out_pf
+    sel_bytes = B * H_r * N * 4 + float(count_l.float().sum().item()) / L * 4
+    out = {"ms_per_step_four_call": round(ms_four, 4),
+           "ms_per_step_four_call_bf16_kr": round(ms_bf16, 4),
+           "topk_budget": k_budget,
+           "project_prefill_GBps": round(proj_gbps, 1),
+           "prefill_16k_TFLOPs": round(pf_tflops, 1),
+           "roof": ("sel_fused_kernel<false>", sel_bytes, "select.hip", us["rtp_topp_select"])}
+    del four
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def config_records(ci, dev, stream, reps=10):
+    """Records of one smaller workload at each of its p: the one-launch layer
+    over R input replicas at distinct addresses (R * B_alg >= 1 GiB, so the
+    caches hold none of a step's inputs: cold), and on one replica (hot);
+    kept-set sizes and unions; boundary exemptions and output errors against
+    the oracle."""
+    import torch
+    import oracle
+    import synth
+    import sparse_long_context_indexer_amd as rtp
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from harness import judge_out, judge_set
+    cfg = synth.CONFIGS[ci]
+    B, N, Hq, Hkv, H_r, d, G_r = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.H_r, cfg.d, cfg.G_r
+    t0 = time.time()
+    q_r, k_r, q = synth.layer_qr(cfg, 0), synth.layer_kr(cfg, 0), synth.layer_q(cfg, 0)
+    K, V = synth.layer_kv(cfg, 0, "K"), synth.layer_kv(cfg, 0, "V")
+    d_in = [torch.from_numpy(x).to(dev) for x in
+            (q_r, k_r, q.view(np.int16), K.view(np.int16), V.view(np.int16))]
+    w_start = max(0, N - cfg.window)
+    w_rows = min(cfg.n_sink, w_start) + (N - w_start)
+    local_kv = Hkv - G_r
+    ws = torch.empty(rtp.decode_layer_workspace_size(B, Hq, Hkv, N, H_r, cfg.n_sink, cfg.window),
+                     dtype=torch.uint8, device=dev)
+    recs = []
+    for p in cfg.p_list:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, H_r, N), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, H_r), dtype=torch.int32, device=dev)
+
+        def call(x, o=out, i=idx, c=cnt):
+            rtp.rtp_decode_layer(x[0], x[1], x[2], x[3], x[4], N, H_r, cfg.n_sink, cfg.window,
+                                 p, cfg.scale, o, i, c, ws)
+        call(d_in)
+        torch.cuda.synchronize()
+        n_sel, union = kept_stats(idx[None], cnt[None], cfg, dev)
+        B_alg = float(B * G_r * N * cfg.r * 4 + union[0] * 2 * d * 2
+                      + B * local_kv * w_rows * 2 * d * 2)
+        R = max(1, math.ceil((1 << 30) / B_alg))
+        reps_in = [d_in] + [[x.clone() for x in d_in] for _ in range(R - 1)]
+
+        def timed(inputs):
+            g = torch.cuda.CUDAGraph()
+            for x in inputs:
+                call(x)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for x in inputs:
+                    call(x)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / (reps * len(inputs))
+        ms_cold = timed(reps_in)
+        ms_hot = timed([d_in] * 8)
+        del reps_in
+        # Against the oracle: exempt boundary tokens and output errors.
+        c = cnt.cpu().numpy()
+        ix = idx.cpu().numpy()
+        o = out.cpu().numpy()
+        exempt, bad, err, rel = 0, 0, 0.0, 0.0
+        for b in range(B):
+            for h in range(Hq):
+                g = h // cfg.G
+                if h < H_r:
+                    s = oracle.scores(q_r[b, h], k_r[b, g])
+                    v = judge_set(s, p, ix[b, h, :c[b, h]])
+                    exempt += len(v.exempt)
+                    bad += len(v.bad) + (0 if v.ok else 1)
+                    rows = np.sort(ix[b, h, :c[b, h]])
+                else:
+                    rows = oracle.local_rows(N, cfg.n_sink, cfg.window)
+                ok, e_abs, e_rel = judge_out(o[b, h], oracle.attention(q[b, h], K[b, g, rows],
+                                                                       V[b, g, rows], cfg.scale))
+                bad += 0 if ok else 1
+                err, rel = max(err, e_abs), max(rel, e_rel)
+        ns = np.array(n_sel[0]).reshape(B, H_r)
+        rec = {"workload": cfg.name, "p": p, "batch": B, "ctx_tokens": N,
+               "steps_per_s": round(1e3 / ms_cold, 1), "ms_per_step": round(ms_cold, 5),
+               "ms_per_step_hot": round(ms_hot, 5), "replicas": R,
+               "tokens_scanned_per_s": B * G_r * N / (ms_cold * 1e-3),
+               "B_alg_bytes": B_alg, "GBps": round(B_alg / (ms_cold * 1e-3) / 1e9, 1),
+               "frac_of_hbm_peak": round(B_alg / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+               "n_S_per_row_head": ns.tolist(), "union_rows": union[0],
+               "exempt_tokens": exempt, "parity_failures": bad,
+               "max_abs_err": err, "max_rel_err": rel}
+        log(f"config {ci} p={p}: {ms_cold * 1e3:.1f} us/step cold ({R} replicas), "
+            f"{ms_hot * 1e3:.1f} hot, {rec['GBps']} GB/s, union {union[0]}, exempt {exempt}, "
+            f"failures {bad}")
+        recs.append(rec)
+    log(f"config {ci} done ({time.time() - t0:.1f}s)")
+    del d_in, ws
+    torch.cuda.empty_cache()
+    return recs
 
 
 def measured_traffic(summary, kernel, source):
