@@ -49,7 +49,8 @@ typedef enum rtp_status {
     RTP_ERR_VALUE = 4,       /* p not in (0,1], bad window/sink, bad scale  */
     RTP_ERR_ALIGN = 5,       /* a pointer or capacity breaks alignment      */
     RTP_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required     */
-    RTP_ERR_HIP = 7          /* the HIP runtime reported an error           */
+    RTP_ERR_HIP = 7,         /* the HIP runtime reported an error           */
+    RTP_ERR_LIMIT = 8        /* beyond the no-allocation entry point's scratch */
 } rtp_status;
 
 /* Workspace kinds for rtp_workspace_size. */
@@ -245,6 +246,31 @@ rtp_status rtp_sparse_decode(const rtp_bf16 *q, const rtp_bf16 *K,
                              int32_t q_head_begin, int32_t n_q_heads,
                              float scale, float *out, void *workspace,
                              size_t ws_bytes, void *stream);
+
+/*
+ * rtp_sparse_decode_noalloc -- rtp_sparse_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results, with the
+ * workspace taken from a static device array of the library (4 MiB per
+ * device, held until the process ends) instead of a caller's buffer.  The
+ * call allocates nothing.  Every call on one device shares that array:
+ * calls that overlap on a device (different streams, threads) race and give
+ * undefined results; calls in sequence are fine.
+ *
+ *   every argument as in rtp_sparse_decode, minus workspace and ws_bytes
+ *   limit: rtp_workspace_size(RTP_WS_SPARSE_DECODE, B, n_q_heads, N) must
+ *   fit in the 4 MiB (B * n_q_heads <= 256 always does)
+ *
+ * Errors: those of rtp_sparse_decode, and RTP_ERR_LIMIT when the sizes need
+ * more than the static scratch.
+ */
+rtp_status rtp_sparse_decode_noalloc(const rtp_bf16 *q, const rtp_bf16 *K,
+                                     const rtp_bf16 *V, const int32_t *idx,
+                                     const int32_t *count, int32_t B, int32_t Hq,
+                                     int32_t Hkv, int32_t N, int64_t kv_cap,
+                                     int32_t d, int32_t q_head_begin,
+                                     int32_t n_q_heads, float scale, float *out,
+                                     void *stream);
 
 /*
  * rtp_sparse_decode_union -- the same attention as rtp_sparse_decode, with

@@ -25,11 +25,13 @@ RTP_WS_SPARSE_UNION = 4
 RTP_WS_DECODE_ATTEND = 5
 
 STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_SHAPE", 3: "RTP_ERR_UNSUPPORTED",
-          4: "RTP_ERR_VALUE", 5: "RTP_ERR_ALIGN", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
+          4: "RTP_ERR_VALUE", 5: "RTP_ERR_ALIGN", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP",
+          8: "RTP_ERR_LIMIT"}
 
 # Every symbol include/rtp.h declares.
 SYMBOLS = ("rtp_index_scores", "rtp_index_scores_bf16", "rtp_index_project", "rtp_topp_select",
-           "rtp_topk_select", "rtp_topp_hist", "rtp_sparse_decode", "rtp_sparse_decode_union",
+           "rtp_topk_select", "rtp_topp_hist", "rtp_sparse_decode", "rtp_sparse_decode_noalloc",
+           "rtp_sparse_decode_union",
            "rtp_local_decode", "rtp_local_decode_ring", "rtp_keep_bits_add_local",
            "rtp_prefill_attend", "rtp_decode_attend", "rtp_scan_local", "rtp_decode_layer",
            "rtp_decode_layer_workspace_size", "rtp_set_wait_limit", "rtp_device_status",
@@ -73,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.rtp_topp_hist.argtypes = [P, I32, I32, I32, P, SZ, P]
         L.rtp_sparse_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32,
                                         I32, I32, F32, P, P, SZ, P]
+        L.rtp_sparse_decode_noalloc.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32,
+                                                I32, I32, F32, P, P]
         L.rtp_sparse_decode_union.argtypes = [P, P, P, P, I32, I32, I32, I32, I64, I32, I32,
                                               I32, F32, P, P, SZ, P]
         L.rtp_local_decode.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, I32, I32,
@@ -336,6 +340,21 @@ def rtp_sparse_decode(q, K, V, idx, count, q_head_begin, scale, out, workspace,
         qp, Kp, Vp, _dev(idx, torch.int32, "idx", (B, n_q, N)),
         _dev(count, torch.int32, "count", (B, n_q)), B, Hq, Hkv, N, cap, d, q_head_begin, n_q,
         float(scale), op, wp, wn, _stream(q, stream))
+
+
+def rtp_sparse_decode_noalloc(q, K, V, idx, count, q_head_begin, scale, out, N=None,
+                              stream=None) -> None:
+    """rtp_sparse_decode with the library's static scratch in place of a
+    workspace (no device allocation); arguments as rtp_sparse_decode's."""
+    import torch
+    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
+    if count.dim() != 2 or idx.dim() != 3:
+        raise ValueError("count must be [B][n_q] and idx [B][n_q][N]")
+    n_q = count.shape[1]
+    N = idx.shape[-1] if N is None else N
+    _call("rtp_sparse_decode_noalloc", qp, Kp, Vp, _dev(idx, torch.int32, "idx", (B, n_q, N)),
+          _dev(count, torch.int32, "count", (B, n_q)), B, Hq, Hkv, N, cap, d, q_head_begin,
+          n_q, float(scale), op, _stream(q, stream))
 
 
 def rtp_sparse_decode_union(q, K, V, keep_bits, N, q_head_begin, scale, out, workspace,

@@ -96,6 +96,7 @@ const char *rtp_status_string(rtp_status s)
     case RTP_ERR_ALIGN: return "a pointer breaks the required alignment";
     case RTP_ERR_WORKSPACE: return "workspace missing or too small";
     case RTP_ERR_HIP: return "the HIP runtime reported an error";
+    case RTP_ERR_LIMIT: return "the sizes exceed the no-allocation entry point's scratch";
     }
     return "unknown status";
 }
@@ -253,6 +254,25 @@ rtp_status rtp_sparse_decode(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf1
     return from_hip(rtp::launch_sparse_decode(q, K, V, idx, count, B, Hq, Hkv, N, kv_cap,
                                               q_head_begin, n_q_heads, scale, out, workspace,
                                               as_stream(stream)));
+}
+
+rtp_status rtp_sparse_decode_noalloc(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,
+                                     const int32_t *idx, const int32_t *count, int32_t B,
+                                     int32_t Hq, int32_t Hkv, int32_t N, int64_t kv_cap,
+                                     int32_t d, int32_t q_head_begin, int32_t n_q_heads,
+                                     float scale, float *out, void *stream)
+{
+    if (!idx || !count) return RTP_ERR_NULL;
+    // check_attention_common wants a workspace pointer: the scratch stands in.
+    static const char kScratch alignas(256) = 0;
+    rtp_status st = check_attention_common(q, K, V, out, &kScratch, B, Hq, Hkv, N, kv_cap, d,
+                                           q_head_begin, n_q_heads, scale);
+    if (st != RTP_OK) return st;
+    if (!aligned(idx, 4) || !aligned(count, 4)) return RTP_ERR_ALIGN;
+    if (rtp::sparse_ws_bytes(B, n_q_heads, N) > rtp::noalloc_scratch_bytes()) return RTP_ERR_LIMIT;
+    return from_hip(rtp::launch_sparse_decode_noalloc(q, K, V, idx, count, B, Hq, Hkv, N, kv_cap,
+                                                      q_head_begin, n_q_heads, scale, out,
+                                                      as_stream(stream)));
 }
 
 rtp_status rtp_sparse_decode_union(const rtp_bf16 *q, const rtp_bf16 *K, const rtp_bf16 *V,

@@ -1192,6 +1192,46 @@ static hipError_t launch_attend(const uint16_t *q, const uint16_t *K, const uint
                   Hq, Hkv, scale * kLog2e, L, Pw, out);
 }
 
+// Scratch of rtp_sparse_decode_noalloc, for callers that cannot allocate:
+// the per-call workspace of the sparse attention (split partials, slice
+// merges, hand-off flags) in a file-scope device array, one per device, held
+// until the process ends.  Flags and counters in it need no clearing (each
+// call leaves them as it found them).  Calls that overlap on one device
+// share it and race.
+constexpr size_t kNoAllocScratch = size_t(4) << 20;
+static __device__ __align__(256) unsigned char rtp_noalloc_scratch[kNoAllocScratch];
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratch; }
+
+// The current device's copy of the scratch array (looked up once per device:
+// in host code the array's name is not a device address).
+static hipError_t noalloc_scratch(void **p)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void *> cache[kMaxDevices];
+    int dev = 0;
+    RTP_TRY(hipGetDevice(&dev));
+    void *a = dev >= 0 && dev < kMaxDevices ? cache[dev].load(std::memory_order_acquire) : nullptr;
+    if (!a) {
+        RTP_TRY(hipGetSymbolAddress(&a, HIP_SYMBOL(rtp_noalloc_scratch)));
+        if (dev >= 0 && dev < kMaxDevices) cache[dev].store(a, std::memory_order_release);
+    }
+    *p = a;
+    return hipSuccess;
+}
+
+hipError_t launch_sparse_decode_noalloc(const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                                        const int32_t *idx, const int32_t *count, int B, int Hq,
+                                        int Hkv, int N, int64_t kv_cap, int q_head_begin,
+                                        int n_q_heads, float scale, float *out,
+                                        hipStream_t stream)
+{
+    void *ws = nullptr;
+    RTP_TRY(noalloc_scratch(&ws));
+    return launch_sparse_decode(q, K, V, idx, count, B, Hq, Hkv, N, kv_cap, q_head_begin,
+                                n_q_heads, scale, out, ws, stream);
+}
+
 hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K, const uint16_t *V,
                                 const int32_t *idx, const int32_t *count, int B, int Hq,
                                 int Hkv, int N, int64_t kv_cap, int q_head_begin,

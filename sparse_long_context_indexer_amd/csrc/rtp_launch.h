@@ -64,6 +64,14 @@ hipError_t launch_sparse_decode(const uint16_t *q, const uint16_t *K,
                                 int n_q_heads, float scale, float *out,
                                 void *ws, hipStream_t stream);
 
+// rtp_sparse_decode with its workspace in a static device array.
+size_t noalloc_scratch_bytes();
+hipError_t launch_sparse_decode_noalloc(const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                                        const int32_t *idx, const int32_t *count, int B, int Hq,
+                                        int Hkv, int N, int64_t kv_cap, int q_head_begin,
+                                        int n_q_heads, float scale, float *out,
+                                        hipStream_t stream);
+
 size_t union_ws_bytes(int64_t B, int64_t n_q, int N);
 hipError_t launch_sparse_decode_union(const uint16_t *q, const uint16_t *K,
                                       const uint16_t *V, const uint32_t *keep_bits,

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         assert rtp.status_string(code)
     assert rtp.status_string(99) == "unknown status"
     assert lib.rtp_last_hip_error() == 0
@@ -459,3 +459,23 @@ def test_binding_checks_every_shape():
         with pytest.raises(ValueError) as e:
             call()
         assert "device tensor" not in str(e.value), (i, str(e.value))
+
+
+def test_sparse_decode_noalloc_validation(lib):
+    f = lib.rtp_sparse_decode_noalloc
+    args = [A, A, A, A, A, 1, 32, 4, 1000, 1000, 128, 0, 8, 0.088, A, None]
+
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return f(*a)
+
+    assert call(3, None) == 1 and call(4, None) == 1 and call(0, None) == 1
+    assert call(10, 64) == 3
+    assert call(8, 0) == 2 and call(12, 0) == 2
+    assert call(13, float("nan")) == 4
+    assert call(3, A + 2) == 5
+    # 4 MiB of scratch holds 256 score rows of partials, not 65535.
+    assert call(5, 65535) == 2 or call(5, 65535) == 8
+    assert call(5, 300) == 8                     # 300 * 8 rows > the scratch
+    assert rtp.status_string(8).startswith("the sizes exceed")
