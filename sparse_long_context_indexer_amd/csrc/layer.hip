@@ -20,26 +20,29 @@
 //   level 1  per head, a block histogram of fp64 mass exp(s - m_b) (m_b the
 //            block's max) over bins of width 1/4 on the logit axis,
 //            floor(4 s), counted down from the block's top bin; the last
-//            bin collects everything further down.  The records are merged
-//            by "last arriver" blocks, 16 at a time, then once more per row
-//            (bins realigned to the merged top, masses rescaled), and the
-//            row's last merger picks each head's boundary bin J* and the
-//            mass A above it.  No atomics touch the histograms in memory.
-//   local    while the threshold is being found, the first blocks run the
-//            local heads: 128-row tiles of the sink + window rows, every
-//            K/V row read once for the G query heads of its KV head.
-//   classify every block waits for its row's threshold (the only wait on
-//            blocks that may come later: it relies on the launch's blocks
-//            being resident together, which the host ensures by launching
-//            at most one block per compute unit), then marks its tokens
-//            above bin J* as kept (the row's idx list and an LDS list) and
-//            writes the tokens of bin J* as candidates (exact score key,
-//            index) for the boundary resolve.
-//   gather   every block attends its own kept rows (per head, split-K
-//            online softmax) and publishes one partial per head; partials
-//            are merged by last arrivers in two levels.
+//            bin collects everything further down.  One block per head (of
+//            the row's last blocks) waits for every record of its row,
+//            realigns them to the row's top bin, rescales them to the row
+//            max, and picks the head's boundary bin J* and the mass A above
+//            it.
+//   local    meanwhile the other blocks run the local heads: 256-row tiles
+//            of the sink + window rows, every K/V row read once for the G
+//            query heads of its KV head.
+//   classify every block waits for its row's thresholds (a wait on blocks
+//            that may come later: it relies on the launch's blocks being
+//            resident together, which the host ensures by launching at most
+//            one block per compute unit), then lists its tokens above bin J*
+//            as kept (the row's idx list and an LDS list), and rescores the
+//            tokens of bin J*: exact score key and index go to the row's
+//            candidate list.  Once every block has classified, each head's
+//            reducer builds the head's level-2 histogram from that list in
+//            LDS (1024 digits of width 1/4096 inside bin J*) and picks the
+//            boundary digit.
+//   gather   every block attends its own level-1 rows while the boundary
+//            digit is picked, then its candidates above that digit; one
+//            partial per head is merged by last arrivers in two levels.
 //   resolve  blocks that finish their gather claim the heads' boundary
-//            bins: a mass-weighted radix select over the candidates' score
+//            digits: a mass-weighted radix select over the candidates' score
 //            keys, ties to the lower index, then the kept boundary rows'
 //            attention, whose partial joins the final merge of the head.
 //
@@ -65,11 +68,13 @@ constexpr int kMH = 8;                  // query heads per KV head, at most
 constexpr int kNB = 128;                // level-1 bins per head (the last: everything lower)
 constexpr float kBPU = 4.0f;            // bins per unit of logit
 constexpr int kGS = 16;                 // records merged per last-arriver step
-constexpr int kTile = 128;              // local rows per item
+constexpr int kTile = 64;               // local rows per item
 constexpr int kPF = 132;                // floats per attention partial: m, l, pad, pad, o[128]
 constexpr int kRU = 8;                  // rows in flight per 16-lane group (sparse rows)
 constexpr int kBatch = 4 * kRU;         // rows per wave batch
 constexpr int kLU = 4;                  // rows in flight per wave (local rows)
+constexpr int kLocIters = kTile / (kNW * kLU);  // local row batches per wave
+constexpr int kFine = 1024;             // level-2 digits of the boundary bin
 constexpr int kResCap = 1536;           // resolve candidates per LDS buffer
 constexpr int kBkCap = 4096;            // kept boundary tokens listed in LDS
 constexpr int kListCap = kMH * kChunk;  // kept-token offsets per block (all heads)
@@ -77,7 +82,8 @@ constexpr float kLog2eF = 1.4426950408889634f;
 
 static_assert(kNB * kMH == kT, "one thread per (head, bin)");
 static_assert(128 * kMH == kT, "one thread per (head, output dimension)");
-static_assert(kTile == kNW * 2 * kLU, "each wave takes 2 * kLU local rows of a tile");
+static_assert(kTile == kNW * kLocIters * kLU, "each wave takes kLocIters * kLU local rows");
+static_assert(kFine == kT, "one thread per level-2 digit");
 
 static __constant__ double kLayerExpTbl[kExpTable] = RTP_EXP2_TABLE;
 
@@ -98,18 +104,29 @@ struct PickRec {            // a head's threshold
     double Pt;              // p * Z
 };
 
-struct RgCtl {  // tagged counters of one (batch row, retrieval KV head)
-    unsigned long long hist_row, pick_ready, classified, claim, res_done, pad[3];
-    unsigned long long kept[kMH], cand[kMH], att_row[kMH];
+struct Pick2Rec {           // a head's level-2 threshold inside the boundary bin
+    int32_t j2;             // boundary digit (mode 0)
+    int32_t mode;           // 0: digits above j2 kept, j2 resolved; 1: every candidate kept;
+                            // 2: every candidate resolved
+    uint32_t ka;            // tokens kept above the boundary bin
+    uint32_t k2;            // candidates kept above the boundary digit
+    uint32_t cstar;         // candidates in the boundary digit (mode 0) or all (mode 2)
+    uint32_t nc;            // candidates
+    double A2;              // mass above the boundary digit, relative to M
 };
-static_assert(sizeof(RgCtl) == 256, "RgCtl is 256 B");
+
+struct RgCtl {  // tagged counters of one (batch row, retrieval KV head)
+    unsigned long long hist_row, pick_ready, classified, pick2_ready, claim, p2_done, fin_done,
+        pad;
+    unsigned long long kept[kMH], cand[kMH], kept2[kMH], att_row[kMH];
+};
+static_assert(sizeof(RgCtl) == 320, "RgCtl is 320 B");
 
 struct LayerWs {
     HistRec *h1;                   // [NB] one per block
-    HistRec *h2;                   // [RG][ngrp] one per group of blocks
     PickRec *pick;                 // [RG][kMH]
+    Pick2Rec *pick2;               // [RG][kMH]
     RgCtl *ctl;                    // [RG]
-    unsigned long long *hist_grp;  // [RG][ngrp]
     unsigned long long *att_grp;   // [RG][ngrp]
     unsigned long long *loc_ctr;   // [B][n_lkv]
     float *att1;                   // [NB][kMH][kPF]
@@ -146,14 +163,24 @@ struct Cand {
 };
 
 struct HistLds {
-    double hist[kMH][kNB];
-    double acc[kMH][kNB];
-    double rf[kGS][kMH];
+    double hist[kMH][kNB];   // the block's histogram
+    double acc[kNB];         // a head's merged histogram (row reducer)
+    double rf[256];          // per block record: exp(m_b - M)
     double ru[kNW];
-    float rm[kGS][kMH];
-    int32_t rT[kGS][kMH];
-    float om[kMH];
-    int32_t oT[kMH];
+    float rm[256];           // per block record: max and top bin
+    int32_t rT[256];
+    int32_t ro[256];         // T - T_b
+    float wm[kNW];
+    int32_t wt[kNW];
+    float M;
+    int32_t T;
+};
+
+struct FineLds {  // a head's level-2 histogram
+    double m[kFine];
+    uint32_t c[kFine];
+    double dscan[kNW];
+    uint32_t uscan[kNW], first[kNW];
 };
 
 struct SlotLds {  // per-wave attention partials
@@ -166,6 +193,7 @@ struct ResLds {
     uint32_t hc[2048];
     double tmp[kWave];
     uint32_t uscan[kNW];
+    double dscan[kNW];
 };
 
 struct ResBufs {
@@ -178,6 +206,7 @@ struct LayerLds {
         HistLds h;
         SlotLds s;
         ResLds r;
+        FineLds f;
     } a;
     union {
         uint32_t gsw[kMH * kTPT / 2][kT];  // scan to classify: this thread's score bins, 2 per word
@@ -185,7 +214,7 @@ struct LayerLds {
         ResBufs rb;
     } b;
     double etbl[kExpTable];
-    float qr[kMH][16];
+    alignas(16) float qr[kMH][16];
     PickRec pick[kMH];
     float mb[kMH];
     int32_t Tb[kMH];
@@ -193,10 +222,13 @@ struct LayerLds {
     uint32_t wcnt[kMH][kNW];
     uint32_t kc[kMH], cc[kMH];
     uint32_t kgb[kMH], cgb[kMH];
+    Pick2Rec pick2[kMH];
+    uint32_t n2[kMH], k2b[kMH];  // level-2 kept rows of the block per head, their slot base
+    uint32_t fka, fnc;           // a head's kept and candidate totals (its reducer)
     int bpre[kMH + 1];
     int hlast[kMH];
     int flag, ticket;
-    uint32_t nkeep, nmove, j, cbefore, ka, nc, kmin, kmax;
+    uint32_t nkeep, nmove, j, cbefore, kmin, kmax;
     double abefore;
 };
 
@@ -245,7 +277,7 @@ __device__ __forceinline__ void st_cand2(uint2 *p, uint2 e)
 
 // Thread 0 polls a tagged counter until it holds at least `level`; after
 // `limit` polls it gives up and sets the timeout bit of the status word.
-__device__ void wait_level(const unsigned long long *ctr, uint32_t level, uint32_t limit,
+__device__ __forceinline__ void wait_level(const unsigned long long *ctr, uint32_t level, uint32_t limit,
                            uint32_t *status)
 {
     for (uint32_t it = 0;; ++it) {
@@ -262,7 +294,7 @@ __device__ void wait_level(const unsigned long long *ctr, uint32_t level, uint32
 // After this block's agent-scope stores: counts the block on ctr and tells
 // every thread whether it was the last of `expected` (the last one resets
 // the counter for the next call).
-__device__ bool arrive_last_blk(unsigned long long *ctr, uint32_t expected, LayerLds &S)
+__device__ __forceinline__ bool arrive_last_blk(unsigned long long *ctr, uint32_t expected, LayerLds &S)
 {
     wait_vmem();
     __syncthreads();
@@ -344,9 +376,9 @@ __device__ __forceinline__ void att_rows(const uint16_t *__restrict__ Kb,
     a.m = mn;
 }
 
-// Merges the four 16-lane groups of the wave and writes the result to the
-// wave's slot for head h.  Every lane of the wave must call it.
-__device__ void att_flush(AttState &a, int w, int h, LayerLds &S)
+// Merges the four 16-lane groups of the wave, then into the wave's slot for
+// head h (an empty slot has m = -inf).  Every lane of the wave must call it.
+__device__ __forceinline__ void att_flush(AttState &a, int w, int h, LayerLds &S)
 {
     const int lane = lane_id(), sub = lane & 15;
 #pragma unroll
@@ -364,11 +396,19 @@ __device__ void att_flush(AttState &a, int w, int h, LayerLds &S)
         a.m = mn;
     }
     if (lane < 16) {
+        const float ms = S.a.s.m[w][h];
+        const float mn = fmaxf(a.m, ms);
+        if (mn == -INFINITY) return;
+        const float fa = rescale2(a.m, mn), fb = rescale2(ms, mn);
+        const bool had = ms != -INFINITY;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) S.a.s.o[w][h][sub * 8 + c] = a.o[c];
+        for (int c = 0; c < 8; ++c) {
+            const float prev = had ? S.a.s.o[w][h][sub * 8 + c] * fb : 0.0f;
+            S.a.s.o[w][h][sub * 8 + c] = fmaf(a.o[c], fa, prev);
+        }
         if (lane == 0) {
-            S.a.s.m[w][h] = a.m;
-            S.a.s.l[w][h] = a.l;
+            S.a.s.l[w][h] = fmaf(a.l, fa, had ? S.a.s.l[w][h] * fb : 0.0f);
+            S.a.s.m[w][h] = mn;
         }
     }
 }
@@ -384,7 +424,7 @@ __device__ __forceinline__ void slots_clear(LayerLds &S)
 // Merges the waves' slots of heads hh < nh into one partial per head at
 // dst + hh * hstride (agent-scope stores).  Thread t takes head t / 128 and
 // output dimension t % 128.
-__device__ void slots_to_partial(int nh, float *dst, int64_t hstride, LayerLds &S)
+__device__ __forceinline__ void slots_to_partial(int nh, float *dst, int64_t hstride, LayerLds &S)
 {
     const int hh = threadIdx.x >> 7, d = threadIdx.x & 127;
     if (hh >= nh) return;
@@ -415,7 +455,7 @@ __device__ void slots_to_partial(int nh, float *dst, int64_t hstride, LayerLds &
 // record (k, hh) at base + k * kstride + hh * kPF (published by other blocks:
 // agent-scope loads).  Writes a merged record at dst + hh * kPF (agent-scope
 // stores) or, with dst NULL, the normalised output row at outp + hh * 128.
-__device__ void merge_records(const float *base, int64_t kstride, int n, int nh, uint32_t hmask,
+__device__ __forceinline__ void merge_records(const float *base, int64_t kstride, int n, int nh, uint32_t hmask,
                               float *dst, float *outp)
 {
     const int hh = threadIdx.x >> 7, d = threadIdx.x & 127;
@@ -461,169 +501,157 @@ __device__ void merge_records(const float *base, int64_t kstride, int n, int nh,
 
 // ------------------------------------------------------------------ scan
 
-// Scores of this thread's tokens c0 + t*kT + tid (t < kTPT) for the G
-// query heads of KV head g of row b: one sequential fma chain per score over
-// dimensions 0..15 from +0, a zero result stored as +0 (bit-identical to
-// rtp_index_scores).  Tokens at or past the chunk's end score -inf.
-template <int G>
-__device__ __forceinline__ void scan_scores(const LayerParams &P, int b, int g, int64_t c0,
-                                            int cn, float (&sc)[kTPT][G])
+// This thread's key rows c0 + t*kT + tid (t < kTPT) of KV head g of row b,
+// all loads issued at once (zeros at or past the chunk's end).
+__device__ __forceinline__ void scan_load(const LayerParams &P, int b, int g, int64_t c0, int cn,
+                                          float4 (&kv)[kTPT][4])
 {
-    constexpr int TPT = kTPT;
     const int tid = threadIdx.x;
     const float4 *kr =
         reinterpret_cast<const float4 *>(P.k_r + ((int64_t)b * P.Hkv_r + g) * P.kr_cap * 16);
-    const float *qb = P.q_r + ((int64_t)b * P.Hq_r + (int64_t)g * G) * 16;
 #pragma unroll
-    for (int t0 = 0; t0 < TPT; t0 += 4) {
-        // (compiler barriers: one batch of rows and one head's q_r live at a
-        // time, instead of every load hoisted to the top)
-        asm volatile("" ::: "memory");
-        float4 kv[4][4];
+    for (int t = 0; t < kTPT; ++t) {
+        const int o = t * kT + tid;
+        if (o < cn) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int o = (t0 + u) * kT + tid;
-            if (o < cn) {
-                const int64_t i = c0 + o;
+            for (int j = 0; j < 4; ++j) kv[t][j] = kr[(c0 + o) * 4 + j];
+        } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) kv[u][j] = kr[i * 4 + j];
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kv[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            asm volatile("" ::: "memory");
-            float q[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) q[j] = qb[h * 16 + j];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float k[16] = {kv[u][0].x, kv[u][0].y, kv[u][0].z, kv[u][0].w,
-                                     kv[u][1].x, kv[u][1].y, kv[u][1].z, kv[u][1].w,
-                                     kv[u][2].x, kv[u][2].y, kv[u][2].z, kv[u][2].w,
-                                     kv[u][3].x, kv[u][3].y, kv[u][3].z, kv[u][3].w};
-                float acc = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) acc = __builtin_fmaf(q[j], k[j], acc);
-                acc = (acc == 0.0f) ? 0.0f : acc;
-                sc[t0 + u][h] = ((t0 + u) * kT + tid < cn) ? acc : -INFINITY;
-            }
+            for (int j = 0; j < 4; ++j) kv[t][j] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
 }
 
-// The score of token i for query head h (row b, KV head g), recomputed with
-// the same chain as scan_scores (q_r of the G heads in S.qr).
-__device__ __forceinline__ float rescore(const LayerParams &P, int b, int g, int64_t i, int h,
-                                         const LayerLds &S)
+// Scores of the loaded rows for the G query heads (q_r from LDS): one
+// sequential fma chain per score over dimensions 0..15 from +0, a zero
+// result stored as +0 (bit-identical to rtp_index_scores).  The kTPT chains
+// of a head advance together, dimension by dimension, so consecutive fmas
+// are independent.  Tokens at or past the chunk's end score -inf.
+template <int G>
+__device__ __forceinline__ void scan_scores(const float4 (&kv)[kTPT][4], int cn, const LayerLds &S,
+                                            float (&sc)[kTPT][G])
 {
-    const float4 *kr = reinterpret_cast<const float4 *>(
-        P.k_r + (((int64_t)b * P.Hkv_r + g) * P.kr_cap + i) * 16);
-    float k[16];
+    const int tid = threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float4 x = kr[j];
-        k[4 * j] = x.x;
-        k[4 * j + 1] = x.y;
-        k[4 * j + 2] = x.z;
-        k[4 * j + 3] = x.w;
+    for (int h = 0; h < G; ++h) {
+        // (a compiler barrier: one head's chains in flight at a time)
+        asm volatile("" ::: "memory");
+        float acc[kTPT];
+#pragma unroll
+        for (int t = 0; t < kTPT; ++t) acc[t] = 0.0f;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+            const float4 q = reinterpret_cast<const float4 *>(S.qr[h])[j4];
+#pragma unroll
+            for (int t = 0; t < kTPT; ++t) acc[t] = __builtin_fmaf(q.x, kv[t][j4].x, acc[t]);
+#pragma unroll
+            for (int t = 0; t < kTPT; ++t) acc[t] = __builtin_fmaf(q.y, kv[t][j4].y, acc[t]);
+#pragma unroll
+            for (int t = 0; t < kTPT; ++t) acc[t] = __builtin_fmaf(q.z, kv[t][j4].z, acc[t]);
+#pragma unroll
+            for (int t = 0; t < kTPT; ++t) acc[t] = __builtin_fmaf(q.w, kv[t][j4].w, acc[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < kTPT; ++t) {
+            const float a = (acc[t] == 0.0f) ? 0.0f : acc[t];
+            sc[t][h] = (t * kT + tid < cn) ? a : -INFINITY;
+        }
     }
-    float acc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc = __builtin_fmaf(S.qr[h][j], k[j], acc);
-    return (acc == 0.0f) ? 0.0f : acc;
 }
 
 // --------------------------------------------------------- level 1 merge
 
-// Merges n <= kGS histogram records in[0..n) (published by other blocks) of
-// the G heads: leaves the merged bins in S.a.h.acc (bin kNB-1: everything
-// below the window), the merged max in S.a.h.om and its bin in S.a.h.oT.
-// Each record's bins are shifted down by the distance of its top bin from
-// the merged top and its masses scaled by exp(m_rec - m_merged); bins that
-// fall out of the window join the last bin.  Summation order is fixed.
+// The row's reducer for head h: merges the n block records of head h (all
+// published) into the row's histogram and publishes the head's threshold.
+// One round of loads: every record's max, top bin and bins together.  Each
+// record's bins are shifted down by the distance of its top bin from the
+// row's top and scaled by exp(m_b - M); bins that fall out of the window
+// join the last bin.  Then: Z = sum of every bin; the boundary bin is the
+// first bin from the top whose running mass (every bin above it plus its
+// own) reaches p Z, tested bin by bin so no rounding of the parallel prefix
+// can skip it; when the total falls short of p Z through rounding, the
+// lowest bin with mass.
 template <int G>
-__device__ void hist_merge(const HistRec *in, int n, LayerLds &S)
+__device__ __forceinline__ void reduce_head(const LayerParams &P, int rg, int h, LayerLds &S)
 {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+    const int n = P.bpr;  // <= 256
     HistLds &H = S.a.h;
-    if (tid < n * kMH) {
-        const int k = tid / kMH, hh = tid % kMH;
-        H.rm[k][hh] = hh < G ? ld_agent(&in[k].m[hh]) : -INFINITY;
-        H.rT[k][hh] = hh < G ? ld_agent_i(&in[k].T[hh]) : 0;
-    }
-    const int hh = tid / kNB, j = tid % kNB;
-    const bool act = hh < G;
-    double v[kGS];
+    const HistRec *in = P.ws.h1 + (int64_t)rg * P.bpr;
+    constexpr int kPer = 256 / (kT / kNB);  // records per thread
+    const int j = tid % kNB, part = tid / kNB;
+    double v[kPer];
 #pragma unroll
-    for (int k = 0; k < kGS; ++k) v[k] = (act && k < n) ? ld_agent(&in[k].mass[hh][j]) : 0.0;
+    for (int k = 0; k < kPer; ++k) {
+        const int b = part + k * (kT / kNB);
+        v[k] = b < n ? ld_agent(&in[b].mass[h][j]) : 0.0;
+    }
+    float m = -INFINITY;
+    int T = -32768;
+    if (tid < n) {
+        m = ld_agent(&in[tid].m[h]);
+        T = ld_agent_i(&in[tid].T[h]);
+        H.rm[tid] = m;
+        H.rT[tid] = T;
+    }
+    H.hist[part][j] = 0.0;  // (the block's own histogram is published)
+    m = wave_max(m);
+    const float tw = wave_max((float)T);
+    if (lane == 0) {
+        H.wm[w] = m;
+        H.wt[w] = (int32_t)tw;
+    }
     __syncthreads();
-    if (tid < G) {
-        float om = -INFINITY;
-        int oT = -32768;
-        for (int k = 0; k < n; ++k) {
-            om = fmaxf(om, H.rm[k][tid]);
-            oT = max(oT, H.rT[k][tid]);
+    if (tid == 0) {
+        float M = H.wm[0];
+        int32_t TT = H.wt[0];
+        for (int i = 1; i < kNW; ++i) {
+            M = fmaxf(M, H.wm[i]);
+            TT = max(TT, H.wt[i]);
         }
-        H.om[tid] = om;
-        H.oT[tid] = oT;
-    }
-    if (act) H.acc[hh][j] = 0.0;
-    __syncthreads();
-    if (tid < n * kMH) {
-        const int k = tid / kMH, h2 = tid % kMH;
-        H.rf[k][h2] = h2 < G ? exp_tang((double)H.rm[k][h2] - (double)H.om[h2], S.etbl) : 0.0;
+        H.M = M;
+        H.T = TT;
     }
     __syncthreads();
+    if (tid < n) {
+        H.ro[tid] = H.T - H.rT[tid];
+        H.rf[tid] = exp_tang((double)H.rm[tid] - (double)H.M, S.etbl);
+    }
+    __syncthreads();
+    // Each of the 8 thread groups adds its records into a row of its own:
+    // the lanes of a wave shift by the same distance, so their bins differ.
     double u = 0.0;
 #pragma unroll
-    for (int k = 0; k < kGS; ++k) {
-        if (k < n) {
-            if (act) {
-                const int o = H.oT[hh] - H.rT[k][hh];
-                const double val = v[k] * H.rf[k][hh];
-                const int dst = j + o;
-                if (j < kNB - 1 && o >= 0 && dst < kNB - 1)
-                    H.acc[hh][dst] += val;
-                else
-                    u += val;
-            }
-            __syncthreads();
+    for (int k = 0; k < kPer; ++k) {
+        const int b = part + k * (kT / kNB);
+        if (b < n) {
+            const int o = H.ro[b];
+            const double val = v[k] * H.rf[b];
+            const int dst = j + o;
+            if (j < kNB - 1 && o >= 0 && dst < kNB - 1)
+                atomicAdd(&H.hist[part][dst], val);
+            else
+                u += val;
         }
     }
     const double ws = wave_sum(u);
-    if (lane_id() == 0) H.ru[tid / kWave] = ws;
+    if (lane == 0) H.ru[w] = ws;
     __syncthreads();
-    if (act && j == kNB - 1) H.acc[hh][kNB - 1] = H.ru[2 * hh] + H.ru[2 * hh + 1];
-    __syncthreads();
-}
-
-// Publishes the merged histogram (S.a.h.acc, om, oT) as a record.
-template <int G>
-__device__ void hist_publish(HistRec *dst, LayerLds &S)
-{
-    const int tid = threadIdx.x, hh = tid / kNB, j = tid % kNB;
-    if (hh < G) st_agent(&dst->mass[hh][j], S.a.h.acc[hh][j]);
-    if (tid < G) {
-        st_agent(&dst->m[tid], S.a.h.om[tid]);
-        st_agent_i(&dst->T[tid], S.a.h.oT[tid]);
+    if (tid < kNB) {
+        double a = 0.0;
+#pragma unroll
+        for (int q = 0; q < kT / kNB; ++q) a += H.hist[q][tid];
+        H.acc[tid] = a;
     }
-}
-
-// The row's threshold from its merged histogram: wave 2h takes head h.
-// Z = sum of every bin; the boundary bin is the first bin from the top whose
-// running mass (every bin above it plus its own) reaches p Z, tested bin by
-// bin so no rounding of the parallel prefix can skip it; when the total
-// falls short of p Z through rounding, the lowest bin with mass.
-template <int G>
-__device__ void pick_threshold(const LayerParams &P, int rg, LayerLds &S)
-{
-    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
-    if ((w & 1) || (w >> 1) >= G) return;
-    const int h = w >> 1;
-    const double w0 = S.a.h.acc[h][2 * lane], w1 = S.a.h.acc[h][2 * lane + 1];
+    __syncthreads();
+    if (tid == 0) {
+        double U = 0.0;
+        for (int i = 0; i < kNW; ++i) U += H.ru[i];
+        H.acc[kNB - 1] += U;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    const double w0 = H.acc[2 * lane], w1 = H.acc[2 * lane + 1];
     const double inc = wave_inclusive_scan(w0 + w1);
     const double Z = read_lane(inc, kWave - 1);
     const double Pt = P.pd * Z;
@@ -649,15 +677,14 @@ __device__ void pick_threshold(const LayerParams &P, int rg, LayerLds &S)
     }
     const uint64_t cm = __ballot(cross >= 0);
     const uint64_t lm = __ballot(low >= 0);
-    int src;
     int js;
     double A;
     if (cm) {
-        src = __ffsll((unsigned long long)cm) - 1;
+        const int src = __ffsll((unsigned long long)cm) - 1;
         js = read_lane(cross, src);
         A = read_lane(cross_b, src);
     } else if (lm) {
-        src = 63 - __clzll((unsigned long long)lm);
+        const int src = 63 - __clzll((unsigned long long)lm);
         js = read_lane(low, src);
         A = read_lane(low_b, src);
     } else {
@@ -670,11 +697,126 @@ __device__ void pick_threshold(const LayerParams &P, int rg, LayerLds &S)
     }
     if (lane == 0) {
         PickRec *pr = P.ws.pick + (int64_t)rg * kMH + h;
-        st_agent(&pr->M, S.a.h.om[h]);
-        st_agent_i(&pr->T, S.a.h.oT[h]);
+        st_agent(&pr->M, H.M);
+        st_agent_i(&pr->T, H.T);
         st_agent_i(&pr->jstar, js);
         st_agent(&pr->A, A);
         st_agent(&pr->Pt, Pt);
+    }
+}
+
+// Level-2 digit of a score inside its level-1 bin: floor(4096 s) counted from
+// the bin's low edge, 1024 digits of width 1/4096 (clamped, so scores beyond
+// the 16-bit bin range land in the end digits).  Monotone in s within a bin.
+__device__ __forceinline__ int fine_digit(float s)
+{
+    const double t = floor((double)s * 4096.0) - (double)score_bin(s) * 1024.0;
+    return (int)fmin(fmax(t, 0.0), (double)(kFine - 1));
+}
+
+// Head h's level-2 threshold, by the head's reducer block once every block
+// of the row has classified.  The head's candidates (the row's candidate
+// list) make a histogram in LDS over 1024 digits of width 1/4096 inside the
+// boundary bin: fp64 mass exp(s - M) and count per digit.  The boundary
+// digit is the first from the top whose running mass from A (the mass above
+// the boundary bin) reaches p Z; the digits above it are kept, the digit
+// itself is resolved.  Also reads the head's kept and candidate totals and
+// resets those counters (every block has added to them).
+template <int G>
+__device__ __forceinline__ void fine_head(const LayerParams &P, int rg, int h, LayerLds &S)
+{
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+    RgCtl &ctl = P.ws.ctl[rg];
+    FineLds &F = S.a.f;
+    F.m[tid] = 0.0;
+    F.c[tid] = 0u;
+    if (tid == 0) {
+        S.fka = (uint32_t)(ld_agent(&ctl.kept[h]) >> 32);
+        S.fnc = (uint32_t)(ld_agent(&ctl.cand[h]) >> 32);
+        ctr_reset(&ctl.kept[h]);
+        ctr_reset(&ctl.cand[h]);
+    }
+    __syncthreads();
+    const PickRec pk = S.pick[h];
+    const uint32_t ka = S.fka, nc = min(S.fnc, (uint32_t)P.N);
+    const bool digits = pk.jstar < kNB - 1 && nc > 0u;
+    if (digits) {
+        const uint2 *gc = P.ws.cand + ((int64_t)rg * G + h) * P.N;
+        const double M = (double)pk.M;
+        constexpr int kU = 8;  // candidates in flight per thread
+        for (uint32_t k0 = 0; k0 < nc; k0 += kU * kT) {
+            uint2 e[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const uint32_t k = k0 + (uint32_t)(u * kT + tid);
+                e[u] = k < nc ? ld_cand2(gc + k) : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (k0 + (uint32_t)(u * kT + tid) < nc) {
+                    const float sv = key_score(e[u].x);
+                    const int d = fine_digit(sv);
+                    atomicAdd(&F.m[d], exp_tang((double)sv - M, S.etbl));
+                    atomicAdd(&F.c[d], 1u);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // Thread t takes digit 1023 - t: exclusive prefixes from the top.
+    const double fm = F.m[kFine - 1 - tid];
+    const uint32_t fc = F.c[kFine - 1 - tid];
+    double tot;
+    const double before = block_exclusive_scan<kT, double>(fm, F.dscan, &tot);
+    uint32_t ctot;
+    const uint32_t cb = block_exclusive_scan<kT, uint32_t>(fc, F.uscan, &ctot);
+    const bool hit = digits && fc != 0u && pk.A + before + fm >= pk.Pt;
+    const uint64_t hm = __ballot(hit);
+    if (lane == 0) F.first[w] = hm ? (uint32_t)(__ffsll((unsigned long long)hm) - 1) : 64u;
+    __syncthreads();
+    int ft = -1;
+    for (int i = 0; i < kNW; ++i)
+        if (F.first[i] < 64u) {
+            ft = i * kWave + (int)F.first[i];
+            break;
+        }
+    Pick2Rec r;
+    r.ka = ka;
+    r.nc = nc;
+    bool writer = tid == 0;
+    if (!digits) {
+        // No candidates, or the boundary bin is the last (no digits): every
+        // candidate goes to the resolve.
+        r.mode = 2;
+        r.j2 = 0;
+        r.k2 = 0u;
+        r.cstar = nc;
+        r.A2 = pk.A;
+    } else if (ft < 0) {
+        // The bin's mass falls short of the target through rounding: every
+        // candidate is kept.
+        r.mode = 1;
+        r.j2 = -1;
+        r.k2 = nc;
+        r.cstar = 0u;
+        r.A2 = pk.A;
+    } else {
+        writer = tid == ft;
+        r.mode = 0;
+        r.j2 = kFine - 1 - ft;
+        r.k2 = cb;
+        r.cstar = fc;
+        r.A2 = pk.A + before;
+    }
+    if (writer) {
+        Pick2Rec *pr = P.ws.pick2 + (int64_t)rg * kMH + h;
+        st_agent_i(&pr->j2, r.j2);
+        st_agent_i(&pr->mode, r.mode);
+        st_agent(&pr->ka, r.ka);
+        st_agent(&pr->k2, r.k2);
+        st_agent(&pr->cstar, r.cstar);
+        st_agent(&pr->nc, r.nc);
+        st_agent(&pr->A2, r.A2);
     }
 }
 
@@ -685,7 +827,7 @@ __device__ void pick_threshold(const LayerParams &P, int rg, LayerLds &S)
 // a wave takes query heads 2lg and 2lg + 1, so every lane group reads the
 // same row (one memory request per row and wave).
 template <int G>
-__device__ void local_item(const LayerParams &P, int item, LayerLds &S)
+__device__ __forceinline__ void local_item(const LayerParams &P, int item, LayerLds &S)
 {
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int lg = lane >> 4, sub = lane & 15;
@@ -716,13 +858,12 @@ __device__ void local_item(const LayerParams &P, int item, LayerLds &S)
     AttState sa, sb;
     att_reset(sa);
     att_reset(sb);
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < kLocIters; ++it) {
         uint4 kw[kLU], vw[kLU];
         bool ok[kLU];
 #pragma unroll
         for (int u = 0; u < kLU; ++u) {
-            const int pos = p0 + w * (2 * kLU) + it * kLU + u;
+            const int pos = p0 + w * (kLocIters * kLU) + it * kLU + u;
             ok[u] = pos < p1;
             const int tok = pos < P.sink_end ? pos : P.w0 + (pos - P.sink_end);
             const int64_t off = ok[u] ? (int64_t)tok * 128 : 0;
@@ -803,23 +944,24 @@ __device__ void local_item(const LayerParams &P, int item, LayerLds &S)
 // -------------------------------------------------------------- classify
 
 // Marks this block's tokens against the row's threshold.  Kept tokens go to
-// the head's LDS list and to the row's idx list (one global slot
-// reservation per head and block); tokens of the boundary bin are rescored
-// and written as candidates (score key, index).
+// the head's LDS list (one global slot reservation per head and block; the
+// idx entries are written later, by level1_idx); tokens of the boundary bin
+// are rescored and written as candidates (score key, index).
 template <int G>
-__device__ void classify(const LayerParams &P, int rg, int b, int g, int64_t c0, int cn,
-                         LayerLds &S)
+__device__ __forceinline__ void classify(const LayerParams &P, int rg, int b, int g, int64_t c0,
+                                         int cn, LayerLds &S)
 {
     constexpr int TPT = kTPT;
     constexpr int cmax = kChunk;
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     RgCtl &ctl = P.ws.ctl[rg];
     // This thread's score bins (read before the block overwrites them with
-    // its lists: the barrier below comes first).
+    // its lists: the barriers below come first).
     uint32_t gsp[G * kTPT / 2];
 #pragma unroll
     for (int e = 0; e < G * kTPT / 2; ++e) gsp[e] = S.b.gsw[e][tid];
     uint32_t km[G], cm[G], ex[G];
+    uint32_t anyc = 0;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const int T = S.pick[h].T, js = S.pick[h].jstar;
@@ -835,6 +977,7 @@ __device__ void classify(const LayerParams &P, int rg, int b, int g, int64_t c0,
         }
         km[h] = k;
         cm[h] = c;
+        anyc |= c;
         const uint32_t mine = (uint32_t)__popc(k) | ((uint32_t)__popc(c) << 16);
         const uint32_t inc = wave_inclusive_scan(mine);
         ex[h] = inc - mine;
@@ -863,48 +1006,82 @@ __device__ void classify(const LayerParams &P, int rg, int b, int g, int64_t c0,
         }
     }
     __syncthreads();
+    // Candidates: the exact score again (the same chain as the scan, from the
+    // key rows of this thread's candidate tokens, all loaded first), its key
+    // to the row's candidate list.
+    const float4 *krow =
+        reinterpret_cast<const float4 *>(P.k_r + ((int64_t)b * P.Hkv_r + g) * P.kr_cap * 16);
+    float4 kv[kTPT][4];
+#pragma unroll
+    for (int t = 0; t < kTPT; ++t) {
+        if ((anyc >> t) & 1u) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kv[t][j] = krow[(c0 + t * kT + tid) * 4 + j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kv[t][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        int32_t *ir = P.idx + ((int64_t)b * P.Hq_r + (int64_t)g * G + h) * P.N;
-        const uint32_t kb = S.kgb[h];
-        uint32_t pos = (S.wcnt[h][w] & 0xFFFFu) + (ex[h] & 0xFFFFu);
-        for (uint32_t m = km[h]; m; m &= m - 1) {
-            const int t = __ffs(m) - 1;
-            const uint32_t slot = kb + pos++;
-            if (slot < (uint32_t)P.N) ir[slot] = (int32_t)(c0 + t * kT + tid);
-        }
+        if (!cm[h]) continue;
         uint2 *cr = P.ws.cand + ((int64_t)rg * G + h) * P.N;
-        const uint32_t cb = S.cgb[h];
-        uint32_t cpos = (S.wcnt[h][w] >> 16) + (ex[h] >> 16);
-        for (uint32_t m = cm[h]; m; m &= m - 1) {
-            const int t = __ffs(m) - 1;
-            const int64_t i = c0 + t * kT + tid;
-            const float s = rescore(P, b, g, i, h, S);
-            const uint32_t slot = cb + cpos++;
-            if (slot < (uint32_t)P.N) st_cand2(cr + slot, make_uint2(score_key(s), (uint32_t)i));
+        uint32_t cpos = S.cgb[h] + (S.wcnt[h][w] >> 16) + (ex[h] >> 16);
+#pragma unroll
+        for (int t = 0; t < kTPT; ++t) {
+            if (!((cm[h] >> t) & 1u)) continue;
+            const float k[16] = {kv[t][0].x, kv[t][0].y, kv[t][0].z, kv[t][0].w,
+                                 kv[t][1].x, kv[t][1].y, kv[t][1].z, kv[t][1].w,
+                                 kv[t][2].x, kv[t][2].y, kv[t][2].z, kv[t][2].w,
+                                 kv[t][3].x, kv[t][3].y, kv[t][3].z, kv[t][3].w};
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc = __builtin_fmaf(S.qr[h][j], k[j], acc);
+            const float sv = (acc == 0.0f) ? 0.0f : acc;
+            const uint32_t i = (uint32_t)(c0 + t * kT + tid);
+            const uint32_t slot = cpos++;
+            if (slot < (uint32_t)P.N) st_cand2(cr + slot, make_uint2(score_key(sv), i));
         }
     }
     wait_vmem();
     __syncthreads();
-    if (tid == 0) ctr_arrive(&ctl.classified);
+}
+
+// The idx entries of the block's level-1 kept tokens, from its LDS lists
+// (coalesced; nothing in the launch reads them).
+template <int G>
+__device__ __forceinline__ void level1_idx(const LayerParams &P, int b, int g, int64_t c0,
+                                           LayerLds &S)
+{
+    constexpr int cmax = kChunk;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        int32_t *ir = P.idx + ((int64_t)b * P.Hq_r + (int64_t)g * G + h) * P.N;
+        const uint32_t kb = S.kgb[h], kc = S.kc[h];
+        for (uint32_t e = threadIdx.x; e < kc; e += kT) {
+            const uint32_t slot = kb + e;
+            if (slot < (uint32_t)P.N) ir[slot] = (int32_t)(c0 + S.b.list[h * cmax + e]);
+        }
+    }
 }
 
 // -------------------------------------------------------- own kept rows
 
-// The block's kept rows of each head (the LDS lists), in batches of
-// kBatch rows per wave; one partial per head goes to att1[blk].
+// Attends the block's listed rows of each head (head h: cnt[h] offsets in
+// the chunk at S.b.list[h * kChunk]), kBatch rows per wave batch, merged
+// into the waves' slots.
 template <int G>
-__device__ void gather_chunk(const LayerParams &P, int b, int g, int64_t c0, int blk, LayerLds &S)
+__device__ __forceinline__ void gather_lists(const LayerParams &P, int b, int g, int64_t c0, const uint32_t *cnt,
+                             LayerLds &S)
 {
     constexpr int cmax = kChunk;
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int lg = lane >> 4, sub = lane & 15;
-    slots_clear(S);
     if (tid == 0) {
         int acc = 0;
         for (int h = 0; h < G; ++h) {
             S.bpre[h] = acc;
-            acc += ((int)S.kc[h] + kBatch - 1) / kBatch;
+            acc += ((int)cnt[h] + kBatch - 1) / kBatch;
         }
         S.bpre[G] = acc;
     }
@@ -929,7 +1106,7 @@ __device__ void gather_chunk(const LayerParams &P, int b, int g, int64_t c0, int
             load_q8(P.q + ((int64_t)b * P.Hq + (int64_t)g * G + h) * 128 + sub * 8, P.qscale, qf);
         }
         const int base = (bi - S.bpre[h]) * kBatch;
-        const int kc = (int)S.kc[h];
+        const int kc = (int)cnt[h];
         int tok[kRU];
 #pragma unroll
         for (int u = 0; u < kRU; ++u) {
@@ -940,7 +1117,76 @@ __device__ void gather_chunk(const LayerParams &P, int b, int g, int64_t c0, int
     }
     if (cur >= 0) att_flush(a, w, cur, S);
     __syncthreads();
-    slots_to_partial(G, P.ws.att1 + (int64_t)blk * kMH * kPF, kPF, S);
+}
+
+// The block's candidates that the level-2 threshold keeps: those above the
+// boundary digit (mode 0) or all of them (mode 1).  They are listed in LDS
+// (offsets in the chunk, head h at S.b.list[h * kChunk], S.n2[h] of them)
+// and written to the head's idx list after the ka tokens of level 1 (one
+// slot reservation per head and block).  Then the block counts itself on
+// p2_done: it reads no candidate of the row after this.
+template <int G>
+__device__ __forceinline__ void level2_lists(const LayerParams &P, int rg, int b, int g, int64_t c0, LayerLds &S)
+{
+    constexpr int cmax = kChunk;
+    const int tid = threadIdx.x;
+    RgCtl &ctl = P.ws.ctl[rg];
+    if (tid < G) S.n2[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const int mode = S.pick2[h].mode;
+        if (mode == 2) continue;
+        const int j2 = S.pick2[h].j2;
+        const uint32_t cb = S.cgb[h];
+        const uint32_t n = min(S.cc[h], (uint32_t)P.N - min(cb, (uint32_t)P.N));
+        const uint2 *cr = P.ws.cand + ((int64_t)rg * G + h) * P.N + cb;
+        for (uint32_t e0 = 0; e0 < n; e0 += kT) {
+            const uint32_t e = e0 + (uint32_t)tid;
+            bool keep = false;
+            uint32_t off = 0u;
+            if (e < n) {
+                const uint2 c = ld_cand2(cr + e);
+                keep = mode == 1 || fine_digit(key_score(c.x)) > j2;
+                off = c.y - (uint32_t)c0;
+            }
+            const int64_t pos = wave_append(keep, &S.n2[h]);
+            if (pos >= 0 && pos < cmax) S.b.list[h * cmax + pos] = (uint16_t)off;
+        }
+    }
+    __syncthreads();
+    if (tid < G) {
+        S.n2[tid] = min(S.n2[tid], (uint32_t)cmax);
+        S.k2b[tid] = S.n2[tid] ? ctr_add(&ctl.kept2[tid], S.n2[tid]) : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        int32_t *ir = P.idx + ((int64_t)b * P.Hq_r + (int64_t)g * G + h) * P.N;
+        const uint32_t base = S.pick2[h].ka + S.k2b[h];
+        for (uint32_t e = tid; e < S.n2[h]; e += kT) {
+            const uint32_t slot = base + e;
+            if (slot < (uint32_t)P.N) ir[slot] = (int32_t)(c0 + S.b.list[h * cmax + e]);
+        }
+    }
+    if (tid == 0) ctr_arrive(&ctl.p2_done);
+}
+
+// One of the row's bpr + G finishers (every block after its level-2 lists,
+// every resolver after its resolve).  The last resets the counters that
+// outlive the waits on them.
+template <int G>
+__device__ __forceinline__ void fin_arrive(const LayerParams &P, RgCtl &ctl)
+{
+    if (ctr_arrive(&ctl.fin_done) != (uint32_t)(P.bpr + G - 1)) return;
+    ctr_reset(&ctl.hist_row);
+    ctr_reset(&ctl.pick_ready);
+    ctr_reset(&ctl.classified);
+    ctr_reset(&ctl.pick2_ready);
+    ctr_reset(&ctl.p2_done);
+#pragma unroll
+    for (int h = 0; h < G; ++h) ctr_reset(&ctl.kept2[h]);
+    ctr_reset(&ctl.fin_done);
 }
 
 // --------------------------------------------------------------- resolve
@@ -1002,7 +1248,7 @@ struct CandSet {
 // compacted in place in memory (in order: positions only move down).
 // Returns the number of survivors.
 template <class Cls>
-__device__ int64_t filter_pass(const CandSet &cs, int64_t n, Cls cls, bool to_lds, Cand *dst,
+__device__ __forceinline__ int64_t filter_pass(const CandSet &cs, int64_t n, Cls cls, bool to_lds, Cand *dst,
                                uint2 *gc, double M, int32_t *ir, uint32_t cap, LayerLds &S)
 {
     const int tid = threadIdx.x;
@@ -1039,7 +1285,7 @@ __device__ int64_t filter_pass(const CandSet &cs, int64_t n, Cls cls, bool to_ld
 // key descending, index ascending), lays their masses out in rank order,
 // and keeps the shortest rank prefix whose running mass from A reaches Pt
 // (all n when none does).
-__device__ void finish_few(const Cand *c, int n, double A, double Pt, int32_t *ir, uint32_t cap,
+__device__ __forceinline__ void finish_few(const Cand *c, int n, double A, double Pt, int32_t *ir, uint32_t cap,
                            LayerLds &S)
 {
     const int l = lane_id();
@@ -1064,24 +1310,40 @@ __device__ void finish_few(const Cand *c, int n, double A, double Pt, int32_t *i
     keep_tok(v && rank <= last, e.idx, ir, cap, S);
 }
 
-// Resolves the boundary bin of head h: appends its kept tokens to the idx
-// list (after the ka rows the blocks kept), writes the head's count, and
-// leaves the kept boundary tokens' count in S.nkeep.
+// Resolves head h's final candidate set: the candidates of the boundary
+// digit (level-2 mode 0) or every candidate (mode 2).  Appends the kept ones
+// at ir (room for cap) and leaves their count in S.nkeep.  A set too large
+// for LDS is compacted in place in the candidate list, which waits until
+// no block reads the list any more.
 template <int G>
-__device__ void resolve_set(const LayerParams &P, int rg, int b, int g, int h, LayerLds &S)
+__device__ __forceinline__ void resolve_set(const LayerParams &P, int rg, int h, int32_t *ir, uint32_t cap,
+                            LayerLds &S)
 {
     const int tid = threadIdx.x;
     const int N = P.N;
-    const uint32_t ka = min(S.ka, (uint32_t)N);
-    int64_t n = (int64_t)min(S.nc, (uint32_t)N - ka);
+    const Pick2Rec q = S.pick2[h];
+    if (q.mode == 1) return;
     const PickRec pk = S.pick[h];
     const double M = (double)pk.M, Pt = pk.Pt;
-    double A = pk.A;
-    int32_t *ir = P.idx + ((int64_t)b * P.Hq_r + (int64_t)g * G + h) * N + ka;
-    const uint32_t cap = (uint32_t)N - ka;
+    double A = q.A2;
     uint2 *gc = P.ws.cand + ((int64_t)rg * G + h) * N;
     CandSet cs{nullptr, gc};
     int cur = 0;
+    int64_t n = (int64_t)min(q.nc, (uint32_t)N);
+    if (q.mode == 0) {
+        const int j2 = q.j2;
+        const bool to_lds = q.cstar <= (uint32_t)kResCap;
+        if (!to_lds) {
+            if (tid == 0)
+                wait_level(&P.ws.ctl[rg].p2_done, (uint32_t)P.bpr, P.spin_limit, P.status);
+            __syncthreads();
+        }
+        n = filter_pass(
+            cs, n, [=](const Cand &x) { return fine_digit(key_score(x.key)) == j2 ? 2 : 0; },
+            to_lds, S.b.rb.buf[0], gc, M, ir, cap, S);
+        if (to_lds) cs.lds = S.b.rb.buf[0];
+    }
+    n = min(n, (int64_t)cap);
     for (int level = 0; level < 8 && n > 0; ++level) {
         if (!cs.lds && n <= kResCap) {
             for (int64_t k = tid; k < n; k += kT) S.b.rb.buf[0][k] = cs.get(k, M, S.etbl);
@@ -1257,28 +1519,25 @@ __device__ void resolve_set(const LayerParams &P, int rg, int b, int g, int h, L
     }
 }
 
-// Claimed head h: resolve its boundary bin, write its count, attend the
-// kept boundary rows and join the head's final merge.
+// Claimed head h: resolve its final candidate set, write the head's count,
+// attend the kept boundary rows and join the head's final merge.
 template <int G>
-__device__ void resolve_head(const LayerParams &P, int rg, int b, int g, int h, LayerLds &S)
+__device__ __forceinline__ void resolve_head(const LayerParams &P, int rg, int b, int g, int h, LayerLds &S)
 {
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int lg = lane >> 4, sub = lane & 15;
     RgCtl &ctl = P.ws.ctl[rg];
-    if (tid == 0) {
-        wait_level(&ctl.classified, (uint32_t)P.bpr, P.spin_limit, P.status);
-        S.ka = (uint32_t)(ld_agent(&ctl.kept[h]) >> 32);
-        S.nc = (uint32_t)(ld_agent(&ctl.cand[h]) >> 32);
-        S.nkeep = 0;
-    }
+    const Pick2Rec q = S.pick2[h];
+    const uint32_t base = min(q.ka + q.k2, (uint32_t)P.N);
+    const uint32_t cap = (uint32_t)P.N - base;
+    int32_t *ir = P.idx + ((int64_t)b * P.Hq_r + (int64_t)g * G + h) * P.N + base;
+    if (tid == 0) S.nkeep = 0;
     __syncthreads();
-    resolve_set<G>(P, rg, b, g, h, S);
+    resolve_set<G>(P, rg, h, ir, cap, S);
     __syncthreads();
-    const uint32_t ka = min(S.ka, (uint32_t)P.N);
-    const uint32_t kb = min(S.nkeep, (uint32_t)P.N - ka);
-    if (tid == 0) P.count[(int64_t)b * P.Hq_r + (int64_t)g * G + h] = (int32_t)(ka + kb);
+    const uint32_t kb = min(S.nkeep, cap);
+    if (tid == 0) P.count[(int64_t)b * P.Hq_r + (int64_t)g * G + h] = (int32_t)(base + kb);
     // The kept boundary rows (listed in LDS, the rest read back from idx).
-    const int32_t *ir = P.idx + ((int64_t)b * P.Hq_r + (int64_t)g * G + h) * P.N + ka;
     wait_vmem();
     slots_clear(S);
     __syncthreads();
@@ -1288,11 +1547,11 @@ __device__ void resolve_head(const LayerParams &P, int rg, int b, int g, int h, 
     AttState a;
     att_reset(a);
     bool any = false;
-    for (int64_t base = (int64_t)w * kBatch; base < kb; base += (int64_t)kNW * kBatch) {
+    for (int64_t e0 = (int64_t)w * kBatch; e0 < kb; e0 += (int64_t)kNW * kBatch) {
         int tok[kRU];
 #pragma unroll
         for (int u = 0; u < kRU; ++u) {
-            const int64_t e = base + lg + 4 * u;
+            const int64_t e = e0 + lg + 4 * u;
             tok[u] = e < kb ? (e < kBkCap ? S.b.rb.bk[e] : ld_agent_i(ir + e)) : -1;
         }
         att_rows(P.K + kvb, P.V + kvb, qf, tok, P.N, a);
@@ -1308,17 +1567,7 @@ __device__ void resolve_head(const LayerParams &P, int rg, int b, int g, int h, 
                       (int64_t)kMH * kPF, P.ngrp + 1, 1, 1u, nullptr, outp);
     }
     __syncthreads();
-    if (tid == 0) {
-        ctr_reset(&ctl.kept[h]);
-        ctr_reset(&ctl.cand[h]);
-        if (ctr_arrive(&ctl.res_done) == (uint32_t)G - 1u) {
-            // Every block of the row has passed the threshold wait and every
-            // resolver the classified wait.
-            ctr_reset(&ctl.pick_ready);
-            ctr_reset(&ctl.classified);
-            ctr_reset(&ctl.res_done);
-        }
-    }
+    if (tid == 0) fin_arrive<G>(P, ctl);
     __syncthreads();
 }
 
@@ -1339,13 +1588,17 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
     const int cn = (int)min((int64_t)P.C, (int64_t)P.N - c0);
     RgCtl &ctl = P.ws.ctl[rg];
 
+    // ---- scan: the key rows first, then the block's constants to LDS while
+    // they arrive; scores in registers
+    float4 kv[kTPT][4];
+    scan_load(P, b, g, c0, cn, kv);
+    asm volatile("" ::: "memory");
     for (int i = tid; i < kMH * kNB; i += kT) S.a.h.hist[i / kNB][i % kNB] = 0.0;
     if (tid < kExpTable) S.etbl[tid] = kLayerExpTbl[tid];
     if (tid < G * 16) S.qr[tid / 16][tid % 16] = P.q_r[((int64_t)b * P.Hq_r + g * G) * 16 + tid];
-
-    // ---- scan: scores in registers
+    __syncthreads();
     float sc[TPT][G];
-    scan_scores<G>(P, b, g, c0, cn, sc);
+    scan_scores<G>(kv, cn, S, sc);
     if (P.scores) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -1374,27 +1627,35 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
     __syncthreads();
 
     // ---- level 1: the block's histogram (mass exp(s - m_b) in fp64); each
-    // score's bin is kept in LDS (two 16-bit bins per word) for the classify
+    // score's bin is kept in LDS (two 16-bit bins per word) for the classify.
+    // No branches: a token past the chunk's end adds +0 to the last bin, so
+    // the kTPT exponentials of a head run interleaved.
+    {
+        uint32_t gw[G * kTPT / 2];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const double mbd = (double)S.mb[h];
-        const int Tb = S.Tb[h];
+        for (int e = 0; e < G * kTPT / 2; ++e) gw[e] = 0u;
 #pragma unroll
-        for (int t = 0; t < TPT; ++t) {
-            const float s = sc[t][h];
-            const int gs = score_bin(s);
-            if (t * kT + tid < cn) {
-                const int j = min(Tb - gs, kNB - 1);
-                atomicAdd(&S.a.h.hist[h][j], exp_tang((double)s - mbd, S.etbl));
+        for (int h = 0; h < G; ++h) {
+            asm volatile("" ::: "memory");
+            const double mbd = (double)S.mb[h];
+            const int Tb = S.Tb[h];
+            double ev[kTPT];
+            int jv[kTPT];
+#pragma unroll
+            for (int t = 0; t < TPT; ++t) {
+                const float s = sc[t][h];
+                const int gs = score_bin(s);
+                jv[t] = min(Tb - gs, kNB - 1);
+                ev[t] = exp_tang((double)s - mbd, S.etbl);
+                const int e = t * G + h;
+                gw[e >> 1] |= ((uint32_t)gs & 0xFFFFu) << (16 * (e & 1));
             }
-        }
-    }
 #pragma unroll
-    for (int e = 0; e < G * kTPT / 2; ++e) {
-        const int e0 = 2 * e, e1 = 2 * e + 1;
-        const uint32_t lo = (uint32_t)score_bin(sc[e0 / G][e0 % G]) & 0xFFFFu;
-        const uint32_t hi = (uint32_t)score_bin(sc[e1 / G][e1 % G]) & 0xFFFFu;
-        S.b.gsw[e][tid] = lo | (hi << 16);
+            for (int t = 0; t < TPT; ++t)
+                atomicAdd(&S.a.h.hist[h][jv[t]], t * kT + tid < cn ? ev[t] : 0.0);
+        }
+#pragma unroll
+        for (int e = 0; e < G * kTPT / 2; ++e) S.b.gsw[e][tid] = gw[e];
     }
     __syncthreads();
     {
@@ -1406,24 +1667,38 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
             st_agent_i(&hr->T[tid], S.Tb[tid]);
         }
     }
-    if (arrive_last_blk(P.ws.hist_grp + (int64_t)rg * P.ngrp + grp, (uint32_t)ngs, S)) {
-        hist_merge<G>(P.ws.h1 + (int64_t)rg * P.bpr + grp * kGS, ngs, S);
-        hist_publish<G>(P.ws.h2 + (int64_t)rg * P.ngrp + grp, S);
-        if (arrive_last_blk(&ctl.hist_row, (uint32_t)P.ngrp, S)) {
-            hist_merge<G>(P.ws.h2 + (int64_t)rg * P.ngrp, P.ngrp, S);
-            pick_threshold<G>(P, rg, S);
-            wait_vmem();
-            __syncthreads();
-            if (tid == 0) ctr_add(&ctl.pick_ready, 1u);
-        }
-    }
+    wait_vmem();
     __syncthreads();
+    if (tid == 0) ctr_arrive(&ctl.hist_row);
 
-    // ---- local heads while the threshold is found
-    for (int item = blk; item < P.NI; item += (int)gridDim.x) local_item<G>(P, item, S);
+    // ---- the row's thresholds: head h is reduced by block r0 + h % nr of
+    // the row (the last nr blocks), once every block has published
+    const int nr = min(G, P.bpr), r0 = P.bpr - nr;
+    if (c >= r0) {
+        if (tid == 0) wait_level(&ctl.hist_row, (uint32_t)P.bpr, P.spin_limit, P.status);
+        __syncthreads();
+        uint32_t nh = 0;
+        for (int h = c - r0; h < G; h += nr) {
+            reduce_head<G>(P, rg, h, S);
+            __syncthreads();
+            ++nh;
+        }
+        wait_vmem();
+        __syncthreads();
+        if (tid == 0) ctr_add(&ctl.pick_ready, nh);
+    }
 
-    // ---- the row's threshold
-    if (tid == 0) wait_level(&ctl.pick_ready, 1u, P.spin_limit, P.status);
+    // ---- local heads while the thresholds are found (blocks that reduce
+    // nothing, when there are any)
+    const int nlb = (int)(gridDim.x / P.bpr) * r0;
+    if (nlb > 0) {
+        if (c < r0)
+            for (int item = rg * r0 + c; item < P.NI; item += nlb) local_item<G>(P, item, S);
+    } else {
+        for (int item = blk; item < P.NI; item += (int)gridDim.x) local_item<G>(P, item, S);
+    }
+
+    if (tid == 0) wait_level(&ctl.pick_ready, (uint32_t)G, P.spin_limit, P.status);
     __syncthreads();
     if (tid < G) {
         const PickRec *pr = P.ws.pick + (int64_t)rg * kMH + tid;
@@ -1438,9 +1713,46 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
     }
     __syncthreads();
     classify<G>(P, rg, b, g, c0, cn, S);
+    if (tid == 0) ctr_arrive(&ctl.classified);
 
-    // ---- the block's own kept rows, then the group's merge
-    gather_chunk<G>(P, b, g, c0, blk, S);
+    // ---- the heads' level-2 thresholds, by the same blocks as level 1
+    if (c >= r0) {
+        if (tid == 0) wait_level(&ctl.classified, (uint32_t)P.bpr, P.spin_limit, P.status);
+        __syncthreads();
+        uint32_t nh = 0;
+        for (int h = c - r0; h < G; h += nr) {
+            fine_head<G>(P, rg, h, S);
+            __syncthreads();
+            ++nh;
+        }
+        wait_vmem();
+        __syncthreads();
+        if (tid == 0) ctr_add(&ctl.pick2_ready, nh);
+    }
+
+    // ---- the block's rows kept by level 1, then those kept by level 2
+    level1_idx<G>(P, b, g, c0, S);
+    slots_clear(S);
+    gather_lists<G>(P, b, g, c0, S.kc, S);
+    if (tid == 0) wait_level(&ctl.pick2_ready, (uint32_t)G, P.spin_limit, P.status);
+    __syncthreads();
+    if (tid < G) {
+        const Pick2Rec *pr = P.ws.pick2 + (int64_t)rg * kMH + tid;
+        Pick2Rec r;
+        r.j2 = ld_agent_i(&pr->j2);
+        r.mode = ld_agent_i(&pr->mode);
+        r.ka = ld_agent(&pr->ka);
+        r.k2 = ld_agent(&pr->k2);
+        r.cstar = ld_agent(&pr->cstar);
+        r.nc = ld_agent(&pr->nc);
+        r.A2 = ld_agent(&pr->A2);
+        S.pick2[tid] = r;
+    }
+    __syncthreads();
+    level2_lists<G>(P, rg, b, g, c0, S);
+    if (tid == 0) fin_arrive<G>(P, ctl);
+    gather_lists<G>(P, b, g, c0, S.n2, S);
+    slots_to_partial(G, P.ws.att1 + (int64_t)blk * kMH * kPF, kPF, S);
     if (arrive_last_blk(P.ws.att_grp + (int64_t)rg * P.ngrp + grp, (uint32_t)ngs, S)) {
         float *gp = P.ws.att2 + ((int64_t)rg * (P.ngrp + 1) + grp) * kMH * kPF;
         merge_records(P.ws.att1 + ((int64_t)rg * P.bpr + grp * kGS) * kMH * kPF,
@@ -1463,7 +1775,7 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
         __syncthreads();
     }
 
-    // ---- boundary bins: claimed by blocks as they finish
+    // ---- final candidate sets: claimed by blocks as they finish
     for (;;) {
         if (tid == 0) {
             const uint32_t t = ctr_add(&ctl.claim, 1u);
@@ -1526,10 +1838,9 @@ static size_t layer_ws_layout(const LayerGeom &L, int B, int N, LayerWs *W, void
         return o;
     };
     const size_t h1 = take((size_t)L.NB * sizeof(HistRec));
-    const size_t h2 = take((size_t)L.RG * L.ngrp * sizeof(HistRec));
     const size_t pk = take((size_t)L.RG * kMH * sizeof(PickRec));
+    const size_t p2 = take((size_t)L.RG * kMH * sizeof(Pick2Rec));
     const size_t ctl = take((size_t)L.RG * sizeof(RgCtl));
-    const size_t hg = take((size_t)L.RG * L.ngrp * 8);
     const size_t ag = take((size_t)L.RG * L.ngrp * 8);
     const size_t lc = take((size_t)B * (L.n_lkv > 0 ? L.n_lkv : 1) * 8);
     const size_t a1 = take((size_t)L.NB * kMH * kPF * sizeof(float));
@@ -1539,10 +1850,9 @@ static size_t layer_ws_layout(const LayerGeom &L, int B, int N, LayerWs *W, void
     if (W) {
         char *p = static_cast<char *>(base);
         W->h1 = reinterpret_cast<HistRec *>(p + h1);
-        W->h2 = reinterpret_cast<HistRec *>(p + h2);
         W->pick = reinterpret_cast<PickRec *>(p + pk);
+        W->pick2 = reinterpret_cast<Pick2Rec *>(p + p2);
         W->ctl = reinterpret_cast<RgCtl *>(p + ctl);
-        W->hist_grp = reinterpret_cast<unsigned long long *>(p + hg);
         W->att_grp = reinterpret_cast<unsigned long long *>(p + ag);
         W->loc_ctr = reinterpret_cast<unsigned long long *>(p + lc);
         W->att1 = reinterpret_cast<float *>(p + a1);

@@ -22,6 +22,19 @@ def _print(*a):
     print(*a, flush=True)
 
 
+@pytest.fixture(autouse=True)
+def _bounded_waits(request):
+    # Waits between blocks give up after about a quarter second here (a
+    # healthy call waits microseconds), and no test may leave a give-up in
+    # the status word, except the one that provokes it.
+    rtp.set_wait_limit(1 << 18)
+    rtp.device_status(clear=True)
+    yield
+    if request.node.name != "test_wait_give_up_is_reported":
+        assert rtp.device_status(clear=True) == 0, "a wait between blocks gave up"
+    rtp.set_wait_limit(1 << 24)
+
+
 # ------------------------------------------------------------ the workloads
 
 @pytest.mark.parametrize("ci", [0, 1, 3])
