@@ -38,13 +38,15 @@
 //            reducer builds the head's level-2 histogram from that list in
 //            LDS (1024 digits of width 1/4096 inside bin J*) and picks the
 //            boundary digit.
-//   gather   every block attends its own level-1 rows while the boundary
-//            digit is picked, then its candidates above that digit; one
-//            partial per head is merged by last arrivers in two levels.
-//   resolve  blocks that finish their gather claim the heads' boundary
-//            digits: a mass-weighted radix select over the candidates' score
-//            keys, ties to the lower index, then the kept boundary rows'
-//            attention, whose partial joins the final merge of the head.
+//   gather   every other block attends its own level-1 rows while the
+//            boundary digits are picked, then its candidates above those
+//            digits; one partial per head is merged by last arrivers in two
+//            levels.
+//   resolve  each head's reducer then resolves the head's boundary digit: a
+//            mass-weighted radix select over its candidates' score keys,
+//            ties to the lower index, then the kept boundary rows'
+//            attention, whose partial joins the head's final merge; then it
+//            attends its own rows.
 //
 // Every wait is bounded (a host-set limit) and reports a give-up in the
 // library's status word; every data-dependent index is range-checked, so a
@@ -76,7 +78,7 @@ constexpr int kLU = 4;                  // rows in flight per wave (local rows)
 constexpr int kLocIters = kTile / (kNW * kLU);  // local row batches per wave
 constexpr int kFine = 1024;             // level-2 digits of the boundary bin
 constexpr int kResCap = 1536;           // resolve candidates per LDS buffer
-constexpr int kBkCap = 4096;            // kept boundary tokens listed in LDS
+constexpr int kBkCap = 2048;            // kept boundary tokens listed in LDS
 constexpr int kListCap = kMH * kChunk;  // kept-token offsets per block (all heads)
 constexpr float kLog2eF = 1.4426950408889634f;
 
@@ -116,8 +118,8 @@ struct Pick2Rec {           // a head's level-2 threshold inside the boundary bi
 };
 
 struct RgCtl {  // tagged counters of one (batch row, retrieval KV head)
-    unsigned long long hist_row, pick_ready, classified, pick2_ready, claim, p2_done, fin_done,
-        pad;
+    unsigned long long hist_row, pick_ready, classified, pick2_ready, p2_done, fin_done, pad0,
+        pad1;
     unsigned long long kept[kMH], cand[kMH], kept2[kMH], att_row[kMH];
 };
 static_assert(sizeof(RgCtl) == 320, "RgCtl is 320 B");
@@ -133,6 +135,7 @@ struct LayerWs {
     float *att2;                   // [RG][ngrp + 1][kMH][kPF]; entry ngrp: the boundary rows
     float *loc;                    // [NI][kMH][kPF]
     uint2 *cand;                   // [RG][G][N]
+    uint2 *pdesc;                  // [RG][kMH][kMH] a reducer's level-1 lists: (idx slot, count)
 };
 
 struct LayerParams {
@@ -164,6 +167,7 @@ struct Cand {
 
 struct HistLds {
     double hist[kMH][kNB];   // the block's histogram
+    double wrow[kNW][kNB];   // a head's records merged per wave (row reducer)
     double acc[kNB];         // a head's merged histogram (row reducer)
     double rf[256];          // per block record: exp(m_b - M)
     double ru[kNW];
@@ -189,16 +193,12 @@ struct SlotLds {  // per-wave attention partials
 };
 
 struct ResLds {
+    Cand buf[2][kResCap];
     double hm[256];
     uint32_t hc[2048];
     double tmp[kWave];
     uint32_t uscan[kNW];
     double dscan[kNW];
-};
-
-struct ResBufs {
-    Cand buf[2][kResCap];
-    int32_t bk[kBkCap];
 };
 
 struct LayerLds {
@@ -211,8 +211,8 @@ struct LayerLds {
     union {
         uint32_t gsw[kMH * kTPT / 2][kT];  // scan to classify: this thread's score bins, 2 per word
         uint16_t list[kListCap];  // kept-token offsets in the chunk, head h at h * kChunk
-        ResBufs rb;
     } b;
+    int32_t bk[kBkCap];           // a resolved head's kept boundary tokens
     double etbl[kExpTable];
     alignas(16) float qr[kMH][16];
     PickRec pick[kMH];
@@ -225,9 +225,11 @@ struct LayerLds {
     Pick2Rec pick2[kMH];
     uint32_t n2[kMH], k2b[kMH];  // level-2 kept rows of the block per head, their slot base
     uint32_t fka, fnc;           // a head's kept and candidate totals (its reducer)
+    uint32_t kt[kMH];            // both lists of a head
+    uint2 pd[kMH][kMH];          // the reducers' level-1 lists: [reducer][head] (idx slot, count)
     int bpre[kMH + 1];
     int hlast[kMH];
-    int flag, ticket;
+    int flag;
     uint32_t nkeep, nmove, j, cbefore, kmin, kmax;
     double abefore;
 };
@@ -522,12 +524,13 @@ __device__ __forceinline__ void scan_load(const LayerParams &P, int b, int g, in
     }
 }
 
-// Scores of the loaded rows for the G query heads (q_r from LDS): one
-// sequential fma chain per score over dimensions 0..15 from +0, a zero
-// result stored as +0 (bit-identical to rtp_index_scores).  The kTPT chains
-// of a head advance together, dimension by dimension, so consecutive fmas
-// are independent.  Tokens at or past the chunk's end score -inf.
-template <int G>
+// Scores of the loaded rows t < NT for the G query heads (q_r from LDS):
+// one sequential fma chain per score over dimensions 0..15 from +0
+// (bit-identical to rtp_index_scores; a chain from +0 never ends at -0, so
+// no sign fix-up is needed).  The NT chains of a head advance together,
+// dimension by dimension, so consecutive fmas are independent.  Tokens at
+// or past the chunk's end score -inf.
+template <int G, int NT>
 __device__ __forceinline__ void scan_scores(const float4 (&kv)[kTPT][4], int cn, const LayerLds &S,
                                             float (&sc)[kTPT][G])
 {
@@ -536,27 +539,93 @@ __device__ __forceinline__ void scan_scores(const float4 (&kv)[kTPT][4], int cn,
     for (int h = 0; h < G; ++h) {
         // (a compiler barrier: one head's chains in flight at a time)
         asm volatile("" ::: "memory");
-        float acc[kTPT];
+        float acc[NT];
 #pragma unroll
-        for (int t = 0; t < kTPT; ++t) acc[t] = 0.0f;
+        for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
             const float4 q = reinterpret_cast<const float4 *>(S.qr[h])[j4];
 #pragma unroll
-            for (int t = 0; t < kTPT; ++t) acc[t] = __builtin_fmaf(q.x, kv[t][j4].x, acc[t]);
+            for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(q.x, kv[t][j4].x, acc[t]);
 #pragma unroll
-            for (int t = 0; t < kTPT; ++t) acc[t] = __builtin_fmaf(q.y, kv[t][j4].y, acc[t]);
+            for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(q.y, kv[t][j4].y, acc[t]);
 #pragma unroll
-            for (int t = 0; t < kTPT; ++t) acc[t] = __builtin_fmaf(q.z, kv[t][j4].z, acc[t]);
+            for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(q.z, kv[t][j4].z, acc[t]);
 #pragma unroll
-            for (int t = 0; t < kTPT; ++t) acc[t] = __builtin_fmaf(q.w, kv[t][j4].w, acc[t]);
+            for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(q.w, kv[t][j4].w, acc[t]);
         }
 #pragma unroll
-        for (int t = 0; t < kTPT; ++t) {
-            const float a = (acc[t] == 0.0f) ? 0.0f : acc[t];
-            sc[t][h] = (t * kT + tid < cn) ? a : -INFINITY;
+        for (int t = 0; t < kTPT; ++t) sc[t][h] = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sc[t][h] = t * kT + tid < cn ? acc[t] : -INFINITY;
+    }
+}
+
+// The block's scores (token slots t < NT hold its tokens: NT = the chunk's
+// length over kT, rounded up), the optional score output, the block's max
+// and top bin per head, then its level-1 histogram (mass exp(s - m_b) in
+// fp64, bins counted down from the top bin) and every score's bin in LDS
+// (two 16-bit bins per word) for the classify.  The histogram has no
+// per-token branch: a token past the chunk's end adds +0 to the last bin,
+// so a head's exponentials run interleaved.
+template <int G, int NT>
+__device__ __forceinline__ void block_scan_hist(const LayerParams &P, int b, int g, int64_t c0,
+                                                int cn, const float4 (&kv)[kTPT][4], LayerLds &S)
+{
+    const int tid = threadIdx.x, w = tid / kWave;
+    float sc[kTPT][G];
+    scan_scores<G, NT>(kv, cn, S, sc);
+    if (P.scores) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float *sr = P.scores + ((int64_t)b * P.Hq_r + (int64_t)g * G + h) * P.N + c0;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (t * kT + tid < cn) sr[t * kT + tid] = sc[t][h];
         }
     }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) m = fmaxf(m, sc[t][h]);
+        m = wave_max(m);
+        if (lane_id() == 0) S.red[h][w] = m;
+    }
+    __syncthreads();
+    if (tid < G) {
+        float m = S.red[tid][0];
+        for (int i = 1; i < kNW; ++i) m = fmaxf(m, S.red[tid][i]);
+        S.mb[tid] = m;
+        S.Tb[tid] = score_bin(m);
+    }
+    __syncthreads();
+    uint32_t gw[G * kTPT / 2];
+#pragma unroll
+    for (int e = 0; e < G * kTPT / 2; ++e) gw[e] = 0u;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        asm volatile("" ::: "memory");
+        const double mbd = (double)S.mb[h];
+        const int Tb = S.Tb[h];
+        double ev[NT];
+        int jv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float s = sc[t][h];
+            const int gs = score_bin(s);
+            jv[t] = min(Tb - gs, kNB - 1);
+            ev[t] = exp_tang((double)s - mbd, S.etbl);
+            const int e = t * G + h;
+            gw[e >> 1] |= ((uint32_t)gs & 0xFFFFu) << (16 * (e & 1));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            atomicAdd(&S.a.h.hist[h][jv[t]], t * kT + tid < cn ? ev[t] : 0.0);
+    }
+#pragma unroll
+    for (int e = 0; e < G * kTPT / 2; ++e) S.b.gsw[e][tid] = gw[e];
+    __syncthreads();
 }
 
 // --------------------------------------------------------- level 1 merge
@@ -578,13 +647,14 @@ __device__ __forceinline__ void reduce_head(const LayerParams &P, int rg, int h,
     const int n = P.bpr;  // <= 256
     HistLds &H = S.a.h;
     const HistRec *in = P.ws.h1 + (int64_t)rg * P.bpr;
-    constexpr int kPer = 256 / (kT / kNB);  // records per thread
-    const int j = tid % kNB, part = tid / kNB;
-    double v[kPer];
+    // Wave w takes records w, w + 16, ...; lane l their bins l and l + 64.
+    constexpr int kPer = 256 / kNW;  // records per wave
+    double v0[kPer], v1[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-        const int b = part + k * (kT / kNB);
-        v[k] = b < n ? ld_agent(&in[b].mass[h][j]) : 0.0;
+        const int b = w + k * kNW;
+        v0[k] = b < n ? ld_agent(&in[b].mass[h][lane]) : 0.0;
+        v1[k] = b < n ? ld_agent(&in[b].mass[h][lane + kWave]) : 0.0;
     }
     float m = -INFINITY;
     int T = -32768;
@@ -594,7 +664,8 @@ __device__ __forceinline__ void reduce_head(const LayerParams &P, int rg, int h,
         H.rm[tid] = m;
         H.rT[tid] = T;
     }
-    H.hist[part][j] = 0.0;  // (the block's own histogram is published)
+    H.wrow[w][lane] = 0.0;
+    H.wrow[w][lane + kWave] = 0.0;
     m = wave_max(m);
     const float tw = wave_max((float)T);
     if (lane == 0) {
@@ -618,20 +689,26 @@ __device__ __forceinline__ void reduce_head(const LayerParams &P, int rg, int h,
         H.rf[tid] = exp_tang((double)H.rm[tid] - (double)H.M, S.etbl);
     }
     __syncthreads();
-    // Each of the 8 thread groups adds its records into a row of its own:
-    // the lanes of a wave shift by the same distance, so their bins differ.
+    // Each wave adds its records into a row of its own, record by record:
+    // the lanes shift by the same distance, so no two touch one bin, and
+    // the wave's LDS operations run in order (no atomics).
     double u = 0.0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-        const int b = part + k * (kT / kNB);
+        const int b = w + k * kNW;
         if (b < n) {
             const int o = H.ro[b];
-            const double val = v[k] * H.rf[b];
-            const int dst = j + o;
-            if (j < kNB - 1 && o >= 0 && dst < kNB - 1)
-                atomicAdd(&H.hist[part][dst], val);
+            const double f = H.rf[b];
+            const double a0 = v0[k] * f, a1 = v1[k] * f;
+            const int d0 = lane + o, d1 = lane + kWave + o;
+            if (o >= 0 && d0 < kNB - 1)
+                H.wrow[w][d0] += a0;
             else
-                u += val;
+                u += a0;
+            if (lane + kWave < kNB - 1 && o >= 0 && d1 < kNB - 1)
+                H.wrow[w][d1] += a1;
+            else
+                u += a1;
         }
     }
     const double ws = wave_sum(u);
@@ -640,7 +717,7 @@ __device__ __forceinline__ void reduce_head(const LayerParams &P, int rg, int h,
     if (tid < kNB) {
         double a = 0.0;
 #pragma unroll
-        for (int q = 0; q < kT / kNB; ++q) a += H.hist[q][tid];
+        for (int q = 0; q < kNW; ++q) a += H.wrow[q][tid];
         H.acc[tid] = a;
     }
     __syncthreads();
@@ -809,6 +886,7 @@ __device__ __forceinline__ void fine_head(const LayerParams &P, int rg, int h, L
         r.A2 = pk.A + before;
     }
     if (writer) {
+        S.pick2[h] = r;
         Pick2Rec *pr = P.ws.pick2 + (int64_t)rg * kMH + h;
         st_agent_i(&pr->j2, r.j2);
         st_agent_i(&pr->mode, r.mode);
@@ -1048,7 +1126,8 @@ __device__ __forceinline__ void classify(const LayerParams &P, int rg, int b, in
 }
 
 // The idx entries of the block's level-1 kept tokens, from its LDS lists
-// (coalesced; nothing in the launch reads them).
+// (coalesced, agent-scope: the blocks that attend a reducer's rows read
+// them).
 template <int G>
 __device__ __forceinline__ void level1_idx(const LayerParams &P, int b, int g, int64_t c0,
                                            LayerLds &S)
@@ -1060,7 +1139,7 @@ __device__ __forceinline__ void level1_idx(const LayerParams &P, int b, int g, i
         const uint32_t kb = S.kgb[h], kc = S.kc[h];
         for (uint32_t e = threadIdx.x; e < kc; e += kT) {
             const uint32_t slot = kb + e;
-            if (slot < (uint32_t)P.N) ir[slot] = (int32_t)(c0 + S.b.list[h * cmax + e]);
+            if (slot < (uint32_t)P.N) st_agent_i(ir + slot, (int32_t)(c0 + S.b.list[h * cmax + e]));
         }
     }
 }
@@ -1068,11 +1147,11 @@ __device__ __forceinline__ void level1_idx(const LayerParams &P, int b, int g, i
 // -------------------------------------------------------- own kept rows
 
 // Attends the block's listed rows of each head (head h: cnt[h] offsets in
-// the chunk at S.b.list[h * kChunk]), kBatch rows per wave batch, merged
-// into the waves' slots.
+// the chunk from S.b.list[h * kChunk + off[h]], off NULL for 0), kBatch
+// rows per wave batch, merged into the waves' slots.
 template <int G>
-__device__ __forceinline__ void gather_lists(const LayerParams &P, int b, int g, int64_t c0, const uint32_t *cnt,
-                             LayerLds &S)
+__device__ __forceinline__ void gather_lists(const LayerParams &P, int b, int g, int64_t c0,
+                                             const uint32_t *off, const uint32_t *cnt, LayerLds &S)
 {
     constexpr int cmax = kChunk;
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
@@ -1107,11 +1186,12 @@ __device__ __forceinline__ void gather_lists(const LayerParams &P, int b, int g,
         }
         const int base = (bi - S.bpre[h]) * kBatch;
         const int kc = (int)cnt[h];
+        const int lo = h * cmax + (off ? (int)off[h] : 0);
         int tok[kRU];
 #pragma unroll
         for (int u = 0; u < kRU; ++u) {
             const int e = base + lg + 4 * u;
-            tok[u] = e < kc ? (int)(c0 + S.b.list[h * cmax + e]) : -1;
+            tok[u] = e < kc ? (int)(c0 + S.b.list[lo + e]) : -1;
         }
         att_rows(Kb, Vb, qf, tok, P.N, a);
     }
@@ -1119,12 +1199,71 @@ __device__ __forceinline__ void gather_lists(const LayerParams &P, int b, int g,
     __syncthreads();
 }
 
+// The row's reducer blocks leave their level-1 rows to the others: block c
+// (c < r0, the blocks that reduce nothing) attends, for each head, its share
+// [c R / r0, (c + 1) R / r0) of the reducers' level-1 lists (R rows in all,
+// tokens read from idx).  Work items (head, batch of kBatch rows) go to the
+// waves in turn, so the heads' short shares run side by side.
+template <int G>
+__device__ __forceinline__ void gather_reducer_rows(const LayerParams &P, int b, int g, int c,
+                                                    int r0, int nr, LayerLds &S)
+{
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+    const int lg = lane >> 4, sub = lane & 15;
+    if (tid < G) {
+        uint32_t R = 0;
+        for (int q = 0; q < nr; ++q) R += S.pd[q][tid].y;
+        const uint32_t lo = (uint32_t)(((uint64_t)R * (uint32_t)c) / (uint32_t)r0);
+        const uint32_t hi = (uint32_t)(((uint64_t)R * (uint32_t)(c + 1)) / (uint32_t)r0);
+        S.kgb[tid] = lo;  // (the block's own slots are written: reused)
+        S.kt[tid] = hi - lo;
+    }
+    __syncthreads();
+    int nbat = 0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) nbat = max(nbat, ((int)S.kt[h] + kBatch - 1) / kBatch);
+    const int64_t kvb = ((int64_t)b * P.Hkv + g) * P.kv_cap * 128 + sub * 8;
+    for (int it = w; it < nbat * G; it += kNW) {
+        const int h = it % G, bi = it / G;
+        const int n = (int)S.kt[h];
+        if (bi * kBatch >= n) continue;
+        const int32_t *ir = P.idx + ((int64_t)b * P.Hq_r + (int64_t)g * G + h) * P.N;
+        float qf[8];
+        load_q8(P.q + ((int64_t)b * P.Hq + (int64_t)g * G + h) * 128 + sub * 8, P.qscale, qf);
+        int tok[kRU];
+#pragma unroll
+        for (int u = 0; u < kRU; ++u) {
+            const int e = bi * kBatch + lg + 4 * u;
+            tok[u] = -1;
+            if (e < n) {
+                uint32_t pos = S.kgb[h] + (uint32_t)e;
+                for (int q = 0; q < nr; ++q) {
+                    const uint2 d = S.pd[q][h];
+                    if (pos < d.y) {
+                        const uint32_t slot = d.x + pos;
+                        if (slot < (uint32_t)P.N) tok[u] = ld_agent_i(ir + slot);
+                        break;
+                    }
+                    pos -= d.y;
+                }
+            }
+        }
+        AttState a;
+        att_reset(a);
+        att_rows(P.K + kvb, P.V + kvb, qf, tok, P.N, a);
+        att_flush(a, w, h, S);
+    }
+    __syncthreads();
+}
+
 // The block's candidates that the level-2 threshold keeps: those above the
 // boundary digit (mode 0) or all of them (mode 1).  They are listed in LDS
-// (offsets in the chunk, head h at S.b.list[h * kChunk], S.n2[h] of them)
-// and written to the head's idx list after the ka tokens of level 1 (one
-// slot reservation per head and block).  Then the block counts itself on
-// p2_done: it reads no candidate of the row after this.
+// after the head's level-1 list (offsets in the chunk from
+// S.b.list[h * kChunk + S.kc[h]], S.n2[h] of them; both lists hold distinct
+// tokens of the chunk, so they fit) and written to the head's idx list after
+// the ka tokens of level 1 (one slot reservation per head and block).  Then
+// the block counts itself on p2_done: it reads no candidate of the row
+// after this.
 template <int G>
 __device__ __forceinline__ void level2_lists(const LayerParams &P, int rg, int b, int g, int64_t c0, LayerLds &S)
 {
@@ -1150,13 +1289,13 @@ __device__ __forceinline__ void level2_lists(const LayerParams &P, int rg, int b
                 keep = mode == 1 || fine_digit(key_score(c.x)) > j2;
                 off = c.y - (uint32_t)c0;
             }
-            const int64_t pos = wave_append(keep, &S.n2[h]);
-            if (pos >= 0 && pos < cmax) S.b.list[h * cmax + pos] = (uint16_t)off;
+            const int64_t pos = wave_append(keep, &S.n2[h]) + (int64_t)S.kc[h];
+            if (keep && pos < cmax) S.b.list[h * cmax + pos] = (uint16_t)off;
         }
     }
     __syncthreads();
     if (tid < G) {
-        S.n2[tid] = min(S.n2[tid], (uint32_t)cmax);
+        S.n2[tid] = min(S.n2[tid], (uint32_t)cmax - S.kc[tid]);
         S.k2b[tid] = S.n2[tid] ? ctr_add(&ctl.kept2[tid], S.n2[tid]) : 0u;
     }
     __syncthreads();
@@ -1164,9 +1303,10 @@ __device__ __forceinline__ void level2_lists(const LayerParams &P, int rg, int b
     for (int h = 0; h < G; ++h) {
         int32_t *ir = P.idx + ((int64_t)b * P.Hq_r + (int64_t)g * G + h) * P.N;
         const uint32_t base = S.pick2[h].ka + S.k2b[h];
+        const int lo = h * cmax + (int)S.kc[h];
         for (uint32_t e = tid; e < S.n2[h]; e += kT) {
             const uint32_t slot = base + e;
-            if (slot < (uint32_t)P.N) ir[slot] = (int32_t)(c0 + S.b.list[h * cmax + e]);
+            if (slot < (uint32_t)P.N) ir[slot] = (int32_t)(c0 + S.b.list[lo + e]);
         }
     }
     if (tid == 0) ctr_arrive(&ctl.p2_done);
@@ -1208,7 +1348,7 @@ __device__ __forceinline__ void keep_tok(bool pred, uint32_t tok, int32_t *ir, u
     const uint64_t below = lane == 0 ? 0ull : (mask & (~0ull >> (64 - lane)));
     const uint32_t pos = base + (uint32_t)__popcll(below);
     if (pos < cap) ir[pos] = (int32_t)tok;
-    if (pos < (uint32_t)kBkCap) S.b.rb.bk[pos] = (int32_t)tok;
+    if (pos < (uint32_t)kBkCap) S.bk[pos] = (int32_t)tok;
 }
 
 // Reserves LDS slots in dst for survivors (one LDS atomic per wave).
@@ -1332,23 +1472,50 @@ __device__ __forceinline__ void resolve_set(const LayerParams &P, int rg, int h,
     int64_t n = (int64_t)min(q.nc, (uint32_t)N);
     if (q.mode == 0) {
         const int j2 = q.j2;
-        const bool to_lds = q.cstar <= (uint32_t)kResCap;
-        if (!to_lds) {
+        if (q.cstar <= (uint32_t)kResCap) {
+            // The boundary digit's candidates into LDS, kU loads in flight
+            // per thread; masses for those only.
+            if (tid == 0) S.nmove = 0;
+            __syncthreads();
+            constexpr int kU = 8;
+            for (int64_t k0 = 0; k0 < n; k0 += (int64_t)kU * kT) {
+                uint2 e[kU];
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int64_t k = k0 + u * kT + tid;
+                    e[u] = k < n ? ld_cand2(gc + k) : make_uint2(0u, 0u);
+                }
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int64_t k = k0 + u * kT + tid;
+                    const float sv = key_score(e[u].x);
+                    const bool ok = k < n && fine_digit(sv) == j2;
+                    Cand c;
+                    c.key = e[u].x;
+                    c.idx = e[u].y;
+                    c.e = ok ? exp_tang((double)sv - M, S.etbl) : 0.0;
+                    move_cand(ok, c, S.a.r.buf[0], S);
+                }
+            }
+            __syncthreads();
+            n = (int64_t)min(S.nmove, (uint32_t)kResCap);
+            cs.lds = S.a.r.buf[0];
+        } else {
+            // In place in the candidate list, once no block reads it.
             if (tid == 0)
                 wait_level(&P.ws.ctl[rg].p2_done, (uint32_t)P.bpr, P.spin_limit, P.status);
             __syncthreads();
+            n = filter_pass(
+                cs, n, [=](const Cand &x) { return fine_digit(key_score(x.key)) == j2 ? 2 : 0; },
+                false, nullptr, gc, M, ir, cap, S);
         }
-        n = filter_pass(
-            cs, n, [=](const Cand &x) { return fine_digit(key_score(x.key)) == j2 ? 2 : 0; },
-            to_lds, S.b.rb.buf[0], gc, M, ir, cap, S);
-        if (to_lds) cs.lds = S.b.rb.buf[0];
     }
     n = min(n, (int64_t)cap);
     for (int level = 0; level < 8 && n > 0; ++level) {
         if (!cs.lds && n <= kResCap) {
-            for (int64_t k = tid; k < n; k += kT) S.b.rb.buf[0][k] = cs.get(k, M, S.etbl);
+            for (int64_t k = tid; k < n; k += kT) S.a.r.buf[0][k] = cs.get(k, M, S.etbl);
             __syncthreads();
-            cs.lds = S.b.rb.buf[0];
+            cs.lds = S.a.r.buf[0];
             cur = 0;
         }
         if (cs.lds && n <= kWave) {
@@ -1431,12 +1598,12 @@ __device__ __forceinline__ void resolve_set(const LayerParams &P, int rg, int h,
                     return d < D ? 1 : (d == D ? (take_all ? 1 : 2) : 0);
                 };
                 const bool to_lds = cs.lds || ns <= kResCap;
-                Cand *dst = cs.lds ? S.b.rb.buf[cur ^ 1] : S.b.rb.buf[0];
+                Cand *dst = cs.lds ? S.a.r.buf[cur ^ 1] : S.a.r.buf[0];
                 n = filter_pass(cs, n, cls, to_lds, dst, gc, M, ir, cap, S);
                 if (take_all) return;
                 if (to_lds) {
                     cur = cs.lds ? (cur ^ 1) : 0;
-                    cs.lds = S.b.rb.buf[cur];
+                    cs.lds = S.a.r.buf[cur];
                 }
             }
             // Indices are distinct: one token remains, and it is needed.
@@ -1510,11 +1677,11 @@ __device__ __forceinline__ void resolve_set(const LayerParams &P, int rg, int h,
             return d > D ? 1 : (d == D ? 2 : 0);
         };
         const bool to_lds = cs.lds || ns <= kResCap;
-        Cand *dst = cs.lds ? S.b.rb.buf[cur ^ 1] : S.b.rb.buf[0];
+        Cand *dst = cs.lds ? S.a.r.buf[cur ^ 1] : S.a.r.buf[0];
         n = filter_pass(cs, n, cls, to_lds, dst, gc, M, ir, cap, S);
         if (to_lds) {
             cur = cs.lds ? (cur ^ 1) : 0;
-            cs.lds = S.b.rb.buf[cur];
+            cs.lds = S.a.r.buf[cur];
         }
     }
 }
@@ -1552,7 +1719,7 @@ __device__ __forceinline__ void resolve_head(const LayerParams &P, int rg, int b
 #pragma unroll
         for (int u = 0; u < kRU; ++u) {
             const int64_t e = e0 + lg + 4 * u;
-            tok[u] = e < kb ? (e < kBkCap ? S.b.rb.bk[e] : ld_agent_i(ir + e)) : -1;
+            tok[u] = e < kb ? (e < kBkCap ? S.bk[e] : ld_agent_i(ir + e)) : -1;
         }
         att_rows(P.K + kvb, P.V + kvb, qf, tok, P.N, a);
         any = true;
@@ -1577,7 +1744,6 @@ template <int G>
 __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
 {
     __shared__ LayerLds S;
-    constexpr int TPT = kTPT;
     const int tid = threadIdx.x;
     const int blk = blockIdx.x;
     const int rg = blk / P.bpr, c = blk - rg * P.bpr;
@@ -1597,67 +1763,12 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
     if (tid < kExpTable) S.etbl[tid] = kLayerExpTbl[tid];
     if (tid < G * 16) S.qr[tid / 16][tid % 16] = P.q_r[((int64_t)b * P.Hq_r + g * G) * 16 + tid];
     __syncthreads();
-    float sc[TPT][G];
-    scan_scores<G>(kv, cn, S, sc);
-    if (P.scores) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float *sr = P.scores + ((int64_t)b * P.Hq_r + (int64_t)g * G + h) * P.N + c0;
-#pragma unroll
-            for (int t = 0; t < TPT; ++t)
-                if (t * kT + tid < cn) sr[t * kT + tid] = sc[t][h];
-        }
+    switch ((cn + kT - 1) / kT) {
+    case 1: block_scan_hist<G, 1>(P, b, g, c0, cn, kv, S); break;
+    case 2: block_scan_hist<G, 2>(P, b, g, c0, cn, kv, S); break;
+    case 3: block_scan_hist<G, 3>(P, b, g, c0, cn, kv, S); break;
+    default: block_scan_hist<G, 4>(P, b, g, c0, cn, kv, S); break;
     }
-    const int w = tid / kWave;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < TPT; ++t) m = fmaxf(m, sc[t][h]);
-        m = wave_max(m);
-        if (lane_id() == 0) S.red[h][w] = m;
-    }
-    __syncthreads();
-    if (tid < G) {
-        float m = S.red[tid][0];
-        for (int i = 1; i < kNW; ++i) m = fmaxf(m, S.red[tid][i]);
-        S.mb[tid] = m;
-        S.Tb[tid] = score_bin(m);
-    }
-    __syncthreads();
-
-    // ---- level 1: the block's histogram (mass exp(s - m_b) in fp64); each
-    // score's bin is kept in LDS (two 16-bit bins per word) for the classify.
-    // No branches: a token past the chunk's end adds +0 to the last bin, so
-    // the kTPT exponentials of a head run interleaved.
-    {
-        uint32_t gw[G * kTPT / 2];
-#pragma unroll
-        for (int e = 0; e < G * kTPT / 2; ++e) gw[e] = 0u;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            asm volatile("" ::: "memory");
-            const double mbd = (double)S.mb[h];
-            const int Tb = S.Tb[h];
-            double ev[kTPT];
-            int jv[kTPT];
-#pragma unroll
-            for (int t = 0; t < TPT; ++t) {
-                const float s = sc[t][h];
-                const int gs = score_bin(s);
-                jv[t] = min(Tb - gs, kNB - 1);
-                ev[t] = exp_tang((double)s - mbd, S.etbl);
-                const int e = t * G + h;
-                gw[e >> 1] |= ((uint32_t)gs & 0xFFFFu) << (16 * (e & 1));
-            }
-#pragma unroll
-            for (int t = 0; t < TPT; ++t)
-                atomicAdd(&S.a.h.hist[h][jv[t]], t * kT + tid < cn ? ev[t] : 0.0);
-        }
-#pragma unroll
-        for (int e = 0; e < G * kTPT / 2; ++e) S.b.gsw[e][tid] = gw[e];
-    }
-    __syncthreads();
     {
         HistRec *hr = P.ws.h1 + blk;
         const int hh = tid / kNB, j = tid % kNB;
@@ -1714,9 +1825,12 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
     __syncthreads();
     classify<G>(P, rg, b, g, c0, cn, S);
     if (tid == 0) ctr_arrive(&ctl.classified);
+    level1_idx<G>(P, b, g, c0, S);
 
-    // ---- the heads' level-2 thresholds, by the same blocks as level 1
-    if (c >= r0) {
+    // ---- the heads' level-2 thresholds, by the same blocks as level 1; the
+    // other blocks attend their level-1 rows meanwhile
+    const bool picker = c >= r0;
+    if (picker) {
         if (tid == 0) wait_level(&ctl.classified, (uint32_t)P.bpr, P.spin_limit, P.status);
         __syncthreads();
         uint32_t nh = 0;
@@ -1725,15 +1839,25 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
             __syncthreads();
             ++nh;
         }
+        if (r0 > 0 && tid < G) {
+            uint2 *pd = P.ws.pdesc + ((int64_t)rg * kMH + (c - r0)) * kMH + tid;
+            st_cand2(pd, make_uint2(S.kgb[tid], S.kc[tid]));
+        }
         wait_vmem();
         __syncthreads();
         if (tid == 0) ctr_add(&ctl.pick2_ready, nh);
+        // Its heads' boundary digits right away, unless a digit holds more
+        // candidates than LDS takes (then they are compacted in place, after
+        // every block has read the list).
+        for (int h = c - r0; h < G; h += nr)
+            if (!(S.pick2[h].mode == 0 && S.pick2[h].cstar > (uint32_t)kResCap))
+                resolve_head<G>(P, rg, b, g, h, S);
+    } else {
+        slots_clear(S);
+        gather_lists<G>(P, b, g, c0, nullptr, S.kc, S);
     }
 
-    // ---- the block's rows kept by level 1, then those kept by level 2
-    level1_idx<G>(P, b, g, c0, S);
-    slots_clear(S);
-    gather_lists<G>(P, b, g, c0, S.kc, S);
+    // ---- the block's level-2 rows
     if (tid == 0) wait_level(&ctl.pick2_ready, (uint32_t)G, P.spin_limit, P.status);
     __syncthreads();
     if (tid < G) {
@@ -1748,10 +1872,30 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
         r.A2 = ld_agent(&pr->A2);
         S.pick2[tid] = r;
     }
+    if (!picker && tid < nr * G) {
+        const int q = tid / G, h = tid % G;
+        S.pd[q][h] = ld_cand2(P.ws.pdesc + ((int64_t)rg * kMH + q) * kMH + h);
+    }
     __syncthreads();
     level2_lists<G>(P, rg, b, g, c0, S);
     if (tid == 0) fin_arrive<G>(P, ctl);
-    gather_lists<G>(P, b, g, c0, S.n2, S);
+    if (picker) {
+        // The boundary digits left, then the block's level-2 rows (its
+        // level-1 rows go to the other blocks; with none, both lists).
+        for (int h = c - r0; h < G; h += nr)
+            if (S.pick2[h].mode == 0 && S.pick2[h].cstar > (uint32_t)kResCap)
+                resolve_head<G>(P, rg, b, g, h, S);
+        slots_clear(S);
+        if (r0 > 0) {
+            gather_lists<G>(P, b, g, c0, S.kc, S.n2, S);
+        } else {
+            if (tid < G) S.kt[tid] = S.kc[tid] + S.n2[tid];
+            gather_lists<G>(P, b, g, c0, nullptr, S.kt, S);
+        }
+    } else {
+        gather_lists<G>(P, b, g, c0, S.kc, S.n2, S);
+        gather_reducer_rows<G>(P, b, g, c, r0, nr, S);
+    }
     slots_to_partial(G, P.ws.att1 + (int64_t)blk * kMH * kPF, kPF, S);
     if (arrive_last_blk(P.ws.att_grp + (int64_t)rg * P.ngrp + grp, (uint32_t)ngs, S)) {
         float *gp = P.ws.att2 + ((int64_t)rg * (P.ngrp + 1) + grp) * kMH * kPF;
@@ -1772,21 +1916,6 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
                           (int64_t)kMH * kPF, P.ngrp + 1, G, hm, nullptr,
                           P.out + ((int64_t)b * P.Hq + (int64_t)g * G) * 128);
         }
-        __syncthreads();
-    }
-
-    // ---- final candidate sets: claimed by blocks as they finish
-    for (;;) {
-        if (tid == 0) {
-            const uint32_t t = ctr_add(&ctl.claim, 1u);
-            if (t == (uint32_t)(G + P.bpr - 1)) ctr_reset(&ctl.claim);
-            S.ticket = (int)t;
-        }
-        __syncthreads();
-        const int ticket = S.ticket;
-        __syncthreads();
-        if (ticket >= G) break;
-        resolve_head<G>(P, rg, b, g, ticket, S);
     }
 }
 
@@ -1847,6 +1976,7 @@ static size_t layer_ws_layout(const LayerGeom &L, int B, int N, LayerWs *W, void
     const size_t a2 = take((size_t)L.RG * (L.ngrp + 1) * kMH * kPF * sizeof(float));
     const size_t lo = take((size_t)(L.NI > 0 ? L.NI : 1) * kMH * kPF * sizeof(float));
     const size_t cd = take((size_t)L.RG * L.G * N * sizeof(uint2));
+    const size_t pd = take((size_t)L.RG * kMH * kMH * sizeof(uint2));
     if (W) {
         char *p = static_cast<char *>(base);
         W->h1 = reinterpret_cast<HistRec *>(p + h1);
@@ -1859,6 +1989,7 @@ static size_t layer_ws_layout(const LayerGeom &L, int B, int N, LayerWs *W, void
         W->att2 = reinterpret_cast<float *>(p + a2);
         W->loc = reinterpret_cast<float *>(p + lo);
         W->cand = reinterpret_cast<uint2 *>(p + cd);
+        W->pdesc = reinterpret_cast<uint2 *>(p + pd);
     }
     return off;
 }
