@@ -5,8 +5,8 @@ CPU-baseline leg are the only users.  The product library never imports it.
 
 This module is argument marshalling around ``oracle.c`` (plain C, fp32 scores
 by a fixed fmaf chain, fp64 masses and attention; see the header of that file
-for the definition each function follows) plus ``decode_layer``, which applies
-those definitions to every head of one decode layer.
+for the definition each function follows).  Tests apply these per-head
+definitions to every head of a decode layer themselves.
 """
 from __future__ import annotations
 

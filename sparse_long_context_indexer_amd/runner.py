@@ -116,6 +116,9 @@ class DecodeLayer:
                              scores=self.scores)
             return
         if self.mode == "scan_local" and self.H_r > 0 and self.H_l > 0:
+            if k_r.dtype != torch.float32:
+                raise ValueError("mode 'scan_local' takes an fp32 indexer key cache "
+                                 "(rtp_scan_local has no bf16 key path)")
             rtp_scan_local(q_r, k_r, self.scores, q, K, V, self.N, self.H_r, self.H_l,
                            self.n_sink, self.window, scale, out, self.ws_local)
             rtp_topp_select(self.scores, p, self.idx, self.count, self.ws_sel)

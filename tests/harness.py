@@ -84,6 +84,9 @@ class SetVerdict:
     bad: list             # tokens in the difference that are not exempt
     mass: float
     note: str = ""
+    oracle_sel: np.ndarray = None  # the oracle's own set
+
+
 
 
 def judge_set(s: np.ndarray, p: float, gpu_set: np.ndarray) -> SetVerdict:
@@ -105,7 +108,7 @@ def judge_set(s: np.ndarray, p: float, gpu_set: np.ndarray) -> SetVerdict:
     pf = float(np.float32(p))
     ok = not dup and not out_of_range and not bad and mass >= pf - MASS_SLACK
     note = ("duplicates " if dup else "") + ("out-of-range " if out_of_range else "")
-    return SetVerdict(ok, len(g), ref.k, exempt, bad, mass, note)
+    return SetVerdict(ok, len(g), ref.k, exempt, bad, mass, note, ref.sel)
 
 
 def judge_out(gpu: np.ndarray, ref: np.ndarray):
@@ -154,6 +157,11 @@ def check_layer(L: Layer, p: float, res: dict, heads=None, report=None):
     rep = report if report is not None else {}
     rep.setdefault("exempt", 0)
     rep.setdefault("k", [])
+    # Heads whose set differs from the oracle's (by exempt tokens only):
+    # (b, h, abs, rel) of the output against the oracle's end-to-end output
+    # over its own set.  Reported, not judged: the bound applies on the
+    # GPU's set (the boundary rule).
+    rep.setdefault("e2e_gap", [])
     for b in range(cfg.B):
         for h in range(cfg.H_r):
             if heads is not None and h not in heads:
@@ -182,6 +190,12 @@ def check_layer(L: Layer, p: float, res: dict, heads=None, report=None):
             ok, err, rel = judge_out(res["out"][b, h], ref)
             if not ok:
                 fails.append(f"sparse out b={b} h={h}: abs={err:.3e} rel={rel:.3e}")
+            if v.exempt:
+                orows = np.sort(v.oracle_sel)
+                e2e = oracle.attention(L.q[b, h], L.kv_rows("K", b, kv, orows),
+                                       L.kv_rows("V", b, kv, orows), cfg.scale)
+                _, err2, rel2 = judge_out(res["out"][b, h], e2e)
+                rep["e2e_gap"].append((b, h, err2, rel2))
         for h in range(cfg.H_r, cfg.Hq):
             if heads is not None and h not in heads:
                 continue

@@ -274,9 +274,29 @@ def test_layer_with_bf16_key_cache():
             assert np.array_equal(sc[b, h].view(np.uint32), want.view(np.uint32)), (b, h)
             v = judge_set(want, 0.9, ix[b, h, :c[b, h]])
             assert v.ok, (b, h, v.k_gpu, v.k_oracle)
+    # The outputs: sparse heads against the oracle's attention over the
+    # GPU's set, local heads over the sinks and window.
+    got = out.cpu().numpy()
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            kv = h // cfg.G
+            if h < cfg.H_r:
+                rows = np.sort(ix[b, h, :c[b, h]])
+            else:
+                rows = oracle.local_rows(cfg.N, cfg.n_sink, cfg.window)
+            ref = oracle.attention(L.q[b, h], L.kv_rows("K", b, kv, rows),
+                                   L.kv_rows("V", b, kv, rows), cfg.scale)
+            ok, err, rel = judge_out(got[b, h], ref)
+            assert ok, (b, h, err, rel)
+    # scan_local has no bf16 key path: the runner says so instead of
+    # reading the keys as fp32.
+    sl = DecodeLayer(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.H_r, cfg.n_sink, cfg.window, dev(),
+                     mode="scan_local")
+    with pytest.raises(ValueError, match="fp32"):
+        sl(L.d["q_r"], torch.from_numpy(kb.view(np.int16)).to(dev()), L.d["q"], L.d["K"],
+           L.d["V"], 0.9, cfg.scale, out)
 
 
-# ----------------------------------------------------------------- prefill
 # ----------------------------------------------------------------- prefill
 
 @pytest.mark.parametrize("T,n_sink,window,hb,nh", [
@@ -309,6 +329,41 @@ def test_prefill_attend_against_oracle(T, n_sink, window, hb, nh):
                 assert ok, (b, h, t, err, rel)
         outside = [h for h in range(Hq) if not hb <= h < hb + nh]
         assert np.all(np.isnan(got[b, outside]))
+
+
+def test_prefill_attend_benched_size():
+    # The size the benchmark times: a 16384-token prompt, 32 query heads on
+    # 4 KV heads, heads 0-7 dense and heads 8-31 on 4 sinks + a 4096-token
+    # window, one launch each.  Sampled queries (the first ones, both sides
+    # of the window edge, random ones, the last ones) against the oracle.
+    B, Hq, Hkv, T = 1, 32, 4, 16384
+    H_r, n_sink, window = 8, 4, 4096
+    cap = T + 3
+    q = synth.normal_bf16(synth.key(86, 1), 0, B * Hq * T * 128).reshape(B, Hq, T, 128)
+    K = synth.normal_bf16(synth.key(86, 2), 0, B * Hkv * cap * 128).reshape(B, Hkv, cap, 128)
+    V = synth.normal_bf16(synth.key(86, 3), 0, B * Hkv * cap * 128).reshape(B, Hkv, cap, 128)
+    scale = 1.0 / math.sqrt(128.0)
+    out = torch.full((B, Hq, T, 128), float("nan"), dtype=torch.float32, device=dev())
+    qd = torch.from_numpy(q.view(np.int16)).to(dev())
+    Kd = torch.from_numpy(K.view(np.int16)).to(dev())
+    Vd = torch.from_numpy(V.view(np.int16)).to(dev())
+    rtp.rtp_prefill_attend(qd, Kd, Vd, 0, H_r, 0, 0, scale, out)
+    rtp.rtp_prefill_attend(qd, Kd, Vd, H_r, Hq - H_r, n_sink, window, scale, out)
+    rng = np.random.default_rng(16384)
+    ts = np.unique(np.concatenate([np.arange(5), np.arange(window - 3, window + 3),
+                                   rng.integers(0, T, 8), np.arange(T - 4, T)]))
+    heads = [0, 3, 7, 8, 19, 31]
+    got = out[:, heads][:, :, torch.from_numpy(ts).to(dev())].cpu().numpy()
+    assert not torch.isnan(out).any().item()
+    del out
+    for b in range(B):
+        for hi, h in enumerate(heads):
+            for ti, t in enumerate(ts):
+                rows = (np.arange(t + 1) if h < H_r
+                        else oracle.local_rows(t + 1, n_sink, window))
+                ref = oracle.attention(q[b, h, t], K[b, h // 8, rows], V[b, h // 8, rows], scale)
+                ok, err, rel = judge_out(got[b, hi, ti], ref)
+                assert ok, (b, h, t, err, rel)
 
 
 # -------------------------------------------------------------- projection
@@ -718,16 +773,20 @@ def test_graph_replays_match_eager(mode):
         assert all(np.array_equal(a_, b_) for a_, b_ in zip(got[4], ref[4])), rep
         assert np.array_equal(got[5], ref[5]), rep
         assert np.allclose(got[0], ref[0], rtol=1e-5, atol=1e-6), rep
-        # eager work between replays: a selection on other scores in the
-        # same workspace
+        # eager work between replays: a selection on other scores (another
+        # shape) in the graph's own select workspace, judged against the
+        # oracle; the next replay must not care
         other.normal_()
-        _select(other.cpu().numpy(), 0.9)
-        rtp.rtp_topp_select(other, 0.5, torch.empty((2, 3, 50_000), dtype=torch.int32,
-                                                    device=dev()),
-                            torch.empty((2, 3), dtype=torch.int32, device=dev()),
-                            torch.empty(rtp.workspace_size(rtp.RTP_WS_TOPP_SELECT, 2, 3, 50_000),
-                                        dtype=torch.uint8, device=dev()))
+        o_np = other.cpu().numpy()
+        e_idx = torch.full((2, 3, 50_000), -7, dtype=torch.int32, device=dev())
+        e_cnt = torch.full((2, 3), -7, dtype=torch.int32, device=dev())
+        rtp.rtp_topp_select(other, 0.5, e_idx, e_cnt, step.ws_sel)
         torch.cuda.synchronize()
+        ec, eix = e_cnt.cpu().numpy(), e_idx.cpu().numpy()
+        for b in range(2):
+            for h in range(3):
+                v = judge_set(o_np[b, h], 0.5, eix[b, h, :ec[b, h]])
+                assert v.ok, (rep, b, h, v.k_gpu, v.k_oracle, v.bad[:5], v.note)
 
 
 # ------------------------------------------------------------ workspaces

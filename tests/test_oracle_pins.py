@@ -180,6 +180,33 @@ def test_topp_nested_in_p_and_mass_bounds():
             assert np.all(ss[:-1] >= ss[1:])
 
 
+def test_set_mass_closed_forms():
+    # Scores [1, 0]: mass({0}) = e / (e + 1) = 1 / (1 + e^-1), and the other
+    # token takes the rest.
+    s = np.array([1.0, 0.0], dtype=np.float32)
+    assert abs(oracle.set_mass(s, [0]) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    assert abs(oracle.set_mass(s, [1]) - 1.0 / (1.0 + math.e)) < 1e-15
+    # A row of N equal scores: any k of them hold k / N, whatever the value.
+    for val in (-3.5, 0.0, 40.0):
+        t = np.full(1000, val, dtype=np.float32)
+        for k in (1, 7, 500, 1000):
+            assert abs(oracle.set_mass(t, np.arange(k) * (1000 // k)) - k / 1000.0) < 1e-13
+    # Scores a + ln w_i for integer weights: mass(S) = sum_S w / sum w; the
+    # shift a is exact in fp32 and must cancel.
+    w = np.array([1, 2, 3, 4, 6], dtype=np.float64)
+    for a in (0.0, -20.0, 30.0):
+        sw = (a + np.log(w)).astype(np.float32)
+        # the fp32 rounding of each score moves its weight by < 2^-23 relative
+        ws = np.exp(sw.astype(np.float64) - float(np.max(sw)))
+        for members in ([0], [4], [1, 3], [0, 1, 2, 3, 4]):
+            want = ws[members].sum() / ws.sum()
+            assert abs(oracle.set_mass(sw, members) - want) < 1e-14
+            approx = w[members].sum() / w.sum()
+            assert abs(oracle.set_mass(sw, members) - approx) < 1e-6
+    # The empty set holds nothing.
+    assert oracle.set_mass(s, np.zeros(0, dtype=np.int64)) == 0.0
+
+
 def test_topp_p_one_selects_all():
     s = np.random.default_rng(3).standard_normal(1000).astype(np.float32)
     r = oracle.topp(s, 1.0)
