@@ -276,7 +276,7 @@ def main():
         del K_all, V_all, kr_all, qr_all, q_all, out_all, ws_layer, step_layer
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        rec["configs"] = [r for ci in (1, 2, 3) for r in config_records(ci, dev, stream)]
+        rec["configs"] = [r for ci in (0, 1, 2, 3) for r in config_records(ci, dev, stream)]
     print(json.dumps(rec), flush=True)
 
     if args.calib_copy:
@@ -407,7 +407,9 @@ def config_records(ci, dev, stream, reps=10):
     over R input replicas at distinct addresses (R * B_alg >= 1 GiB, so the
     caches hold none of a step's inputs: cold), and on one replica (hot);
     kept-set sizes and unions; boundary exemptions and output errors against
-    the oracle."""
+    the oracle; and the oracle's own time for the whole step (every head:
+    scores, full-sort top-p and fp64 attention over its set; local heads
+    over sinks + window), single-threaded, oracle calls only."""
     import torch
     import oracle
     import synth
@@ -483,6 +485,21 @@ def config_records(ci, dev, stream, reps=10):
                                                                        V[b, g, rows], cfg.scale))
                 bad += 0 if ok else 1
                 err, rel = max(err, e_abs), max(rel, e_rel)
+        # The oracle's whole step, timed.
+        t_or = 0.0
+        for b in range(B):
+            for h in range(Hq):
+                g = h // cfg.G
+                t = time.perf_counter()
+                if h < H_r:
+                    sel = oracle.topp(oracle.scores(q_r[b, h], k_r[b, g]), p).sel
+                t_or += time.perf_counter() - t
+                rows = (np.sort(sel) if h < H_r
+                        else oracle.local_rows(N, cfg.n_sink, cfg.window))
+                Kr, Vr = K[b, g, rows], V[b, g, rows]
+                t = time.perf_counter()
+                oracle.attention(q[b, h], Kr, Vr, cfg.scale)
+                t_or += time.perf_counter() - t
         ns = np.array(n_sel[0]).reshape(B, H_r)
         rec = {"workload": cfg.name, "p": p, "batch": B, "ctx_tokens": N,
                "steps_per_s": round(1e3 / ms_cold, 1), "ms_per_step": round(ms_cold, 5),
@@ -492,7 +509,8 @@ def config_records(ci, dev, stream, reps=10):
                "frac_of_hbm_peak": round(B_alg / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                "n_S_per_row_head": ns.tolist(), "union_rows": union[0],
                "exempt_tokens": exempt, "parity_failures": bad,
-               "max_abs_err": err, "max_rel_err": rel}
+               "max_abs_err": err, "max_rel_err": rel,
+               "oracle_s_per_step": round(t_or, 4), "oracle_threads": 1}
         log(f"config {ci} p={p}: {ms_cold * 1e3:.1f} us/step cold ({R} replicas), "
             f"{ms_hot * 1e3:.1f} hot, {rec['GBps']} GB/s, union {union[0]}, exempt {exempt}, "
             f"failures {bad}")
@@ -554,7 +572,10 @@ def cpu_baseline(cfg, p, target_s):
     return {"value": round(layers / cfg.L / spent, 5), "unit": "steps/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{layers} of {cfg.L} layers of {cfg.name} (all 32 heads), "
-                      f"{spent:.1f}s single-threaded; value = layers/{cfg.L}/seconds"}
+                      f"{spent:.1f}s single-threaded; value = layers/{cfg.L}/seconds"
+                      + (" (extrapolated from the layers timed)" if layers < cfg.L
+                         else " (the whole step timed)"),
+            "layers_timed": layers, "extrapolated": layers < cfg.L}
 
 
 if __name__ == "__main__":

@@ -25,9 +25,10 @@
 //            realigns them to the row's top bin, rescales them to the row
 //            max, and picks the head's boundary bin J* and the mass A above
 //            it.
-//   local    meanwhile the other blocks run the local heads: 256-row tiles
+//   local    meanwhile the other blocks run the local heads: 64-row tiles
 //            of the sink + window rows, every K/V row read once for the G
-//            query heads of its KV head.
+//            query heads of its KV head.  When the rows leave compute units
+//            free, extra blocks there take the local tiles instead.
 //   classify every block waits for its row's thresholds (a wait on blocks
 //            that may come later: it relies on the launch's blocks being
 //            resident together, which the host ensures by launching at most
@@ -152,6 +153,7 @@ struct LayerParams {
     int B, Hq, Hkv, N, Hq_r, Hkv_r;
     int bpr, C, ngrp;
     int n_lkv, nlt, NI, nl_rows, sink_end, w0;
+    int NBr, NX;  // row blocks (the grid's first), then blocks for local items only
     int keep_all;
     double pd;
     float qscale;
@@ -1746,6 +1748,11 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
     __shared__ LayerLds S;
     const int tid = threadIdx.x;
     const int blk = blockIdx.x;
+    if (blk >= P.NBr) {
+        // A block beyond the rows: local heads only (no wait on any block).
+        for (int item = blk - P.NBr; item < P.NI; item += P.NX) local_item<G>(P, item, S);
+        return;
+    }
     const int rg = blk / P.bpr, c = blk - rg * P.bpr;
     const int b = rg / P.Hkv_r, g = rg - b * P.Hkv_r;
     const int grp = c / kGS;
@@ -1800,13 +1807,14 @@ __global__ __launch_bounds__(kT) void layer_kernel(LayerParams P)
     }
 
     // ---- local heads while the thresholds are found (blocks that reduce
-    // nothing, when there are any)
-    const int nlb = (int)(gridDim.x / P.bpr) * r0;
-    if (nlb > 0) {
+    // nothing, when there are any), unless blocks beyond the rows take them
+    const int nlb = (P.NBr / P.bpr) * r0;
+    if (P.NX > 0) {
+    } else if (nlb > 0) {
         if (c < r0)
             for (int item = rg * r0 + c; item < P.NI; item += nlb) local_item<G>(P, item, S);
     } else {
-        for (int item = blk; item < P.NI; item += (int)gridDim.x) local_item<G>(P, item, S);
+        for (int item = blk; item < P.NI; item += P.NBr) local_item<G>(P, item, S);
     }
 
     if (tid == 0) wait_level(&ctl.pick_ready, (uint32_t)G, P.spin_limit, P.status);
@@ -1954,6 +1962,8 @@ LayerGeom layer_geom(int cus, int B, int Hq, int Hkv, int N, int Hq_r, int n_sin
     L.nl_rows = (int)(sink_end + (N - w0));
     L.nlt = (L.nl_rows + kTile - 1) / kTile;
     L.NI = L.n_lkv > 0 ? B * L.n_lkv * L.nlt : 0;
+    L.NX = L.NI > 0 ? min(cus - L.NB, L.NI) : 0;
+    if (L.NX < 0) L.NX = 0;
     L.ok = true;
     return L;
 }
@@ -2030,6 +2040,8 @@ hipError_t launch_decode_layer(const LayerGeom &L, const float *q_r, const float
     P.n_lkv = L.n_lkv;
     P.nlt = L.nlt;
     P.NI = L.NI;
+    P.NBr = L.NB;
+    P.NX = L.NX;
     P.nl_rows = L.nl_rows;
     P.sink_end = L.sink_end;
     P.w0 = L.w0;
@@ -2039,7 +2051,7 @@ hipError_t launch_decode_layer(const LayerGeom &L, const float *q_r, const float
     P.spin_limit = spin_limit;
     P.status = status;
     layer_ws_layout(L, B, N, &P.ws, ws);
-    const dim3 grid((unsigned)L.NB), block(kT);
+    const dim3 grid((unsigned)(L.NB + L.NX)), block(kT);
     switch (L.G) {
     case 1: return launch(layer_kernel<1>, grid, block, 0, stream, P);
     case 2: return launch(layer_kernel<2>, grid, block, 0, stream, P);

@@ -123,6 +123,7 @@ struct LayerGeom {
     int n_lkv;     // local KV heads
     int nlt;       // local tiles per (batch row, local KV head)
     int NI;        // local items
+    int NX;        // extra blocks that run only local items (compute units the rows leave free)
     int nl_rows;   // sink + window rows
     int sink_end;  // sinks are rows [0, sink_end)
     int w0;        // the window is rows [w0, N)
