@@ -9,20 +9,27 @@
 //
 // with softmax(scale * q . k) over those keys, fp32 softmax and output.
 //
-// Matrix cores (bf16 in, fp32 accumulate), flash-style: each wave owns 16
-// queries and walks the allowed key tiles of 16 keys with an online softmax.
-//   S^T = K Q^T      4 x v_mfma_f32_16x16x32_bf16: lane l holds dims
-//                    32ks + 8(l/16) .. +7 of key l%16 (A, one 16-B load) and
-//                    of query l%16 (B, kept in registers); the result gives
-//                    lane l keys 4(l/16) + j of query l%16.
-//   O += P V         8 x v_mfma_f32_16x16x16_bf16: P's A operand is exactly
-//                    the lane's own scores (query l%16, keys 4(l/16) + i);
-//                    V's B operand (keys 4(l/16) + i, one dim) is gathered
-//                    from the tile staged in this wave's LDS slice.  O's
-//                    rows are queries 4(l/16) + j, so each query's softmax
-//                    factors are fetched from lane q with a shuffle.
-// P is rounded to bf16 for its MFMA (hi part) and the rounding residue is
-// added by a second MFMA (lo part), so P is carried to about 2^-17.
+// Matrix cores (bf16 in, fp32 accumulate), flash-style.  A block takes 32
+// query positions and up to 8 query heads of one KV head, one wave per head,
+// and walks the allowed keys in tiles of 64.  Each tile's K rows and V^T
+// (V transposed: one row per dimension) are staged once in LDS for all the
+// block's heads, double-buffered: the next tile's loads are in flight while
+// the current tile is multiplied.  Per wave and tile (v_mfma_f32_32x32x16_bf16):
+//
+//   S^T = K Q^T   2 key halves x 8 dim steps: A = 8 dims of one key row (one
+//                 16-B LDS read), B = Q^T (the wave's 32 queries, held in
+//                 registers).  Lane l then holds query l%32 and keys
+//                 8i + 4(l/32) + j of each half (i, j < 4).
+//   O^T += V^T P^T  4 dim tiles x 4 key steps of 16.  The 16 keys of a step
+//                 enter in the order the lanes already hold them: a lane of
+//                 half g supplies keys 4g + (0..3) and 8 + 4g + (0..3), as
+//                 B = its own probabilities and as A = two 8-B reads of V^T.
+//
+// O^T's columns are queries, so each lane's accumulators belong to its own
+// query: the online-softmax rescale needs no exchange, and a query's max and
+// sum combine the lane's 32 values with those of lane l ^ 32.  P enters the
+// second product as a bf16 pair (rounded value and its residue), so it is
+// carried to about 2^-17.
 #include <math.h>
 
 #include "rtp_device.h"
@@ -33,173 +40,225 @@ namespace rtp {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPfThreads = 256;
-constexpr int kPfWaves = kPfThreads / kWave;
-constexpr int kPfQ = 16 * kPfWaves;  // queries per block
+constexpr int kPfWaves = 8;                   // query heads per block, one per wave
+constexpr int kPfThreads = kPfWaves * kWave;  // 512
+constexpr int kPfQ = 32;                      // query positions per block
+constexpr int kPfK = 64;                      // keys per tile
+constexpr int kKRow = 128 + 8;                // bf16 per staged K row (272 B: rows 4 banks apart)
+constexpr int kVRow = kPfK + 4;               // bf16 per staged V^T row (136 B)
 constexpr float kPfLog2e = 1.4426950408889634f;
 
 struct PfArgs {
     const uint16_t *q, *K, *V;
     float *out;
     int Hq, Hkv, T, head_begin, n_heads, n_sink, window;
+    int G;        // query heads per KV head
+    int hc;       // chunks of up to kPfWaves heads per KV head
+    int c_first;  // first chunk (g * hc + s) that holds a head of the range
+    int nc;       // chunks that do
     int64_t kv_cap;
     float qscale;  // scale * log2(e)
 };
 
 struct PfShared {
-    uint16_t v[kPfWaves][16][128];  // each wave's V tile
+    uint16_t k[2][kPfK][kKRow];
+    uint16_t vt[2][128][kVRow];
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// bf16 of x, rounded to nearest even (finite x).
-__device__ __forceinline__ uint32_t bf16_rne(float x)
+__device__ __forceinline__ float shfl_x32(float v)
 {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((lane_id() ^ 32) << 2), __float_as_int(v)));
 }
 
-__device__ __forceinline__ float shfl(float v, int src)
+// Eight floats as bf16, rounded to nearest even.
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8])
 {
-    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+    bf16x8 r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = static_cast<__bf16>(x[t]);
+    return r;
+}
+
+// The tile's global loads: K row t / 8, 16-B pieces 2 (t % 8) and +1; V rows
+// 2 (t / 16) and +1, dims 8 (t % 16) .. +7.  Rows past the prompt read row
+// T - 1 (their keys are masked).
+struct TileRegs {
+    uint4 k0, k1, va, vb;
+};
+
+__device__ __forceinline__ TileRegs tile_load(const uint16_t *Kb, const uint16_t *Vb, int k0, int T)
+{
+    const int t = threadIdx.x;
+    TileRegs r;
+    const int kr = min(k0 + (t >> 3), T - 1);
+    const uint4 *kp = reinterpret_cast<const uint4 *>(Kb + (int64_t)kr * 128) + 2 * (t & 7);
+    r.k0 = kp[0];
+    r.k1 = kp[1];
+    const int va = min(k0 + 2 * (t >> 4), T - 1), vb = min(k0 + 2 * (t >> 4) + 1, T - 1);
+    r.va = *(reinterpret_cast<const uint4 *>(Vb + (int64_t)va * 128) + (t & 15));
+    r.vb = *(reinterpret_cast<const uint4 *>(Vb + (int64_t)vb * 128) + (t & 15));
+    return r;
+}
+
+// K rows as they are; V transposed: dims 8 (t % 16) + d of keys 2 (t / 16)
+// and +1 as one 32-bit word per dimension.
+__device__ __forceinline__ void tile_store(const TileRegs &r, PfShared &sh, int buf)
+{
+    const int t = threadIdx.x;
+    uint4 *kd = reinterpret_cast<uint4 *>(&sh.k[buf][t >> 3][0]) + 2 * (t & 7);
+    kd[0] = r.k0;
+    kd[1] = r.k1;
+    const uint32_t a[4] = {r.va.x, r.va.y, r.va.z, r.va.w};
+    const uint32_t b[4] = {r.vb.x, r.vb.y, r.vb.z, r.vb.w};
+    const int d0 = 8 * (t & 15), kk = 2 * (t >> 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<uint32_t *>(&sh.vt[buf][d0 + 2 * e][kk]) = (a[e] & 0xFFFFu) | (b[e] << 16);
+        *reinterpret_cast<uint32_t *>(&sh.vt[buf][d0 + 2 * e + 1][kk]) = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
+    }
 }
 
 __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
 {
     __shared__ PfShared sh;
-    const int hh = blockIdx.y % a.n_heads, b = blockIdx.y / a.n_heads;
-    const int h = a.head_begin + hh, g = h / (a.Hq / a.Hkv);
-    const int lane = lane_id(), w = threadIdx.x / kWave;
-    const int row = lane & 15, quad = lane >> 4;
-    const int q0 = (int)blockIdx.x * kPfQ + w * 16;
-    if (q0 >= a.T) return;  // whole wave; no block barrier below
+    // Heaviest query tiles (the latest positions) first.
+    const int q0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * kPfQ;
+    const int chunk = a.c_first + (int)blockIdx.y % a.nc, b = (int)blockIdx.y / a.nc;
+    const int g = chunk / a.hc, hs = (chunk % a.hc) * kPfWaves;
+    const int lane = lane_id(), w = threadIdx.x / kWave, gl = lane >> 5;
+    const int h = g * a.G + hs + w;
+    const bool active = hs + w < a.G && h >= a.head_begin && h < a.head_begin + a.n_heads;
 
-    const uint16_t *Qb = a.q + ((int64_t)b * a.Hq + h) * (int64_t)a.T * 128;
     const uint16_t *Kb = a.K + ((int64_t)b * a.Hkv + g) * a.kv_cap * 128;
     const uint16_t *Vb = a.V + ((int64_t)b * a.Hkv + g) * a.kv_cap * 128;
-    // B operand of S^T: query q0 + row (rows past T repeat T - 1), dims
-    // 32 ks + 8 quad .. +7.
-    const int my_q = q0 + row;
-    const int64_t qr = my_q < a.T ? my_q : a.T - 1;
-    bf16x8 qb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        qb[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(Qb + qr * 128 + 32 * ks + 8 * quad));
 
-    // Key ranges of this wave's queries: the union over its 16 queries.
-    const int q_last = min(q0 + 15, a.T - 1);
+    // Tiles: the sink tiles, then the causal / window range.
+    const int q_last = min(q0 + kPfQ - 1, a.T - 1);
     const bool local = a.window >= 1;
-    const int w0_first = local ? max(0, q0 + 1 - a.window) : 0;  // smallest w0 of the wave
-    const int sink_hi = local ? min(a.n_sink, max(0, q_last + 1 - a.window)) : 0;
-    // This lane's query: its allowed keys.
-    const int my_w0 = local ? max(0, my_q + 1 - a.window) : 0;
+    const int w0_first = local ? max(0, q0 + 1 - a.window) : 0;
+    const int w0_last = local ? max(0, q_last + 1 - a.window) : 0;
+    const int sink_hi = local ? min(a.n_sink, w0_last) : 0;  // keys below: some query's sink
+    const int ns = (sink_hi + kPfK - 1) / kPfK;
+    const int kt_first = max(ns, w0_first / kPfK), kt_last = q_last / kPfK;
+    const int nt = ns + max(0, kt_last - kt_first + 1);
+    auto tile_k0 = [&](int it) { return (it < ns ? it : kt_first + it - ns) * kPfK; };
+
+    // B operand of S^T: query q0 + l%32 (rows past T repeat T - 1), dims
+    // 16 ks + 8 (l/32) .. +7.
+    const int my_q = q0 + (lane & 31);
+    const int qc = min(my_q, a.T - 1);
+    bf16x8 qb[8];
+    if (active) {
+        const uint16_t *Qr = a.q + (((int64_t)b * a.Hq + h) * (int64_t)a.T + qc) * 128;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            qb[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Qr + 16 * ks + 8 * gl));
+    }
+    const int my_w0 = local ? max(0, qc + 1 - a.window) : 0;
     const int my_sink = local ? min(a.n_sink, my_w0) : 0;
 
-    float m = -INFINITY, l = 0.0f;  // softmax state of query my_q (lanes with row = q)
-    f32x4 o[8];
+    float m = -INFINITY, l = 0.0f;
+    f32x16 o[4];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] = 0.0f;
 
-    auto tile = [&](int k0) {
-        // S^T for keys k0 .. k0 + 15.
-        uint4 ka[4];
-        const int kr = k0 + row;
-        const int64_t krc = kr < a.T ? kr : a.T - 1;
+    tile_store(tile_load(Kb, Vb, tile_k0(0), a.T), sh, 0);
+    __syncthreads();
+    for (int it = 0; it < nt; ++it) {
+        const int buf = it & 1, k0 = tile_k0(it);
+        // The next tile's loads (the last iteration reloads its own tile
+        // into the idle buffer, which nothing reads).
+        const TileRegs rg = tile_load(Kb, Vb, tile_k0(min(it + 1, nt - 1)), a.T);
+        if (active) {
+            f32x16 s[2];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            ka[ks] = *reinterpret_cast<const uint4 *>(Kb + krc * 128 + 32 * ks + 8 * quad);
-        // Stage the V tile: lane l moves pieces l, l + 64, l + 128, l + 192
-        // (key = piece / 16, 16-B piece = piece % 16).
-        uint4 vx[4];
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int pc = lane + 64 * i, key = k0 + (pc >> 4);
-            const int64_t kc = key < a.T ? key : a.T - 1;
-            vx[i] = *reinterpret_cast<const uint4 *>(Vb + kc * 128 + (pc & 15) * 8);
+                for (int e = 0; e < 16; ++e) s[st][e] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const bf16x8 ka = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const uint4 *>(&sh.k[buf][32 * st + (lane & 31)][16 * ks + 8 * gl]));
+                    s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], s[st], 0, 0, 0);
+                }
+            // Every key of the tile allowed for every query of the block?
+            const bool full = k0 + kPfK - 1 <= q0 &&
+                              (!local || k0 >= w0_last || k0 + kPfK <= min(a.n_sink, w0_first));
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float v = s[st][e] * a.qscale;
+                    if (!full) {
+                        const int key = k0 + 32 * st + 8 * (e >> 2) + 4 * gl + (e & 3);
+                        const bool ok = key <= qc && (!local || key < my_sink || key >= my_w0);
+                        v = ok ? v : -INFINITY;
+                    }
+                    s[st][e] = v;
+                    tmax = fmaxf(tmax, v);
+                }
+            tmax = fmaxf(tmax, shfl_x32(tmax));
+            const float mn = fmaxf(m, tmax);
+            const float corr = m == -INFINITY ? 0.0f : exp2f(m - mn);
+            float psum = 0.0f;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float p = s[st][e] == -INFINITY ? 0.0f : exp2f(s[st][e] - mn);
+                    s[st][e] = p;
+                    psum += p;
+                }
+            psum += shfl_x32(psum);
+            l = l * corr + psum;
+            m = mn;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[dt][e] *= corr;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int st = ks >> 1, i0 = 2 * (ks & 1);
+                float ph[8], pl[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float p = s[st][4 * i0 + t];
+                    ph[t] = p;
+                    pl[t] = p - static_cast<float>(static_cast<__bf16>(p));
+                }
+                const bf16x8 bh = to_bf16x8(ph), bl = to_bf16x8(pl);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const uint16_t *vr = &sh.vt[buf][32 * dt + (lane & 31)][16 * ks + 4 * gl];
+                    const uint2 v0 = *reinterpret_cast<const uint2 *>(vr);
+                    const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 8);
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bh, o[dt], 0, 0, 0);
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bl, o[dt], 0, 0, 0);
+                }
+            }
         }
-        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[ks]), qb[ks], s, 0, 0, 0);
-        // Lane l: keys k0 + 4 quad + j of query my_q, in log2 units.
-        float p[4];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = k0 + 4 * quad + j;
-            const bool ok = my_q < a.T && key <= my_q &&
-                            (!local || key < my_sink || key >= my_w0);
-            p[j] = ok ? s[j] * a.qscale : -INFINITY;
-            tmax = fmaxf(tmax, p[j]);
-        }
-        tmax = fmaxf(tmax, shfl(tmax, lane ^ 16));
-        tmax = fmaxf(tmax, shfl(tmax, lane ^ 32));
-        const float mn = fmaxf(m, tmax);
-        const float corr = (m == -INFINITY) ? (mn == -INFINITY ? 1.0f : 0.0f) : exp2f(m - mn);
-        float psum = 0.0f;
-        uint32_t ph[4], pl[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float e = p[j] == -INFINITY ? 0.0f : exp2f(p[j] - mn);
-            psum += e;
-            ph[j] = bf16_rne(e);
-            pl[j] = bf16_rne(e - __uint_as_float(ph[j] << 16));
-        }
-        psum += shfl(psum, lane ^ 16);
-        psum += shfl(psum, lane ^ 32);
-        l = l * corr + psum;
-        m = mn;
-        // O rows are queries 4 quad + j: their factors come from lane
-        // 4 quad + j (row = that query).
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float cj = shfl(corr, 4 * quad + j);
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) o[nt][j] *= cj;
-        }
-        // V tile into this wave's LDS slice, then the B operands.
-        uint4 *vs = reinterpret_cast<uint4 *>(&sh.v[w][0][0]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vs[lane + 64 * i] = vx[i];
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        const i16x4 ahi = {(short)ph[0], (short)ph[1], (short)ph[2], (short)ph[3]};
-        const i16x4 alo = {(short)pl[0], (short)pl[1], (short)pl[2], (short)pl[3]};
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            i16x4 bv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = (short)sh.v[w][4 * quad + i][16 * nt + row];
-            o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, o[nt], 0, 0, 0);
-            o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, o[nt], 0, 0, 0);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();  // reads done before the next tile's writes
-    };
-
-    // Sink tiles first (local heads), then the window / causal range.
-    int k_begin = 0;
-    if (local) {
-        for (int k0 = 0; k0 < sink_hi; k0 += 16) tile(k0);
-        k_begin = max((w0_first / 16) * 16, ((sink_hi + 15) / 16) * 16);
+        tile_store(rg, sh, buf ^ 1);
+        __syncthreads();
     }
-    for (int k0 = k_begin; k0 <= q_last; k0 += 16) tile(k0);
-
-    // out[q][dim] = O / l for queries 4 quad + j.
-    float *ob = a.out + ((int64_t)b * a.Hq + h) * (int64_t)a.T * 128;
+    if (!active || my_q >= a.T) return;
+    // out[q][dim] = O / l: lane l holds dims 32 dt + 8 i + 4 (l/32) + j.
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float *orow = a.out + (((int64_t)b * a.Hq + h) * (int64_t)a.T + my_q) * 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int qq = q0 + 4 * quad + j;
-        const float lj = shfl(l, 4 * quad + j);
-        const float inv = lj > 0.0f ? 1.0f / lj : 0.0f;
-        if (qq < a.T) {
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) ob[(int64_t)qq * 128 + 16 * nt + row] = o[nt][j] * inv;
-        }
-    }
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<float4 *>(orow + 32 * dt + 8 * i + 4 * gl) =
+                make_float4(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv, o[dt][4 * i + 2] * inv,
+                            o[dt][4 * i + 3] * inv);
 }
 
 }  // namespace
@@ -223,8 +282,14 @@ hipError_t launch_prefill_attend(const uint16_t *q, const uint16_t *K, const uin
     a.window = window;
     a.kv_cap = kv_cap;
     a.qscale = scale * kPfLog2e;
+    a.G = Hq / Hkv;
+    a.hc = (a.G + kPfWaves - 1) / kPfWaves;
+    const int h_last = head_begin + n_heads - 1;
+    a.c_first = (head_begin / a.G) * a.hc + (head_begin % a.G) / kPfWaves;
+    const int c_last = (h_last / a.G) * a.hc + (h_last % a.G) / kPfWaves;
+    a.nc = c_last - a.c_first + 1;
     const int gx = (T + kPfQ - 1) / kPfQ;
-    return launch(prefill_kernel, dim3((unsigned)gx, (unsigned)(B * n_heads)), dim3(kPfThreads), 0,
+    return launch(prefill_kernel, dim3((unsigned)gx, (unsigned)(B * a.nc)), dim3(kPfThreads), 0,
                   stream, a);
 }
 
