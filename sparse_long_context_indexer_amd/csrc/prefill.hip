@@ -59,7 +59,8 @@ struct PfArgs {
     int c_first;  // first chunk (g * hc + s) that holds a head of the range
     int nc;       // chunks that do
     int64_t kv_cap;
-    float qscale;  // scale * log2(e)
+    float qscale;    // |scale| * log2(e)
+    uint32_t qsign;  // 0x80008000 when scale < 0: Q's signs are flipped instead
 };
 
 struct PfShared {
@@ -153,8 +154,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
     if (active) {
         const uint16_t *Qr = a.q + (((int64_t)b * a.Hq + h) * (int64_t)a.T + qc) * 128;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            qb[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Qr + 16 * ks + 8 * gl));
+        for (int ks = 0; ks < 8; ++ks) {
+            uint4 u = *reinterpret_cast<const uint4 *>(Qr + 16 * ks + 8 * gl);
+            u.x ^= a.qsign;
+            u.y ^= a.qsign;
+            u.z ^= a.qsign;
+            u.w ^= a.qsign;
+            qb[ks] = __builtin_bit_cast(bf16x8, u);
+        }
     }
     const int my_w0 = local ? max(0, qc + 1 - a.window) : 0;
     const int my_sink = local ? min(a.n_sink, my_w0) : 0;
@@ -187,42 +194,68 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
                         bf16x8, *reinterpret_cast<const uint4 *>(&sh.k[buf][32 * st + (lane & 31)][16 * ks + 8 * gl]));
                     s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], s[st], 0, 0, 0);
                 }
-            // Every key of the tile allowed for every query of the block?
+            // Masked keys score -inf; a tile whose every key is allowed for
+            // every query of the block skips the test.
             const bool full = k0 + kPfK - 1 <= q0 &&
                               (!local || k0 >= w0_last || k0 + kPfK <= min(a.n_sink, w0_first));
+            uint32_t okm = 0xFFFFFFFFu;  // bit 16 st + e: key allowed
+            if (!full) {
+                okm = 0u;
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = k0 + 32 * st + 8 * (e >> 2) + 4 * gl + (e & 3);
+                        const bool ok = (key <= qc) & (!local | (key < my_sink) | (key >= my_w0));
+                        okm |= (uint32_t)ok << (16 * st + e);
+                        s[st][e] = ok ? s[st][e] : -INFINITY;
+                    }
+            }
+            // The query's max over the tile (both lane halves), in log2 units.
             float tmax = -INFINITY;
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float v = s[st][e] * a.qscale;
-                    if (!full) {
-                        const int key = k0 + 32 * st + 8 * (e >> 2) + 4 * gl + (e & 3);
-                        const bool ok = key <= qc && (!local || key < my_sink || key >= my_w0);
-                        v = ok ? v : -INFINITY;
-                    }
-                    s[st][e] = v;
-                    tmax = fmaxf(tmax, v);
-                }
-            tmax = fmaxf(tmax, shfl_x32(tmax));
-            const float mn = fmaxf(m, tmax);
-            const float corr = m == -INFINITY ? 0.0f : exp2f(m - mn);
+                for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(s[st][e], s[st][e + 1]));
+            tmax = fmaxf(tmax, shfl_x32(tmax)) * a.qscale;
+            // The reference m moves up only when the tile's max exceeds it by
+            // more than 8 (so probabilities stay below 2^8): the rescale of
+            // O and l is rare after the first tiles.
+            if (__ballot(tmax > m + 8.0f)) {
+                const float mn = tmax > m + 8.0f ? tmax : m;
+                const float corr = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+                l *= corr;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[dt][e] *= corr;
+                m = mn;
+            }
+            // p = 2^(s * qscale - m), 0 for a masked key.
+            const float nm = m == -INFINITY ? 0.0f : -m;
             float psum = 0.0f;
+            if (full) {
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+                for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float p = s[st][e] == -INFINITY ? 0.0f : exp2f(s[st][e] - mn);
-                    s[st][e] = p;
-                    psum += p;
-                }
-            psum += shfl_x32(psum);
-            l = l * corr + psum;
-            m = mn;
+                    for (int e = 0; e < 16; ++e) {
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], a.qscale, nm));
+                        s[st][e] = p;
+                        psum += p;
+                    }
+            } else {
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+                for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) o[dt][e] *= corr;
+                    for (int e = 0; e < 16; ++e) {
+                        const float p = (okm >> (16 * st + e)) & 1u
+                                            ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], a.qscale, nm))
+                                            : 0.0f;
+                        s[st][e] = p;
+                        psum += p;
+                    }
+            }
+            l += psum + shfl_x32(psum);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int st = ks >> 1, i0 = 2 * (ks & 1);
@@ -281,7 +314,8 @@ hipError_t launch_prefill_attend(const uint16_t *q, const uint16_t *K, const uin
     a.n_sink = n_sink;
     a.window = window;
     a.kv_cap = kv_cap;
-    a.qscale = scale * kPfLog2e;
+    a.qscale = fabsf(scale) * kPfLog2e;
+    a.qsign = scale < 0.0f ? 0x80008000u : 0u;
     a.G = Hq / Hkv;
     a.hc = (a.G + kPfWaves - 1) / kPfWaves;
     const int h_last = head_begin + n_heads - 1;
