@@ -356,7 +356,7 @@ rtp_status rtp_local_decode_ring(const rtp_bf16 *q, const rtp_bf16 *K,
  * with g = h / (Hq/Hkv): the local rows of each t are those rtp_local_decode
  * reads with N = t + 1.  bf16 products and fp32 accumulation on the matrix
  * cores, fp32 softmax (the probabilities enter the second product as a bf16
- * pair, good to about 2^-17), fp32 output.
+ * pair, good to about 2^-16), fp32 output.
  *
  *   q      bf16 [B][Hq][T][d]       16-B aligned (the prompt's queries, post-RoPE)
  *   K, V   bf16 [B][Hkv][kv_cap][d] 16-B aligned; rows [0, T) are the prompt

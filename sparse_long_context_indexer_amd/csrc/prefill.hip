@@ -27,9 +27,11 @@
 //
 // O^T's columns are queries, so each lane's accumulators belong to its own
 // query: the online-softmax rescale needs no exchange, and a query's max and
-// sum combine the lane's 32 values with those of lane l ^ 32.  P enters the
-// second product as a bf16 pair (rounded value and its residue), so it is
-// carried to about 2^-17.
+// sum combine the lane's 32 values with those of lane l ^ 32.  The softmax
+// reference moves up only when a tile's max exceeds it by more than 8 (log2
+// units), so probabilities stay below 2^8 and the rescale of O is rare.  P
+// enters the second product as a bf16 pair (its top 16 bits, and the exact
+// residue rounded to bf16), so it is carried to about 2^-16.
 #include <math.h>
 
 #include "rtp_device.h"
@@ -259,22 +261,34 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int st = ks >> 1, i0 = 2 * (ks & 1);
-                float ph[8], pl[8];
+                // hi = p truncated to bf16 (its top 16 bits), lo = the exact
+                // fp32 residue p - hi rounded to bf16.
+                uint32_t hw[4];
+                float pl[8];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const float p = s[st][4 * i0 + t];
-                    ph[t] = p;
-                    pl[t] = p - static_cast<float>(static_cast<__bf16>(p));
+                for (int t = 0; t < 8; t += 2) {
+                    const uint32_t u0 = __float_as_uint(s[st][4 * i0 + t]);
+                    const uint32_t u1 = __float_as_uint(s[st][4 * i0 + t + 1]);
+                    hw[t / 2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+                    pl[t] = __uint_as_float(u0) - __uint_as_float(u0 & 0xFFFF0000u);
+                    pl[t + 1] = __uint_as_float(u1) - __uint_as_float(u1 & 0xFFFF0000u);
                 }
-                const bf16x8 bh = to_bf16x8(ph), bl = to_bf16x8(pl);
+                const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+                const bf16x8 bl = to_bf16x8(pl);
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const uint16_t *vr = &sh.vt[buf][32 * dt + (lane & 31)][16 * ks + 4 * gl];
-                    const uint2 v0 = *reinterpret_cast<const uint2 *>(vr);
-                    const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 8);
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bh, o[dt], 0, 0, 0);
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bl, o[dt], 0, 0, 0);
+                for (int dp = 0; dp < 4; dp += 2) {
+                    bf16x8 va[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const uint16_t *vr = &sh.vt[buf][32 * (dp + u) + (lane & 31)][16 * ks + 4 * gl];
+                        const uint2 v0 = *reinterpret_cast<const uint2 *>(vr);
+                        const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 8);
+                        va[u] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                    }
+                    o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], bh, o[dp], 0, 0, 0);
+                    o[dp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], bh, o[dp + 1], 0, 0, 0);
+                    o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], bl, o[dp], 0, 0, 0);
+                    o[dp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], bl, o[dp + 1], 0, 0, 0);
                 }
             }
         }

@@ -331,6 +331,32 @@ def test_prefill_attend_against_oracle(T, n_sink, window, hb, nh):
         assert np.all(np.isnan(got[b, outside]))
 
 
+@pytest.mark.parametrize("scale_kind", ["negative", "zero"])
+def test_prefill_attend_scale_sign(scale_kind):
+    # A negative scale (the kernel flips Q's signs and uses |scale|) and a
+    # zero scale (uniform weights over each query's keys), dense and sinks +
+    # window heads, against the oracle.
+    B, Hq, Hkv, T = 1, 8, 2, 300
+    cap = T
+    q = synth.normal_bf16(synth.key(91, 1), 0, B * Hq * T * 128).reshape(B, Hq, T, 128)
+    K = synth.normal_bf16(synth.key(91, 2), 0, B * Hkv * cap * 128).reshape(B, Hkv, cap, 128)
+    V = synth.normal_bf16(synth.key(91, 3), 0, B * Hkv * cap * 128).reshape(B, Hkv, cap, 128)
+    scale = -1.0 / math.sqrt(128.0) if scale_kind == "negative" else 0.0
+    out = torch.full((B, Hq, T, 128), float("nan"), dtype=torch.float32, device=dev())
+    qd = torch.from_numpy(q.view(np.int16)).to(dev())
+    Kd = torch.from_numpy(K.view(np.int16)).to(dev())
+    Vd = torch.from_numpy(V.view(np.int16)).to(dev())
+    rtp.rtp_prefill_attend(qd, Kd, Vd, 0, 4, 0, 0, scale, out)
+    rtp.rtp_prefill_attend(qd, Kd, Vd, 4, 4, 3, 40, scale, out)
+    got = out.cpu().numpy()
+    for h in range(Hq):
+        for t in (0, 1, 2, 39, 40, 41, 150, 299):
+            rows = np.arange(t + 1) if h < 4 else oracle.local_rows(t + 1, 3, 40)
+            ref = oracle.attention(q[0, h, t], K[0, h // 4, rows], V[0, h // 4, rows], scale)
+            ok, err, rel = judge_out(got[0, h, t], ref)
+            assert ok, (scale_kind, h, t, err, rel)
+
+
 def test_prefill_attend_benched_size():
     # The size the benchmark times: a 16384-token prompt, 32 query heads on
     # 4 KV heads, heads 0-7 dense and heads 8-31 on 4 sinks + a 4096-token
