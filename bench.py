@@ -42,10 +42,12 @@ def parse():
     ap.add_argument("--p", type=float, default=0.9)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-side-stream", action="store_true")
-    ap.add_argument("--sparse-mode", choices=["layer", "fused", "scan_local", "union",
-                                              "per_head"],
+    ap.add_argument("--sparse-mode", choices=["layer", "fused", "topp_attend", "scan_local",
+                                              "union", "per_head"],
                     default="fused",
-                    help="layer: the whole layer in one rtp_decode_layer launch; scan_local: "
+                    help="layer: the whole layer in one rtp_decode_layer launch; topp_attend: "
+                         "the scan, then selection and attention in one rtp_topp_attend "
+                         "launch; scan_local: "
                          "scan and local heads in one rtp_scan_local launch, sparse "
                          "heads in rtp_decode_attend; fused: sparse and local heads in one "
                          "rtp_decode_attend launch; per_head: separate calls, local heads on "
@@ -122,7 +124,8 @@ def main():
 
     # Local heads of a layer run on a side stream, overlapping the retrieval
     # chain of the same layer; each layer joins both before the next starts.
-    side = (None if args.no_side_stream or args.sparse_mode in ("layer", "fused", "scan_local")
+    side = (None if args.no_side_stream
+            or args.sparse_mode in ("layer", "fused", "topp_attend", "scan_local")
             else torch.cuda.Stream(device=dev))
     stream = torch.cuda.current_stream(dev)
 
@@ -339,6 +342,21 @@ def reference_calls(args, cfg, p, dev, stream, L, qr_all, kr_all, q_all, K_all, 
         cfg.n_sink, cfg.window, scale, out_all[l], four.ws_attend) for l in range(L)])
     ms_four, _ = timed_step(lambda l: four(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l],
                                            p, scale, out_all[l]), 5, 1)
+    # Selection and attention in one launch (rtp_topp_attend), on the same
+    # per-layer scores, and the step with it (scan + one launch per layer).
+    ws_ta = torch.empty(rtp.topp_attend_workspace_size(B, Hq, Hkv, N, H_r, cfg.n_sink,
+                                                       cfg.window),
+                        dtype=torch.uint8, device=dev)
+    idx_t = torch.empty_like(idx_l[0])
+    count_t = torch.empty_like(count_l[0])
+    us["rtp_topp_attend"] = time_call(lambda: [rtp.rtp_topp_attend(
+        scores_l[l], q_all[l], K_all[l], V_all[l], cfg.n_sink, cfg.window, p, scale, out_all[l],
+        idx_t, count_t, ws_ta) for l in range(L)])
+    del ws_ta, idx_t, count_t
+    ta = DecodeLayer(B, Hq, Hkv, N, H_r, cfg.n_sink, cfg.window, dev, mode="topp_attend")
+    ms_ta, _ = timed_step(lambda l: ta(qr_all[l], kr_all[l], q_all[l], K_all[l], V_all[l],
+                                       p, scale, out_all[l]), 5, 1)
+    del ta
     # Static top-k at the workload's mean top-p budget (sel_fused_kernel<true>).
     k_budget = max(1, int(round(float(count_l.float().mean().item()))))
     idx_k = torch.empty_like(idx_l[0])
@@ -391,6 +409,7 @@ def reference_calls(args, cfg, p, dev, stream, L, qr_all, kr_all, q_all, K_all, 
     del q_pf, out_pf
     sel_bytes = B * H_r * N * 4 + float(count_l.float().sum().item()) / L * 4
     out = {"ms_per_step_four_call": round(ms_four, 4),
+           "ms_per_step_topp_attend": round(ms_ta, 4),
            "ms_per_step_four_call_bf16_kr": round(ms_bf16, 4),
            "topk_budget": k_budget,
            "project_prefill_GBps": round(proj_gbps, 1),

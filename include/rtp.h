@@ -484,9 +484,58 @@ rtp_status rtp_decode_layer_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, i
                                            size_t *bytes);
 
 /*
+ * rtp_topp_attend -- rtp_topp_select over the retrieval heads' scores
+ * followed by rtp_decode_attend (the retrieval heads' exact attention over
+ * their kept rows, the local heads' sinks + window attention), in one
+ * launch (gist.science summary, method section 3: top-p mass; section 5:
+ * a sort-free histogram threshold and bandwidth-optimised sparse decode;
+ * section 1: the two head roles).  The kept sets and outputs are those of
+ * the two calls.  Attention over the tokens the selection lists first
+ * overlaps the resolution of each row's boundary bin.
+ *
+ * Head roles as in rtp_decode_layer: query heads 0 .. Hq_r-1 are retrieval
+ * heads with score rows [B][Hq_r] (Hq_r a multiple of G = Hq/Hkv), query
+ * heads Hq_r .. Hq-1 local heads.
+ *
+ *   scores  fp32 [B][Hq_r][N]           4-B aligned (rtp_index_scores' output)
+ *   q       bf16 [B][Hq][d]             16-B aligned
+ *   K, V    bf16 [B][Hkv][kv_cap][d]    16-B aligned
+ *   p       in (0, 1]; p = 1 keeps every token (then two launches)
+ *   scale   finite
+ *   n_sink, window   as in rtp_local_decode (ignored when Hq_r == Hq)
+ *   out     fp32 [B][Hq][d]             out, every head written
+ *   idx     int32 [B][Hq_r][N]          out: kept indices, in no particular order
+ *   count   int32 [B][Hq_r]             out: kept-set sizes
+ *   workspace  >= rtp_topp_attend_workspace_size(...) bytes, 256-B aligned;
+ *              contents need no initialisation
+ *   d must be 128; G must be at most 8; B * Hq_r at most 1024 and
+ *   B * Hq_r * N below 2^32 (else RTP_ERR_UNSUPPORTED).
+ *
+ * The launch relies only on blocks being dispatched in index order: a
+ * block waits only for blocks with lower indices.
+ *
+ * Errors: RTP_ERR_NULL, RTP_ERR_UNSUPPORTED, RTP_ERR_SHAPE, RTP_ERR_VALUE
+ * (p, scale, n_sink, window), RTP_ERR_ALIGN, RTP_ERR_WORKSPACE.
+ */
+rtp_status rtp_topp_attend(const float *scores, const rtp_bf16 *q, const rtp_bf16 *K,
+                           const rtp_bf16 *V, int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                           int64_t kv_cap, int32_t d, int32_t Hq_r, int32_t n_sink,
+                           int32_t window, float p, float scale, float *out, int32_t *idx,
+                           int32_t *count, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * rtp_topp_attend_workspace_size -- bytes of workspace rtp_topp_attend needs
+ * for these sizes on the current device (host only).  The same errors as
+ * rtp_topp_attend for the sizes, plus RTP_ERR_NULL when bytes is NULL.
+ */
+rtp_status rtp_topp_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                                          int32_t Hq_r, int32_t n_sink, int32_t window,
+                                          size_t *bytes);
+
+/*
  * Waits between blocks.  Some kernels hand data from block to block inside
  * one launch (rtp_topp_select, rtp_topk_select, rtp_sparse_decode,
- * rtp_decode_attend, rtp_decode_layer); a block that waits polls at most
+ * rtp_decode_attend, rtp_decode_layer, rtp_topp_attend); a block that waits polls at most
  * `polls` times (default 2^24) and then gives up, sets the status bit
  * RTP_STATUS_WAIT_TIMEOUT in the device's sticky status word, and goes on,
  * so the kernel still ends; the results of that call, and the state of its

@@ -34,7 +34,8 @@ SYMBOLS = ("rtp_index_scores", "rtp_index_scores_bf16", "rtp_index_project", "rt
            "rtp_sparse_decode_union",
            "rtp_local_decode", "rtp_local_decode_ring", "rtp_keep_bits_add_local",
            "rtp_prefill_attend", "rtp_decode_attend", "rtp_scan_local", "rtp_decode_layer",
-           "rtp_decode_layer_workspace_size", "rtp_set_wait_limit", "rtp_device_status",
+           "rtp_decode_layer_workspace_size", "rtp_topp_attend", "rtp_topp_attend_workspace_size",
+           "rtp_set_wait_limit", "rtp_device_status",
            "rtp_workspace_size", "rtp_status_string", "rtp_last_hip_error")
 
 # Bit of the device status word (rtp_device_status): a bounded wait gave up.
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
                                        I32, I32, I32, F32, F32, P, P, P, P, P, SZ, P]
         L.rtp_decode_layer_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32,
                                                       ctypes.POINTER(SZ)]
+        L.rtp_topp_attend.argtypes = [P, P, P, P, I32, I32, I32, I32, I64, I32, I32, I32,
+                                      I32, F32, F32, P, P, P, P, SZ, P]
+        L.rtp_topp_attend_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32,
+                                                     ctypes.POINTER(SZ)]
         L.rtp_set_wait_limit.argtypes = [ctypes.c_uint32]
         L.rtp_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), I32]
         L.rtp_workspace_size.argtypes = [I32, I32, I32, I32, ctypes.POINTER(SZ)]
@@ -127,6 +132,15 @@ def decode_layer_workspace_size(B: int, Hq: int, Hkv: int, N: int, Hq_r: int, n_
     out = ctypes.c_size_t(0)
     _call("rtp_decode_layer_workspace_size", B, Hq, Hkv, N, Hq_r, n_sink, window,
                                                  ctypes.byref(out))
+    return out.value
+
+
+def topp_attend_workspace_size(B: int, Hq: int, Hkv: int, N: int, Hq_r: int, n_sink: int,
+                               window: int) -> int:
+    """Workspace bytes of rtp_topp_attend on the current device."""
+    out = ctypes.c_size_t(0)
+    _call("rtp_topp_attend_workspace_size", B, Hq, Hkv, N, Hq_r, n_sink, window,
+          ctypes.byref(out))
     return out.value
 
 
@@ -441,6 +455,28 @@ def rtp_decode_layer(q_r, k_r, q, K, V, N, Hq_r, n_sink, window, p, scale, out, 
         B, Hq, Hkv, N, d, r, Hq_r, n_sink, window, float(p), float(scale), op,
         _dev(idx, torch.int32, "idx", (B, Hq_r, N)), _dev(count, torch.int32, "count", (B, Hq_r)),
         sp, wp, wn, _stream(q, stream))
+
+
+def rtp_topp_attend(scores, q, K, V, n_sink, window, p, scale, out, idx, count, workspace,
+                    stream=None) -> None:
+    """Top-p selection over scores f32 [B][Hq_r][N] (query heads [0, Hq_r)
+    are retrieval heads) and attention for every head in one launch: the
+    retrieval heads over their kept rows, heads [Hq_r, Hq) over sinks +
+    window.  q bf16 [B][Hq][d]; K, V bf16 [B][Hkv][cap][d]; out f32
+    [B][Hq][d]; idx i32 [B][Hq_r][N] and count i32 [B][Hq_r] (out);
+    workspace uint8 [>= topp_attend_workspace_size(B, Hq, Hkv, N, Hq_r,
+    n_sink, window)]."""
+    import torch
+    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
+    if scores.dim() != 3 or scores.shape[0] != B:
+        raise ValueError("scores must be [B][Hq_r][N]")
+    Hq_r, N = scores.shape[1], scores.shape[2]
+    wp, wn = _ws(workspace)
+    _call("rtp_topp_attend",
+        _dev(scores, torch.float32, "scores", (B, Hq_r, N)), qp, Kp, Vp, B, Hq, Hkv, N, cap, d,
+        Hq_r, n_sink, window, float(p), float(scale), op,
+        _dev(idx, torch.int32, "idx", (B, Hq_r, N)), _dev(count, torch.int32, "count", (B, Hq_r)),
+        wp, wn, _stream(q, stream))
 
 
 def rtp_prefill_attend(q, K, V, head_begin, n_heads, n_sink, window, scale, out,

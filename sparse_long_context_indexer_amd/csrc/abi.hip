@@ -468,6 +468,71 @@ rtp_status rtp_decode_layer(const float *q_r, const float *k_r, int64_t kr_cap,
                                              wc.limit, wc.status, as_stream(stream)));
 }
 
+// Sizes of a top-p + attention launch that need no device (checked first).
+static rtp_status topp_attend_sizes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t Hq_r,
+                                    int32_t n_sink, int32_t window)
+{
+    const rtp_status st = layer_sizes(B, Hq, Hkv, N, Hq_r, n_sink, window);
+    if (st != RTP_OK) return st;
+    if (Hq / Hkv > 8 || (int64_t)B * Hq_r > 1024 ||
+        (int64_t)B * Hq_r * (int64_t)N > (int64_t)UINT32_MAX)
+        return RTP_ERR_UNSUPPORTED;
+    return RTP_OK;
+}
+
+// The launch shape on the current device (its compute units).
+static rtp_status topp_attend_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t Hq_r,
+                                    int32_t n_sink, int32_t window, int *cus)
+{
+    const hipError_t e = rtp::device_cus(cus);
+    if (e != hipSuccess) return from_hip(e);
+    return rtp::topp_attend_fits(*cus, B, Hq, Hkv, N, Hq_r, Hq_r < Hq ? n_sink : 0,
+                                 Hq_r < Hq ? window : 1)
+               ? RTP_OK
+               : RTP_ERR_UNSUPPORTED;
+}
+
+rtp_status rtp_topp_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                                          int32_t Hq_r, int32_t n_sink, int32_t window,
+                                          size_t *bytes)
+{
+    if (!bytes) return RTP_ERR_NULL;
+    rtp_status st = topp_attend_sizes(B, Hq, Hkv, N, Hq_r, n_sink, window);
+    if (st != RTP_OK) return st;
+    int cus = 0;
+    st = topp_attend_shape(B, Hq, Hkv, N, Hq_r, n_sink, window, &cus);
+    if (st != RTP_OK) return st;
+    *bytes = rtp::topp_attend_ws_bytes(cus, B, Hq, Hkv, N, Hq_r, Hq_r < Hq ? n_sink : 0,
+                                       Hq_r < Hq ? window : 1);
+    return RTP_OK;
+}
+
+rtp_status rtp_topp_attend(const float *scores, const rtp_bf16 *q, const rtp_bf16 *K,
+                           const rtp_bf16 *V, int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                           int64_t kv_cap, int32_t d, int32_t Hq_r, int32_t n_sink,
+                           int32_t window, float p, float scale, float *out, int32_t *idx,
+                           int32_t *count, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!scores || !q || !K || !V || !out || !idx || !count || !workspace) return RTP_ERR_NULL;
+    if (d != 128) return RTP_ERR_UNSUPPORTED;
+    if (N < 1 || kv_cap < N) return RTP_ERR_SHAPE;
+    rtp_status st = topp_attend_sizes(B, Hq, Hkv, N, Hq_r, n_sink, window);
+    if (st != RTP_OK) return st;
+    if (!(p > 0.0f && p <= 1.0f) || !isfinite(scale)) return RTP_ERR_VALUE;
+    if (!aligned(scores, 4) || !aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) ||
+        !aligned(out, 4) || !aligned(idx, 4) || !aligned(count, 4) || !aligned(workspace, 256))
+        return RTP_ERR_ALIGN;
+    int cus = 0;
+    st = topp_attend_shape(B, Hq, Hkv, N, Hq_r, n_sink, window, &cus);
+    if (st != RTP_OK) return st;
+    const int ns = Hq_r < Hq ? n_sink : 0, win = Hq_r < Hq ? window : 1;
+    if (ws_bytes < rtp::topp_attend_ws_bytes(cus, B, Hq, Hkv, N, Hq_r, ns, win))
+        return RTP_ERR_WORKSPACE;
+    return from_hip(rtp::launch_topp_attend(scores, q, K, V, B, Hq, Hkv, N, kv_cap, Hq_r, ns,
+                                            win, p, scale, out, idx, count, workspace,
+                                            as_stream(stream)));
+}
+
 rtp_status rtp_scan_local(const float *q_r, const float *k_r, float *scores, int32_t Hq_r,
                           int32_t Hkv_r, int64_t kr_cap, int32_t r, const rtp_bf16 *q,
                           const rtp_bf16 *K, const rtp_bf16 *V, int32_t B, int32_t Hq,

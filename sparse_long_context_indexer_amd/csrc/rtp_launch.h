@@ -137,6 +137,17 @@ hipError_t launch_decode_layer(const LayerGeom &L, const float *q_r, const float
                                int32_t *count, float *scores, void *ws, uint32_t spin_limit,
                                uint32_t *status, hipStream_t stream);
 
+// ---- top-p selection and attention over the kept rows in one launch (select.hip)
+// Score row b * H_r + h is query head h of batch row b (the retrieval heads
+// are query heads [0, H_r)); heads [H_r, Hq) are local heads.
+size_t topp_attend_ws_bytes(int cus, int B, int Hq, int Hkv, int N, int H_r, int n_sink,
+                            int window);
+bool topp_attend_fits(int cus, int B, int Hq, int Hkv, int N, int H_r, int n_sink, int window);
+hipError_t launch_topp_attend(const float *scores, const uint16_t *q, const uint16_t *K,
+                              const uint16_t *V, int B, int Hq, int Hkv, int N, int64_t kv_cap,
+                              int H_r, int n_sink, int window, float p, float scale, float *out,
+                              int32_t *idx, int32_t *count, void *ws, hipStream_t stream);
+
 // Compute units of the current device (queried once per device).
 hipError_t device_cus(int *cus);
 

@@ -59,7 +59,8 @@ struct SelRow {
     uint32_t hist_done;  // hist blocks finished
     uint32_t emit_done;  // emit blocks finished
     unsigned long long ready;  // tagged: the row's state below was cleared
-    uint32_t pad[10];
+    uint32_t kept1;      // tokens kept by the emit blocks (published for attention blocks)
+    uint32_t pad[9];
 };
 static_assert(sizeof(SelRow) == 64, "SelRow is one 64-B record");
 
@@ -584,12 +585,13 @@ __device__ void res_choose_count(uint32_t c, int nb, ResShared &S)
     }
 }
 
-// Appends token i to the row's kept list at slot pa and, when the row has
-// a keep bitmap, sets its bit (the emit blocks wrote the bitmap's words with
+// Appends token i to the row's kept list at slot pa (an agent-scope store:
+// attention blocks of the same launch may read it) and, when the row has a
+// keep bitmap, sets its bit (the emit blocks wrote the bitmap's words with
 // agent-scope stores before the resolve started).
 __device__ __forceinline__ void keep_token(int32_t *ir, int64_t pa, uint32_t i, uint32_t *kbr)
 {
-    ir[pa] = (int32_t)i;
+    st_agent(reinterpret_cast<uint32_t *>(ir + pa), i);
     if (kbr) atomicOr(kbr + (i >> 5), 1u << (i & 31u));
 }
 
@@ -862,7 +864,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
         }
     }
     __syncthreads();
-    if (tid == 0) count[r] = (int32_t)(emitted + (uint32_t)S.nn);
+    if (tid == 0) st_agent(reinterpret_cast<uint32_t *>(count + r), emitted + (uint32_t)S.nn);
 }
 
 // What the pick reads of the row: this thread's Hist1 bins and the top
@@ -892,7 +894,7 @@ __device__ __forceinline__ void pick_inputs(SelPtrs P, int64_t r, PickIn &pi)
 // pi): the row's threshold, the chunk's kept tokens and boundary-bin
 // candidates, its share of Hist2; the last chunk of the row to finish
 // resolves the boundary bin.
-template <bool kCount>
+template <bool kCount, bool kAtt = false>
 __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, int N,
                           SelPtrs P, int64_t r, double target, const PickIn &pi,
                           int32_t *__restrict__ idx, int32_t *__restrict__ count,
@@ -1000,7 +1002,9 @@ __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, 
     __syncthreads();
     const unsigned long long base = S.gbase + wbase[w];
     uint32_t oa = (uint32_t)(base >> 32) + (ex >> 16);
-    for (uint32_t m = above; m; m &= m - 1) ir[oa++] = (int32_t)cv.index32(__ffs(m) - 1);
+    // Agent-scope stores: attention blocks of the same launch may read them.
+    for (uint32_t m = above; m; m &= m - 1)
+        st_agent(reinterpret_cast<uint32_t *>(ir + oa++), cv.index32(__ffs(m) - 1));
     uint2 *gcb = cr + (uint32_t)S.gbase;  // this block's candidates' place in the row
     if (staged) {
         // Written out coalesced, in block order.
@@ -1035,10 +1039,29 @@ __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, 
         S.last = atomicAdd(&P.rows[r].emit_done, 1u) == (uint32_t)(P.nblk - 1);
     __syncthreads();
     if (!S.last) return;
+    if constexpr (kAtt) {
+        // Attention blocks of the same launch take the emitted tokens from
+        // here on: their count is published, then `ready` rises to 3.
+        if (threadIdx.x == 0) {
+            const unsigned long long sl =
+                ld_agent(reinterpret_cast<const unsigned long long *>(&P.rows[r].slots));
+            st_agent(&P.rows[r].kept1, (uint32_t)(sl >> 32));
+            wait_vmem();
+            ctr_add(&P.rows[r].ready, 1u);
+        }
+    }
     resolve_row<kCount>(N, P, r, idx, count, kbr, S);
-    // Every block of the row has passed its waits: `ready` is reset for the
-    // next call (in the two-launch selection it already is).
-    if (threadIdx.x == 0) ctr_reset(&P.rows[r].ready);
+    if constexpr (kAtt) {
+        // The row's set and count are complete: `ready` rises to 4 (the
+        // row's last attention merge resets it for the next call).
+        wait_vmem();
+        __syncthreads();
+        if (threadIdx.x == 0) ctr_add(&P.rows[r].ready, 1u);
+    } else {
+        // Every block of the row has passed its waits: `ready` is reset for
+        // the next call (in the two-launch selection it already is).
+        if (threadIdx.x == 0) ctr_reset(&P.rows[r].ready);
+    }
 }
 
 template <bool kCount>
@@ -1196,6 +1219,721 @@ hipError_t launch_topk_select(const float *scores, int64_t R, int N, int k, int3
 {
     if (k >= N) return launch_keep_all(R, N, idx, count, keep_bits, stream);
     return launch_select<true>(scores, R, N, (double)k, idx, count, keep_bits, ws, stream);
+}
+
+// ---------------------------------- selection and attention in one launch
+//
+// The top-p set of each score row and exact attention over it (gist.science
+// summary, method sections 3 and 5), with the local heads over sinks +
+// window (section 1), in one launch.  Block rows [0, 2R) are the histogram
+// and emit blocks above, unchanged except that the row's last emit block
+// publishes the emitted count (`ready` 3) before it resolves and the
+// complete set (`ready` 4) after.  Block rows [2R, 2R + Ay) are A attention
+// blocks, dispatched after every histogram and emit block, so each of their
+// waits ends.  Two stages: 0, the tokens the emit blocks listed (known once
+// every row's emit blocks are done, while the resolves still run), and 1,
+// the tokens the resolves added.  A stage's tokens of all rows, in row
+// order, are cut into A equal contiguous ranges, one per block; the waves
+// of a block cut its range again.  A block leaves one partial (m, l, o) per
+// row its range touches; they merge in groups of 16 blocks (the group's
+// last arriver), then per row and stage, then the two stages of a row (the
+// second to arrive writes the output).  The last attention block to pass
+// its last wait resets every row's `ready` for the next call.
+// Between the stages the block runs its share of the local heads' tiles:
+// 64 sink/window rows of one local KV head for all its query heads, merged
+// by the tile of the (batch row, KV head) that arrives last.  Logits are in
+// log2 units (scale * log2(e) folded into q).
+
+namespace {
+
+constexpr int kAW = kSelThreads / kWave;  // waves per block
+constexpr int kAPF = 132;                 // floats per partial: m, l, pad, pad, o[128]
+constexpr int kARU = 8;                   // rows in flight per 16-lane group
+constexpr int kAGS = 16;                  // partials per group merge
+constexpr int kALT = 64;                  // local rows per tile
+constexpr int kAMH = 8;                   // query heads per KV head, at most
+constexpr int kALU = kALT / kAW;          // local rows per wave and tile
+
+struct AttSlots {  // per-wave partials of up to kAMH heads
+    float m[kAW][kAMH], l[kAW][kAMH];
+    float o[kAW][kAMH][128];
+};
+
+constexpr int kAMaxR = 1024;  // score rows of the launch, at most
+
+struct AttLds {
+    AttSlots s;
+    uint32_t len[kAMaxR];      // a stage's tokens per row
+    uint32_t off[kAMaxR];      // where they start in the row's idx list
+    uint32_t pre[kAMaxR + 1];  // their prefix sums
+    uint32_t uscan[kAW];
+    int last[kAMH];
+    int flag;
+};
+
+struct AttState {
+    float m, l, o[8];
+};
+
+__device__ __forceinline__ float att_rescale(float m_old, float m_new)
+{
+    return m_old == -INFINITY ? 0.0f : exp2f(m_old - m_new);
+}
+
+// Sum over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ float att_sum16(float v)
+{
+    v += dpp<kDppQuadXor1>(v, v);
+    v += dpp<kDppQuadXor2>(v, v);
+    v += dpp<kDppRowHalfMirror>(v, v);
+    v += dpp<kDppRowMirror>(v, v);
+    return v;
+}
+
+__device__ __forceinline__ void att_reset(AttState &a)
+{
+    a.m = -INFINITY;
+    a.l = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a.o[c] = 0.0f;
+}
+
+// This lane's 8 dimensions of a query row, times scale * log2(e).
+__device__ __forceinline__ void att_q8(const uint16_t *p, float qscale, float (&qf)[8])
+{
+    const uint4 w = *reinterpret_cast<const uint4 *>(p);
+    bf16x8_to_f32(w, qf);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qf[c] *= qscale;
+}
+
+// One online-softmax step of this lane's 16-lane group over rows tok[u] (a
+// negative token is no row); Kb/Vb point at the KV head's row 0 plus this
+// lane's 8 dimensions.
+__device__ __forceinline__ void att_rows(const uint16_t *__restrict__ Kb,
+                                         const uint16_t *__restrict__ Vb, const float (&qf)[8],
+                                         const int (&tok)[kARU], AttState &a)
+{
+    uint4 kw[kARU], vw[kARU];
+#pragma unroll
+    for (int u = 0; u < kARU; ++u) {
+        const int64_t off = tok[u] >= 0 ? (int64_t)tok[u] * 128 : 0;
+        kw[u] = ld_nt16(Kb + off);
+        vw[u] = ld_nt16(Vb + off);
+    }
+    float lg[kARU];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kARU; ++u) {
+        float kf[8];
+        bf16x8_to_f32(kw[u], kf);
+        float d = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) d = fmaf(qf[c], kf[c], d);
+        d = att_sum16(d);
+        lg[u] = tok[u] >= 0 ? d : -INFINITY;
+        mx = fmaxf(mx, lg[u]);
+    }
+    const float mn = fmaxf(a.m, mx);
+    if (mn == -INFINITY) return;
+    const float corr = att_rescale(a.m, mn);
+    a.l *= corr;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a.o[c] *= corr;
+#pragma unroll
+    for (int u = 0; u < kARU; ++u) {
+        const float pw = tok[u] >= 0 ? exp2f(lg[u] - mn) : 0.0f;
+        float vf[8];
+        bf16x8_to_f32(vw[u], vf);
+        a.l += pw;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a.o[c] = fmaf(pw, vf[c], a.o[c]);
+    }
+    a.m = mn;
+}
+
+// Merges the four 16-lane groups of the wave into the wave's slot for head
+// h.  Every lane of the wave calls it.
+__device__ __forceinline__ void att_flush(AttState &a, int w, int h, AttLds &S)
+{
+    const int lane = lane_id(), sub = lane & 15;
+#pragma unroll
+    for (int off = 16; off < kWave; off <<= 1) {
+        const float mo = __shfl_xor(a.m, off);
+        const float lo = __shfl_xor(a.l, off);
+        const float mn = fmaxf(a.m, mo);
+        const float fa = att_rescale(a.m, mn), fb = att_rescale(mo, mn);
+        a.l = a.l * fa + lo * fb;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float oo = __shfl_xor(a.o[c], off);
+            a.o[c] = a.o[c] * fa + oo * fb;
+        }
+        a.m = mn;
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) S.s.o[w][h][sub * 8 + c] = a.o[c];
+        if (lane == 0) {
+            S.s.l[w][h] = a.l;
+            S.s.m[w][h] = a.m;
+        }
+    }
+}
+
+// Merges the waves' slots of heads (or rows) hh < nh into one partial each
+// at dst + hh * hstride (agent-scope stores).  Thread t takes slot t / 128
+// and output dimension t % 128.
+__device__ __forceinline__ void att_slots_to_partial(int nh, float *dst, int64_t hstride,
+                                                     AttLds &S)
+{
+    const int hh = threadIdx.x >> 7, d = threadIdx.x & 127;
+    if (hh >= nh) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAW; ++w) M = fmaxf(M, S.s.m[w][hh]);
+    float L = 0.0f, O = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kAW; ++w) {
+            const float mw = S.s.m[w][hh];
+            if (mw != -INFINITY) {
+                const float f = exp2f(mw - M);
+                L = fmaf(S.s.l[w][hh], f, L);
+                O = fmaf(S.s.o[w][hh][d], f, O);
+            }
+        }
+    }
+    float *pp = dst + hh * hstride;
+    st_agent(pp + 4 + d, O);
+    if (d == 0) {
+        st_agent(pp, M);
+        st_agent(pp + 1, L);
+    }
+}
+
+// Merges n partials of each head hh < nh: partial (k, hh) at base + k *
+// kstride + hh * kAPF (agent-scope loads).  Writes the merged partial at
+// dst + hh * kAPF (agent-scope stores) or, with dst NULL, the normalised
+// output row at outp + hh * 128.
+__device__ __forceinline__ void att_merge(const float *base, int64_t kstride, int n, int nh,
+                                          float *dst, float *outp)
+{
+    const int hh = threadIdx.x >> 7, d = threadIdx.x & 127;
+    if (hh >= nh) return;
+    constexpr int kB = 8;
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    for (int k0 = 0; k0 < n; k0 += kB) {
+        float pm[kB], pl[kB], po[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const bool ok = k0 + u < n;
+            const float *pk = base + (int64_t)(ok ? k0 + u : k0) * kstride + hh * kAPF;
+            pm[u] = ok ? ld_agent(pk) : -INFINITY;
+            pl[u] = ld_agent(pk + 1);
+            po[u] = ld_agent(pk + 4 + d);
+        }
+        float mb = M;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) mb = fmaxf(mb, pm[u]);
+        if (mb == -INFINITY) continue;
+        const float cr = att_rescale(M, mb);
+        L *= cr;
+        O *= cr;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const float f = att_rescale(pm[u], mb);
+            L = f > 0.0f ? fmaf(pl[u], f, L) : L;
+            O = f > 0.0f ? fmaf(po[u], f, O) : O;
+        }
+        M = mb;
+    }
+    if (dst) {
+        float *pp = dst + hh * kAPF;
+        st_agent(pp + 4 + d, O);
+        if (d == 0) {
+            st_agent(pp, M);
+            st_agent(pp + 1, L);
+        }
+    } else {
+        outp[hh * 128 + d] = L > 0.0f ? O / L : 0.0f;
+    }
+}
+
+// After this block's agent-scope stores: counts the block on ctr and tells
+// every thread whether it was the last of `expected` (the last one resets
+// the counter for the next call).
+__device__ __forceinline__ bool att_arrive_last(unsigned long long *ctr, uint32_t expected,
+                                                AttLds &S)
+{
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const bool last = ctr_arrive(ctr) == expected - 1u;
+        if (last) ctr_reset(ctr);
+        S.flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    return S.flag != 0;
+}
+
+}  // namespace
+
+struct SelAttArgs {
+    const uint16_t *q, *K, *V;  // bf16: q [B][Hq][128]; K, V [B][Hkv][kv_cap][128]
+    float *out;                 // f32 [B][Hq][128]
+    int Hq, Hkv, H_r, G;        // score row b * H_r + h: query head h of batch row b
+    int64_t kv_cap;
+    float qscale;               // scale * log2(e)
+    int A;                      // attention blocks
+    int maxg;                   // group merges per row and stage, at most: ceil(A / kAGS)
+    int n_lkv;                  // local KV heads, after the H_r / G retrieval ones
+    int nl_rows, sink_end, w0;  // local rows: [0, sink_end), then [w0, N)
+    int nlt;                    // local tiles per (batch row, local KV head)
+    int n_items;                // local tiles in all
+    float *part;                // [R][2][A] block partials
+    float *gpart;               // [R][2][maxg] group merges
+    float *spart;               // [R][2] stage merges
+    unsigned long long *gctr;   // [R][2][maxg] tagged counters
+    unsigned long long *sctr;   // [R][2]
+    unsigned long long *fctr;   // [R]
+    unsigned long long *dctr;   // attention blocks past their last wait
+    float *lpart;               // [n_items][kAMH] local partials
+    unsigned long long *lctr;   // [B * n_lkv]
+};
+
+namespace {
+
+// Local tile `item`: rows [tile*kALT, +kALT) of the sink + window list of
+// local KV head gl of batch row bl, for its G query heads.  Lane group lg of
+// a wave takes query heads 2lg and 2lg + 1, so all four groups read the same
+// row.
+__device__ void att_local_tile(const SelAttArgs &A, int item, AttLds &S)
+{
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+    const int lg = lane >> 4, sub = lane & 15;
+    const int tile = item % A.nlt, rest = item / A.nlt;
+    const int gl = rest % A.n_lkv, bl = rest / A.n_lkv;
+    const int gk = A.H_r / A.G + gl;
+    const int p0 = tile * kALT, p1 = min(A.nl_rows, p0 + kALT);
+    const int ha = 2 * lg, hb = 2 * lg + 1;
+    const bool ua = ha < A.G, ub = hb < A.G;
+    float qa[8], qb[8];
+    const uint16_t *qrow = A.q + ((int64_t)bl * A.Hq + (int64_t)gk * A.G) * 128 + sub * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qa[c] = qb[c] = 0.0f;
+    if (ua) att_q8(qrow + ha * 128, A.qscale, qa);
+    if (ub) att_q8(qrow + hb * 128, A.qscale, qb);
+    const int64_t kvb = ((int64_t)bl * A.Hkv + gk) * A.kv_cap * 128 + sub * 8;
+    uint4 kw[kALU], vw[kALU];
+    bool ok[kALU];
+#pragma unroll
+    for (int u = 0; u < kALU; ++u) {
+        const int pos = p0 + w * kALU + u;
+        ok[u] = pos < p1;
+        const int tok = pos < A.sink_end ? pos : A.w0 + (pos - A.sink_end);
+        const int64_t off = ok[u] ? (int64_t)tok * 128 : 0;
+        kw[u] = ld_nt16(A.K + kvb + off);
+        vw[u] = ld_nt16(A.V + kvb + off);
+    }
+    AttState sa, sb;
+    att_reset(sa);
+    att_reset(sb);
+    float la[kALU], lb[kALU];
+    float ma = -INFINITY, mbx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kALU; ++u) {
+        float kf[8];
+        bf16x8_to_f32(kw[u], kf);
+        float da = 0.0f, db = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            da = fmaf(qa[c], kf[c], da);
+            db = fmaf(qb[c], kf[c], db);
+        }
+        da = att_sum16(da);
+        db = att_sum16(db);
+        la[u] = ok[u] ? da : -INFINITY;
+        lb[u] = ok[u] ? db : -INFINITY;
+        ma = fmaxf(ma, la[u]);
+        mbx = fmaxf(mbx, lb[u]);
+    }
+    sa.m = ma;
+    sb.m = mbx;
+#pragma unroll
+    for (int u = 0; u < kALU; ++u) {
+        const float pa = ok[u] && ma != -INFINITY ? exp2f(la[u] - ma) : 0.0f;
+        const float pb = ok[u] && mbx != -INFINITY ? exp2f(lb[u] - mbx) : 0.0f;
+        float vf[8];
+        bf16x8_to_f32(vw[u], vf);
+        sa.l += pa;
+        sb.l += pb;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            sa.o[c] = fmaf(pa, vf[c], sa.o[c]);
+            sb.o[c] = fmaf(pb, vf[c], sb.o[c]);
+        }
+    }
+    if (ua) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) S.s.o[w][ha][sub * 8 + c] = sa.o[c];
+        if (sub == 0) {
+            S.s.m[w][ha] = sa.m;
+            S.s.l[w][ha] = sa.l;
+        }
+    }
+    if (ub) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) S.s.o[w][hb][sub * 8 + c] = sb.o[c];
+        if (sub == 0) {
+            S.s.m[w][hb] = sb.m;
+            S.s.l[w][hb] = sb.l;
+        }
+    }
+    __syncthreads();
+    att_slots_to_partial(A.G, A.lpart + (int64_t)item * kAMH * kAPF, kAPF, S);
+    if (att_arrive_last(A.lctr + rest, (uint32_t)A.nlt, S)) {
+        float *outp = A.out + ((int64_t)bl * A.Hq + (int64_t)gk * A.G) * 128;
+        att_merge(A.lpart + (int64_t)rest * A.nlt * kAMH * kAPF, (int64_t)kAMH * kAPF, A.nlt, A.G,
+                  nullptr, outp);
+    }
+    __syncthreads();
+}
+
+// The block containing position x of a stage's T tokens: block a < A <= T
+// holds [T a / A, T (a + 1) / A), never empty.
+__device__ __forceinline__ int att_block_of(uint64_t x, uint64_t T, int A)
+{
+    return (int)(((x + 1) * (uint64_t)A - 1) / T);
+}
+
+// The last row r < R with pre[r] <= x (rows with no tokens are skipped).
+__device__ __forceinline__ int att_row_of(const uint32_t *pre, int R, uint32_t x)
+{
+    int lo = 0, hi = R - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Row r's partial of one stage is complete at spart: the second stage to
+// arrive merges both into the output.
+__device__ void att_stage_done(const SelAttArgs &A, const SelPtrs &P, int64_t r, AttLds &S)
+{
+    if (att_arrive_last(A.fctr + r, 2u, S)) {
+        const int b = (int)(r / A.H_r), h = (int)(r % A.H_r);
+        att_merge(A.spart + (int64_t)r * 2 * kAPF, kAPF, 2, 1, nullptr,
+                  A.out + ((int64_t)b * A.Hq + h) * 128);
+    }
+}
+
+// Stage ph of attention block a: its range of the stage's tokens, one
+// partial per row it touches, and the merges it is last for.
+__device__ void att_stage(const SelAttArgs &A, const SelPtrs &P, int R, int a, int ph, int N,
+                          const int32_t *__restrict__ idx, const int32_t *__restrict__ count,
+                          AttLds &S)
+{
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+    const int lg = lane >> 4, sub = lane & 15;
+    // Every row's tokens of this stage are listed: their counts.
+    for (int r = tid; r < R; r += kSelThreads) {
+        wait_row_ready(P.rows[r], 3u + (uint32_t)ph, P.wc);
+        const uint32_t k1 = min(ld_agent(&P.rows[r].kept1), (uint32_t)N);
+        uint32_t len = k1, off = 0;
+        if (ph) {
+            const uint32_t c = min(ld_agent(reinterpret_cast<const uint32_t *>(count + r)),
+                                   (uint32_t)N);
+            len = c > k1 ? c - k1 : 0u;
+            off = k1;
+        }
+        S.len[r] = len;
+        S.off[r] = off;
+    }
+    __syncthreads();
+    if (ph == 1) {
+        // Once every attention block has passed its last wait, the last of
+        // them resets every row's `ready` for the next call.
+        if (att_arrive_last(A.dctr, (uint32_t)A.A, S))
+            for (int r = tid; r < R; r += kSelThreads) ctr_reset(&P.rows[r].ready);
+    }
+    {
+        constexpr int kPer = kAMaxR / kSelThreads;
+        uint32_t loc = 0;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int r = tid * kPer + k;
+            loc += r < R ? S.len[r] : 0u;
+        }
+        uint32_t tot;
+        uint32_t run = block_exclusive_scan<kSelThreads, uint32_t>(loc, S.uscan, &tot);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int r = tid * kPer + k;
+            if (r < R) {
+                S.pre[r] = run;
+                run += S.len[r];
+            }
+        }
+        if (tid == 0) S.pre[R] = tot;
+    }
+    __syncthreads();
+    const uint64_t T = S.pre[R];
+    // Rows with no token in this stage: block r % A reports them.
+    for (int r = a; r < R; r += A.A) {
+        if (S.len[r] == 0u) {
+            if (tid < 128) st_agent(A.spart + ((int64_t)r * 2 + ph) * kAPF + 4 + tid, 0.0f);
+            if (tid == 0) {
+                st_agent(A.spart + ((int64_t)r * 2 + ph) * kAPF, -INFINITY);
+                st_agent(A.spart + ((int64_t)r * 2 + ph) * kAPF + 1, 0.0f);
+            }
+            att_stage_done(A, P, r, S);
+        }
+    }
+    // The first min(A, T) blocks take the tokens, so none of them is empty.
+    const int Ae = (int)min((uint64_t)A.A, T);
+    if (a >= Ae) return;
+    const uint32_t blo = (uint32_t)(T * (uint64_t)a / (uint64_t)Ae);
+    const uint32_t bhi = (uint32_t)(T * (uint64_t)(a + 1) / (uint64_t)Ae);
+    const int r_first = att_row_of(S.pre, R, blo), r_last = att_row_of(S.pre, R, bhi - 1);
+    // Rows in windows of kAMH: the waves cut the window's share of the range.
+    for (int rw = r_first; rw <= r_last; rw += kAMH) {
+        const int nr = min(kAMH, r_last + 1 - rw);
+        const uint32_t plo = max(blo, S.pre[rw]), phi = min(bhi, S.pre[rw + nr]);
+        if (tid < kAW * kAMH) {
+            S.s.m[tid / kAMH][tid % kAMH] = -INFINITY;
+            S.s.l[tid / kAMH][tid % kAMH] = 0.0f;
+        }
+        __syncthreads();
+        const uint32_t span = phi - plo;
+        const uint32_t wlo = plo + (uint32_t)((uint64_t)span * w / kAW);
+        const uint32_t whi = plo + (uint32_t)((uint64_t)span * (w + 1) / kAW);
+        int r = wlo < whi ? att_row_of(S.pre, R, wlo) : rw;
+        for (uint32_t x = wlo; x < whi;) {
+            while (S.pre[r + 1] <= x) ++r;
+            const uint32_t xe = min(whi, S.pre[r + 1]);
+            const int b = r / A.H_r, h = r % A.H_r, g = h / A.G;
+            float qf[8];
+            att_q8(A.q + ((int64_t)b * A.Hq + h) * 128 + sub * 8, A.qscale, qf);
+            const int64_t kvb = ((int64_t)b * A.Hkv + g) * A.kv_cap * 128 + sub * 8;
+            const uint32_t *ir =
+                reinterpret_cast<const uint32_t *>(idx + (int64_t)r * N) + S.off[r] - S.pre[r];
+            AttState st;
+            att_reset(st);
+            for (uint32_t k0 = x + (uint32_t)lg; k0 < xe; k0 += 4u * kARU) {
+                int tok[kARU];
+#pragma unroll
+                for (int u = 0; u < kARU; ++u) {
+                    const uint32_t k = k0 + 4u * (uint32_t)u;
+                    const uint32_t t = k < xe ? ld_agent(ir + k) : 0xFFFFFFFFu;
+                    tok[u] = t < (uint32_t)N ? (int)t : -1;
+                }
+                att_rows(A.K + kvb, A.V + kvb, qf, tok, st);
+            }
+            att_flush(st, w, r - rw, S);
+            x = xe;
+        }
+        __syncthreads();
+        att_slots_to_partial(nr, A.part + ((int64_t)rw * 2 + ph) * A.A * kAPF + (int64_t)a * kAPF,
+                             (int64_t)2 * A.A * kAPF, S);
+        // One arrival per row on its group counter (threads t < nr).
+        wait_vmem();
+        __syncthreads();
+        if (tid < nr) S.last[tid] = 0;
+        // (a row of the window with no token here was reported by block r % A)
+        if (tid < nr && S.len[rw + tid] > 0u) {
+            const int rr = rw + tid;
+            const int a0 = att_block_of(S.pre[rr], T, Ae);
+            const int a1 = att_block_of(S.pre[rr + 1] - 1u, T, Ae);
+            const int gi = (a - a0) / kAGS;
+            const int gn = min(kAGS, a1 - a0 + 1 - gi * kAGS);
+            unsigned long long *ctr = A.gctr + ((int64_t)rr * 2 + ph) * A.maxg + gi;
+            const bool lst = ctr_arrive(ctr) == (uint32_t)gn - 1u;
+            if (lst) ctr_reset(ctr);
+            S.last[tid] = lst ? 1 : 0;
+        }
+        __syncthreads();
+        for (int t = 0; t < nr; ++t) {
+            if (!S.last[t]) continue;
+            const int rr = rw + t;
+            const int a0 = att_block_of(S.pre[rr], T, Ae);
+            const int a1 = att_block_of(S.pre[rr + 1] - 1u, T, Ae);
+            const int gi = (a - a0) / kAGS;
+            const int gn = min(kAGS, a1 - a0 + 1 - gi * kAGS);
+            const int ng = (a1 - a0) / kAGS + 1;
+            const int64_t rs = (int64_t)rr * 2 + ph;
+            att_merge(A.part + (rs * A.A + a0 + gi * kAGS) * kAPF, kAPF, gn, 1,
+                      A.gpart + (rs * A.maxg + gi) * kAPF, nullptr);
+            if (att_arrive_last(A.sctr + rs, (uint32_t)ng, S)) {
+                att_merge(A.gpart + rs * A.maxg * kAPF, kAPF, ng, 1, A.spart + rs * kAPF, nullptr);
+                att_stage_done(A, P, rr, S);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+union SelAttShared {
+    ResShared r;
+    AttLds a;
+};
+
+}  // namespace
+
+// The selection (block rows [0, 2R)) and attention (rows [2R, 2R + Ay))
+// described above.
+__global__ __launch_bounds__(kSelThreads) void sel_attend_kernel(
+    const float *__restrict__ scores, int N, int R, SelPtrs P, double target,
+    int32_t *__restrict__ idx, int32_t *__restrict__ count, SelAttArgs A)
+{
+    __shared__ SelAttShared U;
+    const int blk = blockIdx.x;
+    if ((int)blockIdx.y < R) {
+        ResShared &S = U.r;
+        const int64_t r = blockIdx.y;
+        float v[kSelPerThread];
+        const ChunkView cv = load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);
+        if (blk == 0) clear_row(P, r);
+        hist_body<false>(v, cv, N, r, blk, P, reinterpret_cast<double *>(&S.buf[0][0]), S.etbl,
+                         S.red);
+        wait_vmem();
+        __syncthreads();
+        if (threadIdx.x == 0 &&
+            atomicAdd(&P.rows[r].hist_done, 1u) == (uint32_t)(P.nblk - 1))
+            ctr_add(&P.rows[r].ready, 1u);  // 2: the row's Hist1 is complete
+        return;
+    }
+    if ((int)blockIdx.y < 2 * R) {
+        ResShared &S = U.r;
+        const int64_t r = blockIdx.y - R;
+        float v[kSelPerThread];
+        const ChunkView cv = load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);
+        if (threadIdx.x == 0) wait_row_ready(P.rows[r], 2u, P.wc);
+        __syncthreads();
+        PickIn pi;
+        pick_inputs(P, r, pi);
+        emit_body<false, true>(v, cv, N, P, r, target, pi, idx, count, nullptr, S);
+        return;
+    }
+    AttLds &S = U.a;
+    const int a = ((int)blockIdx.y - 2 * R) * (int)gridDim.x + blk;
+    att_stage(A, P, R, a, 0, N, idx, count, S);
+    for (int it = a; it < A.n_items; it += A.A) att_local_tile(A, it, S);
+    att_stage(A, P, R, a, 1, N, idx, count, S);
+}
+
+struct SelAttGeom {
+    int64_t R;
+    int nblk, Ay, A, maxg, G, n_lkv, nl_rows, sink_end, w0, nlt, n_items;
+    size_t part, gpart, spart, gctr, sctr, fctr, dctr, lpart, lctr, total;
+};
+
+static SelAttGeom sel_att_geom(int cus, int B, int Hq, int Hkv, int N, int H_r, int n_sink,
+                               int window)
+{
+    SelAttGeom g;
+    g.R = (int64_t)B * H_r;
+    const SelLayout L = sel_layout(g.R, N);
+    g.nblk = (int)L.nblk;
+    g.Ay = (cus + g.nblk - 1) / g.nblk;
+    g.A = g.nblk * g.Ay;
+    g.maxg = (g.A + kAGS - 1) / kAGS;
+    g.G = Hq / Hkv;
+    g.n_lkv = Hkv - H_r / g.G;
+    const int w0 = N > window ? N - window : 0;
+    g.w0 = w0;
+    g.sink_end = n_sink < w0 ? n_sink : w0;
+    g.nl_rows = g.sink_end + (N - w0);
+    g.nlt = (g.nl_rows + kALT - 1) / kALT;
+    g.n_items = B * g.n_lkv * g.nlt;
+    size_t off = align_up(L.total, 256);
+    g.part = off;
+    off += align_up((size_t)g.R * 2 * g.A * kAPF * sizeof(float), 256);
+    g.gpart = off;
+    off += align_up((size_t)g.R * 2 * g.maxg * kAPF * sizeof(float), 256);
+    g.spart = off;
+    off += align_up((size_t)g.R * 2 * kAPF * sizeof(float), 256);
+    g.gctr = off;
+    off += align_up((size_t)g.R * 2 * g.maxg * 8, 256);
+    g.sctr = off;
+    off += align_up((size_t)g.R * 2 * 8, 256);
+    g.fctr = off;
+    off += align_up((size_t)g.R * 8, 256);
+    g.dctr = off;
+    off += 256;
+    g.lpart = off;
+    off += align_up((size_t)g.n_items * kAMH * kAPF * sizeof(float), 256);
+    g.lctr = off;
+    off += align_up((size_t)B * g.n_lkv * 8, 256);
+    g.total = off;
+    return g;
+}
+
+size_t topp_attend_ws_bytes(int cus, int B, int Hq, int Hkv, int N, int H_r, int n_sink,
+                            int window)
+{
+    const SelAttGeom g = sel_att_geom(cus, B, Hq, Hkv, N, H_r, n_sink, window);
+    const size_t att = attend_ws_bytes(B, H_r, Hq - H_r, N);  // the p >= 1 path
+    return g.total > att ? g.total : att;
+}
+
+bool topp_attend_fits(int cus, int B, int Hq, int Hkv, int N, int H_r, int n_sink, int window)
+{
+    const SelAttGeom g = sel_att_geom(cus, B, Hq, Hkv, N, H_r, n_sink, window);
+    return g.G <= kAMH && H_r % g.G == 0 && g.R <= kAMaxR && 2 * g.R + g.Ay <= kMaxFusedRows;
+}
+
+hipError_t launch_topp_attend(const float *scores, const uint16_t *q, const uint16_t *K,
+                              const uint16_t *V, int B, int Hq, int Hkv, int N, int64_t kv_cap,
+                              int H_r, int n_sink, int window, float p, float scale, float *out,
+                              int32_t *idx, int32_t *count, void *ws, hipStream_t stream)
+{
+    int cus = 0;
+    RTP_TRY(device_cus(&cus));
+    if (p >= 1.0f) {
+        // Every token is kept: the listing, then the attention launch.
+        RTP_TRY(launch_keep_all((int64_t)B * H_r, N, idx, count, nullptr, stream));
+        return launch_decode_attend(q, K, V, idx, count, B, Hq, Hkv, N, kv_cap, 0, H_r, H_r,
+                                    Hq - H_r, n_sink, window, scale, out, ws, stream);
+    }
+    const SelAttGeom g = sel_att_geom(cus, B, Hq, Hkv, N, H_r, n_sink, window);
+    SelPtrs P = sel_ptrs(ws, g.R, N);
+    RTP_TRY(wait_ctl(&P.wc));
+    char *base = static_cast<char *>(ws);
+    SelAttArgs A;
+    A.q = q;
+    A.K = K;
+    A.V = V;
+    A.out = out;
+    A.Hq = Hq;
+    A.Hkv = Hkv;
+    A.H_r = H_r;
+    A.G = g.G;
+    A.kv_cap = kv_cap;
+    A.qscale = scale * 1.4426950408889634f;
+    A.A = g.A;
+    A.maxg = g.maxg;
+    A.n_lkv = g.n_lkv;
+    A.nl_rows = g.nl_rows;
+    A.sink_end = g.sink_end;
+    A.w0 = g.w0;
+    A.nlt = g.nlt;
+    A.n_items = g.n_items;
+    A.part = reinterpret_cast<float *>(base + g.part);
+    A.gpart = reinterpret_cast<float *>(base + g.gpart);
+    A.spart = reinterpret_cast<float *>(base + g.spart);
+    A.gctr = reinterpret_cast<unsigned long long *>(base + g.gctr);
+    A.sctr = reinterpret_cast<unsigned long long *>(base + g.sctr);
+    A.fctr = reinterpret_cast<unsigned long long *>(base + g.fctr);
+    A.dctr = reinterpret_cast<unsigned long long *>(base + g.dctr);
+    A.lpart = reinterpret_cast<float *>(base + g.lpart);
+    A.lctr = reinterpret_cast<unsigned long long *>(base + g.lctr);
+    return launch(sel_attend_kernel, dim3((unsigned)g.nblk, (unsigned)(2 * g.R + g.Ay)),
+                  dim3(kSelThreads), 0, stream, scores, N, (int)g.R, P, (double)p, idx, count, A);
 }
 
 }  // namespace rtp

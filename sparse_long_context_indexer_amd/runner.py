@@ -14,7 +14,7 @@ from . import (RTP_WS_DECODE_ATTEND, RTP_WS_LOCAL_DECODE, RTP_WS_SPARSE_DECODE,
                RTP_WS_SPARSE_UNION, RTP_WS_TOPP_SELECT, decode_layer_workspace_size, keep_words,
                rtp_decode_attend, rtp_decode_layer, rtp_index_scores, rtp_index_scores_bf16,
                rtp_local_decode, rtp_scan_local, rtp_sparse_decode, rtp_sparse_decode_union,
-               rtp_topp_select, workspace_size)
+               rtp_topp_attend, rtp_topp_select, topp_attend_workspace_size, workspace_size)
 
 
 class DecodeLayer:
@@ -27,12 +27,13 @@ class DecodeLayer:
     and the sparse heads run rtp_sparse_decode_union (each kept row read once
     per KV head); mode "layer": the whole layer in one rtp_decode_layer launch
     (scores kept on chip; with keep_scores they are also written out, for
-    checking)."""
+    checking); mode "topp_attend": the scan, then one rtp_topp_attend launch
+    for the selection and every head's attention."""
 
     def __init__(self, B: int, Hq: int, Hkv: int, N: int, H_r: int, n_sink: int,
                  window: int, device, d: int = 128, mode: str = "fused",
                  keep_scores: bool = True):
-        if mode not in ("fused", "scan_local", "union", "per_head", "layer"):
+        if mode not in ("fused", "scan_local", "union", "per_head", "layer", "topp_attend"):
             raise ValueError(f"unknown mode {mode!r}")
         self.keep_scores = keep_scores
         self.B, self.Hq, self.Hkv, self.N, self.H_r = B, Hq, Hkv, N, H_r
@@ -49,6 +50,16 @@ class DecodeLayer:
             self.count = torch.empty((B, H_r), dtype=torch.int32, device=dev)
             self.ws_layer = torch.empty(
                 decode_layer_workspace_size(B, Hq, Hkv, N, H_r, n_sink, window),
+                dtype=torch.uint8, device=dev)
+            return
+        if mode == "topp_attend":
+            if H_r < 1:
+                raise ValueError("mode 'topp_attend' needs retrieval heads")
+            self.scores = torch.empty((B, H_r, N), dtype=torch.float32, device=dev)
+            self.idx = torch.empty((B, H_r, N), dtype=torch.int32, device=dev)
+            self.count = torch.empty((B, H_r), dtype=torch.int32, device=dev)
+            self.ws_ta = torch.empty(
+                topp_attend_workspace_size(B, Hq, Hkv, N, H_r, n_sink, window),
                 dtype=torch.uint8, device=dev)
             return
         if H_r > 0:
@@ -114,6 +125,11 @@ class DecodeLayer:
             rtp_decode_layer(q_r, k_r, q, K, V, self.N, self.H_r, self.n_sink, self.window, p,
                              scale, out, self.idx, self.count, self.ws_layer,
                              scores=self.scores)
+            return
+        if self.mode == "topp_attend":
+            self.scan(q_r, k_r)
+            rtp_topp_attend(self.scores, q, K, V, self.n_sink, self.window, p, scale, out,
+                            self.idx, self.count, self.ws_ta)
             return
         if self.mode == "scan_local" and self.H_r > 0 and self.H_l > 0:
             if k_r.dtype != torch.float32:

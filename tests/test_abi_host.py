@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     assert sorted(rtp.SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -388,6 +388,45 @@ def test_decode_layer_validation(lib):
         rtp.decode_layer_workspace_size(1, 32, 4, 0, 8, 4, 4096)
     assert e.value.status == 2
     assert lib.rtp_decode_layer_workspace_size(1, 32, 4, 100, 8, 4, 4096, None) == 1
+
+
+def test_topp_attend_validation(lib):
+    # Host-side checks of rtp_topp_attend, in order: NULL, unsupported
+    # dimensions, sizes, values, alignment; all before any device query.
+    f = lib.rtp_topp_attend
+    pos = {"scores": 0, "q": 1, "K": 2, "V": 3, "B": 4, "Hq": 5, "Hkv": 6, "N": 7,
+           "kv_cap": 8, "d": 9, "Hq_r": 10, "sink": 11, "win": 12, "p": 13, "scale": 14,
+           "out": 15, "idx": 16, "count": 17, "ws": 18, "wsb": 19}
+    args = [A, A, A, A, 1, 32, 4, 1000, 1000, 128, 8, 4, 4096, 0.9, 0.088, A, A, A, A, 1 << 30,
+            None]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    for name in ("scores", "q", "K", "V", "out", "idx", "count", "ws"):
+        assert call(**{name: None}) == 1, name
+    assert call(d=64) == 3
+    assert call(N=0) == 2 and call(kv_cap=999) == 2
+    assert call(B=0) == 2 and call(Hkv=3) == 2 and call(Hq_r=0) == 2 and call(Hq_r=33) == 2
+    assert call(Hq_r=12) == 2                   # not whole KV heads (G = 8)
+    assert call(Hkv=2, Hq_r=16) == 3            # G = 16: more than 8 heads per KV head
+    assert call(B=129) == 3                     # more than 1024 score rows
+    assert call(N=1 << 30, kv_cap=1 << 30) == 3  # B * Hq_r * N beyond 32 bits
+    assert call(sink=-1) == 4 and call(win=0) == 4
+    for p in (0.0, -0.1, 1.01, float("nan")):
+        assert call(p=p) == 4, p
+    assert call(scale=float("nan")) == 4
+    assert call(scores=A + 2) == 5 and call(K=A + 8) == 5 and call(ws=A + 16) == 5
+    assert call(idx=A + 2) == 5
+    # With every head a retrieval head, n_sink and window are not checked.
+    assert call(Hq_r=32, sink=-1, win=0, q=A + 4) == 5
+    with pytest.raises(rtp.RtpError) as e:
+        rtp.topp_attend_workspace_size(1, 32, 4, 0, 8, 4, 4096)
+    assert e.value.status == 2
+    assert lib.rtp_topp_attend_workspace_size(1, 32, 4, 100, 8, 4, 4096, None) == 1
 
 
 def test_wait_limit_and_status_entry_points(lib):
