@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
 // --------------------------------------------------------------- emit
 
 struct ResShared;
-template <bool kCount>
+template <bool kCount, bool kVis = false>
 __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
                             uint32_t *kbr, ResShared &S);
 
@@ -585,13 +585,17 @@ __device__ void res_choose_count(uint32_t c, int nb, ResShared &S)
     }
 }
 
-// Appends token i to the row's kept list at slot pa (an agent-scope store:
-// attention blocks of the same launch may read it) and, when the row has a
-// keep bitmap, sets its bit (the emit blocks wrote the bitmap's words with
-// agent-scope stores before the resolve started).
+// Appends token i to the row's kept list at slot pa (with kVis an
+// agent-scope store: other blocks of the same launch read it) and, when the
+// row has a keep bitmap, sets its bit (the emit blocks wrote the bitmap's
+// words with agent-scope stores before the resolve started).
+template <bool kVis>
 __device__ __forceinline__ void keep_token(int32_t *ir, int64_t pa, uint32_t i, uint32_t *kbr)
 {
-    st_agent(reinterpret_cast<uint32_t *>(ir + pa), i);
+    if constexpr (kVis)
+        st_agent(reinterpret_cast<uint32_t *>(ir + pa), i);
+    else
+        ir[pa] = (int32_t)i;
     if (kbr) atomicOr(kbr + (i >> 5), 1u << (i & 31u));
 }
 
@@ -600,6 +604,7 @@ __device__ __forceinline__ uint32_t *nout_ptr(ResShared &S) { return reinterpret
 
 // Ordered in-place filter for candidates in global memory (see the header
 // comment); survivors keep their relative order.
+template <bool kVis>
 __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t mask,
                                      uint32_t keep_digit, bool emit_above, bool by_index,
                                      int32_t *ir, uint32_t *kbr, ResShared &S)
@@ -614,7 +619,7 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
         const bool out = valid && (emit_above ? dg > keep_digit : dg < keep_digit);
         const bool keep = valid && dg == keep_digit;
         const int64_t pa = wave_append(out, nout_ptr(S));
-        if (pa >= 0) keep_token(ir, pa, e.y, kbr);
+        if (pa >= 0) keep_token<kVis>(ir, pa, e.y, kbr);
         uint32_t tot;
         const uint32_t pos = block_exclusive_scan<kResThreads>((uint32_t)keep, S.uscan, &tot);
         // All reads of this chunk are done (the scan synchronised the block),
@@ -635,7 +640,7 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
 // With acc_next, the moved candidates' histogram over key bits [9:0]
 // (mass exp(s - M) and count) is built in S.hm / S.hc on the way, for the
 // next score level.
-template <bool kGlobal, bool kCount>
+template <bool kGlobal, bool kCount, bool kVis = false>
 __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int shift,
                                    uint32_t mask, uint32_t j, bool emit_above, bool by_index,
                                    int32_t *ir, uint32_t *kbr, ResShared &S,
@@ -680,7 +685,7 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
         uint32_t pk = (uint32_t)(base >> 32) + (ex >> 16);
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-            if (outm & (1u << u)) keep_token(ir, pa++, e[u].y, kbr);
+            if (outm & (1u << u)) keep_token<kVis>(ir, pa++, e[u].y, kbr);
             if (keepm & (1u << u)) {
                 dst[pk++] = e[u];
                 if (acc_next) {
@@ -700,7 +705,7 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
 // ascending: the order of the sorted definition), the masses exp(s - M) are
 // laid out in rank order and prefix-summed from A, and the wave keeps the
 // shortest rank prefix whose running mass reaches T (all n if none does).
-template <bool kCount>
+template <bool kCount, bool kVis = false>
 __device__ void resolve_few(const uint2 *cr, int n, double A, double T, double M, int32_t *ir,
                             uint32_t *kbr, ResShared &S)
 {
@@ -722,10 +727,10 @@ __device__ void resolve_few(const uint2 *cr, int n, double A, double T, double M
     const uint64_t hit = __ballot(v && cum >= T);
     const int last = hit ? __ffsll((unsigned long long)hit) - 1 : n - 1;
     const int64_t pa = wave_append(v && rank <= last, nout_ptr(S));
-    if (pa >= 0) keep_token(ir, pa, e.y, kbr);
+    if (pa >= 0) keep_token<kVis>(ir, pa, e.y, kbr);
 }
 
-template <bool kCount>
+template <bool kCount, bool kVis>
 __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
                             uint32_t *kbr, ResShared &S)
 {
@@ -779,7 +784,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
         const uint32_t j = S.j;
         A = S.abefore;  // A plus the mass of the digits above j
         if (in_lds) {
-            n = res_filter_lds<false, kCount>(S.buf[cur], n, S.buf[cur ^ 1], shift, kDig - 1, j, true,
+            n = res_filter_lds<false, kCount, kVis>(S.buf[cur], n, S.buf[cur ^ 1], shift, kDig - 1, j, true,
                                       false, ir, kbr, S);
             cur ^= 1;
             cr = S.buf[cur];
@@ -789,19 +794,19 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
             // wave can finish them.
             few = S.hc[j] <= (uint32_t)kWave;
             next_built = level == 0 && !few;
-            n = res_filter_lds<true, kCount>(gc, n, S.buf[0], shift, kDig - 1, j, true, false, ir, kbr, S,
+            n = res_filter_lds<true, kCount, kVis>(gc, n, S.buf[0], shift, kDig - 1, j, true, false, ir, kbr, S,
                                      next_built, M);
             few = few && n <= kWave;
             in_lds = true;
             cur = 0;
             cr = S.buf[0];
         } else {
-            n = res_filter_global(gc, n, shift, kDig - 1, j, true, false, ir, kbr, S);
+            n = res_filter_global<kVis>(gc, n, shift, kDig - 1, j, true, false, ir, kbr, S);
         }
     }
 
     if (few) {
-        if (tid < kWave) resolve_few<kCount>(cr, (int)n, A, T, M, ir, kbr, S);
+        if (tid < kWave) resolve_few<kCount, kVis>(cr, (int)n, A, T, M, ir, kbr, S);
     } else if (n > 0) {
         // Every survivor now has the same score tau.  Keep the first c of
         // them in index order: the smallest c with A + c * e_tau >= T.
@@ -823,7 +828,7 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
                 const bool valid = k < n;
                 const uint32_t ix = valid ? cand(k).y : 0u;
                 const int64_t pa = wave_append(valid, nout_ptr(S));
-                if (pa >= 0) keep_token(ir, pa, ix, kbr);
+                if (pa >= 0) keep_token<kVis>(ir, pa, ix, kbr);
             }
         } else {
             // Count-only radix select of the c lowest indices: bits [30:20],
@@ -845,26 +850,31 @@ __device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *
                 const uint32_t j = S.j;
                 c -= S.cbefore;
                 if (in_lds) {
-                    n = res_filter_lds<false, kCount>(S.buf[cur], n, S.buf[cur ^ 1], shift, mask, j,
+                    n = res_filter_lds<false, kCount, kVis>(S.buf[cur], n, S.buf[cur ^ 1], shift, mask, j,
                                               false, true, ir, kbr, S);
                     cur ^= 1;
                     cr = S.buf[cur];
                 } else if (S.hc[j] <= (uint32_t)kResCap) {
-                    n = res_filter_lds<true, kCount>(gc, n, S.buf[0], shift, mask, j, false, true, ir,
+                    n = res_filter_lds<true, kCount, kVis>(gc, n, S.buf[0], shift, mask, j, false, true, ir,
                                              kbr, S);
                     in_lds = true;
                     cur = 0;
                     cr = S.buf[0];
                 } else {
-                    n = res_filter_global(gc, n, shift, mask, j, false, true, ir, kbr, S);
+                    n = res_filter_global<kVis>(gc, n, shift, mask, j, false, true, ir, kbr, S);
                 }
             }
             // One token left (its index is fully determined): keep it.
-            if (tid == 0 && n > 0 && c > 0) keep_token(ir, (uint32_t)S.nn++, cand(0).y, kbr);
+            if (tid == 0 && n > 0 && c > 0) keep_token<kVis>(ir, (uint32_t)S.nn++, cand(0).y, kbr);
         }
     }
     __syncthreads();
-    if (tid == 0) st_agent(reinterpret_cast<uint32_t *>(count + r), emitted + (uint32_t)S.nn);
+    if (tid == 0) {
+        if constexpr (kVis)
+            st_agent(reinterpret_cast<uint32_t *>(count + r), emitted + (uint32_t)S.nn);
+        else
+            count[r] = (int32_t)(emitted + (uint32_t)S.nn);
+    }
 }
 
 // What the pick reads of the row: this thread's Hist1 bins and the top
@@ -894,11 +904,19 @@ __device__ __forceinline__ void pick_inputs(SelPtrs P, int64_t r, PickIn &pi)
 // pi): the row's threshold, the chunk's kept tokens and boundary-bin
 // candidates, its share of Hist2; the last chunk of the row to finish
 // resolves the boundary bin.
+struct SelAttArgs;
+// The emit block's part in the selection-and-attention launch (defined with
+// that launch below).
+__device__ void emit_attend(const SelAttArgs &A, const SelPtrs &P, int64_t r, int N,
+                            int32_t *__restrict__ idx, int32_t *__restrict__ count,
+                            uint32_t above, uint32_t ex, const ChunkView &cv, ResShared &S);
+
 template <bool kCount, bool kAtt = false>
 __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, int N,
                           SelPtrs P, int64_t r, double target, const PickIn &pi,
                           int32_t *__restrict__ idx, int32_t *__restrict__ count,
-                          uint32_t *__restrict__ keep_bits, ResShared &S)
+                          uint32_t *__restrict__ keep_bits, ResShared &S,
+                          const SelAttArgs *att = nullptr)
 {
     static_assert(kSelThreads == kResThreads, "the last emit block runs the resolve");
     unsigned long long *wbase = S.wbase;
@@ -1002,9 +1020,7 @@ __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, 
     __syncthreads();
     const unsigned long long base = S.gbase + wbase[w];
     uint32_t oa = (uint32_t)(base >> 32) + (ex >> 16);
-    // Agent-scope stores: attention blocks of the same launch may read them.
-    for (uint32_t m = above; m; m &= m - 1)
-        st_agent(reinterpret_cast<uint32_t *>(ir + oa++), cv.index32(__ffs(m) - 1));
+    for (uint32_t m = above; m; m &= m - 1) ir[oa++] = (int32_t)cv.index32(__ffs(m) - 1);
     uint2 *gcb = cr + (uint32_t)S.gbase;  // this block's candidates' place in the row
     if (staged) {
         // Written out coalesced, in block order.
@@ -1038,30 +1054,15 @@ __device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, 
     if (threadIdx.x == 0)
         S.last = atomicAdd(&P.rows[r].emit_done, 1u) == (uint32_t)(P.nblk - 1);
     __syncthreads();
+    if constexpr (kAtt) {
+        emit_attend(*att, P, r, N, idx, count, above, ex, cv, S);
+        return;
+    }
     if (!S.last) return;
-    if constexpr (kAtt) {
-        // Attention blocks of the same launch take the emitted tokens from
-        // here on: their count is published, then `ready` rises to 3.
-        if (threadIdx.x == 0) {
-            const unsigned long long sl =
-                ld_agent(reinterpret_cast<const unsigned long long *>(&P.rows[r].slots));
-            st_agent(&P.rows[r].kept1, (uint32_t)(sl >> 32));
-            wait_vmem();
-            ctr_add(&P.rows[r].ready, 1u);
-        }
-    }
     resolve_row<kCount>(N, P, r, idx, count, kbr, S);
-    if constexpr (kAtt) {
-        // The row's set and count are complete: `ready` rises to 4 (the
-        // row's last attention merge resets it for the next call).
-        wait_vmem();
-        __syncthreads();
-        if (threadIdx.x == 0) ctr_add(&P.rows[r].ready, 1u);
-    } else {
-        // Every block of the row has passed its waits: `ready` is reset for
-        // the next call (in the two-launch selection it already is).
-        if (threadIdx.x == 0) ctr_reset(&P.rows[r].ready);
-    }
+    // Every block of the row has passed its waits: `ready` is reset for the
+    // next call (in the two-launch selection it already is).
+    if (threadIdx.x == 0) ctr_reset(&P.rows[r].ready);
 }
 
 template <bool kCount>
@@ -1225,24 +1226,22 @@ hipError_t launch_topk_select(const float *scores, int64_t R, int N, int k, int3
 //
 // The top-p set of each score row and exact attention over it (gist.science
 // summary, method sections 3 and 5), with the local heads over sinks +
-// window (section 1), in one launch.  Block rows [0, 2R) are the histogram
-// and emit blocks above, unchanged except that the row's last emit block
-// publishes the emitted count (`ready` 3) before it resolves and the
-// complete set (`ready` 4) after.  Block rows [2R, 2R + Ay) are A attention
-// blocks, dispatched after every histogram and emit block, so each of their
-// waits ends.  Two stages: 0, the tokens the emit blocks listed (known once
-// every row's emit blocks are done, while the resolves still run), and 1,
-// the tokens the resolves added.  A stage's tokens of all rows, in row
-// order, are cut into A equal contiguous ranges, one per block; the waves
-// of a block cut its range again.  A block leaves one partial (m, l, o) per
-// row its range touches; they merge in groups of 16 blocks (the group's
-// last arriver), then per row and stage, then the two stages of a row (the
-// second to arrive writes the output).  The last attention block to pass
-// its last wait resets every row's `ready` for the next call.
-// Between the stages the block runs its share of the local heads' tiles:
-// 64 sink/window rows of one local KV head for all its query heads, merged
-// by the tile of the (batch row, KV head) that arrives last.  Logits are in
-// log2 units (scale * log2(e) folded into q).
+// window (section 1), in the selection's own launch.  The histogram blocks
+// are those above.  Each emit block, once it has counted itself done:
+//   - if it is the row's last, resolves the boundary bin first (the kept
+//     tokens and the count with agent-scope stores) and raises `ready` to 3;
+//   - attends the tokens it emitted itself, from an LDS copy of its own
+//     list (no memory round trip), while the row's resolve runs;
+//   - waits for the row's resolve and attends its share (1/nblk) of the
+//     tokens the resolve added;
+//   - takes local tiles from a shared queue until none is left: 64
+//     sink/window rows of one local KV head for all its query heads, merged
+//     by the tile of the (batch row, KV head) that arrives last.
+// Every emit block thus leaves two partials (m, l, o) per row; they merge in
+// groups of 16 (the group's last arriver), then per row (the last group
+// merger writes the output and resets the row's `ready`).  Every wait is on
+// the row's last emit block, which is already running when it is waited
+// on.  Logits are in log2 units (scale * log2(e) folded into q).
 
 namespace {
 
@@ -1254,22 +1253,28 @@ constexpr int kALT = 64;                  // local rows per tile
 constexpr int kAMH = 8;                   // query heads per KV head, at most
 constexpr int kALU = kALT / kAW;          // local rows per wave and tile
 
-struct AttSlots {  // per-wave partials of up to kAMH heads
-    float m[kAW][kAMH], l[kAW][kAMH];
-    float o[kAW][kAMH][128];
+// Per-wave partial slots in LDS for nh heads: m[w * nh + h], l likewise,
+// o[(w * nh + h) * 128 + d].
+struct SlotView {
+    float *m, *l, *o;
+    int nh;
 };
 
-constexpr int kAMaxR = 1024;  // score rows of the launch, at most
+// Slots for one head in the resolve's digit histogram (free by then).
+__device__ __forceinline__ SlotView slots_one(ResShared &S)
+{
+    static_assert(sizeof(S.hm) >= sizeof(float) * kAW * (2 + 128), "one head's slots fit");
+    float *f = reinterpret_cast<float *>(&S.hm[0]);
+    return SlotView{f, f + kAW, f + 2 * kAW, 1};
+}
 
-struct AttLds {
-    AttSlots s;
-    uint32_t len[kAMaxR];      // a stage's tokens per row
-    uint32_t off[kAMaxR];      // where they start in the row's idx list
-    uint32_t pre[kAMaxR + 1];  // their prefix sums
-    uint32_t uscan[kAW];
-    int last[kAMH];
-    int flag;
-};
+// Slots for kAMH heads in the candidate buffers (free by then).
+__device__ __forceinline__ SlotView slots_heads(ResShared &S)
+{
+    static_assert(sizeof(S.buf) >= sizeof(float) * kAW * kAMH * (2 + 128), "the slots fit");
+    float *f = reinterpret_cast<float *>(&S.buf[0][0]);
+    return SlotView{f, f + kAW * kAMH, f + 2 * kAW * kAMH, kAMH};
+}
 
 struct AttState {
     float m, l, o[8];
@@ -1354,7 +1359,7 @@ __device__ __forceinline__ void att_rows(const uint16_t *__restrict__ Kb,
 
 // Merges the four 16-lane groups of the wave into the wave's slot for head
 // h.  Every lane of the wave calls it.
-__device__ __forceinline__ void att_flush(AttState &a, int w, int h, AttLds &S)
+__device__ __forceinline__ void att_flush(AttState &a, int w, int h, const SlotView &v)
 {
     const int lane = lane_id(), sub = lane & 15;
 #pragma unroll
@@ -1371,36 +1376,37 @@ __device__ __forceinline__ void att_flush(AttState &a, int w, int h, AttLds &S)
         }
         a.m = mn;
     }
+    const int s = w * v.nh + h;
     if (lane < 16) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) S.s.o[w][h][sub * 8 + c] = a.o[c];
+        for (int c = 0; c < 8; ++c) v.o[s * 128 + sub * 8 + c] = a.o[c];
         if (lane == 0) {
-            S.s.l[w][h] = a.l;
-            S.s.m[w][h] = a.m;
+            v.l[s] = a.l;
+            v.m[s] = a.m;
         }
     }
 }
 
-// Merges the waves' slots of heads (or rows) hh < nh into one partial each
-// at dst + hh * hstride (agent-scope stores).  Thread t takes slot t / 128
-// and output dimension t % 128.
-__device__ __forceinline__ void att_slots_to_partial(int nh, float *dst, int64_t hstride,
-                                                     AttLds &S)
+// Merges the waves' slots of heads hh < nh into one partial each at dst +
+// hh * hstride (agent-scope stores).  Thread t takes head t / 128 and output
+// dimension t % 128.
+__device__ __forceinline__ void att_slots_to_partial(int nh, const SlotView &v, float *dst,
+                                                     int64_t hstride)
 {
     const int hh = threadIdx.x >> 7, d = threadIdx.x & 127;
     if (hh >= nh) return;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAW; ++w) M = fmaxf(M, S.s.m[w][hh]);
+    for (int w = 0; w < kAW; ++w) M = fmaxf(M, v.m[w * v.nh + hh]);
     float L = 0.0f, O = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < kAW; ++w) {
-            const float mw = S.s.m[w][hh];
+            const float mw = v.m[w * v.nh + hh];
             if (mw != -INFINITY) {
                 const float f = exp2f(mw - M);
-                L = fmaf(S.s.l[w][hh], f, L);
-                O = fmaf(S.s.o[w][hh][d], f, O);
+                L = fmaf(v.l[w * v.nh + hh], f, L);
+                O = fmaf(v.o[(w * v.nh + hh) * 128 + d], f, O);
             }
         }
     }
@@ -1462,19 +1468,19 @@ __device__ __forceinline__ void att_merge(const float *base, int64_t kstride, in
 
 // After this block's agent-scope stores: counts the block on ctr and tells
 // every thread whether it was the last of `expected` (the last one resets
-// the counter for the next call).
+// the counter for the next call).  `flag` is an LDS word.
 __device__ __forceinline__ bool att_arrive_last(unsigned long long *ctr, uint32_t expected,
-                                                AttLds &S)
+                                                int &flag)
 {
     wait_vmem();
     __syncthreads();
     if (threadIdx.x == 0) {
         const bool last = ctr_arrive(ctr) == expected - 1u;
         if (last) ctr_reset(ctr);
-        S.flag = last ? 1 : 0;
+        flag = last ? 1 : 0;
     }
     __syncthreads();
-    return S.flag != 0;
+    return flag != 0;
 }
 
 }  // namespace
@@ -1485,21 +1491,19 @@ struct SelAttArgs {
     int Hq, Hkv, H_r, G;        // score row b * H_r + h: query head h of batch row b
     int64_t kv_cap;
     float qscale;               // scale * log2(e)
-    int A;                      // attention blocks
-    int maxg;                   // group merges per row and stage, at most: ceil(A / kAGS)
+    int ng;                     // group merges per row: ceil(2 nblk / kAGS)
+    int nE;                     // emit blocks: R * nblk
     int n_lkv;                  // local KV heads, after the H_r / G retrieval ones
     int nl_rows, sink_end, w0;  // local rows: [0, sink_end), then [w0, N)
     int nlt;                    // local tiles per (batch row, local KV head)
     int n_items;                // local tiles in all
-    float *part;                // [R][2][A] block partials
-    float *gpart;               // [R][2][maxg] group merges
-    float *spart;               // [R][2] stage merges
-    unsigned long long *gctr;   // [R][2][maxg] tagged counters
-    unsigned long long *sctr;   // [R][2]
-    unsigned long long *fctr;   // [R]
-    unsigned long long *dctr;   // attention blocks past their last wait
+    float *part;                // [R][2 nblk] block partials
+    float *gpart;               // [R][ng] group merges
+    unsigned long long *gctr;   // [R][ng] tagged counters
+    unsigned long long *rctr;   // [R]
     float *lpart;               // [n_items][kAMH] local partials
     unsigned long long *lctr;   // [B * n_lkv]
+    unsigned long long *lq;     // the local tiles' queue
 };
 
 namespace {
@@ -1508,7 +1512,7 @@ namespace {
 // local KV head gl of batch row bl, for its G query heads.  Lane group lg of
 // a wave takes query heads 2lg and 2lg + 1, so all four groups read the same
 // row.
-__device__ void att_local_tile(const SelAttArgs &A, int item, AttLds &S)
+__device__ void att_local_tile(const SelAttArgs &A, int item, const SlotView &v, int &flag)
 {
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int lg = lane >> 4, sub = lane & 15;
@@ -1575,24 +1579,26 @@ __device__ void att_local_tile(const SelAttArgs &A, int item, AttLds &S)
         }
     }
     if (ua) {
+        const int s = w * v.nh + ha;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) S.s.o[w][ha][sub * 8 + c] = sa.o[c];
+        for (int c = 0; c < 8; ++c) v.o[s * 128 + sub * 8 + c] = sa.o[c];
         if (sub == 0) {
-            S.s.m[w][ha] = sa.m;
-            S.s.l[w][ha] = sa.l;
+            v.m[s] = sa.m;
+            v.l[s] = sa.l;
         }
     }
     if (ub) {
+        const int s = w * v.nh + hb;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) S.s.o[w][hb][sub * 8 + c] = sb.o[c];
+        for (int c = 0; c < 8; ++c) v.o[s * 128 + sub * 8 + c] = sb.o[c];
         if (sub == 0) {
-            S.s.m[w][hb] = sb.m;
-            S.s.l[w][hb] = sb.l;
+            v.m[s] = sb.m;
+            v.l[s] = sb.l;
         }
     }
     __syncthreads();
-    att_slots_to_partial(A.G, A.lpart + (int64_t)item * kAMH * kAPF, kAPF, S);
-    if (att_arrive_last(A.lctr + rest, (uint32_t)A.nlt, S)) {
+    att_slots_to_partial(A.G, v, A.lpart + (int64_t)item * kAMH * kAPF, kAPF);
+    if (att_arrive_last(A.lctr + rest, (uint32_t)A.nlt, flag)) {
         float *outp = A.out + ((int64_t)bl * A.Hq + (int64_t)gk * A.G) * 128;
         att_merge(A.lpart + (int64_t)rest * A.nlt * kAMH * kAPF, (int64_t)kAMH * kAPF, A.nlt, A.G,
                   nullptr, outp);
@@ -1600,200 +1606,154 @@ __device__ void att_local_tile(const SelAttArgs &A, int item, AttLds &S)
     __syncthreads();
 }
 
-// The block containing position x of a stage's T tokens: block a < A <= T
-// holds [T a / A, T (a + 1) / A), never empty.
-__device__ __forceinline__ int att_block_of(uint64_t x, uint64_t T, int A)
+// Publishes the block's one-head slots as partial pi of row r and runs the
+// merges it is last for: the group of 16 partials, then the row (the output,
+// and the reset of the row's `ready`).
+__device__ void att_publish(const SelAttArgs &A, const SelPtrs &P, int64_t r, int pi, int nparts,
+                            const SlotView &v, int &flag)
 {
-    return (int)(((x + 1) * (uint64_t)A - 1) / T);
-}
-
-// The last row r < R with pre[r] <= x (rows with no tokens are skipped).
-__device__ __forceinline__ int att_row_of(const uint32_t *pre, int R, uint32_t x)
-{
-    int lo = 0, hi = R - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= x)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
-// Row r's partial of one stage is complete at spart: the second stage to
-// arrive merges both into the output.
-__device__ void att_stage_done(const SelAttArgs &A, const SelPtrs &P, int64_t r, AttLds &S)
-{
-    if (att_arrive_last(A.fctr + r, 2u, S)) {
-        const int b = (int)(r / A.H_r), h = (int)(r % A.H_r);
-        att_merge(A.spart + (int64_t)r * 2 * kAPF, kAPF, 2, 1, nullptr,
-                  A.out + ((int64_t)b * A.Hq + h) * 128);
-    }
-}
-
-// Stage ph of attention block a: its range of the stage's tokens, one
-// partial per row it touches, and the merges it is last for.
-__device__ void att_stage(const SelAttArgs &A, const SelPtrs &P, int R, int a, int ph, int N,
-                          const int32_t *__restrict__ idx, const int32_t *__restrict__ count,
-                          AttLds &S)
-{
-    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
-    const int lg = lane >> 4, sub = lane & 15;
-    // Every row's tokens of this stage are listed: their counts.
-    for (int r = tid; r < R; r += kSelThreads) {
-        wait_row_ready(P.rows[r], 3u + (uint32_t)ph, P.wc);
-        const uint32_t k1 = min(ld_agent(&P.rows[r].kept1), (uint32_t)N);
-        uint32_t len = k1, off = 0;
-        if (ph) {
-            const uint32_t c = min(ld_agent(reinterpret_cast<const uint32_t *>(count + r)),
-                                   (uint32_t)N);
-            len = c > k1 ? c - k1 : 0u;
-            off = k1;
+    __syncthreads();
+    att_slots_to_partial(1, v, A.part + ((int64_t)r * nparts + pi) * kAPF, kAPF);
+    const int gi = pi / kAGS, gn = min(kAGS, nparts - gi * kAGS);
+    if (att_arrive_last(A.gctr + (int64_t)r * A.ng + gi, (uint32_t)gn, flag)) {
+        att_merge(A.part + ((int64_t)r * nparts + gi * kAGS) * kAPF, kAPF, gn, 1,
+                  A.gpart + ((int64_t)r * A.ng + gi) * kAPF, nullptr);
+        if (att_arrive_last(A.rctr + r, (uint32_t)A.ng, flag)) {
+            const int b = (int)(r / A.H_r), h = (int)(r % A.H_r);
+            att_merge(A.gpart + (int64_t)r * A.ng * kAPF, kAPF, A.ng, 1, nullptr,
+                      A.out + ((int64_t)b * A.Hq + h) * 128);
+            // Every block of the row has passed its wait.
+            if (threadIdx.x == 0) ctr_reset(&P.rows[r].ready);
         }
-        S.len[r] = len;
-        S.off[r] = off;
     }
     __syncthreads();
-    if (ph == 1) {
-        // Once every attention block has passed its last wait, the last of
-        // them resets every row's `ready` for the next call.
-        if (att_arrive_last(A.dctr, (uint32_t)A.A, S))
-            for (int r = tid; r < R; r += kSelThreads) ctr_reset(&P.rows[r].ready);
-    }
-    {
-        constexpr int kPer = kAMaxR / kSelThreads;
-        uint32_t loc = 0;
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int r = tid * kPer + k;
-            loc += r < R ? S.len[r] : 0u;
-        }
-        uint32_t tot;
-        uint32_t run = block_exclusive_scan<kSelThreads, uint32_t>(loc, S.uscan, &tot);
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int r = tid * kPer + k;
-            if (r < R) {
-                S.pre[r] = run;
-                run += S.len[r];
-            }
-        }
-        if (tid == 0) S.pre[R] = tot;
-    }
-    __syncthreads();
-    const uint64_t T = S.pre[R];
-    // Rows with no token in this stage: block r % A reports them.
-    for (int r = a; r < R; r += A.A) {
-        if (S.len[r] == 0u) {
-            if (tid < 128) st_agent(A.spart + ((int64_t)r * 2 + ph) * kAPF + 4 + tid, 0.0f);
-            if (tid == 0) {
-                st_agent(A.spart + ((int64_t)r * 2 + ph) * kAPF, -INFINITY);
-                st_agent(A.spart + ((int64_t)r * 2 + ph) * kAPF + 1, 0.0f);
-            }
-            att_stage_done(A, P, r, S);
-        }
-    }
-    // The first min(A, T) blocks take the tokens, so none of them is empty.
-    const int Ae = (int)min((uint64_t)A.A, T);
-    if (a >= Ae) return;
-    const uint32_t blo = (uint32_t)(T * (uint64_t)a / (uint64_t)Ae);
-    const uint32_t bhi = (uint32_t)(T * (uint64_t)(a + 1) / (uint64_t)Ae);
-    const int r_first = att_row_of(S.pre, R, blo), r_last = att_row_of(S.pre, R, bhi - 1);
-    // Rows in windows of kAMH: the waves cut the window's share of the range.
-    for (int rw = r_first; rw <= r_last; rw += kAMH) {
-        const int nr = min(kAMH, r_last + 1 - rw);
-        const uint32_t plo = max(blo, S.pre[rw]), phi = min(bhi, S.pre[rw + nr]);
-        if (tid < kAW * kAMH) {
-            S.s.m[tid / kAMH][tid % kAMH] = -INFINITY;
-            S.s.l[tid / kAMH][tid % kAMH] = 0.0f;
-        }
-        __syncthreads();
-        const uint32_t span = phi - plo;
-        const uint32_t wlo = plo + (uint32_t)((uint64_t)span * w / kAW);
-        const uint32_t whi = plo + (uint32_t)((uint64_t)span * (w + 1) / kAW);
-        int r = wlo < whi ? att_row_of(S.pre, R, wlo) : rw;
-        for (uint32_t x = wlo; x < whi;) {
-            while (S.pre[r + 1] <= x) ++r;
-            const uint32_t xe = min(whi, S.pre[r + 1]);
-            const int b = r / A.H_r, h = r % A.H_r, g = h / A.G;
-            float qf[8];
-            att_q8(A.q + ((int64_t)b * A.Hq + h) * 128 + sub * 8, A.qscale, qf);
-            const int64_t kvb = ((int64_t)b * A.Hkv + g) * A.kv_cap * 128 + sub * 8;
-            const uint32_t *ir =
-                reinterpret_cast<const uint32_t *>(idx + (int64_t)r * N) + S.off[r] - S.pre[r];
-            AttState st;
-            att_reset(st);
-            for (uint32_t k0 = x + (uint32_t)lg; k0 < xe; k0 += 4u * kARU) {
-                int tok[kARU];
-#pragma unroll
-                for (int u = 0; u < kARU; ++u) {
-                    const uint32_t k = k0 + 4u * (uint32_t)u;
-                    const uint32_t t = k < xe ? ld_agent(ir + k) : 0xFFFFFFFFu;
-                    tok[u] = t < (uint32_t)N ? (int)t : -1;
-                }
-                att_rows(A.K + kvb, A.V + kvb, qf, tok, st);
-            }
-            att_flush(st, w, r - rw, S);
-            x = xe;
-        }
-        __syncthreads();
-        att_slots_to_partial(nr, A.part + ((int64_t)rw * 2 + ph) * A.A * kAPF + (int64_t)a * kAPF,
-                             (int64_t)2 * A.A * kAPF, S);
-        // One arrival per row on its group counter (threads t < nr).
-        wait_vmem();
-        __syncthreads();
-        if (tid < nr) S.last[tid] = 0;
-        // (a row of the window with no token here was reported by block r % A)
-        if (tid < nr && S.len[rw + tid] > 0u) {
-            const int rr = rw + tid;
-            const int a0 = att_block_of(S.pre[rr], T, Ae);
-            const int a1 = att_block_of(S.pre[rr + 1] - 1u, T, Ae);
-            const int gi = (a - a0) / kAGS;
-            const int gn = min(kAGS, a1 - a0 + 1 - gi * kAGS);
-            unsigned long long *ctr = A.gctr + ((int64_t)rr * 2 + ph) * A.maxg + gi;
-            const bool lst = ctr_arrive(ctr) == (uint32_t)gn - 1u;
-            if (lst) ctr_reset(ctr);
-            S.last[tid] = lst ? 1 : 0;
-        }
-        __syncthreads();
-        for (int t = 0; t < nr; ++t) {
-            if (!S.last[t]) continue;
-            const int rr = rw + t;
-            const int a0 = att_block_of(S.pre[rr], T, Ae);
-            const int a1 = att_block_of(S.pre[rr + 1] - 1u, T, Ae);
-            const int gi = (a - a0) / kAGS;
-            const int gn = min(kAGS, a1 - a0 + 1 - gi * kAGS);
-            const int ng = (a1 - a0) / kAGS + 1;
-            const int64_t rs = (int64_t)rr * 2 + ph;
-            att_merge(A.part + (rs * A.A + a0 + gi * kAGS) * kAPF, kAPF, gn, 1,
-                      A.gpart + (rs * A.maxg + gi) * kAPF, nullptr);
-            if (att_arrive_last(A.sctr + rs, (uint32_t)ng, S)) {
-                att_merge(A.gpart + rs * A.maxg * kAPF, kAPF, ng, 1, A.spart + rs * kAPF, nullptr);
-                att_stage_done(A, P, rr, S);
-            }
-            __syncthreads();
-        }
-    }
 }
-
-union SelAttShared {
-    ResShared r;
-    AttLds a;
-};
 
 }  // namespace
 
-// The selection (block rows [0, 2R)) and attention (rows [2R, 2R + Ay))
-// described above.
+__device__ void emit_attend(const SelAttArgs &A, const SelPtrs &P, int64_t r, int N,
+                            int32_t *__restrict__ idx, int32_t *__restrict__ count,
+                            uint32_t above, uint32_t ex, const ChunkView &cv, ResShared &S)
+{
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+    const int lg = lane >> 4, sub = lane & 15;
+    const int e = blockIdx.x, nblk = P.nblk, nparts = 2 * nblk;
+    const bool last = S.last != 0;
+    // This wave's first slot in the block's list of emitted tokens, and
+    // the block's count (the resolve reuses the LDS words they sit in).
+    const uint32_t wkb = (uint32_t)(S.wbase[w] >> 32);
+    const uint32_t nk = (uint32_t)(S.bcount >> 32);
+    __syncthreads();
+    if (last) {
+        if (tid == 0) {
+            const unsigned long long sl =
+                ld_agent(reinterpret_cast<const unsigned long long *>(&P.rows[r].slots));
+            st_agent(&P.rows[r].kept1, (uint32_t)(sl >> 32));
+        }
+        resolve_row<false, true>(N, P, r, idx, count, nullptr, S);
+        wait_vmem();
+        __syncthreads();
+        if (tid == 0) ctr_add(&P.rows[r].ready, 1u);  // 3: the row's set is complete
+    }
+    const int b = (int)(r / A.H_r), h = (int)(r % A.H_r), g = h / A.G;
+    float qf[8];
+    att_q8(A.q + ((int64_t)b * A.Hq + h) * 128 + sub * 8, A.qscale, qf);
+    const int64_t kvb = ((int64_t)b * A.Hkv + g) * A.kv_cap * 128 + sub * 8;
+    const SlotView one = slots_one(S);
+
+    // 1. The tokens this block emitted, from an LDS copy of its list.
+    uint32_t *list = reinterpret_cast<uint32_t *>(&S.buf[0][0]);
+    {
+        uint32_t o = wkb + (ex >> 16);
+        for (uint32_t m = above; m; m &= m - 1) list[o++] = cv.index32(__ffs(m) - 1);
+    }
+    if (tid < kAW) {
+        one.m[tid] = -INFINITY;
+        one.l[tid] = 0.0f;
+    }
+    __syncthreads();
+    {
+        AttState st;
+        att_reset(st);
+        const uint32_t gi = (uint32_t)(w * 4 + lg);  // rows gi + 64 j of the list
+        for (uint32_t k0 = gi; k0 < nk; k0 += 64u * kARU) {
+            int tok[kARU];
+#pragma unroll
+            for (int u = 0; u < kARU; ++u) {
+                const uint32_t k = k0 + 64u * (uint32_t)u;
+                tok[u] = k < nk ? (int)list[k] : -1;
+            }
+            att_rows(A.K + kvb, A.V + kvb, qf, tok, st);
+        }
+        att_flush(st, w, 0, one);
+    }
+    att_publish(A, P, r, e, nparts, one, S.last);
+
+    // 2. This block's share of the tokens the row's resolve added.
+    if (tid == 0) {
+        wait_row_ready(P.rows[r], 3u, P.wc);
+        const uint32_t k1 = min(ld_agent(&P.rows[r].kept1), (uint32_t)N);
+        uint32_t c = min(ld_agent(reinterpret_cast<const uint32_t *>(count + r)), (uint32_t)N);
+        c = max(c, k1);
+        const uint64_t len = c - k1;
+        S.j = k1 + (uint32_t)(len * (uint64_t)e / (uint64_t)nblk);
+        S.cbefore = k1 + (uint32_t)(len * (uint64_t)(e + 1) / (uint64_t)nblk);
+    }
+    if (tid < kAW) {
+        one.m[tid] = -INFINITY;
+        one.l[tid] = 0.0f;
+    }
+    __syncthreads();
+    {
+        const uint32_t lo = S.j, hi = S.cbefore;
+        const uint32_t *ir = reinterpret_cast<const uint32_t *>(idx + r * (int64_t)N);
+        AttState st;
+        att_reset(st);
+        const uint32_t gi = (uint32_t)(w * 4 + lg);
+        for (uint32_t k0 = lo + gi; k0 < hi; k0 += 64u * kARU) {
+            int tok[kARU];
+#pragma unroll
+            for (int u = 0; u < kARU; ++u) {
+                const uint32_t k = k0 + 64u * (uint32_t)u;
+                const uint32_t t = k < hi ? ld_agent(ir + k) : 0xFFFFFFFFu;
+                tok[u] = t < (uint32_t)N ? (int)t : -1;
+            }
+            att_rows(A.K + kvb, A.V + kvb, qf, tok, st);
+        }
+        att_flush(st, w, 0, one);
+    }
+    att_publish(A, P, r, nblk + e, nparts, one, S.last);
+    // 3. Local tiles from the queue; the block whose grab is the last of
+    // all resets it.
+    if (A.n_items > 0) {
+        const SlotView heads = slots_heads(S);
+        for (;;) {
+            if (tid == 0) {
+                const uint32_t it = ctr_add(A.lq, 1u);
+                if (it >= (uint32_t)A.n_items && it == (uint32_t)(A.n_items + A.nE - 1))
+                    ctr_reset(A.lq);
+                S.j = it;
+            }
+            __syncthreads();
+            const uint32_t it = S.j;
+            __syncthreads();
+            if (it >= (uint32_t)A.n_items) break;
+            att_local_tile(A, (int)it, heads, S.last);
+        }
+    }
+
+}
+
+// The selection with attention (block rows [0, R) histogram blocks, [R, 2R)
+// emit blocks, as in sel_fused_kernel).
 __global__ __launch_bounds__(kSelThreads) void sel_attend_kernel(
-    const float *__restrict__ scores, int N, int R, SelPtrs P, double target,
+    const float *__restrict__ scores, int N, SelPtrs P, double target,
     int32_t *__restrict__ idx, int32_t *__restrict__ count, SelAttArgs A)
 {
-    __shared__ SelAttShared U;
+    __shared__ ResShared S;
+    const int R = (int)gridDim.y / 2;
     const int blk = blockIdx.x;
     if ((int)blockIdx.y < R) {
-        ResShared &S = U.r;
         const int64_t r = blockIdx.y;
         float v[kSelPerThread];
         const ChunkView cv = load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);
@@ -1807,41 +1767,29 @@ __global__ __launch_bounds__(kSelThreads) void sel_attend_kernel(
             ctr_add(&P.rows[r].ready, 1u);  // 2: the row's Hist1 is complete
         return;
     }
-    if ((int)blockIdx.y < 2 * R) {
-        ResShared &S = U.r;
-        const int64_t r = blockIdx.y - R;
-        float v[kSelPerThread];
-        const ChunkView cv = load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);
-        if (threadIdx.x == 0) wait_row_ready(P.rows[r], 2u, P.wc);
-        __syncthreads();
-        PickIn pi;
-        pick_inputs(P, r, pi);
-        emit_body<false, true>(v, cv, N, P, r, target, pi, idx, count, nullptr, S);
-        return;
-    }
-    AttLds &S = U.a;
-    const int a = ((int)blockIdx.y - 2 * R) * (int)gridDim.x + blk;
-    att_stage(A, P, R, a, 0, N, idx, count, S);
-    for (int it = a; it < A.n_items; it += A.A) att_local_tile(A, it, S);
-    att_stage(A, P, R, a, 1, N, idx, count, S);
+    const int64_t r = blockIdx.y - R;
+    float v[kSelPerThread];
+    const ChunkView cv = load_chunk(scores + r * (int64_t)N, N, (int64_t)blk * kSelChunk, v);
+    if (threadIdx.x == 0) wait_row_ready(P.rows[r], 2u, P.wc);
+    __syncthreads();
+    PickIn pi;
+    pick_inputs(P, r, pi);
+    emit_body<false, true>(v, cv, N, P, r, target, pi, idx, count, nullptr, S, &A);
 }
 
 struct SelAttGeom {
     int64_t R;
-    int nblk, Ay, A, maxg, G, n_lkv, nl_rows, sink_end, w0, nlt, n_items;
-    size_t part, gpart, spart, gctr, sctr, fctr, dctr, lpart, lctr, total;
+    int nblk, ng, G, n_lkv, nl_rows, sink_end, w0, nlt, n_items;
+    size_t part, gpart, gctr, rctr, lpart, lctr, lq, total;
 };
 
-static SelAttGeom sel_att_geom(int cus, int B, int Hq, int Hkv, int N, int H_r, int n_sink,
-                               int window)
+static SelAttGeom sel_att_geom(int B, int Hq, int Hkv, int N, int H_r, int n_sink, int window)
 {
     SelAttGeom g;
     g.R = (int64_t)B * H_r;
     const SelLayout L = sel_layout(g.R, N);
     g.nblk = (int)L.nblk;
-    g.Ay = (cus + g.nblk - 1) / g.nblk;
-    g.A = g.nblk * g.Ay;
-    g.maxg = (g.A + kAGS - 1) / kAGS;
+    g.ng = (2 * g.nblk + kAGS - 1) / kAGS;
     g.G = Hq / Hkv;
     g.n_lkv = Hkv - H_r / g.G;
     const int w0 = N > window ? N - window : 0;
@@ -1852,23 +1800,19 @@ static SelAttGeom sel_att_geom(int cus, int B, int Hq, int Hkv, int N, int H_r, 
     g.n_items = B * g.n_lkv * g.nlt;
     size_t off = align_up(L.total, 256);
     g.part = off;
-    off += align_up((size_t)g.R * 2 * g.A * kAPF * sizeof(float), 256);
+    off += align_up((size_t)g.R * 2 * g.nblk * kAPF * sizeof(float), 256);
     g.gpart = off;
-    off += align_up((size_t)g.R * 2 * g.maxg * kAPF * sizeof(float), 256);
-    g.spart = off;
-    off += align_up((size_t)g.R * 2 * kAPF * sizeof(float), 256);
+    off += align_up((size_t)g.R * g.ng * kAPF * sizeof(float), 256);
     g.gctr = off;
-    off += align_up((size_t)g.R * 2 * g.maxg * 8, 256);
-    g.sctr = off;
-    off += align_up((size_t)g.R * 2 * 8, 256);
-    g.fctr = off;
+    off += align_up((size_t)g.R * g.ng * 8, 256);
+    g.rctr = off;
     off += align_up((size_t)g.R * 8, 256);
-    g.dctr = off;
-    off += 256;
     g.lpart = off;
     off += align_up((size_t)g.n_items * kAMH * kAPF * sizeof(float), 256);
     g.lctr = off;
     off += align_up((size_t)B * g.n_lkv * 8, 256);
+    g.lq = off;
+    off += 256;
     g.total = off;
     return g;
 }
@@ -1876,15 +1820,17 @@ static SelAttGeom sel_att_geom(int cus, int B, int Hq, int Hkv, int N, int H_r, 
 size_t topp_attend_ws_bytes(int cus, int B, int Hq, int Hkv, int N, int H_r, int n_sink,
                             int window)
 {
-    const SelAttGeom g = sel_att_geom(cus, B, Hq, Hkv, N, H_r, n_sink, window);
+    (void)cus;
+    const SelAttGeom g = sel_att_geom(B, Hq, Hkv, N, H_r, n_sink, window);
     const size_t att = attend_ws_bytes(B, H_r, Hq - H_r, N);  // the p >= 1 path
     return g.total > att ? g.total : att;
 }
 
 bool topp_attend_fits(int cus, int B, int Hq, int Hkv, int N, int H_r, int n_sink, int window)
 {
-    const SelAttGeom g = sel_att_geom(cus, B, Hq, Hkv, N, H_r, n_sink, window);
-    return g.G <= kAMH && H_r % g.G == 0 && g.R <= kAMaxR && 2 * g.R + g.Ay <= kMaxFusedRows;
+    (void)cus;
+    const SelAttGeom g = sel_att_geom(B, Hq, Hkv, N, H_r, n_sink, window);
+    return g.G <= kAMH && H_r % g.G == 0 && 2 * g.R <= kMaxFusedRows;
 }
 
 hipError_t launch_topp_attend(const float *scores, const uint16_t *q, const uint16_t *K,
@@ -1892,15 +1838,13 @@ hipError_t launch_topp_attend(const float *scores, const uint16_t *q, const uint
                               int H_r, int n_sink, int window, float p, float scale, float *out,
                               int32_t *idx, int32_t *count, void *ws, hipStream_t stream)
 {
-    int cus = 0;
-    RTP_TRY(device_cus(&cus));
     if (p >= 1.0f) {
         // Every token is kept: the listing, then the attention launch.
         RTP_TRY(launch_keep_all((int64_t)B * H_r, N, idx, count, nullptr, stream));
         return launch_decode_attend(q, K, V, idx, count, B, Hq, Hkv, N, kv_cap, 0, H_r, H_r,
                                     Hq - H_r, n_sink, window, scale, out, ws, stream);
     }
-    const SelAttGeom g = sel_att_geom(cus, B, Hq, Hkv, N, H_r, n_sink, window);
+    const SelAttGeom g = sel_att_geom(B, Hq, Hkv, N, H_r, n_sink, window);
     SelPtrs P = sel_ptrs(ws, g.R, N);
     RTP_TRY(wait_ctl(&P.wc));
     char *base = static_cast<char *>(ws);
@@ -1915,8 +1859,8 @@ hipError_t launch_topp_attend(const float *scores, const uint16_t *q, const uint
     A.G = g.G;
     A.kv_cap = kv_cap;
     A.qscale = scale * 1.4426950408889634f;
-    A.A = g.A;
-    A.maxg = g.maxg;
+    A.ng = g.ng;
+    A.nE = (int)(g.R * g.nblk);
     A.n_lkv = g.n_lkv;
     A.nl_rows = g.nl_rows;
     A.sink_end = g.sink_end;
@@ -1925,15 +1869,13 @@ hipError_t launch_topp_attend(const float *scores, const uint16_t *q, const uint
     A.n_items = g.n_items;
     A.part = reinterpret_cast<float *>(base + g.part);
     A.gpart = reinterpret_cast<float *>(base + g.gpart);
-    A.spart = reinterpret_cast<float *>(base + g.spart);
     A.gctr = reinterpret_cast<unsigned long long *>(base + g.gctr);
-    A.sctr = reinterpret_cast<unsigned long long *>(base + g.sctr);
-    A.fctr = reinterpret_cast<unsigned long long *>(base + g.fctr);
-    A.dctr = reinterpret_cast<unsigned long long *>(base + g.dctr);
+    A.rctr = reinterpret_cast<unsigned long long *>(base + g.rctr);
     A.lpart = reinterpret_cast<float *>(base + g.lpart);
     A.lctr = reinterpret_cast<unsigned long long *>(base + g.lctr);
-    return launch(sel_attend_kernel, dim3((unsigned)g.nblk, (unsigned)(2 * g.R + g.Ay)),
-                  dim3(kSelThreads), 0, stream, scores, N, (int)g.R, P, (double)p, idx, count, A);
+    A.lq = reinterpret_cast<unsigned long long *>(base + g.lq);
+    return launch(sel_attend_kernel, dim3((unsigned)g.nblk, (unsigned)(2 * g.R)),
+                  dim3(kSelThreads), 0, stream, scores, N, P, (double)p, idx, count, A);
 }
 
 }  // namespace rtp
