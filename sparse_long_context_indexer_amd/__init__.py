@@ -457,6 +457,21 @@ def rtp_decode_layer(q_r, k_r, q, K, V, N, Hq_r, n_sink, window, p, scale, out, 
         sp, wp, wn, _stream(q, stream))
 
 
+def _topp_attend(name, scores, q, K, V, n_sink, window, p, scale, out, idx, count, workspace,
+                 stream):
+    import torch
+    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
+    if scores.dim() != 3 or scores.shape[0] != B:
+        raise ValueError("scores must be [B][Hq_r][N]")
+    Hq_r, N = scores.shape[1], scores.shape[2]
+    wp, wn = _ws(workspace)
+    _call(name,
+        _dev(scores, torch.float32, "scores", (B, Hq_r, N)), qp, Kp, Vp, B, Hq, Hkv, N, cap, d,
+        Hq_r, n_sink, window, float(p), float(scale), op,
+        _dev(idx, torch.int32, "idx", (B, Hq_r, N)), _dev(count, torch.int32, "count", (B, Hq_r)),
+        wp, wn, _stream(q, stream))
+
+
 def rtp_topp_attend(scores, q, K, V, n_sink, window, p, scale, out, idx, count, workspace,
                     stream=None) -> None:
     """Top-p selection over scores f32 [B][Hq_r][N] (query heads [0, Hq_r)
@@ -466,17 +481,8 @@ def rtp_topp_attend(scores, q, K, V, n_sink, window, p, scale, out, idx, count, 
     [B][Hq][d]; idx i32 [B][Hq_r][N] and count i32 [B][Hq_r] (out);
     workspace uint8 [>= topp_attend_workspace_size(B, Hq, Hkv, N, Hq_r,
     n_sink, window)]."""
-    import torch
-    (qp, Kp, Vp, op), (B, Hq, Hkv, cap, d) = _qkv(q, K, V, out)
-    if scores.dim() != 3 or scores.shape[0] != B:
-        raise ValueError("scores must be [B][Hq_r][N]")
-    Hq_r, N = scores.shape[1], scores.shape[2]
-    wp, wn = _ws(workspace)
-    _call("rtp_topp_attend",
-        _dev(scores, torch.float32, "scores", (B, Hq_r, N)), qp, Kp, Vp, B, Hq, Hkv, N, cap, d,
-        Hq_r, n_sink, window, float(p), float(scale), op,
-        _dev(idx, torch.int32, "idx", (B, Hq_r, N)), _dev(count, torch.int32, "count", (B, Hq_r)),
-        wp, wn, _stream(q, stream))
+    _topp_attend("rtp_topp_attend", scores, q, K, V, n_sink, window, p, scale, out, idx, count,
+                 workspace, stream)
 
 
 def rtp_prefill_attend(q, K, V, head_begin, n_heads, n_sink, window, scale, out,

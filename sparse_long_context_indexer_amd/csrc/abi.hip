@@ -507,11 +507,13 @@ rtp_status rtp_topp_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, in
     return RTP_OK;
 }
 
-rtp_status rtp_topp_attend(const float *scores, const rtp_bf16 *q, const rtp_bf16 *K,
-                           const rtp_bf16 *V, int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
-                           int64_t kv_cap, int32_t d, int32_t Hq_r, int32_t n_sink,
-                           int32_t window, float p, float scale, float *out, int32_t *idx,
-                           int32_t *count, void *workspace, size_t ws_bytes, void *stream)
+// rtp_topp_attend: checks, then the launch.
+static rtp_status topp_attend_call(const float *scores, const rtp_bf16 *q, const rtp_bf16 *K,
+                                   const rtp_bf16 *V, int32_t B, int32_t Hq, int32_t Hkv,
+                                   int32_t N, int64_t kv_cap, int32_t d, int32_t Hq_r,
+                                   int32_t n_sink, int32_t window, float p, float scale,
+                                   float *out, int32_t *idx, int32_t *count, void *workspace,
+                                   size_t ws_bytes, void *stream)
 {
     if (!scores || !q || !K || !V || !out || !idx || !count || !workspace) return RTP_ERR_NULL;
     if (d != 128) return RTP_ERR_UNSUPPORTED;
@@ -528,9 +530,19 @@ rtp_status rtp_topp_attend(const float *scores, const rtp_bf16 *q, const rtp_bf1
     const int ns = Hq_r < Hq ? n_sink : 0, win = Hq_r < Hq ? window : 1;
     if (ws_bytes < rtp::topp_attend_ws_bytes(cus, B, Hq, Hkv, N, Hq_r, ns, win))
         return RTP_ERR_WORKSPACE;
-    return from_hip(rtp::launch_topp_attend(scores, q, K, V, B, Hq, Hkv, N, kv_cap, Hq_r, ns,
-                                            win, p, scale, out, idx, count, workspace,
+    return from_hip(rtp::launch_topp_attend(scores, q, K, V, B, Hq, Hkv, N, kv_cap, Hq_r, ns, win,
+                                            p, scale, out, idx, count, workspace,
                                             as_stream(stream)));
+}
+
+rtp_status rtp_topp_attend(const float *scores, const rtp_bf16 *q, const rtp_bf16 *K,
+                           const rtp_bf16 *V, int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                           int64_t kv_cap, int32_t d, int32_t Hq_r, int32_t n_sink,
+                           int32_t window, float p, float scale, float *out, int32_t *idx,
+                           int32_t *count, void *workspace, size_t ws_bytes, void *stream)
+{
+    return topp_attend_call(scores, q, K, V, B, Hq, Hkv, N, kv_cap, d, Hq_r, n_sink, window, p,
+                            scale, out, idx, count, workspace, ws_bytes, stream);
 }
 
 rtp_status rtp_scan_local(const float *q_r, const float *k_r, float *scores, int32_t Hq_r,

@@ -148,6 +148,7 @@ hipError_t launch_topp_attend(const float *scores, const uint16_t *q, const uint
                               int H_r, int n_sink, int window, float p, float scale, float *out,
                               int32_t *idx, int32_t *count, void *ws, hipStream_t stream);
 
+
 // Compute units of the current device (queried once per device).
 hipError_t device_cus(int *cus);
 

@@ -198,7 +198,7 @@ __device__ __forceinline__ ChunkView load_chunk(const float *__restrict__ sr, in
 // blocks (it has the lowest index), so the wait always ends.  The row's
 // last hist block resets `ready` for the next call.
 
-__device__ void clear_row(SelPtrs P, int64_t r)
+__device__ __forceinline__ void clear_row(SelPtrs P, int64_t r)
 {
     Hist1 &g = P.hist1[r];
     Hist2 &h2 = P.hist2[r];
@@ -225,7 +225,7 @@ __device__ void clear_row(SelPtrs P, int64_t r)
 // Waits until the row's tagged `ready` counter holds at least `level`: 1
 // once block 0 has cleared the row, 2 once the row's Hist1 is complete
 // (one-launch selection only).
-__device__ void wait_row_ready(const SelRow &row, uint32_t level, const WaitCtl &wc)
+__device__ __forceinline__ void wait_row_ready(const SelRow &row, uint32_t level, const WaitCtl &wc)
 {
     for (uint32_t it = 0;; ++it) {
         const unsigned long long v = ld_agent(&row.ready);
@@ -266,7 +266,7 @@ struct HistShared {
 // the chunk's top-bin record stored.  Leaves the block's arrival to the
 // caller.
 template <bool kCount>
-__device__ void hist_body(const float (&v)[kSelPerThread], const ChunkView &cv, int N, int64_t r,
+__device__ __forceinline__ void hist_body(const float (&v)[kSelPerThread], const ChunkView &cv, int N, int64_t r,
                           int blk, SelPtrs P, double *hm, double *etbl, float *red)
 {
     for (int i = threadIdx.x; i < kBins1; i += kSelThreads) hm[i] = 0.0;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float *__re
 
 struct ResShared;
 template <bool kCount, bool kVis = false>
-__device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
+__device__ __forceinline__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
                             uint32_t *kbr, ResShared &S);
 
 // ------------------------------------------------------------ resolve
@@ -401,7 +401,7 @@ static_assert(sizeof(double) * kBins1 <= sizeof(uint2) * kResCap, "pick histogra
 constexpr int kPickPer = kBins1 / kSelThreads;  // bins per thread
 
 template <bool kCount>
-__device__ void pick_block(const ChunkTop *tops, int nblk, double target,
+__device__ __forceinline__ void pick_block(const ChunkTop *tops, int nblk, double target,
                            const double (&gmv)[kPickPer], float tm0, double tmass0, ResShared &S)
 {
     double *hm = reinterpret_cast<double *>(&S.buf[0][0]);
@@ -516,7 +516,7 @@ __device__ void pick_block(const ChunkTop *tops, int nblk, double target,
 // the parallel prefix can skip -- or, if the total stays below T, the
 // lowest non-empty digit.  Lane l owns digits kDig - 1 - 16l - [0, 16); it
 // reads them into registers once and decides with selects.
-__device__ void res_choose_mass(double A, double T, ResShared &S)
+__device__ __forceinline__ void res_choose_mass(double A, double T, ResShared &S)
 {
     const int lane = lane_id();
     constexpr int kPerLane = kDig / kWave;
@@ -566,7 +566,7 @@ __device__ void res_choose_mass(double A, double T, ResShared &S)
 
 // Wave 0 chooses the index digit holding the c-th lowest index over nb
 // digits (ascending); lane l owns digits [l*per, (l+1)*per).
-__device__ void res_choose_count(uint32_t c, int nb, ResShared &S)
+__device__ __forceinline__ void res_choose_count(uint32_t c, int nb, ResShared &S)
 {
     const int lane = lane_id();
     const int per = nb / kWave;
@@ -605,7 +605,7 @@ __device__ __forceinline__ uint32_t *nout_ptr(ResShared &S) { return reinterpret
 // Ordered in-place filter for candidates in global memory (see the header
 // comment); survivors keep their relative order.
 template <bool kVis>
-__device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t mask,
+__device__ __forceinline__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t mask,
                                      uint32_t keep_digit, bool emit_above, bool by_index,
                                      int32_t *ir, uint32_t *kbr, ResShared &S)
 {
@@ -641,7 +641,7 @@ __device__ int64_t res_filter_global(uint2 *cr, int64_t n, int shift, uint32_t m
 // (mass exp(s - M) and count) is built in S.hm / S.hc on the way, for the
 // next score level.
 template <bool kGlobal, bool kCount, bool kVis = false>
-__device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int shift,
+__device__ __forceinline__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int shift,
                                    uint32_t mask, uint32_t j, bool emit_above, bool by_index,
                                    int32_t *ir, uint32_t *kbr, ResShared &S,
                                    bool acc_next = false, double M = 0.0)
@@ -706,7 +706,7 @@ __device__ uint32_t res_filter_lds(const uint2 *src, int64_t n, uint2 *dst, int 
 // laid out in rank order and prefix-summed from A, and the wave keeps the
 // shortest rank prefix whose running mass reaches T (all n if none does).
 template <bool kCount, bool kVis = false>
-__device__ void resolve_few(const uint2 *cr, int n, double A, double T, double M, int32_t *ir,
+__device__ __forceinline__ void resolve_few(const uint2 *cr, int n, double A, double T, double M, int32_t *ir,
                             uint32_t *kbr, ResShared &S)
 {
     const int l = lane_id();
@@ -731,7 +731,7 @@ __device__ void resolve_few(const uint2 *cr, int n, double A, double T, double M
 }
 
 template <bool kCount, bool kVis>
-__device__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
+__device__ __forceinline__ void resolve_row(int N, SelPtrs P, int64_t r, int32_t *idx, int32_t *count,
                             uint32_t *kbr, ResShared &S)
 {
     __syncthreads();  // emit is done with the shared words it used
@@ -907,12 +907,12 @@ __device__ __forceinline__ void pick_inputs(SelPtrs P, int64_t r, PickIn &pi)
 struct SelAttArgs;
 // The emit block's part in the selection-and-attention launch (defined with
 // that launch below).
-__device__ void emit_attend(const SelAttArgs &A, const SelPtrs &P, int64_t r, int N,
+__device__ __forceinline__ void emit_attend(const SelAttArgs &A, const SelPtrs &P, int64_t r, int N,
                             int32_t *__restrict__ idx, int32_t *__restrict__ count,
                             uint32_t above, uint32_t ex, const ChunkView &cv, ResShared &S);
 
 template <bool kCount, bool kAtt = false>
-__device__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, int N,
+__device__ __forceinline__ void emit_body(const float (&v)[kSelPerThread], const ChunkView &cv, int N,
                           SelPtrs P, int64_t r, double target, const PickIn &pi,
                           int32_t *__restrict__ idx, int32_t *__restrict__ count,
                           uint32_t *__restrict__ keep_bits, ResShared &S,
@@ -1512,7 +1512,7 @@ namespace {
 // local KV head gl of batch row bl, for its G query heads.  Lane group lg of
 // a wave takes query heads 2lg and 2lg + 1, so all four groups read the same
 // row.
-__device__ void att_local_tile(const SelAttArgs &A, int item, const SlotView &v, int &flag)
+__device__ __forceinline__ void att_local_tile(const SelAttArgs &A, int item, const SlotView &v, int &flag)
 {
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int lg = lane >> 4, sub = lane & 15;
@@ -1609,7 +1609,7 @@ __device__ void att_local_tile(const SelAttArgs &A, int item, const SlotView &v,
 // Publishes the block's one-head slots as partial pi of row r and runs the
 // merges it is last for: the group of 16 partials, then the row (the output,
 // and the reset of the row's `ready`).
-__device__ void att_publish(const SelAttArgs &A, const SelPtrs &P, int64_t r, int pi, int nparts,
+__device__ __forceinline__ void att_publish(const SelAttArgs &A, const SelPtrs &P, int64_t r, int pi, int nparts,
                             const SlotView &v, int &flag)
 {
     __syncthreads();
@@ -1629,9 +1629,30 @@ __device__ void att_publish(const SelAttArgs &A, const SelPtrs &P, int64_t r, in
     __syncthreads();
 }
 
+// Local tiles from the launch's queue until none is left; every emit block
+// calls it once, so the block whose grab is the last of all resets it.
+__device__ __forceinline__ void att_local_queue(const SelAttArgs &A, ResShared &S)
+{
+    if (A.n_items <= 0) return;
+    const SlotView heads = slots_heads(S);
+    for (;;) {
+        if (threadIdx.x == 0) {
+            const uint32_t it = ctr_add(A.lq, 1u);
+            if (it >= (uint32_t)A.n_items && it == (uint32_t)(A.n_items + A.nE - 1))
+                ctr_reset(A.lq);
+            S.j = it;
+        }
+        __syncthreads();
+        const uint32_t it = S.j;
+        __syncthreads();
+        if (it >= (uint32_t)A.n_items) break;
+        att_local_tile(A, (int)it, heads, S.last);
+    }
+}
+
 }  // namespace
 
-__device__ void emit_attend(const SelAttArgs &A, const SelPtrs &P, int64_t r, int N,
+__device__ __forceinline__ void emit_attend(const SelAttArgs &A, const SelPtrs &P, int64_t r, int N,
                             int32_t *__restrict__ idx, int32_t *__restrict__ count,
                             uint32_t above, uint32_t ex, const ChunkView &cv, ResShared &S)
 {
@@ -1723,25 +1744,8 @@ __device__ void emit_attend(const SelAttArgs &A, const SelPtrs &P, int64_t r, in
         att_flush(st, w, 0, one);
     }
     att_publish(A, P, r, nblk + e, nparts, one, S.last);
-    // 3. Local tiles from the queue; the block whose grab is the last of
-    // all resets it.
-    if (A.n_items > 0) {
-        const SlotView heads = slots_heads(S);
-        for (;;) {
-            if (tid == 0) {
-                const uint32_t it = ctr_add(A.lq, 1u);
-                if (it >= (uint32_t)A.n_items && it == (uint32_t)(A.n_items + A.nE - 1))
-                    ctr_reset(A.lq);
-                S.j = it;
-            }
-            __syncthreads();
-            const uint32_t it = S.j;
-            __syncthreads();
-            if (it >= (uint32_t)A.n_items) break;
-            att_local_tile(A, (int)it, heads, S.last);
-        }
-    }
-
+    // 3. Local tiles from the queue.
+    att_local_queue(A, S);
 }
 
 // The selection with attention (block rows [0, R) histogram blocks, [R, 2R)
