@@ -13,8 +13,8 @@
 // query positions and up to 8 query heads of one KV head, one wave per head,
 // and walks the allowed keys in tiles of 64.  Each tile's K rows and V^T
 // (V transposed: one row per dimension) are staged once in LDS for all the
-// block's heads, double-buffered: the next tile's loads are in flight while
-// the current tile is multiplied.  Per wave and tile (v_mfma_f32_32x32x16_bf16):
+// block's heads: waves 0-3 stage K, waves 4-7 V, each load covering whole
+// rows.  Per wave and tile (v_mfma_f32_32x32x16_bf16):
 //
 //   S^T = K Q^T   2 key halves x 8 dim steps: A = 8 dims of one key row (one
 //                 16-B LDS read), B = Q^T (the wave's 32 queries, held in
@@ -23,7 +23,14 @@
 //   O^T += V^T P^T  4 dim tiles x 4 key steps of 16.  The 16 keys of a step
 //                 enter in the order the lanes already hold them: a lane of
 //                 half g supplies keys 4g + (0..3) and 8 + 4g + (0..3), as
-//                 B = its own probabilities and as A = two 8-B reads of V^T.
+//                 B = its own probabilities and as A = one 16-B read of V^T,
+//                 whose key blocks are stored in that order.
+//
+// The two products of an iteration belong to different tiles: S^T of tile
+// it + 1 is issued in the same basic block as the exponentials of tile it,
+// and O^T += V^T P^T of tile it beside the bf16 split of its P, so each
+// wave's matrix-core work overlaps its own vector work.  K is staged one
+// tile ahead of V (two buffers each).
 //
 // O^T's columns are queries, so each lane's accumulators belong to its own
 // query: the online-softmax rescale needs no exchange, and a query's max and
@@ -49,7 +56,7 @@ constexpr int kPfThreads = kPfWaves * kWave;  // 512
 constexpr int kPfQ = 32;                      // query positions per block
 constexpr int kPfK = 64;                      // keys per tile
 constexpr int kKRow = 128 + 8;                // bf16 per staged K row (272 B: rows 4 banks apart)
-constexpr int kVRow = kPfK + 4;               // bf16 per staged V^T row (136 B)
+constexpr int kVRow = kPfK + 8;               // bf16 per staged V^T row (144 B, 16-B aligned)
 constexpr float kPfLog2e = 1.4426950408889634f;
 
 struct PfArgs {
@@ -61,18 +68,29 @@ struct PfArgs {
     int c_first;  // first chunk (g * hc + s) that holds a head of the range
     int nc;       // chunks that do
     int64_t kv_cap;
-    float qscale;    // |scale| * log2(e)
+    float qscale;    // |scale| * log2(e), at least 1e-30 (a masked score of -inf gives 0)
     uint32_t qsign;  // 0x80008000 when scale < 0: Q's signs are flipped instead
 };
 
+constexpr int kPfHalf = kPfThreads / 2;       // threads of one wave group
+constexpr int kKBuf = kPfK * kKRow;           // bf16 per K buffer
+constexpr int kVBuf = 128 * kVRow + 16 * 8;   // bf16 per V^T buffer (a 16-B gap after every 8 rows)
+
 struct PfShared {
-    uint16_t k[2][kPfK][kKRow];
-    uint16_t vt[2][128][kVRow];
+    uint16_t k[2][kKBuf];
+    uint16_t vt[2][kVBuf];
 };
 
 __device__ __forceinline__ float shfl_x32(float v)
 {
     return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((lane_id() ^ 32) << 2), __float_as_int(v)));
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 // Eight floats as bf16, rounded to nearest even.
@@ -84,42 +102,63 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8])
     return r;
 }
 
-// The tile's global loads: K row t / 8, 16-B pieces 2 (t % 8) and +1; V rows
-// 2 (t / 16) and +1, dims 8 (t % 16) .. +7.  Rows past the prompt read row
-// T - 1 (their keys are masked).
-struct TileRegs {
-    uint4 k0, k1, va, vb;
+struct HalfRegs {
+    uint4 r[4];
 };
 
-__device__ __forceinline__ TileRegs tile_load(const uint16_t *Kb, const uint16_t *Vb, int k0, int T)
+// The first wave group stages K rows, the second V rows.  Thread t of a
+// group: K rows t / 16 + 16 j, dims 8 (t % 16) .. +7; or V rows 4 (t / 16)
+// + j, dims 8 (t % 16) .. +7 (j < 4): each load covers whole rows.  Rows past the prompt read
+// row T - 1 (their keys are masked).
+__device__ __forceinline__ HalfRegs k_load(const uint16_t *Kb, int k0, int T)
 {
-    const int t = threadIdx.x;
-    TileRegs r;
-    const int kr = min(k0 + (t >> 3), T - 1);
-    const uint4 *kp = reinterpret_cast<const uint4 *>(Kb + (int64_t)kr * 128) + 2 * (t & 7);
-    r.k0 = kp[0];
-    r.k1 = kp[1];
-    const int va = min(k0 + 2 * (t >> 4), T - 1), vb = min(k0 + 2 * (t >> 4) + 1, T - 1);
-    r.va = *(reinterpret_cast<const uint4 *>(Vb + (int64_t)va * 128) + (t & 15));
-    r.vb = *(reinterpret_cast<const uint4 *>(Vb + (int64_t)vb * 128) + (t & 15));
-    return r;
+    const int t = threadIdx.x & (kPfHalf - 1);
+    HalfRegs h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int kr = min(k0 + 16 * j + (t >> 4), T - 1);
+        h.r[j] = *(reinterpret_cast<const uint4 *>(Kb + (int64_t)kr * 128) + (t & 15));
+    }
+    return h;
 }
 
-// K rows as they are; V transposed: dims 8 (t % 16) + d of keys 2 (t / 16)
-// and +1 as one 32-bit word per dimension.
-__device__ __forceinline__ void tile_store(const TileRegs &r, PfShared &sh, int buf)
+__device__ __forceinline__ HalfRegs v_load(const uint16_t *Vb, int k0, int T)
 {
-    const int t = threadIdx.x;
-    uint4 *kd = reinterpret_cast<uint4 *>(&sh.k[buf][t >> 3][0]) + 2 * (t & 7);
-    kd[0] = r.k0;
-    kd[1] = r.k1;
-    const uint32_t a[4] = {r.va.x, r.va.y, r.va.z, r.va.w};
-    const uint32_t b[4] = {r.vb.x, r.vb.y, r.vb.z, r.vb.w};
-    const int d0 = 8 * (t & 15), kk = 2 * (t >> 4);
+    const int t = threadIdx.x & (kPfHalf - 1);
+    HalfRegs h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint32_t *>(&sh.vt[buf][d0 + 2 * e][kk]) = (a[e] & 0xFFFFu) | (b[e] << 16);
-        *reinterpret_cast<uint32_t *>(&sh.vt[buf][d0 + 2 * e + 1][kk]) = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
+    for (int j = 0; j < 4; ++j) {
+        const int vr = min(k0 + 4 * (t >> 4) + j, T - 1);
+        h.r[j] = *(reinterpret_cast<const uint4 *>(Vb + (int64_t)vr * 128) + (t & 15));
+    }
+    return h;
+}
+
+__device__ __forceinline__ void k_store(const HalfRegs &h, PfShared &sh, int buf)
+{
+    const int t = threadIdx.x & (kPfHalf - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4 *>(&sh.k[buf][(16 * j + (t >> 4)) * kKRow + 8 * (t & 15)]) = h.r[j];
+}
+
+// V transposed: per dimension, the thread's four keys as one 8-B store.
+// Within each 16-key group the 4-key blocks 1 and 2 trade places, so a
+// lane's 8 keys of a product step are contiguous.
+__device__ __forceinline__ void v_store(const HalfRegs &h, PfShared &sh, int buf)
+{
+    const int t = threadIdx.x & (kPfHalf - 1);
+    const int d0 = 8 * (t & 15), sb = (t >> 4) & 3;
+    const int kk = 16 * (t >> 6) + 4 * ((sb == 1) ? 2 : (sb == 2) ? 1 : sb);
+    uint16_t *vt = sh.vt[buf] + (t & 15) * 8;  // the gaps before row d0
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        *reinterpret_cast<uint2 *>(&vt[(d0 + 2 * c) * kVRow + kk]) =
+            make_uint2(__builtin_amdgcn_perm(h.r[1][c], h.r[0][c], 0x05040100u),
+                       __builtin_amdgcn_perm(h.r[3][c], h.r[2][c], 0x05040100u));
+        *reinterpret_cast<uint2 *>(&vt[(d0 + 2 * c + 1) * kVRow + kk]) =
+            make_uint2(__builtin_amdgcn_perm(h.r[1][c], h.r[0][c], 0x07060302u),
+                       __builtin_amdgcn_perm(h.r[3][c], h.r[2][c], 0x07060302u));
     }
 }
 
@@ -133,6 +172,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
     const int lane = lane_id(), w = threadIdx.x / kWave, gl = lane >> 5;
     const int h = g * a.G + hs + w;
     const bool active = hs + w < a.G && h >= a.head_begin && h < a.head_begin + a.n_heads;
+    const bool vgrp = w >= kPfWaves / 2;
 
     const uint16_t *Kb = a.K + ((int64_t)b * a.Hkv + g) * a.kv_cap * 128;
     const uint16_t *Vb = a.V + ((int64_t)b * a.Hkv + g) * a.kv_cap * 128;
@@ -175,50 +215,66 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] = 0.0f;
 
-    tile_store(tile_load(Kb, Vb, tile_k0(0), a.T), sh, 0);
+    const char *lds = reinterpret_cast<const char *>(&sh);
+    const int kl = 2 * ((lane & 31) * kKRow + 8 * gl);
+    const int vl = 2 * (2 * kKBuf + (lane & 31) * kVRow + ((lane & 31) >> 3) * 8 + 8 * gl);
+    // S^T = K Q^T from K buffer kb.
+    auto product_qk = [&](f32x16 (&acc)[2], int kb) {
+        const char *kp = lds + __builtin_amdgcn_readfirstlane(kb * 2 * kKBuf) + kl;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[st][e] = 0.0f;
+#pragma unroll
+        for (int kq = 0; kq < 8; ++kq)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kp + 2 * (32 * st * kKRow + 16 * kq));
+                acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[kq], acc[st], 0, 0, 0);
+            }
+    };
+
+    // K runs one tile ahead of V: the products of an iteration are S^T of
+    // tile it + 1 (K buffer (it + 1) % 2) and O^T += V^T P^T of tile it (V
+    // buffer it % 2); the first group then stages K of tile it + 2 and the
+    // second V of tile it + 1, into the buffers the previous iteration read.
+    HalfRegs rg;
+    if (!vgrp) {
+        k_store(k_load(Kb, tile_k0(0), a.T), sh, 0);
+        if (nt > 1) k_store(k_load(Kb, tile_k0(1), a.T), sh, 1);
+    } else {
+        v_store(v_load(Vb, tile_k0(0), a.T), sh, 0);
+    }
+    __syncthreads();
+    f32x16 s[2], sn[2];
+    if (active) product_qk(s, 0);
     __syncthreads();
     for (int it = 0; it < nt; ++it) {
-        const int buf = it & 1, k0 = tile_k0(it);
-        // The next tile's loads (the last iteration reloads its own tile
-        // into the idle buffer, which nothing reads).
-        const TileRegs rg = tile_load(Kb, Vb, tile_k0(min(it + 1, nt - 1)), a.T);
+        const bool ld = vgrp ? it + 1 < nt : it + 2 < nt;
+        if (ld) rg = vgrp ? v_load(Vb, tile_k0(it + 1), a.T) : k_load(Kb, tile_k0(it + 2), a.T);
         if (active) {
-            f32x16 s[2];
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) s[st][e] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const bf16x8 ka = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const uint4 *>(&sh.k[buf][32 * st + (lane & 31)][16 * ks + 8 * gl]));
-                    s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], s[st], 0, 0, 0);
-                }
-            // Masked keys score -inf; a tile whose every key is allowed for
-            // every query of the block skips the test.
+            const int k0 = tile_k0(it);
+            // Masked keys score -inf (their probability is exactly 0); a tile
+            // whose every key is allowed for every query of the block skips
+            // the test.
             const bool full = k0 + kPfK - 1 <= q0 &&
                               (!local || k0 >= w0_last || k0 + kPfK <= min(a.n_sink, w0_first));
-            uint32_t okm = 0xFFFFFFFFu;  // bit 16 st + e: key allowed
             if (!full) {
-                okm = 0u;
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int key = k0 + 32 * st + 8 * (e >> 2) + 4 * gl + (e & 3);
                         const bool ok = (key <= qc) & (!local | (key < my_sink) | (key >= my_w0));
-                        okm |= (uint32_t)ok << (16 * st + e);
                         s[st][e] = ok ? s[st][e] : -INFINITY;
                     }
             }
             // The query's max over the tile (both lane halves), in log2 units.
-            float tmax = -INFINITY;
+            float tmax = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(s[st][e], s[st][e + 1]));
+                for (int e = 1; e < 16; e += 2) tmax = max3(tmax, s[st][e], s[st][e + (e < 15)]);
             tmax = fmaxf(tmax, shfl_x32(tmax)) * a.qscale;
             // The reference m moves up only when the tile's max exceeds it by
             // more than 8 (so probabilities stay below 2^8): the rescale of
@@ -233,66 +289,60 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
                     for (int e = 0; e < 16; ++e) o[dt][e] *= corr;
                 m = mn;
             }
-            // p = 2^(s * qscale - m), 0 for a masked key.
+            // S^T of the next tile (on the last tile, of a stale buffer,
+            // unused) while p = 2^(s * qscale - m) is taken.
+            product_qk(sn, (it + 1) & 1);
             const float nm = m == -INFINITY ? 0.0f : -m;
             float psum = 0.0f;
-            if (full) {
 #pragma unroll
-                for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], a.qscale, nm));
-                        s[st][e] = p;
-                        psum += p;
-                    }
-            } else {
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const float p = (okm >> (16 * st + e)) & 1u
-                                            ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], a.qscale, nm))
-                                            : 0.0f;
-                        s[st][e] = p;
-                        psum += p;
-                    }
-            }
+                for (int e = 0; e < 16; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], a.qscale, nm));
+                    s[st][e] = p;
+                    psum += p;
+                }
             l += psum + shfl_x32(psum);
+            // O^T += V^T P^T; key-step ks takes elements 8 (ks % 2) .. +7 of
+            // s[ks / 2]: hi = p truncated to bf16 (its top 16 bits), lo = the
+            // exact fp32 residue p - hi rounded to bf16.
+            const char *vp = lds + __builtin_amdgcn_readfirstlane((it & 1) * 2 * kVBuf) + vl;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int st = ks >> 1, i0 = 2 * (ks & 1);
-                // hi = p truncated to bf16 (its top 16 bits), lo = the exact
-                // fp32 residue p - hi rounded to bf16.
+                const int st = ks >> 1, e0 = 8 * (ks & 1);
                 uint32_t hw[4];
-                float pl[8];
+                float lo[8];
 #pragma unroll
                 for (int t = 0; t < 8; t += 2) {
-                    const uint32_t u0 = __float_as_uint(s[st][4 * i0 + t]);
-                    const uint32_t u1 = __float_as_uint(s[st][4 * i0 + t + 1]);
+                    const uint32_t u0 = __float_as_uint(s[st][e0 + t]);
+                    const uint32_t u1 = __float_as_uint(s[st][e0 + t + 1]);
                     hw[t / 2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-                    pl[t] = __uint_as_float(u0) - __uint_as_float(u0 & 0xFFFF0000u);
-                    pl[t + 1] = __uint_as_float(u1) - __uint_as_float(u1 & 0xFFFF0000u);
+                    lo[t] = __uint_as_float(u0) - __uint_as_float(u0 & 0xFFFF0000u);
+                    lo[t + 1] = __uint_as_float(u1) - __uint_as_float(u1 & 0xFFFF0000u);
                 }
                 const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-                const bf16x8 bl = to_bf16x8(pl);
+                const bf16x8 bl = to_bf16x8(lo);
 #pragma unroll
                 for (int dp = 0; dp < 4; dp += 2) {
-                    bf16x8 va[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const uint16_t *vr = &sh.vt[buf][32 * (dp + u) + (lane & 31)][16 * ks + 4 * gl];
-                        const uint2 v0 = *reinterpret_cast<const uint2 *>(vr);
-                        const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 8);
-                        va[u] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-                    }
-                    o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], bh, o[dp], 0, 0, 0);
-                    o[dp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], bh, o[dp + 1], 0, 0, 0);
-                    o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], bl, o[dp], 0, 0, 0);
-                    o[dp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], bl, o[dp + 1], 0, 0, 0);
+                    const bf16x8 v0 =
+                        *reinterpret_cast<const bf16x8 *>(vp + 2 * (32 * dp * kVRow + 4 * dp * 8 + 16 * ks));
+                    const bf16x8 v1 = *reinterpret_cast<const bf16x8 *>(
+                        vp + 2 * (32 * (dp + 1) * kVRow + 4 * (dp + 1) * 8 + 16 * ks));
+                    o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, bh, o[dp], 0, 0, 0);
+                    o[dp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, bh, o[dp + 1], 0, 0, 0);
+                    o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, bl, o[dp], 0, 0, 0);
+                    o[dp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, bl, o[dp + 1], 0, 0, 0);
                 }
             }
+            s[0] = sn[0];
+            s[1] = sn[1];
         }
-        tile_store(rg, sh, buf ^ 1);
+        if (ld) {
+            if (vgrp)
+                v_store(rg, sh, (it + 1) & 1);
+            else
+                k_store(rg, sh, it & 1);
+        }
         __syncthreads();
     }
     if (!active || my_q >= a.T) return;
@@ -328,7 +378,10 @@ hipError_t launch_prefill_attend(const uint16_t *q, const uint16_t *K, const uin
     a.n_sink = n_sink;
     a.window = window;
     a.kv_cap = kv_cap;
-    a.qscale = fabsf(scale) * kPfLog2e;
+    // Clamped above zero so that -inf * qscale stays -inf.  At the clamp,
+    // s * qscale - m is below 1e-8 in magnitude for any scores within 1e22
+    // of each other, so 2^x rounds to exactly 1, as scale = 0 requires.
+    a.qscale = fmaxf(fabsf(scale) * kPfLog2e, 1e-30f);
     a.qsign = scale < 0.0f ? 0x80008000u : 0u;
     a.G = Hq / Hkv;
     a.hc = (a.G + kPfWaves - 1) / kPfWaves;
