@@ -13,8 +13,8 @@
 // query positions and up to 8 query heads of one KV head, one wave per head,
 // and walks the allowed keys in tiles of 64.  Each tile's K rows and V^T
 // (V transposed: one row per dimension) are staged once in LDS for all the
-// block's heads: waves 0-3 stage K, waves 4-7 V, each load covering whole
-// rows.  Per wave and tile (v_mfma_f32_32x32x16_bf16):
+// block's heads: waves 0-3 stage K, waves 4-7 V.  Per wave and tile
+// (v_mfma_f32_32x32x16_bf16):
 //
 //   S^T = K Q^T   2 key halves x 8 dim steps: A = 8 dims of one key row (one
 //                 16-B LDS read), B = Q^T (the wave's 32 queries, held in
@@ -74,7 +74,7 @@ struct PfArgs {
 
 constexpr int kPfHalf = kPfThreads / 2;       // threads of one wave group
 constexpr int kKBuf = kPfK * kKRow;           // bf16 per K buffer
-constexpr int kVBuf = 128 * kVRow + 16 * 8;   // bf16 per V^T buffer (a 16-B gap after every 8 rows)
+constexpr int kVBuf = 128 * kVRow;            // bf16 per V^T buffer
 
 struct PfShared {
     uint16_t k[2][kKBuf];
@@ -107,9 +107,11 @@ struct HalfRegs {
 };
 
 // The first wave group stages K rows, the second V rows.  Thread t of a
-// group: K rows t / 16 + 16 j, dims 8 (t % 16) .. +7; or V rows 4 (t / 16)
-// + j, dims 8 (t % 16) .. +7 (j < 4): each load covers whole rows.  Rows past the prompt read
-// row T - 1 (their keys are masked).
+// group loads, for j < 4: K row 16 j + t / 16, dims 8 (t % 16) .. +7 (each
+// load covers whole rows); or V row 4 (t % 16) + j, dims 8 (t / 16) .. +7
+// (64-B pieces of 16 rows, so that the transposing LDS stores of a wave
+// spread over every bank).  Rows past the prompt read row T - 1 (their keys
+// are masked).
 __device__ __forceinline__ HalfRegs k_load(const uint16_t *Kb, int k0, int T)
 {
     const int t = threadIdx.x & (kPfHalf - 1);
@@ -128,8 +130,8 @@ __device__ __forceinline__ HalfRegs v_load(const uint16_t *Vb, int k0, int T)
     HalfRegs h;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int vr = min(k0 + 4 * (t >> 4) + j, T - 1);
-        h.r[j] = *(reinterpret_cast<const uint4 *>(Vb + (int64_t)vr * 128) + (t & 15));
+        const int vr = min(k0 + 4 * (t & 15) + j, T - 1);
+        h.r[j] = *(reinterpret_cast<const uint4 *>(Vb + (int64_t)vr * 128) + (t >> 4));
     }
     return h;
 }
@@ -142,15 +144,16 @@ __device__ __forceinline__ void k_store(const HalfRegs &h, PfShared &sh, int buf
         *reinterpret_cast<uint4 *>(&sh.k[buf][(16 * j + (t >> 4)) * kKRow + 8 * (t & 15)]) = h.r[j];
 }
 
-// V transposed: per dimension, the thread's four keys as one 8-B store.
-// Within each 16-key group the 4-key blocks 1 and 2 trade places, so a
-// lane's 8 keys of a product step are contiguous.
+// V transposed: per dimension, the thread's four keys as one 8-B store; the
+// 16 lanes of a dimension row write 128 contiguous bytes.  Within each
+// 16-key group the 4-key blocks 1 and 2 trade places, so a lane's 8 keys of
+// a product step are contiguous (one 16-B read).
 __device__ __forceinline__ void v_store(const HalfRegs &h, PfShared &sh, int buf)
 {
     const int t = threadIdx.x & (kPfHalf - 1);
-    const int d0 = 8 * (t & 15), sb = (t >> 4) & 3;
-    const int kk = 16 * (t >> 6) + 4 * ((sb == 1) ? 2 : (sb == 2) ? 1 : sb);
-    uint16_t *vt = sh.vt[buf] + (t & 15) * 8;  // the gaps before row d0
+    const int d0 = 8 * (t >> 4), sb = t & 3;
+    const int kk = 16 * ((t >> 2) & 3) + 4 * ((sb == 1) ? 2 : (sb == 2) ? 1 : sb);
+    uint16_t *vt = sh.vt[buf];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         *reinterpret_cast<uint2 *>(&vt[(d0 + 2 * c) * kVRow + kk]) =
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
 
     const char *lds = reinterpret_cast<const char *>(&sh);
     const int kl = 2 * ((lane & 31) * kKRow + 8 * gl);
-    const int vl = 2 * (2 * kKBuf + (lane & 31) * kVRow + ((lane & 31) >> 3) * 8 + 8 * gl);
+    const int vl = 2 * (2 * kKBuf + (lane & 31) * kVRow + 8 * gl);
     // S^T = K Q^T from K buffer kb.
     auto product_qk = [&](f32x16 (&acc)[2], int kb) {
         const char *kp = lds + __builtin_amdgcn_readfirstlane(kb * 2 * kKBuf) + kl;
@@ -324,10 +327,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
                 const bf16x8 bl = to_bf16x8(lo);
 #pragma unroll
                 for (int dp = 0; dp < 4; dp += 2) {
-                    const bf16x8 v0 =
-                        *reinterpret_cast<const bf16x8 *>(vp + 2 * (32 * dp * kVRow + 4 * dp * 8 + 16 * ks));
-                    const bf16x8 v1 = *reinterpret_cast<const bf16x8 *>(
-                        vp + 2 * (32 * (dp + 1) * kVRow + 4 * (dp + 1) * 8 + 16 * ks));
+                    const bf16x8 v0 = *reinterpret_cast<const bf16x8 *>(vp + 2 * (32 * dp * kVRow + 16 * ks));
+                    const bf16x8 v1 =
+                        *reinterpret_cast<const bf16x8 *>(vp + 2 * (32 * (dp + 1) * kVRow + 16 * ks));
                     o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, bh, o[dp], 0, 0, 0);
                     o[dp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, bh, o[dp + 1], 0, 0, 0);
                     o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, bl, o[dp], 0, 0, 0);
