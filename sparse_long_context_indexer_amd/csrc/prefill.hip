@@ -9,26 +9,27 @@
 //
 // with softmax(scale * q . k) over those keys, fp32 softmax and output.
 //
-// Matrix cores (bf16 in, fp32 accumulate), flash-style.  A block takes 32
-// query positions and up to 8 query heads of one KV head, one wave per head,
-// and walks the allowed keys in tiles of 64.  Each tile's K rows and V^T
-// (V transposed: one row per dimension) are staged once in LDS for all the
-// block's heads: waves 0-3 stage K, waves 4-7 V.  Per wave and tile
-// (v_mfma_f32_32x32x16_bf16):
+// Matrix cores (fp32 accumulate), flash-style.  A block takes 32 query
+// positions and up to 8 query heads of one KV head, one wave per head, and
+// walks the allowed keys in tiles of 64.  Each tile's K rows and V^T (V
+// transposed: one row per dimension, converted to fp16) are staged once in
+// LDS for all the block's heads: waves 0-3 stage K, waves 4-7 V.  Per wave
+// and tile:
 //
-//   S^T = K Q^T   2 key halves x 8 dim steps: A = 8 dims of one key row (one
-//                 16-B LDS read), B = Q^T (the wave's 32 queries, held in
-//                 registers).  Lane l then holds query l%32 and keys
-//                 8i + 4(l/32) + j of each half (i, j < 4).
-//   O^T += V^T P^T  4 dim tiles x 4 key steps of 16.  The 16 keys of a step
-//                 enter in the order the lanes already hold them: a lane of
-//                 half g supplies keys 4g + (0..3) and 8 + 4g + (0..3), as
-//                 B = its own probabilities and as A = one 16-B read of V^T,
-//                 whose key blocks are stored in that order.
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, 2 key halves x 8 dim steps:
+//                 A = 8 dims of one key row (one 16-B LDS read), B = Q^T (the
+//                 wave's 32 queries, held in registers).  Lane l then holds
+//                 query l%32 and keys 8i + 4(l/32) + j of each half (i, j < 4).
+//   O^T += V^T P^T  v_mfma_f32_32x32x16_f16, 4 dim tiles x 4 key steps of 16.
+//                 The 16 keys of a step enter in the order the lanes already
+//                 hold them: a lane of half g supplies keys 4g + (0..3) and
+//                 8 + 4g + (0..3), as B = its own probabilities and as A =
+//                 one 16-B read of V^T, whose key blocks are stored in that
+//                 order.
 //
 // The two products of an iteration belong to different tiles: S^T of tile
 // it + 1 is issued in the same basic block as the exponentials of tile it,
-// and O^T += V^T P^T of tile it beside the bf16 split of its P, so each
+// and O^T += V^T P^T of tile it beside the fp16 rounding of its P, so each
 // wave's matrix-core work overlaps its own vector work.  K is staged one
 // tile ahead of V (two buffers each).
 //
@@ -36,9 +37,15 @@
 // query: the online-softmax rescale needs no exchange, and a query's max and
 // sum combine the lane's 32 values with those of lane l ^ 32.  The softmax
 // reference moves up only when a tile's max exceeds it by more than 8 (log2
-// units), so probabilities stay below 2^8 and the rescale of O is rare.  P
-// enters the second product as a bf16 pair (its top 16 bits, and the exact
-// residue rounded to bf16), so it is carried to about 2^-16.
+// units), so probabilities stay below 2^8 and the rescale of O is rare.
+// Precision: V's bf16 values are exact in fp16 (up to 2^16 in magnitude; a
+// dimension tile holding larger ones is staged scaled, see v_store).  P is
+// rounded to fp16 (at most 2^-11 relative) and the softmax sum l adds the
+// same rounded values, so each output is an exact average of V rows under
+// weights within 2^-10 (relative) of the true ones: its error is at most
+// 2^-10 of the weighted mean of |v - out|.  P carries a factor 2^7, which l
+// cancels, so that fp16 keeps weights at full precision down to 2^-21 of
+// the reference's.
 #include <math.h>
 
 #include "rtp_device.h"
@@ -49,6 +56,9 @@ namespace rtp {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPfWaves = 8;                   // query heads per block, one per wave
@@ -58,6 +68,7 @@ constexpr int kPfK = 64;                      // keys per tile
 constexpr int kKRow = 128 + 8;                // bf16 per staged K row (272 B: rows 4 banks apart)
 constexpr int kVRow = kPfK + 8;               // bf16 per staged V^T row (144 B, 16-B aligned)
 constexpr float kPfLog2e = 1.4426950408889634f;
+constexpr float kPfPScale = 7.0f;              // log2 of the factor carried by P
 
 struct PfArgs {
     const uint16_t *q, *K, *V;
@@ -78,8 +89,12 @@ constexpr int kVBuf = 128 * kVRow;            // bf16 per V^T buffer
 
 struct PfShared {
     uint16_t k[2][kKBuf];
-    uint16_t vt[2][kVBuf];
+    uint16_t vt[2][kVBuf];          // V^T in fp16, each dimension tile scaled by 2^-vshift
+    int32_t vshift[2][kPfWaves / 2];  // per dimension tile: its scale shift (0 almost always)
 };
+
+// Magnitude bits of the smallest bf16 value that fp16 cannot hold (2^16).
+constexpr uint32_t kBf16F16Over = 0x4780u;
 
 __device__ __forceinline__ float shfl_x32(float v)
 {
@@ -90,15 +105,6 @@ __device__ __forceinline__ float max3(float a, float b, float c)
 {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-
-// Eight floats as bf16, rounded to nearest even.
-__device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8])
-{
-    bf16x8 r;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) r[t] = static_cast<__bf16>(x[t]);
     return r;
 }
 
@@ -144,15 +150,56 @@ __device__ __forceinline__ void k_store(const HalfRegs &h, PfShared &sh, int buf
         *reinterpret_cast<uint4 *>(&sh.k[buf][(16 * j + (t >> 4)) * kKRow + 8 * (t & 15)]) = h.r[j];
 }
 
-// V transposed: per dimension, the thread's four keys as one 8-B store; the
-// 16 lanes of a dimension row write 128 contiguous bytes.  Within each
-// 16-key group the 4-key blocks 1 and 2 trade places, so a lane's 8 keys of
-// a product step are contiguous (one 16-B read).
-__device__ __forceinline__ void v_store(const HalfRegs &h, PfShared &sh, int buf)
+// Two bf16 values as two fp16 values, scaled by 2^-k (round to nearest
+// even).  With k = 0 this is exact for magnitudes in [2^-14, 2^16), where
+// fp16 holds every bf16 value.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, int k)
+{
+    float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
+    if (k != 0) {
+        lo = __builtin_amdgcn_ldexpf(lo, -k);
+        hi = __builtin_amdgcn_ldexpf(hi, -k);
+    }
+    const f16x2 c = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+    return __builtin_bit_cast(uint32_t, c);
+}
+
+// V transposed, in fp16: per dimension, the thread's four keys as one 8-B
+// store; the 16 lanes of a dimension row write 128 contiguous bytes.  Within
+// each 16-key group the 4-key blocks 1 and 2 trade places, so a lane's 8
+// keys of a product step are contiguous (one 16-B read).  Staging wave i
+// holds dimensions 32 i .. 32 i + 31 of the tile's 64 keys, which is one
+// dimension tile of the second product.  If one of them has a magnitude of
+// 2^16 or more (beyond fp16), the wave stores them all scaled by 2^-k, k
+// the smallest shift that brings the largest below 2^16, and records k: the
+// product then scales that tile's accumulators by 2^-k before and 2^k after
+// (exact in fp32).  Every value keeps its bf16 bits unless the shift takes
+// it below fp16's normal range, and then stays within 2^-40 of the largest
+// magnitude of its dimension tile.
+__device__ __forceinline__ void v_store(HalfRegs h, PfShared &sh, int buf)
 {
     const int t = threadIdx.x & (kPfHalf - 1);
     const int d0 = 8 * (t >> 4), sb = t & 3;
     const int kk = 16 * ((t >> 2) & 3) + 4 * ((sb == 1) ? 2 : (sb == 2) ? 1 : sb);
+    u16x2 mag = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, h.r[j][c] & 0x7FFF7FFFu));
+    const uint32_t mx = mag.x > mag.y ? mag.x : mag.y;
+    int k = 0;
+    if (__ballot(mx >= kBf16F16Over)) {
+        // The largest magnitude's binade: as floats, these bit patterns
+        // order like the magnitudes.
+        const uint32_t wm = __float_as_uint(wave_max(__uint_as_float(mx << 16))) >> 16;
+        k = (int)(wm >> 7) - 127 - 15;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) h.r[j][c] = bf16x2_to_f16x2(h.r[j][c], k);
+    if (lane_id() == 0) sh.vshift[buf][(threadIdx.x >> 6) & (kPfWaves / 2 - 1)] = k;
     uint16_t *vt = sh.vt[buf];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -295,47 +342,60 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
             // S^T of the next tile (on the last tile, of a stale buffer,
             // unused) while p = 2^(s * qscale - m) is taken.
             product_qk(sn, (it + 1) & 1);
-            const float nm = m == -INFINITY ? 0.0f : -m;
-            float psum = 0.0f;
+            // Probabilities carry a factor 2^7 (cancelled by l): they lie
+            // in (0, 2^15], and fp16 keeps them to 2^-11 relative down to
+            // 2^-21 of the reference's weight.
+            const float nm = m == -INFINITY ? 0.0f : kPfPScale - m;
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], a.qscale, nm));
-                    s[st][e] = p;
-                    psum += p;
-                }
-            l += psum + shfl_x32(psum);
+                for (int e = 0; e < 16; ++e)
+                    s[st][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], a.qscale, nm));
             // O^T += V^T P^T; key-step ks takes elements 8 (ks % 2) .. +7 of
-            // s[ks / 2]: hi = p truncated to bf16 (its top 16 bits), lo = the
-            // exact fp32 residue p - hi rounded to bf16.
+            // s[ks / 2].  P enters as fp16 (round to nearest even) and l
+            // sums the same rounded values.
+            const int *vsh = sh.vshift[it & 1];
+            const bool scaled = __builtin_amdgcn_readfirstlane(vsh[0] | vsh[1] | vsh[2] | vsh[3]) != 0;
+            if (scaled) {
+#pragma unroll
+                for (int dp = 0; dp < 4; ++dp) {
+                    const float f = __builtin_amdgcn_ldexpf(1.0f, -vsh[dp]);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[dp][e] *= f;
+                }
+            }
             const char *vp = lds + __builtin_amdgcn_readfirstlane((it & 1) * 2 * kVBuf) + vl;
+            const f16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+            float psum = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int st = ks >> 1, e0 = 8 * (ks & 1);
-                uint32_t hw[4];
-                float lo[8];
+                f16x8 ph;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) ph[t] = static_cast<_Float16>(s[st][e0 + t]);
 #pragma unroll
                 for (int t = 0; t < 8; t += 2) {
-                    const uint32_t u0 = __float_as_uint(s[st][e0 + t]);
-                    const uint32_t u1 = __float_as_uint(s[st][e0 + t + 1]);
-                    hw[t / 2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-                    lo[t] = __uint_as_float(u0) - __uint_as_float(u0 & 0xFFFF0000u);
-                    lo[t + 1] = __uint_as_float(u1) - __uint_as_float(u1 & 0xFFFF0000u);
+                    const f16x2 pr = {ph[t], ph[t + 1]};
+                    psum = __builtin_amdgcn_fdot2(pr, one, psum, false);
                 }
-                const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-                const bf16x8 bl = to_bf16x8(lo);
 #pragma unroll
                 for (int dp = 0; dp < 4; dp += 2) {
-                    const bf16x8 v0 = *reinterpret_cast<const bf16x8 *>(vp + 2 * (32 * dp * kVRow + 16 * ks));
-                    const bf16x8 v1 =
-                        *reinterpret_cast<const bf16x8 *>(vp + 2 * (32 * (dp + 1) * kVRow + 16 * ks));
-                    o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, bh, o[dp], 0, 0, 0);
-                    o[dp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, bh, o[dp + 1], 0, 0, 0);
-                    o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, bl, o[dp], 0, 0, 0);
-                    o[dp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, bl, o[dp + 1], 0, 0, 0);
+                    const f16x8 v0 = *reinterpret_cast<const f16x8 *>(vp + 2 * (32 * dp * kVRow + 16 * ks));
+                    const f16x8 v1 =
+                        *reinterpret_cast<const f16x8 *>(vp + 2 * (32 * (dp + 1) * kVRow + 16 * ks));
+                    o[dp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0, ph, o[dp], 0, 0, 0);
+                    o[dp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1, ph, o[dp + 1], 0, 0, 0);
                 }
             }
+            if (scaled) {
+#pragma unroll
+                for (int dp = 0; dp < 4; ++dp) {
+                    const float f = __builtin_amdgcn_ldexpf(1.0f, vsh[dp]);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[dp][e] *= f;
+                }
+            }
+            l += psum + shfl_x32(psum);
             s[0] = sn[0];
             s[1] = sn[1];
         }

@@ -357,6 +357,51 @@ def test_prefill_attend_scale_sign(scale_kind):
             assert ok, (scale_kind, h, t, err, rel)
 
 
+def test_prefill_attend_v_beyond_fp16():
+    # V values of 2^16 and more (beyond fp16, in which the kernel stages V):
+    # their dimension tiles are staged scaled by a power of two.  A tiny value
+    # beside a large one in the same tile, dense and sinks + window heads,
+    # every third query against the oracle: |err| <= 2e-3 + (2^-9 + 1e-5) *
+    # sum_i w_i |v_i|.  The kernel rounds P to fp16 and normalises by the sum
+    # of the rounded weights, so each output is an average of V rows under
+    # weights within 2^-10 (relative) of the exact ones: the error scales with
+    # the magnitude of V (the 1e-5 covers fp32 accumulation).
+    B, Hq, Hkv, T = 1, 8, 2, 700
+    q = synth.normal_bf16(synth.key(91, 1), 0, B * Hq * T * 128).reshape(B, Hq, T, 128)
+    K = synth.normal_bf16(synth.key(91, 2), 0, B * Hkv * T * 128).reshape(B, Hkv, T, 128)
+    V = synth.normal_bf16(synth.key(91, 3), 0, B * Hkv * T * 128).reshape(B, Hkv, T, 128)
+
+    def bf(x):
+        return np.uint16(np.array([x], np.float32).view(np.uint32)[0] >> 16)
+    for g in range(Hkv):
+        V[0, g, 70, 5] = bf(327680.0)        # 1.25 * 2^18
+        V[0, g, 71, 6] = bf(2.0 ** -16)      # below fp16's normal range once scaled
+        V[0, g, 300, 100] = bf(-2621440.0)   # -1.25 * 2^21
+        V[0, g, 650, 40] = bf(69632.0)       # 1.0625 * 2^16
+        V[0, g, 651, 41] = bf(65280.0)       # the largest bf16 below 2^16 (no scaling)
+    scale = 1.0 / math.sqrt(128.0)
+    out = torch.full((B, Hq, T, 128), float("nan"), dtype=torch.float32, device=dev())
+    qd = torch.from_numpy(q.view(np.int16)).to(dev())
+    Kd = torch.from_numpy(K.view(np.int16)).to(dev())
+    Vd = torch.from_numpy(V.view(np.int16)).to(dev())
+    rtp.rtp_prefill_attend(qd, Kd, Vd, 0, 4, 0, 0, scale, out)
+    rtp.rtp_prefill_attend(qd, Kd, Vd, 4, 4, 4, 200, scale, out)
+    got = out.cpu().numpy()
+    Vabs = V & np.uint16(0x7FFF)
+    worst = 0.0
+    for h in range(Hq):
+        g = h // 4
+        for t in range(0, T, 3):
+            rows = np.arange(t + 1) if h < 4 else oracle.local_rows(t + 1, 4, 200)
+            ref = oracle.attention(q[0, h, t], K[0, g, rows], V[0, g, rows], scale)
+            mag = oracle.attention(q[0, h, t], K[0, g, rows], Vabs[0, g, rows], scale)
+            err = np.abs(got[0, h, t].astype(np.float64) - ref)
+            bound = 2e-3 + (2.0 ** -9 + 1e-5) * mag
+            assert np.all(err <= bound), (h, t, float(np.max(err - bound)))
+            worst = max(worst, float(np.max(err / bound)))
+    print(f"worst error / bound: {worst:.3g}")
+
+
 def test_prefill_attend_benched_size():
     # The size the benchmark times: a 16384-token prompt, 32 query heads on
     # 4 KV heads, heads 0-7 dense and heads 8-31 on 4 sinks + a 4096-token
@@ -379,6 +424,7 @@ def test_prefill_attend_benched_size():
     ts = np.unique(np.concatenate([np.arange(5), np.arange(window - 3, window + 3),
                                    rng.integers(0, T, 8), np.arange(T - 4, T)]))
     heads = [0, 3, 7, 8, 19, 31]
+    worst = 0.0
     got = out[:, heads][:, :, torch.from_numpy(ts).to(dev())].cpu().numpy()
     assert not torch.isnan(out).any().item()
     del out
@@ -390,6 +436,8 @@ def test_prefill_attend_benched_size():
                 ref = oracle.attention(q[b, h, t], K[b, h // 8, rows], V[b, h // 8, rows], scale)
                 ok, err, rel = judge_out(got[b, hi, ti], ref)
                 assert ok, (b, h, t, err, rel)
+                worst = max(worst, err)
+    print(f"largest abs error: {worst:.3g} (bound 2e-3)")
 
 
 # -------------------------------------------------------------- projection
