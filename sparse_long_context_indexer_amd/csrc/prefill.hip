@@ -299,7 +299,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
     f32x16 s[2], sn[2];
     if (active) product_qk(s, 0);
     __syncthreads();
-    for (int it = 0; it < nt; ++it) {
+    // One tile: cur holds its S^T, nxt receives the next tile's.  Two tiles
+    // per loop trip with the roles swapped, so no copy moves nxt to cur.
+    auto step = [&](int it, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
         const bool ld = vgrp ? it + 1 < nt : it + 2 < nt;
         if (ld) rg = vgrp ? v_load(Vb, tile_k0(it + 1), a.T) : k_load(Kb, tile_k0(it + 2), a.T);
         if (active) {
@@ -316,15 +318,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
                     for (int e = 0; e < 16; ++e) {
                         const int key = k0 + 32 * st + 8 * (e >> 2) + 4 * gl + (e & 3);
                         const bool ok = (key <= qc) & (!local | (key < my_sink) | (key >= my_w0));
-                        s[st][e] = ok ? s[st][e] : -INFINITY;
+                        cur[st][e] = ok ? cur[st][e] : -INFINITY;
                     }
             }
             // The query's max over the tile (both lane halves), in log2 units.
-            float tmax = fmaxf(s[0][0], s[1][0]);
+            float tmax = fmaxf(cur[0][0], cur[1][0]);
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int e = 1; e < 16; e += 2) tmax = max3(tmax, s[st][e], s[st][e + (e < 15)]);
+                for (int e = 1; e < 16; e += 2) tmax = max3(tmax, cur[st][e], cur[st][e + (e < 15)]);
             tmax = fmaxf(tmax, shfl_x32(tmax)) * a.qscale;
             // The reference m moves up only when the tile's max exceeds it by
             // more than 8 (so probabilities stay below 2^8): the rescale of
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
             }
             // S^T of the next tile (on the last tile, of a stale buffer,
             // unused) while p = 2^(s * qscale - m) is taken.
-            product_qk(sn, (it + 1) & 1);
+            product_qk(nxt, (it + 1) & 1);
             // Probabilities carry a factor 2^7 (cancelled by l): they lie
             // in (0, 2^15], and fp16 keeps them to 2^-11 relative down to
             // 2^-21 of the reference's weight.
@@ -350,9 +352,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    s[st][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], a.qscale, nm));
+                    cur[st][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[st][e], a.qscale, nm));
             // O^T += V^T P^T; key-step ks takes elements 8 (ks % 2) .. +7 of
-            // s[ks / 2].  P enters as fp16 (round to nearest even) and l
+            // cur[ks / 2].  P enters as fp16 (round to nearest even) and l
             // sums the same rounded values.
             const int *vsh = sh.vshift[it & 1];
             const bool scaled = __builtin_amdgcn_readfirstlane(vsh[0] | vsh[1] | vsh[2] | vsh[3]) != 0;
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
                 const int st = ks >> 1, e0 = 8 * (ks & 1);
                 f16x8 ph;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) ph[t] = static_cast<_Float16>(s[st][e0 + t]);
+                for (int t = 0; t < 8; ++t) ph[t] = static_cast<_Float16>(cur[st][e0 + t]);
 #pragma unroll
                 for (int t = 0; t < 8; t += 2) {
                     const f16x2 pr = {ph[t], ph[t + 1]};
@@ -396,8 +398,6 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
                 }
             }
             l += psum + shfl_x32(psum);
-            s[0] = sn[0];
-            s[1] = sn[1];
         }
         if (ld) {
             if (vgrp)
@@ -406,7 +406,13 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
                 k_store(rg, sh, it & 1);
         }
         __syncthreads();
+    };
+    int it = 0;
+    for (; it + 1 < nt; it += 2) {
+        step(it, s, sn);
+        step(it + 1, sn, s);
     }
+    if (it < nt) step(it, s, sn);
     if (!active || my_q >= a.T) return;
     // out[q][dim] = O / l: lane l holds dims 32 dt + 8 i + 4 (l/32) + j.
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
