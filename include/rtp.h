@@ -354,9 +354,15 @@ rtp_status rtp_local_decode_ring(const rtp_bf16 *q, const rtp_bf16 *K,
  *   out[b][h][t][:] = sum_i softmax_i(scale * q[b][h][t] . K[b][g][i]) * V[b][g][i][:]
  *
  * with g = h / (Hq/Hkv): the local rows of each t are those rtp_local_decode
- * reads with N = t + 1.  bf16 products and fp32 accumulation on the matrix
- * cores, fp32 softmax (the probabilities enter the second product as a bf16
- * pair, good to about 2^-16), fp32 output.
+ * reads with N = t + 1.  Matrix cores with fp32 accumulation: q.K in bf16;
+ * the second product takes the probabilities rounded to fp16 (2^-11
+ * relative) and V converted to fp16 (exact below 2^16 in magnitude; a block
+ * of 32 dimensions x 64 keys holding a larger value is scaled by a power of
+ * two, each value then kept to within 2^-40 of the block's largest), and
+ * the softmax sum adds the same rounded probabilities: each output is an
+ * average of V rows under weights within 2^-10 (relative) of the exact
+ * softmax, so its error is at most 2^-10 of the weighted mean of
+ * |V - out|.  fp32 softmax and output.
  *
  *   q      bf16 [B][Hq][T][d]       16-B aligned (the prompt's queries, post-RoPE)
  *   K, V   bf16 [B][Hkv][kv_cap][d] 16-B aligned; rows [0, T) are the prompt
