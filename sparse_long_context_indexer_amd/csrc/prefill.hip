@@ -96,9 +96,14 @@ struct PfShared {
 // Magnitude bits of the smallest bf16 value that fp16 cannot hold (2^16).
 constexpr uint32_t kBf16F16Over = 0x4780u;
 
-__device__ __forceinline__ float shfl_x32(float v)
+// v of this lane and of lane l ^ 32 (a VALU swap of the wave's halves).
+struct X32 {
+    float a, b;
+};
+__device__ __forceinline__ X32 pair_x32(float v)
 {
-    return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((lane_id() ^ 32) << 2), __float_as_int(v)));
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
 __device__ __forceinline__ float max3(float a, float b, float c)
@@ -327,7 +332,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int e = 1; e < 16; e += 2) tmax = max3(tmax, cur[st][e], cur[st][e + (e < 15)]);
-            tmax = fmaxf(tmax, shfl_x32(tmax)) * a.qscale;
+            const X32 tp = pair_x32(tmax);
+            tmax = fmaxf(tp.a, tp.b) * a.qscale;
             // The reference m moves up only when the tile's max exceeds it by
             // more than 8 (so probabilities stay below 2^8): the rescale of
             // O and l is rare after the first tiles.
@@ -397,7 +403,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
                     for (int e = 0; e < 16; ++e) o[dp][e] *= f;
                 }
             }
-            l += psum + shfl_x32(psum);
+            const X32 pp = pair_x32(psum);
+            l += pp.a + pp.b;
         }
         if (ld) {
             if (vgrp)
