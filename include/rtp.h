@@ -356,9 +356,10 @@ rtp_status rtp_local_decode_ring(const rtp_bf16 *q, const rtp_bf16 *K,
  * with g = h / (Hq/Hkv): the local rows of each t are those rtp_local_decode
  * reads with N = t + 1.  Matrix cores with fp32 accumulation: q.K in bf16;
  * the second product takes the probabilities rounded to fp16 (2^-11
- * relative) and V converted to fp16 (exact below 2^16 in magnitude; a block
- * of 32 dimensions x 64 keys holding a larger value is scaled by a power of
- * two, each value then kept to within 2^-40 of the block's largest), and
+ * relative) and V converted to fp16 (exact for magnitudes in [2^-14, 2^16);
+ * a block of 32 dimensions x 64 keys whose largest magnitude is 2^16 or
+ * more, or below 2^-10, is scaled by a power of two, each value then kept
+ * to within 2^-40 of the block's largest), and
  * the softmax sum adds the same rounded probabilities: each output is an
  * average of V rows under weights within 2^-10 (relative) of the exact
  * softmax, so its error is at most 2^-10 of the weighted mean of

@@ -95,6 +95,11 @@ struct PfShared {
 
 // Magnitude bits of the smallest bf16 value that fp16 cannot hold (2^16).
 constexpr uint32_t kBf16F16Over = 0x4780u;
+// Biased binade below which a dimension tile's largest value is scaled up
+// (2^-10), and the largest upward shift (the tile's scale factor 2^-k must
+// stay a finite float).
+constexpr int kSmallBinade = 117;
+constexpr int kMaxUp = 100;
 
 // v of this lane and of lane l ^ 32 (a VALU swap of the wave's halves).
 struct X32 {
@@ -157,7 +162,8 @@ __device__ __forceinline__ void k_store(const HalfRegs &h, PfShared &sh, int buf
 
 // Two bf16 values as two fp16 values, scaled by 2^-k (round to nearest
 // even).  With k = 0 this is exact for magnitudes in [2^-14, 2^16), where
-// fp16 holds every bf16 value.
+// fp16 holds every bf16 value; ldexp is exact while the result stays a
+// normal float.
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, int k)
 {
     float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
@@ -174,13 +180,14 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, int k)
 // each 16-key group the 4-key blocks 1 and 2 trade places, so a lane's 8
 // keys of a product step are contiguous (one 16-B read).  Staging wave i
 // holds dimensions 32 i .. 32 i + 31 of the tile's 64 keys, which is one
-// dimension tile of the second product.  If one of them has a magnitude of
-// 2^16 or more (beyond fp16), the wave stores them all scaled by 2^-k, k
-// the smallest shift that brings the largest below 2^16, and records k: the
-// product then scales that tile's accumulators by 2^-k before and 2^k after
-// (exact in fp32).  Every value keeps its bf16 bits unless the shift takes
-// it below fp16's normal range, and then stays within 2^-40 of the largest
-// magnitude of its dimension tile.
+// dimension tile of the second product.  If their largest magnitude is 2^16
+// or more (beyond fp16) or below 2^-10, the wave stores them all scaled by
+// 2^-k, the shift that brings the largest into [2^15, 2^16), and records k:
+// the product then scales that tile's accumulators by 2^-k before and 2^k
+// after (exact in fp32).  Every value keeps its bf16 bits unless it lies
+// below fp16's normal range after the shift, and then stays within 2^-40 of
+// the largest magnitude of its dimension tile (2^-25 absolute when the
+// largest is at least 2^-10 and no shift is applied).
 __device__ __forceinline__ void v_store(HalfRegs h, PfShared &sh, int buf)
 {
     const int t = threadIdx.x & (kPfHalf - 1);
@@ -193,12 +200,19 @@ __device__ __forceinline__ void v_store(HalfRegs h, PfShared &sh, int buf)
         for (int c = 0; c < 4; ++c)
             mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, h.r[j][c] & 0x7FFF7FFFu));
     const uint32_t mx = mag.x > mag.y ? mag.x : mag.y;
+    // Scaled down when the largest magnitude is 2^16 or more (beyond fp16),
+    // up when it is below 2^-10 (so that values near it stay in fp16's
+    // normal range): either way the largest lands in [2^15, 2^16).  All-zero
+    // tiles stay.
+    const bool big = __ballot(mx >= kBf16F16Over) != 0;
+    const bool small = __ballot(mx >= (uint32_t)(kSmallBinade << 7)) == 0 && __ballot(mx != 0u) != 0;
     int k = 0;
-    if (__ballot(mx >= kBf16F16Over)) {
-        // The largest magnitude's binade: as floats, these bit patterns
-        // order like the magnitudes.
+    if (big || small) {
+        // The largest magnitude (as floats, these bit patterns order like
+        // the magnitudes) and its biased binade e.
         const uint32_t wm = __float_as_uint(wave_max(__uint_as_float(mx << 16))) >> 16;
-        k = (int)(wm >> 7) - 127 - 15;
+        const int e = (int)(wm >> 7);
+        k = e - 142 > -kMaxUp ? e - 142 : -kMaxUp;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)

@@ -402,6 +402,37 @@ def test_prefill_attend_v_beyond_fp16():
     print(f"worst error / bound: {worst:.3g}")
 
 
+def test_prefill_attend_v_tiny():
+    # Every V value near 2^-20 (below fp16's normal range): the kernel stages
+    # such dimension tiles scaled up by a power of two, so outputs keep their
+    # relative precision.  Peaked softmax (scale 1), dense and sinks + window
+    # heads, every fourth query against the oracle (max-abs 2e-3 and max-rel
+    # 1e-2 of the row's largest output).
+    B, Hq, Hkv, T = 1, 8, 2, 300
+    q = synth.normal_bf16(synth.key(93, 1), 0, B * Hq * T * 128).reshape(B, Hq, T, 128)
+    K = synth.normal_bf16(synth.key(93, 2), 0, B * Hkv * T * 128).reshape(B, Hkv, T, 128)
+    V = synth.normal_bf16(synth.key(93, 3), 0, B * Hkv * T * 128).reshape(B, Hkv, T, 128)
+    nz = (V & 0x7FFF) != 0
+    V = np.where(nz, V - np.uint16(20 << 7), V).astype(np.uint16)  # exact scaling by 2^-20
+    scale = 1.0
+    out = torch.full((B, Hq, T, 128), float("nan"), dtype=torch.float32, device=dev())
+    qd = torch.from_numpy(q.view(np.int16)).to(dev())
+    Kd = torch.from_numpy(K.view(np.int16)).to(dev())
+    Vd = torch.from_numpy(V.view(np.int16)).to(dev())
+    rtp.rtp_prefill_attend(qd, Kd, Vd, 0, 4, 0, 0, scale, out)
+    rtp.rtp_prefill_attend(qd, Kd, Vd, 4, 4, 4, 64, scale, out)
+    got = out.cpu().numpy()
+    worst = 0.0
+    for h in range(Hq):
+        for t in range(0, T, 4):
+            rows = np.arange(t + 1) if h < 4 else oracle.local_rows(t + 1, 4, 64)
+            ref = oracle.attention(q[0, h, t], K[0, h // 4, rows], V[0, h // 4, rows], scale)
+            ok, err, rel = judge_out(got[0, h, t], ref)
+            assert ok, (h, t, err, rel)
+            worst = max(worst, rel)
+    print(f"largest relative error: {worst:.3g} (bound 1e-2)")
+
+
 def test_prefill_attend_benched_size():
     # The size the benchmark times: a 16384-token prompt, 32 query heads on
     # 4 KV heads, heads 0-7 dense and heads 8-31 on 4 sinks + a 4096-token
