@@ -35,11 +35,14 @@
 //
 // O^T's columns are queries, so each lane's accumulators belong to its own
 // query: the online-softmax rescale needs no exchange, and a query's max and
-// sum combine the lane's 32 values with those of lane l ^ 32.  The softmax
+// sum combine the lane's 32 values with those of lane l ^ 32 (a permlane32
+// swap).  Two tiles per loop trip, with the S^T registers of the current and
+// the next tile trading roles.  The softmax
 // reference moves up only when a tile's max exceeds it by more than 8 (log2
 // units), so probabilities stay below 2^8 and the rescale of O is rare.
-// Precision: V's bf16 values are exact in fp16 (up to 2^16 in magnitude; a
-// dimension tile holding larger ones is staged scaled, see v_store).  P is
+// Precision: V's bf16 values are exact in fp16 between 2^-14 and 2^16 in
+// magnitude (a dimension tile whose largest value lies outside [2^-10,
+// 2^16) is staged scaled by a power of two, see v_store).  P is
 // rounded to fp16 (at most 2^-11 relative) and the softmax sum l adds the
 // same rounded values, so each output is an exact average of V rows under
 // weights within 2^-10 (relative) of the true ones: its error is at most
