@@ -163,19 +163,23 @@ __device__ __forceinline__ void k_store(const HalfRegs &h, PfShared &sh, int buf
         *reinterpret_cast<uint4 *>(&sh.k[buf][(16 * j + (t >> 4)) * kKRow + 8 * (t & 15)]) = h.r[j];
 }
 
-// Two bf16 values as two fp16 values, scaled by 2^-k (round to nearest
-// even).  With k = 0 this is exact for magnitudes in [2^-14, 2^16), where
-// fp16 holds every bf16 value; ldexp is exact while the result stays a
-// normal float.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, int k)
+// Two bf16 values as two fp16 values (round to nearest even): exact for
+// magnitudes in [2^-14, 2^16), where fp16 holds every bf16 value.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w)
 {
-    float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
-    if (k != 0) {
-        lo = __builtin_amdgcn_ldexpf(lo, -k);
-        hi = __builtin_amdgcn_ldexpf(hi, -k);
-    }
-    const f16x2 c = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+    const f16x2 c = {static_cast<_Float16>(__uint_as_float(w << 16)),
+                     static_cast<_Float16>(__uint_as_float(w & 0xFFFF0000u))};
     return __builtin_bit_cast(uint32_t, c);
+}
+
+// Two bf16 values scaled by 2^-k, still as bf16: exact while the results
+// are normal floats (a scaled value keeps its 8 significant bits); results
+// below 2^-126 lose low bits, far below what fp16 keeps anyway.
+__device__ __forceinline__ uint32_t bf16x2_scale(uint32_t w, int k)
+{
+    const float lo = __builtin_amdgcn_ldexpf(__uint_as_float(w << 16), -k);
+    const float hi = __builtin_amdgcn_ldexpf(__uint_as_float(w & 0xFFFF0000u), -k);
+    return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
 }
 
 // V transposed, in fp16: per dimension, the thread's four keys as one 8-B
@@ -217,10 +221,17 @@ __device__ __forceinline__ void v_store(HalfRegs h, PfShared &sh, int buf)
         const int e = (int)(wm >> 7);
         k = e - 142 > -kMaxUp ? e - 142 : -kMaxUp;
     }
+    k = __builtin_amdgcn_readfirstlane(k);  // one value per wave
+    if (k != 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) h.r[j][c] = bf16x2_scale(h.r[j][c], k);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) h.r[j][c] = bf16x2_to_f16x2(h.r[j][c], k);
+        for (int c = 0; c < 4; ++c) h.r[j][c] = bf16x2_to_f16x2(h.r[j][c]);
     if (lane_id() == 0) sh.vshift[buf][(threadIdx.x >> 6) & (kPfWaves / 2 - 1)] = k;
     uint16_t *vt = sh.vt[buf];
 #pragma unroll
