@@ -50,6 +50,7 @@
 // cancels, so that fp16 keeps weights at full precision down to 2^-21 of
 // the reference's.
 #include <math.h>
+#include <stddef.h>
 
 #include "rtp_device.h"
 #include "rtp_launch.h"
@@ -92,9 +93,14 @@ constexpr int kVBuf = 128 * kVRow;            // bf16 per V^T buffer
 
 struct PfShared {
     uint16_t k[2][kKBuf];
-    uint16_t vt[2][kVBuf];          // V^T in fp16, each dimension tile scaled by 2^-vshift
-    int32_t vshift[2][kPfWaves / 2];  // per dimension tile: its scale shift (0 almost always)
+    uint16_t vt[2][kVBuf];  // V^T in fp16, each dimension tile scaled by 2^-vshift
+    // Per buffer, one byte per dimension tile: its scale shift (0 almost
+    // always); read as one word, which every lane of a wave loads at once
+    // without bank conflicts.
+    int8_t vshift[2][kPfWaves / 2];
 };
+
+static_assert(offsetof(PfShared, vshift) % 4 == 0, "each buffer's shifts are one aligned word");
 
 // Magnitude bits of the smallest bf16 value that fp16 cannot hold (2^16).
 constexpr uint32_t kBf16F16Over = 0x4780u;
@@ -232,7 +238,7 @@ __device__ __forceinline__ void v_store(HalfRegs h, PfShared &sh, int buf)
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c) h.r[j][c] = bf16x2_to_f16x2(h.r[j][c]);
-    if (lane_id() == 0) sh.vshift[buf][(threadIdx.x >> 6) & (kPfWaves / 2 - 1)] = k;
+    if (lane_id() == 0) sh.vshift[buf][(threadIdx.x >> 6) & (kPfWaves / 2 - 1)] = (int8_t)k;
     uint16_t *vt = sh.vt[buf];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -390,12 +396,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
             // O^T += V^T P^T; key-step ks takes elements 8 (ks % 2) .. +7 of
             // cur[ks / 2].  P enters as fp16 (round to nearest even) and l
             // sums the same rounded values.
-            const int *vsh = sh.vshift[it & 1];
-            const bool scaled = __builtin_amdgcn_readfirstlane(vsh[0] | vsh[1] | vsh[2] | vsh[3]) != 0;
+            const uint32_t vsh = __builtin_amdgcn_readfirstlane(
+                *reinterpret_cast<const uint32_t *>(sh.vshift[it & 1]));
+            const bool scaled = vsh != 0u;
+            auto shift_of = [&](int dp) { return (int)(int8_t)(vsh >> (8 * dp)); };
             if (scaled) {
 #pragma unroll
                 for (int dp = 0; dp < 4; ++dp) {
-                    const float f = __builtin_amdgcn_ldexpf(1.0f, -vsh[dp]);
+                    const float f = __builtin_amdgcn_ldexpf(1.0f, -shift_of(dp));
 #pragma unroll
                     for (int e = 0; e < 16; ++e) o[dp][e] *= f;
                 }
@@ -426,7 +434,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PfArgs a)
             if (scaled) {
 #pragma unroll
                 for (int dp = 0; dp < 4; ++dp) {
-                    const float f = __builtin_amdgcn_ldexpf(1.0f, vsh[dp]);
+                    const float f = __builtin_amdgcn_ldexpf(1.0f, shift_of(dp));
 #pragma unroll
                     for (int e = 0; e < 16; ++e) o[dp][e] *= f;
                 }
